@@ -1,0 +1,228 @@
+"""Plain, slow CPU oracle for SnapKV observation-window KV selection.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library and imports nothing from the package.
+
+Source: the web page "SnapKV: selecting the KV cache for long prompts with an
+observation window" (charlestar.github.io, 2026-10-20).  Each function below
+cites the section of that page it restates.  Section names are English glosses
+of the page's Chinese headings:
+
+  * "the prompt cache shrinks, the positions keep their origin" (problem setup:
+    L, W, P = L - W, budget C includes the window),
+  * "votes must come from the causal softmax over the full prompt",
+  * "pooling spreads a peak into a neighbourhood preference",
+  * "one full selection computed from Q and K" (worked example, argument rules,
+    short-prompt bypass, tie rule),
+  * "prefill still reads the full K/V; the compressed cache serves decode"
+    (bypass when L < C).
+
+Precision: every floating-point step runs in float64 on values that are exact
+upcasts of the caller's fp32 or bf16 bits.  The page evaluates its example in
+Python floats with exactly rounded sums; this oracle keeps float64 but fixes
+each summation order so that equal inputs give bitwise-equal outputs (this
+matters for exact vote ties):
+
+  * logits: sum over d = 0 .. D-1 in that order,
+  * row normaliser Z_i: exactly rounded (math.fsum),
+  * votes: sum over window rows i = 0 .. W-1 in that order,
+  * avg pooling: the in-range neighbours are summed in ascending order of
+    value (a function of the multiset of neighbours only), then divided by k.
+
+Readings taken where the page is silent (each is also listed in the design doc):
+  * selected prefix indices are returned in ascending order, followed by the
+    window positions P .. L-1 (the page says storage order is free for
+    single-query reads; its example emits score order),
+  * max pooling takes the maximum of the in-range neighbours (padding never
+    wins because every vote is >= 0 and the centre is always in range),
+  * for L < C the whole prompt is kept (bypass), for L == C the whole prefix
+    is selected, which gives the same indices.
+
+Pins: tests/test_oracle_pins.py checks every function here against the page's
+worked example and counterexample, exact rational arithmetic, closed forms,
+brute force over subsets, and PyTorch CPU float64 library routines.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+POOLINGS = ("avg", "max")
+
+
+def validate(L: int, W: int, C: int, D: int, kernel: int, pooling: str) -> None:
+    """Argument rules of the page's worked selection (section "one full
+    selection computed from Q and K"): positive integers, window not longer
+    than the prompt, budget strictly larger than the window, odd pooling
+    width, avg or max pooling, positive head dimension."""
+    for name, value in (("L", L), ("W", W), ("C", C), ("D", D), ("kernel", kernel)):
+        if isinstance(value, bool) or not isinstance(value, (int, np.integer)) or value <= 0:
+            raise ValueError(f"{name} must be a positive integer, got {value!r}")
+    if W > L:
+        raise ValueError("window must not exceed the prompt length")
+    if C <= W:
+        raise ValueError("budget C must exceed the window W")
+    if kernel % 2 != 1:
+        raise ValueError("pooling kernel width must be odd")
+    if pooling not in POOLINGS:
+        raise ValueError("pooling must be 'avg' or 'max'")
+
+
+def window_logits(qwin: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Logits of the W window queries against all L prompt keys.
+
+    Section "votes must come from the causal softmax over the full prompt":
+    l[i, j] = (q_{P+i} . k_j) / sqrt(D).  The dot product is accumulated over
+    d = 0 .. D-1 in that order, in float64.
+    Returns a [W, L] float64 array (no mask applied here).
+    """
+    qwin = np.asarray(qwin, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    W, D = qwin.shape
+    L, D2 = keys.shape
+    if D != D2:
+        raise ValueError("query and key head dimensions differ")
+    acc = np.zeros((W, L), dtype=np.float64)
+    for d in range(D):
+        acc += np.multiply.outer(qwin[:, d], keys[:, d])
+    logits = acc / math.sqrt(D)
+    if not np.all(np.isfinite(logits)):
+        raise ValueError("non-finite dot product")
+    return logits
+
+
+def causal_row_stats(logits: np.ndarray, P: int):
+    """Per window row i (query position t = P + i) over the visible positions
+    j <= t, which include every prefix position and the window positions up to
+    t (section "votes must come from the causal softmax over the full prompt"):
+        m_i = max_j l[i, j],   Z_i = sum_j exp(l[i, j] - m_i).
+    Returns (m, Z), each [W] float64.
+    """
+    W = logits.shape[0]
+    m = np.empty(W, dtype=np.float64)
+    Z = np.empty(W, dtype=np.float64)
+    for i in range(W):
+        visible = logits[i, : P + i + 1]
+        m[i] = visible.max()
+        Z[i] = math.fsum(np.exp(visible - m[i]).tolist())
+    return m, Z
+
+
+def attention_probs(logits: np.ndarray, P: int, m: np.ndarray, Z: np.ndarray) -> np.ndarray:
+    """Full causal softmax of the window rows: alpha[i, j] = exp(l - m_i) / Z_i
+    for j <= P + i and exactly 0 for the masked future positions j > P + i
+    (section "votes must come from the causal softmax over the full prompt")."""
+    W, L = logits.shape
+    probs = np.zeros((W, L), dtype=np.float64)
+    for i in range(W):
+        t = P + i
+        probs[i, : t + 1] = np.exp(logits[i, : t + 1] - m[i]) / Z[i]
+    return probs
+
+
+def prefix_votes(probs: np.ndarray, P: int) -> np.ndarray:
+    """Votes s_j = sum over window rows of alpha[i, j], for prefix columns
+    j < P only, summed over i = 0 .. W-1 in that order (section "votes must come
+    from the causal softmax over the full prompt")."""
+    s = np.zeros(P, dtype=np.float64)
+    for i in range(probs.shape[0]):
+        s = s + probs[i, :P]
+    return s
+
+
+def pool1d(votes: np.ndarray, kernel: int, pooling: str) -> np.ndarray:
+    """Stride-1 1-D pooling of the prefix votes with radius r = (k-1)/2
+    (section "pooling spreads a peak into a neighbourhood preference").
+
+    avg: out-of-range neighbours count as zero and the divisor is always k
+         (PyTorch's count_include_pad=True edge rule).  The in-range
+         neighbours are added in ascending order of value.
+    max: maximum of the in-range neighbours.
+    Neighbours are taken from the prefix only; window votes do not exist.
+    """
+    if pooling not in POOLINGS:
+        raise ValueError("pooling must be 'avg' or 'max'")
+    votes = np.asarray(votes, dtype=np.float64)
+    P = votes.shape[0]
+    r = kernel // 2
+    # nb[j, o] = votes[j - r + o] when 0 <= j - r + o < P, else padding.
+    pad = 0.0 if pooling == "avg" else -np.inf
+    padded = np.concatenate([np.full(r, pad), votes, np.full(r, pad)])
+    nb = np.stack([padded[o:o + P] for o in range(kernel)], axis=1)
+    if pooling == "max":
+        return nb.max(axis=1)
+    # Votes are >= 0, so the zero padding sorts first and adding it is exact:
+    # the running sum equals the ascending-order sum of the in-range values.
+    nb = np.sort(nb, axis=1)
+    total = np.zeros(P, dtype=np.float64)
+    for o in range(kernel):
+        total = total + nb[:, o]
+    return total / kernel
+
+
+def top_prefix(pooled: np.ndarray, count: int) -> np.ndarray:
+    """The `count` prefix positions ranked first by (-pooled_j, j): highest
+    pooled score first, equal scores broken towards the lowest index (section
+    "one full selection computed from Q and K").  Returned in ascending index
+    order (reading: storage order of kept positions is free)."""
+    P = pooled.shape[0]
+    order = np.lexsort((np.arange(P), -pooled))
+    return np.sort(order[:count])
+
+
+def snapkv_select(qwin, keys, values, W: int, C: int, kernel: int = 3, pooling: str = "avg") -> Dict:
+    """SnapKV observation-window selection for one (sequence, head).
+
+    qwin: [W, D] queries of the last W prompt positions (P .. L-1),
+    keys, values: [L, D].
+    Returns a dict with
+      indices [min(L, C)] int64: ascending selected prefix positions, then
+                                 the window positions P .. L-1,
+      keys, values:              rows of K and V at those indices,
+      votes [P], pooled [P]:     float64 (empty when the bypass applies),
+      row_max [W], row_sum [W]:  float64 m_i and Z_i (empty for the bypass).
+    """
+    qwin = np.asarray(qwin, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    L, D = keys.shape
+    if values.shape != keys.shape or qwin.shape != (W, D):
+        raise ValueError("shape mismatch between Qwin, K and V")
+    validate(L, W, C, D, kernel, pooling)
+    for name, x in (("Qwin", qwin), ("K", keys), ("V", values)):
+        if not np.all(np.isfinite(x)):
+            raise ValueError(f"{name} must be finite")
+    empty = np.zeros(0, dtype=np.float64)
+    if L < C:
+        # Short-prompt bypass: keep every position (sections "one full
+        # selection computed from Q and K" and "prefill still reads the full
+        # K/V; the compressed cache serves decode").
+        idx = np.arange(L, dtype=np.int64)
+        return {"indices": idx, "keys": keys.copy(), "values": values.copy(),
+                "votes": empty, "pooled": empty, "row_max": empty, "row_sum": empty}
+    P = L - W
+    logits = window_logits(qwin, keys)
+    m, Z = causal_row_stats(logits, P)
+    probs = attention_probs(logits, P, m, Z)
+    votes = prefix_votes(probs, P)
+    pooled = pool1d(votes, kernel, pooling)
+    chosen = top_prefix(pooled, C - W)
+    idx = np.concatenate([chosen, np.arange(P, L)]).astype(np.int64)
+    return {"indices": idx, "keys": keys[idx], "values": values[idx],
+            "votes": votes, "pooled": pooled, "row_max": m, "row_sum": Z}
+
+
+def snapkv_select_heads(qwin, keys, values, W: int, C: int, kernel: int = 3,
+                        pooling: str = "avg", heads: Sequence[int] | None = None) -> List[Dict]:
+    """Independent selection per head (section "the prompt cache shrinks, the
+    positions keep their origin": every layer and head chooses on its own).
+    qwin [H, W, D], keys/values [H, L, D]; `heads` restricts the evaluation to a
+    subset of heads (results are returned in that order)."""
+    H = keys.shape[0]
+    heads = range(H) if heads is None else heads
+    return [snapkv_select(qwin[h], keys[h], values[h], W, C, kernel, pooling) for h in heads]

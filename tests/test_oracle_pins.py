@@ -1,0 +1,454 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself:
+values printed on the SnapKV observation-window page, exact rational
+arithmetic from the page's printed exp-weight tables, closed forms, brute force
+over subsets, and PyTorch CPU float64 library routines."""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import snapkv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def weights_to_inputs(rows, placeholder, L):
+    """Keys whose coordinate i is ln(w_i[j]) and queries sqrt(D) * e_i, so that
+    q_i . k_j / sqrt(D) = ln w_i[j] (the page's construction)."""
+    W = len(rows)
+    D = W
+    K = np.zeros((L, D))
+    for i, row in enumerate(rows):
+        for j, w in enumerate(row):
+            K[j, i] = math.log(placeholder if w is None else w)
+    Q = np.zeros((W, D))
+    for i in range(W):
+        Q[i, i] = math.sqrt(D)
+    return Q, K
+
+
+def exact_votes(rows, P):
+    """Votes and row sums as exact rationals straight from exp-weights: row i
+    sees positions j <= P + i (None marks the causal future)."""
+    sums = []
+    votes = [Fraction(0)] * P
+    for i, row in enumerate(rows):
+        vis = [Fraction(w) for w in row[: P + i + 1]]
+        Z = sum(vis)
+        sums.append(Z)
+        for j in range(P):
+            votes[j] += vis[j] / Z
+    return votes, sums
+
+
+def exact_pool(votes, k, pooling):
+    P, r = len(votes), k // 2
+    out = []
+    for j in range(P):
+        nb = [votes[p] for p in range(j - r, j + r + 1) if 0 <= p < P]
+        out.append(sum(nb, Fraction(0)) / k if pooling == "avg" else max(nb))
+    return out
+
+
+def exact_top(pooled, n):
+    return sorted(sorted(range(len(pooled)), key=lambda j: (-pooled[j], j))[:n])
+
+
+# ------------------------------------------------------------- worked example
+
+def worked():
+    g = load("worked_example.json")
+    rows = [g["exp_weight_rows"]["query_6"], g["exp_weight_rows"]["query_7"]]
+    Q, K = weights_to_inputs(rows, g["masked_placeholder"], g["L"])
+    V = np.array([[j, -j] for j in range(g["L"])], dtype=np.float64)
+    return g, rows, Q, K, V
+
+
+def test_worked_example_page_values():
+    g, rows, Q, K, V = worked()
+    r = O.snapkv_select(Q, K, V, g["W"], g["C"], g["kernel"], g["pooling"])
+    assert r["indices"].tolist() == g["expected_indices"]
+    assert r["values"].tolist() == g["expected_values"]
+    np.testing.assert_array_equal(r["keys"], K[g["expected_indices"]])
+    # Row sums 25 and 26 in exp-weight units: Z_i * exp(m_i).
+    got = r["row_sum"] * np.exp(r["row_max"])
+    np.testing.assert_allclose(got, [g["row_sums"]["query_6"], g["row_sums"]["query_7"]], rtol=1e-13)
+    assert int(np.argmax(r["votes"])) == g["raw_vote_argmax"]
+    assert int(np.argmax(r["pooled"])) == g["pooled_argmax"]
+    # Position 4 is lifted by its neighbour 3: above position 1 after pooling
+    # although its raw vote is below position 1's.
+    assert r["votes"][4] < r["votes"][1] and r["pooled"][4] > r["pooled"][1]
+
+
+def test_worked_example_exact_rationals():
+    g, rows, Q, K, V = worked()
+    P = g["L"] - g["W"]
+    ev, sums = exact_votes(rows, P)
+    assert sums == [25, 26]
+    assert ev == [Fraction(n, 650) for n in (51, 77, 460, 508, 51, 51)]
+    ep = exact_pool(ev, 3, "avg")
+    assert ep == [Fraction(n, 1950) for n in (128, 588, 1045, 1019, 610, 102)]
+    r = O.snapkv_select(Q, K, V, g["W"], g["C"], 3, "avg")
+    np.testing.assert_allclose(r["votes"], [float(x) for x in ev], rtol=1e-14)
+    np.testing.assert_allclose(r["pooled"], [float(x) for x in ep], rtol=1e-14)
+    # Other widths and modes on the same page data, exact expectations.
+    for k, pooling, C in [(1, "avg", 5), (3, "max", 5), (3, "max", 4), (5, "avg", 5), (5, "max", 3)]:
+        expect = exact_top(exact_pool(ev, k, pooling), C - g["W"])
+        r = O.snapkv_select(Q, K, V, g["W"], C, k, pooling)
+        assert r["indices"].tolist() == expect + [6, 7], (k, pooling, C)
+    # Specific consequences: width 1 picks {1,2,3}; max-3 with C=4 is a
+    # three-way tie (2,3,4 at 508/650) resolved to the lowest indices.
+    assert O.snapkv_select(Q, K, V, 2, 5, 1, "avg")["indices"].tolist() == [1, 2, 3, 6, 7]
+    r = O.snapkv_select(Q, K, V, 2, 4, 3, "max")
+    assert r["indices"].tolist() == [2, 3, 6, 7]
+    assert r["pooled"][2] == r["pooled"][3] == r["pooled"][4]
+
+
+@pytest.mark.parametrize("placeholder", [1e-6, 1.0, 1e6])
+def test_worked_example_masked_entry_has_no_effect(placeholder):
+    g, rows, Q, K, V = worked()
+    Q2, K2 = weights_to_inputs(rows, placeholder, g["L"])
+    a = O.snapkv_select(Q, K, V, 2, 5, 3, "avg")
+    b = O.snapkv_select(Q2, K2, V, 2, 5, 3, "avg")
+    np.testing.assert_allclose(b["votes"], a["votes"], rtol=1e-14)
+    np.testing.assert_allclose(b["row_sum"] * np.exp(b["row_max"]), [25, 26], rtol=1e-13)
+    assert b["indices"].tolist() == a["indices"].tolist()
+
+
+# ------------------------------------------------------------- counterexample
+
+def counter():
+    g = load("counterexample.json")
+    rows = [g["exp_weight_rows"]["query_2"], g["exp_weight_rows"]["query_3"]]
+    Q, K = weights_to_inputs(rows, g["masked_placeholder"], g["L"])
+    V = np.arange(2 * g["L"], dtype=np.float64).reshape(g["L"], 2)
+    return g, rows, Q, K, V
+
+
+def check_counterexample(select_fn):
+    g, rows, Q, K, V = counter()
+    p = g["printed"]["full_softmax"]
+    r = select_fn(Q, K, V, g["W"], g["C"], 1, "avg")
+    np.testing.assert_allclose(r["votes"], [p["A_vote"], p["B_vote"]], rtol=1e-12)
+    pick = g["positions"][p["pick"]]
+    assert r["indices"].tolist() == [pick, 2, 3]
+
+
+def test_counterexample_full_softmax_picks_B():
+    g, rows, Q, K, V = counter()
+    # The reconstructed weights reproduce all eight printed probabilities.
+    full, prefix = g["printed"]["full_softmax"], g["printed"]["prefix_only"]
+    ev, _ = exact_votes(rows, 2)
+    assert [float(x) for x in ev] == pytest.approx([full["A_vote"], full["B_vote"]], rel=1e-15)
+    pre = [[Fraction(w) / sum(Fraction(x) for x in row[:2]) for w in row[:2]] for row in rows]
+    assert [float(pre[0][0]), float(pre[1][0])] == pytest.approx(prefix["A_terms"])
+    assert [float(pre[0][1]), float(pre[1][1])] == pytest.approx(prefix["B_terms"])
+    check_counterexample(O.snapkv_select)
+    # Per-row terms of the full softmax, against the printed ones.
+    r = O.snapkv_select(Q, K, V, 2, 3, 1, "avg")
+    L, P = 4, 2
+    logits = O.window_logits(Q, K)
+    m, Z = O.causal_row_stats(logits, P)
+    probs = O.attention_probs(logits, P, m, Z)
+    np.testing.assert_allclose(probs[:, 0], full["A_terms"], rtol=1e-12)
+    np.testing.assert_allclose(probs[:, 1], full["B_terms"], rtol=1e-12)
+    assert r["votes"][1] > r["votes"][0]
+
+
+def test_negative_control_prefix_only_normalisation_is_caught(monkeypatch):
+    """Plant the page's wrong variant (softmax renormalised over the prefix
+    columns only) into the oracle: the counterexample pin must reject it."""
+    def prefix_only(logits, P, m, Z):
+        W, L = logits.shape
+        probs = np.zeros((W, L))
+        for i in range(W):
+            w = np.exp(logits[i, :P] - logits[i, :P].max())
+            probs[i, :P] = w / w.sum()
+        return probs
+
+    monkeypatch.setattr(O, "attention_probs", prefix_only)
+    g, rows, Q, K, V = counter()
+    r = O.snapkv_select(Q, K, V, 2, 3, 1, "avg")
+    np.testing.assert_allclose(r["votes"], [1.15, 0.85], rtol=1e-12)
+    assert r["indices"][0] == g["positions"]["A"]
+    with pytest.raises(AssertionError):
+        check_counterexample(O.snapkv_select)
+
+
+def test_counterexample_avg3_is_an_exact_tie():
+    g, rows, Q, K, V = counter()
+    r = O.snapkv_select(Q, K, V, 2, 3, 3, "avg")
+    assert r["pooled"][0] == r["pooled"][1]
+    assert r["pooled"][0] == pytest.approx(1 / 3, rel=1e-15)
+    assert r["indices"].tolist() == [0, 2, 3]
+
+
+# ------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("L,W", [(10, 3), (64, 8), (257, 32)])
+def test_uniform_closed_form(L, W):
+    """All keys equal (or all window queries zero): row i is uniform over its
+    P + i + 1 visible positions, so every prefix vote is H_L - H_P."""
+    rng = np.random.default_rng(L)
+    D, P = 8, L - W
+    s_exact = sum(Fraction(1, P + i + 1) for i in range(W))
+    if (L, W) == (10, 3):
+        assert s_exact == Fraction(121, 360)
+    Q = rng.standard_normal((W, D))
+    K = np.tile(rng.standard_normal(D), (L, 1))
+    V = rng.standard_normal((L, D))
+    for (q, k) in [(Q, K), (np.zeros((W, D)), rng.standard_normal((L, D)))]:
+        r = O.snapkv_select(q, k, V, W, W + 1, 3, "avg")
+        np.testing.assert_allclose(r["votes"], float(s_exact), rtol=1e-13)
+        expect = np.full(P, float(s_exact))
+        expect[0] = expect[-1] = float(s_exact) * 2 / 3
+        np.testing.assert_allclose(r["pooled"], expect, rtol=1e-13)
+        r = O.snapkv_select(q, k, V, W, W + 1, 5, "max")
+        np.testing.assert_allclose(r["pooled"], float(s_exact), rtol=1e-13)
+
+
+def test_uniform_ties_go_to_lowest_index():
+    L, W, D = 40, 4, 8
+    P = L - W
+    rng = np.random.default_rng(7)
+    Q = rng.standard_normal((W, D))
+    K = np.tile(rng.standard_normal(D), (L, 1))
+    V = rng.standard_normal((L, D))
+    for n in (1, 5, P - 2):
+        r = O.snapkv_select(Q, K, V, W, W + n, 3, "avg")
+        # interior positions tie exactly; the two edges are lower (2/3)
+        assert r["indices"].tolist() == list(range(1, n + 1)) + list(range(P, L))
+    r = O.snapkv_select(Q, K, V, W, W + P - 1, 3, "avg")
+    assert r["indices"][:P - 1].tolist() == list(range(0, P - 1))
+
+
+def test_identical_keys_give_bitwise_equal_votes():
+    rng = np.random.default_rng(11)
+    L, W, D = 300, 16, 32
+    book = rng.standard_normal((5, D))
+    codes = rng.integers(0, 5, size=L)
+    K = book[codes]
+    Q = rng.standard_normal((W, D))
+    r = O.snapkv_select(Q, K, np.zeros((L, D)), W, W + 20, 5, "avg")
+    P = L - W
+    for c in range(5):
+        vs = r["votes"][codes[:P] == c]
+        assert np.all(vs == vs[0])
+    # equal neighbour multisets give bitwise-equal pooled scores
+    seen = {}
+    for j in range(2, P - 2):
+        key = tuple(sorted(codes[j - 2:j + 3]))
+        if key in seen:
+            assert r["pooled"][j] == seen[key]
+        seen[key] = r["pooled"][j]
+
+
+# ------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bruteforce_subsets(seed):
+    """Tiny prompts from integer exp-weights: the oracle's selection must be a
+    maximum-sum (C-W)-subset of the exact pooled scores, and when the maximum
+    is unique, exactly that subset."""
+    rng = np.random.default_rng(1000 + seed)
+    W = int(rng.integers(1, 4))
+    L = int(rng.integers(W + 2, W + 10))
+    P = L - W
+    C = int(rng.integers(W + 1, L + 1))
+    k = int(rng.choice([1, 3, 5]))
+    pooling = str(rng.choice(["avg", "max"]))
+    rows = [[int(x) for x in rng.integers(1, 60, size=L)] for _ in range(W)]
+    for i in range(W):
+        for j in range(P + i + 1, L):
+            rows[i][j] = None
+    Q, K = weights_to_inputs(rows, 1, L)
+    V = rng.standard_normal((L, W))
+    r = O.snapkv_select(Q, K, V, W, C, k, pooling)
+    ev, _ = exact_votes(rows, P)
+    ep = exact_pool(ev, k, pooling)
+    n = C - W
+    subsets = list(itertools.combinations(range(P), n))
+    sums = [sum((ep[j] for j in s), Fraction(0)) for s in subsets]
+    best = max(sums)
+    winners = [s for s, t in zip(subsets, sums) if t == best]
+    got = tuple(r["indices"][:n].tolist())
+    assert got in winners
+    if len(winners) == 1:
+        assert got == winners[0]
+    assert r["indices"][n:].tolist() == list(range(P, L))
+
+
+def test_bruteforce_exact_ties_lowest_index():
+    """Exact ties built from identical weight columns: among all maximum-sum
+    subsets the oracle returns the lexicographically smallest, i.e. the
+    lowest tied indices."""
+    L, W = 9, 2
+    P = L - W
+    col = [3, 5, 3, 5, 5, 3, 5]
+    rows = [[c for c in col] + [4, None], [c for c in col] + [4, 4]]
+    Q, K = weights_to_inputs(rows, 1, L)
+    V = np.zeros((L, 2))
+    ev, _ = exact_votes(rows, P)
+    for C in range(W + 1, L):
+        n = C - W
+        ep = exact_pool(ev, 1, "avg")
+        subsets = list(itertools.combinations(range(P), n))
+        sums = [sum((ep[j] for j in s), Fraction(0)) for s in subsets]
+        best = min(s for s, t in zip(subsets, sums) if t == max(sums))
+        r = O.snapkv_select(Q, K, V, W, C, 1, "avg")
+        assert tuple(r["indices"][:n].tolist()) == best
+
+
+# ------------------------------------------------------------- libraries
+
+@pytest.mark.parametrize("L,W,D", [(17, 5, 4), (64, 16, 8), (130, 32, 16)])
+def test_full_causal_attention_crosscheck(L, W, D):
+    """Votes equal the column sums, over the last W rows, of the full L x L
+    causal attention that PyTorch computes in float64 (softmax over a
+    triangular mask)."""
+    rng = np.random.default_rng(L * 31 + W)
+    Qfull = rng.standard_normal((L, D)) * 2
+    K = rng.standard_normal((L, D)) * 2
+    V = rng.standard_normal((L, D))
+    P = L - W
+    q, k = torch.from_numpy(Qfull), torch.from_numpy(K)
+    logits = (q @ k.T) / math.sqrt(D)
+    mask = torch.triu(torch.ones(L, L, dtype=torch.bool), diagonal=1)
+    att = torch.softmax(logits.masked_fill(mask, float("-inf")), dim=-1)
+    ref_votes = att[P:, :P].sum(dim=0).numpy()
+    r = O.snapkv_select(Qfull[P:], K, V, W, W + 1, 1, "avg")
+    np.testing.assert_allclose(r["votes"], ref_votes, rtol=1e-12, atol=1e-300)
+    lse = torch.logsumexp(logits.masked_fill(mask, float("-inf"))[P:], dim=-1).numpy()
+    np.testing.assert_allclose(r["row_max"] + np.log(r["row_sum"]), lse, rtol=1e-13)
+    np.testing.assert_allclose(r["row_max"], logits.masked_fill(mask, float("-inf"))[P:].max(dim=-1).values.numpy(), rtol=1e-14)
+
+
+@pytest.mark.parametrize("k", [1, 3, 5, 7, 9])
+@pytest.mark.parametrize("P", [1, 2, 6, 50])
+def test_pool_crosscheck_torch(k, P):
+    rng = np.random.default_rng(k * 100 + P)
+    v = rng.random(P) ** 3
+    t = torch.from_numpy(v)[None, None]
+    r = k // 2
+    if r <= k // 2 and P >= 1:
+        ref_avg = torch.nn.functional.avg_pool1d(t, k, stride=1, padding=r, count_include_pad=True)[0, 0].numpy()
+        ref_max = torch.nn.functional.max_pool1d(t, k, stride=1, padding=r)[0, 0].numpy()
+        np.testing.assert_allclose(O.pool1d(v, k, "avg"), ref_avg, rtol=1e-15)
+        np.testing.assert_array_equal(O.pool1d(v, k, "max"), ref_max)
+
+
+def test_top_prefix_matches_python_sort():
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        P = int(rng.integers(1, 200))
+        s = rng.integers(0, 6, size=P).astype(np.float64)  # many exact ties
+        n = int(rng.integers(1, P + 1))
+        ref = sorted(sorted(range(P), key=lambda j: (-s[j], j))[:n])
+        assert O.top_prefix(s, n).tolist() == ref
+
+
+# ------------------------------------------------------------- invariants
+
+def random_case(seed, L=200, W=16, D=32):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((W, D)) * 1.5, rng.standard_normal((L, D)) * 1.5,
+            rng.standard_normal((L, D)))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_invariants(seed):
+    Q, K, V = random_case(seed)
+    W, L, D = Q.shape[0], K.shape[0], K.shape[1]
+    P = L - W
+    C = 60
+    r = O.snapkv_select(Q, K, V, W, C, 5, "avg")
+    s = r["votes"]
+    assert np.all(s >= 0) and np.all(s <= W)
+    # total prefix vote = sum over rows of (1 - mass on window columns)
+    logits = O.window_logits(Q, K)
+    m, Z = O.causal_row_stats(logits, P)
+    probs = O.attention_probs(logits, P, m, Z)
+    np.testing.assert_allclose(probs.sum(axis=1), 1.0, rtol=1e-13)
+    assert s.sum() == pytest.approx(W - probs[:, P:].sum(), rel=1e-12)
+    # joint permutation of the head dimension
+    perm = np.random.default_rng(seed).permutation(D)
+    r2 = O.snapkv_select(Q[:, perm], K[:, perm], V, W, C, 5, "avg")
+    np.testing.assert_allclose(r2["votes"], s, rtol=1e-12)
+    assert r2["indices"].tolist() == r["indices"].tolist()
+    # V affects only V'
+    r3 = O.snapkv_select(Q, K, V * -3 + 1, W, C, 5, "avg")
+    assert r3["indices"].tolist() == r["indices"].tolist()
+    np.testing.assert_array_equal(r3["values"], (V * -3 + 1)[r["indices"]])
+    # max pooling dominates the raw votes; window indices; pairing
+    rm = O.snapkv_select(Q, K, V, W, C, 5, "max")
+    assert np.all(rm["pooled"] >= rm["votes"])
+    assert r["indices"][C - W:].tolist() == list(range(P, L))
+    np.testing.assert_array_equal(r["keys"], K[r["indices"]])
+    np.testing.assert_array_equal(r["values"], V[r["indices"]])
+    assert len(set(r["indices"].tolist())) == C
+
+
+def test_heads_are_independent():
+    rng = np.random.default_rng(3)
+    H, L, W, D = 3, 120, 8, 16
+    Q = rng.standard_normal((H, W, D)) * 2
+    K = rng.standard_normal((H, L, D)) * 2
+    V = rng.standard_normal((H, L, D))
+    res = O.snapkv_select_heads(Q, K, V, W, 30, 3, "avg")
+    perm = [2, 0, 1]
+    res_p = O.snapkv_select_heads(Q[perm], K[perm], V[perm], W, 30, 3, "avg")
+    for a, h in zip(res_p, perm):
+        assert a["indices"].tolist() == res[h]["indices"].tolist()
+    assert len({tuple(r["indices"].tolist()) for r in res}) > 1
+
+
+def test_bypass_and_full_budget():
+    Q, K, V = random_case(9, L=50, W=10, D=8)
+    r = O.snapkv_select(Q, K, V, 10, 51, 3, "avg")
+    assert r["indices"].tolist() == list(range(50))
+    np.testing.assert_array_equal(r["keys"], K)
+    np.testing.assert_array_equal(r["values"], V)
+    r = O.snapkv_select(Q, K, V, 10, 50, 3, "avg")
+    assert r["indices"].tolist() == list(range(50))
+    Qw = np.random.default_rng(4).standard_normal((50, 8))
+    r = O.snapkv_select(Qw, K, V, 50, 51, 3, "max")  # W == L: empty prefix, bypass
+    assert r["indices"].tolist() == list(range(50))
+
+
+def test_window_equals_prompt_with_budget_equal():
+    # W == L and C == L is rejected? No: C must exceed W, so C = L is invalid.
+    Q, K, V = random_case(2, L=20, W=20, D=4)
+    with pytest.raises(ValueError):
+        O.snapkv_select(Q, K, V, 20, 20, 3, "avg")
+
+
+@pytest.mark.parametrize("args", [
+    dict(W=0), dict(W=51), dict(C=10), dict(C=5), dict(kernel=2), dict(kernel=0),
+    dict(pooling="min"), dict(W=True),
+])
+def test_validation_rules(args):
+    Q, K, V = random_case(1, L=50, W=10, D=8)
+    kw = dict(W=10, C=20, kernel=3, pooling="avg")
+    kw.update(args)
+    q = Q if kw["W"] in (10, True) or not isinstance(kw["W"], int) else np.zeros((max(kw["W"], 0), 8))
+    with pytest.raises(ValueError):
+        O.snapkv_select(q, K, V, kw["W"], kw["C"], kw["kernel"], kw["pooling"])
+
+
+def test_nonfinite_rejected():
+    Q, K, V = random_case(1, L=50, W=10, D=8)
+    K = K.copy()
+    K[3, 2] = np.inf
+    with pytest.raises(ValueError):
+        O.snapkv_select(Q, K, V, 10, 20, 3, "avg")
