@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of observation-window KV selection on one MI355X.
+
+One step = the whole selection path (window logits, causal row statistics,
+votes, pooling, top-(C-W), window append, K/V gather) over one batch of the
+workload; for the default workload that is 32 layer calls, each over the
+layer's 32 heads at L = 32768, W = 32, C = 1024, D = 128, bf16, max pooling
+of width 5, with 1% of prefix keys planted near the window queries' mean.
+Inputs are resident in HBM before the timed region starts; every layer has
+its own K and V, so consecutive calls stream fresh data.
+
+Prints one JSON line.  value = prompt tokens scored per second
+= L * layers * steps / elapsed (a token counts once per layer, over all of
+that layer's heads).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prompt tokens scored/s and HBM GB/s (% of peak), 32 heads, L=32768, D=128"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_alg_bytes(name, w, nch):
+    """Algorithmic bytes one launch of a kernel moves for one layer call."""
+    e = 2 if w.dtype == "bf16" else 4
+    H, L, W, C, D = w.heads, w.L, w.W, w.C, w.D
+    P = L - W
+    q = H * W * D * e
+    if name == "window_stats":      # K once, Qwin, partial (max, sum) per chunk
+        return H * L * D * e + q + H * nch * W * 8
+    if name == "window_votes":      # prefix K, Qwin, partials, votes out
+        return H * P * D * e + q + H * nch * W * 8 + H * P * 4
+    if name == "pool":
+        return H * P * 8
+    if name == "topk":
+        return H * P * 4 + H * C * 4
+    if name == "gather":            # read and write the kept K and V rows
+        return 4 * H * C * D * e + H * C * 4
+    return None
+
+
+def path_alg_bytes(w):
+    """Minimum bytes of the whole path per layer call: K once, Qwin, the
+    kept K/V rows read and written, the indices."""
+    e = 2 if w.dtype == "bf16" else 4
+    return w.heads * (w.L * w.D * e + w.W * w.D * e + 4 * w.C * w.D * e + 4 * w.C)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "prompt_kv_selection_amd", "csrc"))):
+        with open(os.path.join(ROOT, "prompt_kv_selection_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel):
+    """Counter-measured HBM bytes per launch, if the stored counters were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or rec.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle on a bounded sample of the same workload: heads of
+    layer 0 (then layer 1, ...) in a thread pool, until `seconds` of wall time
+    have passed after a full round."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import snapkv_oracle as O
+    from prompt_kv_selection_amd import workloads as WL
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    jobs = [(l, h) for l in range(w.layers) for h in range(w.heads)]
+    inputs = {}
+
+    def prepare(job):
+        q, k, v = WL.head_arrays(w, job[1], layer=job[0])
+        return job, (WL.to_float64(q, w.dtype), WL.to_float64(k, w.dtype), WL.to_float64(v, w.dtype))
+
+    def run(job):
+        q, k, v = inputs.pop(job)
+        O.snapkv_select(q, k, v, w.W, w.C, w.kernel, w.pooling)
+
+    done = 0
+    elapsed = 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while done < len(jobs) and elapsed < seconds:
+            batch = jobs[done:done + threads]
+            inputs.update(dict(ex.map(prepare, batch)))     # input drawing is not timed
+            t0 = time.perf_counter()
+            list(ex.map(run, batch))
+            elapsed += time.perf_counter() - t0
+            done += len(batch)
+    tokens = w.L * done / w.heads
+    return {"value": tokens / elapsed, "unit": "prompt tokens scored/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} heads (layer-major) of the same workload, {elapsed:.1f} s of oracle time; "
+                      f"value = L * heads_done / heads_per_layer / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="spike_l32x_h32_l32k")
+    ap.add_argument("--layers", type=int, default=0, help="layers per step (default: the workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build measures one GPU's share "
+              f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from prompt_kv_selection_amd import binding as B
+    from prompt_kv_selection_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a HIP device")
+    w = WL.get(args.workload)
+    if w.ragged:
+        raise SystemExit("bench.py times single-length workloads")
+    layers = args.layers or w.layers
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    H, L, W, C, D = w.heads, w.L, w.W, w.C, w.D
+
+    log(f"drawing {layers} layer(s) of {w.name}")
+    t0 = time.time()
+    Qs, Ks, Vs = [], [], []
+    for layer in range(layers):
+        Q, K, V = WL.layer_arrays(w, layer=layer)
+        conv = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)) if w.dtype == "bf16" else \
+            (lambda a: torch.from_numpy(a))
+        Qs.append(conv(Q).to(dev))
+        Ks.append(conv(K).to(dev))
+        Vs.append(conv(V).to(dev))
+        del Q, K, V
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM after {time.time() - t0:.1f} s")
+
+    ws = torch.empty(B.kvsel_workspace_bytes(H, L, W, C, D, td), dtype=torch.uint8, device=dev)
+    idx = [torch.empty((H, C), dtype=torch.int32, device=dev) for _ in range(layers)]
+    Ko = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
+    Vo = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for layer in range(layers):
+            B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, H, w.kernel, w.pooling, td,
+                           idx[layer], Ko[layer], Vo[layer], None, None, None, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region, with per-kernel HIP events recorded on the launch stream.
+    B.kvsel_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    per_kernel = B.kvsel_profile_read()
+    B.kvsel_profile_enable(False)
+
+    # Same work without the per-kernel events, for comparison.
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_noprof = start.elapsed_time(stop)
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 1 GiB device-to-device copy done")
+
+    ms_step = ms_total / args.steps
+    tokens_per_s = L * layers * args.steps / (ms_total / 1e3)
+    nch = (L + 1023) // 1024
+    kern = {}
+    for name, (n, ms) in per_kernel.items():
+        ab = kernel_alg_bytes(name, w, nch)
+        avg = ms / n
+        kern[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
+                      "alg_GBps": None if ab is None else round(ab / (avg / 1e3) / 1e9, 1)}
+    dom = max(per_kernel, key=lambda k: per_kernel[k][1])
+    n_dom, ms_dom = per_kernel[dom]
+    ab_dom = kernel_alg_bytes(dom, w, nch)
+    achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
+    traffic = traffic_from_profiles(dom)
+    path_gbps = path_alg_bytes(w) * layers / (ms_step / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "prompt tokens scored/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": layers, "heads": H, "L": L, "W": W, "C": C, "D": D,
+                   "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "path": {"alg_bytes_per_layer": path_alg_bytes(w), "alg_GBps": round(path_gbps, 1),
+                 "frac_of_peak": round(path_gbps / HBM_PEAK_GBPS, 4),
+                 "ms_per_step_without_events": round(ms_noprof / args.steps, 4)},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

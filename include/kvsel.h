@@ -1,0 +1,185 @@
+/*
+ * kvsel.h -- observation-window (SnapKV) KV-cache selection on AMD MI355X.
+ *
+ * C ABI of libkvsel.so.  Every compute step runs in HIP kernels written for
+ * gfx950; the host side only validates arguments, partitions the caller's
+ * workspace and enqueues kernels on the caller's stream.
+ *
+ * What is computed (web page "SnapKV: selecting the KV cache for long prompts
+ * with an observation window", charlestar.github.io, 2026-10-20):
+ *   For one (sequence, head) with prompt length L, window W, budget C (the
+ *   budget includes the window), P = L - W prefix positions
+ *   [section "the prompt cache shrinks, the positions keep their origin"]:
+ *     l[i][j] = Qwin[i] . K[j] / sqrt(D)        window row i = query at P + i
+ *     alpha[i][j] = softmax over the visible positions j <= P + i, with the
+ *                   denominator over every visible prefix AND window position
+ *     s[j] = sum_i alpha[i][j]                  prefix votes, j < P
+ *                   [section "votes must come from the causal softmax over the
+ *                    full prompt"]
+ *     pooled = 1-D pooling of s, stride 1, width k odd, zero padding; avg
+ *              always divides by k; max takes the in-range maximum
+ *                   [section "pooling spreads a peak into a neighbourhood
+ *                    preference"]
+ *     indices = the C - W prefix positions with the highest pooled score,
+ *               equal scores going to the lowest index, in ascending order,
+ *               followed by the window positions P .. L-1
+ *     K_out, V_out = the rows of K and V at those indices, bit copies
+ *                   [section "one full selection computed from Q and K"]
+ *   When L < C the selection is bypassed: indices 0 .. L-1, K_out = K,
+ *   V_out = V [sections "one full selection computed from Q and K" and
+ *   "prefill still reads the full K/V; the compressed cache serves decode"].
+ *   Heads (and layers, and sequences) are independent: each chooses its own
+ *   indices [section "the prompt cache shrinks, the positions keep their
+ *   origin"].
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers unless the name ends in _host.
+ *     Every buffer is owned and allocated by the caller; the library keeps no
+ *     device state between calls and allocates nothing.
+ *   - Element types: dtype KVSEL_BF16 means Qwin, K, V, K_out, V_out hold
+ *     bfloat16; KVSEL_F32 means float32.  Scores are float32, indices int32.
+ *   - Layouts are row-major with the head dimension D contiguous.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; the library never synchronises.  Argument
+ *     errors are detected on the host before anything is enqueued, and then
+ *     no output is touched.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Return value: KVSEL_OK or a negative kvsel_status; kvsel_last_error()
+ *     returns a thread-local message describing the last failure.
+ *   - Supported: D in {64, 128}, 1 <= W <= 128, L < 2^31 / D.  Inputs must be
+ *     finite (a precondition; the page's example rejects non-finite values).
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSEL_OK = 0,
+  KVSEL_EINVAL = -1,       /* argument outside the method's rules or NULL pointer */
+  KVSEL_EUNSUPPORTED = -2, /* valid for the method, not covered by these kernels */
+  KVSEL_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes value */
+  KVSEL_EDEVICE = -4       /* a HIP call or kernel launch failed */
+} kvsel_status;
+
+enum { KVSEL_POOL_AVG = 0, KVSEL_POOL_MAX = 1 };
+enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
+
+/* Library version, (major << 16) | minor. */
+int kvsel_version(void);
+
+/* Thread-local description of the last non-OK return ("" if none). */
+const char* kvsel_last_error(void);
+
+/* Workspace bytes kvsel_select needs for these sizes; 0 if the arguments are
+ * invalid (kvsel_last_error() says why).  Host-only, enqueues nothing. */
+size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype);
+
+/* Full selection for `heads` independent heads of one sequence (a layer's
+ * heads, or several layers folded into `heads`: results are identical).
+ *   Qwin     [heads][W][D]  queries of prompt positions L-W .. L-1
+ *   K, V     [heads][L][D]
+ *   L, W, C  prompt length, window, budget (C includes W); rules: W >= 1,
+ *            W <= L, C > W
+ *   kernel   pooling width, odd, >= 1;  pooling  KVSEL_POOL_AVG | _MAX
+ *   indices  out [heads][C] int32; the first min(L, C) entries of each head
+ *            are written (ascending prefix picks, then L-W .. L-1)
+ *   K_out, V_out  out [heads][C][D]; the first min(L, C) rows are written
+ *   row_stats_opt out [heads][W][2] float32 (m_i, Z_i): the maximum logit of
+ *            window row i over its visible positions, and
+ *            Z_i = sum_j exp(l[i][j] - m_i); or NULL.  Not written for L < C.
+ *   votes_opt, pooled_opt  out [heads][L-W] float32 votes / pooled scores, or
+ *            NULL.  Not written for L < C.
+ *   workspace, workspace_bytes  device scratch of at least
+ *            kvsel_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+int kvsel_select(const void* Qwin, const void* K, const void* V,
+                 int L, int W, int C, int D, int heads,
+                 int kernel, int pooling, int dtype,
+                 int32_t* indices, void* K_out, void* V_out,
+                 float* row_stats_opt, float* votes_opt, float* pooled_opt,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for kvsel_select_varlen; 0 on invalid arguments. */
+size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B,
+                                    int heads, int W, int D, int dtype);
+
+/* Ragged batch of B sequences, packed without padding (the page's example is
+ * one unpadded sample; a ragged batch is B such samples side by side).
+ *   cu_L_host [B+1]  host array, cu_L[0] = 0, L_b = cu_L[b+1] - cu_L[b]
+ *   C_host    [B]    host array, budget of each sequence; cu_C is its
+ *                    exclusive prefix sum, cu_P that of P_b = L_b - W
+ *   Qwin      [B][heads][W][D]
+ *   K, V      sequence b is [heads][L_b][D] at element heads * cu_L[b] * D
+ *   indices   sequence b is [heads][C_b] at element heads * cu_C[b]
+ *   K_out, V_out  sequence b is [heads][C_b][D] at element heads * cu_C[b] * D
+ *   row_stats_opt [B][heads][W][2] or NULL
+ *   votes_opt, pooled_opt  sequence b is [heads][P_b] at heads * cu_P[b], or NULL
+ * Every sequence must satisfy the rules of kvsel_select.  Outputs of a
+ * bypassed sequence (L_b < C_b) follow kvsel_select.
+ */
+int kvsel_select_varlen(const void* Qwin, const void* K, const void* V,
+                        const int32_t* cu_L_host, const int32_t* C_host, int B,
+                        int W, int D, int heads, int kernel, int pooling, int dtype,
+                        int32_t* indices, void* K_out, void* V_out,
+                        float* row_stats_opt, float* votes_opt, float* pooled_opt,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps of the selection as separate entry points (same definitions as
+ * above), for callers that bring their own scores or indices.
+ *
+ * kvsel_topk: for each of `rows` score rows of length n (row r at
+ *   scores + r * n, float32, every value finite and >= 0), write the `count`
+ *   positions with the highest score, equal scores going to the lowest index,
+ *   in ascending order, to out + r * ld_out.  1 <= count <= n.
+ *   Workspace: kvsel_topk_workspace_bytes(rows, n) bytes.
+ *   [section "one full selection computed from Q and K": ranking and tie rule]
+ */
+size_t kvsel_topk_workspace_bytes(int rows, int n);
+int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* kvsel_pool1d: pooled[r][j] for `rows` rows of n votes (row-major), width
+ * `kernel` odd >= 1, KVSEL_POOL_AVG (zero padding, divide by kernel) or
+ * KVSEL_POOL_MAX (in-range maximum).  out may not alias votes.
+ * [section "pooling spreads a peak into a neighbourhood preference"] */
+int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling,
+                 float* pooled, void* stream);
+
+/* kvsel_gather: for each of `heads` heads, K_out[h][m] = K[h][indices[h*ld_idx+m]]
+ * and V_out[h][m] likewise, for m < count; K, V are [heads][L][D], K_out,
+ * V_out [heads][count][D].  Indices must lie in [0, L); the kernel clamps
+ * out-of-range values into that range instead of faulting.
+ * [section "one full selection computed from Q and K": K and V gathered with
+ * the same indices] */
+int kvsel_gather(const void* K, const void* V, const int32_t* indices, int ld_idx,
+                 int heads, int L, int count, int D, int dtype,
+                 void* K_out, void* V_out, void* stream);
+
+/* Per-kernel timing for benchmarks (not part of the selection itself).
+ * kvsel_profile_enable(1) clears the record and, until kvsel_profile_enable(0),
+ * brackets every kernel this library launches with two HIP events recorded on
+ * the launch stream.  kvsel_profile_read() waits for the recorded events,
+ * fills up to max_entries records (one per kernel name: launches and summed
+ * elapsed milliseconds) and returns how many kernel names were seen, or a
+ * negative kvsel_status.  Host memory only; not for use under graph capture. */
+typedef struct {
+  char name[32];
+  int launches;
+  double total_ms;
+} kvsel_kernel_time;
+
+int kvsel_profile_enable(int on);
+int kvsel_profile_read(kvsel_kernel_time* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

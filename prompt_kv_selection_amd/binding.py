@@ -1,0 +1,193 @@
+"""ctypes binding of libkvsel.so (C ABI in include/kvsel.h).
+
+Functions carry the C names and take PyTorch tensors; they only marshal
+pointers, sizes and the current HIP stream.  Every step of the selection runs
+in the library's HIP kernels: there is no other implementation behind these
+calls, and importing this module raises if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+
+KVSEL_OK = 0
+KVSEL_EINVAL = -1
+KVSEL_EUNSUPPORTED = -2
+KVSEL_EWORKSPACE = -3
+KVSEL_EDEVICE = -4
+POOL = {"avg": 0, "max": 1}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m prompt_kv_selection_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+lib.kvsel_version.restype = _i
+lib.kvsel_version.argtypes = []
+lib.kvsel_last_error.restype = ctypes.c_char_p
+lib.kvsel_last_error.argtypes = []
+lib.kvsel_workspace_bytes.restype = _sz
+lib.kvsel_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+lib.kvsel_varlen_workspace_bytes.restype = _sz
+lib.kvsel_varlen_workspace_bytes.argtypes = [_i32p, _i32p, _i, _i, _i, _i, _i]
+lib.kvsel_select.restype = _i
+lib.kvsel_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_select_varlen.restype = _i
+lib.kvsel_select_varlen.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i, _i, _i, _i, _i, _i, _i,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_topk_workspace_bytes.restype = _sz
+lib.kvsel_topk_workspace_bytes.argtypes = [_i, _i]
+lib.kvsel_topk.restype = _i
+lib.kvsel_topk.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _sz, _vp]
+lib.kvsel_pool1d.restype = _i
+lib.kvsel_pool1d.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
+lib.kvsel_gather.restype = _i
+lib.kvsel_gather.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+
+
+class KvselError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"kvsel error {code}: {message}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != KVSEL_OK:
+        raise KvselError(rc, kvsel_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32_array(values: Sequence[int]):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+def kvsel_version() -> int:
+    return lib.kvsel_version()
+
+
+def kvsel_last_error() -> str:
+    return lib.kvsel_last_error().decode()
+
+
+def kvsel_workspace_bytes(heads: int, L: int, W: int, C: int, D: int, dtype) -> int:
+    n = lib.kvsel_workspace_bytes(heads, L, W, C, D, DTYPE.get(dtype, dtype))
+    if n == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return n
+
+
+def kvsel_varlen_workspace_bytes(cu_L: Sequence[int], C: Sequence[int], heads: int, W: int, D: int, dtype) -> int:
+    B = len(C)
+    n = lib.kvsel_varlen_workspace_bytes(_i32_array(cu_L), _i32_array(C), B, heads, W, D, DTYPE.get(dtype, dtype))
+    if n == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return n
+
+
+def kvsel_select(Qwin, K, V, L, W, C, D, heads, kernel, pooling, dtype, indices, K_out, V_out,
+                 row_stats=None, votes=None, pooled=None, workspace=None, workspace_bytes=None,
+                 stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_select(_ptr(Qwin), _ptr(K), _ptr(V), L, W, C, D, heads, kernel,
+                            POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
+                            _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(row_stats), _ptr(votes),
+                            _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_select_varlen(Qwin, K, V, cu_L, C, W, D, heads, kernel, pooling, dtype, indices, K_out, V_out,
+                        row_stats=None, votes=None, pooled=None, workspace=None, workspace_bytes=None,
+                        stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_select_varlen(_ptr(Qwin), _ptr(K), _ptr(V), _i32_array(cu_L), _i32_array(C), len(C),
+                                   W, D, heads, kernel, POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
+                                   _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(row_stats), _ptr(votes),
+                                   _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_topk(scores, rows, n, count, out, ld_out, workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(lib.kvsel_topk(_ptr(scores), rows, n, count, _ptr(out), ld_out, _ptr(workspace), workspace_bytes,
+                          _stream(stream)))
+
+
+def kvsel_pool1d(votes, rows, n, kernel, pooling, pooled, stream=None) -> None:
+    _check(lib.kvsel_pool1d(_ptr(votes), rows, n, kernel, POOL.get(pooling, pooling), _ptr(pooled),
+                            _stream(stream)))
+
+
+def kvsel_gather(K, V, indices, ld_idx, heads, L, count, D, dtype, K_out, V_out, stream=None) -> None:
+    _check(lib.kvsel_gather(_ptr(K), _ptr(V), _ptr(indices), ld_idx, heads, L, count, D,
+                            DTYPE.get(dtype, dtype), _ptr(K_out), _ptr(V_out), _stream(stream)))
+
+
+# ------------------------------------------------------------ conveniences
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def select(Qwin: torch.Tensor, K: torch.Tensor, V: torch.Tensor, C: int, kernel: int = 5,
+           pooling: str = "avg", with_scores: bool = False, workspace: Optional[torch.Tensor] = None,
+           stream=None):
+    """Allocate outputs and run kvsel_select on Qwin [H, W, D], K, V [H, L, D].
+    Returns (indices [H, C], K_out [H, C, D], V_out [H, C, D]) plus
+    (row_stats [H, W, 2], votes [H, P], pooled [H, P]) if with_scores."""
+    H, L, D = K.shape
+    W = Qwin.shape[1]
+    dev = K.device
+    ws = workspace if workspace is not None else _workspace(kvsel_workspace_bytes(H, L, W, C, D, K.dtype), dev)
+    idx = torch.empty((H, C), dtype=torch.int32, device=dev)
+    Ko = torch.empty((H, C, D), dtype=K.dtype, device=dev)
+    Vo = torch.empty((H, C, D), dtype=V.dtype, device=dev)
+    rs = vt = pl = None
+    if with_scores:
+        rs = torch.empty((H, W, 2), dtype=torch.float32, device=dev)
+        vt = torch.empty((H, max(L - W, 0)), dtype=torch.float32, device=dev)
+        pl = torch.empty((H, max(L - W, 0)), dtype=torch.float32, device=dev)
+    kvsel_select(Qwin, K, V, L, W, C, D, H, kernel, pooling, K.dtype, idx, Ko, Vo, rs, vt, pl, ws,
+                 stream=stream)
+    return (idx, Ko, Vo, rs, vt, pl) if with_scores else (idx, Ko, Vo)
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+lib.kvsel_profile_enable.restype = _i
+lib.kvsel_profile_enable.argtypes = [_i]
+lib.kvsel_profile_read.restype = _i
+lib.kvsel_profile_read.argtypes = [ctypes.POINTER(_KernelTime), _i]
+
+
+def kvsel_profile_enable(on: bool) -> None:
+    _check(lib.kvsel_profile_enable(1 if on else 0))
+
+
+def kvsel_profile_read() -> dict:
+    """{kernel name: (launches, total milliseconds)} since profiling was enabled."""
+    buf = (_KernelTime * 64)()
+    n = lib.kvsel_profile_read(buf, 64)
+    if n < 0:
+        raise KvselError(n, kvsel_last_error())
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 64))}

@@ -1,0 +1,419 @@
+// C ABI of libkvsel: argument validation, workspace layout and the launch
+// sequence of the observation-window selection.  Declarations and the
+// contract of every entry point are in include/kvsel.h.
+//
+// Argument rules follow the worked selection on the web page "SnapKV:
+// selecting the KV cache for long prompts with an observation window"
+// (section "one full selection computed from Q and K"): positive sizes,
+// window not longer than the prompt, budget larger than the window, odd
+// pooling width, avg or max pooling.  A prompt shorter than its budget is
+// kept whole (same section, and section "prefill still reads the full K/V;
+// the compressed cache serves decode").
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kvsel.h"
+#include "kvsel_internal.h"
+
+using namespace kvsel;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return KVSEL_OK;
+}
+
+constexpr int kMaxW = 128;
+constexpr int kMaxKernel = 63;
+constexpr long long kMaxL = 1LL << 24;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_shape(int heads, int W, int D, int dtype) {
+  if (heads < 1) return fail(KVSEL_EINVAL, "heads must be >= 1 (got %d)", heads);
+  if (W < 1) return fail(KVSEL_EINVAL, "window W must be >= 1 (got %d)", W);
+  if (D < 1) return fail(KVSEL_EINVAL, "head dimension D must be >= 1 (got %d)", D);
+  if (dtype != KVSEL_F32 && dtype != KVSEL_BF16) return fail(KVSEL_EINVAL, "unknown dtype %d", dtype);
+  return KVSEL_OK;
+}
+
+// Limits of these kernels (valid for the method, not covered here).
+int check_support(int W, int D) {
+  if (D != 64 && D != 128) return fail(KVSEL_EUNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+  if (W > kMaxW) return fail(KVSEL_EUNSUPPORTED, "window %d exceeds the supported maximum %d", W, kMaxW);
+  return KVSEL_OK;
+}
+
+int check_pool(int kernel, int pooling) {
+  if (kernel < 1 || kernel % 2 != 1) return fail(KVSEL_EINVAL, "pooling width must be odd and >= 1 (got %d)", kernel);
+  if (pooling != KVSEL_POOL_AVG && pooling != KVSEL_POOL_MAX)
+    return fail(KVSEL_EINVAL, "pooling must be KVSEL_POOL_AVG or KVSEL_POOL_MAX (got %d)", pooling);
+  if (kernel > kMaxKernel) return fail(KVSEL_EUNSUPPORTED, "pooling width %d exceeds %d", kernel, kMaxKernel);
+  return KVSEL_OK;
+}
+
+// Per-sequence layout of a (possibly ragged) batch.
+struct Plan {
+  int B = 0, heads = 0, W = 0, D = 0, dtype = 0;
+  std::vector<int> L, C, nch;
+  std::vector<long long> cuL, cuC, cuP, part;  // exclusive prefix sums
+  long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots
+  long long vote_elems = 0;   // heads * sum of P_b
+  size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, bytes = 0;
+};
+
+int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p) {
+  if (cu_L == nullptr || C_host == nullptr) return fail(KVSEL_EINVAL, "cu_L_host and C_host must not be NULL");
+  if (B < 1) return fail(KVSEL_EINVAL, "batch B must be >= 1 (got %d)", B);
+  int rc = check_shape(heads, W, D, dtype);
+  if (rc) return rc;
+  if (cu_L[0] != 0) return fail(KVSEL_EINVAL, "cu_L[0] must be 0 (got %d)", cu_L[0]);
+  p.B = B;
+  p.heads = heads;
+  p.W = W;
+  p.D = D;
+  p.dtype = dtype;
+  p.L.resize(B);
+  p.C.resize(B);
+  p.nch.resize(B);
+  p.cuL.assign(B + 1, 0);
+  p.cuC.assign(B + 1, 0);
+  p.cuP.assign(B + 1, 0);
+  p.part.assign(B + 1, 0);
+  for (int b = 0; b < B; ++b) {
+    const long long L = (long long)cu_L[b + 1] - cu_L[b];
+    const int C = C_host[b];
+    if (L < 1) return fail(KVSEL_EINVAL, "sequence %d: prompt length must be >= 1 (got %lld)", b, L);
+    if (L > kMaxL) return fail(KVSEL_EUNSUPPORTED, "sequence %d: prompt length %lld exceeds %lld", b, L, kMaxL);
+    if (W > L) return fail(KVSEL_EINVAL, "sequence %d: window %d exceeds prompt length %lld", b, W, L);
+    if (C <= W) return fail(KVSEL_EINVAL, "sequence %d: budget %d must exceed the window %d", b, C, W);
+    p.L[b] = (int)L;
+    p.C[b] = C;
+    p.nch[b] = L < C ? 0 : (int)((L + kChunk - 1) / kChunk);
+    p.cuL[b + 1] = p.cuL[b] + L;
+    p.cuC[b + 1] = p.cuC[b] + C;
+    p.cuP[b + 1] = p.cuP[b] + (L - W);
+    p.part[b + 1] = p.part[b] + (long long)heads * p.nch[b];
+  }
+  if ((rc = check_support(W, D))) return rc;
+  p.part_slots = p.part[B];
+  p.vote_elems = (long long)heads * p.cuP[B];
+  size_t off = 0;
+  p.off_pm = off;
+  off = align256(off + (size_t)p.part_slots * W * sizeof(float));
+  p.off_pz = off;
+  off = align256(off + (size_t)p.part_slots * W * sizeof(float));
+  p.off_votes = off;
+  off = align256(off + (size_t)p.vote_elems * sizeof(float));
+  p.off_pooled = off;
+  off = align256(off + (size_t)p.vote_elems * sizeof(float));
+  p.bytes = std::max<size_t>(off, 256);
+  return KVSEL_OK;
+}
+
+Launch base_launch(const Plan& p, int kernel, int pooling) {
+  Launch a{};
+  a.heads = p.heads;
+  a.W = p.W;
+  a.D = p.D;
+  a.kernel = kernel;
+  a.pooling = pooling;
+  a.window = 1;
+  a.scale2 = (float)(1.4426950408889634074 / sqrt((double)p.D));
+  return a;
+}
+
+int device_error(hipError_t e, const char* what) {
+  return fail(KVSEL_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Optional event timing of every launch (kvsel_profile_enable).
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<TimedLaunch> g_prof;
+
+template <typename F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return launch();
+  TimedLaunch t{name, nullptr, nullptr};
+  hipError_t e;
+  if ((e = hipEventCreate(&t.start)) != hipSuccess) return e;
+  if ((e = hipEventCreate(&t.stop)) != hipSuccess) return e;
+  if ((e = hipEventRecord(t.start, st)) != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  if ((e = hipEventRecord(t.stop, st)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(t);
+  return hipSuccess;
+}
+
+void drop_profile_events() {
+  for (auto& t : g_prof) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_prof.clear();
+}
+
+int run_select(const void* Q, const void* K, const void* V, const Plan& p, int kernel, int pooling,
+               int32_t* indices, void* K_out, void* V_out, float* row_stats, float* votes_opt,
+               float* pooled_opt, void* workspace, hipStream_t st) {
+  char* ws = (char*)workspace;
+  float* pm = (float*)(ws + p.off_pm);
+  float* pz = (float*)(ws + p.off_pz);
+  float* votes = votes_opt ? votes_opt : (float*)(ws + p.off_votes);
+  float* pooled = pooled_opt ? pooled_opt : (float*)(ws + p.off_pooled);
+  const int rpb = gather_rows_per_block(p.D, p.dtype);
+
+  for (int b0 = 0; b0 < p.B; b0 += kMaxSegs) {
+    const int nb = std::min(kMaxSegs, p.B - b0);
+    Launch a = base_launch(p, kernel, pooling);
+    a.n = nb;
+    int items = 0, rows = 0, gitems = 0, maxP = 0;
+    for (int k = 0; k < nb; ++k) {
+      const int b = b0 + k;
+      Seg& s = a.seg[k];
+      s.b = b;
+      s.L = p.L[b];
+      s.C = p.C[b];
+      s.nout = std::min(s.L, s.C);
+      s.h0 = 0;
+      s.nh = p.heads;
+      s.nch = p.nch[b];
+      s.item0 = items;
+      s.row0 = rows;
+      s.gitem0 = gitems;
+      s.gblk = (s.nout + rpb - 1) / rpb;
+      s.idx_ld = s.C;
+      s.out_ld = s.C;
+      s.vote_ld = s.L - p.W;
+      s.kv_off = (long long)p.heads * p.cuL[b] * p.D;
+      s.idx_off = (long long)p.heads * p.cuC[b];
+      s.out_off = s.idx_off;
+      s.vote_off = (long long)p.heads * p.cuP[b];
+      s.part_base = p.part[b];
+      items += s.nh * s.nch;
+      rows += s.nh;
+      gitems += s.nh * s.gblk;
+      if (s.L >= s.C) maxP = std::max(maxP, s.L - p.W);
+    }
+    hipError_t e;
+    if (items > 0) {
+      e = timed("window_stats", st, [&] { return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, st); });
+      if (e != hipSuccess) return device_error(e, "window_stats launch");
+      e = timed("window_votes", st,
+                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
+      if (e != hipSuccess) return device_error(e, "window_votes launch");
+      e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, st); });
+      if (e != hipSuccess) return device_error(e, "pool launch");
+    }
+    e = timed("topk", st, [&] { return launch_topk(a, rows, pooled, indices, st); });
+    if (e != hipSuccess) return device_error(e, "topk launch");
+    e = timed("gather", st, [&] { return launch_gather(a, gitems, p.dtype, K, V, indices, K_out, V_out, st); });
+    if (e != hipSuccess) return device_error(e, "gather launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvsel_version(void) { return (0 << 16) | 1; }
+
+const char* kvsel_last_error(void) { return g_error.c_str(); }
+
+size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B, int heads, int W,
+                                    int D, int dtype) {
+  Plan p;
+  if (make_plan(cu_L_host, C_host, B, heads, W, D, dtype, p) != KVSEL_OK) return 0;
+  ok();
+  return p.bytes;
+}
+
+size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype) {
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  return kvsel_varlen_workspace_bytes(cu, c, 1, heads, W, D, dtype);
+}
+
+int kvsel_select_varlen(const void* Qwin, const void* K, const void* V, const int32_t* cu_L_host,
+                        const int32_t* C_host, int B, int W, int D, int heads, int kernel, int pooling, int dtype,
+                        int32_t* indices, void* K_out, void* V_out, float* row_stats_opt, float* votes_opt,
+                        float* pooled_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(cu_L_host, C_host, B, heads, W, D, dtype, p);
+  if (rc) return rc;
+  if ((rc = check_pool(kernel, pooling))) return rc;
+  if (!Qwin || !K || !V || !indices || !K_out || !V_out)
+    return fail(KVSEL_EINVAL, "Qwin, K, V, indices, K_out and V_out must not be NULL");
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.bytes)
+    return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, p.bytes);
+  const size_t esz = dtype == KVSEL_BF16 ? 2 : 4;
+  if ((uintptr_t)Qwin % 16 || (uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)K_out % 16 ||
+      (uintptr_t)V_out % 16)
+    return fail(KVSEL_EINVAL, "Qwin, K, V, K_out and V_out must be 16-byte aligned");
+  (void)esz;
+  return run_select(Qwin, K, V, p, kernel, pooling, indices, K_out, V_out, row_stats_opt, votes_opt, pooled_opt,
+                    workspace, (hipStream_t)stream);
+}
+
+int kvsel_select(const void* Qwin, const void* K, const void* V, int L, int W, int C, int D, int heads, int kernel,
+                 int pooling, int dtype, int32_t* indices, void* K_out, void* V_out, float* row_stats_opt,
+                 float* votes_opt, float* pooled_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  return kvsel_select_varlen(Qwin, K, V, cu, c, 1, W, D, heads, kernel, pooling, dtype, indices, K_out, V_out,
+                             row_stats_opt, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
+}
+
+size_t kvsel_topk_workspace_bytes(int rows, int n) {
+  (void)rows;
+  (void)n;
+  ok();
+  return 0;
+}
+
+int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!scores || !out) return fail(KVSEL_EINVAL, "scores and out must not be NULL");
+  if (rows < 1 || n < 1) return fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
+  if (count < 1 || count > n) return fail(KVSEL_EINVAL, "count must be in [1, n] (got %d, n = %d)", count, n);
+  if (ld_out < count) return fail(KVSEL_EINVAL, "ld_out %d is smaller than count %d", ld_out, count);
+  Launch a{};
+  a.n = 1;
+  a.heads = rows;
+  a.window = 0;
+  Seg& s = a.seg[0];
+  s.L = n;
+  s.C = count;
+  s.nout = count;
+  s.nh = rows;
+  s.idx_ld = ld_out;
+  s.vote_ld = n;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed("topk", st, [&] { return launch_topk(a, rows, scores, out, st); });
+  if (e != hipSuccess) return device_error(e, "topk launch");
+  return ok();
+}
+
+int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling, float* pooled, void* stream) {
+  if (!votes || !pooled) return fail(KVSEL_EINVAL, "votes and pooled must not be NULL");
+  if (votes == pooled) return fail(KVSEL_EINVAL, "pooled must not alias votes");
+  if (rows < 1 || n < 1) return fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
+  int rc = check_pool(kernel, pooling);
+  if (rc) return rc;
+  Launch a{};
+  a.n = 1;
+  a.heads = rows;
+  a.kernel = kernel;
+  a.pooling = pooling;
+  a.window = 0;
+  Seg& s = a.seg[0];
+  s.L = n;
+  s.C = n;
+  s.nh = rows;
+  s.vote_ld = n;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed("pool", st, [&] { return launch_pool(a, rows, n, votes, pooled, st); });
+  if (e != hipSuccess) return device_error(e, "pool launch");
+  return ok();
+}
+
+int kvsel_gather(const void* K, const void* V, const int32_t* indices, int ld_idx, int heads, int L, int count,
+                 int D, int dtype, void* K_out, void* V_out, void* stream) {
+  if (!K || !V || !indices || !K_out || !V_out) return fail(KVSEL_EINVAL, "pointers must not be NULL");
+  if (heads < 1 || L < 1 || count < 1)
+    return fail(KVSEL_EINVAL, "heads, L and count must be >= 1 (got %d, %d, %d)", heads, L, count);
+  if (ld_idx < count) return fail(KVSEL_EINVAL, "ld_idx %d is smaller than count %d", ld_idx, count);
+  if (dtype != KVSEL_F32 && dtype != KVSEL_BF16) return fail(KVSEL_EINVAL, "unknown dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(KVSEL_EUNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+  if ((uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)K_out % 16 || (uintptr_t)V_out % 16)
+    return fail(KVSEL_EINVAL, "K, V, K_out and V_out must be 16-byte aligned");
+  const int rpb = gather_rows_per_block(D, dtype);
+  Launch a{};
+  a.n = 1;
+  a.heads = heads;
+  a.D = D;
+  a.window = 0;
+  Seg& s = a.seg[0];
+  s.L = L;
+  s.C = count;
+  s.nout = count;
+  s.nh = heads;
+  s.gblk = (count + rpb - 1) / rpb;
+  s.idx_ld = ld_idx;
+  s.out_ld = count;
+  const long long items = (long long)heads * s.gblk;
+  if (items > 0x7FFFFFFFLL) return fail(KVSEL_EUNSUPPORTED, "gather grid too large");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed("gather", st, [&] { return launch_gather(a, (int)items, dtype, K, V, indices, K_out, V_out, st); });
+  if (e != hipSuccess) return device_error(e, "gather launch");
+  return ok();
+}
+
+int kvsel_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) drop_profile_events();
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int kvsel_profile_read(kvsel_kernel_time* out, int max_entries) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<kvsel_kernel_time> acc;
+  for (auto& t : g_prof) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return device_error(e, "profile event");
+    auto it = std::find_if(acc.begin(), acc.end(), [&](const kvsel_kernel_time& k) { return strcmp(k.name, t.name) == 0; });
+    if (it == acc.end()) {
+      kvsel_kernel_time k{};
+      snprintf(k.name, sizeof k.name, "%s", t.name);
+      acc.push_back(k);
+      it = acc.end() - 1;
+    }
+    it->launches += 1;
+    it->total_ms += ms;
+  }
+  for (int i = 0; i < (int)acc.size() && i < max_entries && out; ++i) out[i] = acc[i];
+  ok();
+  return (int)acc.size();
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations shared by the HIP sources of libkvsel.
+//
+// Work is described by a small table of segments passed to every kernel by
+// value.  A segment is one sequence b (prompt length L, budget C) restricted
+// to a contiguous range of heads [h0, h0 + nh).  Heads, layers and sequences
+// are independent units of the selection, so any partition into segments
+// gives the same results.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+constexpr int kMaxSegs = 16;       // segments per launch
+constexpr int kWaves = 4;          // waves per scoring workgroup
+constexpr int kWaveTiles = 8;      // 32-position tiles per wave
+constexpr int kChunk = kWaves * kWaveTiles * 32;  // positions per scoring workgroup
+constexpr int kTopkThreads = 1024;
+constexpr int kPoolBlock = 256;
+
+struct Seg {
+  int b;          // sequence index (Q and row-stat offsets)
+  int L;          // prompt length
+  int C;          // budget (includes the window); L < C means bypass
+  int nout;       // rows to emit per head: min(L, C), or the gather count
+  int h0, nh;     // head range
+  int nch;        // scoring chunks per head, ceil(L / kChunk)
+  int item0;      // first scoring workgroup of this segment in the launch
+  int row0;       // first (segment, head) row of this segment in the launch
+  int gitem0;     // first gather workgroup of this segment in the launch
+  int gblk;       // gather workgroups per head
+  int idx_ld;     // indices between heads
+  int out_ld;     // K_out / V_out rows between heads
+  int vote_ld;    // votes / pooled floats between heads
+  long long kv_off;    // element offset of (b, head 0, row 0) in K and V
+  long long idx_off;   // element offset of (b, head 0) in indices
+  long long out_off;   // row offset of (b, head 0) in K_out / V_out
+  long long vote_off;  // element offset of (b, head 0) in votes / pooled
+  long long part_base; // partial-stat slot of (b, head 0, chunk 0)
+};
+
+struct Launch {
+  int n;          // segments in use
+  int heads;      // heads per sequence (stride of Qwin and row stats)
+  int W, D;
+  int kernel, pooling;
+  int window;     // 1: append the window positions after the picks
+  float scale2;   // log2(e) / sqrt(D)
+  Seg seg[kMaxSegs];
+};
+
+// Segment holding `item` given the per-segment start field (sorted ascending).
+template <int Field>
+__device__ __forceinline__ int find_seg(const Launch& a, int item) {
+  int e = 0;
+  for (int k = 1; k < a.n; ++k) {
+    const int start = Field == 0 ? a.seg[k].item0 : Field == 1 ? a.seg[k].row0 : a.seg[k].gitem0;
+    if (item >= start) e = k;
+  }
+  return e;
+}
+
+enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
+
+// Host-side launchers (return hipSuccess or the launch error).
+hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
+                               float* part_m, float* part_z, hipStream_t st);
+hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
+                               const float* part_m, const float* part_z, float* votes,
+                               float* row_stats, hipStream_t st);
+hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
+                       hipStream_t st);
+hipError_t launch_topk(const Launch& a, int rows, const float* scores, int32_t* indices,
+                       hipStream_t st);
+int gather_rows_per_block(int D, int dtype);
+hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
+                         const int32_t* indices, void* K_out, void* V_out, hipStream_t st);
+
+}  // namespace kvsel

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI, no GPU needed: the library loads, exports
+every function include/kvsel.h declares, sizes workspaces, and rejects invalid
+arguments before anything is enqueued (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from prompt_kv_selection_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(B):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(B.lib, name), name
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for name in names:
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_error_string(B):
+    assert B.kvsel_version() >= 1
+    assert isinstance(B.kvsel_last_error(), str)
+
+
+def test_workspace_sizes(B):
+    n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
+    # partial stats (32 heads x 32 chunks x 32 rows x 2) + votes + pooled
+    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4
+    assert expect_min <= n <= expect_min + 4 * 256
+    assert n % 256 == 0
+    assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W
+    assert "budget" in B.kvsel_last_error()
+    cu = (ctypes.c_int32 * 3)(0, 5000, 12000)
+    cs = (ctypes.c_int32 * 2)(500, 1200)
+    assert B.lib.kvsel_varlen_workspace_bytes(cu, cs, 2, 8, 32, 128, 1) > 0
+    # bypassed sequences need no partial stats, still own their vote slots
+    cs2 = (ctypes.c_int32 * 2)(6000, 1200)
+    assert B.lib.kvsel_varlen_workspace_bytes(cu, cs2, 2, 8, 32, 128, 1) < \
+        B.lib.kvsel_varlen_workspace_bytes(cu, cs, 2, 8, 32, 128, 1)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every case below fails validation
+
+
+def call_select(B, **kw):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, L=1024, W=32, C=256, D=128, heads=4, kernel=5, pooling=0, dtype=1,
+                idx=FAKE, Ko=FAKE, Vo=FAKE, ws=FAKE, wsb=1 << 30)
+    args.update(kw)
+    return B.lib.kvsel_select(args["Q"], args["K"], args["V"], args["L"], args["W"], args["C"], args["D"],
+                              args["heads"], args["kernel"], args["pooling"], args["dtype"], args["idx"],
+                              args["Ko"], args["Vo"], None, None, None, args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=0), -1), (dict(W=1025), -1), (dict(C=32), -1), (dict(C=10), -1),
+    (dict(kernel=4), -1), (dict(kernel=0), -1), (dict(kernel=-3), -1), (dict(pooling=2), -1),
+    (dict(dtype=7), -1), (dict(heads=0), -1), (dict(L=0), -1), (dict(D=0), -1),
+    (dict(D=96), -2), (dict(W=129, L=4096, C=512), -2), (dict(kernel=65), -2),
+    (dict(Q=None), -1), (dict(K=None), -1), (dict(Vo=None), -1), (dict(idx=None), -1),
+    (dict(ws=None), -1), (dict(wsb=1024), -3), (dict(ws=ctypes.c_void_p(0x10010)), -1),
+    (dict(K=ctypes.c_void_p(0x10008)), -1),
+])
+def test_select_argument_errors(B, kw, code):
+    assert call_select(B, **kw) == code
+    assert B.kvsel_last_error() != ""
+
+
+def test_varlen_argument_errors(B):
+    lib = B.lib
+    cu_bad = (ctypes.c_int32 * 3)(0, 5000, 4000)  # negative length
+    cs = (ctypes.c_int32 * 2)(500, 400)
+    rc = lib.kvsel_select_varlen(FAKE, FAKE, FAKE, cu_bad, cs, 2, 32, 128, 8, 5, 0, 1, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None)
+    assert rc == -1 and "sequence 1" in B.kvsel_last_error()
+    cu = (ctypes.c_int32 * 3)(1, 5000, 9000)
+    rc = lib.kvsel_select_varlen(FAKE, FAKE, FAKE, cu, cs, 2, 32, 128, 8, 5, 0, 1, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None)
+    assert rc == -1
+    rc = lib.kvsel_select_varlen(FAKE, FAKE, FAKE, None, cs, 2, 32, 128, 8, 5, 0, 1, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None)
+    assert rc == -1
+    cu = (ctypes.c_int32 * 3)(0, 20, 9000)    # window longer than sequence 0
+    rc = lib.kvsel_select_varlen(FAKE, FAKE, FAKE, cu, cs, 2, 32, 128, 8, 5, 0, 1, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None)
+    assert rc == -1 and "window" in B.kvsel_last_error()
+
+
+def test_step_entry_point_errors(B):
+    lib = B.lib
+    assert lib.kvsel_topk(FAKE, 4, 100, 0, FAKE, 10, None, 0, None) == -1
+    assert lib.kvsel_topk(FAKE, 4, 100, 101, FAKE, 200, None, 0, None) == -1
+    assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 9, None, 0, None) == -1
+    assert lib.kvsel_topk(None, 4, 100, 10, FAKE, 10, None, 0, None) == -1
+    assert lib.kvsel_pool1d(FAKE, 4, 100, 2, 0, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 0, FAKE, None) == -1  # aliasing
+    assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 5, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.kvsel_gather(FAKE, FAKE, FAKE, 10, 4, 100, 20, 128, 1, FAKE, FAKE, None) == -1  # ld < count
+    assert lib.kvsel_gather(FAKE, FAKE, FAKE, 20, 4, 100, 20, 80, 1, FAKE, FAKE, None) == -2
+    assert lib.kvsel_gather(FAKE, FAKE, FAKE, 20, 4, 100, 20, 128, 3, FAKE, FAKE, None) == -1

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Tolerances are stated in tests/parity.py."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import snapkv_oracle as O
+from prompt_kv_selection_amd import workloads as WL
+
+from parity import (band_check, bits, check_gather, check_head, close, gpu_internal_topk, log, run_select,
+                    to_device)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from prompt_kv_selection_amd import binding
+    return binding
+
+
+def embed_weights(rows, placeholder, L, D):
+    """The pages' construction embedded at head dimension D in fp32:
+    q_i = sqrt(D) e_i and k_j[i] = ln w_i[j], other coordinates zero."""
+    W = len(rows)
+    K = np.zeros((L, D), dtype=np.float32)
+    for i, row in enumerate(rows):
+        for j, w in enumerate(row):
+            K[j, i] = math.log(placeholder if w is None else w)
+    Q = np.zeros((W, D), dtype=np.float32)
+    for i in range(W):
+        Q[i, i] = math.sqrt(D)
+    return Q, K
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_worked_example(B, D):
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    rows = [g["exp_weight_rows"]["query_6"], g["exp_weight_rows"]["query_7"]]
+    Q, K = embed_weights(rows, g["masked_placeholder"], g["L"], D)
+    V = np.zeros((g["L"], D), dtype=np.float32)
+    V[:, 0] = np.arange(g["L"])
+    V[:, 1] = -np.arange(g["L"])
+    log(f"worked example D={D}")
+    Qd, Kd, Vd = (to_device(x[None], "f32") for x in (Q, K, V))
+    out = run_select(Qd, Kd, Vd, g["L"], g["W"], g["C"], g["kernel"], g["pooling"], "f32")
+    assert out["idx"][0].tolist() == g["expected_indices"]
+    assert out["Vo"][0, :, :2].cpu().tolist() == g["expected_values"]
+    np.testing.assert_allclose(out["votes"][0], np.array([51, 77, 460, 508, 51, 51]) / 650, rtol=1e-5)
+    np.testing.assert_allclose(out["pooled"][0], np.array([128, 588, 1045, 1019, 610, 102]) / 1950, rtol=1e-5)
+    zs = out["rs"][0, :, 1] * np.exp(out["rs"][0, :, 0])
+    np.testing.assert_allclose(zs, [25, 26], rtol=1e-5)
+    # max-3 with C = 4: three-way exact tie, lowest indices
+    out = run_select(Qd, Kd, Vd, g["L"], 2, 4, 3, "max", "f32")
+    assert out["idx"][0].tolist() == [2, 3, 6, 7]
+    check_gather(out, Kd, Vd, 4, g["L"])
+
+
+def test_counterexample(B):
+    g = json.load(open(os.path.join(GOLDEN, "counterexample.json")))
+    rows = [g["exp_weight_rows"]["query_2"], g["exp_weight_rows"]["query_3"]]
+    Q, K = embed_weights(rows, g["masked_placeholder"], g["L"], 64)
+    V = np.random.default_rng(0).standard_normal((g["L"], 64)).astype(np.float32)
+    Qd, Kd, Vd = (to_device(x[None], "f32") for x in (Q, K, V))
+    log("counterexample")
+    out = run_select(Qd, Kd, Vd, g["L"], 2, 3, 1, "avg", "f32")
+    p = g["printed"]["full_softmax"]
+    np.testing.assert_allclose(out["votes"][0], [p["A_vote"], p["B_vote"]], rtol=1e-5)
+    assert out["idx"][0].tolist() == [g["positions"]["B"], 2, 3]
+    out = run_select(Qd, Kd, Vd, g["L"], 2, 3, 3, "avg", "f32")
+    assert out["pooled"][0][0] == out["pooled"][0][1]  # exact tie on the GPU too
+    assert out["idx"][0].tolist() == [g["positions"]["A"], 2, 3]
+
+
+CASES = [
+    # dtype, D, H, L, W, C, kernel, pooling
+    ("bf16", 128, 3, 4096, 32, 512, 5, "avg"),
+    ("bf16", 128, 2, 3001, 32, 700, 5, "max"),     # ragged tile and chunk tails
+    ("bf16", 128, 2, 1057, 7, 100, 3, "avg"),      # W not a multiple of 32
+    ("bf16", 128, 2, 2500, 64, 300, 7, "avg"),
+    ("bf16", 128, 1, 3000, 100, 900, 9, "max"),
+    ("bf16", 128, 1, 2100, 128, 1000, 1, "avg"),
+    ("bf16", 64, 2, 2049, 33, 200, 3, "avg"),
+    ("bf16", 64, 2, 5000, 1, 2, 5, "avg"),         # W = 1, a single pick
+    ("f32", 64, 2, 1024, 32, 256, 3, "avg"),
+    ("f32", 128, 2, 1500, 40, 1500, 5, "max"),     # L == C: the whole prefix
+    ("f32", 128, 1, 777, 16, 17, 15, "avg"),       # C = W + 1
+    ("bf16", 128, 2, 300, 32, 1024, 5, "avg"),     # bypass L < C
+    ("bf16", 128, 2, 32, 32, 64, 5, "avg"),        # W == L, bypass
+    ("bf16", 128, 1, 40, 8, 33, 21, "avg"),        # wide kernel, tiny prompt
+    ("bf16", 128, 1, 1025, 32, 600, 63, "avg"),    # widest supported kernel
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[1]}-H{c[2]}-L{c[3]}-W{c[4]}-C{c[5]}-k{c[6]}{c[7]}"
+                                             for c in CASES])
+def test_random_cases(B, case):
+    dtype, D, H, L, W, C, kernel, pooling = case
+    w = WL.Workload("case", seed=L * 7 + W, heads=H, L=L, W=W, C=C, D=D, dtype=dtype, kernel=kernel,
+                    pooling=pooling, keys="spike", spike_frac=0.02 if L - W >= 50 else 0.0)
+    Q, K, V = WL.layer_arrays(w)
+    log(f"random case {case}")
+    Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
+    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype)
+    for h in range(H):
+        ref = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h], dtype),
+                              WL.to_float64(V[h], dtype), W, C, kernel, pooling)
+        check_head(out, h, ref, L, W, C, f"{case} head {h}")
+    check_gather(out, Kd, Vd, C, L)
+
+
+def test_identical_keys_give_identical_scores(B):
+    w = WL.reduced(WL.get("tied_h64_l128k"), L=8192, heads=2)
+    Q, K, V = WL.layer_arrays(w)
+    log("identical keys")
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
+    P = w.L - w.W
+    for h in range(2):
+        rows, inv = np.unique(K[h, :P], axis=0, return_inverse=True)
+        inv = inv.ravel()
+        for c in range(len(rows)):
+            v = out["votes"][h][inv == c]
+            assert np.all(v == v[0]), f"head {h} code {c}: GPU votes of equal keys differ"
+        ref = O.snapkv_select(WL.to_float64(Q[h], "bf16"), WL.to_float64(K[h], "bf16"),
+                              WL.to_float64(V[h], "bf16"), w.W, w.C, w.kernel, w.pooling)
+        check_head(out, h, ref, w.L, w.W, w.C, f"tied head {h}")
+
+
+def test_deterministic(B):
+    w = WL.reduced(WL.get("lognorm_h32_l16k"), L=6000, heads=4)
+    Q, K, V = WL.layer_arrays(w)
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    log("determinism")
+    a = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
+    b = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
+    assert torch.equal(a["idx"], b["idx"])
+    np.testing.assert_array_equal(a["votes"].view(np.int32), b["votes"].view(np.int32))
+    np.testing.assert_array_equal(a["pooled"].view(np.int32), b["pooled"].view(np.int32))
+    assert torch.equal(bits(a["Ko"]), bits(b["Ko"]))
+
+
+# ----------------------------------------------------------------- steps
+
+@pytest.mark.parametrize("rows,n,count", [(1, 1, 1), (3, 1000, 17), (4, 32736, 992), (2, 131008, 4032),
+                                          (5, 70001, 70001), (2, 9000, 1)])
+def test_topk_step_exact(B, rows, n, count):
+    """Top-k on given fp32 scores: exactly the oracle's ranking of the same
+    values, lowest index first on ties (many exact ties here)."""
+    rng = np.random.default_rng(n + count)
+    s = (rng.integers(0, 50, size=(rows, n)) * 0.125).astype(np.float32)
+    s[:, ::7] = rng.random((rows, len(range(0, n, 7)))).astype(np.float32)
+    if rows > 1:
+        s[1] = 0.0  # a row of all-equal zeros
+    sd = torch.from_numpy(s).cuda()
+    ld = count + 3
+    out = torch.full((rows, ld), -1, dtype=torch.int32, device="cuda")
+    log(f"topk rows={rows} n={n} count={count}")
+    B.kvsel_topk(sd, rows, n, count, out, ld)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r, :count], O.top_prefix(s[r].astype(np.float64), count))
+        assert np.all(got[r, count:] == -1)
+
+
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9, 11, 13, 31])
+@pytest.mark.parametrize("pooling", ["avg", "max"])
+def test_pool_step(B, kernel, pooling):
+    rng = np.random.default_rng(kernel)
+    rows, n = 3, 5003
+    v = (rng.random((rows, n)) ** 4).astype(np.float32)
+    v[0, :100] = 0.25  # runs of equal values
+    vd = torch.from_numpy(v).cuda()
+    pd = torch.empty_like(vd)
+    B.kvsel_pool1d(vd, rows, n, kernel, pooling, pd)
+    torch.cuda.synchronize()
+    got = pd.cpu().numpy()
+    for r in range(rows):
+        ref = O.pool1d(v[r].astype(np.float64), kernel, pooling)
+        if pooling == "max":
+            np.testing.assert_array_equal(got[r], ref.astype(np.float32))
+        else:
+            np.testing.assert_allclose(got[r], ref, rtol=1e-6, atol=0)
+    # equal neighbour multisets give bit-equal results
+    assert np.all(got[0, kernel:100 - kernel] == got[0, kernel])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_gather_step(B, dtype, D):
+    rng = np.random.default_rng(D)
+    H, L, count = 3, 1000, 300
+    K = rng.standard_normal((H, L, D)).astype(np.float32)
+    V = rng.standard_normal((H, L, D)).astype(np.float32)
+    if dtype == "bf16":
+        K, V = WL.f32_to_bf16_bits(K), WL.f32_to_bf16_bits(V)
+    idx = rng.integers(0, L, size=(H, count + 5)).astype(np.int32)
+    Kd, Vd = to_device(K, dtype), to_device(V, dtype)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Ko = torch.zeros((H, count, D), dtype=td, device="cuda")
+    Vo = torch.zeros((H, count, D), dtype=td, device="cuda")
+    B.kvsel_gather(Kd, Vd, torch.from_numpy(idx).cuda(), count + 5, H, L, count, D, td, Ko, Vo)
+    torch.cuda.synchronize()
+    for h in range(H):
+        np.testing.assert_array_equal(bits(Ko[h]).cpu().numpy(), bits(Kd[h][idx[h, :count].tolist()]).cpu().numpy())
+        np.testing.assert_array_equal(bits(Vo[h]).cpu().numpy(), bits(Vd[h][idx[h, :count].tolist()]).cpu().numpy())
+
+
+# ----------------------------------------------------------------- ragged
+
+def test_varlen_matches_per_sequence_calls(B):
+    w = WL.reduced(WL.get("ragged_b8_h32_l4k_64k"), heads=4, batch=5, L_min=900, L_max=5000)
+    Q, K, V, Ls, Cs, cu = WL.ragged_arrays(w)
+    Ls = list(Ls)
+    Cs = list(Cs)
+    Cs[2] = Ls[2] + 5  # one bypassed sequence
+    H, W, D = w.heads, w.W, w.D
+    log(f"varlen lengths {Ls} budgets {Cs}")
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    cuC = np.concatenate([[0], np.cumsum(Cs)])
+    cuP = np.concatenate([[0], np.cumsum([L - W for L in Ls])])
+    ws = torch.empty(B.kvsel_varlen_workspace_bytes(cu.tolist(), Cs, H, W, D, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.full((H * int(cuC[-1]),), -1, dtype=torch.int32, device="cuda")
+    Ko = torch.zeros((H * int(cuC[-1]), D), dtype=torch.bfloat16, device="cuda")
+    Vo = torch.zeros_like(Ko)
+    rs = torch.zeros((len(Ls), H, W, 2), dtype=torch.float32, device="cuda")
+    vt = torch.zeros((H * int(cuP[-1]),), dtype=torch.float32, device="cuda")
+    pl = torch.zeros_like(vt)
+    B.kvsel_select_varlen(Qd, Kd, Vd, cu.tolist(), Cs, W, D, H, w.kernel, w.pooling, torch.bfloat16, idx, Ko, Vo,
+                          rs, vt, pl, ws)
+    torch.cuda.synchronize()
+    for b, (L, C) in enumerate(zip(Ls, Cs)):
+        k = Kd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D)
+        v = Vd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D)
+        single = run_select(Qd[b].contiguous(), k.contiguous(), v.contiguous(), L, W, C, w.kernel, w.pooling,
+                            "bf16")
+        n_out = min(L, C)
+        got_idx = idx[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C)[:, :n_out]
+        assert torch.equal(got_idx, single["idx"][:, :n_out]), f"sequence {b}"
+        got_k = Ko[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C, D)[:, :n_out]
+        assert torch.equal(bits(got_k), bits(single["Ko"][:, :n_out])), f"sequence {b} K_out"
+        if L >= C:
+            got_v = vt[H * int(cuP[b]): H * int(cuP[b + 1])].view(H, L - W).cpu().numpy()
+            np.testing.assert_array_equal(got_v.view(np.int32), single["votes"].view(np.int32))
+            np.testing.assert_array_equal(rs[b].cpu().numpy().view(np.int32), single["rs"].view(np.int32))
+        if b in (0, 2):
+            h = 1
+            q1, k1, v1 = WL.head_arrays(w, h, seq=b)
+            ref = O.snapkv_select(WL.to_float64(q1, "bf16"), WL.to_float64(k1, "bf16"), WL.to_float64(v1, "bf16"),
+                                  W, C, w.kernel, w.pooling)
+            check_head(single, h, ref, L, W, C, f"varlen seq {b} head {h}")
+
+
+# ----------------------------------------------------------------- full size
+
+FULL = [
+    ("fp32_h1_l1k", [0], 0),
+    ("lognorm_h32_l16k", [0, 17, 31], 0),
+    ("spike_l32x_h32_l32k", [0, 13, 31], 0),
+    ("spike_l32x_h32_l32k", [5], 31),
+    ("tied_h64_l128k", [0, 63], 0),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,heads,layer", FULL, ids=[f"{n}-layer{l}" for n, _, l in FULL])
+def test_full_size_workloads(B, name, heads, layer):
+    """Full-size workloads in the configuration the benchmark times (one call
+    per layer over all heads); the oracle checks sampled heads, every head's
+    gather is checked bit-exact and its picks against its own scores."""
+    w = WL.get(name)
+    log(f"full size {name} layer {layer}: drawing inputs")
+    Q, K, V = WL.layer_arrays(w, layer=layer)
+    Qd, Kd, Vd = to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    del K, V
+    log(f"full size {name}: GPU call H={w.heads} L={w.L}")
+    out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, w.dtype)
+    check_gather(out, Kd, Vd, w.C, w.L)
+    n = w.C - w.W
+    idx = out["idx"].cpu().numpy()
+    for h in range(w.heads):
+        gpu_internal_topk(idx[h, :n], out["pooled"][h], n, f"{name} head {h}")
+    for h in heads:
+        log(f"full size {name}: oracle head {h}")
+        q, k, v = WL.head_arrays(w, h, layer=layer)
+        ref = O.snapkv_select(WL.to_float64(q, w.dtype), WL.to_float64(k, w.dtype), WL.to_float64(v, w.dtype),
+                              w.W, w.C, w.kernel, w.pooling)
+        check_head(out, h, ref, w.L, w.W, w.C, f"{name} head {h}")
+
+
+@pytest.mark.slow
+def test_full_size_ragged(B):
+    w = WL.get("ragged_b8_h32_l4k_64k")
+    log("full size ragged: drawing inputs")
+    Q, K, V, Ls, Cs, cu = WL.ragged_arrays(w)
+    H, W, D = w.heads, w.W, w.D
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    del K, V
+    cuC = np.concatenate([[0], np.cumsum(Cs)])
+    cuP = np.concatenate([[0], np.cumsum([L - W for L in Ls])])
+    ws = torch.empty(B.kvsel_varlen_workspace_bytes(cu.tolist(), Cs, H, W, D, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    idx = torch.full((H * int(cuC[-1]),), -1, dtype=torch.int32, device="cuda")
+    Ko = torch.zeros((H * int(cuC[-1]), D), dtype=torch.bfloat16, device="cuda")
+    Vo = torch.zeros_like(Ko)
+    rs = torch.zeros((len(Ls), H, W, 2), dtype=torch.float32, device="cuda")
+    vt = torch.zeros((H * int(cuP[-1]),), dtype=torch.float32, device="cuda")
+    pl = torch.zeros_like(vt)
+    log(f"full size ragged: GPU call lengths {Ls}")
+    B.kvsel_select_varlen(Qd, Kd, Vd, cu.tolist(), Cs, W, D, H, w.kernel, w.pooling, torch.bfloat16, idx, Ko, Vo,
+                          rs, vt, pl, ws)
+    torch.cuda.synchronize()
+    for b in (0, 7):
+        L, C = Ls[b], Cs[b]
+        h = 3 * b % H
+        log(f"full size ragged: oracle sequence {b} head {h}")
+        q, k, v = WL.head_arrays(w, h, seq=b)
+        ref = O.snapkv_select(WL.to_float64(q, "bf16"), WL.to_float64(k, "bf16"), WL.to_float64(v, "bf16"),
+                              W, C, w.kernel, w.pooling)
+        sub = dict(idx=idx[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C),
+                   votes=vt[H * int(cuP[b]): H * int(cuP[b + 1])].view(H, L - W).cpu().numpy(),
+                   pooled=pl[H * int(cuP[b]): H * int(cuP[b + 1])].view(H, L - W).cpu().numpy(),
+                   rs=rs[b].cpu().numpy())
+        check_head(sub, h, ref, L, W, C, f"ragged seq {b} head {h}")
+        kk = Kd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D)
+        got = Ko[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C, D)
+        ii = sub["idx"].long()
+        assert torch.equal(bits(got), bits(torch.gather(kk, 1, ii[:, :, None].expand(H, C, D))))
