@@ -71,6 +71,23 @@ typedef enum {
 enum { KVSEL_POOL_AVG = 0, KVSEL_POOL_MAX = 1 };
 enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
 
+/* Process-wide options (kvsel_set_option / kvsel_get_option).
+ * KVSEL_OPT_SCORING selects how the window scores are computed:
+ *   KVSEL_SCORING_AUTO (default): the faster of the two for the shape
+ *     (currently two-pass everywhere);
+ *   KVSEL_SCORING_TWO_PASS: one kernel for the row statistics, a second for
+ *     the votes (K is read twice);
+ *   KVSEL_SCORING_SINGLE_READ: one cooperative kernel that reads K once;
+ *     it covers bf16, D in {64, 128}, W <= 64 and prompts short enough for
+ *     one round of the co-resident grid; calls whose shape it does not cover
+ *     return KVSEL_EUNSUPPORTED.
+ * Both give the same indices and K/V rows up to the documented rounding of
+ * the scores.  Not thread-safe with respect to concurrent calls. */
+enum { KVSEL_OPT_SCORING = 0 };
+enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };
+int kvsel_set_option(int option, int value);
+int kvsel_get_option(int option);
+
 /* Library version, (major << 16) | minor. */
 int kvsel_version(void);
 
@@ -138,7 +155,8 @@ int kvsel_select_varlen(const void* Qwin, const void* K, const void* V,
  *   scores + r * n, float32, every value finite and >= 0), write the `count`
  *   positions with the highest score, equal scores going to the lowest index,
  *   in ascending order, to out + r * ld_out.  1 <= count <= n.
- *   Workspace: kvsel_topk_workspace_bytes(rows, n) bytes.
+ *   Workspace: kvsel_topk_workspace_bytes(rows, n) bytes, 256-byte aligned
+ *   (0 is returned for invalid sizes).
  *   [section "one full selection computed from Q and K": ranking and tie rule]
  */
 size_t kvsel_topk_workspace_bytes(int rows, int n);

@@ -126,7 +126,16 @@ def kvsel_select_varlen(Qwin, K, V, cu_L, C, W, D, heads, kernel, pooling, dtype
                                    _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def kvsel_topk(scores, rows, n, count, out, ld_out, workspace=None, workspace_bytes=0, stream=None) -> None:
+def kvsel_topk_workspace_bytes(rows: int, n: int) -> int:
+    v = lib.kvsel_topk_workspace_bytes(rows, n)
+    if v == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return v
+
+
+def kvsel_topk(scores, rows, n, count, out, ld_out, workspace=None, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.kvsel_topk(_ptr(scores), rows, n, count, _ptr(out), ld_out, _ptr(workspace), workspace_bytes,
                           _stream(stream)))
 
@@ -191,3 +200,22 @@ def kvsel_profile_read() -> dict:
     if n < 0:
         raise KvselError(n, kvsel_last_error())
     return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 64))}
+
+
+KVSEL_OPT_SCORING = 0
+SCORING = {"auto": 0, "two_pass": 1, "single_read": 2}
+lib.kvsel_set_option.restype = _i
+lib.kvsel_set_option.argtypes = [_i, _i]
+lib.kvsel_get_option.restype = _i
+lib.kvsel_get_option.argtypes = [_i]
+
+
+def kvsel_set_option(option: int, value: int) -> None:
+    _check(lib.kvsel_set_option(option, value))
+
+
+def kvsel_get_option(option: int) -> int:
+    v = lib.kvsel_get_option(option)
+    if v < 0:
+        raise KvselError(v, kvsel_last_error())
+    return v

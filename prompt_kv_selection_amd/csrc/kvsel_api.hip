@@ -76,12 +76,16 @@ int check_pool(int kernel, int pooling) {
 // Per-sequence layout of a (possibly ragged) batch.
 struct Plan {
   int B = 0, heads = 0, W = 0, D = 0, dtype = 0;
-  std::vector<int> L, C, nch;
-  std::vector<long long> cuL, cuC, cuP, part;  // exclusive prefix sums
-  long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots
+  std::vector<int> L, C, nch, fc;
+  std::vector<long long> cuL, cuC, cuP, part, fpart;  // exclusive prefix sums
+  int fS = 0;                 // single-read scoring: positions per workgroup per round
+  long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots, either path
   long long vote_elems = 0;   // heads * sum of P_b
-  size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, bytes = 0;
+  size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_ctr = 0, off_status = 0, off_hist = 0, bytes = 0;
 };
+
+// Process-wide options.
+int g_scoring = KVSEL_SCORING_AUTO;
 
 int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p) {
   if (cu_L == nullptr || C_host == nullptr) return fail(KVSEL_EINVAL, "cu_L_host and C_host must not be NULL");
@@ -101,6 +105,9 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   p.cuC.assign(B + 1, 0);
   p.cuP.assign(B + 1, 0);
   p.part.assign(B + 1, 0);
+  p.fpart.assign(B + 1, 0);
+  p.fc.resize(B);
+  p.fS = fused_positions(W, D);
   for (int b = 0; b < B; ++b) {
     const long long L = (long long)cu_L[b + 1] - cu_L[b];
     const int C = C_host[b];
@@ -115,6 +122,8 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
     p.cuC[b + 1] = p.cuC[b] + C;
     p.cuP[b + 1] = p.cuP[b] + (L - W);
     p.part[b + 1] = p.part[b] + (long long)heads * p.nch[b];
+    p.fc[b] = L < C ? 0 : (int)((L + p.fS - 1) / p.fS);
+    p.fpart[b + 1] = p.fpart[b] + (long long)heads * p.fc[b];
   }
   if ((rc = check_support(W, D))) return rc;
   p.part_slots = p.part[B];
@@ -128,7 +137,13 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)p.vote_elems * sizeof(float));
   p.off_pooled = off;
   off = align256(off + (size_t)p.vote_elems * sizeof(float));
-  p.bytes = std::max<size_t>(off, 256);
+  p.off_ctr = off;  // single-read scoring: one exchange record per (sequence, head)
+  off = align256(off + (size_t)B * heads * fused_exchange_bytes());
+  p.off_status = off;
+  off = align256(off + 256);
+  p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
+  off = align256(off + (size_t)B * heads * 2048 * 4);
+  p.bytes = off;
   return KVSEL_OK;
 }
 
@@ -193,12 +208,39 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   float* pz = (float*)(ws + p.off_pz);
   float* votes = votes_opt ? votes_opt : (float*)(ws + p.off_votes);
   float* pooled = pooled_opt ? pooled_opt : (float*)(ws + p.off_pooled);
+  unsigned* counters = (unsigned*)(ws + p.off_ctr);
+  unsigned* status = (unsigned*)(ws + p.off_status);
   const int rpb = gather_rows_per_block(p.D, p.dtype);
+
+  // Single-read scoring needs every head of a round co-resident: each prompt
+  // must fit one round of the grid (ceil(L / S) <= grid).
+  bool fused_ok = p.dtype == KVSEL_BF16 && p.W <= 64 && (p.D == 64 || p.D == 128);
+  const int grid = fused_ok ? fused_grid(p.W, p.D) : 0;
+  fused_ok = fused_ok && grid > 0;
+  bool need_scoring = false;
+  for (int b = 0; b < p.B; ++b) need_scoring = need_scoring || p.L[b] >= p.C[b];
+  for (int b = 0; b < p.B && fused_ok; ++b) fused_ok = p.fc[b] <= grid;
+  if (g_scoring == KVSEL_SCORING_SINGLE_READ && need_scoring && !fused_ok)
+    return fail(KVSEL_EUNSUPPORTED, "single-read scoring does not cover this shape (bf16, D 64/128, W <= 64, "
+                                    "ceil(L / %d) <= %d)", p.fS, grid);
+  // AUTO takes the faster path for the shape; on this chip the two-pass
+  // kernels currently outrun the single-read kernel, so AUTO picks two-pass.
+  const bool use_fused = fused_ok && g_scoring == KVSEL_SCORING_SINGLE_READ;
+  uint32_t* hist = (uint32_t*)(ws + p.off_hist);
+  {
+    // Exchange records, status word and histograms start at zero.
+    hipError_t e = timed("fill", st, [&] {
+      return launch_fill_u32(counters, (long long)(p.bytes - p.off_ctr) / 4, 0u, st);
+    });
+    if (e != hipSuccess) return device_error(e, "fill launch");
+  }
 
   for (int b0 = 0; b0 < p.B; b0 += kMaxSegs) {
     const int nb = std::min(kMaxSegs, p.B - b0);
     Launch a = base_launch(p, kernel, pooling);
     a.n = nb;
+    a.S = p.fS;
+    a.rounds = 0;
     int items = 0, rows = 0, gitems = 0, maxP = 0;
     for (int k = 0; k < nb; ++k) {
       const int b = b0 + k;
@@ -221,23 +263,38 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       s.idx_off = (long long)p.heads * p.cuC[b];
       s.out_off = s.idx_off;
       s.vote_off = (long long)p.heads * p.cuP[b];
-      s.part_base = p.part[b];
+      s.part_base = use_fused ? p.fpart[b] : p.part[b];
+      s.fc = p.fc[b];
+      s.fhpr = s.fc > 0 && grid > 0 ? std::min(s.nh, grid / s.fc) : 0;
+      s.fnr = s.fhpr > 0 ? (s.nh + s.fhpr - 1) / s.fhpr : 0;
+      s.fr0 = a.rounds;
+      a.rounds += s.fnr;
       items += s.nh * s.nch;
       rows += s.nh;
       gitems += s.nh * s.gblk;
       if (s.L >= s.C) maxP = std::max(maxP, s.L - p.W);
     }
     hipError_t e;
-    if (items > 0) {
+    if (items > 0 && use_fused) {
+      e = timed("window_fused", st,
+                [&] { return launch_fused_scoring(a, Q, K, counters, status, votes, row_stats, st); });
+      if (e != hipSuccess) return device_error(e, "window_fused launch");
+    } else if (items > 0) {
       e = timed("window_stats", st, [&] { return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, st); });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
-      e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, st); });
+    }
+    if (items > 0) {
+      e = timed("pool", st, [&] {
+        return launch_pool(a, rows, maxP, votes, pooled, hist + (long long)b0 * p.heads * 2048, st);
+      });
       if (e != hipSuccess) return device_error(e, "pool launch");
     }
-    e = timed("topk", st, [&] { return launch_topk(a, rows, pooled, indices, st); });
+    e = timed("topk", st, [&] {
+      return launch_topk(a, rows, pooled, hist + (long long)b0 * p.heads * 2048, indices, st);
+    });
     if (e != hipSuccess) return device_error(e, "topk launch");
     e = timed("gather", st, [&] { return launch_gather(a, gitems, p.dtype, K, V, indices, K_out, V_out, st); });
     if (e != hipSuccess) return device_error(e, "gather launch");
@@ -249,7 +306,20 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
 
 extern "C" {
 
-int kvsel_version(void) { return (0 << 16) | 1; }
+int kvsel_version(void) { return (0 << 16) | 2; }
+
+int kvsel_set_option(int option, int value) {
+  if (option != KVSEL_OPT_SCORING) return fail(KVSEL_EINVAL, "unknown option %d", option);
+  if (value < KVSEL_SCORING_AUTO || value > KVSEL_SCORING_SINGLE_READ)
+    return fail(KVSEL_EINVAL, "invalid scoring value %d", value);
+  g_scoring = value;
+  return ok();
+}
+
+int kvsel_get_option(int option) {
+  if (option != KVSEL_OPT_SCORING) return fail(KVSEL_EINVAL, "unknown option %d", option);
+  return g_scoring;
+}
 
 const char* kvsel_last_error(void) { return g_error.c_str(); }
 
@@ -300,20 +370,25 @@ int kvsel_select(const void* Qwin, const void* K, const void* V, int L, int W, i
 }
 
 size_t kvsel_topk_workspace_bytes(int rows, int n) {
-  (void)rows;
-  (void)n;
+  if (rows < 1 || n < 1) {
+    fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
+    return 0;
+  }
   ok();
-  return 0;
+  return align256((size_t)rows * 2048 * 4);
 }
 
 int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out, void* workspace,
                size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!scores || !out) return fail(KVSEL_EINVAL, "scores and out must not be NULL");
   if (rows < 1 || n < 1) return fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
   if (count < 1 || count > n) return fail(KVSEL_EINVAL, "count must be in [1, n] (got %d, n = %d)", count, n);
   if (ld_out < count) return fail(KVSEL_EINVAL, "ld_out %d is smaller than count %d", ld_out, count);
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = align256((size_t)rows * 2048 * 4);
+  if (workspace_bytes < need)
+    return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
   Launch a{};
   a.n = 1;
   a.heads = rows;
@@ -326,7 +401,12 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   s.idx_ld = ld_out;
   s.vote_ld = n;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = timed("topk", st, [&] { return launch_topk(a, rows, scores, out, st); });
+  uint32_t* hist = (uint32_t*)workspace;
+  hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
+  if (e != hipSuccess) return device_error(e, "fill launch");
+  e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
+  if (e != hipSuccess) return device_error(e, "histogram launch");
+  e = timed("topk", st, [&] { return launch_topk(a, rows, scores, hist, out, st); });
   if (e != hipSuccess) return device_error(e, "topk launch");
   return ok();
 }
@@ -349,7 +429,7 @@ int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling, f
   s.nh = rows;
   s.vote_ld = n;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = timed("pool", st, [&] { return launch_pool(a, rows, n, votes, pooled, st); });
+  hipError_t e = timed("pool", st, [&] { return launch_pool(a, rows, n, votes, pooled, nullptr, st); });
   if (e != hipSuccess) return device_error(e, "pool launch");
   return ok();
 }

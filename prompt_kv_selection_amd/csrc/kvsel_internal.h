@@ -38,6 +38,11 @@ struct Seg {
   long long out_off;   // row offset of (b, head 0) in K_out / V_out
   long long vote_off;  // element offset of (b, head 0) in votes / pooled
   long long part_base; // partial-stat slot of (b, head 0, chunk 0)
+  // single-read scoring schedule (see kvsel_fused.hip)
+  int fc;         // chunks per head, ceil(L / S)
+  int fhpr;       // heads per round
+  int fr0;        // first round of this segment
+  int fnr;        // rounds of this segment
 };
 
 struct Launch {
@@ -47,6 +52,8 @@ struct Launch {
   int kernel, pooling;
   int window;     // 1: append the window positions after the picks
   float scale2;   // log2(e) / sqrt(D)
+  int S;          // single-read scoring: positions per workgroup per round
+  int rounds;     // single-read scoring: rounds over all segments
   Seg seg[kMaxSegs];
 };
 
@@ -69,10 +76,23 @@ hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                const float* part_m, const float* part_z, float* votes,
                                float* row_stats, hipStream_t st);
+// Pooling (pooled may be nullptr: histogram of the input only) with the
+// first-digit histogram of each row added into hist[row][2048] (nullptr: none).
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
-                       hipStream_t st);
-hipError_t launch_topk(const Launch& a, int rows, const float* scores, int32_t* indices,
-                       hipStream_t st);
+                       uint32_t* hist, hipStream_t st);
+// Top-(C-W) per row given the first-digit histograms.
+hipError_t launch_topk(const Launch& a, int rows, const float* scores, const uint32_t* hist,
+                       int32_t* indices, hipStream_t st);
+// Single-read scoring (cooperative persistent kernel).  fused_positions()
+// gives S for the kernel variant, fused_grid() the co-resident grid (0 if the
+// variant cannot run); launch_fused_scoring() returns hipErrorNotSupported
+// when the shape is not covered.
+int fused_positions(int W, int D);
+int fused_grid(int W, int D);
+int fused_exchange_bytes();  // per-(sequence, head) exchange record
+hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* exchange,
+                                unsigned* status, float* votes, float* row_stats, hipStream_t st);
+hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);

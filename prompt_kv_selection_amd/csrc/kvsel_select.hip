@@ -14,14 +14,22 @@
 //    position.
 //
 // Top-k.  Pooled scores are finite and >= 0, so their float32 bit patterns
-// order like the values.  One 1024-thread workgroup per (sequence, head) row
-// runs a 3-digit (11/11/10 bit) most-significant-first radix select with LDS
-// histograms to find the threshold pattern tau and how many tau-equal
-// positions are still needed; a single scan of packed (greater, equal)
-// counts over the row in index order then writes the picks in ascending
-// order, the lowest tau-equal indices first.
+// order like the values.  A most-significant-first radix select (digits of
+// 11, 11 and 10 bits) finds the threshold pattern tau of the (C-W)-th largest
+// score and how many tau-equal positions are still needed.  The first digit's
+// histogram is built by the pooling kernel across many workgroups; one
+// 1024-thread workgroup per (sequence, head) row then gathers the positions
+// of the boundary digit into LDS and finishes the select there.  A single
+// scan of packed (greater, equal) counts over the row in index order writes
+// the picks in ascending order, the lowest tau-equal indices first.
 
 #include "kvsel_internal.h"
+
+// Instrumentation hook at the phases of the select kernel (point 0..4);
+// empty unless a profiling build defines it.
+#ifndef KVSEL_SELECT_MARK
+#define KVSEL_SELECT_MARK(point)
+#endif
 
 namespace kvsel {
 
@@ -52,8 +60,62 @@ __device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* sh, ui
   return v + base;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const Launch a, const float* __restrict__ scores,
-                                                            int32_t* __restrict__ indices) {
+// Wave-aggregated append position: lanes with `pred` get consecutive slots
+// starting at the returned base (one LDS atomic per wave).
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter, uint32_t& slot) {
+  const unsigned long long mask = __ballot(pred);
+  if (mask == 0) {  // wave-uniform: nothing to append
+    slot = 0;
+    return 0;
+  }
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+  const int leader = __ffsll((long long)mask) - 1;
+  uint32_t base = 0;
+  if (mask != 0 && (int)(threadIdx.x & 63) == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+  base = __shfl(base, leader < 0 ? 0 : leader);
+  slot = base + below;
+  return (uint32_t)__popcll(mask);
+}
+
+// Given hist[] (LDS) of the digits of the candidates, find the digit holding
+// the need-th largest: returns (digit, rank of the target inside the digit).
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
+                                           uint32_t* s_digit, uint32_t* s_need) {
+  const int tid = threadIdx.x;
+  const int per = nb / kTopkThreads;
+  uint32_t local = 0;
+  for (int u = 0; u < per; ++u) local += hist[nb - 1 - (tid * per + u)];
+  uint32_t total;
+  const uint32_t incl = block_scan_1024(local, sh, total);
+  const uint32_t excl = incl - local;
+  if (excl < need && need <= incl) {
+    uint32_t cum = excl;
+    for (int u = 0; u < per; ++u) {
+      const uint32_t d = (uint32_t)(nb - 1 - (tid * per + u));
+      if (cum + hist[d] >= need) {
+        *s_digit = d;
+        *s_need = need - cum;
+        break;
+      }
+      cum += hist[d];
+    }
+  }
+  __syncthreads();
+}
+
+// Select kernel: one 1024-thread workgroup per (sequence, head) row.  The
+// first digit (bits 31..21) comes from the histogram the pooling kernel built;
+// the positions in that digit are gathered into LDS and the remaining 21 bits
+// are resolved there (or, when the digit holds more than kCand positions, by
+// passes over the row).  A final in-order pass writes the picks ascending.
+constexpr int kCand = 16384;
+constexpr int kPickBuf = 8192;
+constexpr int kPoolSpan = 8;
+constexpr int kMaxPoolRadius = 31;  // pooling width up to 63
+
+__global__ __launch_bounds__(kTopkThreads) void select_kernel(const Launch a, const float* __restrict__ scores,
+                                                              const uint32_t* __restrict__ ghist,
+                                                              int32_t* __restrict__ indices) {
   const int row = blockIdx.x;
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
   const int h = s.h0 + (row - s.row0);
@@ -70,65 +132,113 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const Launch a, cons
   const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
 
   __shared__ uint32_t hist[2048];
+  __shared__ uint32_t cand[kCand];
+  __shared__ int32_t picks[kPickBuf];  // picks collected here, written out at the end
   __shared__ uint32_t sh[32];
-  __shared__ uint32_t s_prefix, s_need;
-  uint32_t prefix = 0, need = count;
+  __shared__ uint32_t s_digit, s_need, s_ncand;
 
-  // Radix select: after the three digits, `prefix` is the full pattern of
-  // the count-th largest score and `need` the number of positions equal to
-  // it that belong to the selection.
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-    const int bits = pass == 2 ? 10 : 11;
+  KVSEL_SELECT_MARK(0);
+  const uint32_t* gh = ghist + (long long)row * 2048;
+  for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = gh[d];
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+  pick_digit(hist, 2048, count, sh, &s_digit, &s_need);
+  const uint32_t d1 = s_digit;
+  uint32_t need = s_need;
+  const uint32_t in_d1 = hist[d1];
+  __syncthreads();
+
+  // Gather the keys of digit d1 into LDS when they fit (any order: only the
+  // threshold is needed); otherwise the remaining digits read the row.
+  KVSEL_SELECT_MARK(1);
+  const bool in_lds = in_d1 <= (uint32_t)kCand;
+  if (in_lds) {
+    constexpr int U = 16;  // independent loads in flight per thread
+    for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
+      uint32_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads + tid;
+        kk[u] = j < P ? key[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads + tid;
+        const bool hit = j < P && (kk[u] >> 21) == d1;
+        uint32_t slot;
+        wave_append(hit, &s_ncand, slot);
+        if (hit && slot < (uint32_t)kCand) cand[slot] = kk[u];
+      }
+    }
+    __syncthreads();
+  }
+  KVSEL_SELECT_MARK(2);
+  const uint32_t n_src = in_lds ? s_ncand : (uint32_t)P;
+  uint32_t prefix = d1;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const int bits = pass == 0 ? 11 : 10;
     const int hi = shift + bits;
     const uint32_t nb = 1u << bits;
     for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = 0u;
     __syncthreads();
-    for (int j = tid; j < P; j += kTopkThreads) {
-      const uint32_t k = key[j];
-      if (pass == 0 || (k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
+    for (uint32_t i = tid; i < n_src; i += kTopkThreads) {
+      const uint32_t k = in_lds ? cand[i] : key[i];
+      if ((k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
     }
     __syncthreads();
-    // Thread t owns bins in descending order, so the inclusive scan counts
-    // positions at or above each bin.
-    const int per = (int)nb / kTopkThreads;
-    uint32_t local = 0;
-    for (int u = 0; u < per; ++u) local += hist[nb - 1u - (uint32_t)(tid * per + u)];
-    uint32_t total;
-    const uint32_t incl = block_scan_1024(local, sh, total);
-    const uint32_t excl = incl - local;
-    if (excl < need && need <= incl) {
-      uint32_t cum = excl;
-      for (int u = 0; u < per; ++u) {
-        const uint32_t d = nb - 1u - (uint32_t)(tid * per + u);
-        const uint32_t cnt = hist[d];
-        if (cum + cnt >= need) {
-          s_prefix = (prefix << bits) | d;
-          s_need = need - cum;
-          break;
-        }
-        cum += cnt;
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
+    pick_digit(hist, (int)nb, need, sh, &s_digit, &s_need);
+    prefix = (prefix << bits) | s_digit;
     need = s_need;
     __syncthreads();
   }
+  const uint32_t tau = prefix;
+  KVSEL_SELECT_MARK(3);
 
-  const uint32_t tau = prefix, need_eq = need;
+  // In-order pass: every score above tau, then the lowest-index need_eq
+  // scores equal to tau, written ascending.
+  // The candidate buffer is free again: it stages a tile of scores at a
+  // time, from which each thread scans kPer consecutive ones (rows of
+  // kPer + 1 words in LDS, so the scans are conflict-free).  The next tile's
+  // coalesced loads are issued before the current tile is processed.
+  const uint32_t need_eq = need;
+  const bool buffered = count <= (uint32_t)kPickBuf;  // else picks go straight to memory
   uint32_t gt_run = 0, eq_run = 0;
   constexpr int kPer = 8;
-  for (int base = 0; base < P; base += kPer * kTopkThreads) {
+  constexpr int kTile = kPer * kTopkThreads;
+  static_assert((kPer + 1) * kTopkThreads <= kCand, "staging tile exceeds the candidate buffer");
+  uint32_t nxt[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = u * kTopkThreads + tid;
+    nxt[u] = j < P ? key[j] : 0u;
+  }
+  for (int base = 0; base < P; base += kTile) {
+    uint32_t cur[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) cur[u] = nxt[u];
+    if (base + kTile < P) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int j = base + kTile + u * kTopkThreads + tid;
+        nxt[u] = j < P ? key[j] : 0u;
+      }
+    }
+    __syncthreads();  // previous tile fully consumed
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kTopkThreads + tid;  // position base + i
+      cand[(i / kPer) * (kPer + 1) + i % kPer] = cur[u];
+    }
+    __syncthreads();
     const int j0 = base + tid * kPer;
     uint32_t kk[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) kk[u] = cand[tid * (kPer + 1) + u];
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int j = j0 + u;
-      kk[u] = j < P ? key[j] : 0u;
-      if (j < P) {
+      if (j0 + u < P) {
         ngt += kk[u] > tau;
         neq += kk[u] == tau;
       }
@@ -148,7 +258,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const Launch a, cons
           ++eq_seen;
         }
         if (take) {
-          if (pos < count) out[pos] = j;
+          if (pos < count) {
+            if (buffered)
+              picks[pos] = j;
+            else
+              out[pos] = j;
+          }
           ++pos;
         }
       }
@@ -156,21 +271,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const Launch a, cons
     gt_run += total >> 16;
     eq_run += total & 0xFFFFu;
   }
+  if (buffered) {
+    __syncthreads();
+    for (uint32_t m = tid; m < count; m += kTopkThreads) out[m] = picks[m];
+  }
   if (a.window)
     for (int w = tid; w < a.W; w += kTopkThreads) out[count + w] = P + w;
+  KVSEL_SELECT_MARK(4);
 }
 
 // Avg pooling sums the k neighbours (zero padding included) in ascending
-// order, so equal neighbour multisets give bit-equal pooled scores.
+// order, so equal neighbour multisets give bit-equal pooled scores.  `c`
+// points at the centre of a zero-padded run of at least r values per side.
 template <int KW>
-__device__ __forceinline__ float avg_sorted(const float* __restrict__ v, int j, int P) {
+__device__ __forceinline__ float avg_sorted(const float* c) {
   constexpr int r = KW / 2;
   float x[KW];
 #pragma unroll
-  for (int o = 0; o < KW; ++o) {
-    const int p = j - r + o;
-    x[o] = (p >= 0 && p < P) ? v[p] : 0.f;
-  }
+  for (int o = 0; o < KW; ++o) x[o] = c[o - r];
 #pragma unroll
   for (int i = 1; i < KW; ++i)
 #pragma unroll
@@ -185,12 +303,11 @@ __device__ __forceinline__ float avg_sorted(const float* __restrict__ v, int j, 
   return sum / (float)KW;
 }
 
-__device__ float avg_sorted_any(const float* __restrict__ v, int j, int P, int kw) {
-  float x[63];
+__device__ float avg_sorted_any(const float* c, int kw) {
+  float x[2 * kMaxPoolRadius + 1];
   const int r = kw / 2;
   for (int o = 0; o < kw; ++o) {
-    const int p = j - r + o;
-    float val = (p >= 0 && p < P) ? v[p] : 0.f;
+    const float val = c[o - r];
     int k = o;
     while (k > 0 && x[k - 1] > val) {
       x[k] = x[k - 1];
@@ -203,36 +320,81 @@ __device__ float avg_sorted_any(const float* __restrict__ v, int j, int P, int k
   return sum / (float)kw;
 }
 
-__global__ __launch_bounds__(kPoolBlock) void pool_kernel(const Launch a, const float* __restrict__ votes,
-                                                          float* __restrict__ pooled) {
+// Pooling of the prefix votes fused with the first radix digit of the
+// selection: each workgroup pools kPoolBlock * kPoolSpan positions of one row and
+// adds its LDS histogram of bits 31..21 of the pooled scores to the row's
+// histogram.  With pooled == nullptr the input is taken as already pooled
+// (histogram only); with ghist == nullptr no histogram is built.
+__global__ __launch_bounds__(kPoolBlock) void pool_hist_kernel(const Launch a, const float* __restrict__ votes,
+                                                               float* __restrict__ pooled,
+                                                               uint32_t* __restrict__ ghist) {
   const int row = blockIdx.x;
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
   if (s.L < s.C) return;
   const int h = s.h0 + (row - s.row0);
   const int P = s.L - (a.window ? a.W : 0);
-  const int j = blockIdx.y * kPoolBlock + threadIdx.x;
-  if (j >= P) return;
+  const int base = blockIdx.y * kPoolBlock * kPoolSpan;
+  if (base >= P) return;
+  __shared__ uint32_t hist[2048];
+  if (ghist != nullptr) {
+    for (int d = threadIdx.x; d < 2048; d += kPoolBlock) hist[d] = 0u;
+    __syncthreads();
+  }
   const float* v = votes + s.vote_off + (long long)h * s.vote_ld;
-  float* o = pooled + s.vote_off + (long long)h * s.vote_ld;
+  float* o = pooled ? pooled + s.vote_off + (long long)h * s.vote_ld : nullptr;
   const int kw = a.kernel, r = kw / 2;
-  if (a.pooling == 1) {
-    float mx = v[j];
-    const int lo = max(0, j - r), hi = min(P - 1, j + r);
-    for (int p = lo; p <= hi; ++p) mx = fmaxf(mx, v[p]);
-    o[j] = mx;
-    return;
+  // The block's positions plus a halo of r on each side, staged through LDS
+  // with coalesced loads; out-of-range neighbours are the zero padding (avg)
+  // or excluded (max: -inf never wins, the centre is always in range).
+  constexpr int kSpan = kPoolBlock * kPoolSpan;
+  __shared__ float tile[kSpan + 2 * kMaxPoolRadius];
+  const float pad = a.pooling == 1 ? -INFINITY : 0.f;
+  for (int i = threadIdx.x; i < kSpan + 2 * r; i += kPoolBlock) {
+    const int p = base - r + i;
+    tile[i] = (p >= 0 && p < P) ? v[p] : pad;
   }
-  float res;
-  switch (kw) {
-    case 1: res = v[j]; break;
-    case 3: res = avg_sorted<3>(v, j, P); break;
-    case 5: res = avg_sorted<5>(v, j, P); break;
-    case 7: res = avg_sorted<7>(v, j, P); break;
-    case 9: res = avg_sorted<9>(v, j, P); break;
-    case 11: res = avg_sorted<11>(v, j, P); break;
-    default: res = avg_sorted_any(v, j, P, kw); break;
+  __syncthreads();
+  // Each thread pools kPoolSpan consecutive positions; equal first digits of
+  // neighbouring positions are counted once per run, which keeps the LDS
+  // atomics off the few hot bins of smooth score profiles.
+  const int i0 = threadIdx.x * kPoolSpan;
+  uint32_t run_bin = 0xFFFFFFFFu, run_len = 0;
+  for (int u = 0; u < kPoolSpan; ++u) {
+    const int j = base + i0 + u;
+    if (j >= P) break;
+    const float* c = tile + i0 + u + r;  // centre
+    float res;
+    if (o == nullptr || kw == 1) {
+      res = c[0];
+    } else if (a.pooling == 1) {
+      res = c[0];
+      for (int q = -r; q <= r; ++q) res = fmaxf(res, c[q]);
+    } else {
+      switch (kw) {
+        case 3: res = avg_sorted<3>(c); break;
+        case 5: res = avg_sorted<5>(c); break;
+        case 7: res = avg_sorted<7>(c); break;
+        case 9: res = avg_sorted<9>(c); break;
+        case 11: res = avg_sorted<11>(c); break;
+        default: res = avg_sorted_any(c, kw); break;
+      }
+    }
+    if (o) o[j] = res;
+    const uint32_t bin = __float_as_uint(res) >> 21;
+    if (bin != run_bin) {
+      if (run_len && ghist != nullptr) atomicAdd(&hist[run_bin], run_len);
+      run_bin = bin;
+      run_len = 0;
+    }
+    ++run_len;
   }
-  o[j] = res;
+  if (run_len && ghist != nullptr) atomicAdd(&hist[run_bin], run_len);
+  if (ghist != nullptr) {
+    __syncthreads();
+    uint32_t* gh = ghist + (long long)row * 2048;
+    for (int d = threadIdx.x; d < 2048; d += kPoolBlock)
+      if (hist[d]) atomicAdd(gh + d, hist[d]);
+  }
 }
 
 // K/V gather: one 16-byte piece of one row per thread.  RU = pieces per row.
@@ -258,16 +420,18 @@ __global__ __launch_bounds__(256) void gather_kernel(const Launch a, const uint4
   Vo[out_row * RU + part] = vv;
 }
 
-hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled, hipStream_t st) {
-  const int yb = (max_n + kPoolBlock - 1) / kPoolBlock;
+hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled, uint32_t* hist,
+                       hipStream_t st) {
+  const int yb = (max_n + kPoolBlock * kPoolSpan - 1) / (kPoolBlock * kPoolSpan);
   if (rows <= 0 || yb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3(rows, yb), dim3(kPoolBlock), 0, st, a, votes, pooled);
+  hipLaunchKernelGGL(pool_hist_kernel, dim3(rows, yb), dim3(kPoolBlock), 0, st, a, votes, pooled, hist);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Launch& a, int rows, const float* scores, int32_t* indices, hipStream_t st) {
+hipError_t launch_topk(const Launch& a, int rows, const float* scores, const uint32_t* hist, int32_t* indices,
+                       hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, scores, indices);
+  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, scores, hist, indices);
   return hipGetLastError();
 }
 

@@ -84,9 +84,22 @@ def gpu_internal_topk(gpu_prefix: np.ndarray, gpu_pooled_f32: np.ndarray, n: int
                                   err_msg=f"{what}: GPU picks differ from top-n of the GPU's own scores")
 
 
-def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str):
-    """Run kvsel_select with every optional output; returns host numpy arrays."""
+def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto"):
+    """Run kvsel_select with every optional output; returns host numpy arrays.
+    `scoring` picks the scoring path (auto, two_pass, single_read)."""
     from prompt_kv_selection_amd import binding as B
+    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[scoring])
+    try:
+        return _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype)
+    finally:
+        B.kvsel_set_option(B.KVSEL_OPT_SCORING, 0)
+
+
+def single_read_covers(dtype, D, W):
+    return dtype == "bf16" and D in (64, 128) and W <= 64
+
+
+def _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype):
     H, _, D = Kd.shape
     td = torch_dtype(dtype)
     ws = torch.empty(B.kvsel_workspace_bytes(H, L, W, C, D, td), dtype=torch.uint8, device="cuda")

@@ -41,9 +41,11 @@ def test_version_and_error_string(B):
 
 def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
-    # partial stats (32 heads x 32 chunks x 32 rows x 2) + votes + pooled
-    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4
-    assert expect_min <= n <= expect_min + 4 * 256
+    # partial (max, sum) per (head, chunk, row) for the finer single-read
+    # chunking (512 positions: 64 chunks), votes, pooled, per-head counters,
+    # status word
+    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8320 + 256 + 32 * 2048 * 4
+    assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W
     assert "budget" in B.kvsel_last_error()
@@ -108,9 +110,23 @@ def test_step_entry_point_errors(B):
     assert lib.kvsel_topk(FAKE, 4, 100, 101, FAKE, 200, None, 0, None) == -1
     assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 9, None, 0, None) == -1
     assert lib.kvsel_topk(None, 4, 100, 10, FAKE, 10, None, 0, None) == -1
+    assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, None, 0, None) == -1          # no workspace
+    assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, FAKE, 1024, None) == -3       # too small
+    assert lib.kvsel_topk_workspace_bytes(4, 100) == 4 * 2048 * 4
+    assert lib.kvsel_topk_workspace_bytes(0, 100) == 0
     assert lib.kvsel_pool1d(FAKE, 4, 100, 2, 0, ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 0, FAKE, None) == -1  # aliasing
     assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 5, ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvsel_gather(FAKE, FAKE, FAKE, 10, 4, 100, 20, 128, 1, FAKE, FAKE, None) == -1  # ld < count
     assert lib.kvsel_gather(FAKE, FAKE, FAKE, 20, 4, 100, 20, 80, 1, FAKE, FAKE, None) == -2
     assert lib.kvsel_gather(FAKE, FAKE, FAKE, 20, 4, 100, 20, 128, 3, FAKE, FAKE, None) == -1
+
+
+def test_options(B):
+    lib = B.lib
+    assert lib.kvsel_get_option(0) == 0
+    assert lib.kvsel_set_option(0, 3) == -1
+    assert lib.kvsel_set_option(1, 0) == -1
+    assert lib.kvsel_get_option(5) == -1
+    assert lib.kvsel_set_option(0, 1) == 0 and lib.kvsel_get_option(0) == 1
+    assert lib.kvsel_set_option(0, 0) == 0 and lib.kvsel_get_option(0) == 0

@@ -13,7 +13,7 @@ from oracle import snapkv_oracle as O
 from prompt_kv_selection_amd import workloads as WL
 
 from parity import (band_check, bits, check_gather, check_head, close, gpu_internal_topk, log, run_select,
-                    to_device)
+                    single_read_covers, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,16 +100,22 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[1]}-H{c[2]}-L{c[3]}-W{c[4]}-C{c[5]}-k{c[6]}{c[7]}"
                                              for c in CASES])
-def test_random_cases(B, case):
+def test_random_cases(B, case, scoring):
     dtype, D, H, L, W, C, kernel, pooling = case
     w = WL.Workload("case", seed=L * 7 + W, heads=H, L=L, W=W, C=C, D=D, dtype=dtype, kernel=kernel,
                     pooling=pooling, keys="spike", spike_frac=0.02 if L - W >= 50 else 0.0)
     Q, K, V = WL.layer_arrays(w)
-    log(f"random case {case}")
+    log(f"random case {case} scoring={scoring}")
     Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
-    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype)
+    if scoring == "single_read" and not single_read_covers(dtype, D, W) and L >= C:
+        with pytest.raises(B.KvselError) as ei:
+            run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring)
+        assert ei.value.code == B.KVSEL_EUNSUPPORTED
+        return
+    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring)
     for h in range(H):
         ref = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h], dtype),
                               WL.to_float64(V[h], dtype), W, C, kernel, pooling)
@@ -117,12 +123,13 @@ def test_random_cases(B, case):
     check_gather(out, Kd, Vd, C, L)
 
 
-def test_identical_keys_give_identical_scores(B):
+@pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
+def test_identical_keys_give_identical_scores(B, scoring):
     w = WL.reduced(WL.get("tied_h64_l128k"), L=8192, heads=2)
     Q, K, V = WL.layer_arrays(w)
-    log("identical keys")
+    log(f"identical keys scoring={scoring}")
     Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
-    out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
+    out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16", scoring)
     P = w.L - w.W
     for h in range(2):
         rows, inv = np.unique(K[h, :P], axis=0, return_inverse=True)
@@ -135,13 +142,14 @@ def test_identical_keys_give_identical_scores(B):
         check_head(out, h, ref, w.L, w.W, w.C, f"tied head {h}")
 
 
-def test_deterministic(B):
+@pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
+def test_deterministic(B, scoring):
     w = WL.reduced(WL.get("lognorm_h32_l16k"), L=6000, heads=4)
     Q, K, V = WL.layer_arrays(w)
     Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
-    log("determinism")
-    a = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
-    b = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16")
+    log(f"determinism scoring={scoring}")
+    a = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16", scoring)
+    b = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16", scoring)
     assert torch.equal(a["idx"], b["idx"])
     np.testing.assert_array_equal(a["votes"].view(np.int32), b["votes"].view(np.int32))
     np.testing.assert_array_equal(a["pooled"].view(np.int32), b["pooled"].view(np.int32))
@@ -164,7 +172,8 @@ def test_topk_step_exact(B, rows, n, count):
     ld = count + 3
     out = torch.full((rows, ld), -1, dtype=torch.int32, device="cuda")
     log(f"topk rows={rows} n={n} count={count}")
-    B.kvsel_topk(sd, rows, n, count, out, ld)
+    ws = torch.empty(B.kvsel_topk_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+    B.kvsel_topk(sd, rows, n, count, out, ld, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for r in range(rows):
