@@ -78,7 +78,7 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  *   KVSEL_SCORING_TWO_PASS: one kernel for the row statistics, a second for
  *     the votes (K is read twice);
  *   KVSEL_SCORING_SINGLE_READ: one cooperative kernel that reads K once;
- *     it covers bf16, D in {64, 128}, W <= 64 and prompts short enough for
+ *     it covers bf16, D in {64, 128}, W <= 32 and prompts short enough for
  *     one round of the co-resident grid; calls whose shape it does not cover
  *     return KVSEL_EUNSUPPORTED.
  * Both give the same indices and K/V rows up to the documented rounding of

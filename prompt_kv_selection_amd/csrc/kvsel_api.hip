@@ -122,7 +122,7 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
     p.cuC[b + 1] = p.cuC[b] + C;
     p.cuP[b + 1] = p.cuP[b] + (L - W);
     p.part[b + 1] = p.part[b] + (long long)heads * p.nch[b];
-    p.fc[b] = L < C ? 0 : (int)((L + p.fS - 1) / p.fS);
+    p.fc[b] = (L < C || p.fS == 0) ? 0 : (int)((L + p.fS - 1) / p.fS);
     p.fpart[b + 1] = p.fpart[b] + (long long)heads * p.fc[b];
   }
   if ((rc = check_support(W, D))) return rc;
@@ -214,14 +214,14 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
 
   // Single-read scoring needs every head of a round co-resident: each prompt
   // must fit one round of the grid (ceil(L / S) <= grid).
-  bool fused_ok = p.dtype == KVSEL_BF16 && p.W <= 64 && (p.D == 64 || p.D == 128);
+  bool fused_ok = p.dtype == KVSEL_BF16 && p.fS > 0 && (p.D == 64 || p.D == 128);
   const int grid = fused_ok ? fused_grid(p.W, p.D) : 0;
   fused_ok = fused_ok && grid > 0;
   bool need_scoring = false;
   for (int b = 0; b < p.B; ++b) need_scoring = need_scoring || p.L[b] >= p.C[b];
   for (int b = 0; b < p.B && fused_ok; ++b) fused_ok = p.fc[b] <= grid;
   if (g_scoring == KVSEL_SCORING_SINGLE_READ && need_scoring && !fused_ok)
-    return fail(KVSEL_EUNSUPPORTED, "single-read scoring does not cover this shape (bf16, D 64/128, W <= 64, "
+    return fail(KVSEL_EUNSUPPORTED, "single-read scoring does not cover this shape (bf16, D 64/128, W <= 32, "
                                     "ceil(L / %d) <= %d)", p.fS, grid);
   // AUTO takes the faster path for the shape; on this chip the two-pass
   // kernels currently outrun the single-read kernel, so AUTO picks two-pass.

@@ -96,7 +96,7 @@ def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = 
 
 
 def single_read_covers(dtype, D, W):
-    return dtype == "bf16" and D in (64, 128) and W <= 64
+    return dtype == "bf16" and D in (64, 128) and W <= 32
 
 
 def _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype):

@@ -41,10 +41,9 @@ def test_version_and_error_string(B):
 
 def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
-    # partial (max, sum) per (head, chunk, row) for the finer single-read
-    # chunking (512 positions: 64 chunks), votes, pooled, per-head counters,
-    # status word
-    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8320 + 256 + 32 * 2048 * 4
+    # two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
+    # per-head exchange records, status word, first-digit histograms
+    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 4160 + 256 + 32 * 2048 * 4
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W

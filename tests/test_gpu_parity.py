@@ -129,6 +129,13 @@ def test_identical_keys_give_identical_scores(B, scoring):
     Q, K, V = WL.layer_arrays(w)
     log(f"identical keys scoring={scoring}")
     Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    if scoring == "single_read" and not single_read_covers("bf16", w.D, w.W):
+        with pytest.raises(B.KvselError) as ei:
+            run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16", scoring)
+        assert ei.value.code == B.KVSEL_EUNSUPPORTED
+        w = WL.reduced(w, W=32, C=w.C)  # same recipe with a window the path covers
+        Q, K, V = WL.layer_arrays(w)
+        Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
     out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, "bf16", scoring)
     P = w.L - w.W
     for h in range(2):
