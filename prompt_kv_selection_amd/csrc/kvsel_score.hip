@@ -11,8 +11,9 @@
 //
 // Tiling.  One MFMA tile is 32 window rows x 32 prompt positions.  Qwin is the
 // A operand (rows) and stays in VGPRs for the whole workgroup; a tile of 32 K
-// rows is the B operand, loaded straight from HBM, each lane taking 16 bytes
-// per k-step from one K row.  In the 32x32 accumulator a lane owns one
+// rows is the B operand, streamed from HBM into a per-wave LDS ring with
+// coalesced 1 KiB direct-to-LDS loads, then read by each lane as 16 bytes per
+// k-step of one K row.  In the 32x32 accumulator a lane owns one
 // position (lane % 32) and 16 of the 32 window rows, so
 //   * the per-row max / sum of exponentials run inside the lane across the
 //     positions it visits, then across the 32 lanes of its half,
@@ -43,19 +44,86 @@ constexpr float kLn2 = 0.693147180559945309f;
 // output layout: lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4).
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// ---- K tiles: 32 prompt rows streamed from HBM straight into LDS.
+//
+// Each wave owns a ring of RING tile buffers.  A tile load is NL
+// global_load_lds_dwordx4 instructions: instruction i moves 64 consecutive
+// 16-byte pieces of the tile (1 KiB, coalesced), lane l's piece landing at
+// LDS byte M0 + 16 l.  Piece c of tile row r is stored at slot
+// r * PR + (c ^ (r % PR)), so the operand reads below (32 rows, one piece
+// each) hit distinct LDS banks.
+template <typename T, int D>
+struct TileGeom {
+  static constexpr int PR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  static constexpr int NL = PR / 2;                   // load instructions per tile
+  static constexpr int PIECES = 32 * PR;              // pieces per tile
+  static constexpr int RING = PR >= 32 ? 1 : 2;       // tiles in flight per wave (LDS budget)
+};
+
+// Byte offsets (from the tile's first row) of lane's piece in each load
+// instruction; fixed for the life of the kernel.
+template <typename T, int D>
+struct TileOffsets {
+  using G = TileGeom<T, D>;
+  unsigned v[G::NL];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int i = 0; i < G::NL; ++i) v[i] = piece_offset(i, lane, 32);
+  }
+  // Offset with rows at or past `rows` replaced by row rows - 1.
+  static __device__ __forceinline__ unsigned piece_offset(int i, int lane, int rows) {
+    const int piece = i * 64 + lane;
+    const int r = piece / G::PR;
+    const int c = (piece % G::PR) ^ (r & (G::PR - 1));
+    return (unsigned)((min(r, rows - 1) * G::PR + c) * 16);
+  }
+};
+
+// Load the `rows` (1..32) rows starting at `first` as one tile; rows past
+// `rows` repeat the last row (read, never used).
+template <typename T, int D>
+__device__ __forceinline__ void issue_tile(const T* first, int rows, const TileOffsets<T, D>& off,
+                                           const uint4* lds_tile, int lane) {
+  using G = TileGeom<T, D>;
+  const unsigned base = (unsigned)(uintptr_t)lds_tile;
+#pragma unroll
+  for (int i = 0; i < G::NL; ++i) {
+    const unsigned o = rows >= 32 ? off.v[i] : TileOffsets<T, D>::piece_offset(i, lane, rows);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(o), "s"(first)
+                 : "memory", "m0");
+  }
+}
+
+// Wait until at most `after` of this wave's tile loads are still in flight
+// (the loads of one wave complete in issue order).  These loads are not seen
+// by the compiler's own wait insertion, so every wait on them is explicit.
+template <int NL>
+__device__ __forceinline__ void wait_tiles(int after) {
+  switch (after) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory"); break;
+  }
+}
+
 // Operand registers of one 32-row tile (a Qwin row block or 32 K rows).
+// Lane half g takes pieces 2 s + g (s < PR / 2) of row lane % 32: for bf16
+// these are the 8-element k-steps of v_mfma_f32_32x32x16_bf16; for fp32 each
+// piece feeds four v_mfma_f32_32x32x2f32 steps, pairing element 8q+e (half 0)
+// with 8q+4+e (half 1).
 template <typename T, int D>
 struct Operands;
 
 template <int D>
 struct Operands<__bf16, D> {
-  static constexpr int NS = D / 16;  // k-steps of v_mfma_f32_32x32x16_bf16
+  static constexpr int NS = D / 16;
   bf16x8 v[NS];
-  // Lane half g takes elements [16 s + 8 g, 16 s + 8 g + 8) of the row.
-  __device__ __forceinline__ void load(const __bf16* __restrict__ row, int g) {
-    const uint4* p = reinterpret_cast<const uint4*>(row);
+  __device__ __forceinline__ void from_tile(const uint4* tile, int n, int g) {
+    constexpr int PR = TileGeom<__bf16, D>::PR;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) v[s] = __builtin_bit_cast(bf16x8, p[2 * s + g]);
+    for (int s = 0; s < NS; ++s) v[s] = __builtin_bit_cast(bf16x8, tile[n * PR + ((2 * s + g) ^ (n & (PR - 1)))]);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -65,14 +133,12 @@ struct Operands<__bf16, D> {
 
 template <int D>
 struct Operands<float, D> {
-  static constexpr int NQ = D / 8;  // 4 k-steps of v_mfma_f32_32x32x2_f32 per float4
+  static constexpr int NQ = D / 8;
   f32x4 v[NQ];
-  // Lane half g takes elements [8 q + 4 g, 8 q + 4 g + 4) of the row; k-step
-  // (q, e) pairs element 8q+e (half 0) with 8q+4+e (half 1).
-  __device__ __forceinline__ void load(const float* __restrict__ row, int g) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(row);
+  __device__ __forceinline__ void from_tile(const uint4* tile, int n, int g) {
+    constexpr int PR = TileGeom<float, D>::PR;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) v[q] = p[2 * q + g];
+    for (int q = 0; q < NQ; ++q) v[q] = __builtin_bit_cast(f32x4, tile[n * PR + ((2 * q + g) ^ (n & (PR - 1)))]);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -102,208 +168,410 @@ __device__ __forceinline__ f32x16 tile_dot(const Operands<float, D>& a, const Op
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Merge (m2, z) with (mo, zo): running maximum in base 2 and the sum of
-// exponentials rescaled to it.
+// Add one logit x to (running maximum m, sum z of exp2(. - m)) with a single
+// exponential: exp2(-|x - m|) rescales whichever side is smaller.
+__device__ __forceinline__ void online_add(float& m, float& z, float x) {
+  const float d = x - m;
+  const float e = exp2_fast(-fabsf(d));
+  z = d > 0.f ? fmaf(z, e, 1.f) : z + e;
+  m = fmaxf(m, x);
+}
+
+// Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
+// exponentials rescaled to it (one exponential: the larger side keeps scale 1).
 __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
-  const float mn = fmaxf(m, mo);
-  z = z * exp2_fast(m - mn) + zo * exp2_fast(mo - mn);
-  m = mn;
+  const float d = mo - m;
+  const float e = exp2_fast(-fabsf(d));
+  z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
+  m = fmaxf(m, mo);
 }
 
-struct Where {
-  int e, h, hl, c;
-};
-
-__device__ __forceinline__ Where locate_chunk(const Launch& a) {
-  Where w;
-  w.e = find_seg<kFieldItem>(a, blockIdx.x);
-  const Seg& s = a.seg[w.e];
-  const int local = blockIdx.x - s.item0;
-  w.hl = local / s.nch;
-  w.c = local - w.hl * s.nch;
-  w.h = s.h0 + w.hl;
-  return w;
-}
-
+// Qwin row block rb (32 rows) is staged through LDS like a K tile, by wave
+// rb, so that no load the compiler tracks is pending in the tile loops.
 template <typename T, int D, int RB>
-__device__ __forceinline__ void load_queries(const Launch& a, const Seg& s, int h, const T* __restrict__ Q,
-                                             int n, int g, Operands<T, D> (&qa)[RB]) {
-  const T* q = Q + ((long long)s.b * a.heads + h) * (long long)a.W * D;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = rb * 32 + n;
-    if (row < a.W)
-      qa[rb].load(q + (long long)row * D, g);
-    else
-      qa[rb].zero();
+__device__ __forceinline__ void issue_queries(const Launch& a, const Seg& s, int h, const T* __restrict__ Q,
+                                              uint4 (*qt)[TileGeom<T, D>::PIECES], const TileOffsets<T, D>& off,
+                                              int wave, int lane) {
+  if (wave < RB) {
+    const T* q = Q + ((long long)s.b * a.heads + h) * (long long)a.W * D + (long long)wave * 32 * D;
+    issue_tile<T, D>(q, min(32, a.W - wave * 32), off, qt[wave], lane);
   }
 }
 
-// Per-chunk row statistics.  Workgroup = kWaves waves over kChunk positions
-// of one (sequence, head); writes, for every window row i < W, the base-2
-// maximum of the visible logits in the chunk and the sum of exp2(x - max).
+// Operands of the staged Qwin; rows past W are zero.
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch a, const T* __restrict__ Q,
+__device__ __forceinline__ void queries_from_lds(const Launch& a, const uint4 (*qt)[TileGeom<T, D>::PIECES], int n,
+                                                 int g, Operands<T, D> (&qa)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qa[rb].from_tile(qt[rb], n, g);
+    if (rb * 32 + n >= a.W) qa[rb].zero();
+  }
+}
+
+// One scoring item: chunk c (kChunk positions) of head h of segment e.  A
+// wave covers kWaveTiles tiles of the chunk starting at pb, of which nt hold
+// positions below the kernel's limit (L for statistics, P for votes).
+template <typename T, int D>
+struct Item {
+  int e, h, c, pb, nt;
+  const T* kh;
+  int L;
+};
+
+template <typename T, int D, bool kVotes>
+__device__ __forceinline__ Item<T, D> locate_item(const Launch& a, const T* __restrict__ K, int item, int wave) {
+  Item<T, D> it;
+  it.e = find_seg<kFieldItem>(a, item);
+  const Seg& s = a.seg[it.e];
+  const int local = item - s.item0;
+  const int hl = local / s.nch;
+  it.c = local - hl * s.nch;
+  it.h = s.h0 + hl;
+  it.L = s.L;
+  it.kh = K + s.kv_off + (long long)it.h * s.L * D;
+  it.pb = it.c * kChunk + wave * (kWaveTiles * 32);
+  const int limit = kVotes ? s.L - a.W : s.L;
+  it.nt = max(0, min(kWaveTiles, (limit - it.pb + 31) / 32));
+  return it;
+}
+
+// Contiguous, balanced range of items of this workgroup.
+__device__ __forceinline__ void item_range(int items, int& lo, int& hi) {
+  lo = (int)((long long)blockIdx.x * items / gridDim.x);
+  hi = (int)((long long)(blockIdx.x + 1) * items / gridDim.x);
+}
+
+// The K tile stream of one wave over all items of its workgroup's range:
+// tile loads run up to RING tiles ahead of the consumer, across item
+// boundaries; buffer = tile count % RING.
+template <typename T, int D, bool kVotes>
+struct WaveStream {
+  using G = TileGeom<T, D>;
+  uint4 (*ring)[G::PIECES];
+  TileOffsets<T, D> off;
+  int issued, done;  // tiles issued / consumed by this wave
+  int item, hi, t;   // issue cursor: item, next tile in it
+  Item<T, D> cur;    // the cursor's item
+  __device__ __forceinline__ void start(const Launch& a, const T* __restrict__ K, int lo, int hi_, int wave,
+                                        int lane) {
+    off.init(lane);
+    issued = done = 0;
+    hi = hi_;
+    item = lo;
+    t = 0;
+    if (item < hi) cur = locate_item<T, D, kVotes>(a, K, item, wave);
+    for (int r = 0; r < G::RING; ++r) issue_next(a, K, wave, lane);
+  }
+  __device__ __forceinline__ void issue_next(const Launch& a, const T* __restrict__ K, int wave, int lane) {
+    while (item < hi && t >= cur.nt) {
+      ++item;
+      t = 0;
+      if (item < hi) cur = locate_item<T, D, kVotes>(a, K, item, wave);
+    }
+    if (item >= hi) return;
+    const int p0 = cur.pb + t * 32;
+    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % G::RING], lane);
+    ++t;
+    ++issued;
+  }
+  // The next tile in stream order has landed; returns its buffer.
+  __device__ __forceinline__ const uint4* wait() {
+    wait_tiles<G::NL>(issued - done - 1);
+    return ring[done % G::RING];
+  }
+  // After the operand reads of the tile (waited for here): reuse its buffer
+  // for the next load.
+  __device__ __forceinline__ void release(const Launch& a, const T* __restrict__ K, int wave, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ++done;
+    issue_next(a, K, wave, lane);
+  }
+};
+
+// Stage Qwin of (segment e, head h) and read it into operand registers.  On
+// entry no wave still reads qt; on exit every wave has its copy.  Waits for
+// all of this wave's loads in flight (a K tile stream drains once here).
+template <typename T, int D, int RB>
+__device__ __forceinline__ void stage_queries(const Launch& a, int e, int h, const T* __restrict__ Q,
+                                              uint4 (*qt)[TileGeom<T, D>::PIECES], const TileOffsets<T, D>& off,
+                                              int wave, int lane, Operands<T, D> (&qa)[RB]) {
+  issue_queries<T, D, RB>(a, a.seg[e], h, Q, qt, off, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  queries_from_lds<T, D, RB>(a, qt, lane & 31, lane >> 5, qa);
+}
+
+// Partial row statistics.  Persistent workgroups of kWaves waves walk a
+// contiguous range of (sequence, head, chunk) items.  Consecutive items of
+// one head form a run; for each window row i < W the run's base-2 maximum of
+// the visible logits and sum of exp2(x - max) are written to the slot of its
+// last chunk, and the other chunks of the run get (kNegBig, 0), which leaves
+// any merge unchanged.
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch a, int items,
+                                                                  const T* __restrict__ Q,
                                                                   const T* __restrict__ K,
                                                                   float* __restrict__ part_m,
                                                                   float* __restrict__ part_z) {
-  const Where w = locate_chunk(a);
-  const Seg& s = a.seg[w.e];
-  const int L = s.L, W = a.W, P = L - W;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using G = TileGeom<T, D>;
+  __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
+  __shared__ uint4 qt[RB][G::PIECES];
+  __shared__ float sm[2][kWaves][RB * 32], sz[2][kWaves][RB * 32];
+  const int W = a.W;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
+  int lo, hi;
+  item_range(items, lo, hi);
+
+  WaveStream<T, D, false> ws;
+  ws.ring = ring[wave];
+  ws.start(a, K, lo, hi, wave, lane);
 
   Operands<T, D> qa[RB];
-  load_queries<T, D, RB>(a, s, w.h, Q, n, g, qa);
-  const T* kb = K + s.kv_off + (long long)w.h * L * D;
-
-  float m[RB][16], z[RB][16];
+  float m[RB][16], z[RB][16];  // this lane's running statistics of the current run
+  int runs = 0;
+  for (int item = lo; item < hi; ++item) {
+    const Item<T, D> it = locate_item<T, D, false>(a, K, item, wave);
+    const Seg& s = a.seg[it.e];
+    const int L = s.L, P = L - W;
+    const bool first = item == lo || find_seg<kFieldItem>(a, item - 1) != it.e ||
+                       (item - 1 - s.item0) / s.nch != it.h - s.h0;
+    const bool last = item + 1 == hi || find_seg<kFieldItem>(a, item + 1) != it.e ||
+                      (item + 1 - s.item0) / s.nch != it.h - s.h0;
+    if (first) {
+      // qt is free: every wave read it before the barrier that ended the
+      // previous staging, and has since passed that run's final barrier.
+      stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      m[rb][r] = kNegBig;
-      z[rb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          m[rb][r] = kNegBig;
+          z[rb][r] = 0.f;
+        }
     }
 
-  const int p_begin = w.c * kChunk + wave * (kWaveTiles * 32);
-  for (int t = 0; t < kWaveTiles; ++t) {
-    const int p0 = p_begin + t * 32;
-    if (p0 >= L) break;
-    const int j = p0 + n;
-    Operands<T, D> kt;
-    kt.load(kb + (long long)min(j, L - 1) * D, g);
+    for (int t = 0; t < it.nt; ++t) {
+      const int p0 = it.pb + t * 32;
+      const int j = p0 + n;
+      Operands<T, D> kt;
+      kt.from_tile(ws.wait(), n, g);
+      ws.release(a, K, wave, lane);  // the tile is in registers: refill its buffer now
+      // Rows i >= W hold zero queries and are never written, so only the
+      // causal bound j <= P + i masks, and only in tiles reaching past P.
+      const bool full = p0 + 31 <= P;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const f32x16 acc = tile_dot<D>(qa[rb], kt);
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x16 acc = tile_dot<D>(qa[rb], kt);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = rb * 32 + acc_row(r, g);
-        const bool visible = (j < L) && (i < W) && (j <= P + i);
-        const float x = visible ? acc[r] * a.scale2 : -INFINITY;
-        const float mn = fmaxf(m[rb][r], x);
-        z[rb][r] = z[rb][r] * exp2_fast(m[rb][r] - mn) + exp2_fast(x - mn);
-        m[rb][r] = mn;
+        for (int r = 0; r < 16; ++r) {
+          const int i = rb * 32 + acc_row(r, g);
+          float x = acc[r] * a.scale2;
+          if (!full && j > P + i) x = -INFINITY;
+          online_add(m[rb][r], z[rb][r], x);
+        }
       }
     }
-  }
 
-  // Across the 32 lanes of each half (same rows, different positions).
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) {
-        const float mo = __shfl_xor(m[rb][r], off);
-        const float zo = __shfl_xor(z[rb][r], off);
-        lse_merge(m[rb][r], z[rb][r], mo, zo);
+    const long long slot = (s.part_base + (long long)it.h * s.nch + it.c) * W;
+    if (!last) {
+      // The run's statistics go to its last chunk; the others hold the
+      // neutral element of the merge.
+      if ((int)threadIdx.x < W) {
+        part_m[slot + threadIdx.x] = kNegBig;
+        part_z[slot + threadIdx.x] = 0.f;
       }
+      continue;
+    }
 
-  __shared__ float sm[kWaves][RB * 32], sz[kWaves][RB * 32];
-  if (n == 0) {
+    // Across the 32 lanes of each half (same rows, different positions).
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = rb * 32 + acc_row(r, g);
-        sm[wave][i] = m[rb][r];
-        sz[wave][i] = z[rb][r];
-      }
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < W) {
-    const int i = threadIdx.x;
-    float mm = sm[0][i], zz = sz[0][i];
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
-    for (int v = 1; v < kWaves; ++v) lse_merge(mm, zz, sm[v][i], sz[v][i]);
-    const long long slot = (s.part_base + (long long)w.h * s.nch + w.c) * W + i;
-    part_m[slot] = mm;
-    part_z[slot] = zz;
+        for (int off = 16; off >= 1; off >>= 1) {
+          const float mo = __shfl_xor(m[rb][r], off);
+          const float zo = __shfl_xor(z[rb][r], off);
+          lse_merge(m[rb][r], z[rb][r], mo, zo);
+        }
+
+    // Run k uses buffer k & 1: the merge of run k happens before any wave
+    // passes the barrier of run k + 1.
+    const int pbuf = runs++ & 1;
+    if (n == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = rb * 32 + acc_row(r, g);
+          sm[pbuf][wave][i] = m[rb][r];
+          sz[pbuf][wave][i] = z[rb][r];
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < W) {
+      const int i = threadIdx.x;
+      float mm = sm[pbuf][0][i], zz = sz[pbuf][0][i];
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) lse_merge(mm, zz, sm[pbuf][v][i], sz[pbuf][v][i]);
+      part_m[slot + i] = mm;
+      part_z[slot + i] = zz;
+    }
   }
 }
 
-// Votes of the prefix positions of one chunk.  Merges the head's partial row
-// statistics, recomputes the chunk's logits and sums the softmax
-// probabilities over the window rows.
-template <typename T, int D, int RB>
-__global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
-    const Launch a, const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ part_m,
-    const float* __restrict__ part_z, float* __restrict__ votes, float* __restrict__ row_stats) {
-  const Where w = locate_chunk(a);
-  const Seg& s = a.seg[w.e];
-  const int L = s.L, W = a.W, P = L - W;
-  if (w.c * kChunk >= P) return;  // chunk holds window positions only
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, g = lane >> 5;
-
-  __shared__ float s_m[RB * 32], s_iz[RB * 32];
-  if ((int)threadIdx.x < RB * 32) {
-    const int i = threadIdx.x;
-    // Rows past W: zero queries give x = 0, so (m, 1/Z) = (0, 0) drops them.
-    float mm = 0.f, iz = 0.f;
-    if (i < W) {
-      const long long base = (s.part_base + (long long)w.h * s.nch) * W + i;
-      mm = kNegBig;
-      for (int c = 0; c < s.nch; ++c) mm = fmaxf(mm, part_m[base + (long long)c * W]);
-      float zz = 0.f;
-      for (int c = 0; c < s.nch; ++c) {
-        const long long k = base + (long long)c * W;
-        zz += part_z[k] * exp2_fast(part_m[k] - mm);
+// Final (max, 1/sum) of every window row of head h from its nch partials,
+// into s_m / s_iz (rows W .. RB*32-1 get (0, 0): with zero queries their
+// logits are 0, so they add nothing).  Every thread of the workgroup takes
+// part: thread t < G*W (G = threads / W groups) merges row t % W over chunks
+// t / W, t / W + G, ...; the G results per row are then merged through LDS.
+template <int RBW>
+__device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, int h,
+                                               const float* __restrict__ part_m, const float* __restrict__ part_z,
+                                               float* __restrict__ row_stats, bool write_stats, float* s_gm,
+                                               float* s_gz, float* s_m, float* s_iz) {
+  const int W = a.W, t = threadIdx.x;
+  const int G = (kWaves * 64) / W;
+  const long long base = (s.part_base + (long long)h * s.nch) * W;
+  if (t < G * W) {
+    const int i = t % W, grp = t / W;
+    float mm = kNegBig, zz = 0.f;
+    int c = grp;
+    // Batches of four independent loads.
+    for (; c + 3 * G < s.nch; c += 4 * G) {
+      float pm[4], pz[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pm[u] = part_m[base + (long long)(c + u * G) * W + i];
+        pz[u] = part_z[base + (long long)(c + u * G) * W + i];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_merge(mm, zz, pm[u], pz[u]);
+    }
+    for (; c < s.nch; c += G) lse_merge(mm, zz, part_m[base + (long long)c * W + i], part_z[base + (long long)c * W + i]);
+    s_gm[t] = mm;
+    s_gz[t] = zz;
+  }
+  __syncthreads();
+  if (t < RBW) {
+    float mm = 0.f, iz = 0.f;
+    if (t < W) {
+      float zz = 0.f;
+      mm = kNegBig;
+      for (int grp = 0; grp < G; ++grp) lse_merge(mm, zz, s_gm[grp * W + t], s_gz[grp * W + t]);
       iz = 1.f / zz;
-      if (row_stats != nullptr && w.c == 0) {
-        float* rs = row_stats + (((long long)s.b * a.heads + w.h) * W + i) * 2;
+      if (row_stats != nullptr && write_stats) {
+        float* rs = row_stats + (((long long)s.b * a.heads + h) * W + t) * 2;
         rs[0] = mm * kLn2;
         rs[1] = zz;
       }
     }
-    s_m[i] = mm;
-    s_iz[i] = iz;
+    s_m[t] = mm;
+    s_iz[t] = iz;
   }
   __syncthreads();
+}
+
+// Votes of prefix positions.  Persistent workgroups walk a contiguous range of
+// items; at each new head they merge its partial row statistics, then
+// recompute each chunk's logits and sum the softmax probabilities over the
+// window rows.
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
+    const Launch a, int items, const T* __restrict__ Q, const T* __restrict__ K,
+    const float* __restrict__ part_m, const float* __restrict__ part_z, float* __restrict__ votes,
+    float* __restrict__ row_stats) {
+  using G = TileGeom<T, D>;
+  __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
+  __shared__ uint4 qt[RB][G::PIECES];
+  __shared__ float s_m[RB * 32], s_iz[RB * 32];
+  __shared__ float s_gm[kWaves * 64], s_gz[kWaves * 64];
+  const int W = a.W;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  int lo, hi;
+  item_range(items, lo, hi);
+
+  WaveStream<T, D, true> ws;
+  ws.ring = ring[wave];
+  ws.start(a, K, lo, hi, wave, lane);
 
   Operands<T, D> qa[RB];
-  load_queries<T, D, RB>(a, s, w.h, Q, n, g, qa);
   float mr[RB][16], izr[RB][16];
+  int qe = -1, qh = -1;
+  for (int item = lo; item < hi; ++item) {
+    const Item<T, D> it = locate_item<T, D, true>(a, K, item, wave);
+    const Seg& s = a.seg[it.e];
+    const int L = s.L, P = L - W;
+    if (it.c * kChunk >= P) continue;  // chunk holds window positions only
+    if (it.e != qe || it.h != qh) {
+      stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
+      qe = it.e;
+      qh = it.h;
+      // The run holding chunk 0 of the head starts there: its workgroup
+      // alone writes the row statistics.
+      merge_partials<RB * 32>(a, s, it.h, part_m, part_z, row_stats, it.c == 0, s_gm, s_gz, s_m, s_iz);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = rb * 32 + acc_row(r, g);
-      mr[rb][r] = s_m[i];
-      izr[rb][r] = s_iz[i];
+        for (int r = 0; r < 16; ++r) {
+          const int i = rb * 32 + acc_row(r, g);
+          mr[rb][r] = s_m[i];
+          izr[rb][r] = s_iz[i];
+        }
+      // Nobody reads qt or s_m again before the next staging rewrites them.
+      __syncthreads();
     }
 
-  const T* kb = K + s.kv_off + (long long)w.h * L * D;
-  float* vout = votes + s.vote_off + (long long)w.h * s.vote_ld;
-  const int p_begin = w.c * kChunk + wave * (kWaveTiles * 32);
-  for (int t = 0; t < kWaveTiles; ++t) {
-    const int p0 = p_begin + t * 32;
-    if (p0 >= P) break;
-    const int j = p0 + n;
-    Operands<T, D> kt;
-    kt.load(kb + (long long)min(j, L - 1) * D, g);
-    float tot = 0.f;
+    float* vout = votes + s.vote_off + (long long)it.h * s.vote_ld;
+    for (int t = 0; t < it.nt; ++t) {
+      const int j = it.pb + t * 32 + n;
+      Operands<T, D> kt;
+      kt.from_tile(ws.wait(), n, g);
+      ws.release(a, K, wave, lane);  // the tile is in registers: refill its buffer now
+      float tot = 0.f;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const f32x16 acc = tile_dot<D>(qa[rb], kt);
-      float part = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        const f32x16 acc = tile_dot<D>(qa[rb], kt);
+        float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part += exp2_fast(acc[r] * a.scale2 - mr[rb][r]) * izr[rb][r];
-      tot += part;
+        for (int r = 0; r < 16; ++r) part += exp2_fast(acc[r] * a.scale2 - mr[rb][r]) * izr[rb][r];
+        tot += part;
+      }
+      const float other = __shfl_xor(tot, 32);
+      // Same expression for every position: (half 0 rows) + (half 1 rows).
+      const float v = g == 0 ? tot + other : other + tot;
+      if (g == 0 && j < P) vout[j] = v;
     }
-    const float other = __shfl_xor(tot, 32);
-    // Same expression for every position: (half 0 rows) + (half 1 rows).
-    const float v = g == 0 ? tot + other : other + tot;
-    if (g == 0 && j < P) vout[j] = v;
   }
+}
+
+// Persistent grid: as many workgroups as can be resident at once (cached per
+// kernel variant and device), never more than there are items.
+template <typename Kern>
+static int resident_grid(Kern kern, int items) {
+  static int per_cu[64] = {};
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return items;
+  if (per_cu[dev] == 0) {
+    int n = 0, c = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kWaves * 64, 0) != hipSuccess || n < 1) n = 1;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 1;
+    cus[dev] = c;
+    per_cu[dev] = n;
+  }
+  const long long slots = (long long)per_cu[dev] * cus[dev];
+  return (int)(items < slots ? items : slots);
 }
 
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
                           hipStream_t st) {
-  hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(items), dim3(kWaves * 64), 0, st, a,
+  const int grid = resident_grid(window_stats_kernel<T, D, RB>, items);
+  hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
                      (const T*)Q, (const T*)K, pm, pz);
   return hipGetLastError();
 }
@@ -311,7 +579,8 @@ static hipError_t stats_t(const Launch& a, int items, const void* Q, const void*
 template <typename T, int D, int RB>
 static hipError_t votes_t(const Launch& a, int items, const void* Q, const void* K, const float* pm,
                           const float* pz, float* votes, float* rs, hipStream_t st) {
-  hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(items), dim3(kWaves * 64), 0, st, a,
+  const int grid = resident_grid(window_votes_kernel<T, D, RB>, items);
+  hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
                      (const T*)Q, (const T*)K, pm, pz, votes, rs);
   return hipGetLastError();
 }
