@@ -46,13 +46,13 @@ def kernel_alg_bytes(name, w, nch):
         return H * L * D * e + q + H * nch * W * 8
     if name == "window_votes":      # prefix K, Qwin, partials, votes out
         return H * P * D * e + q + H * nch * W * 8 + H * P * 4
-    if name == "pool":
+    if name == "pool":              # votes in, pooled out
         return H * P * 8
-    if name == "topk":
-        return H * P * 4 + H * C * 4
-    if name == "gather":            # read and write the kept K and V rows
-        return 4 * H * C * D * e + H * C * 4
-    if name == "fill":              # per-head counters cleared for the exchange
+    if name == "threshold":         # pooled scores read once, histograms, segment counts
+        return H * P * 4 + H * 2048 * 4
+    if name == "emit":              # pooled scores, kept K and V rows read and written, indices
+        return H * P * 4 + 4 * H * C * D * e + H * C * 4
+    if name == "fill":              # per-head exchange records cleared
         return H * 64 + 256
     return None
 

@@ -81,8 +81,13 @@ struct Plan {
   int fS = 0;                 // single-read scoring: positions per workgroup per round
   long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots, either path
   long long vote_elems = 0;   // heads * sum of P_b
-  size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_ctr = 0, off_status = 0, off_hist = 0, bytes = 0;
+  size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_cut = 0, off_segcnt = 0, off_ctr = 0,
+         off_status = 0, off_hist = 0, bytes = 0;
 };
+
+// Selection workspace per (sequence, head) row: threshold and segment counts.
+constexpr size_t kCutBytes = 2 * sizeof(uint32_t);
+constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
 
 // Process-wide options.
 int g_scoring = KVSEL_SCORING_AUTO;
@@ -137,6 +142,10 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)p.vote_elems * sizeof(float));
   p.off_pooled = off;
   off = align256(off + (size_t)p.vote_elems * sizeof(float));
+  p.off_cut = off;  // selection threshold per (sequence, head)
+  off = align256(off + (size_t)B * heads * kCutBytes);
+  p.off_segcnt = off;  // per-segment counts above / on the threshold
+  off = align256(off + (size_t)B * heads * kSegCntBytes);
   p.off_ctr = off;  // single-read scoring: one exchange record per (sequence, head)
   off = align256(off + (size_t)B * heads * fused_exchange_bytes());
   p.off_status = off;
@@ -210,7 +219,8 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   float* pooled = pooled_opt ? pooled_opt : (float*)(ws + p.off_pooled);
   unsigned* counters = (unsigned*)(ws + p.off_ctr);
   unsigned* status = (unsigned*)(ws + p.off_status);
-  const int rpb = gather_rows_per_block(p.D, p.dtype);
+  uint32_t* cut = (uint32_t*)(ws + p.off_cut);
+  uint32_t* segcnt = (uint32_t*)(ws + p.off_segcnt);
 
   // Single-read scoring needs every head of a round co-resident: each prompt
   // must fit one round of the grid (ceil(L / S) <= grid).
@@ -227,8 +237,9 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   // kernels currently outrun the single-read kernel, so AUTO picks two-pass.
   const bool use_fused = fused_ok && g_scoring == KVSEL_SCORING_SINGLE_READ;
   uint32_t* hist = (uint32_t*)(ws + p.off_hist);
-  {
-    // Exchange records, status word and histograms start at zero.
+  if (use_fused) {
+    // Exchange records, status word and histograms start at zero (on the
+    // two-pass path the statistics kernel clears the histograms).
     hipError_t e = timed("fill", st, [&] {
       return launch_fill_u32(counters, (long long)(p.bytes - p.off_ctr) / 4, 0u, st);
     });
@@ -241,7 +252,7 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     a.n = nb;
     a.S = p.fS;
     a.rounds = 0;
-    int items = 0, rows = 0, gitems = 0, maxP = 0;
+    int items = 0, rows = 0, maxP = 0, maxN = 0;
     for (int k = 0; k < nb; ++k) {
       const int b = b0 + k;
       Seg& s = a.seg[k];
@@ -254,8 +265,8 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       s.nch = p.nch[b];
       s.item0 = items;
       s.row0 = rows;
-      s.gitem0 = gitems;
-      s.gblk = (s.nout + rpb - 1) / rpb;
+      s.gitem0 = 0;
+      s.gblk = 0;
       s.idx_ld = s.C;
       s.out_ld = s.C;
       s.vote_ld = s.L - p.W;
@@ -271,33 +282,37 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       a.rounds += s.fnr;
       items += s.nh * s.nch;
       rows += s.nh;
-      gitems += s.nh * s.gblk;
       if (s.L >= s.C) maxP = std::max(maxP, s.L - p.W);
+      maxN = std::max(maxN, s.L >= s.C ? s.L - p.W : s.L);
     }
+    a.seg_size = selection_seg_size(maxN);
+    uint32_t* ghist = hist + (long long)b0 * p.heads * 2048;
+    uint32_t* gcut = (uint32_t*)((char*)cut + (size_t)b0 * p.heads * kCutBytes);
+    uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
     if (items > 0 && use_fused) {
       e = timed("window_fused", st,
                 [&] { return launch_fused_scoring(a, Q, K, counters, status, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
     } else if (items > 0) {
-      e = timed("window_stats", st, [&] { return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, st); });
+      e = timed("window_stats", st, [&] {
+        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, st);
+      });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     }
     if (items > 0) {
-      e = timed("pool", st, [&] {
-        return launch_pool(a, rows, maxP, votes, pooled, hist + (long long)b0 * p.heads * 2048, st);
-      });
+      e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, ghist, st); });
       if (e != hipSuccess) return device_error(e, "pool launch");
+      e = timed("threshold", st, [&] { return launch_threshold(a, rows, pooled, ghist, gcut, gseg, st); });
+      if (e != hipSuccess) return device_error(e, "threshold launch");
     }
-    e = timed("topk", st, [&] {
-      return launch_topk(a, rows, pooled, hist + (long long)b0 * p.heads * 2048, indices, st);
+    e = timed("emit", st, [&] {
+      return launch_emit(a, rows, maxN, p.dtype, pooled, gcut, gseg, indices, K, V, K_out, V_out, st);
     });
-    if (e != hipSuccess) return device_error(e, "topk launch");
-    e = timed("gather", st, [&] { return launch_gather(a, gitems, p.dtype, K, V, indices, K_out, V_out, st); });
-    if (e != hipSuccess) return device_error(e, "gather launch");
+    if (e != hipSuccess) return device_error(e, "emit launch");
   }
   return ok();
 }
@@ -369,13 +384,18 @@ int kvsel_select(const void* Qwin, const void* K, const void* V, int L, int W, i
                              row_stats_opt, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
 }
 
+static size_t topk_workspace(int rows) {
+  return align256((size_t)rows * 2048 * 4) + align256((size_t)rows * kCutBytes) +
+         align256((size_t)rows * kSegCntBytes);
+}
+
 size_t kvsel_topk_workspace_bytes(int rows, int n) {
   if (rows < 1 || n < 1) {
     fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
     return 0;
   }
   ok();
-  return align256((size_t)rows * 2048 * 4);
+  return topk_workspace(rows);
 }
 
 int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out, void* workspace,
@@ -386,7 +406,7 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   if (ld_out < count) return fail(KVSEL_EINVAL, "ld_out %d is smaller than count %d", ld_out, count);
   if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
-  const size_t need = align256((size_t)rows * 2048 * 4);
+  const size_t need = topk_workspace(rows);
   if (workspace_bytes < need)
     return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
   Launch a{};
@@ -400,14 +420,21 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   s.nh = rows;
   s.idx_ld = ld_out;
   s.vote_ld = n;
+  a.seg_size = selection_seg_size(n);
   hipStream_t st = (hipStream_t)stream;
   uint32_t* hist = (uint32_t*)workspace;
+  uint32_t* cut = (uint32_t*)((char*)workspace + align256((size_t)rows * 2048 * 4));
+  uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
   hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
   if (e != hipSuccess) return device_error(e, "fill launch");
   e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
   if (e != hipSuccess) return device_error(e, "histogram launch");
-  e = timed("topk", st, [&] { return launch_topk(a, rows, scores, hist, out, st); });
-  if (e != hipSuccess) return device_error(e, "topk launch");
+  e = timed("threshold", st, [&] { return launch_threshold(a, rows, scores, hist, cut, segcnt, st); });
+  if (e != hipSuccess) return device_error(e, "threshold launch");
+  e = timed("emit", st, [&] {
+    return launch_emit(a, rows, n, 0, scores, cut, segcnt, out, nullptr, nullptr, nullptr, nullptr, st);
+  });
+  if (e != hipSuccess) return device_error(e, "emit launch");
   return ok();
 }
 

@@ -54,6 +54,7 @@ struct Launch {
   float scale2;   // log2(e) / sqrt(D)
   int S;          // single-read scoring: positions per workgroup per round
   int rounds;     // single-read scoring: rounds over all segments
+  int seg_size;   // selection: positions per emit workgroup (multiple of 2048)
   Seg seg[kMaxSegs];
 };
 
@@ -71,8 +72,11 @@ __device__ __forceinline__ int find_seg(const Launch& a, int item) {
 enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
 
 // Host-side launchers (return hipSuccess or the launch error).
+// window_stats also zeroes zero_words words at zero (the selection's
+// histograms), which the kernels after it accumulate into.
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               float* part_m, float* part_z, hipStream_t st);
+                               float* part_m, float* part_z, uint32_t* zero, long long zero_words,
+                               hipStream_t st);
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                const float* part_m, const float* part_z, float* votes,
                                float* row_stats, hipStream_t st);
@@ -80,9 +84,21 @@ hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void
 // first-digit histogram of each row added into hist[row][2048] (nullptr: none).
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
                        uint32_t* hist, hipStream_t st);
-// Top-(C-W) per row given the first-digit histograms.
-hipError_t launch_topk(const Launch& a, int rows, const float* scores, const uint32_t* hist,
-                       int32_t* indices, hipStream_t st);
+// Top-(C-W) per row given the first-digit histograms, in two launches.
+// launch_threshold finds each row's threshold score and how many positions
+// of each segment (seg_size positions) lie above it or on it, into cut
+// (2 words per row) and segcnt (2 * kMaxSegRow words per row).
+// launch_emit writes every row's picks ascending, then the window positions
+// (a.window), and copies their K and V rows when K != nullptr (dtype, D give
+// the row size); bypass rows (L < C) keep every position.
+constexpr int kSegUnit = 2048;    // positions per emit pass
+constexpr int kMaxSegRow = 512;   // emit segments per row
+int selection_seg_size(long long max_positions);
+hipError_t launch_threshold(const Launch& a, int rows, const float* scores, const uint32_t* hist, uint32_t* cut,
+                            uint32_t* segcnt, hipStream_t st);
+hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, const float* scores,
+                       const uint32_t* cut, const uint32_t* segcnt, int32_t* indices, const void* K, const void* V,
+                       void* K_out, void* V_out, hipStream_t st);
 // Single-read scoring (cooperative persistent kernel).  fused_positions()
 // gives S for the kernel variant, fused_grid() the co-resident grid (0 if the
 // variant cannot run); launch_fused_scoring() returns hipErrorNotSupported

@@ -313,7 +313,9 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
                                                                   const T* __restrict__ Q,
                                                                   const T* __restrict__ K,
                                                                   float* __restrict__ part_m,
-                                                                  float* __restrict__ part_z) {
+                                                                  float* __restrict__ part_z,
+                                                                  uint32_t* __restrict__ zero,
+                                                                  long long zero_words) {
   using G = TileGeom<T, D>;
   __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
@@ -327,6 +329,11 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
   WaveStream<T, D, false> ws;
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
+
+  // Side duty: clear the histograms of the selection that follows.
+  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < zero_words;
+       q += (long long)gridDim.x * blockDim.x)
+    zero[q] = 0u;
 
   Operands<T, D> qa[RB];
   float m[RB][16], z[RB][16];  // this lane's running statistics of the current run
@@ -569,10 +576,10 @@ static int resident_grid(Kern kern, int items) {
 
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
-                          hipStream_t st) {
+                          uint32_t* zero, long long zero_words, hipStream_t st) {
   const int grid = resident_grid(window_stats_kernel<T, D, RB>, items);
   hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz);
+                     (const T*)Q, (const T*)K, pm, pz, zero, zero_words);
   return hipGetLastError();
 }
 
@@ -613,8 +620,9 @@ static hipError_t votes_t(const Launch& a, int items, const void* Q, const void*
   } while (0)
 
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               float* part_m, float* part_z, hipStream_t st) {
-  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, st);
+                               float* part_m, float* part_z, uint32_t* zero, long long zero_words,
+                               hipStream_t st) {
+  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, zero, zero_words, st);
 }
 
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,

@@ -19,9 +19,11 @@
 // score and how many tau-equal positions are still needed.  The first digit's
 // histogram is built by the pooling kernel across many workgroups; one
 // 1024-thread workgroup per (sequence, head) row then gathers the positions
-// of the boundary digit into LDS and finishes the select there.  A single
-// scan of packed (greater, equal) counts over the row in index order writes
-// the picks in ascending order, the lowest tau-equal indices first.
+// of the boundary digit into LDS, finishes the select there and counts, per
+// segment of the row, the positions above tau and on tau.  An emit workgroup
+// per segment then knows how many picks precede it: it scans its positions
+// in index order, writes its picks (the lowest tau-equal indices first) at
+// their final slots, and copies their K and V rows.
 
 #include "kvsel_internal.h"
 
@@ -33,10 +35,11 @@
 
 namespace kvsel {
 
-// Inclusive scan over the 1024 threads of the block; `total` gets the sum.
-__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* sh, uint32_t& total) {
+// Inclusive scan over the NT threads of the block; `total` gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  constexpr int kWavesPerBlock = kTopkThreads / 64;
+  constexpr int kWavesPerBlock = NT / 64;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t o = __shfl_up(v, off);
@@ -86,7 +89,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_
   uint32_t local = 0;
   for (int u = 0; u < per; ++u) local += hist[nb - 1 - (tid * per + u)];
   uint32_t total;
-  const uint32_t incl = block_scan_1024(local, sh, total);
+  const uint32_t incl = block_scan<kTopkThreads>(local, sh, total);
   const uint32_t excl = incl - local;
   if (excl < need && need <= incl) {
     uint32_t cum = excl;
@@ -103,56 +106,59 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_
   __syncthreads();
 }
 
-// Select kernel: one 1024-thread workgroup per (sequence, head) row.  The
-// first digit (bits 31..21) comes from the histogram the pooling kernel built;
-// the positions in that digit are gathered into LDS and the remaining 21 bits
-// are resolved there (or, when the digit holds more than kCand positions, by
-// passes over the row).  A final in-order pass writes the picks ascending.
+// Threshold kernel: one 1024-thread workgroup per (sequence, head) row.  The
+// first digit (bits 31..21) comes from the histogram the pooling kernel built.
+// One pass over the row counts, per segment, the positions whose digit is
+// above it and gathers the positions of that digit (key and index) into LDS,
+// where the remaining 21 bits are resolved; when the digit holds more than
+// kCand positions the remaining digits read the row instead.  The digit's
+// positions above and on tau are then added to the segment counts.
 constexpr int kCand = 16384;
-constexpr int kPickBuf = 8192;
 constexpr int kPoolSpan = 8;
 constexpr int kMaxPoolRadius = 31;  // pooling width up to 63
 
-__global__ __launch_bounds__(kTopkThreads) void select_kernel(const Launch a, const float* __restrict__ scores,
-                                                              const uint32_t* __restrict__ ghist,
-                                                              int32_t* __restrict__ indices) {
+__global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a, const float* __restrict__ scores,
+                                                                 const uint32_t* __restrict__ ghist,
+                                                                 uint32_t* __restrict__ cut,
+                                                                 uint32_t* __restrict__ segcnt) {
   const int row = blockIdx.x;
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  if (s.L < s.C) return;  // bypass: every position is kept
   const int h = s.h0 + (row - s.row0);
-  const int tid = threadIdx.x;
-  int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
-  const int L = s.L;
-  if (L < s.C) {  // bypass: keep the whole prompt
-    for (int j = tid; j < L; j += kTopkThreads) out[j] = j;
-    return;
-  }
+  const int tid = threadIdx.x, lane = tid & 63;
   const int W = a.window ? a.W : 0;
-  const int P = L - W;
+  const int P = s.L - W;
   const uint32_t count = (uint32_t)(s.C - W);
   const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
+  const int segsz = a.seg_size;
+  const int nseg = (P + segsz - 1) / segsz;
 
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t cand[kCand];
-  __shared__ int32_t picks[kPickBuf];  // picks collected here, written out at the end
+  __shared__ uint32_t cand_key[kCand];
+  __shared__ int32_t cand_pos[kCand];
+  __shared__ uint32_t sgt[kMaxSegRow], seq[kMaxSegRow];
   __shared__ uint32_t sh[32];
   __shared__ uint32_t s_digit, s_need, s_ncand;
 
   KVSEL_SELECT_MARK(0);
   const uint32_t* gh = ghist + (long long)row * 2048;
   for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = gh[d];
+  for (int q = tid; q < nseg; q += kTopkThreads) {
+    sgt[q] = 0u;
+    seq[q] = 0u;
+  }
   if (tid == 0) s_ncand = 0;
   __syncthreads();
   pick_digit(hist, 2048, count, sh, &s_digit, &s_need);
   const uint32_t d1 = s_digit;
   uint32_t need = s_need;
-  const uint32_t in_d1 = hist[d1];
+  const bool in_lds = hist[d1] <= (uint32_t)kCand;
   __syncthreads();
 
-  // Gather the keys of digit d1 into LDS when they fit (any order: only the
-  // threshold is needed); otherwise the remaining digits read the row.
+  // The 64 positions a wave reads at once are consecutive and segments are
+  // multiples of 64 long, so each wave's counts go to one segment.
   KVSEL_SELECT_MARK(1);
-  const bool in_lds = in_d1 <= (uint32_t)kCand;
-  if (in_lds) {
+  {
     constexpr int U = 16;  // independent loads in flight per thread
     for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
       uint32_t kk[U];
@@ -164,10 +170,19 @@ __global__ __launch_bounds__(kTopkThreads) void select_kernel(const Launch a, co
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * kTopkThreads + tid;
-        const bool hit = j < P && (kk[u] >> 21) == d1;
-        uint32_t slot;
-        wave_append(hit, &s_ncand, slot);
-        if (hit && slot < (uint32_t)kCand) cand[slot] = kk[u];
+        const int jw = j - lane;
+        const uint32_t d = kk[u] >> 21;
+        const unsigned long long above = __ballot(j < P && d > d1);
+        if (above != 0 && lane == 0) atomicAdd(&sgt[jw / segsz], (uint32_t)__popcll(above));
+        if (in_lds) {
+          const bool hit = j < P && d == d1;
+          uint32_t slot;
+          wave_append(hit, &s_ncand, slot);
+          if (hit && slot < (uint32_t)kCand) {
+            cand_key[slot] = kk[u];
+            cand_pos[slot] = j;
+          }
+        }
       }
     }
     __syncthreads();
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(kTopkThreads) void select_kernel(const Launch a, co
     for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = 0u;
     __syncthreads();
     for (uint32_t i = tid; i < n_src; i += kTopkThreads) {
-      const uint32_t k = in_lds ? cand[i] : key[i];
+      const uint32_t k = in_lds ? cand_key[i] : key[i];
       if ((k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
     }
     __syncthreads();
@@ -195,89 +210,197 @@ __global__ __launch_bounds__(kTopkThreads) void select_kernel(const Launch a, co
   const uint32_t tau = prefix;
   KVSEL_SELECT_MARK(3);
 
-  // In-order pass: every score above tau, then the lowest-index need_eq
-  // scores equal to tau, written ascending.
-  // The candidate buffer is free again: it stages a tile of scores at a
-  // time, from which each thread scans kPer consecutive ones (rows of
-  // kPer + 1 words in LDS, so the scans are conflict-free).  The next tile's
-  // coalesced loads are issued before the current tile is processed.
-  const uint32_t need_eq = need;
-  const bool buffered = count <= (uint32_t)kPickBuf;  // else picks go straight to memory
-  uint32_t gt_run = 0, eq_run = 0;
-  constexpr int kPer = 8;
-  constexpr int kTile = kPer * kTopkThreads;
-  static_assert((kPer + 1) * kTopkThreads <= kCand, "staging tile exceeds the candidate buffer");
-  uint32_t nxt[kPer];
+  // Positions of digit d1 above tau and on tau, per segment.
+  if (in_lds) {
+    for (uint32_t i = tid; i < n_src; i += kTopkThreads) {
+      const uint32_t k = cand_key[i];
+      const int q = cand_pos[i] / segsz;
+      if (k > tau)
+        atomicAdd(&sgt[q], 1u);
+      else if (k == tau)
+        atomicAdd(&seq[q], 1u);
+    }
+  } else {
+    constexpr int U = 8;
+    for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
+      uint32_t kk[U];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int j = u * kTopkThreads + tid;
-    nxt[u] = j < P ? key[j] : 0u;
-  }
-  for (int base = 0; base < P; base += kTile) {
-    uint32_t cur[kPer];
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads + tid;
+        kk[u] = j < P ? key[j] : 0u;
+      }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) cur[u] = nxt[u];
-    if (base + kTile < P) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int j = base + kTile + u * kTopkThreads + tid;
-        nxt[u] = j < P ? key[j] : 0u;
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kTopkThreads + tid;
+        const int jw = j - lane;
+        const bool in = j < P && (kk[u] >> 21) == d1;
+        const unsigned long long gt = __ballot(in && kk[u] > tau), eq = __ballot(in && kk[u] == tau);
+        if (lane == 0) {
+          if (gt) atomicAdd(&sgt[jw / segsz], (uint32_t)__popcll(gt));
+          if (eq) atomicAdd(&seq[jw / segsz], (uint32_t)__popcll(eq));
+        }
       }
     }
-    __syncthreads();  // previous tile fully consumed
+  }
+  __syncthreads();
+  uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
+  for (int q = tid; q < nseg; q += kTopkThreads) {
+    sc[q] = sgt[q];
+    sc[kMaxSegRow + q] = seq[q];
+  }
+  if (tid == 0) {
+    cut[2 * row] = tau;
+    cut[2 * row + 1] = need;
+  }
+  KVSEL_SELECT_MARK(4);
+}
+
+// Emit kernel: workgroup (segment, row).  Output slots [dst0, dst0 + n) get
+// the positions src[0..n) and, with RU > 0, their K and V rows (RU 16-byte
+// pieces per row, consecutive threads on consecutive pieces).
+constexpr int kEmitThreads = 256;
+constexpr int kEmitPer = kSegUnit / kEmitThreads;
+
+template <int RU>
+__device__ __forceinline__ void emit_rows(int n, int dst0, const int32_t* src, int32_t* out, long long in_row0,
+                                          long long out_row0, const uint4* __restrict__ K,
+                                          const uint4* __restrict__ V, uint4* __restrict__ Ko,
+                                          uint4* __restrict__ Vo) {
+  for (int i = threadIdx.x; i < n; i += kEmitThreads) out[dst0 + i] = src[i];
+  if (RU > 0) {
+    constexpr int kFly = 4;  // pieces of K and of V in flight per thread
+    const int total = n * RU;
+    for (int e0 = 0; e0 < total; e0 += kFly * kEmitThreads) {
+      // Every slot is loaded (past the end: the last piece again), so the
+      // pieces stay in registers; only the stores are guarded.
+      uint4 kv[kFly], vv[kFly];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * kTopkThreads + tid;  // position base + i
-      cand[(i / kPer) * (kPer + 1) + i % kPer] = cur[u];
+      for (int f = 0; f < kFly; ++f) {
+        const int e = min(e0 + f * kEmitThreads + (int)threadIdx.x, total - 1);
+        const long long from = (in_row0 + src[e / RU]) * RU + e % RU;
+        kv[f] = K[from];
+        vv[f] = V[from];
+      }
+#pragma unroll
+      for (int f = 0; f < kFly; ++f) {
+        const int e = e0 + f * kEmitThreads + (int)threadIdx.x;
+        if (e < total) {
+          const long long to = (out_row0 + dst0 + e / RU) * RU + e % RU;
+          Ko[to] = kv[f];
+          Vo[to] = vv[f];
+        }
+      }
+    }
+  }
+}
+
+template <int RU>
+__global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, const float* __restrict__ scores,
+                                                            const uint32_t* __restrict__ cut,
+                                                            const uint32_t* __restrict__ segcnt,
+                                                            int32_t* __restrict__ indices,
+                                                            const uint4* __restrict__ K, const uint4* __restrict__ V,
+                                                            uint4* __restrict__ Ko, uint4* __restrict__ Vo) {
+  const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  const int h = s.h0 + (row - s.row0);
+  int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
+  const long long in_row0 = RU > 0 ? s.kv_off / a.D + (long long)h * s.L : 0;
+  const long long out_row0 = RU > 0 ? s.out_off + (long long)h * s.out_ld : 0;
+  const int segsz = a.seg_size;
+  __shared__ int32_t src[kSegUnit];
+  __shared__ uint32_t stage[kSegUnit + kSegUnit / kEmitPer];
+  __shared__ uint32_t sh[8];
+  __shared__ uint32_t s_before[2];
+
+  if (s.L < s.C) {  // bypass: position j goes to slot j
+    const int end = min(s.L, (seg + 1) * segsz);
+    for (int j0 = seg * segsz; j0 < end; j0 += kSegUnit) {
+      const int n = min(kSegUnit, end - j0);
+      for (int i = tid; i < n; i += kEmitThreads) src[i] = j0 + i;
+      __syncthreads();
+      emit_rows<RU>(n, j0, src, out, in_row0, out_row0, K, V, Ko, Vo);
+      __syncthreads();
+    }
+    return;
+  }
+  const int W = a.window ? a.W : 0, P = s.L - W;
+  const int count = s.C - W;
+  const int nseg = (P + segsz - 1) / segsz;
+  if (seg > nseg) return;
+  if (seg == nseg) {  // the window positions follow the picks
+    if (W == 0) return;
+    for (int w = tid; w < W; w += kEmitThreads) src[w] = P + w;
+    __syncthreads();
+    emit_rows<RU>(W, count, src, out, in_row0, out_row0, K, V, Ko, Vo);
+    return;
+  }
+
+  // Picks above tau and tau-equal positions in the segments before this one.
+  const uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
+  if (tid < 2) s_before[tid] = 0u;
+  __syncthreads();
+  {
+    uint32_t g = 0, e = 0;
+    for (int q = tid; q < seg; q += kEmitThreads) {
+      g += sc[q];
+      e += sc[kMaxSegRow + q];
+    }
+    if (g) atomicAdd(&s_before[0], g);
+    if (e) atomicAdd(&s_before[1], e);
+  }
+  __syncthreads();
+  const uint32_t tau = cut[2 * row], need_eq = cut[2 * row + 1];
+  uint32_t gt_run = s_before[0], eq_run = s_before[1];
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
+
+  const int end = min(P, (seg + 1) * segsz);
+  for (int j0 = seg * segsz; j0 < end; j0 += kSegUnit) {
+    // Coalesced loads staged through LDS; thread t then scans positions
+    // j0 + t * kEmitPer + u in order (rows of kEmitPer + 1 words: no conflicts).
+#pragma unroll
+    for (int u = 0; u < kEmitPer; ++u) {
+      const int i = u * kEmitThreads + tid;
+      const int j = j0 + i;
+      stage[(i / kEmitPer) * (kEmitPer + 1) + i % kEmitPer] = j < end ? key[j] : 0u;
     }
     __syncthreads();
-    const int j0 = base + tid * kPer;
-    uint32_t kk[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) kk[u] = cand[tid * (kPer + 1) + u];
+    uint32_t kk[kEmitPer];
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      if (j0 + u < P) {
-        ngt += kk[u] > tau;
-        neq += kk[u] == tau;
-      }
+    for (int u = 0; u < kEmitPer; ++u) {
+      kk[u] = stage[tid * (kEmitPer + 1) + u];
+      const bool in = j0 + tid * kEmitPer + u < end;
+      ngt += in && kk[u] > tau;
+      neq += in && kk[u] == tau;
     }
     const uint32_t packed = (ngt << 16) | neq;
     uint32_t total;
-    const uint32_t ex = block_scan_1024(packed, sh, total) - packed;
-    uint32_t eq_seen = eq_run + (ex & 0xFFFFu);
-    uint32_t pos = gt_run + (ex >> 16) + min(eq_seen, need_eq);
+    const uint32_t ex = block_scan<kEmitThreads>(packed, sh, total) - packed;
+    // Slot of a pick = picks above tau before it + min(tau-equal before it,
+    // need_eq); those of this pass are consecutive from dst0.
+    const uint32_t dst0 = gt_run + min(eq_run, need_eq);
+    uint32_t gb = gt_run + (ex >> 16), eb = eq_run + (ex & 0xFFFFu);
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = j0 + u;
-      if (j < P) {
-        bool take = kk[u] > tau;
-        if (kk[u] == tau) {
-          take = eq_seen < need_eq;
-          ++eq_seen;
+    for (int u = 0; u < kEmitPer; ++u) {
+      const int j = j0 + tid * kEmitPer + u;
+      if (j < end) {
+        const bool gt = kk[u] > tau, eq = kk[u] == tau;
+        if (gt || (eq && eb < need_eq)) {
+          const uint32_t dst = gb + min(eb, need_eq);
+          if (dst < (uint32_t)count) src[dst - dst0] = j;
         }
-        if (take) {
-          if (pos < count) {
-            if (buffered)
-              picks[pos] = j;
-            else
-              out[pos] = j;
-          }
-          ++pos;
-        }
+        gb += gt;
+        eb += eq;
       }
     }
     gt_run += total >> 16;
     eq_run += total & 0xFFFFu;
-  }
-  if (buffered) {
+    const uint32_t dst1 = min(gt_run + min(eq_run, need_eq), (uint32_t)count);
     __syncthreads();
-    for (uint32_t m = tid; m < count; m += kTopkThreads) out[m] = picks[m];
+    emit_rows<RU>((int)(dst1 - min(dst0, dst1)), (int)dst0, src, out, in_row0, out_row0, K, V, Ko, Vo);
+    __syncthreads();
   }
-  if (a.window)
-    for (int w = tid; w < a.W; w += kTopkThreads) out[count + w] = P + w;
-  KVSEL_SELECT_MARK(4);
 }
 
 // Avg pooling sums the k neighbours (zero padding included) in ascending
@@ -304,19 +427,21 @@ __device__ __forceinline__ float avg_sorted(const float* c) {
 }
 
 __device__ float avg_sorted_any(const float* c, int kw) {
-  float x[2 * kMaxPoolRadius + 1];
+  // Same ascending order without a local array: each step adds every copy of
+  // the next larger value among the kw neighbours.
   const int r = kw / 2;
-  for (int o = 0; o < kw; ++o) {
-    const float val = c[o - r];
-    int k = o;
-    while (k > 0 && x[k - 1] > val) {
-      x[k] = x[k - 1];
-      --k;
-    }
-    x[k] = val;
+  float sum = 0.f, cur = -INFINITY;
+  int added = 0;
+  while (added < kw) {
+    float v = INFINITY;
+    for (int o = -r; o <= r; ++o)
+      if (c[o] > cur) v = fminf(v, c[o]);
+    int copies = 0;
+    for (int o = -r; o <= r; ++o) copies += c[o] == v;
+    for (int m = 0; m < copies; ++m) sum += v;
+    added += copies;
+    cur = v;
   }
-  float sum = 0.f;
-  for (int o = 0; o < kw; ++o) sum += x[o];
   return sum / (float)kw;
 }
 
@@ -428,10 +553,37 @@ hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Launch& a, int rows, const float* scores, const uint32_t* hist, int32_t* indices,
-                       hipStream_t st) {
+int selection_seg_size(long long max_positions) {
+  const long long units = (max_positions + kSegUnit - 1) / kSegUnit;
+  const long long per = (units + kMaxSegRow - 1) / kMaxSegRow;
+  return (int)(kSegUnit * (per < 1 ? 1 : per));
+}
+
+hipError_t launch_threshold(const Launch& a, int rows, const float* scores, const uint32_t* hist, uint32_t* cut,
+                            uint32_t* segcnt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, scores, hist, indices);
+  hipLaunchKernelGGL(threshold_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, scores, hist, cut, segcnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, const float* scores,
+                       const uint32_t* cut, const uint32_t* segcnt, int32_t* indices, const void* K, const void* V,
+                       void* K_out, void* V_out, hipStream_t st) {
+  if (rows <= 0 || max_positions <= 0) return hipSuccess;
+  const dim3 grid((max_positions + a.seg_size - 1) / a.seg_size + 1, rows);
+  const uint4* k = (const uint4*)K;
+  const uint4* v = (const uint4*)V;
+  uint4* ko = (uint4*)K_out;
+  uint4* vo = (uint4*)V_out;
+  const int ru = K == nullptr ? 0 : a.D * (dtype == 1 ? 2 : 4) / 16;
+  if (ru == 0)
+    hipLaunchKernelGGL(emit_kernel<0>, grid, dim3(kEmitThreads), 0, st, a, scores, cut, segcnt, indices, k, v, ko, vo);
+  else if (ru == 8)
+    hipLaunchKernelGGL(emit_kernel<8>, grid, dim3(kEmitThreads), 0, st, a, scores, cut, segcnt, indices, k, v, ko, vo);
+  else if (ru == 16)
+    hipLaunchKernelGGL(emit_kernel<16>, grid, dim3(kEmitThreads), 0, st, a, scores, cut, segcnt, indices, k, v, ko, vo);
+  else
+    hipLaunchKernelGGL(emit_kernel<32>, grid, dim3(kEmitThreads), 0, st, a, scores, cut, segcnt, indices, k, v, ko, vo);
   return hipGetLastError();
 }
 

@@ -42,8 +42,10 @@ def test_version_and_error_string(B):
 def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
     # two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
-    # per-head exchange records, status word, first-digit histograms
-    expect_min = 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 4160 + 256 + 32 * 2048 * 4
+    # selection threshold and per-segment counts, per-head exchange records,
+    # status word, first-digit histograms
+    expect_min = (2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
+                  + 32 * 4160 + 256 + 32 * 2048 * 4)
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W
@@ -111,7 +113,7 @@ def test_step_entry_point_errors(B):
     assert lib.kvsel_topk(None, 4, 100, 10, FAKE, 10, None, 0, None) == -1
     assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, None, 0, None) == -1          # no workspace
     assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, FAKE, 1024, None) == -3       # too small
-    assert lib.kvsel_topk_workspace_bytes(4, 100) == 4 * 2048 * 4
+    assert lib.kvsel_topk_workspace_bytes(4, 100) == 4 * 2048 * 4 + 256 + 4 * 2 * 512 * 4  # histograms, cut, counts
     assert lib.kvsel_topk_workspace_bytes(0, 100) == 0
     assert lib.kvsel_pool1d(FAKE, 4, 100, 2, 0, ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 0, FAKE, None) == -1  # aliasing
