@@ -146,8 +146,8 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)B * heads * kCutBytes);
   p.off_segcnt = off;  // per-segment counts above / on the threshold
   off = align256(off + (size_t)B * heads * kSegCntBytes);
-  p.off_ctr = off;  // single-read scoring: one exchange record per (sequence, head)
-  off = align256(off + (size_t)B * heads * fused_exchange_bytes());
+  p.off_ctr = off;  // single-read scoring: one exchange slot per (sequence, head, chunk)
+  off = align256(off + (size_t)p.fpart[B] * fused_exchange_bytes());
   p.off_status = off;
   off = align256(off + 256);
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)

@@ -10,15 +10,28 @@
 //
 // Why one kernel.  A vote needs each row's final maximum and normaliser, which
 // depend on all L positions of the head, so a plain implementation reads K
-// twice.  Here the logits of a chunk stay in VGPRs while the head's row maxima
-// and row sums are agreed on across the workgroups that hold its chunks.
+// twice.  Here the exponentials of a chunk stay in VGPRs until the head's row
+// statistics have been agreed on across the workgroups that hold its chunks.
 //
 // Schedule.  A cooperative launch of one workgroup per CU (all co-resident).
 // Work proceeds in rounds; in a round every workgroup owns one chunk of
 // S = 512 positions of some head (heads_per_round heads, each split over
-// ceil(L / S) workgroups).  Two register sets form a pipeline: in step k the
-// workgroup streams round k while it normalises and votes round k - 1, and
-// the K ring keeps a whole round of loads in flight through the exchanges.
+// fc = ceil(L / S) workgroups).  Two register sets form a pipeline: in step k
+// the workgroup streams round k and normalises it against the chunk's own row
+// maxima, then votes round k - 1, whose head-wide statistics were exchanged
+// while round k streamed.
+//
+// Exchange.  A vote is sum_i exp2(x_ij - M_i) / Z_i.  With the chunk's own
+// maxima m_i the streamed exponentials are u_ij = exp2(x_ij - m_i) and
+// z_i = sum_j u_ij, and the vote is sum_i u_ij * exp2(m_i - M_i) / Z_i with
+// M_i = max over chunks of m_i and Z_i = sum over chunks of
+// z_i * exp2(m_i - M_i).  So one exchange per round suffices: every workgroup
+// stores (m_i, z_i) of its chunk as one 64-bit word per row into its own slot
+// (no atomics), and one round later reads the fc slots of the head and merges
+// them in a fixed order (the result does not depend on arrival order).  The
+// lowest mantissa bit of every published m_i is set, and the same tagged m_i
+// is used for the chunk's exponentials, so a set bit marks a written word in a
+// slot array that starts zeroed.
 //
 // Roles inside a workgroup.  Four streaming waves and one controller wave.
 //  * Streaming waves read global memory only through direct-to-LDS loads of
@@ -27,14 +40,8 @@
 //    explicit vmcnt counts, so the HBM stream never drains while they compute.
 //    They form the logits on MFMA (v_mfma_f32_32x32x16_bf16, Qwin rows from
 //    LDS), exponentials and votes, and talk to the controller through LDS.
-//  * The controller wave does every other global access: it loads Qwin
-//    (double-buffered in LDS), folds the waves' partial row maxima into the
-//    head's maxima (atomic max on order-preserving codes), adds the partial
-//    row sums to the head's sums (fixed point round(z * 2^30) plus an arrival
-//    count in the top bits, one 64-bit atomic add per row: the total does not
-//    depend on arrival order), polls for completion, broadcasts the final
-//    values through LDS, and writes the votes.  Its global traffic therefore
-//    never sits in the streaming waves' in-order vmcnt queue.
+//  * The controller wave does every other global access: Qwin (double
+//    buffered in LDS), the slot store, the slot reads, and the votes.
 // All exchange accesses are agent scope (they bypass the per-XCD L2); every
 // wait is bounded, and a timed-out wait records a flag and marks the head's
 // votes NaN, so the grid always drains.
@@ -47,10 +54,13 @@
 
 #include "kvsel_internal.h"
 
-// Instrumentation hook in the streaming waves (step k, point 0..3); empty
-// unless a profiling build defines it.
+// Instrumentation hooks in the streaming waves (step k, point 0..3) and the
+// controller (step k, point 4..7); empty unless a profiling build defines them.
 #ifndef KVSEL_FUSED_MARK
 #define KVSEL_FUSED_MARK(k, point)
+#endif
+#ifndef KVSEL_FUSED_CTL_MARK
+#define KVSEL_FUSED_CTL_MARK(k, point)
 #endif
 
 namespace kvsel {
@@ -62,10 +72,10 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr int kSW = 4;                    // streaming waves
+constexpr int kSW = 8;                    // streaming waves (two per SIMD)
 constexpr int kThreads = (kSW + 1) * 64;  // plus one controller wave
-constexpr int kTT = 4;                    // 32-position tiles per streaming wave per round
-constexpr int kNBuf = 4;                  // K tiles in flight per streaming wave
+constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
+constexpr int kNBuf = 2;                  // K tiles in flight per streaming wave
 constexpr int kS = kSW * kTT * 32;        // positions per workgroup per round
 constexpr long kSpin = 1L << 22;          // bound of every wait loop
 
@@ -99,40 +109,21 @@ __device__ __forceinline__ Work round_work(const Launch& a, int r) {
   return w;
 }
 
-// ---- per-(sequence, head) exchange record in the workspace, zeroed per call
-constexpr int kRowStride = 64;                          // bytes between rows (one line each)
-constexpr int kHeadRec = 64 + 2 * 32 * kRowStride;      // counter line, 32 max rows, 32 sum rows
-constexpr double kZScale = 1073741824.0;                // 2^30
-constexpr unsigned long long kArrive = 1ull << 55;      // one arrival in the sum words
-constexpr unsigned long long kSumMask = kArrive - 1;
-struct HeadRec {
-  unsigned* cnt_max;  // chunks whose maxima are folded in
-  char* rows;
-  __device__ __forceinline__ unsigned* m_enc(int i) const { return reinterpret_cast<unsigned*>(rows + i * kRowStride); }
-  __device__ __forceinline__ unsigned long long* z_word(int i) const {
-    return reinterpret_cast<unsigned long long*>(rows + (32 + i) * kRowStride);
-  }
-};
-__device__ __forceinline__ HeadRec head_rec(unsigned* ex, int hs) {
-  char* base = reinterpret_cast<char*>(ex) + (long long)hs * kHeadRec;
-  return HeadRec{reinterpret_cast<unsigned*>(base), base + 64};
-}
-// Monotone map of floats to unsigned integers (larger float, larger code).
-__device__ __forceinline__ unsigned f2ord(float f) {
-  const unsigned b = __float_as_uint(f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float ord2f(unsigned u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+// ---- exchange slots in the workspace, zeroed per call: per (sequence,
+// head, chunk) 32 words of 64 bits, word i = (tagged m_i bits, z_i bits).
+constexpr int kSlotWords = 32;
+__device__ __forceinline__ float tag_max(float m) { return __uint_as_float(__float_as_uint(m) | 1u); }
+__device__ __forceinline__ unsigned long long pack_slot(float m, float z) {
+  return ((unsigned long long)__float_as_uint(z) << 32) | __float_as_uint(m);
 }
 
 // ---- LDS signalling between the waves of the workgroup.  A wave's LDS
 // operations complete in order, so data written before a signal is visible to
 // a wave that has seen the signal.
 struct Sync {
-  unsigned cnt_a, cnt_b, cnt_c;    // streaming-wave arrivals (max, sum, votes partials)
+  unsigned cnt_b, cnt_c;           // streaming-wave arrivals (row statistics, votes)
   unsigned q_ready;                // Qwin of rounds < q_ready is in LDS
-  unsigned m_ready, z_ready;       // final row max / normaliser of rounds < value broadcast
+  unsigned s_ready;                // vote scales of rounds < s_ready are in LDS
   unsigned timeout;
 };
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -167,23 +158,30 @@ struct TileGeom {
   static constexpr int PIECES = 32 * PR;   // pieces per tile
 };
 
-// Issue the loads of the 32-row tile starting at p0 into an LDS tile.  Piece c
-// of tile row r lands at r * PR + (c ^ (r % PR)).
+// Issue the loads of the 32-row tile starting at row p0 of a head's K (rows
+// past L repeat row L - 1) into an LDS tile: one scalar base address and a
+// 32-bit offset per lane.  Piece c of tile row r lands at r * PR + (c ^ (r % PR)).
 template <int D>
 __device__ __forceinline__ void issue_tile(const __bf16* __restrict__ kh, int L, int p0, const uint4* lds_tile,
                                            int lane) {
   using G = TileGeom<D>;
   const unsigned base = (unsigned)(uintptr_t)lds_tile;
+  // The base is wave-uniform; make that explicit for the scalar operand
+  // (readfirstlane returns int: each half is widened as unsigned).
+  const unsigned long long fa = (unsigned long long)(uintptr_t)(kh + (long long)p0 * D);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(fa >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)fa);
+  const __bf16* first = (const __bf16*)(((unsigned long long)hi << 32) | (unsigned long long)lo);
+  const int rows = min(32, L - p0);
 #pragma unroll
   for (int i = 0; i < G::NL; ++i) {
     const int piece = i * 64 + lane;
     const int r = piece / G::PR;
     const int c = (piece % G::PR) ^ (r & (G::PR - 1));
-    const int row = min(p0 + r, L - 1);
-    const __bf16* g = kh + (long long)row * D + c * 8;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    const unsigned off = (unsigned)((min(r, rows - 1) * G::PR + c) * 16);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(g)
+                 : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(off), "s"(first)
                  : "memory", "m0");
   }
 }
@@ -226,15 +224,17 @@ __device__ __forceinline__ int tiles_after(const Stream& st, int q) {
   return n;
 }
 
-// Phase A (streaming wave): logits of round k into x, row maxima to LDS.
+// Phase A (streaming wave): logits of round k into x; this wave's row maxima
+// and sums of exponentials to LDS.
 template <int D>
 __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int k, const __bf16* __restrict__ K,
                                              uint4 (*ring)[TileGeom<D>::PIECES], const uint4* __restrict__ qbuf,
-                                             float (&x)[kTT][16], Stream& st, float* s_maxp, Sync* sy) {
+                                             float (&x)[kTT][16], Stream& st, float* s_maxp, float* s_zp,
+                                             Sync* sy) {
   using G = TileGeom<D>;
   const Seg& s = a.seg[w.e];
   const int L = s.L, W = a.W, P = L - W;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
   lds_wait_ge(&sy->q_ready, (unsigned)k + 1, &sy->timeout);
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
@@ -252,6 +252,10 @@ __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int
         const bf16x8 qa = __builtin_bit_cast(bf16x8, qbuf[off]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, acc, 0, 0, 0);
       }
+      // Every operand has been read: refill the buffer before the VALU work.
+      lds_fence();
+      st.issued &= ~(1u << (q & 31));
+      stream_issue<D>(a, K, q + kNBuf, wave, lane, ring, st);
       const int j = p0 + n;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -262,11 +266,12 @@ __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[t][r] = -INFINITY;
+      st.issued &= ~(1u << (q & 31));
+      stream_issue<D>(a, K, q + kNBuf, wave, lane, ring, st);
     }
-    lds_fence();  // operands are in registers before the slot is reused
-    st.issued &= ~(1u << (q & 31));
-    stream_issue<D>(a, K, q + kNBuf, wave, lane, ring, st);
   }
+  // This wave's row maxima and sums of exp2(x - max), without waiting for the
+  // other waves: the controller merges the four pairs.
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     float mm = kNegBig;
@@ -274,9 +279,17 @@ __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int
     for (int t = 0; t < kTT; ++t) mm = fmaxf(mm, x[t][r]);
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
-    if (n == 0) s_maxp[wave * 32 + acc_row(r, g)] = mm;
+    float zz = 0.f;
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) zz += exp2_fast(x[t][r] - mm);
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) zz += __shfl_xor(zz, off);
+    if (n == 0) {
+      s_maxp[wave * 32 + acc_row(r, g)] = mm;
+      s_zp[wave * 32 + acc_row(r, g)] = zz;
+    }
   }
-  lds_add(&sy->cnt_a);
+  lds_add(&sy->cnt_b);
 }
 
 // Streaming waves that own no chunk in round k still advance their tile
@@ -284,44 +297,29 @@ __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int
 template <int D>
 __device__ __forceinline__ void phase_skip(const Launch& a, int k, const __bf16* __restrict__ K,
                                            uint4 (*ring)[TileGeom<D>::PIECES], Stream& st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int t = 0; t < kTT; ++t) stream_issue<D>(a, K, k * kTT + t + kNBuf, wave, lane, ring, st);
 }
 
-// Phase B (streaming wave): u = exp2(x - m) in place, partial row sums to LDS.
-__device__ __forceinline__ void phase_normalise(int k, float (&x)[kTT][16], const float* s_m, float* s_zp, Sync* sy) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 31, g = lane >> 5;
-  lds_wait_ge(&sy->m_ready, (unsigned)k + 1, &sy->timeout);
+// Phase B (streaming wave): votes of the wave's positions into LDS, from the
+// head-wide row maxima M and inverse normalisers.  Same arithmetic as the
+// two-pass kernels: equal key rows give bit-equal votes.
+__device__ __forceinline__ void phase_votes(int k, const float (&x)[kTT][16], const float* s_m, const float* s_iz,
+                                            float* s_votes, Sync* sy) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
+  lds_wait_ge(&sy->s_ready, (unsigned)k + 1, &sy->timeout);
+  float mr[16], iz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float m = s_m[acc_row(r, g)];
-    float zz = 0.f;
-#pragma unroll
-    for (int t = 0; t < kTT; ++t) {
-      x[t][r] = exp2_fast(x[t][r] - m);
-      zz += x[t][r];
-    }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) zz += __shfl_xor(zz, off);
-    if (n == 0) s_zp[wave * 32 + acc_row(r, g)] = zz;
+    mr[r] = s_m[acc_row(r, g)];
+    iz[r] = s_iz[acc_row(r, g)];
   }
-  lds_add(&sy->cnt_b);
-}
-
-// Phase C (streaming wave): votes of the wave's positions into LDS.
-__device__ __forceinline__ void phase_votes(int k, const float (&u)[kTT][16], const float* s_iz, float* s_votes,
-                                            Sync* sy) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 31, g = lane >> 5;
-  lds_wait_ge(&sy->z_ready, (unsigned)k + 1, &sy->timeout);
-  float iz[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) iz[r] = s_iz[acc_row(r, g)];
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
     float tot = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tot += u[t][r] * iz[r];
+    for (int r = 0; r < 16; ++r) tot += exp2_fast(x[t][r] - mr[r]) * iz[r];
     const float other = __shfl_xor(tot, 32);
     const float v = g == 0 ? tot + other : other + tot;
     if (g == 0) s_votes[wave * kTT * 32 + t * 32 + n] = v;
@@ -352,111 +350,129 @@ __device__ __forceinline__ void ctl_load_q(const Launch& a, int k, const __bf16*
   }
 }
 
-// Controller: bounded poll of a global counter (lane 0), wave-uniform result.
-__device__ __forceinline__ bool ctl_poll(unsigned* cnt, unsigned target, unsigned* status) {
-  int ok = 1;
-  if ((threadIdx.x & 63) == 0) {
-    long spins = 0;
-    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpin) {
-        __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-    }
-  }
-  return __shfl(ok, 0) != 0;
+// Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
+// exponentials rescaled to it.
+__device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
+  const float d = mo - m;
+  const float e = exp2_fast(-fabsf(d));
+  z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
+  m = fmaxf(m, mo);
 }
 
+// Controller: the head-wide row statistics of round r from the fc slots of
+// its head.  Lane l merges row l % 32 over the slots of parity l / 32 (the
+// words of rows >= W are never written and never read); the two halves are
+// merged last, so every workgroup of the head merges in the same order.  The
+// reads are repeated until every word carries its tag (bounded).
+__device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, const unsigned long long* ex,
+                                               float& M, float& Z) {
+  const Seg& s = a.seg[w.e];
+  const int fc = s.fc, W = a.W;
+  const int lane = threadIdx.x & 63, i = lane & 31, half = lane >> 5;
+  const unsigned long long* base = ex + (s.part_base + (long long)w.h * fc) * kSlotWords;
+  float mm = kNegBig, zz = 0.f;
+  bool ok = true;
+  constexpr int kBatch = 16;  // words per lane in flight
+  for (int c0 = 0; c0 < fc; c0 += 2 * kBatch) {
+    unsigned long long v[kBatch];
+    long spins = 0;
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = min(c0 + 2 * u + half, fc - 1);
+        v[u] = __hip_atomic_load(base + (long long)c * kSlotWords + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      bool valid = true;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + 2 * u + half;
+        if (c < fc && i < W) valid = valid && (v[u] & 1ull) != 0;
+      }
+      if (__ballot(!valid) == 0) break;
+      if (++spins > kSpin) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + 2 * u + half;
+      if (c < fc && i < W) lse_merge(mm, zz, __uint_as_float((unsigned)v[u]), __uint_as_float((unsigned)(v[u] >> 32)));
+    }
+  }
+  const float mo = __shfl_xor(mm, 32), zo = __shfl_xor(zz, 32);
+  if (half == 0) lse_merge(mm, zz, mo, zo);
+  M = mm;
+  Z = zz;
+  return __ballot(!ok) == 0;
+}
+
+// Controller wave.  Step k: (1) head statistics of round k - 1 from the slots
+// (overlapping the streaming of round k), (2) publish the chunk's (m, z) of
+// round k (merged from the four waves), (3) Qwin of round k + 2, (4) votes of round k - 1 to memory.
 template <int D>
-__device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsigned* __restrict__ ex,
+__device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsigned long long* __restrict__ ex,
                            unsigned* __restrict__ status, float* __restrict__ votes, float* __restrict__ row_stats,
                            uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_maxp)[kSW * 32],
-                           float (*s_zp)[kSW * 32], float (*s_m)[32], float (*s_iz)[32],
-                           float (*s_votes)[kS], Sync* sy) {
+                           float (*s_zp)[kSW * 32], float (*s_m)[32], float (*s_iz)[32], float (*s_votes)[kS],
+                           Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   ctl_load_q<D>(a, 0, Q, qbufs[0]);
   ctl_load_q<D>(a, 1, Q, qbufs[1]);
   lds_set(&sy->q_ready, 2u);
-  unsigned on_a = 0, on_b = 0, on_c = 0;  // owned rounds whose phase A / B / C partials were awaited
+  unsigned on_b = 0, on_c = 0;  // owned rounds whose phase B / C results were awaited
   for (int k = 0; k < a.rounds + 1; ++k) {
     const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
-    // (1) Final maxima of round k - 1: all of its chunks have folded theirs in.
+    // (1) Head-wide statistics of round k - 1.
     if (w1.on) {
-      const HeadRec hr = head_rec(ex, w1.hs);
-      const bool ok = ctl_poll(hr.cnt_max, (unsigned)a.seg[w1.e].fc, status);
+      float M, Z;
+      const bool ok = ctl_head_stats(a, w1, ex, M, Z);
+      if (!ok && lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (lane < W) {
-        const float m = ord2f(__hip_atomic_load(hr.m_enc(lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        s_m[(k - 1) & 1][lane] = ok ? m : __builtin_nanf("");
+        s_m[(k - 1) & 1][lane] = ok ? M : __builtin_nanf("");
+        s_iz[(k - 1) & 1][lane] = ok ? 1.f / Z : __builtin_nanf("");
+        if (row_stats != nullptr && w1.c == 0) {
+          float* rs = row_stats + ((long long)w1.hs * W + lane) * 2;
+          rs[0] = M * kLn2;
+          rs[1] = Z;
+        }
       }
     }
-    if (k >= 1) lds_set(&sy->m_ready, (unsigned)k);
-    // (2) Fold this workgroup's maxima of round k into the head's.
+    if (k >= 1) lds_set(&sy->s_ready, (unsigned)k);
+    KVSEL_FUSED_CTL_MARK(k, 4);
+    // (2) This chunk's (m, z) of round k, one 64-bit word per row.
     if (w0.on) {
-      ++on_a;
-      lds_wait_ge(&sy->cnt_a, kSW * on_a, &sy->timeout);
-      if (lane < W) {
-        float mm = s_maxp[k & 1][lane];
-#pragma unroll
-        for (int v = 1; v < kSW; ++v) mm = fmaxf(mm, s_maxp[k & 1][v * 32 + lane]);
-        __hip_atomic_fetch_max(head_rec(ex, w0.hs).m_enc(lane), f2ord(mm), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    // Qwin of round k + 2 goes into the buffer of round k: its last user (the
-    // latest owned round of the same parity) has finished phase A, which was
-    // awaited above or at an earlier step.
-    ctl_load_q<D>(a, k + 2, Q, qbufs[k & 1]);
-    lds_set(&sy->q_ready, (unsigned)(k + 3));
-    // (3) Add this workgroup's row sums of round k - 1 (value and arrival).
-    if (w1.on) {
       ++on_b;
       lds_wait_ge(&sy->cnt_b, kSW * on_b, &sy->timeout);
       if (lane < W) {
-        float zz = s_zp[(k - 1) & 1][lane];
+        // Merge the four waves' (max, sum) pairs in wave order against the
+        // tagged chunk maximum.
+        float m = s_maxp[k & 1][lane];
 #pragma unroll
-        for (int v = 1; v < kSW; ++v) zz += s_zp[(k - 1) & 1][v * 32 + lane];
-        const unsigned long long fix = (unsigned long long)__double2ll_rn((double)zz * kZScale) + kArrive;
-        __hip_atomic_fetch_add(head_rec(ex, w1.hs).z_word(lane), fix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int v = 1; v < kSW; ++v) m = fmaxf(m, s_maxp[k & 1][v * 32 + lane]);
+        m = tag_max(m);
+        // A wave with no visible position in the row has sum 0 and the
+        // sentinel maximum, whose ulp is huge: it adds nothing.
+        float zz = 0.f;
+#pragma unroll
+        for (int v = 0; v < kSW; ++v) {
+          const float zv = s_zp[k & 1][v * 32 + lane];
+          if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
+        }
+        const Seg& s = a.seg[w0.e];
+        unsigned long long* slot = ex + (s.part_base + (long long)w0.h * s.fc + w0.c) * kSlotWords;
+        __hip_atomic_store(slot + lane, pack_slot(m, zz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    // The maxima must have landed before their arrival is counted.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (w0.on && lane == 0)
-      __hip_atomic_fetch_add(head_rec(ex, w0.hs).cnt_max, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // (4) Final normalisers of round k - 1: every sum word carries fc arrivals.
-    if (w1.on) {
-      const HeadRec hr = head_rec(ex, w1.hs);
-      const unsigned fc = (unsigned)a.seg[w1.e].fc;
-      unsigned long long zw = 0;
-      bool done = false;
-      long spins = 0;
-      while (!done) {
-        zw = lane < W ? __hip_atomic_load(hr.z_word(lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : (unsigned long long)fc << 55;
-        done = __ballot((unsigned)(zw >> 55) < fc) == 0;
-        if (!done) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > kSpin) {
-            if (lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-      }
-      if (lane < W) {
-        const double Z = (double)(zw & kSumMask) / kZScale;
-        s_iz[(k - 1) & 1][lane] = done ? (float)(1.0 / Z) : __builtin_nanf("");
-        if (row_stats != nullptr && w1.c == 0) {
-          float* rs = row_stats + ((long long)w1.hs * W + lane) * 2;
-          rs[0] = s_m[(k - 1) & 1][lane] * kLn2;
-          rs[1] = (float)Z;
-        }
-      }
-    }
-    if (k >= 1) lds_set(&sy->z_ready, (unsigned)k);
-    // (5) Votes of round k - 1 to memory (prefix positions only).
+    KVSEL_FUSED_CTL_MARK(k, 5);
+    // (3) Qwin of round k + 2 goes into the buffer of round k, whose phase A
+    // has finished (awaited in (2), or the round is not owned).
+    ctl_load_q<D>(a, k + 2, Q, qbufs[k & 1]);
+    lds_set(&sy->q_ready, (unsigned)(k + 3));
+    KVSEL_FUSED_CTL_MARK(k, 6);
+    // (4) Votes of round k - 1 to memory (prefix positions only).
     if (w1.on) {
       ++on_c;
       lds_wait_ge(&sy->cnt_c, kSW * on_c, &sy->timeout);
@@ -467,13 +483,14 @@ __device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsign
       for (int i = lane; i < kS; i += 64)
         if (j0 + i < P) vout[j0 + i] = s_votes[(k - 1) & 1][i];
     }
+    KVSEL_FUSED_CTL_MARK(k, 7);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,
-                                                                  unsigned* __restrict__ ex,
+                                                                  unsigned long long* __restrict__ ex,
                                                                   unsigned* __restrict__ status,
                                                                   float* __restrict__ votes,
                                                                   float* __restrict__ row_stats) {
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __shared__ float s_m[2][32], s_iz[2][32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
-  if (threadIdx.x == 0) sy = Sync{0, 0, 0, 0, 0, 0, 0};
+  if (threadIdx.x == 0) sy = Sync{0, 0, 0, 0, 0};
   __syncthreads();  // the only workgroup barrier; afterwards waves meet through LDS flags
   const int wave = threadIdx.x >> 6;
   if (wave == kSW) {
@@ -498,23 +515,19 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   Stream st{0u};
   for (int q = 0; q < kNBuf; ++q) stream_issue<D>(a, K, q, wave, lane, ring, st);
   float xa[kTT][16], xb[kTT][16];
-  // Step k streams round k into one register set while round k - 1 is
-  // normalised and voted from the other; the sets swap every step.  The
-  // exchanges of round k - 1 overlap the loads of round k + 1, which the
-  // ring has already issued.
+  // Step k streams round k into one register set (with this wave's row
+  // statistics), then votes round k - 1 from the other set; the sets swap
+  // every step.  The exchange of round k - 1 overlaps the streaming of round k.
   auto step = [&](int k, float (&X0)[kTT][16], float (&X1)[kTT][16]) {
     KVSEL_FUSED_MARK(k, 0);
     const Work w0 = round_work(a, k);
     if (w0.on)
-      phase_stream<D>(a, w0, k, K, ring, s_q[k & 1], X0, st, s_maxp[k & 1], &sy);
+      phase_stream<D>(a, w0, k, K, ring, s_q[k & 1], X0, st, s_maxp[k & 1], s_zp[k & 1], &sy);
     else
       phase_skip<D>(a, k, K, ring, st);
     KVSEL_FUSED_MARK(k, 1);
-    if (round_work(a, k - 1).on) {
-      phase_normalise(k - 1, X1, s_m[(k - 1) & 1], s_zp[(k - 1) & 1], &sy);
-      KVSEL_FUSED_MARK(k, 2);
-      phase_votes(k - 1, X1, s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
-    }
+    KVSEL_FUSED_MARK(k, 2);
+    if (round_work(a, k - 1).on) phase_votes(k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
     KVSEL_FUSED_MARK(k, 3);
   };
   const int steps = a.rounds + 1;
@@ -558,8 +571,8 @@ int grid_for() {
 }
 
 template <int D>
-hipError_t launch_t(const Launch& a, const void* Q, const void* K, unsigned* ex, unsigned* status, float* votes,
-                    float* row_stats, hipStream_t st) {
+hipError_t launch_t(const Launch& a, const void* Q, const void* K, unsigned long long* ex, unsigned* status,
+                    float* votes, float* row_stats, hipStream_t st) {
   const int grid = grid_for<D>();
   if (grid <= 0) return hipErrorNotSupported;
   Launch la = a;
@@ -583,13 +596,14 @@ int fused_grid(int W, int D) {
   return 0;
 }
 
-int fused_exchange_bytes() { return kHeadRec; }
+int fused_exchange_bytes() { return kSlotWords * 8; }
 
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* ex, unsigned* status,
                                 float* votes, float* row_stats, hipStream_t st) {
   if (a.W > 32 || a.S != kS) return hipErrorNotSupported;
-  if (a.D == 128) return launch_t<128>(a, Q, K, ex, status, votes, row_stats, st);
-  if (a.D == 64) return launch_t<64>(a, Q, K, ex, status, votes, row_stats, st);
+  unsigned long long* slots = reinterpret_cast<unsigned long long*>(ex);
+  if (a.D == 128) return launch_t<128>(a, Q, K, slots, status, votes, row_stats, st);
+  if (a.D == 64) return launch_t<64>(a, Q, K, slots, status, votes, row_stats, st);
   return hipErrorNotSupported;
 }
 

@@ -105,7 +105,7 @@ hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, 
 // when the shape is not covered.
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
-int fused_exchange_bytes();  // per-(sequence, head) exchange record
+int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* exchange,
                                 unsigned* status, float* votes, float* row_stats, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);

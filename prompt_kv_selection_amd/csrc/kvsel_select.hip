@@ -428,21 +428,23 @@ __device__ __forceinline__ float avg_sorted(const float* c) {
 
 __device__ float avg_sorted_any(const float* c, int kw) {
   // Same ascending order without a local array: each step adds every copy of
-  // the next larger value among the kw neighbours.
+  // the next larger value among the kw neighbours.  At most kw steps; a NaN
+  // among the neighbours is never counted and makes the result NaN.
   const int r = kw / 2;
   float sum = 0.f, cur = -INFINITY;
   int added = 0;
-  while (added < kw) {
+  for (int step = 0; step < kw && added < kw; ++step) {
     float v = INFINITY;
     for (int o = -r; o <= r; ++o)
       if (c[o] > cur) v = fminf(v, c[o]);
     int copies = 0;
     for (int o = -r; o <= r; ++o) copies += c[o] == v;
+    if (copies == 0) break;
     for (int m = 0; m < copies; ++m) sum += v;
     added += copies;
     cur = v;
   }
-  return sum / (float)kw;
+  return added == kw ? sum / (float)kw : __builtin_nanf("");
 }
 
 // Pooling of the prefix votes fused with the first radix digit of the

@@ -42,10 +42,11 @@ def test_version_and_error_string(B):
 def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
     # two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
-    # selection threshold and per-segment counts, per-head exchange records,
+    # selection threshold and per-segment counts, single-read exchange slots
+    # (per head and 512-position chunk),
     # status word, first-digit histograms
     expect_min = (2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 4160 + 256 + 32 * 2048 * 4)
+                  + 32 * 64 * 256 + 256 + 32 * 2048 * 4)
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W
