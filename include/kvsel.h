@@ -73,8 +73,8 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
 
 /* Process-wide options (kvsel_set_option / kvsel_get_option).
  * KVSEL_OPT_SCORING selects how the window scores are computed:
- *   KVSEL_SCORING_AUTO (default): the faster of the two for the shape
- *     (currently two-pass everywhere);
+ *   KVSEL_SCORING_AUTO (default): the faster of the two for the shape:
+ *     single-read wherever it applies, else two-pass;
  *   KVSEL_SCORING_TWO_PASS: one kernel for the row statistics, a second for
  *     the votes (K is read twice);
  *   KVSEL_SCORING_SINGLE_READ: one cooperative kernel that reads K once;
@@ -82,8 +82,14 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  *     one round of the co-resident grid; calls whose shape it does not cover
  *     return KVSEL_EUNSUPPORTED.
  * Both give the same indices and K/V rows up to the documented rounding of
- * the scores.  Not thread-safe with respect to concurrent calls. */
-enum { KVSEL_OPT_SCORING = 0 };
+ * the scores.  The single-read kernel needs all its workgroups (one per CU)
+ * resident at once; it checks that at start, and if the device is shared
+ * with other work and they are not, the two-pass kernels queued after it
+ * compute the scores instead (same results, K read twice).
+ * KVSEL_OPT_FORCE_FALLBACK (testing): 1 makes every single-read launch take
+ *   that fallback; 0 (default) off.
+ * Not thread-safe with respect to concurrent calls. */
+enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1 };
 enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };
 int kvsel_set_option(int option, int value);
 int kvsel_get_option(int option);

@@ -203,6 +203,7 @@ def kvsel_profile_read() -> dict:
 
 
 KVSEL_OPT_SCORING = 0
+KVSEL_OPT_FORCE_FALLBACK = 1
 SCORING = {"auto": 0, "two_pass": 1, "single_read": 2}
 lib.kvsel_set_option.restype = _i
 lib.kvsel_set_option.argtypes = [_i, _i]

@@ -91,6 +91,7 @@ constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
 
 // Process-wide options.
 int g_scoring = KVSEL_SCORING_AUTO;
+int g_force_fallback = 0;
 
 int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p) {
   if (cu_L == nullptr || C_host == nullptr) return fail(KVSEL_EINVAL, "cu_L_host and C_host must not be NULL");
@@ -148,8 +149,8 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)B * heads * kSegCntBytes);
   p.off_ctr = off;  // single-read scoring: one exchange slot per (sequence, head, chunk)
   off = align256(off + (size_t)p.fpart[B] * fused_exchange_bytes());
-  p.off_status = off;
-  off = align256(off + 256);
+  p.off_status = off;  // per launch group: error flags, arrivals, residency decision, spare
+  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * 4 * sizeof(unsigned));
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
   off = align256(off + (size_t)B * heads * 2048 * 4);
   p.bytes = off;
@@ -233,9 +234,9 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   if (g_scoring == KVSEL_SCORING_SINGLE_READ && need_scoring && !fused_ok)
     return fail(KVSEL_EUNSUPPORTED, "single-read scoring does not cover this shape (bf16, D 64/128, W <= 32, "
                                     "ceil(L / %d) <= %d)", p.fS, grid);
-  // AUTO takes the faster path for the shape; on this chip the two-pass
-  // kernels currently outrun the single-read kernel, so AUTO picks two-pass.
-  const bool use_fused = fused_ok && g_scoring == KVSEL_SCORING_SINGLE_READ;
+  // AUTO takes the faster path for the shape: the single-read kernel wherever
+  // it applies (it reads K once), else two-pass.
+  const bool use_fused = fused_ok && g_scoring != KVSEL_SCORING_TWO_PASS;
   uint32_t* hist = (uint32_t*)(ws + p.off_hist);
   if (use_fused) {
     // Exchange records, status word and histograms start at zero (on the
@@ -274,7 +275,8 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       s.idx_off = (long long)p.heads * p.cuC[b];
       s.out_off = s.idx_off;
       s.vote_off = (long long)p.heads * p.cuP[b];
-      s.part_base = use_fused ? p.fpart[b] : p.part[b];
+      s.part_base = p.part[b];
+      s.fslot_base = p.fpart[b];
       s.fc = p.fc[b];
       s.fhpr = s.fc > 0 && grid > 0 ? std::min(s.nh, grid / s.fc) : 0;
       s.fnr = s.fhpr > 0 ? (s.nh + s.fhpr - 1) / s.fhpr : 0;
@@ -290,17 +292,28 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     uint32_t* gcut = (uint32_t*)((char*)cut + (size_t)b0 * p.heads * kCutBytes);
     uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
+    const unsigned* gate = nullptr;
     if (items > 0 && use_fused) {
+      unsigned* gstatus = status + 4 * (b0 / kMaxSegs);
+      if (g_force_fallback) {
+        e = launch_fill_u32(gstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
+        if (e != hipSuccess) return device_error(e, "fill launch");
+      }
       e = timed("window_fused", st,
-                [&] { return launch_fused_scoring(a, Q, K, counters, status, votes, row_stats, st); });
+                [&] { return launch_fused_scoring(a, Q, K, counters, gstatus, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
-    } else if (items > 0) {
+      // The two-pass kernels follow as the fallback: they return at once
+      // unless the single-read kernel found its grid not resident.
+      gate = gstatus + 2;
+    }
+    if (items > 0) {
       e = timed("window_stats", st, [&] {
-        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, st);
+        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, gate, st);
       });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
-      e = timed("window_votes", st,
-                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
+      e = timed("window_votes", st, [&] {
+        return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, gate, st);
+      });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     }
     if (items > 0) {
@@ -324,16 +337,24 @@ extern "C" {
 int kvsel_version(void) { return (0 << 16) | 2; }
 
 int kvsel_set_option(int option, int value) {
-  if (option != KVSEL_OPT_SCORING) return fail(KVSEL_EINVAL, "unknown option %d", option);
-  if (value < KVSEL_SCORING_AUTO || value > KVSEL_SCORING_SINGLE_READ)
-    return fail(KVSEL_EINVAL, "invalid scoring value %d", value);
-  g_scoring = value;
-  return ok();
+  if (option == KVSEL_OPT_SCORING) {
+    if (value < KVSEL_SCORING_AUTO || value > KVSEL_SCORING_SINGLE_READ)
+      return fail(KVSEL_EINVAL, "invalid scoring value %d", value);
+    g_scoring = value;
+    return ok();
+  }
+  if (option == KVSEL_OPT_FORCE_FALLBACK) {
+    if (value != 0 && value != 1) return fail(KVSEL_EINVAL, "invalid fallback value %d", value);
+    g_force_fallback = value;
+    return ok();
+  }
+  return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
 int kvsel_get_option(int option) {
-  if (option != KVSEL_OPT_SCORING) return fail(KVSEL_EINVAL, "unknown option %d", option);
-  return g_scoring;
+  if (option == KVSEL_OPT_SCORING) return g_scoring;
+  if (option == KVSEL_OPT_FORCE_FALLBACK) return g_force_fallback;
+  return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
 const char* kvsel_last_error(void) { return g_error.c_str(); }

@@ -13,7 +13,7 @@
 // twice.  Here the exponentials of a chunk stay in VGPRs until the head's row
 // statistics have been agreed on across the workgroups that hold its chunks.
 //
-// Schedule.  A cooperative launch of one workgroup per CU (all co-resident).
+// Schedule.  One workgroup per CU, all resident together (checked at start).
 // Work proceeds in rounds; in a round every workgroup owns one chunk of
 // S = 512 positions of some head (heads_per_round heads, each split over
 // fc = ceil(L / S) workgroups).  Two register sets form a pipeline: in step k
@@ -73,7 +73,7 @@ namespace {
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
-constexpr int kThreads = (kSW + 1) * 64;  // plus one controller wave
+constexpr int kThreads = (kSW + 2) * 64;  // plus the exchange and memory waves
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
 constexpr int kNBuf = 2;                  // K tiles in flight per streaming wave
 constexpr int kS = kSW * kTT * 32;        // positions per workgroup per round
@@ -109,6 +109,30 @@ __device__ __forceinline__ Work round_work(const Launch& a, int r) {
   return w;
 }
 
+// ---- reductions over the 32 lanes of each half-wave on the VALU (DPP):
+// row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast15 into rows 1
+// and 3; the results are in lanes 31 (half 0) and 63 (half 1).  Lanes whose
+// DPP source is out of range take the neutral value.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f(float neutral, float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(neutral), __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_f<0x111>(v, v));
+  v = fmaxf(v, dpp_f<0x112>(v, v));
+  v = fmaxf(v, dpp_f<0x114>(v, v));
+  v = fmaxf(v, dpp_f<0x118>(v, v));
+  return fmaxf(v, dpp_f<0x142, 0xA>(v, v));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  v += dpp_f<0x111>(0.f, v);
+  v += dpp_f<0x112>(0.f, v);
+  v += dpp_f<0x114>(0.f, v);
+  v += dpp_f<0x118>(0.f, v);
+  return v + dpp_f<0x142, 0xA>(0.f, v);
+}
+
 // ---- exchange slots in the workspace, zeroed per call: per (sequence,
 // head, chunk) 32 words of 64 bits, word i = (tagged m_i bits, z_i bits).
 constexpr int kSlotWords = 32;
@@ -124,6 +148,7 @@ struct Sync {
   unsigned cnt_b, cnt_c;           // streaming-wave arrivals (row statistics, votes)
   unsigned q_ready;                // Qwin of rounds < q_ready is in LDS
   unsigned s_ready;                // vote scales of rounds < s_ready are in LDS
+  unsigned v_done;                 // votes of rounds < v_done have left LDS
   unsigned timeout;
 };
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -277,15 +302,16 @@ __device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int
     float mm = kNegBig;
 #pragma unroll
     for (int t = 0; t < kTT; ++t) mm = fmaxf(mm, x[t][r]);
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    mm = half_max(mm);
+    const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mm), 31));
+    const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mm), 63));
+    const float mh = g == 0 ? m0 : m1;
     float zz = 0.f;
 #pragma unroll
-    for (int t = 0; t < kTT; ++t) zz += exp2_fast(x[t][r] - mm);
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) zz += __shfl_xor(zz, off);
-    if (n == 0) {
-      s_maxp[wave * 32 + acc_row(r, g)] = mm;
+    for (int t = 0; t < kTT; ++t) zz += exp2_fast(x[t][r] - mh);
+    zz = half_sum(zz);
+    if (n == 31) {
+      s_maxp[wave * 32 + acc_row(r, g)] = mh;
       s_zp[wave * 32 + acc_row(r, g)] = zz;
     }
   }
@@ -309,6 +335,7 @@ __device__ __forceinline__ void phase_votes(int k, const float (&x)[kTT][16], co
                                             float* s_votes, Sync* sy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
   lds_wait_ge(&sy->s_ready, (unsigned)k + 1, &sy->timeout);
+  lds_wait_ge(&sy->v_done, (unsigned)(k >= 1 ? k - 1 : 0), &sy->timeout);  // round k - 2 left this buffer
   float mr[16], iz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -327,27 +354,22 @@ __device__ __forceinline__ void phase_votes(int k, const float (&x)[kTT][16], co
   lds_add(&sy->cnt_c);
 }
 
-// Controller: load Qwin of round k into an LDS buffer (swizzled like K).
+// Controller: start loading Qwin of round k into an LDS buffer with
+// direct-to-LDS loads, swizzled like K (rows W..31 repeat row W - 1 until
+// ctl_finish_q clears them).  Returns whether the round is owned.
 template <int D>
-__device__ __forceinline__ void ctl_load_q(const Launch& a, int k, const __bf16* __restrict__ Q, uint4* qbuf) {
-  using G = TileGeom<D>;
+__device__ __forceinline__ bool ctl_issue_q(const Launch& a, int k, const __bf16* __restrict__ Q, uint4* qbuf) {
   const Work w = round_work(a, k);
-  if (!w.on) return;
-  const int lane = threadIdx.x & 63;
-  const __bf16* q = Q + (long long)w.hs * a.W * D;
-  uint4 v[G::NL];
-#pragma unroll
-  for (int i = 0; i < G::NL; ++i) {
-    const int piece = i * 64 + lane;
-    const int r = piece / G::PR, c = piece % G::PR;
-    v[i] = r < a.W ? *reinterpret_cast<const uint4*>(q + (long long)r * D + c * 8) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < G::NL; ++i) {
-    const int piece = i * 64 + lane;
-    const int r = piece / G::PR, c = piece % G::PR;
-    qbuf[r * G::PR + (c ^ (r & (G::PR - 1)))] = v[i];
-  }
+  if (!w.on) return false;
+  issue_tile<D>(Q + (long long)w.hs * a.W * D, a.W, 0, qbuf, threadIdx.x & 63);
+  return true;
+}
+
+// Controller, once the Qwin loads have landed: rows W..31 become zero.
+template <int D>
+__device__ __forceinline__ void ctl_finish_q(int W, uint4* qbuf) {
+  using G = TileGeom<D>;
+  for (int p = W * G::PR + (int)(threadIdx.x & 63); p < G::PIECES; p += 64) qbuf[p] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
@@ -369,7 +391,7 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
   const Seg& s = a.seg[w.e];
   const int fc = s.fc, W = a.W;
   const int lane = threadIdx.x & 63, i = lane & 31, half = lane >> 5;
-  const unsigned long long* base = ex + (s.part_base + (long long)w.h * fc) * kSlotWords;
+  const unsigned long long* base = ex + (s.fslot_base + (long long)w.h * fc) * kSlotWords;
   float mm = kNegBig, zz = 0.f;
   bool ok = true;
   constexpr int kBatch = 16;  // words per lane in flight
@@ -408,21 +430,16 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
   return __ballot(!ok) == 0;
 }
 
-// Controller wave.  Step k: (1) head statistics of round k - 1 from the slots
+// Exchange wave.  Step k: (1) head statistics of round k - 1 from the slots
 // (overlapping the streaming of round k), (2) publish the chunk's (m, z) of
-// round k (merged from the four waves), (3) Qwin of round k + 2, (4) votes of round k - 1 to memory.
+// round k, merged from the streaming waves' pairs.
 template <int D>
-__device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsigned long long* __restrict__ ex,
-                           unsigned* __restrict__ status, float* __restrict__ votes, float* __restrict__ row_stats,
-                           uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_maxp)[kSW * 32],
-                           float (*s_zp)[kSW * 32], float (*s_m)[32], float (*s_iz)[32], float (*s_votes)[kS],
-                           Sync* sy) {
+__device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ ex, unsigned* __restrict__ status,
+                             float* __restrict__ row_stats, float (*s_maxp)[kSW * 32], float (*s_zp)[kSW * 32],
+                             float (*s_m)[32], float (*s_iz)[32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
-  ctl_load_q<D>(a, 0, Q, qbufs[0]);
-  ctl_load_q<D>(a, 1, Q, qbufs[1]);
-  lds_set(&sy->q_ready, 2u);
-  unsigned on_b = 0, on_c = 0;  // owned rounds whose phase B / C results were awaited
+  unsigned on_b = 0;  // owned rounds whose phase A results were awaited
   for (int k = 0; k < a.rounds + 1; ++k) {
     const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
     // (1) Head-wide statistics of round k - 1.
@@ -447,7 +464,7 @@ __device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsign
       ++on_b;
       lds_wait_ge(&sy->cnt_b, kSW * on_b, &sy->timeout);
       if (lane < W) {
-        // Merge the four waves' (max, sum) pairs in wave order against the
+        // Merge the waves' (max, sum) pairs in wave order against the
         // tagged chunk maximum.
         float m = s_maxp[k & 1][lane];
 #pragma unroll
@@ -462,17 +479,41 @@ __device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsign
           if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
         }
         const Seg& s = a.seg[w0.e];
-        unsigned long long* slot = ex + (s.part_base + (long long)w0.h * s.fc + w0.c) * kSlotWords;
+        unsigned long long* slot = ex + (s.fslot_base + (long long)w0.h * s.fc + w0.c) * kSlotWords;
         __hip_atomic_store(slot + lane, pack_slot(m, zz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     KVSEL_FUSED_CTL_MARK(k, 5);
-    // (3) Qwin of round k + 2 goes into the buffer of round k, whose phase A
-    // has finished (awaited in (2), or the round is not owned).
-    ctl_load_q<D>(a, k + 2, Q, qbufs[k & 1]);
+  }
+}
+
+// Memory wave.  Step k: (3) Qwin of round k + 2 into the buffer of round k
+// once round k's phase A is done, (4) votes of round k - 1 to memory, then
+// the votes buffer may be reused (v_done).
+template <int D>
+__device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
+                           uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_votes)[kS], Sync* sy) {
+  const int lane = threadIdx.x & 63;
+  const int W = a.W;
+  if (ctl_issue_q<D>(a, 0, Q, qbufs[0]) | ctl_issue_q<D>(a, 1, Q, qbufs[1])) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    ctl_finish_q<D>(W, qbufs[0]);
+    ctl_finish_q<D>(W, qbufs[1]);
+  }
+  lds_set(&sy->q_ready, 2u);
+  unsigned on_b = 0, on_c = 0;  // owned rounds whose phase A / B results were awaited
+  for (int k = 0; k < a.rounds + 1; ++k) {
+    const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
+    if (w0.on) {
+      ++on_b;
+      lds_wait_ge(&sy->cnt_b, kSW * on_b, &sy->timeout);
+    }
+    if (ctl_issue_q<D>(a, k + 2, Q, qbufs[k & 1])) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      ctl_finish_q<D>(W, qbufs[k & 1]);
+    }
     lds_set(&sy->q_ready, (unsigned)(k + 3));
     KVSEL_FUSED_CTL_MARK(k, 6);
-    // (4) Votes of round k - 1 to memory (prefix positions only).
     if (w1.on) {
       ++on_c;
       lds_wait_ge(&sy->cnt_c, kSW * on_c, &sy->timeout);
@@ -483,8 +524,37 @@ __device__ void controller(const Launch& a, const __bf16* __restrict__ Q, unsign
       for (int i = lane; i < kS; i += 64)
         if (j0 + i < P) vout[j0 + i] = s_votes[(k - 1) & 1][i];
     }
+    if (k >= 1) lds_set(&sy->v_done, (unsigned)k);  // votes of rounds < k are out of LDS
     KVSEL_FUSED_CTL_MARK(k, 7);
   }
+}
+
+// Residency handshake (thread 0 of each workgroup).  The rounds need every
+// workgroup of the grid running at once, which a plain launch of one
+// workgroup per CU gives on an otherwise idle device but does not promise.
+// Each workgroup counts its arrival; the last arrival decides GO; one that
+// has waited longer than the bound decides ABORT.  Both decisions are a
+// compare-and-swap on one zeroed word, so every workgroup follows the same
+// one, and GO implies that all of them are resident.
+constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
+__device__ __forceinline__ unsigned residency(unsigned* arrive, unsigned* state) {
+  const unsigned n = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if (n == gridDim.x) {
+    unsigned expect = 0u;
+    __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const long long t0 = wall_clock64();
+  unsigned s;
+  while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+    if (wall_clock64() - t0 > kResidencyTicks) {
+      unsigned expect = 0u;
+      __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return s;
 }
 
 template <int D>
@@ -501,11 +571,19 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __shared__ float s_m[2][32], s_iz[2][32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
-  if (threadIdx.x == 0) sy = Sync{0, 0, 0, 0, 0};
+  __shared__ unsigned s_go;
+  if (threadIdx.x == 0) {
+    sy = Sync{0, 0, 0, 0, 0, 0};
+    s_go = residency(status + 1, status + 2);
+  }
   __syncthreads();  // the only workgroup barrier; afterwards waves meet through LDS flags
+  if (s_go != kFusedGo) return;  // not all resident: the two-pass kernels queued next take over
   const int wave = threadIdx.x >> 6;
-  if (wave == kSW) {
-    controller<D>(a, Q, ex, status, votes, row_stats, s_q, s_maxp, s_zp, s_m, s_iz, s_votes, &sy);
+  if (wave >= kSW) {
+    if (wave == kSW)
+      ctl_exchange<D>(a, ex, status, row_stats, s_maxp, s_zp, s_m, s_iz, &sy);
+    else
+      ctl_memory<D>(a, Q, votes, s_q, s_votes, &sy);
     if ((threadIdx.x & 63) == 0 && sy.timeout)
       __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -578,8 +656,9 @@ hipError_t launch_t(const Launch& a, const void* Q, const void* K, unsigned long
   Launch la = a;
   const __bf16* q = (const __bf16*)Q;
   const __bf16* k = (const __bf16*)K;
-  void* args[] = {&la, &q, &k, &ex, &status, &votes, &row_stats};
-  return hipLaunchCooperativeKernel((const void*)window_fused_kernel<D>, dim3(grid), dim3(kThreads), args, 0, st);
+  hipLaunchKernelGGL((window_fused_kernel<D>), dim3(grid), dim3(kThreads), 0, st, la, q, k, ex, status, votes,
+                     row_stats);
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -37,7 +37,8 @@ struct Seg {
   long long idx_off;   // element offset of (b, head 0) in indices
   long long out_off;   // row offset of (b, head 0) in K_out / V_out
   long long vote_off;  // element offset of (b, head 0) in votes / pooled
-  long long part_base; // partial-stat slot of (b, head 0, chunk 0)
+  long long part_base; // two-pass partial-stat slot of (b, head 0, chunk 0)
+  long long fslot_base;  // single-read exchange slot of (b, head 0, chunk 0)
   // single-read scoring schedule (see kvsel_fused.hip)
   int fc;         // chunks per head, ceil(L / S)
   int fhpr;       // heads per round
@@ -73,13 +74,16 @@ enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
 
 // Host-side launchers (return hipSuccess or the launch error).
 // window_stats also zeroes zero_words words at zero (the selection's
-// histograms), which the kernels after it accumulate into.
+// histograms), which the kernels after it accumulate into.  With gate !=
+// nullptr both kernels do nothing when *gate == kFusedGo: the single-read
+// kernel queued before them has already computed the scores.
+constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                float* part_m, float* part_z, uint32_t* zero, long long zero_words,
-                               hipStream_t st);
+                               const unsigned* gate, hipStream_t st);
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                const float* part_m, const float* part_z, float* votes,
-                               float* row_stats, hipStream_t st);
+                               float* row_stats, const unsigned* gate, hipStream_t st);
 // Pooling (pooled may be nullptr: histogram of the input only) with the
 // first-digit histogram of each row added into hist[row][2048] (nullptr: none).
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
@@ -99,10 +103,12 @@ hipError_t launch_threshold(const Launch& a, int rows, const float* scores, cons
 hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, const float* scores,
                        const uint32_t* cut, const uint32_t* segcnt, int32_t* indices, const void* K, const void* V,
                        void* K_out, void* V_out, hipStream_t st);
-// Single-read scoring (cooperative persistent kernel).  fused_positions()
-// gives S for the kernel variant, fused_grid() the co-resident grid (0 if the
-// variant cannot run); launch_fused_scoring() returns hipErrorNotSupported
-// when the shape is not covered.
+// Single-read scoring (persistent kernel, one workgroup per CU).
+// fused_positions() gives S for the kernel variant, fused_grid() the grid (0
+// if the variant cannot run); launch_fused_scoring() returns
+// hipErrorNotSupported when the shape is not covered.  status points at 3
+// zeroed words: error flags, arrivals, and the residency decision
+// (kFusedGo or kFusedAbort), which gates the two-pass kernels queued after.
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
 int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot

@@ -86,13 +86,18 @@ def gpu_internal_topk(gpu_prefix: np.ndarray, gpu_pooled_f32: np.ndarray, n: int
 
 def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto"):
     """Run kvsel_select with every optional output; returns host numpy arrays.
-    `scoring` picks the scoring path (auto, two_pass, single_read)."""
+    `scoring` picks the scoring path (auto, two_pass, single_read, or
+    single_read_fallback: the single-read launch forced onto its two-pass
+    fallback)."""
     from prompt_kv_selection_amd import binding as B
-    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[scoring])
+    fallback = scoring == "single_read_fallback"
+    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING["single_read" if fallback else scoring])
+    B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 1 if fallback else 0)
     try:
         return _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype)
     finally:
         B.kvsel_set_option(B.KVSEL_OPT_SCORING, 0)
+        B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 0)
 
 
 def single_read_covers(dtype, D, W):

@@ -128,7 +128,11 @@ def test_options(B):
     lib = B.lib
     assert lib.kvsel_get_option(0) == 0
     assert lib.kvsel_set_option(0, 3) == -1
-    assert lib.kvsel_set_option(1, 0) == -1
+    assert lib.kvsel_get_option(1) == 0                       # forced fallback off
+    assert lib.kvsel_set_option(1, 2) == -1
+    assert lib.kvsel_set_option(1, 1) == 0 and lib.kvsel_get_option(1) == 1
+    assert lib.kvsel_set_option(1, 0) == 0 and lib.kvsel_get_option(1) == 0
+    assert lib.kvsel_set_option(2, 0) == -1
     assert lib.kvsel_get_option(5) == -1
     assert lib.kvsel_set_option(0, 1) == 0 and lib.kvsel_get_option(0) == 1
     assert lib.kvsel_set_option(0, 0) == 0 and lib.kvsel_get_option(0) == 0

@@ -123,6 +123,28 @@ def test_random_cases(B, case, scoring):
     check_gather(out, Kd, Vd, C, L)
 
 
+FALLBACK_CASES = [c for c in CASES if single_read_covers(c[0], c[1], c[4]) and c[3] >= c[5]][:3]
+
+
+@pytest.mark.parametrize("case", FALLBACK_CASES, ids=[f"L{c[3]}-W{c[4]}-C{c[5]}" for c in FALLBACK_CASES])
+def test_single_read_fallback(B, case):
+    """The single-read launch told (from the host) that its grid is not
+    resident exits at once; the two-pass kernels queued after it must then
+    produce every score."""
+    dtype, D, H, L, W, C, kernel, pooling = case
+    w = WL.Workload("case", seed=L * 11 + W, heads=H, L=L, W=W, C=C, D=D, dtype=dtype, kernel=kernel,
+                    pooling=pooling, keys="spike", spike_frac=0.02)
+    Q, K, V = WL.layer_arrays(w)
+    log(f"single-read fallback case {case}")
+    Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
+    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, "single_read_fallback")
+    for h in range(H):
+        ref = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h], dtype),
+                              WL.to_float64(V[h], dtype), W, C, kernel, pooling)
+        check_head(out, h, ref, L, W, C, f"fallback {case} head {h}")
+    check_gather(out, Kd, Vd, C, L)
+
+
 @pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
 def test_identical_keys_give_identical_scores(B, scoring):
     w = WL.reduced(WL.get("tied_h64_l128k"), L=8192, heads=2)
