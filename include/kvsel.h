@@ -84,8 +84,8 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  * Both give the same indices and K/V rows up to the documented rounding of
  * the scores.  The single-read kernel needs all its workgroups (one per CU)
  * resident at once; it checks that at start, and if the device is shared
- * with other work and they are not, the two-pass kernels queued after it
- * compute the scores instead (same results, K read twice).
+ * with other work and they are not, it scores each head inside a single
+ * workgroup instead (two passes over that head's K; same results, slower).
  * KVSEL_OPT_FORCE_FALLBACK (testing): 1 makes every single-read launch take
  *   that fallback; 0 (default) off.
  * Not thread-safe with respect to concurrent calls. */

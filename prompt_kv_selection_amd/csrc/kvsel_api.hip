@@ -292,7 +292,6 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     uint32_t* gcut = (uint32_t*)((char*)cut + (size_t)b0 * p.heads * kCutBytes);
     uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
-    const unsigned* gate = nullptr;
     if (items > 0 && use_fused) {
       unsigned* gstatus = status + 4 * (b0 / kMaxSegs);
       if (g_force_fallback) {
@@ -302,18 +301,13 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       e = timed("window_fused", st,
                 [&] { return launch_fused_scoring(a, Q, K, counters, gstatus, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
-      // The two-pass kernels follow as the fallback: they return at once
-      // unless the single-read kernel found its grid not resident.
-      gate = gstatus + 2;
-    }
-    if (items > 0) {
+    } else if (items > 0) {
       e = timed("window_stats", st, [&] {
-        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, gate, st);
+        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, st);
       });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
-      e = timed("window_votes", st, [&] {
-        return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, gate, st);
-      });
+      e = timed("window_votes", st,
+                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     }
     if (items > 0) {

@@ -529,6 +529,150 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
   }
 }
 
+// Fallback when the grid is not all resident (ABORT): the workgroups take
+// whole (segment, head) units from a counter and score each one alone, in
+// two passes over its K (row statistics, then votes), so no workgroup ever
+// waits for another.  The streaming waves do the passes; every wave of the
+// workgroup takes part in each barrier.  Slower than the round schedule,
+// same arithmetic.
+template <int D>
+__device__ __forceinline__ void solo_pass(const Launch& a, const Seg& s, const __bf16* __restrict__ kh, int limit,
+                                          bool votes_pass, uint4 (*ring)[TileGeom<D>::PIECES], const uint4* qbuf,
+                                          const float* s_m, const float* s_iz, float* vout, float (&m)[16],
+                                          float (&z)[16]) {
+  using G = TileGeom<D>;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const int L = s.L, P = L - a.W;
+  const int tiles = (limit + 31) / 32;
+  const int nw = tiles > wave ? (tiles - wave + kSW - 1) / kSW : 0;  // tiles wave, wave + kSW, ...
+  float mr[16], iz[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    mr[r] = votes_pass ? s_m[acc_row(r, g)] : 0.f;
+    iz[r] = votes_pass ? s_iz[acc_row(r, g)] : 0.f;
+  }
+  int issued = 0;
+  for (; issued < kNBuf && issued < nw; ++issued)
+    issue_tile<D>(kh, L, (wave + kSW * issued) * 32, ring[issued % kNBuf], lane);
+  for (int i = 0; i < nw; ++i) {
+    wait_tiles<D>(issued - i - 1);
+    const uint4* tile = ring[i % kNBuf];
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int c = 2 * kk + g;
+      const int off = n * G::PR + (c ^ (n & (G::PR - 1)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qbuf[off]),
+                                                    __builtin_bit_cast(bf16x8, tile[off]), acc, 0, 0, 0);
+    }
+    lds_fence();
+    if (issued < nw) {
+      issue_tile<D>(kh, L, (wave + kSW * issued) * 32, ring[issued % kNBuf], lane);
+      ++issued;
+    }
+    const int j = (wave + kSW * i) * 32 + n;
+    if (votes_pass) {
+      float tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot += exp2_fast(acc[r] * a.scale2 - mr[r]) * iz[r];
+      const float other = __shfl_xor(tot, 32);
+      const float v = g == 0 ? tot + other : other + tot;
+      if (g == 0 && j < P) vout[j] = v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, g);
+        const float x = (j < L && j <= P + row) ? acc[r] * a.scale2 : -INFINITY;
+        const float d = x - m[r];
+        const float e = exp2_fast(-fabsf(d));
+        z[r] = d > 0.f ? fmaf(z[r], e, 1.f) : z[r] + e;
+        m[r] = fmaxf(m[r], x);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int D>
+__device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                           unsigned* __restrict__ counter, float* __restrict__ votes, float* __restrict__ row_stats,
+                           uint4 (*s_ring)[kNBuf][TileGeom<D>::PIECES], uint4* qbuf, float* s_maxp, float* s_zp,
+                           float* s_m, float* s_iz) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, W = a.W;
+  const bool streams = wave < kSW;
+  const Seg& last = a.seg[a.n - 1];
+  const unsigned units = (unsigned)(last.row0 + last.nh);
+  __shared__ unsigned s_unit;
+  for (;;) {
+    if (threadIdx.x == 0) s_unit = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const unsigned u = s_unit;
+    __syncthreads();
+    if (u >= units) break;
+    const int e = find_seg<kFieldRow>(a, (int)u);
+    const Seg& s = a.seg[e];
+    if (s.L < s.C) continue;  // bypass: nothing to score
+    const int h = s.h0 + ((int)u - s.row0);
+    const int hs = s.b * a.heads + h;
+    if (wave == 0) {
+      issue_tile<D>(Q + (long long)hs * W * D, W, 0, qbuf, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      ctl_finish_q<D>(W, qbuf);
+    }
+    __syncthreads();
+    const __bf16* kh = K + s.kv_off + (long long)h * s.L * D;
+    float m[16], z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      m[r] = kNegBig;
+      z[r] = 0.f;
+    }
+    if (streams) solo_pass<D>(a, s, kh, s.L, false, s_ring[wave], qbuf, s_m, s_iz, nullptr, m, z);
+    // This wave's (max, sum) per row, then the waves merged in order.
+    if (streams) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float mh0 = half_max(m[r]);
+      const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 31));
+      const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 63));
+      const float mh = g == 0 ? m0 : m1;
+      const float zz = half_sum(z[r] > 0.f ? z[r] * exp2_fast(m[r] - mh) : 0.f);
+      if ((lane & 31) == 31) {
+        s_maxp[wave * 32 + acc_row(r, g)] = mh;
+        s_zp[wave * 32 + acc_row(r, g)] = zz;
+      }
+    }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < W) {
+      const int i = threadIdx.x;
+      float M = s_maxp[i];
+      for (int v = 1; v < kSW; ++v) M = fmaxf(M, s_maxp[v * 32 + i]);
+      float Z = 0.f;
+      for (int v = 0; v < kSW; ++v) {
+        const float zv = s_zp[v * 32 + i];
+        if (zv > 0.f) Z += zv * exp2_fast(s_maxp[v * 32 + i] - M);
+      }
+      s_m[i] = M;
+      s_iz[i] = 1.f / Z;
+      if (row_stats != nullptr) {
+        float* rs = row_stats + ((long long)hs * W + i) * 2;
+        rs[0] = M * kLn2;
+        rs[1] = Z;
+      }
+    } else if ((int)threadIdx.x < 32) {
+      s_m[threadIdx.x] = 0.f;  // rows past W: zero queries, dropped by 1/Z = 0
+      s_iz[threadIdx.x] = 0.f;
+    }
+    __syncthreads();
+    float* vout = votes + s.vote_off + (long long)h * s.vote_ld;
+    if (streams) solo_pass<D>(a, s, kh, s.L - W, true, s_ring[wave], qbuf, s_m, s_iz, vout, m, z);
+    __syncthreads();  // s_m, s_iz and qbuf are rewritten for the next unit
+  }
+}
+
 // Residency handshake (thread 0 of each workgroup).  The rounds need every
 // workgroup of the grid running at once, which a plain launch of one
 // workgroup per CU gives on an otherwise idle device but does not promise.
@@ -576,9 +720,12 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
     sy = Sync{0, 0, 0, 0, 0, 0};
     s_go = residency(status + 1, status + 2);
   }
-  __syncthreads();  // the only workgroup barrier; afterwards waves meet through LDS flags
-  if (s_go != kFusedGo) return;  // not all resident: the two-pass kernels queued next take over
+  __syncthreads();  // afterwards waves meet through LDS flags (or, in the fallback, barriers)
   const int wave = threadIdx.x >> 6;
+  if (s_go != kFusedGo) {  // not all resident: whole heads, one workgroup each
+    solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
+    return;
+  }
   if (wave >= kSW) {
     if (wave == kSW)
       ctl_exchange<D>(a, ex, status, row_stats, s_maxp, s_zp, s_m, s_iz, &sy);

@@ -74,16 +74,13 @@ enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
 
 // Host-side launchers (return hipSuccess or the launch error).
 // window_stats also zeroes zero_words words at zero (the selection's
-// histograms), which the kernels after it accumulate into.  With gate !=
-// nullptr both kernels do nothing when *gate == kFusedGo: the single-read
-// kernel queued before them has already computed the scores.
-constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
+// histograms), which the kernels after it accumulate into.
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                float* part_m, float* part_z, uint32_t* zero, long long zero_words,
-                               const unsigned* gate, hipStream_t st);
+                               hipStream_t st);
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                const float* part_m, const float* part_z, float* votes,
-                               float* row_stats, const unsigned* gate, hipStream_t st);
+                               float* row_stats, hipStream_t st);
 // Pooling (pooled may be nullptr: histogram of the input only) with the
 // first-digit histogram of each row added into hist[row][2048] (nullptr: none).
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
@@ -106,9 +103,11 @@ hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, 
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns
-// hipErrorNotSupported when the shape is not covered.  status points at 3
-// zeroed words: error flags, arrivals, and the residency decision
-// (kFusedGo or kFusedAbort), which gates the two-pass kernels queued after.
+// hipErrorNotSupported when the shape is not covered.  status points at 4
+// zeroed words: error flags, arrivals, the residency decision (kFusedGo or
+// kFusedAbort; a host-written kFusedAbort forces the fallback) and the
+// fallback's work counter.
+constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
 int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot

@@ -315,13 +315,11 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
                                                                   float* __restrict__ part_m,
                                                                   float* __restrict__ part_z,
                                                                   uint32_t* __restrict__ zero,
-                                                                  long long zero_words,
-                                                                  const unsigned* __restrict__ gate) {
+                                                                  long long zero_words) {
   using G = TileGeom<T, D>;
   __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
   __shared__ float sm[2][kWaves][RB * 32], sz[2][kWaves][RB * 32];
-  if (gate != nullptr && __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kFusedGo) return;
   const int W = a.W;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
@@ -491,13 +489,12 @@ template <typename T, int D, int RB>
 __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
     const Launch a, int items, const T* __restrict__ Q, const T* __restrict__ K,
     const float* __restrict__ part_m, const float* __restrict__ part_z, float* __restrict__ votes,
-    float* __restrict__ row_stats, const unsigned* __restrict__ gate) {
+    float* __restrict__ row_stats) {
   using G = TileGeom<T, D>;
   __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
   __shared__ float s_m[RB * 32], s_iz[RB * 32];
   __shared__ float s_gm[kWaves * 64], s_gz[kWaves * 64];
-  if (gate != nullptr && __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kFusedGo) return;
   const int W = a.W;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
@@ -579,19 +576,19 @@ static int resident_grid(Kern kern, int items) {
 
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
-                          uint32_t* zero, long long zero_words, const unsigned* gate, hipStream_t st) {
+                          uint32_t* zero, long long zero_words, hipStream_t st) {
   const int grid = resident_grid(window_stats_kernel<T, D, RB>, items);
   hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, zero, zero_words, gate);
+                     (const T*)Q, (const T*)K, pm, pz, zero, zero_words);
   return hipGetLastError();
 }
 
 template <typename T, int D, int RB>
 static hipError_t votes_t(const Launch& a, int items, const void* Q, const void* K, const float* pm,
-                          const float* pz, float* votes, float* rs, const unsigned* gate, hipStream_t st) {
+                          const float* pz, float* votes, float* rs, hipStream_t st) {
   const int grid = resident_grid(window_votes_kernel<T, D, RB>, items);
   hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, votes, rs, gate);
+                     (const T*)Q, (const T*)K, pm, pz, votes, rs);
   return hipGetLastError();
 }
 
@@ -624,14 +621,14 @@ static hipError_t votes_t(const Launch& a, int items, const void* Q, const void*
 
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                float* part_m, float* part_z, uint32_t* zero, long long zero_words,
-                               const unsigned* gate, hipStream_t st) {
-  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, zero, zero_words, gate, st);
+                               hipStream_t st) {
+  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, zero, zero_words, st);
 }
 
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                const float* part_m, const float* part_z, float* votes,
-                               float* row_stats, const unsigned* gate, hipStream_t st) {
-  KVSEL_DISPATCH(votes_t, a, items, Q, K, part_m, part_z, votes, row_stats, gate, st);
+                               float* row_stats, hipStream_t st) {
+  KVSEL_DISPATCH(votes_t, a, items, Q, K, part_m, part_z, votes, row_stats, st);
 }
 
 }  // namespace kvsel

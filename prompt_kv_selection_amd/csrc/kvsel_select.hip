@@ -63,23 +63,6 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_
   return v + base;
 }
 
-// Wave-aggregated append position: lanes with `pred` get consecutive slots
-// starting at the returned base (one LDS atomic per wave).
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter, uint32_t& slot) {
-  const unsigned long long mask = __ballot(pred);
-  if (mask == 0) {  // wave-uniform: nothing to append
-    slot = 0;
-    return 0;
-  }
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-  const int leader = __ffsll((long long)mask) - 1;
-  uint32_t base = 0;
-  if (mask != 0 && (int)(threadIdx.x & 63) == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader < 0 ? 0 : leader);
-  slot = base + below;
-  return (uint32_t)__popcll(mask);
-}
-
 // Given hist[] (LDS) of the digits of the candidates, find the digit holding
 // the need-th largest: returns (digit, rank of the target inside the digit).
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
@@ -116,6 +99,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_
 constexpr int kCand = 16384;
 constexpr int kPoolSpan = 8;
 constexpr int kMaxPoolRadius = 31;  // pooling width up to 63
+static_assert(2 * kMaxPoolRadius < kPoolBlock, "the right halo is loaded by one thread per position");
 
 __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a, const float* __restrict__ scores,
                                                                  const uint32_t* __restrict__ ghist,
@@ -156,10 +140,16 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a,
   __syncthreads();
 
   // The 64 positions a wave reads at once are consecutive and segments are
-  // multiples of 64 long, so each wave's counts go to one segment.
+  // multiples of 64 long, so each wave's counts go to one segment.  The
+  // digit-d1 positions are appended without contended atomics: every wave
+  // counts its own, wave 0 turns the counts into offsets, then every wave
+  // writes its positions (still in registers) at its offset.
   KVSEL_SELECT_MARK(1);
   {
-    constexpr int U = 16;  // independent loads in flight per thread
+    constexpr int U = 32;  // independent loads in flight per thread (a 32K row in one batch)
+    constexpr int kWavesPerBlock = kTopkThreads / 64;
+    __shared__ uint32_t wave_n[kWavesPerBlock];
+    const int wv = tid >> 6;
     for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
       uint32_t kk[U];
 #pragma unroll
@@ -167,6 +157,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a,
         const int j = j0 + u * kTopkThreads + tid;
         kk[u] = j < P ? key[j] : 0u;
       }
+      uint32_t mine = 0;  // this wave's digit-d1 positions in the block
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * kTopkThreads + tid;
@@ -174,14 +165,27 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a,
         const uint32_t d = kk[u] >> 21;
         const unsigned long long above = __ballot(j < P && d > d1);
         if (above != 0 && lane == 0) atomicAdd(&sgt[jw / segsz], (uint32_t)__popcll(above));
-        if (in_lds) {
-          const bool hit = j < P && d == d1;
-          uint32_t slot;
-          wave_append(hit, &s_ncand, slot);
+        mine += (uint32_t)__popcll(__ballot(j < P && d == d1));
+      }
+      if (in_lds) {
+        if (lane == 0) wave_n[wv] = mine;
+        __syncthreads();
+        uint32_t base = s_ncand;
+        for (int v = 0; v < wv; ++v) base += wave_n[v];
+        __syncthreads();
+        if (tid == kTopkThreads - 1) s_ncand = base + mine;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * kTopkThreads + tid;
+          const bool hit = j < P && (kk[u] >> 21) == d1;
+          const unsigned long long m = __ballot(hit);
+          const uint32_t slot =
+              base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
           if (hit && slot < (uint32_t)kCand) {
             cand_key[slot] = kk[u];
             cand_pos[slot] = j;
           }
+          base += (uint32_t)__popcll(m);
         }
       }
     }
@@ -336,6 +340,16 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
     return;
   }
 
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
+  const int end = min(P, (seg + 1) * segsz);
+  // The first pass's scores are loaded before the segment counts so that the
+  // two latencies overlap.
+  uint32_t first[kEmitPer];
+#pragma unroll
+  for (int u = 0; u < kEmitPer; ++u) {
+    const int j = seg * segsz + u * kEmitThreads + tid;
+    first[u] = j < end ? key[j] : 0u;
+  }
   // Picks above tau and tau-equal positions in the segments before this one.
   const uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
   if (tid < 2) s_before[tid] = 0u;
@@ -352,9 +366,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
   __syncthreads();
   const uint32_t tau = cut[2 * row], need_eq = cut[2 * row + 1];
   uint32_t gt_run = s_before[0], eq_run = s_before[1];
-  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
 
-  const int end = min(P, (seg + 1) * segsz);
   for (int j0 = seg * segsz; j0 < end; j0 += kSegUnit) {
     // Coalesced loads staged through LDS; thread t then scans positions
     // j0 + t * kEmitPer + u in order (rows of kEmitPer + 1 words: no conflicts).
@@ -362,7 +374,8 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
     for (int u = 0; u < kEmitPer; ++u) {
       const int i = u * kEmitThreads + tid;
       const int j = j0 + i;
-      stage[(i / kEmitPer) * (kEmitPer + 1) + i % kEmitPer] = j < end ? key[j] : 0u;
+      const uint32_t v = j0 == seg * segsz ? first[u] : (j < end ? key[j] : 0u);
+      stage[(i / kEmitPer) * (kEmitPer + 1) + i % kEmitPer] = v;
     }
     __syncthreads();
     uint32_t kk[kEmitPer];
@@ -475,10 +488,21 @@ __global__ __launch_bounds__(kPoolBlock) void pool_hist_kernel(const Launch a, c
   // or excluded (max: -inf never wins, the centre is always in range).
   constexpr int kSpan = kPoolBlock * kPoolSpan;
   __shared__ float tile[kSpan + 2 * kMaxPoolRadius];
+  __shared__ float res_out[kSpan];  // pooled scores, written out coalesced
   const float pad = a.pooling == 1 ? -INFINITY : 0.f;
-  for (int i = threadIdx.x; i < kSpan + 2 * r; i += kPoolBlock) {
-    const int p = base - r + i;
-    tile[i] = (p >= 0 && p < P) ? v[p] : pad;
+  {
+    // Every load is issued before the first LDS write (one latency).
+    float tv[kPoolSpan];
+#pragma unroll
+    for (int u = 0; u < kPoolSpan; ++u) {
+      const int p = base - r + u * kPoolBlock + (int)threadIdx.x;
+      tv[u] = (p >= 0 && p < P) ? v[p] : pad;
+    }
+    const int ph = base - r + kSpan + (int)threadIdx.x;  // right halo, 2r <= 62 < kPoolBlock
+    const float th = ((int)threadIdx.x < 2 * r && ph >= 0 && ph < P) ? v[ph] : pad;
+#pragma unroll
+    for (int u = 0; u < kPoolSpan; ++u) tile[u * kPoolBlock + threadIdx.x] = tv[u];
+    if ((int)threadIdx.x < 2 * r) tile[kSpan + threadIdx.x] = th;
   }
   __syncthreads();
   // Each thread pools kPoolSpan consecutive positions; equal first digits of
@@ -506,7 +530,7 @@ __global__ __launch_bounds__(kPoolBlock) void pool_hist_kernel(const Launch a, c
         default: res = avg_sorted_any(c, kw); break;
       }
     }
-    if (o) o[j] = res;
+    res_out[i0 + u] = res;
     const uint32_t bin = __float_as_uint(res) >> 21;
     if (bin != run_bin) {
       if (run_len && ghist != nullptr) atomicAdd(&hist[run_bin], run_len);
@@ -516,8 +540,10 @@ __global__ __launch_bounds__(kPoolBlock) void pool_hist_kernel(const Launch a, c
     ++run_len;
   }
   if (run_len && ghist != nullptr) atomicAdd(&hist[run_bin], run_len);
+  __syncthreads();
+  if (o)
+    for (int i = threadIdx.x; i < kSpan && base + i < P; i += kPoolBlock) o[base + i] = res_out[i];
   if (ghist != nullptr) {
-    __syncthreads();
     uint32_t* gh = ghist + (long long)row * 2048;
     for (int d = threadIdx.x; d < 2048; d += kPoolBlock)
       if (hist[d]) atomicAdd(gh + d, hist[d]);
