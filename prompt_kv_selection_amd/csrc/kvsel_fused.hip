@@ -495,11 +495,10 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
                            uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_votes)[kS], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
-  if (ctl_issue_q<D>(a, 0, Q, qbufs[0]) | ctl_issue_q<D>(a, 1, Q, qbufs[1])) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    ctl_finish_q<D>(W, qbufs[0]);
-    ctl_finish_q<D>(W, qbufs[1]);
-  }
+  // Qwin of rounds 0 and 1 was issued before the residency handshake.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  ctl_finish_q<D>(W, qbufs[0]);
+  ctl_finish_q<D>(W, qbufs[1]);
   lds_set(&sy->q_ready, 2u);
   unsigned on_b = 0, on_c = 0;  // owned rounds whose phase A / B results were awaited
   for (int k = 0; k < a.rounds + 1; ++k) {
@@ -716,13 +715,24 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
   __shared__ unsigned s_go;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // The first K tiles and Qwin of rounds 0 and 1 are issued before the
+  // residency handshake, so their latency overlaps it.
+  Stream st{0u};
+  if (wave < kSW) {
+    for (int q = 0; q < kNBuf; ++q) stream_issue<D>(a, K, q, wave, lane, s_ring[wave], st);
+  } else if (wave == kSW + 1) {
+    ctl_issue_q<D>(a, 0, Q, s_q[0]);
+    ctl_issue_q<D>(a, 1, Q, s_q[1]);
+  }
   if (threadIdx.x == 0) {
     sy = Sync{0, 0, 0, 0, 0, 0};
     s_go = residency(status + 1, status + 2);
   }
   __syncthreads();  // afterwards waves meet through LDS flags (or, in the fallback, barriers)
-  const int wave = threadIdx.x >> 6;
   if (s_go != kFusedGo) {  // not all resident: whole heads, one workgroup each
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads above land before LDS is reused
     solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
     return;
   }
@@ -735,10 +745,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
       __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  const int lane = threadIdx.x & 63;
   uint4 (*ring)[G::PIECES] = s_ring[wave];
-  Stream st{0u};
-  for (int q = 0; q < kNBuf; ++q) stream_issue<D>(a, K, q, wave, lane, ring, st);
   float xa[kTT][16], xb[kTT][16];
   // Step k streams round k into one register set (with this wave's row
   // statistics), then votes round k - 1 from the other set; the sets swap
