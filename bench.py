@@ -48,8 +48,10 @@ def kernel_alg_bytes(name, w, nch):
         return H * P * D * e + q + H * nch * W * 8 + H * P * 4
     if name == "pool":              # votes in, pooled out
         return H * P * 8
-    if name == "threshold":         # pooled scores read once, histograms, segment counts
-        return H * P * 4 + H * 2048 * 4
+    if name == "candidates":        # pooled scores read once (the histogram reads hit L2)
+        return H * P * 4
+    if name == "threshold":         # histograms, segment counts (the candidates: data-dependent, few)
+        return H * 2048 * 4 + H * 2 * 512 * 4
     if name == "emit":              # pooled scores, kept K and V rows read and written, indices
         return H * P * 4 + 4 * H * C * D * e + H * C * 4
     if name == "fill":              # per-head exchange records cleared
@@ -64,9 +66,24 @@ def path_alg_bytes(w):
     return w.heads * (w.L * w.D * e + w.W * w.D * e + 4 * w.C * w.D * e + 4 * w.C)
 
 
-def source_digest():
+# Sources each kernel is compiled from: stored counter bytes stay valid while
+# these files are unchanged.
+KERNEL_SOURCES = {
+    "window_fused": ("kvsel_fused.hip", "kvsel_internal.h"),
+    "fill": ("kvsel_fused.hip", "kvsel_internal.h"),
+    "window_stats": ("kvsel_score.hip", "kvsel_internal.h"),
+    "window_votes": ("kvsel_score.hip", "kvsel_internal.h"),
+    "pool": ("kvsel_select.hip", "kvsel_internal.h"),
+    "candidates": ("kvsel_select.hip", "kvsel_internal.h"),
+    "threshold": ("kvsel_select.hip", "kvsel_internal.h"),
+    "emit": ("kvsel_select.hip", "kvsel_internal.h"),
+    "gather": ("kvsel_select.hip", "kvsel_internal.h"),
+}
+
+
+def source_digest(kernel):
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "prompt_kv_selection_amd", "csrc"))):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "prompt_kv_selection_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -74,14 +91,14 @@ def source_digest():
 
 def traffic_from_profiles(kernel):
     """Counter-measured HBM bytes per launch, if the stored counters were
-    taken on the current kernel sources."""
+    taken on the kernel's current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get("kernels", {}).get(kernel)
-    if not ent or rec.get("source_digest") != source_digest():
+    if not ent or kernel not in KERNEL_SOURCES or ent.get("source_digest") != source_digest(kernel):
         return None
     return ent.get("bytes_per_launch")
 

@@ -222,6 +222,9 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   unsigned* status = (unsigned*)(ws + p.off_status);
   uint32_t* cut = (uint32_t*)(ws + p.off_cut);
   uint32_t* segcnt = (uint32_t*)(ws + p.off_segcnt);
+  // The selection's candidate scores reuse the workspace votes buffer, which
+  // nothing reads after pooling (or which is unused when votes_opt is given).
+  uint32_t* cand = (uint32_t*)(ws + p.off_votes);
 
   // Single-read scoring needs every head of a round co-resident: each prompt
   // must fit one round of the grid (ceil(L / S) <= grid).
@@ -313,7 +316,10 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     if (items > 0) {
       e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, ghist, st); });
       if (e != hipSuccess) return device_error(e, "pool launch");
-      e = timed("threshold", st, [&] { return launch_threshold(a, rows, pooled, ghist, gcut, gseg, st); });
+      e = timed("candidates", st,
+                [&] { return launch_candidates(a, rows, maxP, pooled, ghist, cand, gseg, st); });
+      if (e != hipSuccess) return device_error(e, "candidates launch");
+      e = timed("threshold", st, [&] { return launch_threshold(a, rows, ghist, cand, gcut, gseg, st); });
       if (e != hipSuccess) return device_error(e, "threshold launch");
     }
     e = timed("emit", st, [&] {
@@ -399,9 +405,9 @@ int kvsel_select(const void* Qwin, const void* K, const void* V, int L, int W, i
                              row_stats_opt, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
 }
 
-static size_t topk_workspace(int rows) {
+static size_t topk_workspace(int rows, int n) {
   return align256((size_t)rows * 2048 * 4) + align256((size_t)rows * kCutBytes) +
-         align256((size_t)rows * kSegCntBytes);
+         align256((size_t)rows * kSegCntBytes) + align256((size_t)rows * n * 4);
 }
 
 size_t kvsel_topk_workspace_bytes(int rows, int n) {
@@ -410,7 +416,7 @@ size_t kvsel_topk_workspace_bytes(int rows, int n) {
     return 0;
   }
   ok();
-  return topk_workspace(rows);
+  return topk_workspace(rows, n);
 }
 
 int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out, void* workspace,
@@ -421,7 +427,7 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   if (ld_out < count) return fail(KVSEL_EINVAL, "ld_out %d is smaller than count %d", ld_out, count);
   if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
-  const size_t need = topk_workspace(rows);
+  const size_t need = topk_workspace(rows, n);
   if (workspace_bytes < need)
     return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
   Launch a{};
@@ -440,11 +446,14 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   uint32_t* hist = (uint32_t*)workspace;
   uint32_t* cut = (uint32_t*)((char*)workspace + align256((size_t)rows * 2048 * 4));
   uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
+  uint32_t* cand = (uint32_t*)((char*)segcnt + align256((size_t)rows * kSegCntBytes));
   hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
   if (e != hipSuccess) return device_error(e, "fill launch");
   e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
   if (e != hipSuccess) return device_error(e, "histogram launch");
-  e = timed("threshold", st, [&] { return launch_threshold(a, rows, scores, hist, cut, segcnt, st); });
+  e = timed("candidates", st, [&] { return launch_candidates(a, rows, n, scores, hist, cand, segcnt, st); });
+  if (e != hipSuccess) return device_error(e, "candidates launch");
+  e = timed("threshold", st, [&] { return launch_threshold(a, rows, hist, cand, cut, segcnt, st); });
   if (e != hipSuccess) return device_error(e, "threshold launch");
   e = timed("emit", st, [&] {
     return launch_emit(a, rows, n, 0, scores, cut, segcnt, out, nullptr, nullptr, nullptr, nullptr, st);

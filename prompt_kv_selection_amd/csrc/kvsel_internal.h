@@ -85,17 +85,22 @@ hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void
 // first-digit histogram of each row added into hist[row][2048] (nullptr: none).
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled,
                        uint32_t* hist, hipStream_t st);
-// Top-(C-W) per row given the first-digit histograms, in two launches.
-// launch_threshold finds each row's threshold score and how many positions
-// of each segment (seg_size positions) lie above it or on it, into cut
-// (2 words per row) and segcnt (2 * kMaxSegRow words per row).
-// launch_emit writes every row's picks ascending, then the window positions
-// (a.window), and copies their K and V rows when K != nullptr (dtype, D give
-// the row size); bypass rows (L < C) keep every position.
+// Top-(C-W) per row given the first-digit histograms, in three launches.
+// launch_candidates counts, per segment of a row (seg_size positions), the
+// scores above the boundary digit and copies the boundary digit's scores to
+// cand (one word per score, same layout as scores).  launch_threshold finds
+// each row's threshold score from them and how many picks above it and
+// positions on it precede each segment, into cut (2 words per row) and
+// segcnt (2 * kMaxSegRow words per row).  launch_emit writes every row's
+// picks ascending, then the window positions (a.window), and copies their K
+// and V rows when K != nullptr (dtype, D give the row size); bypass rows
+// (L < C) keep every position.
 constexpr int kSegUnit = 2048;    // positions per emit pass
 constexpr int kMaxSegRow = 512;   // emit segments per row
 int selection_seg_size(long long max_positions);
-hipError_t launch_threshold(const Launch& a, int rows, const float* scores, const uint32_t* hist, uint32_t* cut,
+hipError_t launch_candidates(const Launch& a, int rows, int max_n, const float* scores, const uint32_t* hist,
+                             uint32_t* cand, uint32_t* segcnt, hipStream_t st);
+hipError_t launch_threshold(const Launch& a, int rows, const uint32_t* hist, const uint32_t* cand, uint32_t* cut,
                             uint32_t* segcnt, hipStream_t st);
 hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, const float* scores,
                        const uint32_t* cut, const uint32_t* segcnt, int32_t* indices, const void* K, const void* V,

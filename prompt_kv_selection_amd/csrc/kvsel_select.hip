@@ -17,10 +17,12 @@
 // order like the values.  A most-significant-first radix select (digits of
 // 11, 11 and 10 bits) finds the threshold pattern tau of the (C-W)-th largest
 // score and how many tau-equal positions are still needed.  The first digit's
-// histogram is built by the pooling kernel across many workgroups; one
-// 1024-thread workgroup per (sequence, head) row then gathers the positions
-// of the boundary digit into LDS, finishes the select there and counts, per
-// segment of the row, the positions above tau and on tau.  An emit workgroup
+// histogram is built by the pooling kernel across many workgroups.  A
+// candidates workgroup per (segment, row) then counts its positions above the
+// boundary digit and copies the boundary digit's scores into the segment's
+// range of a candidate buffer; one 1024-thread workgroup per row gathers the
+// (few) candidates into LDS, finishes the select there and turns the
+// per-segment counts above tau and on tau into prefixes.  An emit workgroup
 // per segment then knows how many picks precede it: it scans its positions
 // in index order, writes its picks (the lowest tau-equal indices first) at
 // their final slots, and copies their K and V rows.
@@ -65,14 +67,15 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_
 
 // Given hist[] (LDS) of the digits of the candidates, find the digit holding
 // the need-th largest: returns (digit, rank of the target inside the digit).
+template <int NT>
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
                                            uint32_t* s_digit, uint32_t* s_need) {
   const int tid = threadIdx.x;
-  const int per = nb / kTopkThreads;
+  const int per = nb / NT;
   uint32_t local = 0;
   for (int u = 0; u < per; ++u) local += hist[nb - 1 - (tid * per + u)];
   uint32_t total;
-  const uint32_t incl = block_scan<kTopkThreads>(local, sh, total);
+  const uint32_t incl = block_scan<NT>(local, sh, total);
   const uint32_t excl = incl - local;
   if (excl < need && need <= incl) {
     uint32_t cum = excl;
@@ -89,110 +92,161 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb, uint32_
   __syncthreads();
 }
 
-// Threshold kernel: one 1024-thread workgroup per (sequence, head) row.  The
-// first digit (bits 31..21) comes from the histogram the pooling kernel built.
-// One pass over the row counts, per segment, the positions whose digit is
-// above it and gathers the positions of that digit (key and index) into LDS,
-// where the remaining 21 bits are resolved; when the digit holds more than
-// kCand positions the remaining digits read the row instead.  The digit's
-// positions above and on tau are then added to the segment counts.
 constexpr int kCand = 16384;
 constexpr int kPoolSpan = 8;
 constexpr int kMaxPoolRadius = 31;  // pooling width up to 63
 static_assert(2 * kMaxPoolRadius < kPoolBlock, "the right halo is loaded by one thread per position");
 
-__global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a, const float* __restrict__ scores,
-                                                                 const uint32_t* __restrict__ ghist,
+// Candidates kernel: workgroup (segment, row).  Every workgroup of a row
+// derives the same first digit d1 (bits 31..21 of the threshold) from the
+// row's histogram, counts its segment's positions whose digit is above d1
+// and copies the scores whose digit is d1 (the candidates) to the start of
+// the segment's own range of the row's candidate buffer.  The segment's two
+// counts go to segcnt: [q] above d1, [kMaxSegRow + q] candidates.
+constexpr int kCandThreads = 256;
+constexpr int kCandPer = kSegUnit / kCandThreads;
+
+__global__ __launch_bounds__(kCandThreads) void candidates_kernel(const Launch a, const float* __restrict__ scores,
+                                                                  const uint32_t* __restrict__ ghist,
+                                                                  uint32_t* __restrict__ cand,
+                                                                  uint32_t* __restrict__ segcnt) {
+  const int row = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  if (s.L < s.C) return;  // bypass: every position is kept
+  const int h = s.h0 + (row - s.row0);
+  const int W = a.window ? a.W : 0;
+  const int P = s.L - W;
+  const int segsz = a.seg_size;
+  const int j0 = seg * segsz;
+  if (j0 >= P) return;
+  const int end = min(P, j0 + segsz);
+  const long long off = s.vote_off + (long long)h * s.vote_ld;
+  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores) + off;
+  uint32_t* crow = cand + off + j0;
+
+  // The first unit's scores are requested before the histogram so that the
+  // two latencies overlap.
+  uint32_t kk[kCandPer];
+#pragma unroll
+  for (int u = 0; u < kCandPer; ++u) {
+    const int j = j0 + u * kCandThreads + tid;
+    kk[u] = j < end ? key[j] : 0u;
+  }
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t sh[8];
+  __shared__ uint32_t wave_n[kCandThreads / 64];
+  __shared__ uint32_t s_digit, s_need;
+  const uint32_t* gh = ghist + (long long)row * 2048;
+  for (int d = tid; d < 2048; d += kCandThreads) hist[d] = gh[d];
+  __syncthreads();
+  pick_digit<kCandThreads>(hist, 2048, (uint32_t)(s.C - W), sh, &s_digit, &s_need);
+  const uint32_t d1 = s_digit;
+
+  uint32_t above = 0, base = 0;  // base: candidates of the earlier units (block-uniform)
+  for (int jb = j0; jb < end; jb += kSegUnit) {
+    if (jb != j0) {
+#pragma unroll
+      for (int u = 0; u < kCandPer; ++u) {
+        const int j = jb + u * kCandThreads + tid;
+        kk[u] = j < end ? key[j] : 0u;
+      }
+    }
+    // Count, scan the per-wave counts, then write at the scanned offsets.
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < kCandPer; ++u) {
+      const int j = jb + u * kCandThreads + tid;
+      const uint32_t d = kk[u] >> 21;
+      above += j < end && d > d1;
+      mine += (uint32_t)__popcll(__ballot(j < end && d == d1));
+    }
+    if (lane == 0) wave_n[wv] = mine;
+    __syncthreads();
+    uint32_t wbase = base, unit_n = 0;
+    for (int v = 0; v < kCandThreads / 64; ++v) {
+      wbase += v < wv ? wave_n[v] : 0u;
+      unit_n += wave_n[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kCandPer; ++u) {
+      const int j = jb + u * kCandThreads + tid;
+      const bool hit = j < end && (kk[u] >> 21) == d1;
+      const unsigned long long m = __ballot(hit);
+      const uint32_t slot =
+          wbase + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (hit) crow[slot] = kk[u];
+      wbase += (uint32_t)__popcll(m);
+    }
+    base += unit_n;
+    __syncthreads();  // wave_n is rewritten by the next unit
+  }
+  uint32_t total;
+  (void)block_scan<kCandThreads>(above, sh, total);
+  if (tid == 0) {
+    uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
+    sc[seg] = total;
+    sc[kMaxSegRow + seg] = base;
+  }
+}
+
+// Threshold kernel: one 1024-thread workgroup per (sequence, head) row.  It
+// takes the row's candidates (the scores of first digit d1, segment by
+// segment from the candidates kernel) into LDS, resolves the remaining 21
+// bits there (two radix digits of 11 and 10 bits; with more than kCand
+// candidates the digits read the candidate buffer instead), and rewrites the
+// segment counts as exclusive prefixes over the segments: picks above tau and
+// tau-equal positions before segment q, which is where the emit workgroup of
+// segment q starts.
+__global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a, const uint32_t* __restrict__ ghist,
+                                                                 const uint32_t* __restrict__ cand,
                                                                  uint32_t* __restrict__ cut,
                                                                  uint32_t* __restrict__ segcnt) {
   const int row = blockIdx.x;
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
-  if (s.L < s.C) return;  // bypass: every position is kept
+  if (s.L < s.C) return;
   const int h = s.h0 + (row - s.row0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int kWavesPerBlock = kTopkThreads / 64;
   const int W = a.window ? a.W : 0;
   const int P = s.L - W;
-  const uint32_t count = (uint32_t)(s.C - W);
-  const uint32_t* key = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
   const int segsz = a.seg_size;
   const int nseg = (P + segsz - 1) / segsz;
+  const uint32_t* crow = cand + s.vote_off + (long long)h * s.vote_ld;
+  uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
 
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t cand_key[kCand];
-  __shared__ int32_t cand_pos[kCand];
-  __shared__ uint32_t sgt[kMaxSegRow], seq[kMaxSegRow];
+  __shared__ uint32_t sgt[kMaxSegRow], seq[kMaxSegRow], cbase[kMaxSegRow];
   __shared__ uint32_t sh[32];
-  __shared__ uint32_t s_digit, s_need, s_ncand;
+  __shared__ uint32_t s_digit, s_need;
+  static_assert(kMaxSegRow <= kTopkThreads, "one thread per segment in the scans");
 
   KVSEL_SELECT_MARK(0);
   const uint32_t* gh = ghist + (long long)row * 2048;
   for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = gh[d];
-  for (int q = tid; q < nseg; q += kTopkThreads) {
-    sgt[q] = 0u;
-    seq[q] = 0u;
-  }
-  if (tid == 0) s_ncand = 0;
+  const uint32_t nq = tid < nseg ? sc[kMaxSegRow + tid] : 0u;
+  if (tid < nseg) sgt[tid] = sc[tid];
   __syncthreads();
-  pick_digit(hist, 2048, count, sh, &s_digit, &s_need);
+  pick_digit<kTopkThreads>(hist, 2048, (uint32_t)(s.C - W), sh, &s_digit, &s_need);
   const uint32_t d1 = s_digit;
   uint32_t need = s_need;
-  const bool in_lds = hist[d1] <= (uint32_t)kCand;
+  uint32_t ncand;
+  const uint32_t cincl = block_scan<kTopkThreads>(nq, sh, ncand);
+  if (tid < nseg) cbase[tid] = cincl - nq;
   __syncthreads();
+  const bool in_lds = ncand <= (uint32_t)kCand;
 
-  // The 64 positions a wave reads at once are consecutive and segments are
-  // multiples of 64 long, so each wave's counts go to one segment.  The
-  // digit-d1 positions are appended without contended atomics: every wave
-  // counts its own, wave 0 turns the counts into offsets, then every wave
-  // writes its positions (still in registers) at its offset.
+  // Segment q's candidates are crow[q * segsz + i], i < n_q; in LDS they sit
+  // at cand_key[cbase[q] + i].  One wave per segment.
   KVSEL_SELECT_MARK(1);
-  {
-    constexpr int U = 32;  // independent loads in flight per thread (a 32K row in one batch)
-    constexpr int kWavesPerBlock = kTopkThreads / 64;
-    __shared__ uint32_t wave_n[kWavesPerBlock];
-    const int wv = tid >> 6;
-    for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
-      uint32_t kk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kTopkThreads + tid;
-        kk[u] = j < P ? key[j] : 0u;
-      }
-      uint32_t mine = 0;  // this wave's digit-d1 positions in the block
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kTopkThreads + tid;
-        const int jw = j - lane;
-        const uint32_t d = kk[u] >> 21;
-        const unsigned long long above = __ballot(j < P && d > d1);
-        if (above != 0 && lane == 0) atomicAdd(&sgt[jw / segsz], (uint32_t)__popcll(above));
-        mine += (uint32_t)__popcll(__ballot(j < P && d == d1));
-      }
-      if (in_lds) {
-        if (lane == 0) wave_n[wv] = mine;
-        __syncthreads();
-        uint32_t base = s_ncand;
-        for (int v = 0; v < wv; ++v) base += wave_n[v];
-        __syncthreads();
-        if (tid == kTopkThreads - 1) s_ncand = base + mine;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * kTopkThreads + tid;
-          const bool hit = j < P && (kk[u] >> 21) == d1;
-          const unsigned long long m = __ballot(hit);
-          const uint32_t slot =
-              base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          if (hit && slot < (uint32_t)kCand) {
-            cand_key[slot] = kk[u];
-            cand_pos[slot] = j;
-          }
-          base += (uint32_t)__popcll(m);
-        }
-      }
+  if (in_lds) {
+    for (int q = wv; q < nseg; q += kWavesPerBlock) {
+      const uint32_t n = (q + 1 < nseg ? cbase[q + 1] : ncand) - cbase[q];
+      for (uint32_t i = lane; i < n; i += 64) cand_key[cbase[q] + i] = crow[(long long)q * segsz + i];
     }
     __syncthreads();
   }
   KVSEL_SELECT_MARK(2);
-  const uint32_t n_src = in_lds ? s_ncand : (uint32_t)P;
   uint32_t prefix = d1;
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
@@ -201,12 +255,22 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a,
     const uint32_t nb = 1u << bits;
     for (int d = tid; d < 2048; d += kTopkThreads) hist[d] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < n_src; i += kTopkThreads) {
-      const uint32_t k = in_lds ? cand_key[i] : key[i];
-      if ((k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
+    if (in_lds) {
+      for (uint32_t i = tid; i < ncand; i += kTopkThreads) {
+        const uint32_t k = cand_key[i];
+        if ((k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
+      }
+    } else {
+      for (int q = wv; q < nseg; q += kWavesPerBlock) {
+        const uint32_t n = (q + 1 < nseg ? cbase[q + 1] : ncand) - cbase[q];
+        for (uint32_t i = lane; i < n; i += 64) {
+          const uint32_t k = crow[(long long)q * segsz + i];
+          if ((k >> hi) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1u)], 1u);
+        }
+      }
     }
     __syncthreads();
-    pick_digit(hist, (int)nb, need, sh, &s_digit, &s_need);
+    pick_digit<kTopkThreads>(hist, (int)nb, need, sh, &s_digit, &s_need);
     prefix = (prefix << bits) | s_digit;
     need = s_need;
     __syncthreads();
@@ -214,43 +278,30 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_kernel(const Launch a,
   const uint32_t tau = prefix;
   KVSEL_SELECT_MARK(3);
 
-  // Positions of digit d1 above tau and on tau, per segment.
-  if (in_lds) {
-    for (uint32_t i = tid; i < n_src; i += kTopkThreads) {
-      const uint32_t k = cand_key[i];
-      const int q = cand_pos[i] / segsz;
-      if (k > tau)
-        atomicAdd(&sgt[q], 1u);
-      else if (k == tau)
-        atomicAdd(&seq[q], 1u);
+  // Candidates above tau and on tau, per segment (one wave per segment).
+  for (int q = wv; q < nseg; q += kWavesPerBlock) {
+    const uint32_t n = (q + 1 < nseg ? cbase[q + 1] : ncand) - cbase[q];
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+      const uint32_t i = i0 + lane;
+      const uint32_t k = i < n ? (in_lds ? cand_key[cbase[q] + i] : crow[(long long)q * segsz + i]) : 0u;
+      gt += (uint32_t)__popcll(__ballot(i < n && k > tau));
+      eq += (uint32_t)__popcll(__ballot(i < n && k == tau));
     }
-  } else {
-    constexpr int U = 8;
-    for (int j0 = 0; j0 < P; j0 += U * kTopkThreads) {
-      uint32_t kk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kTopkThreads + tid;
-        kk[u] = j < P ? key[j] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kTopkThreads + tid;
-        const int jw = j - lane;
-        const bool in = j < P && (kk[u] >> 21) == d1;
-        const unsigned long long gt = __ballot(in && kk[u] > tau), eq = __ballot(in && kk[u] == tau);
-        if (lane == 0) {
-          if (gt) atomicAdd(&sgt[jw / segsz], (uint32_t)__popcll(gt));
-          if (eq) atomicAdd(&seq[jw / segsz], (uint32_t)__popcll(eq));
-        }
-      }
+    if (lane == 0) {
+      sgt[q] += gt;
+      seq[q] = eq;
     }
   }
   __syncthreads();
-  uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
-  for (int q = tid; q < nseg; q += kTopkThreads) {
-    sc[q] = sgt[q];
-    sc[kMaxSegRow + q] = seq[q];
+  // Exclusive prefixes over the segments, one scan per count.
+  const uint32_t g = tid < nseg ? sgt[tid] : 0u, e = tid < nseg ? seq[tid] : 0u;
+  uint32_t tg, te;
+  const uint32_t gi = block_scan<kTopkThreads>(g, sh, tg);
+  const uint32_t ei = block_scan<kTopkThreads>(e, sh, te);
+  if (tid < nseg) {
+    sc[tid] = gi - g;
+    sc[kMaxSegRow + tid] = ei - e;
   }
   if (tid == 0) {
     cut[2 * row] = tau;
@@ -315,7 +366,6 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
   __shared__ int32_t src[kSegUnit];
   __shared__ uint32_t stage[kSegUnit + kSegUnit / kEmitPer];
   __shared__ uint32_t sh[8];
-  __shared__ uint32_t s_before[2];
 
   if (s.L < s.C) {  // bypass: position j goes to slot j
     const int end = min(s.L, (seg + 1) * segsz);
@@ -350,22 +400,11 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
     const int j = seg * segsz + u * kEmitThreads + tid;
     first[u] = j < end ? key[j] : 0u;
   }
-  // Picks above tau and tau-equal positions in the segments before this one.
+  // Picks above tau and tau-equal positions in the segments before this one
+  // (exclusive prefixes written by the threshold kernel).
   const uint32_t* sc = segcnt + (long long)row * 2 * kMaxSegRow;
-  if (tid < 2) s_before[tid] = 0u;
-  __syncthreads();
-  {
-    uint32_t g = 0, e = 0;
-    for (int q = tid; q < seg; q += kEmitThreads) {
-      g += sc[q];
-      e += sc[kMaxSegRow + q];
-    }
-    if (g) atomicAdd(&s_before[0], g);
-    if (e) atomicAdd(&s_before[1], e);
-  }
-  __syncthreads();
   const uint32_t tau = cut[2 * row], need_eq = cut[2 * row + 1];
-  uint32_t gt_run = s_before[0], eq_run = s_before[1];
+  uint32_t gt_run = sc[seg], eq_run = sc[kMaxSegRow + seg];
 
   for (int j0 = seg * segsz; j0 < end; j0 += kSegUnit) {
     // Coalesced loads staged through LDS; thread t then scans positions
@@ -587,10 +626,18 @@ int selection_seg_size(long long max_positions) {
   return (int)(kSegUnit * (per < 1 ? 1 : per));
 }
 
-hipError_t launch_threshold(const Launch& a, int rows, const float* scores, const uint32_t* hist, uint32_t* cut,
+hipError_t launch_candidates(const Launch& a, int rows, int max_n, const float* scores, const uint32_t* hist,
+                             uint32_t* cand, uint32_t* segcnt, hipStream_t st) {
+  if (rows <= 0 || max_n <= 0) return hipSuccess;
+  const dim3 grid((max_n + a.seg_size - 1) / a.seg_size, rows);
+  hipLaunchKernelGGL(candidates_kernel, grid, dim3(kCandThreads), 0, st, a, scores, hist, cand, segcnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold(const Launch& a, int rows, const uint32_t* hist, const uint32_t* cand, uint32_t* cut,
                             uint32_t* segcnt, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(threshold_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, scores, hist, cut, segcnt);
+  hipLaunchKernelGGL(threshold_kernel, dim3(rows), dim3(kTopkThreads), 0, st, a, hist, cand, cut, segcnt);
   return hipGetLastError();
 }
 

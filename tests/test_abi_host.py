@@ -114,7 +114,8 @@ def test_step_entry_point_errors(B):
     assert lib.kvsel_topk(None, 4, 100, 10, FAKE, 10, None, 0, None) == -1
     assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, None, 0, None) == -1          # no workspace
     assert lib.kvsel_topk(FAKE, 4, 100, 10, FAKE, 10, FAKE, 1024, None) == -3       # too small
-    assert lib.kvsel_topk_workspace_bytes(4, 100) == 4 * 2048 * 4 + 256 + 4 * 2 * 512 * 4  # histograms, cut, counts
+    # histograms, cut, segment counts, candidate scores (one word per score)
+    assert lib.kvsel_topk_workspace_bytes(4, 100) == 4 * 2048 * 4 + 256 + 4 * 2 * 512 * 4 + 1792
     assert lib.kvsel_topk_workspace_bytes(0, 100) == 0
     assert lib.kvsel_pool1d(FAKE, 4, 100, 2, 0, ctypes.c_void_p(0x20000), None) == -1
     assert lib.kvsel_pool1d(FAKE, 4, 100, 3, 0, FAKE, None) == -1  # aliasing
