@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layers per step (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scoring", choices=("auto", "two_pass", "single_read"), default="auto",
+                    help="scoring path (auto: single-read wherever it applies)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -195,6 +197,7 @@ def main():
     Ko = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
     Vo = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
     stream = torch.cuda.current_stream()
+    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[args.scoring])
 
     def step():
         for layer in range(layers):
@@ -265,7 +268,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "layers": layers, "heads": H, "L": L, "W": W, "C": C, "D": D,
-                   "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys},
+                   "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys,
+                   "scoring": args.scoring},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "path": {"alg_bytes_per_layer": path_alg_bytes(w), "alg_GBps": round(path_gbps, 1),
