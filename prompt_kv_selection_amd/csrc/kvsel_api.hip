@@ -129,7 +129,7 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
     p.cuP[b + 1] = p.cuP[b] + (L - W);
     p.part[b + 1] = p.part[b] + (long long)heads * p.nch[b];
     p.fc[b] = (L < C || p.fS == 0) ? 0 : (int)((L + p.fS - 1) / p.fS);
-    p.fpart[b + 1] = p.fpart[b] + (long long)heads * p.fc[b];
+    p.fpart[b + 1] = p.fpart[b] + (long long)heads * fused_slot_stride(p.fc[b]);
   }
   if ((rc = check_support(W, D))) return rc;
   p.part_slots = p.part[B];
@@ -149,8 +149,8 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)B * heads * kSegCntBytes);
   p.off_ctr = off;  // single-read scoring: one exchange slot per (sequence, head, chunk)
   off = align256(off + (size_t)p.fpart[B] * fused_exchange_bytes());
-  p.off_status = off;  // per launch group: error flags, arrivals, residency decision, spare
-  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * 4 * sizeof(unsigned));
+  p.off_status = off;  // per launch group: error flags, arrivals, residency decision, fallback counter
+  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned));
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
   off = align256(off + (size_t)B * heads * 2048 * 4);
   p.bytes = off;
@@ -296,7 +296,7 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
     if (items > 0 && use_fused) {
-      unsigned* gstatus = status + 4 * (b0 / kMaxSegs);
+      unsigned* gstatus = status + (long long)kFusedStatusWords * (b0 / kMaxSegs);
       if (g_force_fallback) {
         e = launch_fill_u32(gstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
         if (e != hipSuccess) return device_error(e, "fill launch");

@@ -33,15 +33,19 @@
 // is used for the chunk's exponentials, so a set bit marks a written word in a
 // slot array that starts zeroed.
 //
-// Roles inside a workgroup.  Four streaming waves and one controller wave.
+// Roles inside a workgroup.  Eight streaming waves, an exchange wave and a
+// memory wave.
 //  * Streaming waves read global memory only through direct-to-LDS loads of
 //    K tiles (global_load_lds_dwordx4, 1 KB contiguous per instruction) into a
-//    private ring of four 32-row tiles, issued ahead and waited for with
-//    explicit vmcnt counts, so the HBM stream never drains while they compute.
-//    They form the logits on MFMA (v_mfma_f32_32x32x16_bf16, Qwin rows from
-//    LDS), exponentials and votes, and talk to the controller through LDS.
-//  * The controller wave does every other global access: Qwin (double
-//    buffered in LDS), the slot store, the slot reads, and the votes.
+//    private ring of 32-row tiles, issued ahead and waited for with explicit
+//    vmcnt counts, so the HBM stream never drains while they compute.  They
+//    form the logits on MFMA (v_mfma_f32_32x32x16_bf16, Qwin rows from LDS),
+//    exponentials and votes, and talk to the other two waves through LDS.
+//  * The exchange wave only reads the head's slots and merges them, so a
+//    slow exchange never holds up the publication of the next round.
+//  * The memory wave publishes the chunk's slot as soon as the streaming
+//    waves have their row statistics, loads Qwin (double buffered in LDS)
+//    and writes the votes.
 // All exchange accesses are agent scope (they bypass the per-XCD L2); every
 // wait is bounded, and a timed-out wait records a flag and marks the head's
 // votes NaN, so the grid always drains.
@@ -133,6 +137,15 @@ __device__ __forceinline__ float half_sum(float v) {
   return v + dpp_f<0x142, 0xA>(0.f, v);
 }
 
+// Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
+// exponentials rescaled to it.
+__device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
+  const float d = mo - m;
+  const float e = exp2_fast(-fabsf(d));
+  z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
+  m = fmaxf(m, mo);
+}
+
 // ---- exchange slots in the workspace, zeroed per call: per (sequence,
 // head, chunk) 32 words of 64 bits, word i = (tagged m_i bits, z_i bits).
 constexpr int kSlotWords = 32;
@@ -145,7 +158,11 @@ __device__ __forceinline__ unsigned long long pack_slot(float m, float z) {
 // operations complete in order, so data written before a signal is visible to
 // a wave that has seen the signal.
 struct Sync {
-  unsigned cnt_b, cnt_c;           // streaming-wave arrivals (row statistics, votes)
+  // Streaming-wave arrivals (row statistics, votes), counted per round
+  // parity: a streaming wave can finish round k + 1 before another finishes
+  // round k (never round k + 2, which waits for round k's exchange), so a
+  // single running count could reach a round's target early.
+  unsigned cnt_b[2], cnt_c[2];
   unsigned q_ready;                // Qwin of rounds < q_ready is in LDS
   unsigned s_ready;                // vote scales of rounds < s_ready are in LDS
   unsigned v_done;                 // votes of rounds < v_done have left LDS
@@ -223,117 +240,132 @@ __device__ __forceinline__ void wait_tiles(int tiles_after) {
   }
 }
 
-// The tile stream of one streaming wave: tile q = round * kTT + t covers
-// positions c * kS + wave * kTT * 32 + t * 32 of the round's head.
-struct Stream {
-  unsigned issued;  // bit (q % 32): tile q has loads outstanding
+// The K tiles one streaming wave owns in a round: kTT consecutive 32-row
+// tiles of one head from row p0 (rows past L repeat row L - 1).  Tile t of
+// a round always uses ring buffer t, and tiles are consumed in the order
+// they were issued, so the wave's outstanding loads are counted, not named.
+static_assert(kNBuf == kTT, "one ring buffer per tile of a round");
+struct WaveTiles {
+  const __bf16* kh;  // the head's K
+  int L, p0;
+  bool on;           // the workgroup owns the round
 };
 
 template <int D>
-__device__ __forceinline__ void stream_issue(const Launch& a, const __bf16* __restrict__ K, int q, int wave,
-                                             int lane, uint4 (*ring)[TileGeom<D>::PIECES], Stream& st) {
-  const int k = q / kTT, t = q - (q / kTT) * kTT;
+__device__ __forceinline__ WaveTiles wave_tiles(const Launch& a, const __bf16* __restrict__ K, int k, int wave) {
+  WaveTiles t{K, 0, 0, false};
   const Work w = round_work(a, k);
-  if (!w.on) return;
+  if (!w.on) return t;
   const Seg& s = a.seg[w.e];
-  const int p0 = w.c * kS + wave * kTT * 32 + t * 32;
-  if (p0 >= s.L) return;
-  issue_tile<D>(K + s.kv_off + (long long)w.h * s.L * D, s.L, p0, ring[q % kNBuf], lane);
-  st.issued |= 1u << (q & 31);
+  t.kh = K + s.kv_off + (long long)w.h * s.L * D;
+  t.L = s.L;
+  t.p0 = w.c * kS + wave * kTT * 32;
+  t.on = true;
+  return t;
 }
 
-__device__ __forceinline__ int tiles_after(const Stream& st, int q) {
-  int n = 0;
-#pragma unroll
-  for (int j = 1; j < kNBuf; ++j) n += (st.issued >> ((q + j) & 31)) & 1u;
-  return n;
-}
-
-// Phase A (streaming wave): logits of round k into x; this wave's row maxima
-// and sums of exponentials to LDS.
 template <int D>
-__device__ __forceinline__ void phase_stream(const Launch& a, const Work& w, int k, const __bf16* __restrict__ K,
+__device__ __forceinline__ void issue_wave_tile(const WaveTiles& wt, int t, uint4 (*ring)[TileGeom<D>::PIECES],
+                                                int& issued) {
+  if (wt.on && wt.p0 + 32 * t < wt.L) {
+    issue_tile<D>(wt.kh, wt.L, wt.p0 + 32 * t, ring[t], threadIdx.x & 63);
+    ++issued;
+  }
+}
+
+// Phase A (streaming wave): the logits of round k, twice from the same
+// operands.  Q.K^T (a lane per position, its window rows in registers) is
+// kept in x for the votes; K.Q^T (a lane per window row, positions in
+// registers) gives the row statistics with lane-local reductions: the
+// maximum and the sum of exp2 over the lane's positions, then one merge of
+// the two half-waves, which hold the same rows over different positions.
+// Logits stay unscaled; exponents are fma(l, scale2, -m) with m already
+// scaled.  The wave's (max, sum) per row go to LDS.  Every tile's buffer is
+// refilled with the next round's tile as soon as its operands are read.
+template <int D>
+__device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveTiles& cur, const WaveTiles& nxt,
                                              uint4 (*ring)[TileGeom<D>::PIECES], const uint4* __restrict__ qbuf,
-                                             float (&x)[kTT][16], Stream& st, float* s_maxp, float* s_zp,
-                                             Sync* sy) {
+                                             f32x16 (&x)[kTT], int& issued, int& consumed, float* s_maxp,
+                                             float* s_zp, Sync* sy) {
   using G = TileGeom<D>;
-  const Seg& s = a.seg[w.e];
-  const int L = s.L, W = a.W, P = L - W;
+  const int L = cur.L, W = a.W, P = L - W;
+  const float sc = a.scale2;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
   lds_wait_ge(&sy->q_ready, (unsigned)k + 1, &sy->timeout);
+  float mrow = kNegBig, zrow = 0.f;  // row n over this lane's positions of the round
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
-    const int q = k * kTT + t;
-    const int p0 = w.c * kS + wave * kTT * 32 + t * 32;
+    const int p0 = cur.p0 + 32 * t;
     if (p0 < L) {
-      wait_tiles<D>(tiles_after(st, q));
-      const uint4* tile = ring[q % kNBuf];
-      f32x16 acc = {};
+      wait_tiles<D>(issued - consumed - 1);
+      const uint4* tile = ring[t];
+      // Operands in groups of four k-steps: their LDS reads are issued
+      // together, and the registers of a group are free for the next.
+      constexpr int kGroup = 4;
+      f32x16 acc = {}, act = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int c = 2 * kk + g;
-        const int off = n * G::PR + (c ^ (n & (G::PR - 1)));
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, tile[off]);
-        const bf16x8 qa = __builtin_bit_cast(bf16x8, qbuf[off]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, acc, 0, 0, 0);
+      for (int k0 = 0; k0 < D / 16; k0 += kGroup) {
+        bf16x8 qa[kGroup], kb[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          const int off = n * G::PR + ((2 * (k0 + u) + g) ^ (n & (G::PR - 1)));
+          kb[u] = __builtin_bit_cast(bf16x8, tile[off]);
+          qa[u] = __builtin_bit_cast(bf16x8, qbuf[off]);
+        }
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u], kb[u], acc, 0, 0, 0);
+          act = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[u], qa[u], act, 0, 0, 0);
+        }
       }
       // Every operand has been read: refill the buffer before the VALU work.
       lds_fence();
-      st.issued &= ~(1u << (q & 31));
-      stream_issue<D>(a, K, q + kNBuf, wave, lane, ring, st);
-      const int j = p0 + n;
+      ++consumed;
+      issue_wave_tile<D>(nxt, t, ring, issued);
+      x[t] = acc;
+      // act[r]: row n at position p0 + acc_row(r, g).  Only a tile that
+      // reaches the window or the end of the prompt needs the mask.
+      float tm = kNegBig;
+      if (p0 + 32 <= P) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = acc_row(r, g);
-        const bool visible = (j < L) && (i < W) && (j <= P + i);
-        x[t][r] = visible ? acc[r] * a.scale2 : -INFINITY;
+        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, act[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = p0 + acc_row(r, g);
+          if (!(j < L && j <= P + n)) act[r] = -INFINITY;
+          tm = fmaxf(tm, act[r]);
+        }
       }
+      const float tms = tm * sc;
+      float tz = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tz += exp2_fast(fmaf(act[r], sc, -tms));
+      lse_merge(mrow, zrow, tms, tz);
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[t][r] = -INFINITY;
-      st.issued &= ~(1u << (q & 31));
-      stream_issue<D>(a, K, q + kNBuf, wave, lane, ring, st);
+      issue_wave_tile<D>(nxt, t, ring, issued);
     }
   }
-  // This wave's row maxima and sums of exp2(x - max), without waiting for the
-  // other waves: the controller merges the four pairs.
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float mm = kNegBig;
-#pragma unroll
-    for (int t = 0; t < kTT; ++t) mm = fmaxf(mm, x[t][r]);
-    mm = half_max(mm);
-    const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mm), 31));
-    const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mm), 63));
-    const float mh = g == 0 ? m0 : m1;
-    float zz = 0.f;
-#pragma unroll
-    for (int t = 0; t < kTT; ++t) zz += exp2_fast(x[t][r] - mh);
-    zz = half_sum(zz);
-    if (n == 31) {
-      s_maxp[wave * 32 + acc_row(r, g)] = mh;
-      s_zp[wave * 32 + acc_row(r, g)] = zz;
-    }
+  // Lane n and lane n + 32 merge (half 0, half 1) in that order.
+  const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mrow), __float_as_uint(mrow), false, false);
+  const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zrow), __float_as_uint(zrow), false, false);
+  float m = __uint_as_float(pm[0]), z = __uint_as_float(pz[0]);
+  lse_merge(m, z, __uint_as_float(pm[1]), __uint_as_float(pz[1]));
+  if (g == 0) {
+    s_maxp[wave * 32 + n] = m;
+    s_zp[wave * 32 + n] = z;
   }
-  lds_add(&sy->cnt_b);
+  lds_add(&sy->cnt_b[k & 1]);
 }
 
-// Streaming waves that own no chunk in round k still advance their tile
-// stream (issue the tiles kNBuf ahead).
-template <int D>
-__device__ __forceinline__ void phase_skip(const Launch& a, int k, const __bf16* __restrict__ K,
-                                           uint4 (*ring)[TileGeom<D>::PIECES], Stream& st) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int t = 0; t < kTT; ++t) stream_issue<D>(a, K, k * kTT + t + kNBuf, wave, lane, ring, st);
-}
-
-// Phase B (streaming wave): votes of the wave's positions into LDS, from the
-// head-wide row maxima M and inverse normalisers.  Same arithmetic as the
-// two-pass kernels: equal key rows give bit-equal votes.
-__device__ __forceinline__ void phase_votes(int k, const float (&x)[kTT][16], const float* s_m, const float* s_iz,
-                                            float* s_votes, Sync* sy) {
+// Phase B (streaming wave): votes of the wave's positions into LDS from the
+// head-wide scaled row maxima M and inverse normalisers.  Prefix positions
+// are visible to every window row, so no mask is needed; rows past W have
+// zero logits and zero 1/Z.  Equal key rows give bit-equal votes.
+__device__ __forceinline__ void phase_votes(const Launch& a, int k, const f32x16 (&x)[kTT], const float* s_m,
+                                            const float* s_iz, float* s_votes, Sync* sy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
+  const float sc = a.scale2;
   lds_wait_ge(&sy->s_ready, (unsigned)k + 1, &sy->timeout);
   lds_wait_ge(&sy->v_done, (unsigned)(k >= 1 ? k - 1 : 0), &sy->timeout);  // round k - 2 left this buffer
   float mr[16], iz[16];
@@ -346,12 +378,12 @@ __device__ __forceinline__ void phase_votes(int k, const float (&x)[kTT][16], co
   for (int t = 0; t < kTT; ++t) {
     float tot = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tot += exp2_fast(x[t][r] - mr[r]) * iz[r];
-    const float other = __shfl_xor(tot, 32);
-    const float v = g == 0 ? tot + other : other + tot;
+    for (int r = 0; r < 16; ++r) tot = fmaf(exp2_fast(fmaf(x[t][r], sc, -mr[r])), iz[r], tot);
+    const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+    const float v = __uint_as_float(pt[0]) + __uint_as_float(pt[1]);
     if (g == 0) s_votes[wave * kTT * 32 + t * 32 + n] = v;
   }
-  lds_add(&sy->cnt_c);
+  lds_add(&sy->cnt_c[k & 1]);
 }
 
 // Controller: start loading Qwin of round k into an LDS buffer with
@@ -372,38 +404,38 @@ __device__ __forceinline__ void ctl_finish_q(int W, uint4* qbuf) {
   for (int p = W * G::PR + (int)(threadIdx.x & 63); p < G::PIECES; p += 64) qbuf[p] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
-// exponentials rescaled to it.
-__device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
-  const float d = mo - m;
-  const float e = exp2_fast(-fabsf(d));
-  z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
-  m = fmaxf(m, mo);
-}
 
-// Controller: the head-wide row statistics of round r from the fc slots of
-// its head.  Lane l merges row l % 32 over the slots of parity l / 32 (the
-// words of rows >= W are never written and never read); the two halves are
-// merged last, so every workgroup of the head merges in the same order.  The
-// reads are repeated until every word carries its tag (bounded).
+// Exchange wave: the head-wide row statistics of round r from the fc slots of
+// its head.  Lane l handles row l % 32 over the slots of parity l / 32 (the
+// words of rows >= W are never written and never read), kBatch slots per
+// lane per pass, all loads of a pass in flight together.  A pass is reread
+// until every word carries its tag (bounded).  Within a pass the maximum
+// comes first and the rescaled sum follows in slot order; passes, then the
+// two halves, are merged in order, so every workgroup of the head computes
+// bit-identical statistics.
 __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, const unsigned long long* ex,
                                                float& M, float& Z) {
   const Seg& s = a.seg[w.e];
   const int fc = s.fc, W = a.W;
   const int lane = threadIdx.x & 63, i = lane & 31, half = lane >> 5;
-  const unsigned long long* base = ex + (s.fslot_base + (long long)w.h * fc) * kSlotWords;
+  const unsigned long long* base = ex + (s.fslot_base + (long long)w.h * fused_slot_stride(fc)) * kSlotWords;
   float mm = kNegBig, zz = 0.f;
   bool ok = true;
-  constexpr int kBatch = 16;  // words per lane in flight
+  constexpr int kBatch = 32;  // words per lane in flight
+  static_assert(2 * kBatch == 64, "a pass reads the slots of one padding unit (fused_slot_stride)");
+  // Word (slot c0 + 2u + half, row i) sits at a wave-uniform base plus a
+  // 32-bit lane offset.  Slots up to the padded stride exist, so every load
+  // of a pass is in bounds; those past fc are ignored.
+  const unsigned lane_off = (unsigned)(half * kSlotWords + i) * 8u;
   for (int c0 = 0; c0 < fc; c0 += 2 * kBatch) {
     unsigned long long v[kBatch];
+    const char* pass_base = (const char*)(base + (long long)c0 * kSlotWords);
     long spins = 0;
     for (;;) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int c = min(c0 + 2 * u + half, fc - 1);
-        v[u] = __hip_atomic_load(base + (long long)c * kSlotWords + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = __hip_atomic_load((const unsigned long long*)(pass_base + lane_off + u * 2 * kSlotWords * 8),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       bool valid = true;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -417,11 +449,16 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
       }
       __builtin_amdgcn_s_sleep(2);
     }
+    float bm = kNegBig;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int c = c0 + 2 * u + half;
-      if (c < fc && i < W) lse_merge(mm, zz, __uint_as_float((unsigned)v[u]), __uint_as_float((unsigned)(v[u] >> 32)));
-    }
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + 2 * u + half < fc && i < W) bm = fmaxf(bm, __uint_as_float((unsigned)v[u]));
+    float bz = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + 2 * u + half < fc && i < W)
+        bz = fmaf(__uint_as_float((unsigned)(v[u] >> 32)), exp2_fast(__uint_as_float((unsigned)v[u]) - bm), bz);
+    lse_merge(mm, zz, bm, bz);
   }
   const float mo = __shfl_xor(mm, 32), zo = __shfl_xor(zz, 32);
   if (half == 0) lse_merge(mm, zz, mo, zo);
@@ -430,23 +467,23 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
   return __ballot(!ok) == 0;
 }
 
-// Exchange wave.  Step k: (1) head statistics of round k - 1 from the slots
-// (overlapping the streaming of round k), (2) publish the chunk's (m, z) of
-// round k, merged from the streaming waves' pairs.
+// Exchange wave.  Step k: head statistics of round k - 1 from the slots
+// (overlapping the streaming of round k) into the statistics buffer of round
+// k - 1, once the votes of round k - 3, which read the same buffer, are done.
 template <int D>
 __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ ex, unsigned* __restrict__ status,
-                             float* __restrict__ row_stats, float (*s_maxp)[kSW * 32], float (*s_zp)[kSW * 32],
-                             float (*s_m)[32], float (*s_iz)[32], Sync* sy) {
+                             float* __restrict__ row_stats, float (*s_m)[32], float (*s_iz)[32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
-  unsigned on_b = 0;  // owned rounds whose phase A results were awaited
-  for (int k = 0; k < a.rounds + 1; ++k) {
-    const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
-    // (1) Head-wide statistics of round k - 1.
+  unsigned votes_due[2] = {0, 0};  // owned rounds up to k - 3, per parity: their votes must be done
+  for (int k = 1; k < a.rounds + 1; ++k) {
+    const Work w1 = round_work(a, k - 1);
+    if (k >= 3 && round_work(a, k - 3).on) ++votes_due[(k - 3) & 1];
     if (w1.on) {
       float M, Z;
       const bool ok = ctl_head_stats(a, w1, ex, M, Z);
       if (!ok && lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_wait_ge(&sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1], &sy->timeout);
       if (lane < W) {
         s_m[(k - 1) & 1][lane] = ok ? M : __builtin_nanf("");
         s_iz[(k - 1) & 1][lane] = ok ? 1.f / Z : __builtin_nanf("");
@@ -455,14 +492,37 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
           rs[0] = M * kLn2;
           rs[1] = Z;
         }
+      } else if (lane < 32) {  // rows past W: zero queries, dropped by 1/Z = 0
+        s_m[(k - 1) & 1][lane] = 0.f;
+        s_iz[(k - 1) & 1][lane] = 0.f;
       }
     }
-    if (k >= 1) lds_set(&sy->s_ready, (unsigned)k);
+    lds_set(&sy->s_ready, (unsigned)k);
     KVSEL_FUSED_CTL_MARK(k, 4);
-    // (2) This chunk's (m, z) of round k, one 64-bit word per row.
+  }
+}
+
+// Memory wave.  Step k: (1) once round k's phase A is done, the chunk's
+// (m, z) of round k, merged from the streaming waves' pairs, to its slot;
+// (2) Qwin of round k + 2 into the buffer of round k; (3) votes of round
+// k - 1 to memory, then the votes buffer may be reused (v_done).
+template <int D>
+__device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
+                           unsigned long long* __restrict__ ex, uint4 (*qbufs)[TileGeom<D>::PIECES],
+                           float (*s_maxp)[kSW * 32], float (*s_zp)[kSW * 32], float (*s_votes)[kS], Sync* sy) {
+  const int lane = threadIdx.x & 63;
+  const int W = a.W;
+  // Qwin of rounds 0 and 1 was issued before the residency handshake.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  ctl_finish_q<D>(W, qbufs[0]);
+  ctl_finish_q<D>(W, qbufs[1]);
+  lds_set(&sy->q_ready, 2u);
+  unsigned on_b[2] = {0, 0}, on_c[2] = {0, 0};  // owned rounds awaited so far, per parity
+  for (int k = 0; k < a.rounds + 1; ++k) {
+    const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
     if (w0.on) {
-      ++on_b;
-      lds_wait_ge(&sy->cnt_b, kSW * on_b, &sy->timeout);
+      ++on_b[k & 1];
+      lds_wait_ge(&sy->cnt_b[k & 1], kSW * on_b[k & 1], &sy->timeout);
       if (lane < W) {
         // Merge the waves' (max, sum) pairs in wave order against the
         // tagged chunk maximum.
@@ -479,34 +539,12 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
           if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
         }
         const Seg& s = a.seg[w0.e];
-        unsigned long long* slot = ex + (s.fslot_base + (long long)w0.h * s.fc + w0.c) * kSlotWords;
+        unsigned long long* slot =
+            ex + (s.fslot_base + (long long)w0.h * fused_slot_stride(s.fc) + w0.c) * kSlotWords;
         __hip_atomic_store(slot + lane, pack_slot(m, zz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     KVSEL_FUSED_CTL_MARK(k, 5);
-  }
-}
-
-// Memory wave.  Step k: (3) Qwin of round k + 2 into the buffer of round k
-// once round k's phase A is done, (4) votes of round k - 1 to memory, then
-// the votes buffer may be reused (v_done).
-template <int D>
-__device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
-                           uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_votes)[kS], Sync* sy) {
-  const int lane = threadIdx.x & 63;
-  const int W = a.W;
-  // Qwin of rounds 0 and 1 was issued before the residency handshake.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  ctl_finish_q<D>(W, qbufs[0]);
-  ctl_finish_q<D>(W, qbufs[1]);
-  lds_set(&sy->q_ready, 2u);
-  unsigned on_b = 0, on_c = 0;  // owned rounds whose phase A / B results were awaited
-  for (int k = 0; k < a.rounds + 1; ++k) {
-    const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
-    if (w0.on) {
-      ++on_b;
-      lds_wait_ge(&sy->cnt_b, kSW * on_b, &sy->timeout);
-    }
     if (ctl_issue_q<D>(a, k + 2, Q, qbufs[k & 1])) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       ctl_finish_q<D>(W, qbufs[k & 1]);
@@ -514,8 +552,8 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
     lds_set(&sy->q_ready, (unsigned)(k + 3));
     KVSEL_FUSED_CTL_MARK(k, 6);
     if (w1.on) {
-      ++on_c;
-      lds_wait_ge(&sy->cnt_c, kSW * on_c, &sy->timeout);
+      ++on_c[(k - 1) & 1];
+      lds_wait_ge(&sy->cnt_c[(k - 1) & 1], kSW * on_c[(k - 1) & 1], &sy->timeout);
       const Seg& s = a.seg[w1.e];
       const int P = s.L - W;
       float* vout = votes + s.vote_off + (long long)w1.h * s.vote_ld;
@@ -675,17 +713,30 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
 // Residency handshake (thread 0 of each workgroup).  The rounds need every
 // workgroup of the grid running at once, which a plain launch of one
 // workgroup per CU gives on an otherwise idle device but does not promise.
-// Each workgroup counts its arrival; the last arrival decides GO; one that
-// has waited longer than the bound decides ABORT.  Both decisions are a
-// compare-and-swap on one zeroed word, so every workgroup follows the same
-// one, and GO implies that all of them are resident.
+// Each workgroup counts its arrival in one of kArriveGroups counters (on
+// separate lines: arrivals on one word would be serialised one after the
+// other); the last arrival of a group counts the group, and the last group
+// decides GO.  A workgroup that has waited longer than the bound decides
+// ABORT.  Both decisions are a compare-and-swap on one zeroed word, so every
+// workgroup follows the same one, and GO implies that all of them are
+// resident.
 constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
-__device__ __forceinline__ unsigned residency(unsigned* arrive, unsigned* state) {
-  const unsigned n = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  if (n == gridDim.x) {
-    unsigned expect = 0u;
-    __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned residency(unsigned* status) {
+  unsigned* groups = status + 1;
+  unsigned* state = status + 2;
+  const unsigned grid = gridDim.x;
+  const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
+  const unsigned g = blockIdx.x % ng;
+  const unsigned members = (grid - g + ng - 1) / ng;
+  unsigned* ctr = status + kArriveStride * (1 + g);
+  const unsigned n = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if (n == members) {
+    const unsigned done = __hip_atomic_fetch_add(groups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    if (done == ng) {
+      unsigned expect = 0u;
+      __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   const long long t0 = wall_clock64();
   unsigned s;
@@ -719,16 +770,18 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   const int lane = threadIdx.x & 63;
   // The first K tiles and Qwin of rounds 0 and 1 are issued before the
   // residency handshake, so their latency overlaps it.
-  Stream st{0u};
+  WaveTiles cur{K, 0, 0, false};
+  int issued = 0, consumed = 0;
   if (wave < kSW) {
-    for (int q = 0; q < kNBuf; ++q) stream_issue<D>(a, K, q, wave, lane, s_ring[wave], st);
+    cur = wave_tiles<D>(a, K, 0, wave);
+    for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(cur, t, s_ring[wave], issued);
   } else if (wave == kSW + 1) {
     ctl_issue_q<D>(a, 0, Q, s_q[0]);
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
   if (threadIdx.x == 0) {
-    sy = Sync{0, 0, 0, 0, 0, 0};
-    s_go = residency(status + 1, status + 2);
+    sy = Sync{{0, 0}, {0, 0}, 0, 0, 0, 0};
+    s_go = residency(status);
   }
   __syncthreads();  // afterwards waves meet through LDS flags (or, in the fallback, barriers)
   if (s_go != kFusedGo) {  // not all resident: whole heads, one workgroup each
@@ -738,29 +791,33 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   }
   if (wave >= kSW) {
     if (wave == kSW)
-      ctl_exchange<D>(a, ex, status, row_stats, s_maxp, s_zp, s_m, s_iz, &sy);
+      ctl_exchange<D>(a, ex, status, row_stats, s_m, s_iz, &sy);
     else
-      ctl_memory<D>(a, Q, votes, s_q, s_votes, &sy);
+      ctl_memory<D>(a, Q, votes, ex, s_q, s_maxp, s_zp, s_votes, &sy);
     if ((threadIdx.x & 63) == 0 && sy.timeout)
       __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   uint4 (*ring)[G::PIECES] = s_ring[wave];
-  float xa[kTT][16], xb[kTT][16];
+  f32x16 xa[kTT], xb[kTT];
+  bool prev_on = false;
   // Step k streams round k into one register set (with this wave's row
   // statistics), then votes round k - 1 from the other set; the sets swap
   // every step.  The exchange of round k - 1 overlaps the streaming of round k.
-  auto step = [&](int k, float (&X0)[kTT][16], float (&X1)[kTT][16]) {
+  auto step = [&](int k, f32x16 (&X0)[kTT], f32x16 (&X1)[kTT]) {
     KVSEL_FUSED_MARK(k, 0);
-    const Work w0 = round_work(a, k);
-    if (w0.on)
-      phase_stream<D>(a, w0, k, K, ring, s_q[k & 1], X0, st, s_maxp[k & 1], s_zp[k & 1], &sy);
-    else
-      phase_skip<D>(a, k, K, ring, st);
+    const WaveTiles nxt = wave_tiles<D>(a, K, k + 1, wave);
+    if (cur.on) {
+      phase_stream<D>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
+    } else {
+      for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(nxt, t, ring, issued);
+    }
     KVSEL_FUSED_MARK(k, 1);
     KVSEL_FUSED_MARK(k, 2);
-    if (round_work(a, k - 1).on) phase_votes(k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
+    if (prev_on) phase_votes(a, k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
     KVSEL_FUSED_MARK(k, 3);
+    prev_on = cur.on;
+    cur = nxt;
   };
   const int steps = a.rounds + 1;
   for (int k = 0; k < steps; k += 2) {

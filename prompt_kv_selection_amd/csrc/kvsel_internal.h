@@ -108,14 +108,22 @@ hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, 
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns
-// hipErrorNotSupported when the shape is not covered.  status points at 4
-// zeroed words: error flags, arrivals, the residency decision (kFusedGo or
-// kFusedAbort; a host-written kFusedAbort forces the fallback) and the
-// fallback's work counter.
+// hipErrorNotSupported when the shape is not covered.  status points at
+// kFusedStatusWords zeroed words: error flags, arrived groups, the residency
+// decision (kFusedGo or kFusedAbort; a host-written kFusedAbort forces the
+// fallback), the fallback's work counter, then kArriveGroups arrival counters
+// kArriveStride words apart (same-address atomics serialise, so the
+// workgroups' arrivals are spread over separate lines).
 constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
+constexpr int kArriveGroups = 16;
+constexpr int kArriveStride = 64;
+constexpr int kFusedStatusWords = kArriveStride * (kArriveGroups + 1);
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
 int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
+// Exchange slots per head for fc chunks: fc rounded up to whole read passes
+// of the exchange wave (the padding is never written and never merged).
+__host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64 * 64; }
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* exchange,
                                 unsigned* status, float* votes, float* row_stats, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);

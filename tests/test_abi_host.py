@@ -44,9 +44,10 @@ def test_workspace_sizes(B):
     # two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
     # selection threshold and per-segment counts, single-read exchange slots
     # (per head and 512-position chunk),
-    # status word, first-digit histograms
+    # status words (error flags, decision, fallback counter and 16 arrival
+    # counters on lines of their own), first-digit histograms
     expect_min = (2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 64 * 256 + 256 + 32 * 2048 * 4)
+                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4)
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W

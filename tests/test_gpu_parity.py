@@ -298,6 +298,48 @@ def test_varlen_matches_per_sequence_calls(B):
             check_head(single, h, ref, L, W, C, f"varlen seq {b} head {h}")
 
 
+def test_repeated_ragged_calls_agree(B):
+    """Regression test for the single-read kernel's per-round arrival counts:
+    in a ragged batch the last chunk of a head leaves some streaming waves of
+    its workgroup without tiles, so they finish a round early and start the
+    next; a stale partial statistic then changed a head's normaliser now and
+    then.  Every call must give the oracle's row sums, and all calls must
+    agree bit for bit."""
+    w = WL.reduced(WL.get("ragged_b8_h32_l4k_64k"), heads=4, batch=5, L_min=900, L_max=5000)
+    Q, K, V, Ls, Cs, cu = WL.ragged_arrays(w)
+    H, W, D = w.heads, w.W, w.D
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    cuC = np.concatenate([[0], np.cumsum(Cs)])
+    cuP = np.concatenate([[0], np.cumsum([L - W for L in Ls])])
+    ref = {}
+    for b, (L, C) in enumerate(zip(Ls, Cs)):
+        for h in range(H):
+            q, k, v = WL.head_arrays(w, h, seq=b)
+            ref[(b, h)] = O.snapkv_select(WL.to_float64(q, "bf16"), WL.to_float64(k, "bf16"),
+                                          WL.to_float64(v, "bf16"), W, C, w.kernel, w.pooling)
+    first = None
+    for rep in range(6):
+        ws = torch.empty(B.kvsel_varlen_workspace_bytes(cu.tolist(), list(Cs), H, W, D, torch.bfloat16),
+                         dtype=torch.uint8, device="cuda")
+        idx = torch.full((H * int(cuC[-1]),), -1, dtype=torch.int32, device="cuda")
+        Ko = torch.zeros((H * int(cuC[-1]), D), dtype=torch.bfloat16, device="cuda")
+        Vo = torch.zeros_like(Ko)
+        rs = torch.zeros((len(Ls), H, W, 2), dtype=torch.float32, device="cuda")
+        vt = torch.zeros((H * int(cuP[-1]),), dtype=torch.float32, device="cuda")
+        B.kvsel_select_varlen(Qd, Kd, Vd, cu.tolist(), list(Cs), W, D, H, w.kernel, w.pooling, torch.bfloat16,
+                              idx, Ko, Vo, rs, vt, None, ws)
+        torch.cuda.synchronize()
+        got = (idx.cpu().numpy(), rs.cpu().numpy(), vt.cpu().numpy())
+        for (b, h), r in ref.items():
+            close(got[1][b, h, :, 1], r["row_sum"], f"call {rep} sequence {b} head {h} row sums")
+            close(np.exp(got[1][b, h, :, 0] - r["row_max"]), np.ones(W), f"call {rep} sequence {b} head {h} row maxima")
+        if first is None:
+            first = got
+        else:
+            for a, g, what in zip(first, got, ("indices", "row stats", "votes")):
+                assert np.array_equal(a.view(np.int32), g.view(np.int32)), f"call {rep}: {what} differ from call 0"
+
+
 # ----------------------------------------------------------------- full size
 
 FULL = [
