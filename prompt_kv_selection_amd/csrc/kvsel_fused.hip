@@ -33,8 +33,8 @@
 // is used for the chunk's exponentials, so a set bit marks a written word in a
 // slot array that starts zeroed.
 //
-// Roles inside a workgroup.  Eight streaming waves, an exchange wave and a
-// memory wave.
+// Roles inside a workgroup.  Eight streaming waves, an exchange wave, a
+// memory wave and a publisher wave.
 //  * Streaming waves read global memory only through direct-to-LDS loads of
 //    K tiles (global_load_lds_dwordx4, 1 KB contiguous per instruction) into a
 //    private ring of 32-row tiles, issued ahead and waited for with explicit
@@ -43,9 +43,10 @@
 //    exponentials and votes, and talk to the other two waves through LDS.
 //  * The exchange wave only reads the head's slots and merges them, so a
 //    slow exchange never holds up the publication of the next round.
-//  * The memory wave publishes the chunk's slot as soon as the streaming
-//    waves have their row statistics, loads Qwin (double buffered in LDS)
-//    and writes the votes.
+//  * The publisher wave stores the chunk's slot as soon as the streaming
+//    waves have their row statistics.
+//  * The memory wave loads Qwin (double buffered in LDS) and writes the
+//    votes.
 // All exchange accesses are agent scope (they bypass the per-XCD L2); every
 // wait is bounded, and a timed-out wait records a flag and marks the head's
 // votes NaN, so the grid always drains.
@@ -77,7 +78,7 @@ namespace {
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
-constexpr int kThreads = (kSW + 2) * 64;  // plus the exchange and memory waves
+constexpr int kThreads = (kSW + 3) * 64;  // plus the exchange, memory and publisher waves
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
 constexpr int kNBuf = 2;                  // K tiles in flight per streaming wave
 constexpr int kS = kSW * kTT * 32;        // positions per workgroup per round
@@ -167,21 +168,27 @@ struct Sync {
   unsigned s_ready;                // vote scales of rounds < s_ready are in LDS
   unsigned v_done;                 // votes of rounds < v_done have left LDS
   unsigned timeout;
+  unsigned abort;                  // the grid is not all resident: every wave leaves its loop
 };
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned lds_get(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_wait_ge(unsigned* p, unsigned target, unsigned* timeout) {
+// Wait until *p >= target.  Returns false if the workgroup is aborting (the
+// caller then leaves its loop); a wait past the spin bound records a timeout
+// and returns true, so the grid always drains.
+__device__ __forceinline__ bool lds_wait_ge(Sync* sy, unsigned* p, unsigned target) {
   long spins = 0;
   while (lds_get(p) < target) {
+    if (lds_get(&sy->abort)) return false;
     __builtin_amdgcn_s_sleep(1);
     if (++spins > kSpin) {
-      *timeout = 1;
+      sy->timeout = 1;
       break;
     }
   }
   asm volatile("" ::: "memory");
+  return !lds_get(&sy->abort);
 }
 __device__ __forceinline__ void lds_add(unsigned* p) {
   lds_fence();
@@ -291,7 +298,7 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
   const int L = cur.L, W = a.W, P = L - W;
   const float sc = a.scale2;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
-  lds_wait_ge(&sy->q_ready, (unsigned)k + 1, &sy->timeout);
+  if (!lds_wait_ge(sy, &sy->q_ready, (unsigned)k + 1)) return;
   float mrow = kNegBig, zrow = 0.f;  // row n over this lane's positions of the round
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
@@ -366,8 +373,8 @@ __device__ __forceinline__ void phase_votes(const Launch& a, int k, const f32x16
                                             const float* s_iz, float* s_votes, Sync* sy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
   const float sc = a.scale2;
-  lds_wait_ge(&sy->s_ready, (unsigned)k + 1, &sy->timeout);
-  lds_wait_ge(&sy->v_done, (unsigned)(k >= 1 ? k - 1 : 0), &sy->timeout);  // round k - 2 left this buffer
+  if (!lds_wait_ge(sy, &sy->s_ready, (unsigned)k + 1)) return;
+  if (!lds_wait_ge(sy, &sy->v_done, (unsigned)(k >= 1 ? k - 1 : 0))) return;  // round k - 2 left this buffer
   float mr[16], iz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -483,7 +490,7 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
       float M, Z;
       const bool ok = ctl_head_stats(a, w1, ex, M, Z);
       if (!ok && lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lds_wait_ge(&sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1], &sy->timeout);
+      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1])) return;
       if (lane < W) {
         s_m[(k - 1) & 1][lane] = ok ? M : __builtin_nanf("");
         s_iz[(k - 1) & 1][lane] = ok ? 1.f / Z : __builtin_nanf("");
@@ -502,14 +509,50 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
   }
 }
 
-// Memory wave.  Step k: (1) once round k's phase A is done, the chunk's
-// (m, z) of round k, merged from the streaming waves' pairs, to its slot;
-// (2) Qwin of round k + 2 into the buffer of round k; (3) votes of round
-// k - 1 to memory, then the votes buffer may be reused (v_done).
+// Publisher wave.  Once round k's phase A is done, the chunk's (m, z) of
+// round k, merged from the streaming waves' pairs, goes to its slot.  A wave
+// of its own, so that publication never waits behind a Qwin load or a votes
+// write (which waits for the previous exchange).
+__device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex, float (*s_maxp)[kSW * 32],
+                            float (*s_zp)[kSW * 32], Sync* sy) {
+  const int lane = threadIdx.x & 63;
+  const int W = a.W;
+  unsigned on_b[2] = {0, 0};  // owned rounds awaited so far, per parity
+  for (int k = 0; k < a.rounds; ++k) {
+    const Work w0 = round_work(a, k);
+    if (!w0.on) continue;
+    ++on_b[k & 1];
+    if (!lds_wait_ge(sy, &sy->cnt_b[k & 1], kSW * on_b[k & 1])) return;
+    if (lane < W) {
+      // Merge the waves' (max, sum) pairs in wave order against the tagged
+      // chunk maximum.
+      float m = s_maxp[k & 1][lane];
+#pragma unroll
+      for (int v = 1; v < kSW; ++v) m = fmaxf(m, s_maxp[k & 1][v * 32 + lane]);
+      m = tag_max(m);
+      // A wave with no visible position in the row has sum 0 and the
+      // sentinel maximum, whose ulp is huge: it adds nothing.
+      float zz = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSW; ++v) {
+        const float zv = s_zp[k & 1][v * 32 + lane];
+        if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
+      }
+      const Seg& s = a.seg[w0.e];
+      unsigned long long* slot =
+          ex + (s.fslot_base + (long long)w0.h * fused_slot_stride(s.fc) + w0.c) * kSlotWords;
+      __hip_atomic_store(slot + lane, pack_slot(m, zz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    KVSEL_FUSED_CTL_MARK(k, 5);
+  }
+}
+
+// Memory wave.  Step k: (1) Qwin of round k + 2 into the buffer of round k
+// once round k's phase A is done; (2) votes of round k - 1 to memory, then
+// the votes buffer may be reused (v_done).
 template <int D>
 __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
-                           unsigned long long* __restrict__ ex, uint4 (*qbufs)[TileGeom<D>::PIECES],
-                           float (*s_maxp)[kSW * 32], float (*s_zp)[kSW * 32], float (*s_votes)[kS], Sync* sy) {
+                           uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_votes)[kS], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   // Qwin of rounds 0 and 1 was issued before the residency handshake.
@@ -522,29 +565,8 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
     const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
     if (w0.on) {
       ++on_b[k & 1];
-      lds_wait_ge(&sy->cnt_b[k & 1], kSW * on_b[k & 1], &sy->timeout);
-      if (lane < W) {
-        // Merge the waves' (max, sum) pairs in wave order against the
-        // tagged chunk maximum.
-        float m = s_maxp[k & 1][lane];
-#pragma unroll
-        for (int v = 1; v < kSW; ++v) m = fmaxf(m, s_maxp[k & 1][v * 32 + lane]);
-        m = tag_max(m);
-        // A wave with no visible position in the row has sum 0 and the
-        // sentinel maximum, whose ulp is huge: it adds nothing.
-        float zz = 0.f;
-#pragma unroll
-        for (int v = 0; v < kSW; ++v) {
-          const float zv = s_zp[k & 1][v * 32 + lane];
-          if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
-        }
-        const Seg& s = a.seg[w0.e];
-        unsigned long long* slot =
-            ex + (s.fslot_base + (long long)w0.h * fused_slot_stride(s.fc) + w0.c) * kSlotWords;
-        __hip_atomic_store(slot + lane, pack_slot(m, zz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (!lds_wait_ge(sy, &sy->cnt_b[k & 1], kSW * on_b[k & 1])) return;
     }
-    KVSEL_FUSED_CTL_MARK(k, 5);
     if (ctl_issue_q<D>(a, k + 2, Q, qbufs[k & 1])) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       ctl_finish_q<D>(W, qbufs[k & 1]);
@@ -553,7 +575,7 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
     KVSEL_FUSED_CTL_MARK(k, 6);
     if (w1.on) {
       ++on_c[(k - 1) & 1];
-      lds_wait_ge(&sy->cnt_c[(k - 1) & 1], kSW * on_c[(k - 1) & 1], &sy->timeout);
+      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * on_c[(k - 1) & 1])) return;
       const Seg& s = a.seg[w1.e];
       const int P = s.L - W;
       float* vout = votes + s.vote_off + (long long)w1.h * s.vote_ld;
@@ -710,45 +732,58 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
   }
 }
 
-// Residency handshake (thread 0 of each workgroup).  The rounds need every
-// workgroup of the grid running at once, which a plain launch of one
-// workgroup per CU gives on an otherwise idle device but does not promise.
-// Each workgroup counts its arrival in one of kArriveGroups counters (on
-// separate lines: arrivals on one word would be serialised one after the
-// other); the last arrival of a group counts the group, and the last group
-// decides GO.  A workgroup that has waited longer than the bound decides
-// ABORT.  Both decisions are a compare-and-swap on one zeroed word, so every
-// workgroup follows the same one, and GO implies that all of them are
-// resident.
+// Residency handshake.  The rounds need every workgroup of the grid running
+// at once, which a plain launch of one workgroup per CU gives on an
+// otherwise idle device but does not promise.  It runs in two parts so that
+// it overlaps the streaming of round 0, which depends on no other
+// workgroup:
+//  * arrival, issued at kernel start before any K load (so the atomic is
+//    not queued behind the first tiles): one of kArriveGroups counters on
+//    separate lines (arrivals on one word would be serialised);
+//  * the decision, in the exchange wave before its first read of another
+//    workgroup's slot: the last arrival of a group counts the group, the
+//    last group decides GO; a workgroup that has waited longer than the
+//    bound decides ABORT.  Both are a compare-and-swap on one zeroed word,
+//    so every workgroup follows the same decision, and GO implies that all
+//    of them are resident.
 constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
-__device__ __forceinline__ unsigned residency(unsigned* status) {
-  unsigned* groups = status + 1;
-  unsigned* state = status + 2;
-  const unsigned grid = gridDim.x;
+__device__ __forceinline__ unsigned arrival_group(unsigned grid) {
   const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
-  const unsigned g = blockIdx.x % ng;
-  const unsigned members = (grid - g + ng - 1) / ng;
-  unsigned* ctr = status + kArriveStride * (1 + g);
-  const unsigned n = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  if (n == members) {
-    const unsigned done = __hip_atomic_fetch_add(groups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    if (done == ng) {
-      unsigned expect = 0u;
-      __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+  return blockIdx.x % ng;
+}
+__device__ __forceinline__ unsigned arrive(unsigned* status) {
+  unsigned* ctr = status + kArriveStride * (1 + arrival_group(gridDim.x));
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+// Lane 0 of the calling wave decides; the decision is returned to every lane.
+__device__ __forceinline__ unsigned decide(unsigned* status, unsigned arrived) {
+  unsigned s = 0u;
+  if ((threadIdx.x & 63) == 0) {
+    unsigned* groups = status + 1;
+    unsigned* state = status + 2;
+    const unsigned grid = gridDim.x;
+    const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
+    const unsigned g = arrival_group(grid);
+    const unsigned members = (grid - g + ng - 1) / ng;
+    if (arrived == members) {
+      const unsigned done = __hip_atomic_fetch_add(groups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+      if (done == ng) {
+        unsigned expect = 0u;
+        __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    const long long t0 = wall_clock64();
+    while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+      if (wall_clock64() - t0 > kResidencyTicks) {
+        unsigned expect = 0u;
+        __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_sleep(2);
     }
   }
-  const long long t0 = wall_clock64();
-  unsigned s;
-  while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-    if (wall_clock64() - t0 > kResidencyTicks) {
-      unsigned expect = 0u;
-      __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return s;
+  return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
 }
 
 template <int D>
@@ -765,11 +800,13 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __shared__ float s_m[2][32], s_iz[2][32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
-  __shared__ unsigned s_go;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  // The first K tiles and Qwin of rounds 0 and 1 are issued before the
-  // residency handshake, so their latency overlaps it.
+  unsigned arrived = 0u;
+  if (wave == kSW && lane == 0) arrived = arrive(status);
+  if (threadIdx.x == 0) sy = Sync{{0, 0}, {0, 0}, 0, 0, 0, 0, 0};
+  __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
+  // The first K tiles and Qwin of rounds 0 and 1.
   WaveTiles cur{K, 0, 0, false};
   int issued = 0, consumed = 0;
   if (wave < kSW) {
@@ -779,53 +816,54 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
     ctl_issue_q<D>(a, 0, Q, s_q[0]);
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
-  if (threadIdx.x == 0) {
-    sy = Sync{{0, 0}, {0, 0}, 0, 0, 0, 0};
-    s_go = residency(status);
+  if (wave == kSW) {
+    if (decide(status, arrived) == kFusedGo)
+      ctl_exchange<D>(a, ex, status, row_stats, s_m, s_iz, &sy);
+    else
+      lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
+  } else if (wave == kSW + 1) {
+    ctl_memory<D>(a, Q, votes, s_q, s_votes, &sy);
+  } else if (wave == kSW + 2) {
+    ctl_publish(a, ex, s_maxp, s_zp, &sy);
+  } else {
+    uint4 (*ring)[G::PIECES] = s_ring[wave];
+    f32x16 xa[kTT], xb[kTT];
+    bool prev_on = false;
+    // Step k streams round k into one register set (with this wave's row
+    // statistics), then votes round k - 1 from the other set; the sets swap
+    // every step.  The exchange of round k - 1 overlaps the streaming of
+    // round k.
+    auto step = [&](int k, f32x16 (&X0)[kTT], f32x16 (&X1)[kTT]) {
+      KVSEL_FUSED_MARK(k, 0);
+      const WaveTiles nxt = wave_tiles<D>(a, K, k + 1, wave);
+      if (cur.on) {
+        phase_stream<D>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
+      } else {
+        for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(nxt, t, ring, issued);
+      }
+      KVSEL_FUSED_MARK(k, 1);
+      KVSEL_FUSED_MARK(k, 2);
+      if (prev_on) phase_votes(a, k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
+      KVSEL_FUSED_MARK(k, 3);
+      prev_on = cur.on;
+      cur = nxt;
+    };
+    const int steps = a.rounds + 1;
+    for (int k = 0; k < steps; k += 2) {
+      step(k, xa, xb);
+      if (k + 1 >= steps || lds_get(&sy.abort)) break;
+      step(k + 1, xb, xa);
+      if (lds_get(&sy.abort)) break;
+    }
   }
-  __syncthreads();  // afterwards waves meet through LDS flags (or, in the fallback, barriers)
-  if (s_go != kFusedGo) {  // not all resident: whole heads, one workgroup each
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads above land before LDS is reused
+  // Every wave's loads have landed before LDS is reused or the wave ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (sy.abort) {  // not all resident: whole heads, one workgroup each
     solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
     return;
   }
-  if (wave >= kSW) {
-    if (wave == kSW)
-      ctl_exchange<D>(a, ex, status, row_stats, s_m, s_iz, &sy);
-    else
-      ctl_memory<D>(a, Q, votes, ex, s_q, s_maxp, s_zp, s_votes, &sy);
-    if ((threadIdx.x & 63) == 0 && sy.timeout)
-      __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  uint4 (*ring)[G::PIECES] = s_ring[wave];
-  f32x16 xa[kTT], xb[kTT];
-  bool prev_on = false;
-  // Step k streams round k into one register set (with this wave's row
-  // statistics), then votes round k - 1 from the other set; the sets swap
-  // every step.  The exchange of round k - 1 overlaps the streaming of round k.
-  auto step = [&](int k, f32x16 (&X0)[kTT], f32x16 (&X1)[kTT]) {
-    KVSEL_FUSED_MARK(k, 0);
-    const WaveTiles nxt = wave_tiles<D>(a, K, k + 1, wave);
-    if (cur.on) {
-      phase_stream<D>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
-    } else {
-      for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(nxt, t, ring, issued);
-    }
-    KVSEL_FUSED_MARK(k, 1);
-    KVSEL_FUSED_MARK(k, 2);
-    if (prev_on) phase_votes(a, k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
-    KVSEL_FUSED_MARK(k, 3);
-    prev_on = cur.on;
-    cur = nxt;
-  };
-  const int steps = a.rounds + 1;
-  for (int k = 0; k < steps; k += 2) {
-    step(k, xa, xb);
-    if (k + 1 >= steps) break;
-    step(k + 1, xb, xa);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (threadIdx.x == 0 && sy.timeout) __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
