@@ -54,6 +54,8 @@ def kernel_alg_bytes(name, w, nch):
         return H * 2048 * 4 + H * 2 * 512 * 4
     if name == "emit":              # pooled scores, kept K and V rows read and written, indices
         return H * P * 4 + 4 * H * C * D * e + H * C * 4
+    if name == "select":            # votes read, indices written, kept K and V rows read and written
+        return H * P * 4 + H * C * 4 + 4 * H * C * D * e
     if name == "fill":              # per-head exchange records cleared
         return H * 64 + 256
     return None
@@ -78,6 +80,7 @@ KERNEL_SOURCES = {
     "threshold": ("kvsel_select.hip", "kvsel_internal.h"),
     "emit": ("kvsel_select.hip", "kvsel_internal.h"),
     "gather": ("kvsel_select.hip", "kvsel_internal.h"),
+    "select": ("kvsel_select.hip", "kvsel_internal.h"),
 }
 
 

@@ -241,8 +241,14 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   // it applies (it reads K once), else two-pass.
   const bool use_fused = fused_ok && g_scoring != KVSEL_SCORING_TWO_PASS;
   uint32_t* hist = (uint32_t*)(ws + p.off_hist);
+  // Rows of at most select_rows_max() prefix positions are resolved by one
+  // workgroup each (threshold and picks) and copied by the gather kernel;
+  // longer rows go through the segment-parallel candidates, threshold and
+  // emit kernels.
+  bool whole_rows = true;
+  for (int b = 0; b < p.B && whole_rows; ++b) whole_rows = p.L[b] < p.C[b] || p.L[b] - p.W <= select_rows_max();
   if (use_fused) {
-    // Exchange records, status word and histograms start at zero (on the
+    // Exchange records, status words and histograms start at zero (on the
     // two-pass path the statistics kernel clears the histograms).
     hipError_t e = timed("fill", st, [&] {
       return launch_fill_u32(counters, (long long)(p.bytes - p.off_ctr) / 4, 0u, st);
@@ -312,6 +318,25 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
+    }
+    if (whole_rows) {
+      if (items > 0) {
+        e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, ghist, st); });
+        if (e != hipSuccess) return device_error(e, "pool launch");
+      }
+      e = timed("select", st, [&] { return launch_select_hist(a, rows, pooled, ghist, indices, st); });
+      if (e != hipSuccess) return device_error(e, "select launch");
+      const int rpb = gather_rows_per_block(p.D, p.dtype);
+      int gitems = 0;
+      for (int k = 0; k < nb; ++k) {
+        Seg& s = a.seg[k];
+        s.gitem0 = gitems;
+        s.gblk = (s.nout + rpb - 1) / rpb;
+        gitems += s.nh * s.gblk;
+      }
+      e = timed("gather", st, [&] { return launch_gather(a, gitems, p.dtype, K, V, indices, K_out, V_out, st); });
+      if (e != hipSuccess) return device_error(e, "gather launch");
+      continue;
     }
     if (items > 0) {
       e = timed("pool", st, [&] { return launch_pool(a, rows, maxP, votes, pooled, ghist, st); });
@@ -451,6 +476,11 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   if (e != hipSuccess) return device_error(e, "fill launch");
   e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
   if (e != hipSuccess) return device_error(e, "histogram launch");
+  if (n <= select_rows_max()) {  // one workgroup per row
+    e = timed("select", st, [&] { return launch_select_hist(a, rows, scores, hist, out, st); });
+    if (e != hipSuccess) return device_error(e, "select launch");
+    return ok();
+  }
   e = timed("candidates", st, [&] { return launch_candidates(a, rows, n, scores, hist, cand, segcnt, st); });
   if (e != hipSuccess) return device_error(e, "candidates launch");
   e = timed("threshold", st, [&] { return launch_threshold(a, rows, hist, cand, cut, segcnt, st); });

@@ -105,6 +105,13 @@ hipError_t launch_threshold(const Launch& a, int rows, const uint32_t* hist, con
 hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, const float* scores,
                        const uint32_t* cut, const uint32_t* segcnt, int32_t* indices, const void* K, const void* V,
                        void* K_out, void* V_out, hipStream_t st);
+// Threshold and picks of whole rows of at most select_rows_max() prefix
+// positions, one workgroup per row, from the pooled scores and their
+// first-digit histograms (launch_pool): the picks ascending, then the window
+// positions (a.window), into the indices.  Bypass rows are left alone.
+int select_rows_max();
+hipError_t launch_select_hist(const Launch& a, int rows, const float* scores, const uint32_t* hist,
+                              int32_t* indices, hipStream_t st);
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns

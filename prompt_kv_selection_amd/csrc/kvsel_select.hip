@@ -620,6 +620,159 @@ hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes,
   return hipGetLastError();
 }
 
+// ---- threshold and picks of whole rows (rows of at most kSelMaxP positions)
+//
+// Given a row's pooled scores and the histogram of their first radix digit
+// (bits 31..21, built by pool_hist_kernel across many workgroups), one
+// 1024-thread workgroup per row finds the boundary digit, compacts that
+// digit's scores (the candidates) into LDS, resolves the remaining 21 bits
+// over them, and writes the picks in index order (tau-equal positions lowest
+// index first) followed by the window positions.  Position u * 1024 + t
+// belongs to thread t (column u), so the loads are coalesced; the output
+// order comes from per-(column, wave) counts and one scan over them.
+constexpr int kSelThreads = 1024;
+constexpr int kSelCols = 36;
+constexpr int kSelMaxP = kSelThreads * kSelCols;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelCand = 32768;  // candidates held in LDS (more: the digits scan the registers)
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(const Launch a, const float* __restrict__ scores,
+                                                                  const uint32_t* __restrict__ ghist,
+                                                                  int32_t* __restrict__ indices) {
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  const int h = s.h0 + (row - s.row0);
+  int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
+  if (s.L < s.C) {  // bypass: every position is kept
+    for (int m = tid; m < s.L; m += kSelThreads) out[m] = m;
+    return;
+  }
+  const int W = a.window ? a.W : 0;
+  const int P = s.L - W, count = s.C - W;
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t cw[kSelCols * kSelWaves];  // per (column, wave) counts, then their exclusive prefixes
+  __shared__ uint32_t cl[kSelCand];
+  __shared__ uint32_t sh[32];
+  __shared__ uint32_t s_digit, s_need;
+
+  // Every load is issued before the first use.
+  const uint32_t* kr = reinterpret_cast<const uint32_t*>(scores + s.vote_off + (long long)h * s.vote_ld);
+  uint32_t key[kSelCols];
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u) {
+    const int j = u * kSelThreads + tid;
+    key[u] = j < P ? kr[j] : 0u;
+  }
+  const uint32_t* gh = ghist + (long long)row * 2048;
+  for (int d = tid; d < 2048; d += kSelThreads) hist[d] = gh[d];
+  __syncthreads();
+  pick_digit<kSelThreads>(hist, 2048, (uint32_t)count, sh, &s_digit, &s_need);
+  const uint32_t d1 = s_digit;
+  uint32_t need = s_need;
+
+  // Candidates of the boundary digit, compacted into LDS in any order.
+  uint64_t cm = 0;
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u)
+    if (u * kSelThreads + tid < P && (key[u] >> 21) == d1) cm |= 1ull << u;
+  const uint32_t nmine = (uint32_t)__popcll(cm);
+  uint32_t ncand;
+  uint32_t coff = block_scan<kSelThreads>(nmine, sh, ncand) - nmine;
+  const bool in_lds = ncand <= (uint32_t)kSelCand;
+  if (in_lds) {
+#pragma unroll
+    for (int u = 0; u < kSelCols; ++u)
+      if ((cm >> u) & 1ull) cl[coff++] = key[u];
+  }
+  __syncthreads();
+  // The other two digits (11 and 10 bits) over the candidates.
+  uint32_t prefix = d1;
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
+    const int bits = pass == 1 ? 11 : 10;
+    const int nb = 1 << bits;
+    for (int d = tid; d < nb; d += kSelThreads) hist[d] = 0u;
+    __syncthreads();
+    if (in_lds) {
+      for (uint32_t i = tid; i < ncand; i += kSelThreads) {
+        const uint32_t k = cl[i];
+        if ((k >> (shift + bits)) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSelCols; ++u) {
+        const uint32_t k = key[u];
+        if (((cm >> u) & 1ull) && (k >> (shift + bits)) == prefix)
+          atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    pick_digit<kSelThreads>(hist, nb, need, sh, &s_digit, &s_need);
+    prefix = (prefix << bits) | s_digit;
+    need = s_need;
+  }
+  const uint32_t tau = prefix, need_eq = need;
+
+  // Rank of each tau-equal position among them in index order: counts per
+  // (column, wave), one scan, then the lanes below in the wave.
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u) {
+    const uint64_t m = __ballot(u * kSelThreads + tid < P && key[u] == tau);
+    if (lane == 0) cw[u * kSelWaves + wv] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  uint32_t tot;
+  {
+    const uint32_t c = tid < kSelCols * kSelWaves ? cw[tid] : 0u;
+    const uint32_t ex = block_scan<kSelThreads>(c, sh, tot) - c;
+    if (tid < kSelCols * kSelWaves) cw[tid] = ex;
+  }
+  __syncthreads();
+  uint64_t pm = 0;  // this thread's picks, bit u for column u
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u) {
+    const bool valid = u * kSelThreads + tid < P;
+    const bool eq = valid && key[u] == tau;
+    const uint64_t m = __ballot(eq);
+    const uint32_t rank = cw[u * kSelWaves + wv] + lanes_below(m);
+    if ((valid && key[u] > tau) || (eq && rank < need_eq)) pm |= 1ull << u;
+  }
+  __syncthreads();  // the eq prefixes are read
+  // Output slot of each pick: counts per (column, wave), one scan.
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u) {
+    const uint64_t m = __ballot((pm >> u) & 1ull);
+    if (lane == 0) cw[u * kSelWaves + wv] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  {
+    const uint32_t c = tid < kSelCols * kSelWaves ? cw[tid] : 0u;
+    const uint32_t ex = block_scan<kSelThreads>(c, sh, tot) - c;
+    if (tid < kSelCols * kSelWaves) cw[tid] = ex;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSelCols; ++u) {
+    const bool pick = (pm >> u) & 1ull;
+    const uint64_t m = __ballot(pick);
+    if (pick) out[cw[u * kSelWaves + wv] + lanes_below(m)] = u * kSelThreads + tid;
+  }
+  for (int i = tid; i < W; i += kSelThreads) out[count + i] = P + i;
+}
+
+int select_rows_max() { return kSelMaxP; }
+
+hipError_t launch_select_hist(const Launch& a, int rows, const float* scores, const uint32_t* hist,
+                              int32_t* indices, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(select_hist_kernel, dim3(rows), dim3(kSelThreads), 0, st, a, scores, hist, indices);
+  return hipGetLastError();
+}
+
 int selection_seg_size(long long max_positions) {
   const long long units = (max_positions + kSegUnit - 1) / kSegUnit;
   const long long per = (units + kMaxSegRow - 1) / kMaxSegRow;
