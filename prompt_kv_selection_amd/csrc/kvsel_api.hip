@@ -82,7 +82,7 @@ struct Plan {
   long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots, either path
   long long vote_elems = 0;   // heads * sum of P_b
   size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_cut = 0, off_segcnt = 0, off_ctr = 0,
-         off_status = 0, off_hist = 0, bytes = 0;
+         off_status = 0, off_hist = 0, off_coop = 0, bytes = 0;
 };
 
 // Selection workspace per (sequence, head) row: threshold and segment counts.
@@ -153,6 +153,9 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned));
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
   off = align256(off + (size_t)B * heads * 2048 * 4);
+  p.off_coop = off;  // cooperative selection: status per launch group, then per-row words
+  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned) +
+                 (size_t)B * heads * coop_row_words() * sizeof(unsigned));
   p.bytes = off;
   return KVSEL_OK;
 }
@@ -247,9 +250,28 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
   // emit kernels.
   bool whole_rows = true;
   for (int b = 0; b < p.B && whole_rows; ++b) whole_rows = p.L[b] < p.C[b] || p.L[b] - p.W <= select_rows_max();
-  if (use_fused) {
-    // Exchange records, status words and histograms start at zero (on the
-    // two-pass path the statistics kernel clears the histograms).
+  // The cooperative selection (pooling, threshold, picks and K/V copy in
+  // one launch, a workgroup per segment of a row) where its grid fits the
+  // device at once.
+  const int coop_cap = (kernel == 1 || kernel == 3 || kernel == 5 || kernel == 7) ? coop_grid_capacity(p.D, p.dtype) : 0;
+  std::vector<int> coop_segs((p.B + kMaxSegs - 1) / kMaxSegs, 0);
+  bool any_coop = false;
+  for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
+    const int nb = std::min(kMaxSegs, p.B - b0);
+    int segs = 1;
+    for (int b = b0; b < b0 + nb; ++b) {
+      const int n = p.L[b] < p.C[b] ? p.L[b] : p.L[b] - p.W;
+      segs = std::max(segs, (n + coop_segment() - 1) / coop_segment());
+    }
+    if (segs <= coop_max_segments() && (long long)segs * nb * p.heads <= coop_cap) {
+      coop_segs[gi] = segs;
+      any_coop = true;
+    }
+  }
+  if (use_fused || any_coop) {
+    // Exchange records, status words, histograms and the cooperative
+    // selection's words start at zero (on the two-pass path without the
+    // cooperative selection the statistics kernel clears the histograms).
     hipError_t e = timed("fill", st, [&] {
       return launch_fill_u32(counters, (long long)(p.bytes - p.off_ctr) / 4, 0u, st);
     });
@@ -318,6 +340,18 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
+    }
+    if (coop_segs[b0 / kMaxSegs] > 0) {
+      unsigned* cstatus = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * (b0 / kMaxSegs);
+      unsigned* crows = (unsigned*)(ws + p.off_coop) +
+                        (long long)kFusedStatusWords * ((p.B + kMaxSegs - 1) / kMaxSegs) +
+                        (long long)b0 * p.heads * coop_row_words();
+      e = timed("select", st, [&] {
+        return launch_select_coop(a, rows, coop_segs[b0 / kMaxSegs], p.dtype, votes, pooled_opt, crows, cstatus,
+                                  indices, K, V, K_out, V_out, st);
+      });
+      if (e != hipSuccess) return device_error(e, "select launch");
+      continue;
     }
     if (whole_rows) {
       if (items > 0) {

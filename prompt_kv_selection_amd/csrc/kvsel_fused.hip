@@ -732,60 +732,6 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
   }
 }
 
-// Residency handshake.  The rounds need every workgroup of the grid running
-// at once, which a plain launch of one workgroup per CU gives on an
-// otherwise idle device but does not promise.  It runs in two parts so that
-// it overlaps the streaming of round 0, which depends on no other
-// workgroup:
-//  * arrival, issued at kernel start before any K load (so the atomic is
-//    not queued behind the first tiles): one of kArriveGroups counters on
-//    separate lines (arrivals on one word would be serialised);
-//  * the decision, in the exchange wave before its first read of another
-//    workgroup's slot: the last arrival of a group counts the group, the
-//    last group decides GO; a workgroup that has waited longer than the
-//    bound decides ABORT.  Both are a compare-and-swap on one zeroed word,
-//    so every workgroup follows the same decision, and GO implies that all
-//    of them are resident.
-constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
-__device__ __forceinline__ unsigned arrival_group(unsigned grid) {
-  const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
-  return blockIdx.x % ng;
-}
-__device__ __forceinline__ unsigned arrive(unsigned* status) {
-  unsigned* ctr = status + kArriveStride * (1 + arrival_group(gridDim.x));
-  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-}
-// Lane 0 of the calling wave decides; the decision is returned to every lane.
-__device__ __forceinline__ unsigned decide(unsigned* status, unsigned arrived) {
-  unsigned s = 0u;
-  if ((threadIdx.x & 63) == 0) {
-    unsigned* groups = status + 1;
-    unsigned* state = status + 2;
-    const unsigned grid = gridDim.x;
-    const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
-    const unsigned g = arrival_group(grid);
-    const unsigned members = (grid - g + ng - 1) / ng;
-    if (arrived == members) {
-      const unsigned done = __hip_atomic_fetch_add(groups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-      if (done == ng) {
-        unsigned expect = 0u;
-        __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    const long long t0 = wall_clock64();
-    while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-      if (wall_clock64() - t0 > kResidencyTicks) {
-        unsigned expect = 0u;
-        __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,

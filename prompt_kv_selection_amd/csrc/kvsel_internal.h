@@ -112,6 +112,18 @@ hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, 
 int select_rows_max();
 hipError_t launch_select_hist(const Launch& a, int rows, const float* scores, const uint32_t* hist,
                               int32_t* indices, hipStream_t st);
+// Cooperative selection: coop_segment() positions of a row per workgroup,
+// at most coop_max_segments() per row, grid (segs, rows) of at most
+// coop_grid_capacity() workgroups; pooling, top-(C-W), window and the K/V
+// copy in one launch (pooling widths 1, 3, 5, 7).  coop [rows][coop_row_words()]
+// and status (kFusedStatusWords) start at zero.  pooled may be nullptr.
+int coop_max_segments();
+int coop_segment();
+int coop_row_words();
+int coop_grid_capacity(int D, int dtype);
+hipError_t launch_select_coop(const Launch& a, int rows, int segs, int dtype, const float* votes, float* pooled,
+                              unsigned* coop, unsigned* status, int32_t* indices, const void* K, const void* V,
+                              void* K_out, void* V_out, hipStream_t st);
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns
@@ -125,6 +137,61 @@ constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
 constexpr int kArriveGroups = 16;
 constexpr int kArriveStride = 64;
 constexpr int kFusedStatusWords = kArriveStride * (kArriveGroups + 1);
+// Residency handshake of kernels whose workgroups wait for each other (the
+// single-read scoring and the cooperative selection).  They need every
+// workgroup of the grid running at once, which a plain launch of a grid that
+// fits the device gives on an otherwise idle device but does not promise.
+// It runs in two parts so that it can overlap work that depends on no other
+// workgroup:
+//  * arrival, issued at kernel start before any K load (so the atomic is
+//    not queued behind the first tiles): one of kArriveGroups counters on
+//    separate lines (arrivals on one word would be serialised);
+//  * the decision, in the exchange wave before its first read of another
+//    workgroup's slot: the last arrival of a group counts the group, the
+//    last group decides GO; a workgroup that has waited longer than the
+//    bound decides ABORT.  Both are a compare-and-swap on one zeroed word,
+//    so every workgroup follows the same decision, and GO implies that all
+//    of them are resident.
+constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
+__device__ inline unsigned arrival_group(unsigned grid) {
+  const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
+  return blockIdx.x % ng;
+}
+__device__ inline unsigned arrive(unsigned* status) {
+  unsigned* ctr = status + kArriveStride * (1 + arrival_group(gridDim.x));
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+// Lane 0 of the calling wave decides; the decision is returned to every lane.
+__device__ inline unsigned decide(unsigned* status, unsigned arrived) {
+  unsigned s = 0u;
+  if ((threadIdx.x & 63) == 0) {
+    unsigned* groups = status + 1;
+    unsigned* state = status + 2;
+    const unsigned grid = gridDim.x;
+    const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
+    const unsigned g = arrival_group(grid);
+    const unsigned members = (grid - g + ng - 1) / ng;
+    if (arrived == members) {
+      const unsigned done = __hip_atomic_fetch_add(groups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+      if (done == ng) {
+        unsigned expect = 0u;
+        __hip_atomic_compare_exchange_strong(state, &expect, kFusedGo, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    const long long t0 = wall_clock64();
+    while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
+      if (wall_clock64() - t0 > kResidencyTicks) {
+        unsigned expect = 0u;
+        __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
+}
+
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
 int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot

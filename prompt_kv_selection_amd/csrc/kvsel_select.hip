@@ -773,6 +773,422 @@ hipError_t launch_select_hist(const Launch& a, int rows, const float* scores, co
   return hipGetLastError();
 }
 
+// Pooling of width KW over the window w (registers, centre w[KW / 2]), as in
+// pool_hist_kernel.
+template <int KW, bool MAX>
+__device__ __forceinline__ float pool_window(const float (&w)[KW]) {
+  constexpr int r = KW / 2;
+  if (KW == 1) return w[0];
+  if (MAX) {
+    float res = w[r];
+#pragma unroll
+    for (int q = 0; q < KW; ++q) res = fmaxf(res, w[q]);
+    return res;
+  }
+  return avg_sorted<KW>(w + r);
+}
+
+// ---- cooperative selection: segments of a row in parallel
+//
+// A row's P prefix positions are cut into segments of kCoopSeg positions,
+// one 512-thread workgroup each (thread t owns kCoopPer consecutive
+// positions of its segment), which pools its votes into keys kept in
+// registers.  The threshold tau of the (C-W)-th largest key is found digit
+// by digit (11, 11 and 10 bits): every segment adds its histogram of the
+// digit (over its keys that match the digits found so far) into the row's
+// histogram with device-scope atomics, and every segment reads the row's
+// histogram until its bins add up to the number of keys taking part (P,
+// then the count of the chosen bin): bins only grow, so a matching sum
+// means every bin is final.  Each segment then publishes its counts above
+// and on tau (one 64-bit word, zero until written), and from the earlier
+// segments' counts knows where its picks go: it writes them in index order
+// (tau-equal ones lowest index first) and copies their K and V rows; the
+// last segment adds the window.  The grid must be resident at once; the
+// residency handshake decides this, and otherwise the first workgroup of
+// each row runs every segment of its row in turn, with the same arithmetic
+// and results.
+constexpr int kCoopThreads = 512;
+constexpr int kCoopPer = 8;
+constexpr int kCoopSeg = kCoopThreads * kCoopPer;
+constexpr int kCoopMaxSeg = 64;
+constexpr int kCoopStride = kCoopPer + 1;         // LDS words per thread (odd: conflict-free reads)
+constexpr int kCoopHalo = kCoopThreads * kCoopStride;  // LDS index of the halo slots
+constexpr int kCoopHist = 2048 + 2048 + 1024;     // the row's histograms of the three digits
+constexpr int kCoopRowWords = kCoopHist + 2 * kCoopMaxSeg;  // + the segments' 64-bit counts
+static_assert(kMaxPoolRadius >= 3, "pooling widths up to 7");
+
+// Wait until word i of p is non-zero for every i < n (one wave polls,
+// then the workgroup meets).  Bounded: a timed-out wait sets an error flag.
+__device__ void coop_wait(const unsigned long long* p, int n, unsigned* err) {
+  if (threadIdx.x < 64) {
+    long spins = 0;
+    for (;;) {
+      bool ok = true;
+      for (int i = threadIdx.x; i < n; i += 64)
+        ok = ok && __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0ull;
+      if (__ballot(!ok) == 0) break;
+      if (++spins > (1L << 22)) {
+        if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// Read the row histogram gh[nb] into hist until its bins add up to total.
+template <int NT>
+__device__ void coop_read_hist(const uint32_t* gh, int nb, uint32_t total, uint32_t* hist, uint32_t* sh,
+                               unsigned* err) {
+  long spins = 0;
+  for (;;) {
+    uint32_t part = 0;
+    for (int d = threadIdx.x; d < nb; d += NT) {
+      const uint32_t c = __hip_atomic_load(gh + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hist[d] = c;
+      part += c;
+    }
+    uint32_t sum;
+    (void)block_scan<NT>(part, sh, sum);
+    if (sum == total) break;
+    if (++spins > (1L << 20)) {
+      if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+}
+
+// Keys of segment g: pooled scores of positions g * kCoopSeg + t * kCoopPer + u
+// (0 past P), through LDS with r neighbours on each side.
+template <int KW, bool MAX>
+__device__ __forceinline__ void coop_keys(const float* __restrict__ v, int P, int g, float* sv,
+                                          uint32_t (&key)[kCoopPer]) {
+  constexpr int r = KW / 2;
+  const int tid = threadIdx.x, j0 = g * kCoopSeg;
+  const float pad = MAX ? -INFINITY : 0.f;
+  auto at = [](int i) {  // LDS index of segment position i (-r <= i < kCoopSeg + r)
+    return i < 0 ? kCoopHalo + (i + r) : (i >= kCoopSeg ? kCoopHalo + 2 * r + (i - kCoopSeg)
+                                                         : (i / kCoopPer) * kCoopStride + i % kCoopPer);
+  };
+  __syncthreads();  // the previous segment's reads are done
+  float tv[kCoopPer];
+#pragma unroll
+  for (int k = 0; k < kCoopPer; ++k) {
+    const int p = j0 + k * kCoopThreads + tid;
+    tv[k] = p < P ? v[p] : pad;
+  }
+  float hl = pad, hh = pad;
+  if (tid < r) {
+    const int pl = j0 - r + tid, ph = j0 + kCoopSeg + tid;
+    hl = pl >= 0 && pl < P ? v[pl] : pad;
+    hh = ph < P ? v[ph] : pad;
+  }
+#pragma unroll
+  for (int k = 0; k < kCoopPer; ++k) sv[at(k * kCoopThreads + tid)] = tv[k];
+  if (tid < r) {
+    sv[at(tid - r)] = hl;
+    sv[at(kCoopSeg + tid)] = hh;
+  }
+  __syncthreads();
+  float w[KW];
+  const int i0 = tid * kCoopPer;
+#pragma unroll
+  for (int q = 0; q < KW - 1; ++q) w[q + 1] = sv[at(i0 - r + q)];
+#pragma unroll
+  for (int u = 0; u < kCoopPer; ++u) {
+#pragma unroll
+    for (int q = 0; q < KW - 1; ++q) w[q] = w[q + 1];
+    w[KW - 1] = sv[at(i0 + u + r)];
+    key[u] = j0 + i0 + u < P ? __float_as_uint(pool_window<KW, MAX>(w)) : 0u;
+  }
+}
+
+// This segment's histogram of a digit (bits shift .. shift + bits - 1) over
+// its keys whose higher bits equal prefix (all keys for the first digit),
+// added into gh with device-scope atomics.
+__device__ __forceinline__ void coop_add_hist(const uint32_t (&key)[kCoopPer], int valid, int shift, int bits,
+                                              uint32_t prefix, bool first, uint32_t* hist, uint32_t* gh) {
+  const int tid = threadIdx.x, nb = 1 << bits;
+  for (int d = tid; d < nb; d += kCoopThreads) hist[d] = 0u;
+  __syncthreads();
+  uint32_t run_bin = 0xFFFFFFFFu, run_len = 0;  // equal digits of consecutive positions: one atomic per run
+#pragma unroll
+  for (int u = 0; u < kCoopPer; ++u) {
+    const uint32_t k = key[u];
+    if (u < valid && (first || (k >> (shift + bits)) == prefix)) {
+      const uint32_t b = (k >> shift) & (uint32_t)(nb - 1);
+      if (b != run_bin) {
+        if (run_len) atomicAdd(&hist[run_bin], run_len);
+        run_bin = b;
+        run_len = 0;
+      }
+      ++run_len;
+    }
+  }
+  if (run_len) atomicAdd(&hist[run_bin], run_len);
+  __syncthreads();
+  for (int d = tid; d < nb; d += kCoopThreads)
+    if (hist[d]) __hip_atomic_fetch_add(gh + d, hist[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copy output rows m0 .. m0 + n of K and V from source rows first + i
+// (sel == nullptr) or sel[i] (LDS), RU 16-byte pieces per row, consecutive
+// threads on consecutive pieces, four pieces of each in flight per thread.
+template <int RU>
+__device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const int32_t* sel, long long in_row0,
+                                               long long out_row0, const uint4* __restrict__ K,
+                                               const uint4* __restrict__ V, uint4* __restrict__ Ko,
+                                               uint4* __restrict__ Vo) {
+  constexpr int kFly = 4;
+  const int total = n * RU, tid = threadIdx.x;
+  for (int e0 = 0; e0 < total; e0 += kFly * kCoopThreads) {
+    uint4 kv[kFly], vv[kFly];
+#pragma unroll
+    for (int f = 0; f < kFly; ++f) {
+      const int e = min(e0 + f * kCoopThreads + tid, total - 1);
+      const int i = e / RU;
+      const long long from = (in_row0 + (sel ? sel[i] : first + i)) * RU + e % RU;
+      kv[f] = K[from];
+      vv[f] = V[from];
+    }
+#pragma unroll
+    for (int f = 0; f < kFly; ++f) {
+      const int e = e0 + f * kCoopThreads + tid;
+      if (e < total) {
+        const long long to = (out_row0 + m0 + e / RU) * RU + e % RU;
+        Ko[to] = kv[f];
+        Vo[to] = vv[f];
+      }
+    }
+  }
+}
+
+template <int RU, int KW, bool MAX>
+__global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
+    const Launch a, const float* __restrict__ votes, float* __restrict__ pooled, unsigned* __restrict__ coop,
+    unsigned* __restrict__ status, int32_t* __restrict__ indices, const uint4* __restrict__ K,
+    const uint4* __restrict__ V, uint4* __restrict__ Ko, uint4* __restrict__ Vo) {
+  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  __shared__ float sv[kCoopHalo + 8];
+  __shared__ uint32_t hist[2048];
+  __shared__ int32_t picks[kCoopSeg];
+  __shared__ uint32_t sh[32];
+  __shared__ uint32_t s_digit, s_need;
+  __shared__ unsigned s_go;
+  __shared__ uint32_t s_cnt[kCoopMaxSeg], s_pre[kCoopMaxSeg];  // per-segment counts and prefixes
+  static_assert(kCoopPer == 8, "the window ranks below use 8 positions per thread");
+
+  // Arrival first; the decision is taken once the own segment's keys are
+  // in place (they depend on no other workgroup), before anything is
+  // published.
+  unsigned arrived = 0u;
+  if (tid == 0) arrived = arrive(status);
+  const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  const int h = s.h0 + (row - s.row0);
+  int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
+  const long long in_row0 = s.kv_off / a.D + (long long)h * s.L;
+  const long long out_row0 = s.out_off + (long long)h * s.out_ld;
+  // Output rows m0 .. m0 + n from source rows first + i (sel == nullptr)
+  // or sel[i].
+  auto copy = [&](int m0, int n, int first, const int32_t* sel) {
+    coop_copy_rows<RU>(m0, n, first, sel, in_row0, out_row0, K, V, Ko, Vo);
+  };
+  if (s.L < s.C) {  // bypass: every position, segment by segment
+    if (tid == 0) s_go = decide(status, arrived);
+    __syncthreads();
+    const bool go = s_go == kFusedGo;
+    if (!go && seg != 0) return;
+    for (int g = go ? seg : 0; g < (go ? seg + 1 : (s.L + kCoopSeg - 1) / kCoopSeg); ++g) {
+      const int m0 = g * kCoopSeg, n = max(0, min(kCoopSeg, s.L - m0));
+      for (int i = tid; i < n; i += kCoopThreads) out[m0 + i] = m0 + i;
+      copy(m0, n, m0, nullptr);
+    }
+    return;
+  }
+  const int W = a.window ? a.W : 0;
+  const int P = s.L - W, count = s.C - W;
+  const int nseg = (P + kCoopSeg - 1) / kCoopSeg;
+  const float* v = votes + s.vote_off + (long long)h * s.vote_ld;
+  uint32_t* words = coop + (long long)row * kCoopRowWords;
+  uint32_t* gh1 = words;
+  uint32_t* gh2 = words + 2048;
+  uint32_t* gh3 = words + 4096;
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(words + kCoopHist);
+  uint32_t key[kCoopPer];
+  auto valid_of = [&](int g) { return max(0, min(kCoopPer, P - g * kCoopSeg - tid * kCoopPer)); };
+  // The own segment's keys depend on no other workgroup: computed before
+  // the decision.
+  if (seg < nseg) coop_keys<KW, MAX>(v, P, seg, sv, key);
+  if (tid == 0) s_go = decide(status, arrived);
+  __syncthreads();
+  const bool go = s_go == kFusedGo;
+  if (go ? seg >= nseg : seg != 0) return;  // not all resident: the row's first workgroup does every segment
+  const int g0 = go ? seg : 0, g1 = go ? seg + 1 : nseg;  // the segments this workgroup runs
+
+  // The three digits of tau.
+  uint32_t prefix = 0u, need = (uint32_t)count, total = (uint32_t)P;
+  for (int digit = 0; digit < 3; ++digit) {
+    const int shift = digit == 0 ? 21 : (digit == 1 ? 10 : 0);
+    const int bits = digit == 2 ? 10 : 11;
+    uint32_t* gh = digit == 0 ? gh1 : (digit == 1 ? gh2 : gh3);
+    for (int g = g0; g < g1; ++g) {
+      if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
+      if (digit == 0 && pooled != nullptr) {
+        float* o = pooled + s.vote_off + (long long)h * s.vote_ld + g * kCoopSeg + tid * kCoopPer;
+        const int n = valid_of(g);
+#pragma unroll
+        for (int u = 0; u < kCoopPer; ++u)
+          if (u < n) o[u] = __uint_as_float(key[u]);
+      }
+      coop_add_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist, gh);
+    }
+    coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, status);
+    pick_digit<kCoopThreads>(hist, 1 << bits, need, sh, &s_digit, &s_need);
+    total = hist[s_digit];
+    prefix = (prefix << bits) | s_digit;
+    need = s_need;
+    __syncthreads();  // hist is rewritten by the next digit
+  }
+  const uint32_t tau = prefix, need_eq = need;
+  for (int g = g0; g < g1; ++g) {
+    if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
+    const int n = valid_of(g);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < kCoopPer; ++u) {
+      gt += u < n && key[u] > tau;
+      eq += u < n && key[u] == tau;
+    }
+    uint32_t tg, te;
+    (void)block_scan<kCoopThreads>(gt, sh, tg);
+    (void)block_scan<kCoopThreads>(eq, sh, te);
+    if (tid == 0)
+      __hip_atomic_store(cnt + g, (unsigned long long)(tg + 1u) | ((unsigned long long)te << 32), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  coop_wait(cnt, nseg, status);
+
+  // Phase 4: picks in index order at their final slots, and their rows.
+  // Per segment: the picks and tau-equal positions of the earlier segments
+  // (all counts read at once, a lane each, and scanned).
+  if (tid < 64) {
+    const unsigned long long c =
+        tid < nseg ? __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1ull;
+    const uint32_t gq = (uint32_t)c - 1u, eqq = (uint32_t)(c >> 32);
+    uint32_t eq_incl = eqq;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(eq_incl, o);
+      if (tid >= o) eq_incl += t;
+    }
+    const uint32_t eqb = eq_incl - eqq;
+    const uint32_t mine_picks = gq + (need_eq > eqb ? min(eqq, need_eq - eqb) : 0u);
+    uint32_t p_incl = mine_picks;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(p_incl, o);
+      if (tid >= o) p_incl += t;
+    }
+    s_cnt[tid] = eqb;              // tau-equal positions before segment tid
+    s_pre[tid] = p_incl - mine_picks;  // picks before segment tid
+  }
+  __syncthreads();
+  for (int g = g0; g < g1; ++g) {
+    if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
+    const uint32_t before = s_pre[g], eq_before = s_cnt[g];
+    uint32_t eq = 0;
+#pragma unroll
+    for (int u = 0; u < kCoopPer; ++u) eq += g * kCoopSeg + tid * kCoopPer + u < P && key[u] == tau;
+    uint32_t tot;
+    const uint32_t eqb = eq_before + block_scan<kCoopThreads>(eq, sh, tot) - eq;  // tau-equal before my first
+    uint32_t pm = 0, seen = eqb;
+#pragma unroll
+    for (int u = 0; u < kCoopPer; ++u) {
+      const bool valid = g * kCoopSeg + tid * kCoopPer + u < P;
+      if (valid && key[u] > tau) pm |= 1u << u;
+      if (valid && key[u] == tau) {
+        if (seen < need_eq) pm |= 1u << u;
+        ++seen;
+      }
+    }
+    const uint32_t np = (uint32_t)__popc(pm);
+    uint32_t ntot;
+    uint32_t off = block_scan<kCoopThreads>(np, sh, ntot) - np;
+#pragma unroll
+    for (int u = 0; u < kCoopPer; ++u)
+      if ((pm >> u) & 1u) {
+        const int j = g * kCoopSeg + tid * kCoopPer + u;
+        out[before + off] = j;
+        picks[off++] = j;
+      }
+    __syncthreads();
+    if (RU > 0) copy((int)before, (int)ntot, 0, picks);
+    if (g == nseg - 1 && W > 0) {  // the window follows the picks
+      for (int i = tid; i < W; i += kCoopThreads) out[count + i] = P + i;
+      if (RU > 0) copy(count, W, P, nullptr);
+    }
+    __syncthreads();  // picks[] is rewritten by the next segment
+  }
+  (void)lane;
+}
+
+int coop_max_segments() { return kCoopMaxSeg; }
+int coop_segment() { return kCoopSeg; }
+int coop_row_words() { return kCoopRowWords; }
+
+template <int RU>
+hipError_t launch_select_coop_ru(const Launch& a, dim3 grid, const float* votes, float* pooled, unsigned* coop,
+                                 unsigned* status, int32_t* indices, const uint4* k, const uint4* v, uint4* ko,
+                                 uint4* vo, hipStream_t st) {
+  const bool mx = a.pooling == 1;
+#define KVSEL_COOP(KW, MX)                                                                                      \
+  hipLaunchKernelGGL((select_coop_kernel<RU, KW, MX>), grid, dim3(kCoopThreads), 0, st, a, votes, pooled, coop, \
+                     status, indices, k, v, ko, vo)
+  switch (a.kernel) {
+    case 1: KVSEL_COOP(1, false); break;
+    case 3: if (mx) KVSEL_COOP(3, true); else KVSEL_COOP(3, false); break;
+    case 5: if (mx) KVSEL_COOP(5, true); else KVSEL_COOP(5, false); break;
+    case 7: if (mx) KVSEL_COOP(7, true); else KVSEL_COOP(7, false); break;
+    default: return hipErrorNotSupported;
+  }
+#undef KVSEL_COOP
+  return hipGetLastError();
+}
+
+int coop_grid_capacity(int D, int dtype) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const void* f = D * (dtype == 1 ? 2 : 4) / 16 == 8    ? (const void*)select_coop_kernel<8, 5, true>
+                  : D * (dtype == 1 ? 2 : 4) / 16 == 16 ? (const void*)select_coop_kernel<16, 5, true>
+                                                        : (const void*)select_coop_kernel<32, 5, true>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kCoopThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
+
+hipError_t launch_select_coop(const Launch& a, int rows, int segs, int dtype, const float* votes, float* pooled,
+                              unsigned* coop, unsigned* status, int32_t* indices, const void* K, const void* V,
+                              void* K_out, void* V_out, hipStream_t st) {
+  if (rows <= 0 || segs <= 0) return hipSuccess;
+  const dim3 grid(segs, rows);
+  const uint4* k = (const uint4*)K;
+  const uint4* v = (const uint4*)V;
+  uint4* ko = (uint4*)K_out;
+  uint4* vo = (uint4*)V_out;
+  switch (a.D * (dtype == 1 ? 2 : 4) / 16) {
+    case 8: return launch_select_coop_ru<8>(a, grid, votes, pooled, coop, status, indices, k, v, ko, vo, st);
+    case 16:
+      return launch_select_coop_ru<16>(a, grid, votes, pooled, coop, status, indices, k, v, ko, vo, st);
+    case 32:
+      return launch_select_coop_ru<32>(a, grid, votes, pooled, coop, status, indices, k, v, ko, vo, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 int selection_seg_size(long long max_positions) {
   const long long units = (max_positions + kSegUnit - 1) / kSegUnit;
   const long long per = (units + kMaxSegRow - 1) / kMaxSegRow;
