@@ -87,7 +87,9 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  * with other work and they are not, it scores each head inside a single
  * workgroup instead (two passes over that head's K; same results, slower).
  * KVSEL_OPT_FORCE_FALLBACK (testing): 1 makes every single-read launch take
- *   that fallback; 0 (default) off.
+ *   that fallback, and every cooperative selection launch (whose workgroups
+ *   also wait for each other) its own: the first workgroup of each row then
+ *   runs all of the row's segments; 0 (default) off.
  * Not thread-safe with respect to concurrent calls. */
 enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1 };
 enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };

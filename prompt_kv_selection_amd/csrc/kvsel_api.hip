@@ -346,6 +346,10 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       unsigned* crows = (unsigned*)(ws + p.off_coop) +
                         (long long)kFusedStatusWords * ((p.B + kMaxSegs - 1) / kMaxSegs) +
                         (long long)b0 * p.heads * coop_row_words();
+      if (g_force_fallback) {
+        e = launch_fill_u32(cstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
+        if (e != hipSuccess) return device_error(e, "fill launch");
+      }
       e = timed("select", st, [&] {
         return launch_select_coop(a, rows, coop_segs[b0 / kMaxSegs], p.dtype, votes, pooled_opt, crows, cstatus,
                                   indices, K, V, K_out, V_out, st);

@@ -97,6 +97,9 @@ CASES = [
     ("bf16", 128, 2, 32, 32, 64, 5, "avg"),        # W == L, bypass
     ("bf16", 128, 1, 40, 8, 33, 21, "avg"),        # wide kernel, tiny prompt
     ("bf16", 128, 1, 1025, 32, 600, 63, "avg"),    # widest supported kernel
+    ("bf16", 128, 2, 20000, 32, 1024, 5, "max"),   # five selection segments
+    ("bf16", 128, 2, 12289, 32, 3000, 3, "avg"),   # four segments, the last one position long
+    ("bf16", 128, 1, 9000, 32, 9500, 5, "avg"),    # bypass over several segments
 ]
 
 
@@ -123,7 +126,8 @@ def test_random_cases(B, case, scoring):
     check_gather(out, Kd, Vd, C, L)
 
 
-FALLBACK_CASES = [c for c in CASES if single_read_covers(c[0], c[1], c[4]) and c[3] >= c[5]][:3]
+FALLBACK_CASES = [c for c in CASES if single_read_covers(c[0], c[1], c[4]) and c[3] >= c[5]][:3] + [
+    ("bf16", 128, 2, 20000, 32, 1024, 5, "max")]
 
 
 @pytest.mark.parametrize("case", FALLBACK_CASES, ids=[f"L{c[3]}-W{c[4]}-C{c[5]}" for c in FALLBACK_CASES])
