@@ -34,12 +34,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_alg_bytes(name, w, nch):
-    """Algorithmic bytes one launch of a kernel moves for one layer call."""
+def kernel_alg_bytes(name, w, nch, lse=False):
+    """Algorithmic bytes one launch of a kernel moves for one layer call
+    (lse: the row statistics are handed over, so only the prefix keys, Qwin
+    and the W log-sum-exps per head are read for the votes)."""
     e = 2 if w.dtype == "bf16" else 4
     H, L, W, C, D = w.heads, w.L, w.W, w.C, w.D
     P = L - W
     q = H * W * D * e
+    if lse and name in ("window_fused", "window_votes"):
+        return H * P * D * e + q + H * W * 4 + H * P * 4
     if name == "window_fused":      # K once, Qwin, votes out (partials are noise)
         return H * L * D * e + q + H * P * 4
     if name == "window_stats":      # K once, Qwin, partial (max, sum) per chunk
@@ -156,6 +160,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scoring", choices=("auto", "two_pass", "single_read"), default="auto",
                     help="scoring path (auto: single-read wherever it applies)")
+    ap.add_argument("--lse", action="store_true",
+                    help="row statistics handed over (kvsel_select_lse), as prefill attention would; each "
+                         "layer's log-sum-exps come from one untimed call of the full path")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -202,10 +209,24 @@ def main():
     stream = torch.cuda.current_stream()
     B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[args.scoring])
 
-    def step():
+    lses = []
+    if args.lse:
+        rs = torch.empty((H, W, 2), dtype=torch.float32, device=dev)
         for layer in range(layers):
             B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, H, w.kernel, w.pooling, td,
-                           idx[layer], Ko[layer], Vo[layer], None, None, None, ws, stream=stream)
+                           idx[layer], Ko[layer], Vo[layer], rs, None, None, ws, stream=stream)
+            lses.append((rs[:, :, 0].double() + rs[:, :, 1].double().log()).float().contiguous())
+        torch.cuda.synchronize()
+        log("row log-sum-exps of every layer ready")
+
+    def step():
+        for layer in range(layers):
+            if args.lse:
+                B.kvsel_select_lse(Qs[layer], Ks[layer], Vs[layer], lses[layer], L, W, C, D, H, w.kernel,
+                                   w.pooling, td, idx[layer], Ko[layer], Vo[layer], None, None, ws, stream=stream)
+            else:
+                B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, H, w.kernel, w.pooling, td,
+                               idx[layer], Ko[layer], Vo[layer], None, None, None, ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -246,15 +267,15 @@ def main():
     nch = (L + 1023) // 1024
     kern = {}
     for name, (n, ms) in per_kernel.items():
-        ab = kernel_alg_bytes(name, w, nch)
+        ab = kernel_alg_bytes(name, w, nch, args.lse)
         avg = ms / n
         kern[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
                       "alg_GBps": None if ab is None else round(ab / (avg / 1e3) / 1e9, 1)}
     dom = max((k for k in per_kernel if kernel_alg_bytes(k, w, nch) is not None), key=lambda k: per_kernel[k][1])
     n_dom, ms_dom = per_kernel[dom]
-    ab_dom = kernel_alg_bytes(dom, w, nch)
+    ab_dom = kernel_alg_bytes(dom, w, nch, args.lse)
     achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
-    traffic = traffic_from_profiles(dom)
+    traffic = None if args.lse else traffic_from_profiles(dom)
     path_gbps = path_alg_bytes(w) * layers / (ms_step / 1e3) / 1e9
 
     result = {
@@ -272,7 +293,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": layers, "heads": H, "L": L, "W": W, "C": C, "D": D,
                    "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys,
-                   "scoring": args.scoring},
+                   "scoring": args.scoring, "row_stats": "handed_over" if args.lse else "computed"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "path": {"alg_bytes_per_layer": path_alg_bytes(w), "alg_GBps": round(path_gbps, 1),

@@ -82,7 +82,11 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  *     one round of the co-resident grid; calls whose shape it does not cover
  *     return KVSEL_EUNSUPPORTED.
  * Both give the same indices and K/V rows up to the documented rounding of
- * the scores.  The single-read kernel needs all its workgroups (one per CU)
+ * the scores.  With the row statistics handed over (kvsel_select_lse and
+ * kvsel_select_varlen_lse) there is one pass over K either way:
+ * SINGLE_READ takes the persistent one-workgroup-per-CU kernel (same
+ * coverage, no co-residency needed), TWO_PASS the votes kernel of the
+ * two-pass path (every supported shape), AUTO the former where it applies.  The single-read kernel needs all its workgroups (one per CU)
  * resident at once; it checks that at start, and if the device is shared
  * with other work and they are not, it scores each head inside a single
  * workgroup instead (two passes over that head's K; same results, slower).
@@ -131,6 +135,28 @@ int kvsel_select(const void* Qwin, const void* K, const void* V,
                  float* row_stats_opt, float* votes_opt, float* pooled_opt,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Selection with the window rows' softmax statistics handed over by the
+ * caller.  Prefill attention already forms the full causal softmax of every
+ * prompt query over the whole K [section "prefill still reads the full K/V;
+ * the compressed cache serves decode"]; the normalisers of its last W query
+ * rows are exactly those the votes need [section "votes must come from the
+ * causal softmax over the full prompt"], so the row-statistics pass is
+ * skipped and K is read once.
+ *   row_lse  [heads][W] float32: lse_i = ln sum_{j <= P+i} exp(l[i][j]) of
+ *            window row i over its visible prefix and window positions, l as
+ *            above (the 1/sqrt(D) scale included).  From kvsel_select's
+ *            row_stats_opt: lse_i = m_i + ln Z_i.  Finite, 4-byte aligned.
+ * The votes are s[j] = sum_i exp(l[i][j] - lse_i): they follow the given
+ * statistics (an error d_i in lse_i scales row i's probabilities by
+ * exp(-d_i)).  Every other argument is as for kvsel_select; there is no
+ * row-statistics output.  Workspace: kvsel_workspace_bytes(...). */
+int kvsel_select_lse(const void* Qwin, const void* K, const void* V, const float* row_lse,
+                     int L, int W, int C, int D, int heads,
+                     int kernel, int pooling, int dtype,
+                     int32_t* indices, void* K_out, void* V_out,
+                     float* votes_opt, float* pooled_opt,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for kvsel_select_varlen; 0 on invalid arguments. */
 size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B,
                                     int heads, int W, int D, int dtype);
@@ -155,6 +181,16 @@ int kvsel_select_varlen(const void* Qwin, const void* K, const void* V,
                         int32_t* indices, void* K_out, void* V_out,
                         float* row_stats_opt, float* votes_opt, float* pooled_opt,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Ragged batch with handed-over statistics (see kvsel_select_lse):
+ * row_lse [B][heads][W] float32; every other argument as for
+ * kvsel_select_varlen.  Workspace: kvsel_varlen_workspace_bytes(...). */
+int kvsel_select_varlen_lse(const void* Qwin, const void* K, const void* V, const float* row_lse,
+                            const int32_t* cu_L_host, const int32_t* C_host, int B,
+                            int W, int D, int heads, int kernel, int pooling, int dtype,
+                            int32_t* indices, void* K_out, void* V_out,
+                            float* votes_opt, float* pooled_opt,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Steps of the selection as separate entry points (same definitions as
  * above), for callers that bring their own scores or indices.

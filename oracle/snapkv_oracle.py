@@ -217,6 +217,57 @@ def snapkv_select(qwin, keys, values, W: int, C: int, kernel: int = 3, pooling: 
             "votes": votes, "pooled": pooled, "row_max": m, "row_sum": Z}
 
 
+def row_log_sum_exp(logits: np.ndarray, P: int) -> np.ndarray:
+    """Natural-log log-sum-exp of each window row over its visible positions
+    j <= P + i: lse_i = ln sum_j exp(l[i, j]) = m_i + ln Z_i, the log of the
+    softmax denominator of row i (section "votes must come from the causal
+    softmax over the full prompt").  Prefill attention forms the same causal
+    softmax for every prompt query over the full K (section "prefill still
+    reads the full K/V; the compressed cache serves decode"), so these are the
+    normalisers of its last W rows.  Returns [W] float64."""
+    m, Z = causal_row_stats(logits, P)
+    return m + np.log(Z)
+
+
+def snapkv_select_lse(qwin, keys, values, row_lse, W: int, C: int, kernel: int = 3,
+                      pooling: str = "avg") -> Dict:
+    """Selection with the row normalisers handed over as log-sum-exps.
+
+    Same steps as snapkv_select, except that the causal softmax of window row
+    i is alpha[i, j] = exp(l[i, j] - row_lse[i]) for j <= P + i (0 beyond),
+    with row_lse taken as given instead of computed from K.  With the exact
+    row_log_sum_exp this is snapkv_select; an error d_i in row_lse[i] scales
+    row i's probabilities by exp(-d_i).
+    Returns indices, keys, values, votes and pooled as snapkv_select does.
+    """
+    qwin = np.asarray(qwin, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    row_lse = np.asarray(row_lse, dtype=np.float64)
+    L, D = keys.shape
+    if values.shape != keys.shape or qwin.shape != (W, D) or row_lse.shape != (W,):
+        raise ValueError("shape mismatch between Qwin, K, V and row_lse")
+    validate(L, W, C, D, kernel, pooling)
+    for name, x in (("Qwin", qwin), ("K", keys), ("V", values), ("row_lse", row_lse)):
+        if not np.all(np.isfinite(x)):
+            raise ValueError(f"{name} must be finite")
+    empty = np.zeros(0, dtype=np.float64)
+    if L < C:
+        idx = np.arange(L, dtype=np.int64)
+        return {"indices": idx, "keys": keys.copy(), "values": values.copy(), "votes": empty, "pooled": empty}
+    P = L - W
+    logits = window_logits(qwin, keys)
+    probs = np.zeros((W, L), dtype=np.float64)
+    for i in range(W):
+        t = P + i
+        probs[i, : t + 1] = np.exp(logits[i, : t + 1] - row_lse[i])
+    votes = prefix_votes(probs, P)
+    pooled = pool1d(votes, kernel, pooling)
+    chosen = top_prefix(pooled, C - W)
+    idx = np.concatenate([chosen, np.arange(P, L)]).astype(np.int64)
+    return {"indices": idx, "keys": keys[idx], "values": values[idx], "votes": votes, "pooled": pooled}
+
+
 def snapkv_select_heads(qwin, keys, values, W: int, C: int, kernel: int = 3,
                         pooling: str = "avg", heads: Sequence[int] | None = None) -> List[Dict]:
     """Independent selection per head (section "the prompt cache shrinks, the

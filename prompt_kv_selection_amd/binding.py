@@ -47,6 +47,12 @@ lib.kvsel_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
 lib.kvsel_select_varlen.restype = _i
 lib.kvsel_select_varlen.argtypes = [_vp, _vp, _vp, _i32p, _i32p, _i, _i, _i, _i, _i, _i, _i,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_select_lse.restype = _i
+lib.kvsel_select_lse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_select_varlen_lse.restype = _i
+lib.kvsel_select_varlen_lse.argtypes = [_vp, _vp, _vp, _vp, _i32p, _i32p, _i, _i, _i, _i, _i, _i, _i,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.kvsel_topk_workspace_bytes.restype = _sz
 lib.kvsel_topk_workspace_bytes.argtypes = [_i, _i]
 lib.kvsel_topk.restype = _i
@@ -124,6 +130,25 @@ def kvsel_select_varlen(Qwin, K, V, cu_L, C, W, D, heads, kernel, pooling, dtype
                                    W, D, heads, kernel, POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
                                    _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(row_stats), _ptr(votes),
                                    _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_select_lse(Qwin, K, V, row_lse, L, W, C, D, heads, kernel, pooling, dtype, indices, K_out, V_out,
+                     votes=None, pooled=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_select_lse(_ptr(Qwin), _ptr(K), _ptr(V), _ptr(row_lse), L, W, C, D, heads, kernel,
+                                POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
+                                _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(votes), _ptr(pooled),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_select_varlen_lse(Qwin, K, V, row_lse, cu_L, C, W, D, heads, kernel, pooling, dtype, indices, K_out,
+                            V_out, votes=None, pooled=None, workspace=None, workspace_bytes=None,
+                            stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_select_varlen_lse(_ptr(Qwin), _ptr(K), _ptr(V), _ptr(row_lse), _i32_array(cu_L),
+                                       _i32_array(C), len(C), W, D, heads, kernel, POOL.get(pooling, pooling),
+                                       DTYPE.get(dtype, dtype), _ptr(indices), _ptr(K_out), _ptr(V_out),
+                                       _ptr(votes), _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kvsel_topk_workspace_bytes(rows: int, n: int) -> int:

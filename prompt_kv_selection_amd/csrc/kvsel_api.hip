@@ -213,8 +213,10 @@ void drop_profile_events() {
   g_prof.clear();
 }
 
-int run_select(const void* Q, const void* K, const void* V, const Plan& p, int kernel, int pooling,
-               int32_t* indices, void* K_out, void* V_out, float* row_stats, float* votes_opt,
+// lse: the window rows' natural-log log-sum-exps [sequence][head][W] handed
+// over by the caller, or nullptr (then the scoring kernels find them).
+int run_select(const void* Q, const void* K, const void* V, const float* lse, const Plan& p, int kernel,
+               int pooling, int32_t* indices, void* K_out, void* V_out, float* row_stats, float* votes_opt,
                float* pooled_opt, void* workspace, hipStream_t st) {
   char* ws = (char*)workspace;
   float* pm = (float*)(ws + p.off_pm);
@@ -268,7 +270,7 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
       any_coop = true;
     }
   }
-  if (use_fused || any_coop) {
+  if (use_fused || any_coop || lse != nullptr) {
     // Exchange records, status words, histograms and the cooperative
     // selection's words start at zero (on the two-pass path without the
     // cooperative selection the statistics kernel clears the histograms).
@@ -325,20 +327,24 @@ int run_select(const void* Q, const void* K, const void* V, const Plan& p, int k
     hipError_t e;
     if (items > 0 && use_fused) {
       unsigned* gstatus = status + (long long)kFusedStatusWords * (b0 / kMaxSegs);
-      if (g_force_fallback) {
+      if (g_force_fallback && lse == nullptr) {
         e = launch_fill_u32(gstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
         if (e != hipSuccess) return device_error(e, "fill launch");
       }
       e = timed("window_fused", st,
-                [&] { return launch_fused_scoring(a, Q, K, counters, gstatus, votes, row_stats, st); });
+                [&] { return launch_fused_scoring(a, Q, K, lse, counters, gstatus, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
+    } else if (items > 0 && lse != nullptr) {
+      e = timed("window_votes", st,
+                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, lse, votes, nullptr, st); });
+      if (e != hipSuccess) return device_error(e, "window_votes launch");
     } else if (items > 0) {
       e = timed("window_stats", st, [&] {
         return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, st);
       });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
       e = timed("window_votes", st,
-                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, votes, row_stats, st); });
+                [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, nullptr, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     }
     if (coop_segs[b0 / kMaxSegs] > 0) {
@@ -436,10 +442,11 @@ size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype) {
   return kvsel_varlen_workspace_bytes(cu, c, 1, heads, W, D, dtype);
 }
 
-int kvsel_select_varlen(const void* Qwin, const void* K, const void* V, const int32_t* cu_L_host,
-                        const int32_t* C_host, int B, int W, int D, int heads, int kernel, int pooling, int dtype,
-                        int32_t* indices, void* K_out, void* V_out, float* row_stats_opt, float* votes_opt,
-                        float* pooled_opt, void* workspace, size_t workspace_bytes, void* stream) {
+static int select_entry(const void* Qwin, const void* K, const void* V, const float* lse,
+                        const int32_t* cu_L_host, const int32_t* C_host, int B, int W, int D, int heads, int kernel,
+                        int pooling, int dtype, int32_t* indices, void* K_out, void* V_out, float* row_stats_opt,
+                        float* votes_opt, float* pooled_opt, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   Plan p;
   int rc = make_plan(cu_L_host, C_host, B, heads, W, D, dtype, p);
   if (rc) return rc;
@@ -455,8 +462,37 @@ int kvsel_select_varlen(const void* Qwin, const void* K, const void* V, const in
       (uintptr_t)V_out % 16)
     return fail(KVSEL_EINVAL, "Qwin, K, V, K_out and V_out must be 16-byte aligned");
   (void)esz;
-  return run_select(Qwin, K, V, p, kernel, pooling, indices, K_out, V_out, row_stats_opt, votes_opt, pooled_opt,
-                    workspace, (hipStream_t)stream);
+  return run_select(Qwin, K, V, lse, p, kernel, pooling, indices, K_out, V_out, row_stats_opt, votes_opt,
+                    pooled_opt, workspace, (hipStream_t)stream);
+}
+
+int kvsel_select_varlen(const void* Qwin, const void* K, const void* V, const int32_t* cu_L_host,
+                        const int32_t* C_host, int B, int W, int D, int heads, int kernel, int pooling, int dtype,
+                        int32_t* indices, void* K_out, void* V_out, float* row_stats_opt, float* votes_opt,
+                        float* pooled_opt, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_entry(Qwin, K, V, nullptr, cu_L_host, C_host, B, W, D, heads, kernel, pooling, dtype, indices, K_out,
+                      V_out, row_stats_opt, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
+}
+
+int kvsel_select_varlen_lse(const void* Qwin, const void* K, const void* V, const float* row_lse,
+                            const int32_t* cu_L_host, const int32_t* C_host, int B, int W, int D, int heads,
+                            int kernel, int pooling, int dtype, int32_t* indices, void* K_out, void* V_out,
+                            float* votes_opt, float* pooled_opt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!row_lse) return fail(KVSEL_EINVAL, "row_lse must not be NULL");
+  if ((uintptr_t)row_lse % 4) return fail(KVSEL_EINVAL, "row_lse must be 4-byte aligned");
+  return select_entry(Qwin, K, V, row_lse, cu_L_host, C_host, B, W, D, heads, kernel, pooling, dtype, indices,
+                      K_out, V_out, nullptr, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
+}
+
+int kvsel_select_lse(const void* Qwin, const void* K, const void* V, const float* row_lse, int L, int W, int C,
+                     int D, int heads, int kernel, int pooling, int dtype, int32_t* indices, void* K_out,
+                     void* V_out, float* votes_opt, float* pooled_opt, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  return kvsel_select_varlen_lse(Qwin, K, V, row_lse, cu, c, 1, W, D, heads, kernel, pooling, dtype, indices, K_out,
+                                 V_out, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
 }
 
 int kvsel_select(const void* Qwin, const void* K, const void* V, int L, int W, int C, int D, int heads, int kernel,

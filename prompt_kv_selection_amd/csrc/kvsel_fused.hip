@@ -77,6 +77,7 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
 constexpr int kThreads = (kSW + 3) * 64;  // plus the exchange, memory and publisher waves
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
@@ -289,7 +290,8 @@ __device__ __forceinline__ void issue_wave_tile(const WaveTiles& wt, int t, uint
 // Logits stay unscaled; exponents are fma(l, scale2, -m) with m already
 // scaled.  The wave's (max, sum) per row go to LDS.  Every tile's buffer is
 // refilled with the next round's tile as soon as its operands are read.
-template <int D>
+// With kLse the row statistics are given, and only Q.K^T is formed.
+template <int D, bool kLse>
 __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveTiles& cur, const WaveTiles& nxt,
                                              uint4 (*ring)[TileGeom<D>::PIECES], const uint4* __restrict__ qbuf,
                                              f32x16 (&x)[kTT], int& issued, int& consumed, float* s_maxp,
@@ -322,7 +324,7 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u], kb[u], acc, 0, 0, 0);
-          act = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[u], qa[u], act, 0, 0, 0);
+          if constexpr (!kLse) act = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[u], qa[u], act, 0, 0, 0);
         }
       }
       // Every operand has been read: refill the buffer before the VALU work.
@@ -330,6 +332,7 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
       ++consumed;
       issue_wave_tile<D>(nxt, t, ring, issued);
       x[t] = acc;
+      if constexpr (kLse) continue;
       // act[r]: row n at position p0 + acc_row(r, g).  Only a tile that
       // reaches the window or the end of the prompt needs the mask.
       float tm = kNegBig;
@@ -353,14 +356,16 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
       issue_wave_tile<D>(nxt, t, ring, issued);
     }
   }
-  // Lane n and lane n + 32 merge (half 0, half 1) in that order.
-  const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mrow), __float_as_uint(mrow), false, false);
-  const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zrow), __float_as_uint(zrow), false, false);
-  float m = __uint_as_float(pm[0]), z = __uint_as_float(pz[0]);
-  lse_merge(m, z, __uint_as_float(pm[1]), __uint_as_float(pz[1]));
-  if (g == 0) {
-    s_maxp[wave * 32 + n] = m;
-    s_zp[wave * 32 + n] = z;
+  if constexpr (!kLse) {
+    // Lane n and lane n + 32 merge (half 0, half 1) in that order.
+    const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mrow), __float_as_uint(mrow), false, false);
+    const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zrow), __float_as_uint(zrow), false, false);
+    float m = __uint_as_float(pm[0]), z = __uint_as_float(pz[0]);
+    lse_merge(m, z, __uint_as_float(pm[1]), __uint_as_float(pz[1]));
+    if (g == 0) {
+      s_maxp[wave * 32 + n] = m;
+      s_zp[wave * 32 + n] = z;
+    }
   }
   lds_add(&sy->cnt_b[k & 1]);
 }
@@ -506,6 +511,36 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
     }
     lds_set(&sy->s_ready, (unsigned)k);
     KVSEL_FUSED_CTL_MARK(k, 4);
+  }
+}
+
+// Exchange wave with the row statistics given as natural-log log-sum-exps
+// (lse[sequence][head][W]): exp(l - lse) is the probability itself, so the
+// votes use M = lse * log2(e) and 1/Z = 1.  Each round's values are loaded
+// one step ahead.
+__device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*s_m)[32], float (*s_iz)[32],
+                        Sync* sy) {
+  const int lane = threadIdx.x & 63;
+  const int W = a.W;
+  auto load = [&](int r) -> float {
+    const Work w = round_work(a, r);
+    return (w.on && lane < W) ? lse[(long long)w.hs * W + lane] : 0.f;
+  };
+  unsigned votes_due[2] = {0, 0};  // as in ctl_exchange
+  float next = load(0);
+  for (int k = 1; k < a.rounds + 1; ++k) {
+    const Work w1 = round_work(a, k - 1);
+    if (k >= 3 && round_work(a, k - 3).on) ++votes_due[(k - 3) & 1];
+    const float cur = next;
+    next = load(k);
+    if (w1.on) {
+      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1])) return;
+      if (lane < 32) {  // rows past W: zero queries, dropped by 1/Z = 0
+        s_m[(k - 1) & 1][lane] = lane < W ? cur * kLog2e : 0.f;
+        s_iz[(k - 1) & 1][lane] = lane < W ? 1.f : 0.f;
+      }
+    }
+    lds_set(&sy->s_ready, (unsigned)k);
   }
 }
 
@@ -732,9 +767,10 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
   }
 }
 
-template <int D>
+template <int D, bool kLse>
 __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,
+                                                                  const float* __restrict__ lse,
                                                                   unsigned long long* __restrict__ ex,
                                                                   unsigned* __restrict__ status,
                                                                   float* __restrict__ votes,
@@ -749,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   unsigned arrived = 0u;
-  if (wave == kSW && lane == 0) arrived = arrive(status);
+  if (!kLse && wave == kSW && lane == 0) arrived = arrive(status);
   if (threadIdx.x == 0) sy = Sync{{0, 0}, {0, 0}, 0, 0, 0, 0, 0};
   __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
   // The first K tiles and Qwin of rounds 0 and 1.
@@ -763,14 +799,16 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
   if (wave == kSW) {
-    if (decide(status, arrived) == kFusedGo)
+    if constexpr (kLse)
+      ctl_lse(a, lse, s_m, s_iz, &sy);  // no workgroup waits for another
+    else if (decide(status, arrived) == kFusedGo)
       ctl_exchange<D>(a, ex, status, row_stats, s_m, s_iz, &sy);
     else
       lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
   } else if (wave == kSW + 1) {
     ctl_memory<D>(a, Q, votes, s_q, s_votes, &sy);
   } else if (wave == kSW + 2) {
-    ctl_publish(a, ex, s_maxp, s_zp, &sy);
+    if constexpr (!kLse) ctl_publish(a, ex, s_maxp, s_zp, &sy);
   } else {
     uint4 (*ring)[G::PIECES] = s_ring[wave];
     f32x16 xa[kTT], xb[kTT];
@@ -783,7 +821,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
       KVSEL_FUSED_MARK(k, 0);
       const WaveTiles nxt = wave_tiles<D>(a, K, k + 1, wave);
       if (cur.on) {
-        phase_stream<D>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
+        phase_stream<D, kLse>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
       } else {
         for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(nxt, t, ring, issued);
       }
@@ -805,9 +843,11 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   // Every wave's loads have landed before LDS is reused or the wave ends.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (sy.abort) {  // not all resident: whole heads, one workgroup each
-    solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
-    return;
+  if constexpr (!kLse) {
+    if (sy.abort) {  // not all resident: whole heads, one workgroup each
+      solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
+      return;
+    }
   }
   if (threadIdx.x == 0 && sy.timeout) __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -819,11 +859,11 @@ __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
 
 struct GridCache {
   int device = -1;
-  int grid[2] = {-1, -1};
+  int grid[2][2] = {{-1, -1}, {-1, -1}};
 };
 GridCache g_grid;
 
-template <int D>
+template <int D, bool kLse>
 int grid_for() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -831,10 +871,10 @@ int grid_for() {
     g_grid = GridCache{};
     g_grid.device = dev;
   }
-  int& slot = g_grid.grid[D == 128];
+  int& slot = g_grid.grid[kLse][D == 128];
   if (slot < 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_fused_kernel<D>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_fused_kernel<D, kLse>, kThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
@@ -843,16 +883,16 @@ int grid_for() {
   return slot;
 }
 
-template <int D>
-hipError_t launch_t(const Launch& a, const void* Q, const void* K, unsigned long long* ex, unsigned* status,
-                    float* votes, float* row_stats, hipStream_t st) {
-  const int grid = grid_for<D>();
+template <int D, bool kLse>
+hipError_t launch_t(const Launch& a, const void* Q, const void* K, const float* lse, unsigned long long* ex,
+                    unsigned* status, float* votes, float* row_stats, hipStream_t st) {
+  const int grid = grid_for<D, kLse>();
   if (grid <= 0) return hipErrorNotSupported;
   Launch la = a;
   const __bf16* q = (const __bf16*)Q;
   const __bf16* k = (const __bf16*)K;
-  hipLaunchKernelGGL((window_fused_kernel<D>), dim3(grid), dim3(kThreads), 0, st, la, q, k, ex, status, votes,
-                     row_stats);
+  hipLaunchKernelGGL((window_fused_kernel<D, kLse>), dim3(grid), dim3(kThreads), 0, st, la, q, k, lse, ex, status,
+                     votes, row_stats);
   return hipGetLastError();
 }
 
@@ -865,19 +905,25 @@ int fused_positions(int W, int D) {
 
 int fused_grid(int W, int D) {
   if (W > 32) return 0;
-  if (D == 128) return grid_for<128>();
-  if (D == 64) return grid_for<64>();
+  // The variant with given row statistics has the same resources.
+  if (D == 128) return grid_for<128, false>();
+  if (D == 64) return grid_for<64, false>();
   return 0;
 }
 
 int fused_exchange_bytes() { return kSlotWords * 8; }
 
-hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* ex, unsigned* status,
-                                float* votes, float* row_stats, hipStream_t st) {
+hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* ex,
+                                unsigned* status, float* votes, float* row_stats, hipStream_t st) {
   if (a.W > 32 || a.S != kS) return hipErrorNotSupported;
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(ex);
-  if (a.D == 128) return launch_t<128>(a, Q, K, slots, status, votes, row_stats, st);
-  if (a.D == 64) return launch_t<64>(a, Q, K, slots, status, votes, row_stats, st);
+  if (lse != nullptr) {
+    if (a.D == 128) return launch_t<128, true>(a, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 64) return launch_t<64, true>(a, Q, K, lse, slots, status, votes, nullptr, st);
+    return hipErrorNotSupported;
+  }
+  if (a.D == 128) return launch_t<128, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 64) return launch_t<64, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
   return hipErrorNotSupported;
 }
 

@@ -78,8 +78,11 @@ enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
                                float* part_m, float* part_z, uint32_t* zero, long long zero_words,
                                hipStream_t st);
+// With lse != nullptr ([sequence][head][W] natural-log row log-sum-exps,
+// one per window row) the partials are not read and no row statistics are
+// written.
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               const float* part_m, const float* part_z, float* votes,
+                               const float* part_m, const float* part_z, const float* lse, float* votes,
                                float* row_stats, hipStream_t st);
 // Pooling (pooled may be nullptr: histogram of the input only) with the
 // first-digit histogram of each row added into hist[row][2048] (nullptr: none).
@@ -198,7 +201,9 @@ int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
 // Exchange slots per head for fc chunks: fc rounded up to whole read passes
 // of the exchange wave (the padding is never written and never merged).
 __host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64 * 64; }
-hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, unsigned* exchange,
+// With lse != nullptr (as for launch_window_votes) the workgroups exchange
+// nothing and need not be co-resident: exchange and status are not used.
+hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* exchange,
                                 unsigned* status, float* votes, float* row_stats, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);

@@ -39,6 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;   // finite "no position seen yet" max
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
 
 // Window row held in accumulator register r by lane half g (32x32 MFMA
 // output layout: lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4).
@@ -488,8 +489,8 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
 template <typename T, int D, int RB>
 __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
     const Launch a, int items, const T* __restrict__ Q, const T* __restrict__ K,
-    const float* __restrict__ part_m, const float* __restrict__ part_z, float* __restrict__ votes,
-    float* __restrict__ row_stats) {
+    const float* __restrict__ part_m, const float* __restrict__ part_z, const float* __restrict__ lse,
+    float* __restrict__ votes, float* __restrict__ row_stats) {
   using G = TileGeom<T, D>;
   __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
@@ -517,9 +518,21 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
       stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
       qe = it.e;
       qh = it.h;
-      // The run holding chunk 0 of the head starts there: its workgroup
-      // alone writes the row statistics.
-      merge_partials<RB * 32>(a, s, it.h, part_m, part_z, row_stats, it.c == 0, s_gm, s_gz, s_m, s_iz);
+      if (lse != nullptr) {
+        // Row log-sum-exps handed over by the caller: exp(l - lse) is the
+        // probability itself, so M = lse * log2(e) and 1/Z = 1.
+        if ((int)threadIdx.x < RB * 32) {
+          const int i = threadIdx.x;
+          const bool row = i < W;
+          s_m[i] = row ? lse[((long long)s.b * a.heads + it.h) * W + i] * kLog2e : 0.f;
+          s_iz[i] = row ? 1.f : 0.f;
+        }
+        __syncthreads();
+      } else {
+        // The run holding chunk 0 of the head starts there: its workgroup
+        // alone writes the row statistics.
+        merge_partials<RB * 32>(a, s, it.h, part_m, part_z, row_stats, it.c == 0, s_gm, s_gz, s_m, s_iz);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -585,10 +598,10 @@ static hipError_t stats_t(const Launch& a, int items, const void* Q, const void*
 
 template <typename T, int D, int RB>
 static hipError_t votes_t(const Launch& a, int items, const void* Q, const void* K, const float* pm,
-                          const float* pz, float* votes, float* rs, hipStream_t st) {
+                          const float* pz, const float* lse, float* votes, float* rs, hipStream_t st) {
   const int grid = resident_grid(window_votes_kernel<T, D, RB>, items);
   hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, votes, rs);
+                     (const T*)Q, (const T*)K, pm, pz, lse, votes, rs);
   return hipGetLastError();
 }
 
@@ -626,9 +639,9 @@ hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void
 }
 
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               const float* part_m, const float* part_z, float* votes,
+                               const float* part_m, const float* part_z, const float* lse, float* votes,
                                float* row_stats, hipStream_t st) {
-  KVSEL_DISPATCH(votes_t, a, items, Q, K, part_m, part_z, votes, row_stats, st);
+  KVSEL_DISPATCH(votes_t, a, items, Q, K, part_m, part_z, lse, votes, row_stats, st);
 }
 
 }  // namespace kvsel

@@ -100,6 +100,44 @@ def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = 
         B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 0)
 
 
+def run_select_lse(Qd, Kd, Vd, lse_d, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto"):
+    """Run kvsel_select_lse (row statistics handed over as lse_d [H, W]
+    float32 on the device) with votes and pooled outputs; host numpy arrays."""
+    from prompt_kv_selection_amd import binding as B
+    H, _, D = Kd.shape
+    td = torch_dtype(dtype)
+    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[scoring])
+    try:
+        ws = torch.empty(B.kvsel_workspace_bytes(H, L, W, C, D, td), dtype=torch.uint8, device="cuda")
+        idx = torch.full((H, C), -7, dtype=torch.int32, device="cuda")
+        Ko = torch.zeros((H, C, D), dtype=td, device="cuda")
+        Vo = torch.zeros((H, C, D), dtype=td, device="cuda")
+        vt = torch.full((H, L - W), float("nan"), dtype=torch.float32, device="cuda")
+        pl = torch.full((H, L - W), float("nan"), dtype=torch.float32, device="cuda")
+        B.kvsel_select_lse(Qd, Kd, Vd, lse_d, L, W, C, D, H, kernel, pooling, td, idx, Ko, Vo, vt, pl, ws)
+        torch.cuda.synchronize()
+    finally:
+        B.kvsel_set_option(B.KVSEL_OPT_SCORING, 0)
+    return dict(idx=idx, Ko=Ko, Vo=Vo, votes=vt.cpu().numpy(), pooled=pl.cpu().numpy())
+
+
+def check_head_lse(out, h, ref, L, W, C, what):
+    """Compare head h of a kvsel_select_lse result with the oracle's
+    snapkv_select_lse result on the same (float32) statistics."""
+    n_out = min(L, C)
+    idx = out["idx"][h, :n_out].cpu().numpy()
+    if L < C:
+        np.testing.assert_array_equal(idx, np.arange(L), err_msg=what)
+        return
+    P = L - W
+    close(out["votes"][h], ref["votes"], f"{what} votes")
+    close(out["pooled"][h], ref["pooled"], f"{what} pooled")
+    n = C - W
+    band_check(idx[:n], ref["pooled"], n, what)
+    gpu_internal_topk(idx[:n], out["pooled"][h], n, what)
+    np.testing.assert_array_equal(idx[n:], np.arange(P, L), err_msg=f"{what} window")
+
+
 def single_read_covers(dtype, D, W):
     return dtype == "bf16" and D in (64, 128) and W <= 32
 

@@ -88,6 +88,25 @@ def test_select_argument_errors(B, kw, code):
     assert B.kvsel_last_error() != ""
 
 
+def test_lse_argument_errors(B):
+    lib = B.lib
+    args = [FAKE, FAKE, FAKE]
+    tail = [1024, 32, 256, 128, 4, 5, 0, 1, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None]
+    assert lib.kvsel_select_lse(*args, None, *tail) == -1 and "row_lse" in B.kvsel_last_error()
+    assert lib.kvsel_select_lse(*args, ctypes.c_void_p(0x10002), *tail) == -1
+    bad = list(tail)
+    bad[2] = 32  # C == W
+    assert lib.kvsel_select_lse(*args, FAKE, *bad) == -1
+    bad = list(tail)
+    bad[-2] = 1024  # workspace too small
+    assert lib.kvsel_select_lse(*args, FAKE, *bad) == -3
+    cu = (ctypes.c_int32 * 3)(0, 5000, 4000)
+    cs = (ctypes.c_int32 * 2)(500, 400)
+    rc = lib.kvsel_select_varlen_lse(FAKE, FAKE, FAKE, FAKE, cu, cs, 2, 32, 128, 8, 5, 0, 1, FAKE, FAKE, FAKE,
+                                     None, None, FAKE, 1 << 30, None)
+    assert rc == -1 and "sequence 1" in B.kvsel_last_error()
+
+
 def test_varlen_argument_errors(B):
     lib = B.lib
     cu_bad = (ctypes.c_int32 * 3)(0, 5000, 4000)  # negative length

@@ -194,6 +194,78 @@ def test_counterexample_avg3_is_an_exact_tie():
     assert r["indices"].tolist() == [0, 2, 3]
 
 
+# ------------------------------------------------------------- handed-over row statistics
+
+def test_worked_example_row_lse_and_votes():
+    """The page's row sums 25 and 26 (in exp-weight units) are the row
+    log-sum-exps ln 25 and ln 26; with them handed over, the votes are the
+    page's, and so is the selection."""
+    g, rows, Q, K, V = worked()
+    P = g["L"] - g["W"]
+    lse = O.row_log_sum_exp(O.window_logits(Q, K), P)
+    np.testing.assert_allclose(lse, [math.log(25), math.log(26)], rtol=1e-14)
+    r = O.snapkv_select_lse(Q, K, V, [math.log(25), math.log(26)], g["W"], g["C"], 3, "avg")
+    np.testing.assert_allclose(r["votes"], [n / 650 for n in (51, 77, 460, 508, 51, 51)], rtol=1e-14)
+    np.testing.assert_allclose(r["pooled"], [n / 1950 for n in (128, 588, 1045, 1019, 610, 102)], rtol=1e-14)
+    assert r["indices"].tolist() == g["expected_indices"]
+    assert r["values"].tolist() == g["expected_values"]
+
+
+def test_counterexample_handed_over_normaliser():
+    """The counterexample through handed-over statistics: the full-prompt
+    normalisers (ln 100, ln 40 from the exp-weight rows) pick B with the
+    printed votes; the page's wrong prefix-only normalisers (ln 10, ln 36)
+    reproduce its wrong votes 1.15 / 0.85 and pick A."""
+    g, rows, Q, K, V = counter()
+    full, prefix = g["printed"]["full_softmax"], g["printed"]["prefix_only"]
+    lse = O.row_log_sum_exp(O.window_logits(Q, K), 2)
+    np.testing.assert_allclose(lse, [math.log(100), math.log(40)], rtol=1e-14)
+    r = O.snapkv_select_lse(Q, K, V, lse, 2, 3, 1, "avg")
+    np.testing.assert_allclose(r["votes"], [full["A_vote"], full["B_vote"]], rtol=1e-12)
+    assert r["indices"].tolist() == [g["positions"][full["pick"]], 2, 3]
+    r = O.snapkv_select_lse(Q, K, V, [math.log(10), math.log(36)], 2, 3, 1, "avg")
+    np.testing.assert_allclose(r["votes"], [sum(prefix["A_terms"]), sum(prefix["B_terms"])], rtol=1e-12)
+    assert r["indices"].tolist() == [g["positions"]["A"], 2, 3]
+
+
+@pytest.mark.parametrize("L,W,D", [(17, 5, 4), (130, 32, 16)])
+def test_row_lse_crosscheck_torch(L, W, D):
+    """row_log_sum_exp equals PyTorch's float64 logsumexp over the causally
+    masked logits, and the votes from it equal the column sums of PyTorch's
+    full causal attention."""
+    rng = np.random.default_rng(L * 7 + W)
+    Qfull = rng.standard_normal((L, D)) * 2
+    K = rng.standard_normal((L, D)) * 2
+    V = rng.standard_normal((L, D))
+    P = L - W
+    q, k = torch.from_numpy(Qfull), torch.from_numpy(K)
+    logits = ((q @ k.T) / math.sqrt(D)).masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    ref_lse = torch.logsumexp(logits[P:], dim=-1).numpy()
+    np.testing.assert_allclose(O.row_log_sum_exp(O.window_logits(Qfull[P:], K), P), ref_lse, rtol=1e-13)
+    ref_votes = torch.softmax(logits, dim=-1)[P:, :P].sum(dim=0).numpy()
+    r = O.snapkv_select_lse(Qfull[P:], K, V, ref_lse, W, W + 3, 1, "avg")
+    np.testing.assert_allclose(r["votes"], ref_votes, rtol=1e-12)
+    full = O.snapkv_select(Qfull[P:], K, V, W, W + 3, 1, "avg")
+    assert r["indices"].tolist() == full["indices"].tolist()
+
+
+def test_row_lse_shift_scales_rows():
+    """An offset d added to row i's log-sum-exp scales that row's
+    probabilities by exp(-d): the same offset on every row scales every vote,
+    and the ranking does not change."""
+    rng = np.random.default_rng(5)
+    L, W, D = 40, 4, 8
+    Q, K, V = rng.standard_normal((W, D)), rng.standard_normal((L, D)), rng.standard_normal((L, D))
+    lse = O.row_log_sum_exp(O.window_logits(Q, K), L - W)
+    base = O.snapkv_select_lse(Q, K, V, lse, W, 12, 3, "max")
+    half = O.snapkv_select_lse(Q, K, V, lse + math.log(2), W, 12, 3, "max")
+    np.testing.assert_allclose(half["votes"], base["votes"] / 2, rtol=1e-13)
+    assert half["indices"].tolist() == base["indices"].tolist()
+    one = O.snapkv_select_lse(Q, K, V, lse + np.array([0, 0, math.log(3), 0]), W, 12, 3, "max")
+    probs = O.attention_probs(O.window_logits(Q, K), L - W, *O.causal_row_stats(O.window_logits(Q, K), L - W))
+    np.testing.assert_allclose(one["votes"], base["votes"] - probs[2, : L - W] * (2 / 3), rtol=1e-12)
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("L,W", [(10, 3), (64, 8), (257, 32)])
