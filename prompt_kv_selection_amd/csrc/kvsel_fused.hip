@@ -16,10 +16,12 @@
 // Schedule.  One workgroup per CU, all resident together (checked at start).
 // Work proceeds in rounds; in a round every workgroup owns one chunk of
 // S = 512 positions of some head (heads_per_round heads, each split over
-// fc = ceil(L / S) workgroups).  Two register sets form a pipeline: in step k
-// the workgroup streams round k and normalises it against the chunk's own row
-// maxima, then votes round k - 1, whose head-wide statistics were exchanged
-// while round k streamed.
+// fc = ceil(L / S) workgroups).  A round's logits wait two rounds for the
+// head-wide statistics: in step k the workgroup streams round k into one of
+// two register sets (and reduces it to the chunk's own row statistics), votes
+// round k - 2 from a third set kept in LDS, then moves round k - 1 from the
+// other register set into LDS.  The exchange of round k - 2 overlapped the
+// streaming of rounds k - 1 and k.
 //
 // Exchange.  A vote is sum_i exp2(x_ij - M_i) / Z_i.  With the chunk's own
 // maxima m_i the streamed exponentials are u_ij = exp2(x_ij - m_i) and
@@ -27,8 +29,8 @@
 // M_i = max over chunks of m_i and Z_i = sum over chunks of
 // z_i * exp2(m_i - M_i).  So one exchange per round suffices: every workgroup
 // stores (m_i, z_i) of its chunk as one 64-bit word per row into its own slot
-// (no atomics), and one round later reads the fc slots of the head and merges
-// them in a fixed order (the result does not depend on arrival order).  The
+// (no atomics), and while the next rounds stream reads the fc slots of the
+// head and merges them in a fixed order (the result does not depend on arrival order).  The
 // lowest mantissa bit of every published m_i is set, and the same tagged m_i
 // is used for the chunk's exponentials, so a set bit marks a written word in a
 // slot array that starts zeroed.
@@ -37,8 +39,11 @@
 // memory wave and a publisher wave.
 //  * Streaming waves read global memory only through direct-to-LDS loads of
 //    K tiles (global_load_lds_dwordx4, 1 KB contiguous per instruction) into a
-//    private ring of 32-row tiles, issued ahead and waited for with explicit
-//    vmcnt counts, so the HBM stream never drains while they compute.  They
+//    private 32-row tile buffer, one tile in flight per wave: the next tile is
+//    issued as soon as the current one's operands are in registers.  Eight
+//    tiles (64 KB) in flight per CU keep HBM busy; deeper queues would only
+//    lengthen the wait of every other memory access of the CU, the exchange's
+//    included.  They
 //    form the logits on MFMA (v_mfma_f32_32x32x16_bf16, Qwin rows from LDS),
 //    exponentials and votes, and talk to the other two waves through LDS.
 //  * The exchange wave only reads the head's slots and merges them, so a
@@ -81,8 +86,15 @@ constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
 constexpr int kThreads = (kSW + 3) * 64;  // plus the exchange, memory and publisher waves
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
-constexpr int kNBuf = 2;                  // K tiles in flight per streaming wave
+constexpr int kNBuf = 1;                  // K tiles in flight per streaming wave
 constexpr int kS = kSW * kTT * 32;        // positions per workgroup per round
+constexpr int kLag = 2;                   // steps between streaming a round and voting it
+// Round-indexed LDS buffers and arrival counters.  Streaming waves of a
+// workgroup are at most kLag + 1 rounds apart (a wave in step k has the
+// statistics of round k - kLag - 1, which needed every wave's round
+// k - kLag - 1), so kNR > kLag + 1 rounds never share an entry while in use.
+constexpr int kNR = 4;
+static_assert(kNR > kLag + 1, "round-indexed entries outlive the skew of the waves");
 constexpr long kSpin = 1L << 22;          // bound of every wait loop
 
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
@@ -161,10 +173,9 @@ __device__ __forceinline__ unsigned long long pack_slot(float m, float z) {
 // a wave that has seen the signal.
 struct Sync {
   // Streaming-wave arrivals (row statistics, votes), counted per round
-  // parity: a streaming wave can finish round k + 1 before another finishes
-  // round k (never round k + 2, which waits for round k's exchange), so a
-  // single running count could reach a round's target early.
-  unsigned cnt_b[2], cnt_c[2];
+  // modulo kNR: a streaming wave can run up to kLag + 1 rounds ahead of
+  // another, so a single running count could reach a round's target early.
+  unsigned cnt_b[kNR], cnt_c[kNR];
   unsigned q_ready;                // Qwin of rounds < q_ready is in LDS
   unsigned s_ready;                // vote scales of rounds < s_ready are in LDS
   unsigned v_done;                 // votes of rounds < v_done have left LDS
@@ -249,10 +260,11 @@ __device__ __forceinline__ void wait_tiles(int tiles_after) {
 }
 
 // The K tiles one streaming wave owns in a round: kTT consecutive 32-row
-// tiles of one head from row p0 (rows past L repeat row L - 1).  Tile t of
-// a round always uses ring buffer t, and tiles are consumed in the order
-// they were issued, so the wave's outstanding loads are counted, not named.
-static_assert(kNBuf == kTT, "one ring buffer per tile of a round");
+// tiles of one head from row p0 (rows past L repeat row L - 1).  A wave's
+// tiles form one sequence (its existing tiles of round k, then of round
+// k + 1, ...) through its single buffer: at most one tile is outstanding, and
+// at the start of step k it is the wave's first tile of round k, if any.
+static_assert(kNBuf == 1, "one tile in flight per streaming wave");
 struct WaveTiles {
   const __bf16* kh;  // the head's K
   int L, p0;
@@ -273,10 +285,9 @@ __device__ __forceinline__ WaveTiles wave_tiles(const Launch& a, const __bf16* _
 }
 
 template <int D>
-__device__ __forceinline__ void issue_wave_tile(const WaveTiles& wt, int t, uint4 (*ring)[TileGeom<D>::PIECES],
-                                                int& issued) {
+__device__ __forceinline__ void issue_wave_tile(const WaveTiles& wt, int t, uint4* buf, int& issued) {
   if (wt.on && wt.p0 + 32 * t < wt.L) {
-    issue_tile<D>(wt.kh, wt.L, wt.p0 + 32 * t, ring[t], threadIdx.x & 63);
+    issue_tile<D>(wt.kh, wt.L, wt.p0 + 32 * t, buf, threadIdx.x & 63);
     ++issued;
   }
 }
@@ -288,12 +299,12 @@ __device__ __forceinline__ void issue_wave_tile(const WaveTiles& wt, int t, uint
 // maximum and the sum of exp2 over the lane's positions, then one merge of
 // the two half-waves, which hold the same rows over different positions.
 // Logits stay unscaled; exponents are fma(l, scale2, -m) with m already
-// scaled.  The wave's (max, sum) per row go to LDS.  Every tile's buffer is
-// refilled with the next round's tile as soon as its operands are read.
+// scaled.  The wave's (max, sum) per row go to LDS.  The buffer is refilled
+// with the wave's next tile as soon as the operands are read.
 // With kLse the row statistics are given, and only Q.K^T is formed.
 template <int D, bool kLse>
 __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveTiles& cur, const WaveTiles& nxt,
-                                             uint4 (*ring)[TileGeom<D>::PIECES], const uint4* __restrict__ qbuf,
+                                             uint4* buf, const uint4* __restrict__ qbuf,
                                              f32x16 (&x)[kTT], int& issued, int& consumed, float* s_maxp,
                                              float* s_zp, Sync* sy) {
   using G = TileGeom<D>;
@@ -307,7 +318,7 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
     const int p0 = cur.p0 + 32 * t;
     if (p0 < L) {
       wait_tiles<D>(issued - consumed - 1);
-      const uint4* tile = ring[t];
+      const uint4* tile = buf;
       // Operands in groups of four k-steps: their LDS reads are issued
       // together, and the registers of a group are free for the next.
       constexpr int kGroup = 4;
@@ -327,10 +338,14 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
           if constexpr (!kLse) act = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[u], qa[u], act, 0, 0, 0);
         }
       }
-      // Every operand has been read: refill the buffer before the VALU work.
+      // Every operand has been read: refill the buffer before the VALU work,
+      // with tile t + 1 of this round or else the first of the next.
       lds_fence();
       ++consumed;
-      issue_wave_tile<D>(nxt, t, ring, issued);
+      if (t + 1 < kTT && p0 + 32 < L)
+        issue_wave_tile<D>(cur, t + 1, buf, issued);
+      else
+        issue_wave_tile<D>(nxt, 0, buf, issued);
       x[t] = acc;
       if constexpr (kLse) continue;
       // act[r]: row n at position p0 + acc_row(r, g).  Only a tile that
@@ -352,8 +367,8 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
 #pragma unroll
       for (int r = 0; r < 16; ++r) tz += exp2_fast(fmaf(act[r], sc, -tms));
       lse_merge(mrow, zrow, tms, tz);
-    } else {
-      issue_wave_tile<D>(nxt, t, ring, issued);
+    } else if (t == 0) {  // no tile of this round: the next round's first
+      issue_wave_tile<D>(nxt, 0, buf, issued);
     }
   }
   if constexpr (!kLse) {
@@ -367,35 +382,55 @@ __device__ __forceinline__ void phase_stream(const Launch& a, int k, const WaveT
       s_zp[wave * 32 + n] = z;
     }
   }
-  lds_add(&sy->cnt_b[k & 1]);
+  lds_add(&sy->cnt_b[k % kNR]);
 }
 
-// Phase B (streaming wave): votes of the wave's positions into LDS from the
-// head-wide scaled row maxima M and inverse normalisers.  Prefix positions
-// are visible to every window row, so no mask is needed; rows past W have
-// zero logits and zero 1/Z.  Equal key rows give bit-equal votes.
-__device__ __forceinline__ void phase_votes(const Launch& a, int k, const f32x16 (&x)[kTT], const float* s_m,
-                                            const float* s_iz, float* s_votes, Sync* sy) {
+// The wave's logits of a round kept in LDS between its two steps:
+// element 4q + e of tile t of lane l is component e of float4 (t * 4 + q) * 64
+// + l (each instruction moves 1 KB contiguous, free of bank conflicts).
+__device__ __forceinline__ void store_x(float4* sx, const f32x16 (&x)[kTT]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < kTT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      sx[(t * 4 + q) * 64 + lane] = make_float4(x[t][4 * q], x[t][4 * q + 1], x[t][4 * q + 2], x[t][4 * q + 3]);
+}
+
+// Phase B (streaming wave): votes of round k's positions into LDS from the
+// logits kept in LDS and the head-wide row log-normalisers in base 2
+// (M_i + log2 Z_i, so that exp2(x - M_i - log2 Z_i) is the probability).
+// Prefix positions are visible to every window row, so no mask is needed;
+// rows past W have zero logits and an infinite log-normaliser.  Equal key
+// rows give bit-equal votes.
+__device__ __forceinline__ void phase_votes(const Launch& a, int k, const float4* sx, const float* s_m,
+                                            float* s_votes, Sync* sy) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = lane & 31, g = lane >> 5;
   const float sc = a.scale2;
   if (!lds_wait_ge(sy, &sy->s_ready, (unsigned)k + 1)) return;
   if (!lds_wait_ge(sy, &sy->v_done, (unsigned)(k >= 1 ? k - 1 : 0))) return;  // round k - 2 left this buffer
-  float mr[16], iz[16];
+  float mr[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    mr[r] = s_m[acc_row(r, g)];
-    iz[r] = s_iz[acc_row(r, g)];
-  }
+  for (int r = 0; r < 16; ++r) mr[r] = s_m[acc_row(r, g)];
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
+    float xt[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = sx[(t * 4 + q) * 64 + lane];
+      xt[4 * q] = v.x;
+      xt[4 * q + 1] = v.y;
+      xt[4 * q + 2] = v.z;
+      xt[4 * q + 3] = v.w;
+    }
     float tot = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tot = fmaf(exp2_fast(fmaf(x[t][r], sc, -mr[r])), iz[r], tot);
+    for (int r = 0; r < 16; ++r) tot += exp2_fast(fmaf(xt[r], sc, -mr[r]));
     const auto pt = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
     const float v = __uint_as_float(pt[0]) + __uint_as_float(pt[1]);
     if (g == 0) s_votes[wave * kTT * 32 + t * 32 + n] = v;
   }
-  lds_add(&sy->cnt_c[k & 1]);
+  lds_add(&sy->cnt_c[k % kNR]);
 }
 
 // Controller: start loading Qwin of round k into an LDS buffer with
@@ -479,68 +514,62 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
   return __ballot(!ok) == 0;
 }
 
-// Exchange wave.  Step k: head statistics of round k - 1 from the slots
-// (overlapping the streaming of round k) into the statistics buffer of round
-// k - 1, once the votes of round k - 3, which read the same buffer, are done.
+// Exchange wave: the head statistics of each round in turn from the slots
+// (overlapping the streaming of the next rounds) into the round's statistics
+// buffer, once the votes of round j - kNR, which read the same buffer, are
+// done.  s_ready = j + 1 announces round j.
 template <int D>
 __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ ex, unsigned* __restrict__ status,
-                             float* __restrict__ row_stats, float (*s_m)[32], float (*s_iz)[32], Sync* sy) {
+                             float* __restrict__ row_stats, float (*s_m)[32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
-  unsigned votes_due[2] = {0, 0};  // owned rounds up to k - 3, per parity: their votes must be done
-  for (int k = 1; k < a.rounds + 1; ++k) {
-    const Work w1 = round_work(a, k - 1);
-    if (k >= 3 && round_work(a, k - 3).on) ++votes_due[(k - 3) & 1];
-    if (w1.on) {
+  unsigned votes_due[kNR] = {};  // owned rounds up to j - kNR, per residue: their votes must be done
+  for (int j = 0; j < a.rounds; ++j) {
+    const Work w = round_work(a, j);
+    if (j >= kNR && round_work(a, j - kNR).on) ++votes_due[j % kNR];
+    if (w.on) {
       float M, Z;
-      const bool ok = ctl_head_stats(a, w1, ex, M, Z);
+      const bool ok = ctl_head_stats(a, w, ex, M, Z);
       if (!ok && lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1])) return;
+      if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
       if (lane < W) {
-        s_m[(k - 1) & 1][lane] = ok ? M : __builtin_nanf("");
-        s_iz[(k - 1) & 1][lane] = ok ? 1.f / Z : __builtin_nanf("");
-        if (row_stats != nullptr && w1.c == 0) {
-          float* rs = row_stats + ((long long)w1.hs * W + lane) * 2;
+        s_m[j % kNR][lane] = ok ? M + __log2f(Z) : __builtin_nanf("");
+        if (row_stats != nullptr && w.c == 0) {
+          float* rs = row_stats + ((long long)w.hs * W + lane) * 2;
           rs[0] = M * kLn2;
           rs[1] = Z;
         }
-      } else if (lane < 32) {  // rows past W: zero queries, dropped by 1/Z = 0
-        s_m[(k - 1) & 1][lane] = 0.f;
-        s_iz[(k - 1) & 1][lane] = 0.f;
+      } else if (lane < 32) {  // rows past W: zero queries, dropped by the infinite normaliser
+        s_m[j % kNR][lane] = INFINITY;
       }
     }
-    lds_set(&sy->s_ready, (unsigned)k);
-    KVSEL_FUSED_CTL_MARK(k, 4);
+    lds_set(&sy->s_ready, (unsigned)(j + 1));
+    KVSEL_FUSED_CTL_MARK(j, 4);
   }
 }
 
 // Exchange wave with the row statistics given as natural-log log-sum-exps
-// (lse[sequence][head][W]): exp(l - lse) is the probability itself, so the
-// votes use M = lse * log2(e) and 1/Z = 1.  Each round's values are loaded
-// one step ahead.
-__device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*s_m)[32], float (*s_iz)[32],
-                        Sync* sy) {
+// (lse[sequence][head][W]): the base-2 log-normaliser is lse * log2(e).
+// Each round's values are loaded one round ahead.
+__device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*s_m)[32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   auto load = [&](int r) -> float {
     const Work w = round_work(a, r);
     return (w.on && lane < W) ? lse[(long long)w.hs * W + lane] : 0.f;
   };
-  unsigned votes_due[2] = {0, 0};  // as in ctl_exchange
+  unsigned votes_due[kNR] = {};  // as in ctl_exchange
   float next = load(0);
-  for (int k = 1; k < a.rounds + 1; ++k) {
-    const Work w1 = round_work(a, k - 1);
-    if (k >= 3 && round_work(a, k - 3).on) ++votes_due[(k - 3) & 1];
+  for (int j = 0; j < a.rounds; ++j) {
+    const Work w = round_work(a, j);
+    if (j >= kNR && round_work(a, j - kNR).on) ++votes_due[j % kNR];
     const float cur = next;
-    next = load(k);
-    if (w1.on) {
-      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * votes_due[(k - 1) & 1])) return;
-      if (lane < 32) {  // rows past W: zero queries, dropped by 1/Z = 0
-        s_m[(k - 1) & 1][lane] = lane < W ? cur * kLog2e : 0.f;
-        s_iz[(k - 1) & 1][lane] = lane < W ? 1.f : 0.f;
-      }
+    next = load(j + 1);
+    if (w.on) {
+      if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
+      if (lane < 32) s_m[j % kNR][lane] = lane < W ? cur * kLog2e : INFINITY;  // rows past W drop out
     }
-    lds_set(&sy->s_ready, (unsigned)k);
+    lds_set(&sy->s_ready, (unsigned)(j + 1));
   }
 }
 
@@ -552,26 +581,26 @@ __device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex
                             float (*s_zp)[kSW * 32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
-  unsigned on_b[2] = {0, 0};  // owned rounds awaited so far, per parity
+  unsigned on_b[kNR] = {};  // owned rounds awaited so far, per residue
   for (int k = 0; k < a.rounds; ++k) {
     const Work w0 = round_work(a, k);
     if (!w0.on) continue;
-    ++on_b[k & 1];
-    if (!lds_wait_ge(sy, &sy->cnt_b[k & 1], kSW * on_b[k & 1])) return;
+    ++on_b[k % kNR];
+    if (!lds_wait_ge(sy, &sy->cnt_b[k % kNR], kSW * on_b[k % kNR])) return;
     if (lane < W) {
       // Merge the waves' (max, sum) pairs in wave order against the tagged
       // chunk maximum.
-      float m = s_maxp[k & 1][lane];
+      float m = s_maxp[k % kNR][lane];
 #pragma unroll
-      for (int v = 1; v < kSW; ++v) m = fmaxf(m, s_maxp[k & 1][v * 32 + lane]);
+      for (int v = 1; v < kSW; ++v) m = fmaxf(m, s_maxp[k % kNR][v * 32 + lane]);
       m = tag_max(m);
       // A wave with no visible position in the row has sum 0 and the
       // sentinel maximum, whose ulp is huge: it adds nothing.
       float zz = 0.f;
 #pragma unroll
       for (int v = 0; v < kSW; ++v) {
-        const float zv = s_zp[k & 1][v * 32 + lane];
-        if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k & 1][v * 32 + lane] - m);
+        const float zv = s_zp[k % kNR][v * 32 + lane];
+        if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k % kNR][v * 32 + lane] - m);
       }
       const Seg& s = a.seg[w0.e];
       unsigned long long* slot =
@@ -583,7 +612,7 @@ __device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex
 }
 
 // Memory wave.  Step k: (1) Qwin of round k + 2 into the buffer of round k
-// once round k's phase A is done; (2) votes of round k - 1 to memory, then
+// once round k's phase A is done; (2) votes of round k - kLag to memory, then
 // the votes buffer may be reused (v_done).
 template <int D>
 __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
@@ -595,12 +624,13 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
   ctl_finish_q<D>(W, qbufs[0]);
   ctl_finish_q<D>(W, qbufs[1]);
   lds_set(&sy->q_ready, 2u);
-  unsigned on_b[2] = {0, 0}, on_c[2] = {0, 0};  // owned rounds awaited so far, per parity
-  for (int k = 0; k < a.rounds + 1; ++k) {
-    const Work w0 = round_work(a, k), w1 = round_work(a, k - 1);
+  unsigned on_b[kNR] = {}, on_c[kNR] = {};  // owned rounds awaited so far, per residue
+  for (int k = 0; k < a.rounds + kLag; ++k) {
+    const int kv = k - kLag;  // round whose votes leave in this step
+    const Work w0 = round_work(a, k), w1 = round_work(a, kv);
     if (w0.on) {
-      ++on_b[k & 1];
-      if (!lds_wait_ge(sy, &sy->cnt_b[k & 1], kSW * on_b[k & 1])) return;
+      ++on_b[k % kNR];
+      if (!lds_wait_ge(sy, &sy->cnt_b[k % kNR], kSW * on_b[k % kNR])) return;
     }
     if (ctl_issue_q<D>(a, k + 2, Q, qbufs[k & 1])) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -609,16 +639,16 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
     lds_set(&sy->q_ready, (unsigned)(k + 3));
     KVSEL_FUSED_CTL_MARK(k, 6);
     if (w1.on) {
-      ++on_c[(k - 1) & 1];
-      if (!lds_wait_ge(sy, &sy->cnt_c[(k - 1) & 1], kSW * on_c[(k - 1) & 1])) return;
+      ++on_c[kv % kNR];
+      if (!lds_wait_ge(sy, &sy->cnt_c[kv % kNR], kSW * on_c[kv % kNR])) return;
       const Seg& s = a.seg[w1.e];
       const int P = s.L - W;
       float* vout = votes + s.vote_off + (long long)w1.h * s.vote_ld;
       const int j0 = w1.c * kS;
       for (int i = lane; i < kS; i += 64)
-        if (j0 + i < P) vout[j0 + i] = s_votes[(k - 1) & 1][i];
+        if (j0 + i < P) vout[j0 + i] = s_votes[kv & 1][i];
     }
-    if (k >= 1) lds_set(&sy->v_done, (unsigned)k);  // votes of rounds < k are out of LDS
+    if (kv >= 0) lds_set(&sy->v_done, (unsigned)(kv + 1));  // votes of rounds <= kv are out of LDS
     KVSEL_FUSED_CTL_MARK(k, 7);
   }
 }
@@ -778,31 +808,32 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   using G = TileGeom<D>;
   __shared__ uint4 s_ring[kSW][kNBuf][G::PIECES];
   __shared__ uint4 s_q[2][G::PIECES];
-  __shared__ float s_maxp[2][kSW * 32], s_zp[2][kSW * 32];
-  __shared__ float s_m[2][32], s_iz[2][32];
+  __shared__ float4 s_x[kSW][kTT * 4 * 64];  // each wave's logits of one round
+  __shared__ float s_maxp[kNR][kSW * 32], s_zp[kNR][kSW * 32];
+  __shared__ float s_m[kNR][32], s_iz[32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   unsigned arrived = 0u;
   if (!kLse && wave == kSW && lane == 0) arrived = arrive(status);
-  if (threadIdx.x == 0) sy = Sync{{0, 0}, {0, 0}, 0, 0, 0, 0, 0};
+  if (threadIdx.x == 0) sy = Sync{};
   __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
   // The first K tiles and Qwin of rounds 0 and 1.
   WaveTiles cur{K, 0, 0, false};
   int issued = 0, consumed = 0;
   if (wave < kSW) {
     cur = wave_tiles<D>(a, K, 0, wave);
-    for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(cur, t, s_ring[wave], issued);
+    issue_wave_tile<D>(cur, 0, s_ring[wave][0], issued);
   } else if (wave == kSW + 1) {
     ctl_issue_q<D>(a, 0, Q, s_q[0]);
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
   if (wave == kSW) {
     if constexpr (kLse)
-      ctl_lse(a, lse, s_m, s_iz, &sy);  // no workgroup waits for another
+      ctl_lse(a, lse, s_m, &sy);  // no workgroup waits for another
     else if (decide(status, arrived) == kFusedGo)
-      ctl_exchange<D>(a, ex, status, row_stats, s_m, s_iz, &sy);
+      ctl_exchange<D>(a, ex, status, row_stats, s_m, &sy);
     else
       lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
   } else if (wave == kSW + 1) {
@@ -810,29 +841,34 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   } else if (wave == kSW + 2) {
     if constexpr (!kLse) ctl_publish(a, ex, s_maxp, s_zp, &sy);
   } else {
-    uint4 (*ring)[G::PIECES] = s_ring[wave];
+    uint4* buf = s_ring[wave][0];
+    float4* sx = s_x[wave];
     f32x16 xa[kTT], xb[kTT];
-    bool prev_on = false;
+    bool on1 = false, on2 = false;  // rounds k - 1 and k - 2 owned
     // Step k streams round k into one register set (with this wave's row
-    // statistics), then votes round k - 1 from the other set; the sets swap
-    // every step.  The exchange of round k - 1 overlaps the streaming of
-    // round k.
+    // statistics), votes round k - 2 from the logits in LDS, then moves round
+    // k - 1 from the other register set into LDS; the register sets swap
+    // every step.  The exchange of round k - 2 overlapped the streaming of
+    // rounds k - 1 and k.
     auto step = [&](int k, f32x16 (&X0)[kTT], f32x16 (&X1)[kTT]) {
       KVSEL_FUSED_MARK(k, 0);
       const WaveTiles nxt = wave_tiles<D>(a, K, k + 1, wave);
       if (cur.on) {
-        phase_stream<D, kLse>(a, k, cur, nxt, ring, s_q[k & 1], X0, issued, consumed, s_maxp[k & 1], s_zp[k & 1], &sy);
+        phase_stream<D, kLse>(a, k, cur, nxt, buf, s_q[k & 1], X0, issued, consumed, s_maxp[k % kNR],
+                              s_zp[k % kNR], &sy);
       } else {
-        for (int t = 0; t < kTT; ++t) issue_wave_tile<D>(nxt, t, ring, issued);
+        issue_wave_tile<D>(nxt, 0, buf, issued);  // nothing was outstanding
       }
       KVSEL_FUSED_MARK(k, 1);
+      if (on2) phase_votes(a, k - 2, sx, s_m[(k - 2) % kNR], s_votes[(k - 2) & 1], &sy);
       KVSEL_FUSED_MARK(k, 2);
-      if (prev_on) phase_votes(a, k - 1, X1, s_m[(k - 1) & 1], s_iz[(k - 1) & 1], s_votes[(k - 1) & 1], &sy);
+      if (on1) store_x(sx, X1);  // after the votes above have read sx (LDS order within the wave)
       KVSEL_FUSED_MARK(k, 3);
-      prev_on = cur.on;
+      on2 = on1;
+      on1 = cur.on;
       cur = nxt;
     };
-    const int steps = a.rounds + 1;
+    const int steps = a.rounds + kLag;
     for (int k = 0; k < steps; k += 2) {
       step(k, xa, xb);
       if (k + 1 >= steps || lds_get(&sy.abort)) break;
@@ -845,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __syncthreads();
   if constexpr (!kLse) {
     if (sy.abort) {  // not all resident: whole heads, one workgroup each
-      solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz[0]);
+      solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz);
       return;
     }
   }
