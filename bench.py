@@ -76,6 +76,7 @@ def path_alg_bytes(w):
 # these files are unchanged.
 KERNEL_SOURCES = {
     "window_fused": ("kvsel_fused.hip", "kvsel_internal.h"),
+    "window_fused_lse": ("kvsel_fused.hip", "kvsel_internal.h"),
     "fill": ("kvsel_fused.hip", "kvsel_internal.h"),
     "window_stats": ("kvsel_score.hip", "kvsel_internal.h"),
     "window_votes": ("kvsel_score.hip", "kvsel_internal.h"),
@@ -275,7 +276,7 @@ def main():
     n_dom, ms_dom = per_kernel[dom]
     ab_dom = kernel_alg_bytes(dom, w, nch, args.lse)
     achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
-    traffic = None if args.lse else traffic_from_profiles(dom)
+    traffic = traffic_from_profiles(dom + "_lse" if args.lse else dom)
     path_gbps = path_alg_bytes(w) * layers / (ms_step / 1e3) / 1e9
 
     result = {
