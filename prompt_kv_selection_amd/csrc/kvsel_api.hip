@@ -270,13 +270,21 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       any_coop = true;
     }
   }
+  bool all_coop = true;
+  for (int gsegs : coop_segs) all_coop = all_coop && gsegs > 0;
   if (use_fused || any_coop || lse != nullptr) {
     // Exchange records, status words, histograms and the cooperative
     // selection's words start at zero (on the two-pass path without the
     // cooperative selection the statistics kernel clears the histograms).
-    hipError_t e = timed("fill", st, [&] {
-      return launch_fill_u32(counters, (long long)(p.bytes - p.off_ctr) / 4, 0u, st);
-    });
+    // Without the single-read kernel the exchange records are not read;
+    // with the cooperative selection everywhere the histograms are not.
+    // Exchange records, status words and histograms are contiguous, then
+    // the cooperative selection's words.
+    const size_t lo1 = use_fused ? p.off_ctr : p.off_hist;
+    const size_t hi1 = all_coop ? p.off_hist : p.off_coop;
+    const long long n1 = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
+    const long long n2 = any_coop ? (long long)(p.bytes - p.off_coop) : 0;
+    hipError_t e = timed("fill", st, [&] { return launch_zero2(ws + lo1, n1, ws + p.off_coop, n2, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");
   }
 

@@ -893,6 +893,15 @@ __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
   if (i < n) p[i] = v;
 }
 
+// Zero two ranges of 16-byte units in one launch.
+__global__ void zero2_kernel(uint4* p1, long long n1, uint4* p2, long long n2) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (i < n1)
+    p1[i] = make_uint4(0u, 0u, 0u, 0u);
+  else if (i - n1 < n2)
+    p2[i - n1] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 struct GridCache {
   int device = -1;
   int grid[2][2] = {{-1, -1}, {-1, -1}};
@@ -961,6 +970,15 @@ hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, c
   if (a.D == 128) return launch_t<128, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
   if (a.D == 64) return launch_t<64, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
   return hipErrorNotSupported;
+}
+
+hipError_t launch_zero2(void* p1, long long bytes1, void* p2, long long bytes2, hipStream_t st) {
+  if ((uintptr_t)p1 % 16 || (uintptr_t)p2 % 16 || bytes1 % 16 || bytes2 % 16) return hipErrorInvalidValue;
+  const long long n1 = bytes1 / 16, n2 = bytes2 / 16;
+  if (n1 + n2 <= 0) return hipSuccess;
+  const int blocks = (int)((n1 + n2 + 255) / 256);
+  hipLaunchKernelGGL(zero2_kernel, dim3(blocks), dim3(256), 0, st, (uint4*)p1, n1, (uint4*)p2, n2);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st) {

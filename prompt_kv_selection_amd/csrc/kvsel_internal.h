@@ -206,6 +206,9 @@ __host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* exchange,
                                 unsigned* status, float* votes, float* row_stats, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
+// Zero [p1, p1 + bytes1) and [p2, p2 + bytes2) in one launch (16-byte
+// aligned pointers and sizes, else hipErrorInvalidValue).
+hipError_t launch_zero2(void* p1, long long bytes1, void* p2, long long bytes2, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);

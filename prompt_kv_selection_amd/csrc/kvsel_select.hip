@@ -35,6 +35,12 @@
 #define KVSEL_SELECT_MARK(point)
 #endif
 
+// Instrumentation hook of the cooperative selection (point 0..7 of the
+// calling workgroup); empty unless a profiling build defines it.
+#ifndef KVSEL_SELROWS_MARK
+#define KVSEL_SELROWS_MARK(point)
+#endif
+
 namespace kvsel {
 
 // Inclusive scan over the NT threads of the block; `total` gets the sum.
@@ -807,6 +813,14 @@ __device__ __forceinline__ float pool_window(const float (&w)[KW]) {
 // residency handshake decides this, and otherwise the first workgroup of
 // each row runs every segment of its row in turn, with the same arithmetic
 // and results.
+//
+// Candidate round.  When the first digit's boundary bin holds at most
+// kCandCap keys (the usual case), the last two digits and the count
+// exchange are replaced by one exchange: each segment publishes its keys of
+// that bin with their positions (at offsets the first digit's atomic adds
+// returned, so the row's candidates fill a dense range) and its count of
+// keys above the bin; every segment then resolves tau and every segment's
+// counts from the same list in LDS.
 constexpr int kCoopThreads = 512;
 constexpr int kCoopPer = 8;
 constexpr int kCoopSeg = kCoopThreads * kCoopPer;
@@ -814,7 +828,9 @@ constexpr int kCoopMaxSeg = 64;
 constexpr int kCoopStride = kCoopPer + 1;         // LDS words per thread (odd: conflict-free reads)
 constexpr int kCoopHalo = kCoopThreads * kCoopStride;  // LDS index of the halo slots
 constexpr int kCoopHist = 2048 + 2048 + 1024;     // the row's histograms of the three digits
-constexpr int kCoopRowWords = kCoopHist + 2 * kCoopMaxSeg;  // + the segments' 64-bit counts
+constexpr int kCandCap = kCoopSeg;                // candidates of the candidate round (64-bit entries)
+// The row's words: histograms, the segments' 64-bit counts, the candidates.
+constexpr int kCoopRowWords = kCoopHist + 2 * kCoopMaxSeg + 2 * kCandCap;
 static_assert(kMaxPoolRadius >= 3, "pooling widths up to 7");
 
 // Wait until word i of p is non-zero for every i < n (one wave polls,
@@ -908,9 +924,11 @@ __device__ __forceinline__ void coop_keys(const float* __restrict__ v, int P, in
 
 // This segment's histogram of a digit (bits shift .. shift + bits - 1) over
 // its keys whose higher bits equal prefix (all keys for the first digit),
-// added into gh with device-scope atomics.
+// added into gh with device-scope atomics.  With ret != nullptr the bins'
+// values before this segment's adds are kept in ret (LDS).
 __device__ __forceinline__ void coop_add_hist(const uint32_t (&key)[kCoopPer], int valid, int shift, int bits,
-                                              uint32_t prefix, bool first, uint32_t* hist, uint32_t* gh) {
+                                              uint32_t prefix, bool first, uint32_t* hist, uint32_t* gh,
+                                              uint32_t* ret = nullptr) {
   const int tid = threadIdx.x, nb = 1 << bits;
   for (int d = tid; d < nb; d += kCoopThreads) hist[d] = 0u;
   __syncthreads();
@@ -930,8 +948,45 @@ __device__ __forceinline__ void coop_add_hist(const uint32_t (&key)[kCoopPer], i
   }
   if (run_len) atomicAdd(&hist[run_bin], run_len);
   __syncthreads();
+  if (ret != nullptr) {
+    for (int d = tid; d < nb; d += kCoopThreads)
+      if (hist[d]) ret[d] = __hip_atomic_fetch_add(gh + d, hist[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   for (int d = tid; d < nb; d += kCoopThreads)
     if (hist[d]) __hip_atomic_fetch_add(gh + d, hist[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Candidate round, reading side: wait until the nseg count words and the
+// n candidate entries are all written (non-zero), then take the count words
+// (cw) and the candidates' keys (ck) into LDS.  Bounded: a timed-out wait
+// sets an error flag.
+__device__ void coop_read_candidates(const unsigned long long* cnt, int nseg, const unsigned long long* cbuf, int n,
+                                     unsigned long long* cw, uint32_t* ck, uint32_t* sh, unsigned* err) {
+  const int tid = threadIdx.x;
+  long spins = 0;
+  for (;;) {
+    uint32_t missing = 0;
+    if (tid < nseg) {
+      const unsigned long long c = __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      missing += c == 0ull;
+      cw[tid] = c;
+    }
+    for (int i = tid; i < n; i += kCoopThreads) {
+      const unsigned long long e = __hip_atomic_load(cbuf + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      missing += e == 0ull;
+      ck[i] = (uint32_t)e;
+    }
+    uint32_t total;
+    (void)block_scan<kCoopThreads>(missing, sh, total);
+    if (total == 0) break;
+    if (++spins > (1L << 20)) {
+      if (tid == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
 }
 
 // Copy output rows m0 .. m0 + n of K and V from source rows first + i
@@ -979,13 +1034,23 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   __shared__ uint32_t s_digit, s_need;
   __shared__ unsigned s_go;
   __shared__ uint32_t s_cnt[kCoopMaxSeg], s_pre[kCoopMaxSeg];  // per-segment counts and prefixes
+  __shared__ uint32_t s_ret[2048];                               // first-digit bins before this segment's adds
+  __shared__ uint32_t s_cg[kCoopMaxSeg], s_ce[kCoopMaxSeg];      // candidates above / on tau per segment
+  __shared__ unsigned long long s_cw[kCoopMaxSeg];                // the segments' count words
+  static_assert(kCandCap <= kCoopHalo, "candidate keys alias sv");
+  static_assert(kCandCap < 65536, "a candidate range packs into 16-bit fields");
   static_assert(kCoopPer == 8, "the window ranks below use 8 positions per thread");
 
   // Arrival first; the decision is taken once the own segment's keys are
   // in place (they depend on no other workgroup), before anything is
   // published.
+  KVSEL_SELROWS_MARK(0);
   unsigned arrived = 0u;
-  if (tid == 0) arrived = arrive(status);
+  if (tid == 0) {
+    arrived = arrive(status);
+    s_digit = 0u;  // in range even if a timed-out wait leaves no bin chosen
+    s_need = 0u;
+  }
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
   const int h = s.h0 + (row - s.row0);
   int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
@@ -1017,6 +1082,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   uint32_t* gh2 = words + 2048;
   uint32_t* gh3 = words + 4096;
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(words + kCoopHist);
+  unsigned long long* cbuf = cnt + kCoopMaxSeg;  // the candidate round's entries (position + 1, key)
   uint32_t key[kCoopPer];
   auto valid_of = [&](int g) { return max(0, min(kCoopPer, P - g * kCoopSeg - tid * kCoopPer)); };
   // The own segment's keys depend on no other workgroup: computed before
@@ -1025,11 +1091,15 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   if (tid == 0) s_go = decide(status, arrived);
   __syncthreads();
   const bool go = s_go == kFusedGo;
+  KVSEL_SELROWS_MARK(1);
   if (go ? seg >= nseg : seg != 0) return;  // not all resident: the row's first workgroup does every segment
   const int g0 = go ? seg : 0, g1 = go ? seg + 1 : nseg;  // the segments this workgroup runs
 
-  // The three digits of tau.
+  // The digits of tau: the first across the segments; then either the
+  // candidate round or the other two digits and the count exchange.
   uint32_t prefix = 0u, need = (uint32_t)count, total = (uint32_t)P;
+  bool cand_round = false;
+  uint32_t* ck = reinterpret_cast<uint32_t*>(sv);  // candidate keys (the candidate round)
   for (int digit = 0; digit < 3; ++digit) {
     const int shift = digit == 0 ? 21 : (digit == 1 ? 10 : 0);
     const int bits = digit == 2 ? 10 : 11;
@@ -1043,7 +1113,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
         for (int u = 0; u < kCoopPer; ++u)
           if (u < n) o[u] = __uint_as_float(key[u]);
       }
-      coop_add_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist, gh);
+      coop_add_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist, gh, go && digit == 0 ? s_ret : nullptr);
     }
     coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, status);
     pick_digit<kCoopThreads>(hist, 1 << bits, need, sh, &s_digit, &s_need);
@@ -1051,33 +1121,124 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     prefix = (prefix << bits) | s_digit;
     need = s_need;
     __syncthreads();  // hist is rewritten by the next digit
+    KVSEL_SELROWS_MARK(2 + digit);
+    if (digit == 0 && go && total <= (uint32_t)kCandCap) {  // the same for every segment of the row
+      cand_round = true;
+      break;
+    }
   }
-  const uint32_t tau = prefix, need_eq = need;
-  for (int g = g0; g < g1; ++g) {
-    if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
-    const int n = valid_of(g);
-    uint32_t gt = 0, eq = 0;
+  if (cand_round) {
+    // Publish this segment's keys of the boundary bin (at the offset its
+    // first-digit add returned, so its candidates form one range) and a
+    // count word: keys above the bin + 1, the range's start and length.
+    const uint32_t d1 = prefix;
+    const int n = valid_of(seg);
+    uint32_t above = 0, mine = 0;
 #pragma unroll
     for (int u = 0; u < kCoopPer; ++u) {
-      gt += u < n && key[u] > tau;
-      eq += u < n && key[u] == tau;
+      above += u < n && (key[u] >> 21) > d1;
+      mine += u < n && (key[u] >> 21) == d1;
     }
-    uint32_t tg, te;
-    (void)block_scan<kCoopThreads>(gt, sh, tg);
-    (void)block_scan<kCoopThreads>(eq, sh, te);
-    if (tid == 0)
-      __hip_atomic_store(cnt + g, (unsigned long long)(tg + 1u) | ((unsigned long long)te << 32), __ATOMIC_RELAXED,
+    uint32_t tot_above, tot_mine;
+    (void)block_scan<kCoopThreads>(above, sh, tot_above);
+    const uint32_t base = s_ret[d1];  // meaningful when this segment has candidates
+    uint32_t off = base + block_scan<kCoopThreads>(mine, sh, tot_mine) - mine;
+#pragma unroll
+    for (int u = 0; u < kCoopPer; ++u)
+      if (u < n && (key[u] >> 21) == d1) {
+        const unsigned long long j1 = (unsigned long long)(seg * kCoopSeg + tid * kCoopPer + u + 1);
+        if (off < (uint32_t)kCandCap)  // always, unless a timed-out wait left the bin count short
+          __hip_atomic_store(cbuf + off, (j1 << 32) | key[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++off;
+      }
+    if (tid == 0) {
+      const unsigned long long range = tot_mine ? ((unsigned long long)(tot_mine << 16) | base) : 0ull;
+      __hip_atomic_store(cnt + seg, (unsigned long long)(tot_above + 1u) | (range << 32), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // sv becomes the candidate keys
+    KVSEL_SELROWS_MARK(3);
+    coop_read_candidates(cnt, nseg, cbuf, (int)total, s_cw, ck, sh, status);
+    KVSEL_SELROWS_MARK(4);
+    // The last two digits of tau over the candidates, in LDS.
+    for (int digit = 1; digit < 3; ++digit) {
+      const int shift = digit == 1 ? 10 : 0;
+      const int bits = digit == 1 ? 11 : 10;
+      const int nb = 1 << bits;
+      for (int d = tid; d < nb; d += kCoopThreads) hist[d] = 0u;
+      __syncthreads();
+      for (int i = tid; i < (int)total; i += kCoopThreads)
+        if ((ck[i] >> (shift + bits)) == prefix) atomicAdd(&hist[(ck[i] >> shift) & (uint32_t)(nb - 1)], 1u);
+      __syncthreads();
+      KVSEL_SELROWS_MARK(6 + 2 * digit);
+      pick_digit<kCoopThreads>(hist, nb, need, sh, &s_digit, &s_need);
+      prefix = (prefix << bits) | s_digit;
+      need = s_need;
+      __syncthreads();
+      KVSEL_SELROWS_MARK(7 + 2 * digit);
+    }
+    // Every segment's candidates above and on tau: a wave per segment over
+    // the segment's range of candidates.
+    for (int q = tid >> 6; q < nseg; q += kCoopThreads / 64) {
+      const uint32_t range = (uint32_t)(s_cw[q] >> 32);
+      const int lo = (int)(range & 0xFFFFu), hi = min(lo + (int)(range >> 16), (int)total);
+      uint32_t gt = 0, eq = 0;
+      for (int i = lo + lane; i < hi; i += 64) {
+        gt += ck[i] > prefix;
+        eq += ck[i] == prefix;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        gt += __shfl_xor(gt, o);
+        eq += __shfl_xor(eq, o);
+      }
+      if (lane == 0) {
+        s_cg[q] = gt;
+        s_ce[q] = eq;
+      }
+    }
+    __syncthreads();
+    KVSEL_SELROWS_MARK(12);
   }
-  coop_wait(cnt, nseg, status);
+  const uint32_t tau = prefix, need_eq = need;
+  if (!cand_round) {
+    for (int g = g0; g < g1; ++g) {
+      if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
+      const int n = valid_of(g);
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int u = 0; u < kCoopPer; ++u) {
+        gt += u < n && key[u] > tau;
+        eq += u < n && key[u] == tau;
+      }
+      uint32_t tg, te;
+      (void)block_scan<kCoopThreads>(gt, sh, tg);
+      (void)block_scan<kCoopThreads>(eq, sh, te);
+      if (tid == 0)
+        __hip_atomic_store(cnt + g, (unsigned long long)(tg + 1u) | ((unsigned long long)te << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    KVSEL_SELROWS_MARK(5);
+    coop_wait(cnt, nseg, status);
+    KVSEL_SELROWS_MARK(6);
+  }
 
   // Phase 4: picks in index order at their final slots, and their rows.
   // Per segment: the picks and tau-equal positions of the earlier segments
-  // (all counts read at once, a lane each, and scanned).
+  // (all counts read at once, a lane each, and scanned).  In the candidate
+  // round a segment's count word holds its keys above the boundary bin, and
+  // the candidates add those above and on tau.
   if (tid < 64) {
-    const unsigned long long c =
-        tid < nseg ? __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1ull;
-    const uint32_t gq = (uint32_t)c - 1u, eqq = (uint32_t)(c >> 32);
+    uint32_t gq = 0u, eqq = 0u;
+    if (tid < nseg) {
+      const unsigned long long c = __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gq = (uint32_t)c - 1u;
+      eqq = (uint32_t)(c >> 32);
+      if (cand_round) {  // the word holds the keys above the boundary bin and the candidate range
+        gq += s_cg[tid];
+        eqq = s_ce[tid];
+      }
+    }
     uint32_t eq_incl = eqq;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -1132,6 +1293,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     }
     __syncthreads();  // picks[] is rewritten by the next segment
   }
+  KVSEL_SELROWS_MARK(13);
   (void)lane;
 }
 

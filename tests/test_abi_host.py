@@ -46,9 +46,10 @@ def test_workspace_sizes(B):
     # (per head and 512-position chunk),
     # status words (error flags, decision, fallback counter and 16 arrival
     # counters on lines of their own), first-digit histograms, the
-    # cooperative selection's status words and per-row words
+    # cooperative selection's status words and per-row words (histograms,
+    # segment counts, candidate entries)
     expect_min = (2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128) * 4)
+                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128 + 8192) * 4)
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W

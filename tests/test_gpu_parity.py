@@ -100,6 +100,7 @@ CASES = [
     ("bf16", 128, 2, 20000, 32, 1024, 5, "max"),   # five selection segments
     ("bf16", 128, 2, 12289, 32, 3000, 3, "avg"),   # four segments, the last one position long
     ("bf16", 128, 1, 9000, 32, 9500, 5, "avg"),    # bypass over several segments
+    ("bf16", 128, 2, 20000, 32, 2048, 3, "max"),   # codebook keys below: exact ties across segments
 ]
 
 
@@ -108,10 +109,11 @@ CASES = [
                                              for c in CASES])
 def test_random_cases(B, case, scoring):
     dtype, D, H, L, W, C, kernel, pooling = case
+    keys = "codebook" if (L, C) == (20000, 2048) else "spike"
     w = WL.Workload("case", seed=L * 7 + W, heads=H, L=L, W=W, C=C, D=D, dtype=dtype, kernel=kernel,
-                    pooling=pooling, keys="spike", spike_frac=0.02 if L - W >= 50 else 0.0)
+                    pooling=pooling, keys=keys, spike_frac=0.02 if L - W >= 50 else 0.0)
     Q, K, V = WL.layer_arrays(w)
-    log(f"random case {case} scoring={scoring}")
+    log(f"random case {case} keys={keys} scoring={scoring}")
     Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
     if scoring == "single_read" and not single_read_covers(dtype, D, W) and L >= C:
         with pytest.raises(B.KvselError) as ei:
@@ -173,6 +175,32 @@ def test_identical_keys_give_identical_scores(B, scoring):
         ref = O.snapkv_select(WL.to_float64(Q[h], "bf16"), WL.to_float64(K[h], "bf16"),
                               WL.to_float64(V[h], "bf16"), w.W, w.C, w.kernel, w.pooling)
         check_head(out, h, ref, w.L, w.W, w.C, f"tied head {h}")
+
+
+@pytest.mark.parametrize("pooling", ["max", "avg"])
+def test_uniform_votes_select_lowest_indices(B, pooling):
+    """Zero window queries make every logit 0, so every vote is the closed
+    form H_L - H_P and (max pooling, or avg away from the edges) every pooled
+    score is equal: the selection's boundary bin holds every key (the digit
+    path of the cooperative selection, not the candidate round), and ties go
+    to the lowest indices."""
+    H, L, W, C, D, k = 2, 20000, 32, 1024, 128, 5
+    rng = np.random.default_rng(7)
+    Q = np.zeros((H, W, D), dtype=np.float32)
+    K = rng.standard_normal((H, L, D)).astype(np.float32)
+    V = rng.standard_normal((H, L, D)).astype(np.float32)
+    Qd, Kd, Vd = (to_device(WL.f32_to_bf16_bits(x), "bf16") for x in (Q, K, V))
+    log(f"uniform votes pooling={pooling}")
+    out = run_select(Qd, Kd, Vd, L, W, C, k, pooling, "bf16")
+    P = L - W
+    closed = sum(1.0 / (P + i + 1) for i in range(W))
+    np.testing.assert_allclose(out["votes"], closed, rtol=1e-5)
+    n = C - W
+    first = 0 if pooling == "max" else k // 2  # avg: the edge positions score lower
+    for h in range(H):
+        assert out["idx"][h, :n].tolist() == list(range(first, first + n)), f"head {h}"
+        assert out["idx"][h, n:C].tolist() == list(range(P, L))
+    check_gather(out, Kd, Vd, C, L)
 
 
 @pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
