@@ -924,11 +924,9 @@ __device__ __forceinline__ void coop_keys(const float* __restrict__ v, int P, in
 
 // This segment's histogram of a digit (bits shift .. shift + bits - 1) over
 // its keys whose higher bits equal prefix (all keys for the first digit),
-// added into gh with device-scope atomics.  With ret != nullptr the bins'
-// values before this segment's adds are kept in ret (LDS).
-__device__ __forceinline__ void coop_add_hist(const uint32_t (&key)[kCoopPer], int valid, int shift, int bits,
-                                              uint32_t prefix, bool first, uint32_t* hist, uint32_t* gh,
-                                              uint32_t* ret = nullptr) {
+// into hist (LDS).
+__device__ __forceinline__ void coop_local_hist(const uint32_t (&key)[kCoopPer], int valid, int shift, int bits,
+                                                uint32_t prefix, bool first, uint32_t* hist) {
   const int tid = threadIdx.x, nb = 1 << bits;
   for (int d = tid; d < nb; d += kCoopThreads) hist[d] = 0u;
   __syncthreads();
@@ -948,6 +946,13 @@ __device__ __forceinline__ void coop_add_hist(const uint32_t (&key)[kCoopPer], i
   }
   if (run_len) atomicAdd(&hist[run_bin], run_len);
   __syncthreads();
+}
+
+// Add the LDS histogram hist[1 << bits] into gh with device-scope atomics.
+// With ret != nullptr the bins' values before this segment's adds are kept
+// in ret (LDS).
+__device__ __forceinline__ void coop_push_hist(int bits, const uint32_t* hist, uint32_t* gh, uint32_t* ret) {
+  const int tid = threadIdx.x, nb = 1 << bits;
   if (ret != nullptr) {
     for (int d = tid; d < nb; d += kCoopThreads)
       if (hist[d]) ret[d] = __hip_atomic_fetch_add(gh + d, hist[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1085,9 +1090,12 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   unsigned long long* cbuf = cnt + kCoopMaxSeg;  // the candidate round's entries (position + 1, key)
   uint32_t key[kCoopPer];
   auto valid_of = [&](int g) { return max(0, min(kCoopPer, P - g * kCoopSeg - tid * kCoopPer)); };
-  // The own segment's keys depend on no other workgroup: computed before
-  // the decision.
-  if (seg < nseg) coop_keys<KW, MAX>(v, P, seg, sv, key);
+  // The own segment's keys and their first-digit histogram depend on no
+  // other workgroup: computed before the decision.
+  if (seg < nseg) {
+    coop_keys<KW, MAX>(v, P, seg, sv, key);
+    coop_local_hist(key, valid_of(seg), 21, 11, 0u, true, hist);
+  }
   if (tid == 0) s_go = decide(status, arrived);
   __syncthreads();
   const bool go = s_go == kFusedGo;
@@ -1113,7 +1121,8 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
         for (int u = 0; u < kCoopPer; ++u)
           if (u < n) o[u] = __uint_as_float(key[u]);
       }
-      coop_add_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist, gh, go && digit == 0 ? s_ret : nullptr);
+      if (!(go && digit == 0)) coop_local_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist);  // else done
+      coop_push_hist(bits, hist, gh, go && digit == 0 ? s_ret : nullptr);
     }
     coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, status);
     pick_digit<kCoopThreads>(hist, 1 << bits, need, sh, &s_digit, &s_need);
@@ -1139,10 +1148,11 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
       above += u < n && (key[u] >> 21) > d1;
       mine += u < n && (key[u] >> 21) == d1;
     }
-    uint32_t tot_above, tot_mine;
-    (void)block_scan<kCoopThreads>(above, sh, tot_above);
+    uint32_t tot;  // both counts of a segment are at most kCoopSeg < 2^16: one scan of the pair
+    const uint32_t incl = block_scan<kCoopThreads>(above | (mine << 16), sh, tot);
+    const uint32_t tot_above = tot & 0xFFFFu, tot_mine = tot >> 16;
     const uint32_t base = s_ret[d1];  // meaningful when this segment has candidates
-    uint32_t off = base + block_scan<kCoopThreads>(mine, sh, tot_mine) - mine;
+    uint32_t off = base + (incl >> 16) - mine;
 #pragma unroll
     for (int u = 0; u < kCoopPer; ++u)
       if (u < n && (key[u] >> 21) == d1) {
