@@ -60,9 +60,7 @@ def kernel_alg_bytes(name, w, nch, lse=False):
         return H * P * 4 + 4 * H * C * D * e + H * C * 4
     if name == "select":            # votes read, indices written, kept K and V rows read and written
         return H * P * 4 + H * C * 4 + 4 * H * C * D * e
-    if name == "fill":              # per-head exchange records cleared
-        return H * 64 + 256
-    return None
+    return None                     # fill: workspace clearing, not the method's traffic
 
 
 def path_alg_bytes(w):
