@@ -44,10 +44,16 @@
  *     errors are detected on the host before anything is enqueued, and then
  *     no output is touched.  Device faults surface at the caller's next
  *     synchronisation.
- *   - Return value: KVSEL_OK or a negative kvsel_status; kvsel_last_error()
+ *   - Return value: KVSEL_OK or a negative kvsel_status_code; kvsel_last_error()
  *     returns a thread-local message describing the last failure.
  *   - Supported: D in {64, 128}, 1 <= W <= 128, L < 2^31 / D.  Inputs must be
- *     finite (a precondition; the page's example rejects non-finite values).
+ *     finite (the page's example rejects non-finite values and dot
+ *     products [section "one full selection computed from Q and K"]).  This
+ *     is a precondition, checked on the device without a host round trip:
+ *     every call flags a non-finite or zero row normaliser (which a
+ *     non-finite key or dot product produces), and the validating mode
+ *     (KVSEL_OPT_VALIDATE) also scans every Qwin, K and V element; the flags
+ *     are read with kvsel_status().
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef KVSEL_H
@@ -65,8 +71,9 @@ typedef enum {
   KVSEL_EINVAL = -1,       /* argument outside the method's rules or NULL pointer */
   KVSEL_EUNSUPPORTED = -2, /* valid for the method, not covered by these kernels */
   KVSEL_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes value */
-  KVSEL_EDEVICE = -4       /* a HIP call or kernel launch failed */
-} kvsel_status;
+  KVSEL_EDEVICE = -4,      /* a HIP call or kernel launch failed (kvsel_status: a device-side wait timed out) */
+  KVSEL_ENONFINITE = -5    /* kvsel_status: a non-finite input or row normaliser was seen */
+} kvsel_status_code;
 
 enum { KVSEL_POOL_AVG = 0, KVSEL_POOL_MAX = 1 };
 enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
@@ -94,8 +101,11 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  *   that fallback, and every cooperative selection launch (whose workgroups
  *   also wait for each other) its own: the first workgroup of each row then
  *   runs all of the row's segments; 0 (default) off.
+ * KVSEL_OPT_VALIDATE: 1 makes every selection call first scan its Qwin, K
+ *   and V (and row_lse) for non-finite values (two extra reads of K and V);
+ *   0 (default) off.
  * Not thread-safe with respect to concurrent calls. */
-enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1 };
+enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1, KVSEL_OPT_VALIDATE = 2 };
 enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };
 int kvsel_set_option(int option, int value);
 int kvsel_get_option(int option);
@@ -105,6 +115,18 @@ int kvsel_version(void);
 
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* kvsel_last_error(void);
+
+/* Device-side outcome of the last selection call (kvsel_select*,
+ * kvsel_select*_lse) that used this workspace: waits for `stream`, then reads
+ * the flags the call's kernels left in the workspace header.  Returns
+ * KVSEL_OK; KVSEL_ENONFINITE if a non-finite input (validating mode) or a
+ * non-finite or zero row normaliser was seen (the outputs follow the
+ * arithmetic but carry no meaning); KVSEL_EDEVICE if a bounded wait between
+ * workgroups timed out (the outputs of that call are unreliable); or
+ * KVSEL_EINVAL for a NULL or misaligned workspace.  Each selection call
+ * clears the flags at its start.  This is the only entry point that
+ * synchronises. */
+int kvsel_status(const void* workspace, void* stream);
 
 /* Workspace bytes kvsel_select needs for these sizes; 0 if the arguments are
  * invalid (kvsel_last_error() says why).  Host-only, enqueues nothing. */
@@ -230,7 +252,7 @@ int kvsel_gather(const void* K, const void* V, const int32_t* indices, int ld_id
  * the launch stream.  kvsel_profile_read() waits for the recorded events,
  * fills up to max_entries records (one per kernel name: launches and summed
  * elapsed milliseconds) and returns how many kernel names were seen, or a
- * negative kvsel_status.  Host memory only; not for use under graph capture. */
+ * negative kvsel_status_code.  Host memory only; not for use under graph capture. */
 typedef struct {
   char name[32];
   int launches;

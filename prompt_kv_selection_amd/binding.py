@@ -22,6 +22,7 @@ KVSEL_EINVAL = -1
 KVSEL_EUNSUPPORTED = -2
 KVSEL_EWORKSPACE = -3
 KVSEL_EDEVICE = -4
+KVSEL_ENONFINITE = -5
 POOL = {"avg": 0, "max": 1}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -37,6 +38,8 @@ lib.kvsel_version.restype = _i
 lib.kvsel_version.argtypes = []
 lib.kvsel_last_error.restype = ctypes.c_char_p
 lib.kvsel_last_error.argtypes = []
+lib.kvsel_status.restype = _i
+lib.kvsel_status.argtypes = [_vp, _vp]
 lib.kvsel_workspace_bytes.restype = _sz
 lib.kvsel_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 lib.kvsel_varlen_workspace_bytes.restype = _sz
@@ -95,6 +98,12 @@ def kvsel_version() -> int:
 
 def kvsel_last_error() -> str:
     return lib.kvsel_last_error().decode()
+
+
+def kvsel_status(workspace, stream=None) -> int:
+    """Device-side outcome of the last selection call that used `workspace`
+    (waits for the stream): KVSEL_OK, KVSEL_ENONFINITE or KVSEL_EDEVICE."""
+    return lib.kvsel_status(_ptr(workspace), _stream(stream))
 
 
 def kvsel_workspace_bytes(heads: int, L: int, W: int, C: int, D: int, dtype) -> int:
@@ -229,6 +238,7 @@ def kvsel_profile_read() -> dict:
 
 KVSEL_OPT_SCORING = 0
 KVSEL_OPT_FORCE_FALLBACK = 1
+KVSEL_OPT_VALIDATE = 2
 SCORING = {"auto": 0, "two_pass": 1, "single_read": 2}
 lib.kvsel_set_option.restype = _i
 lib.kvsel_set_option.argtypes = [_i, _i]

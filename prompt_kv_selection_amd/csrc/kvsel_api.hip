@@ -85,6 +85,10 @@ struct Plan {
          off_status = 0, off_hist = 0, off_coop = 0, bytes = 0;
 };
 
+// The workspace starts with a 256-byte header; word 0 holds the error flags
+// of the last selection call (kvsel_status).
+constexpr size_t kHeaderBytes = 256;
+
 // Selection workspace per (sequence, head) row: threshold and segment counts.
 constexpr size_t kCutBytes = 2 * sizeof(uint32_t);
 constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
@@ -92,6 +96,7 @@ constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
 // Process-wide options.
 int g_scoring = KVSEL_SCORING_AUTO;
 int g_force_fallback = 0;
+int g_validate = 0;
 
 int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p) {
   if (cu_L == nullptr || C_host == nullptr) return fail(KVSEL_EINVAL, "cu_L_host and C_host must not be NULL");
@@ -134,7 +139,7 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   if ((rc = check_support(W, D))) return rc;
   p.part_slots = p.part[B];
   p.vote_elems = (long long)heads * p.cuP[B];
-  size_t off = 0;
+  size_t off = kHeaderBytes;
   p.off_pm = off;
   off = align256(off + (size_t)p.part_slots * W * sizeof(float));
   p.off_pz = off;
@@ -169,6 +174,7 @@ Launch base_launch(const Plan& p, int kernel, int pooling) {
   a.pooling = pooling;
   a.window = 1;
   a.scale2 = (float)(1.4426950408889634074 / sqrt((double)p.D));
+  a.err = nullptr;
   return a;
 }
 
@@ -272,25 +278,45 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   }
   bool all_coop = true;
   for (int gsegs : coop_segs) all_coop = all_coop && gsegs > 0;
-  if (use_fused || any_coop || lse != nullptr) {
-    // Exchange records, status words, histograms and the cooperative
-    // selection's words start at zero (on the two-pass path without the
-    // cooperative selection the statistics kernel clears the histograms).
-    // Without the single-read kernel the exchange records are not read;
-    // with the cooperative selection everywhere the histograms are not.
-    // Exchange records, status words and histograms are contiguous, then
-    // the cooperative selection's words.
+  unsigned* err = (unsigned*)ws;  // the header's error word
+  {
+    // The header, and the exchange records, status words, histograms and
+    // the cooperative selection's words that are in use, start at zero (on
+    // the two-pass path without the cooperative selection the statistics
+    // kernel clears the histograms).  Exchange records, status words and
+    // histograms are contiguous, then the cooperative selection's words.
+    const bool hists = !all_coop && (use_fused || lse != nullptr);
     const size_t lo1 = use_fused ? p.off_ctr : p.off_hist;
-    const size_t hi1 = all_coop ? p.off_hist : p.off_coop;
-    const long long n1 = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
-    const long long n2 = any_coop ? (long long)(p.bytes - p.off_coop) : 0;
-    hipError_t e = timed("fill", st, [&] { return launch_zero2(ws + lo1, n1, ws + p.off_coop, n2, st); });
+    const size_t hi1 = hists ? p.off_coop : (use_fused ? p.off_hist : lo1);
+    ZeroRanges z{};
+    z.p[0] = ws;
+    z.bytes[0] = (long long)kHeaderBytes;
+    z.p[1] = ws + lo1;
+    z.bytes[1] = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
+    z.p[2] = ws + p.off_coop;
+    z.bytes[2] = any_coop ? (long long)(p.bytes - p.off_coop) : 0;
+    hipError_t e = timed("fill", st, [&] { return launch_zero(z, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");
+  }
+  if (g_validate) {
+    // Validating mode: every input element of every sequence is finite.
+    const size_t esz = p.dtype == KVSEL_BF16 ? 2 : 4;
+    const long long q16 = (long long)p.B * p.heads * p.W * p.D * (long long)esz / 16;
+    const long long kv16 = (long long)p.heads * p.cuL[p.B] * p.D * (long long)esz / 16;
+    hipError_t e = timed("check", st, [&] {
+      hipError_t r = launch_check_finite(Q, q16, p.dtype, err, st);
+      if (r == hipSuccess) r = launch_check_finite(K, kv16, p.dtype, err, st);
+      if (r == hipSuccess) r = launch_check_finite(V, kv16, p.dtype, err, st);
+      if (r == hipSuccess && lse != nullptr) r = launch_check_finite(lse, (long long)p.B * p.heads * p.W / 4, 0, err, st);
+      return r;
+    });
+    if (e != hipSuccess) return device_error(e, "check launch");
   }
 
   for (int b0 = 0; b0 < p.B; b0 += kMaxSegs) {
     const int nb = std::min(kMaxSegs, p.B - b0);
     Launch a = base_launch(p, kernel, pooling);
+    a.err = err;
     a.n = nb;
     a.S = p.fS;
     a.rounds = 0;
@@ -425,16 +451,39 @@ int kvsel_set_option(int option, int value) {
     g_force_fallback = value;
     return ok();
   }
+  if (option == KVSEL_OPT_VALIDATE) {
+    if (value != 0 && value != 1) return fail(KVSEL_EINVAL, "invalid validate value %d", value);
+    g_validate = value;
+    return ok();
+  }
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
 int kvsel_get_option(int option) {
   if (option == KVSEL_OPT_SCORING) return g_scoring;
   if (option == KVSEL_OPT_FORCE_FALLBACK) return g_force_fallback;
+  if (option == KVSEL_OPT_VALIDATE) return g_validate;
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
 const char* kvsel_last_error(void) { return g_error.c_str(); }
+
+int kvsel_status(const void* workspace, void* stream) {
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  unsigned flags = 0;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&flags, workspace, sizeof flags, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_error(e, "status read");
+  if (flags & (kErrExchangeWait | kErrLdsWait | kErrSelectWait))
+    return fail(KVSEL_EDEVICE, "a bounded device-side wait timed out (flags 0x%x): the outputs of that call are "
+                               "unreliable", flags);
+  if (flags & kErrNonFinite)
+    return fail(KVSEL_ENONFINITE, "a non-finite input value or a non-finite or zero row normaliser (flags 0x%x)",
+                flags);
+  return ok();
+}
 
 size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B, int heads, int W,
                                     int D, int dtype) {

@@ -62,6 +62,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kvsel_internal.h"
 
 // Instrumentation hooks in the streaming waves (step k, point 0..3) and the
@@ -530,7 +532,8 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
     if (w.on) {
       float M, Z;
       const bool ok = ctl_head_stats(a, w, ex, M, Z);
-      if (!ok && lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!ok && lane == 0) raise_error(a.err, kErrExchangeWait);
+      if (__ballot(ok && lane < W && !stats_ok(M, Z)) != 0 && lane == 0) raise_error(a.err, kErrNonFinite);
       if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
       if (lane < W) {
         s_m[j % kNR][lane] = ok ? M + __log2f(Z) : __builtin_nanf("");
@@ -565,6 +568,7 @@ __device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*
     if (j >= kNR && round_work(a, j - kNR).on) ++votes_due[j % kNR];
     const float cur = next;
     next = load(j + 1);
+    if (__ballot(w.on && lane < W && !isfinite(cur)) != 0 && lane == 0) raise_error(a.err, kErrNonFinite);
     if (w.on) {
       if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
       if (lane < 32) s_m[j % kNR][lane] = lane < W ? cur * kLog2e : INFINITY;  // rows past W drop out
@@ -600,7 +604,7 @@ __device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex
 #pragma unroll
       for (int v = 0; v < kSW; ++v) {
         const float zv = s_zp[k % kNR][v * 32 + lane];
-        if (zv > 0.f) zz += zv * exp2_fast(s_maxp[k % kNR][v * 32 + lane] - m);
+        if (zv != 0.f) zz += zv * exp2_fast(s_maxp[k % kNR][v * 32 + lane] - m);  // a NaN sum propagates
       }
       const Seg& s = a.seg[w0.e];
       unsigned long long* slot =
@@ -762,7 +766,7 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
       const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 31));
       const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 63));
       const float mh = g == 0 ? m0 : m1;
-      const float zz = half_sum(z[r] > 0.f ? z[r] * exp2_fast(m[r] - mh) : 0.f);
+      const float zz = half_sum(z[r] != 0.f ? z[r] * exp2_fast(m[r] - mh) : 0.f);  // a NaN sum propagates
       if ((lane & 31) == 31) {
         s_maxp[wave * 32 + acc_row(r, g)] = mh;
         s_zp[wave * 32 + acc_row(r, g)] = zz;
@@ -777,10 +781,11 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
       float Z = 0.f;
       for (int v = 0; v < kSW; ++v) {
         const float zv = s_zp[v * 32 + i];
-        if (zv > 0.f) Z += zv * exp2_fast(s_maxp[v * 32 + i] - M);
+        if (zv != 0.f) Z += zv * exp2_fast(s_maxp[v * 32 + i] - M);  // a NaN sum propagates
       }
       s_m[i] = M;
       s_iz[i] = 1.f / Z;
+      if (!stats_ok(M, Z)) raise_error(a.err, kErrNonFinite);
       if (row_stats != nullptr) {
         float* rs = row_stats + ((long long)hs * W + i) * 2;
         rs[0] = M * kLn2;
@@ -885,7 +890,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
       return;
     }
   }
-  if (threadIdx.x == 0 && sy.timeout) __hip_atomic_fetch_or(status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && sy.timeout) raise_error(a.err, kErrLdsWait);
 }
 
 __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
@@ -893,13 +898,38 @@ __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
   if (i < n) p[i] = v;
 }
 
-// Zero two ranges of 16-byte units in one launch.
-__global__ void zero2_kernel(uint4* p1, long long n1, uint4* p2, long long n2) {
-  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
-  if (i < n1)
-    p1[i] = make_uint4(0u, 0u, 0u, 0u);
-  else if (i - n1 < n2)
-    p2[i - n1] = make_uint4(0u, 0u, 0u, 0u);
+// Zero up to kZeroRanges ranges of 16-byte units in one launch (n[] in units).
+struct ZeroUnits {
+  uint4* p[kZeroRanges];
+  long long n[kZeroRanges];
+};
+__global__ void zero_kernel(const ZeroUnits z) {
+  long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < kZeroRanges; ++r) {
+    if (i < z.n[r]) {
+      z.p[r][i] = make_uint4(0u, 0u, 0u, 0u);
+      return;
+    }
+    i -= z.n[r];
+  }
+}
+
+// Validating mode: any non-finite element among n 16-byte units.
+__global__ void check_finite_kernel(const uint4* __restrict__ p, long long n, int bf16, unsigned* err) {
+  bool bad = false;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const uint4 u = p[i];
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (bf16)  // two bf16 values per word: exponent bits all ones
+        bad = bad || (w[q] & 0x7F80u) == 0x7F80u || (w[q] & 0x7F800000u) == 0x7F800000u;
+      else
+        bad = bad || (w[q] & 0x7F800000u) == 0x7F800000u;
+    }
+  }
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) raise_error(err, kErrNonFinite);
 }
 
 struct GridCache {
@@ -972,12 +1002,26 @@ hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, c
   return hipErrorNotSupported;
 }
 
-hipError_t launch_zero2(void* p1, long long bytes1, void* p2, long long bytes2, hipStream_t st) {
-  if ((uintptr_t)p1 % 16 || (uintptr_t)p2 % 16 || bytes1 % 16 || bytes2 % 16) return hipErrorInvalidValue;
-  const long long n1 = bytes1 / 16, n2 = bytes2 / 16;
-  if (n1 + n2 <= 0) return hipSuccess;
-  const int blocks = (int)((n1 + n2 + 255) / 256);
-  hipLaunchKernelGGL(zero2_kernel, dim3(blocks), dim3(256), 0, st, (uint4*)p1, n1, (uint4*)p2, n2);
+hipError_t launch_zero(const ZeroRanges& r, hipStream_t st) {
+  ZeroUnits z{};
+  long long total = 0;
+  for (int i = 0; i < kZeroRanges; ++i) {
+    if (r.bytes[i] <= 0) continue;
+    if ((uintptr_t)r.p[i] % 16 || r.bytes[i] % 16) return hipErrorInvalidValue;
+    z.p[i] = (uint4*)r.p[i];
+    z.n[i] = r.bytes[i] / 16;
+    total += z.n[i];
+  }
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, z);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const void* p, long long n16, int dtype, unsigned* err, hipStream_t st) {
+  if (n16 <= 0) return hipSuccess;
+  const long long blocks = std::min<long long>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(check_finite_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)p, n16,
+                     dtype == 1 ? 1 : 0, err);
   return hipGetLastError();
 }
 

@@ -56,8 +56,22 @@ struct Launch {
   int S;          // single-read scoring: positions per workgroup per round
   int rounds;     // single-read scoring: rounds over all segments
   int seg_size;   // selection: positions per emit workgroup (multiple of 2048)
+  unsigned* err;  // error flags of the call (the workspace header word), or nullptr
   Seg seg[kMaxSegs];
 };
+
+// Error flags of a call, ORed into Launch::err.
+enum : unsigned {
+  kErrExchangeWait = 1u,  // single-read scoring: a wait for another workgroup's statistics timed out
+  kErrLdsWait = 2u,       // single-read scoring: a wait between the waves of a workgroup timed out
+  kErrSelectWait = 4u,    // selection: a wait for another workgroup's histogram or counts timed out
+  kErrNonFinite = 8u,     // a non-finite input (validating mode) or a non-finite or zero row normaliser
+};
+__device__ inline void raise_error(unsigned* err, unsigned bit) {
+  if (err != nullptr) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A window row's statistics are usable: finite maximum, finite positive normaliser.
+__device__ inline bool stats_ok(float m, float z) { return isfinite(m) && isfinite(z) && z > 0.f; }
 
 // Segment holding `item` given the per-segment start field (sorted ascending).
 template <int Field>
@@ -206,9 +220,17 @@ __host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* exchange,
                                 unsigned* status, float* votes, float* row_stats, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
-// Zero [p1, p1 + bytes1) and [p2, p2 + bytes2) in one launch (16-byte
-// aligned pointers and sizes, else hipErrorInvalidValue).
-hipError_t launch_zero2(void* p1, long long bytes1, void* p2, long long bytes2, hipStream_t st);
+// Zero up to kZeroRanges byte ranges in one launch (16-byte aligned pointers
+// and sizes, else hipErrorInvalidValue; empty ranges are skipped).
+constexpr int kZeroRanges = 3;
+struct ZeroRanges {
+  void* p[kZeroRanges];
+  long long bytes[kZeroRanges];
+};
+hipError_t launch_zero(const ZeroRanges& r, hipStream_t st);
+// Validating mode: sets kErrNonFinite in *err if any of the n 16-byte units
+// at p holds a non-finite value of the element type (dtype 1: bf16, 0: fp32).
+hipError_t launch_check_finite(const void* p, long long n16, int dtype, unsigned* err, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);

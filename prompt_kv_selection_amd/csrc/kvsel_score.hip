@@ -470,6 +470,7 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
       mm = kNegBig;
       for (int grp = 0; grp < G; ++grp) lse_merge(mm, zz, s_gm[grp * W + t], s_gz[grp * W + t]);
       iz = 1.f / zz;
+      if (write_stats && !stats_ok(mm, zz)) raise_error(a.err, kErrNonFinite);
       if (row_stats != nullptr && write_stats) {
         float* rs = row_stats + (((long long)s.b * a.heads + h) * W + t) * 2;
         rs[0] = mm * kLn2;
@@ -524,7 +525,9 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
         if ((int)threadIdx.x < RB * 32) {
           const int i = threadIdx.x;
           const bool row = i < W;
-          s_m[i] = row ? lse[((long long)s.b * a.heads + it.h) * W + i] * kLog2e : 0.f;
+          const float l = row ? lse[((long long)s.b * a.heads + it.h) * W + i] : 0.f;
+          if (row && it.c == 0 && !isfinite(l)) raise_error(a.err, kErrNonFinite);
+          s_m[i] = l * kLog2e;
           s_iz[i] = row ? 1.f : 0.f;
         }
         __syncthreads();

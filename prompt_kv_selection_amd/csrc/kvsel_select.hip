@@ -844,7 +844,7 @@ __device__ void coop_wait(const unsigned long long* p, int n, unsigned* err) {
         ok = ok && __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0ull;
       if (__ballot(!ok) == 0) break;
       if (++spins > (1L << 22)) {
-        if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) raise_error(err, kErrSelectWait);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -869,7 +869,7 @@ __device__ void coop_read_hist(const uint32_t* gh, int nb, uint32_t total, uint3
     (void)block_scan<NT>(part, sh, sum);
     if (sum == total) break;
     if (++spins > (1L << 20)) {
-      if (threadIdx.x == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) raise_error(err, kErrSelectWait);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -986,7 +986,7 @@ __device__ void coop_read_candidates(const unsigned long long* cnt, int nseg, co
     (void)block_scan<kCoopThreads>(missing, sh, total);
     if (total == 0) break;
     if (++spins > (1L << 20)) {
-      if (tid == 0) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) raise_error(err, kErrSelectWait);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -1124,7 +1124,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
       if (!(go && digit == 0)) coop_local_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist);  // else done
       coop_push_hist(bits, hist, gh, go && digit == 0 ? s_ret : nullptr);
     }
-    coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, status);
+    coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, a.err);
     pick_digit<kCoopThreads>(hist, 1 << bits, need, sh, &s_digit, &s_need);
     total = hist[s_digit];
     prefix = (prefix << bits) | s_digit;
@@ -1168,7 +1168,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     }
     __syncthreads();  // sv becomes the candidate keys
     KVSEL_SELROWS_MARK(3);
-    coop_read_candidates(cnt, nseg, cbuf, (int)total, s_cw, ck, sh, status);
+    coop_read_candidates(cnt, nseg, cbuf, (int)total, s_cw, ck, sh, a.err);
     KVSEL_SELROWS_MARK(4);
     // The last two digits of tau over the candidates, in LDS.
     for (int digit = 1; digit < 3; ++digit) {
@@ -1229,7 +1229,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     KVSEL_SELROWS_MARK(5);
-    coop_wait(cnt, nseg, status);
+    coop_wait(cnt, nseg, a.err);
     KVSEL_SELROWS_MARK(6);
   }
 

@@ -41,14 +41,14 @@ def test_version_and_error_string(B):
 
 def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
-    # two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
+    # header (error flags), two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
     # selection threshold and per-segment counts, single-read exchange slots
     # (per head and 512-position chunk),
     # status words (error flags, decision, fallback counter and 16 arrival
     # counters on lines of their own), first-digit histograms, the
     # cooperative selection's status words and per-row words (histograms,
     # segment counts, candidate entries)
-    expect_min = (2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
+    expect_min = (256 + 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
                   + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128 + 8192) * 4)
     assert expect_min <= n <= expect_min + 7 * 256
     assert n % 256 == 0
@@ -147,15 +147,26 @@ def test_step_entry_point_errors(B):
     assert lib.kvsel_gather(FAKE, FAKE, FAKE, 20, 4, 100, 20, 128, 3, FAKE, FAKE, None) == -1
 
 
+def test_status_entry_point_errors(B):
+    assert B.lib.kvsel_status(None, None) == -1
+    assert B.lib.kvsel_status(ctypes.c_void_p(0x10010), None) == -1 and "aligned" in B.kvsel_last_error()
+    assert B.KVSEL_ENONFINITE == -5
+
+
 def test_options(B):
     lib = B.lib
+    assert lib.kvsel_get_option(2) == 0                       # validating mode off
+    assert lib.kvsel_set_option(2, 3) == -1
+    assert lib.kvsel_set_option(2, 1) == 0 and lib.kvsel_get_option(2) == 1
+    assert lib.kvsel_set_option(2, 0) == 0 and lib.kvsel_get_option(2) == 0
     assert lib.kvsel_get_option(0) == 0
     assert lib.kvsel_set_option(0, 3) == -1
     assert lib.kvsel_get_option(1) == 0                       # forced fallback off
     assert lib.kvsel_set_option(1, 2) == -1
     assert lib.kvsel_set_option(1, 1) == 0 and lib.kvsel_get_option(1) == 1
     assert lib.kvsel_set_option(1, 0) == 0 and lib.kvsel_get_option(1) == 0
-    assert lib.kvsel_set_option(2, 0) == -1
+    assert lib.kvsel_set_option(4, 0) == -1
     assert lib.kvsel_get_option(5) == -1
+    assert lib.kvsel_set_option(3, 0) == -1
     assert lib.kvsel_set_option(0, 1) == 0 and lib.kvsel_get_option(0) == 1
     assert lib.kvsel_set_option(0, 0) == 0 and lib.kvsel_get_option(0) == 0
