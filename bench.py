@@ -34,14 +34,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_alg_bytes(name, w, nch, lse=False):
+def kernel_alg_bytes(name, w, nch, lse=False, group=1):
     """Algorithmic bytes one launch of a kernel moves for one layer call
     (lse: the row statistics are handed over, so only the prefix keys, Qwin
-    and the W log-sum-exps per head are read for the votes)."""
+    and the W log-sum-exps per head are read for the votes; group: query
+    heads per K/V head, whose K is read once for the whole group)."""
     e = 2 if w.dtype == "bf16" else 4
     H, L, W, C, D = w.heads, w.L, w.W, w.C, w.D
     P = L - W
     q = H * W * D * e
+    if group > 1:
+        Hkv = H // group
+        if name == "window_stats":      # K of every K/V head once, Qwin, partials
+            return Hkv * L * D * e + q + H * nch * W * 8
+        if name == "window_votes":      # prefix K of every K/V head, Qwin, partials (or lse), votes out
+            return Hkv * P * D * e + q + (H * W * 4 if lse else H * nch * W * 8) + H * P * 4
     if lse and name in ("window_fused", "window_votes"):
         return H * P * D * e + q + H * W * 4 + H * P * 4
     if name == "window_fused":      # K once, Qwin, votes out (partials are noise)
@@ -63,11 +70,11 @@ def kernel_alg_bytes(name, w, nch, lse=False):
     return None                     # fill: workspace clearing, not the method's traffic
 
 
-def path_alg_bytes(w):
-    """Minimum bytes of the whole path per layer call: K once, Qwin, the
-    kept K/V rows read and written, the indices."""
+def path_alg_bytes(w, group=1):
+    """Minimum bytes of the whole path per layer call: K of every K/V head
+    once, Qwin, the kept K/V rows read and written, the indices."""
     e = 2 if w.dtype == "bf16" else 4
-    return w.heads * (w.L * w.D * e + w.W * w.D * e + 4 * w.C * w.D * e + 4 * w.C)
+    return (w.heads // group) * w.L * w.D * e + w.heads * (w.W * w.D * e + 4 * w.C * w.D * e + 4 * w.C)
 
 
 # Sources each kernel is compiled from: stored counter bytes stay valid while
@@ -162,6 +169,9 @@ def main():
     ap.add_argument("--lse", action="store_true",
                     help="row statistics handed over (kvsel_select_lse), as prefill attention would; each "
                          "layer's log-sum-exps come from one untimed call of the full path")
+    ap.add_argument("--gqa", type=int, default=1,
+                    help="query heads per K/V head: the layer's K/V has heads / GQA heads, each streamed once for "
+                         "its group (kvsel_select_gqa)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -189,9 +199,17 @@ def main():
 
     log(f"drawing {layers} layer(s) of {w.name}")
     t0 = time.time()
+    G = args.gqa
+    if G < 1 or H % G:
+        raise SystemExit(f"--gqa must divide the {H} heads")
+    Hkv = H // G
     Qs, Ks, Vs = [], [], []
     for layer in range(layers):
-        Q, K, V = WL.layer_arrays(w, layer=layer)
+        if G > 1:  # K/V of the K/V heads only; Qwin of every query head
+            _, K, V = WL.layer_arrays(w, layer=layer, heads=range(Hkv))
+            Q, _, _ = WL.layer_arrays(WL.reduced(w, L=W, C=W + 1), layer=layer)
+        else:
+            Q, K, V = WL.layer_arrays(w, layer=layer)
         conv = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)) if w.dtype == "bf16" else \
             (lambda a: torch.from_numpy(a))
         Qs.append(conv(Q).to(dev))
@@ -201,7 +219,8 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs resident in HBM after {time.time() - t0:.1f} s")
 
-    ws = torch.empty(B.kvsel_workspace_bytes(H, L, W, C, D, td), dtype=torch.uint8, device=dev)
+    ws_bytes = B.kvsel_gqa_workspace_bytes(H, Hkv, L, W, C, D, td)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     idx = [torch.empty((H, C), dtype=torch.int32, device=dev) for _ in range(layers)]
     Ko = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
     Vo = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
@@ -212,15 +231,19 @@ def main():
     if args.lse:
         rs = torch.empty((H, W, 2), dtype=torch.float32, device=dev)
         for layer in range(layers):
-            B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, H, w.kernel, w.pooling, td,
-                           idx[layer], Ko[layer], Vo[layer], rs, None, None, ws, stream=stream)
+            B.kvsel_select_gqa(Qs[layer], Ks[layer], Vs[layer], None, L, W, C, D, H, Hkv, w.kernel, w.pooling, td,
+                               idx[layer], Ko[layer], Vo[layer], rs, None, None, ws, stream=stream)
             lses.append((rs[:, :, 0].double() + rs[:, :, 1].double().log()).float().contiguous())
         torch.cuda.synchronize()
         log("row log-sum-exps of every layer ready")
 
     def step():
         for layer in range(layers):
-            if args.lse:
+            if G > 1:
+                B.kvsel_select_gqa(Qs[layer], Ks[layer], Vs[layer], lses[layer] if args.lse else None, L, W, C, D, H,
+                                   Hkv, w.kernel, w.pooling, td, idx[layer], Ko[layer], Vo[layer], None, None, None,
+                                   ws, stream=stream)
+            elif args.lse:
                 B.kvsel_select_lse(Qs[layer], Ks[layer], Vs[layer], lses[layer], L, W, C, D, H, w.kernel,
                                    w.pooling, td, idx[layer], Ko[layer], Vo[layer], None, None, ws, stream=stream)
             else:
@@ -266,16 +289,16 @@ def main():
     nch = (L + 1023) // 1024
     kern = {}
     for name, (n, ms) in per_kernel.items():
-        ab = kernel_alg_bytes(name, w, nch, args.lse)
+        ab = kernel_alg_bytes(name, w, nch, args.lse, G)
         avg = ms / n
         kern[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
                       "alg_GBps": None if ab is None else round(ab / (avg / 1e3) / 1e9, 1)}
     dom = max((k for k in per_kernel if kernel_alg_bytes(k, w, nch) is not None), key=lambda k: per_kernel[k][1])
     n_dom, ms_dom = per_kernel[dom]
-    ab_dom = kernel_alg_bytes(dom, w, nch, args.lse)
+    ab_dom = kernel_alg_bytes(dom, w, nch, args.lse, G)
     achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
-    traffic = traffic_from_profiles(dom + "_lse" if args.lse else dom)
-    path_gbps = path_alg_bytes(w) * layers / (ms_step / 1e3) / 1e9
+    traffic = None if G > 1 else traffic_from_profiles(dom + "_lse" if args.lse else dom)
+    path_gbps = path_alg_bytes(w, G) * layers / (ms_step / 1e3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -292,10 +315,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": layers, "heads": H, "L": L, "W": W, "C": C, "D": D,
                    "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys,
-                   "scoring": args.scoring, "row_stats": "handed_over" if args.lse else "computed"},
+                   "scoring": args.scoring, "row_stats": "handed_over" if args.lse else "computed",
+                   "kv_heads": Hkv},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
-        "path": {"alg_bytes_per_layer": path_alg_bytes(w), "alg_GBps": round(path_gbps, 1),
+        "path": {"alg_bytes_per_layer": path_alg_bytes(w, G), "alg_GBps": round(path_gbps, 1),
                  "frac_of_peak": round(path_gbps / HBM_PEAK_GBPS, 4),
                  "ms_per_step_with_kernel_events": round(ms_events / args.steps, 4)},
         "kernels": kern,

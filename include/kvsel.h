@@ -179,6 +179,30 @@ int kvsel_select_lse(const void* Qwin, const void* K, const void* V, const float
                      float* votes_opt, float* pooled_opt,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Grouped-query attention: q_heads query heads served by kv_heads K/V heads
+ * (group G = q_heads / kv_heads).  The model's integration expands K/V to the
+ * query heads before compressing each query head on its own [section "under
+ * GQA the saving is not just C divided by L"]; this computes exactly that
+ * result (query head h reads K/V head h / G, consecutive query heads sharing
+ * one, as repeat_kv expands them), but streams each K/V head once for the
+ * whole group instead of once per query head.
+ *   Qwin    [q_heads][W][D]; K, V [kv_heads][L][D]
+ *   indices [q_heads][C]; K_out, V_out [q_heads][C][D] (the expanded cache)
+ *   row_lse_opt [q_heads][W] handed-over statistics (as for kvsel_select_lse),
+ *           or NULL (then they are computed: two passes over each K/V head);
+ *           row_stats_opt must be NULL when row_lse_opt is given
+ *   row_stats_opt [q_heads][W][2], votes_opt / pooled_opt [q_heads][L-W] or NULL
+ * Rules: q_heads a positive multiple of kv_heads >= 1; with G > 1, W a
+ * multiple of 32 and G * W <= 128 (else KVSEL_EUNSUPPORTED).  Every other
+ * argument as for kvsel_select.  Workspace: kvsel_gqa_workspace_bytes(...). */
+size_t kvsel_gqa_workspace_bytes(int q_heads, int kv_heads, int L, int W, int C, int D, int dtype);
+int kvsel_select_gqa(const void* Qwin, const void* K, const void* V, const float* row_lse_opt,
+                     int L, int W, int C, int D, int q_heads, int kv_heads,
+                     int kernel, int pooling, int dtype,
+                     int32_t* indices, void* K_out, void* V_out,
+                     float* row_stats_opt, float* votes_opt, float* pooled_opt,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for kvsel_select_varlen; 0 on invalid arguments. */
 size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B,
                                     int heads, int W, int D, int dtype);

@@ -268,6 +268,35 @@ def snapkv_select_lse(qwin, keys, values, row_lse, W: int, C: int, kernel: int =
     return {"indices": idx, "keys": keys[idx], "values": values[idx], "votes": votes, "pooled": pooled}
 
 
+def snapkv_select_gqa(qwin, keys, values, W: int, C: int, kernel: int = 3, pooling: str = "avg",
+                      row_lse=None) -> List[Dict]:
+    """Grouped-query attention: qwin [H_q, W, D] against keys/values
+    [H_kv, L, D], group G = H_q / H_kv.  The integration the page describes
+    expands K/V to the H_q query heads before compressing each query head on
+    its own (section "under GQA the saving is not just C divided by L"), so
+    query head h selects with key/value head h // G (consecutive query heads
+    share one, as the repetition expands them).  row_lse: None, or [H_q, W]
+    handed-over statistics (snapkv_select_lse).  Returns one result per
+    query head."""
+    Hq, Hkv = len(qwin), len(keys)
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a positive multiple of the key/value heads")
+    G = Hq // Hkv
+    if row_lse is None:
+        return [snapkv_select(qwin[h], keys[h // G], values[h // G], W, C, kernel, pooling) for h in range(Hq)]
+    return [snapkv_select_lse(qwin[h], keys[h // G], values[h // G], row_lse[h], W, C, kernel, pooling)
+            for h in range(Hq)]
+
+
+def expanded_cache_ratio(q_heads: int, kv_heads: int, L: int, C: int, g: int) -> float:
+    """Persistent K/V of the expanded selection (every query head keeps
+    min(L, C) prompt positions plus g generated tokens) over the native
+    grouped full cache (kv_heads heads of L + g positions); batch, layers,
+    head dimension and element size cancel (section "under GQA the saving is
+    not just C divided by L")."""
+    return q_heads * (min(L, C) + g) / (kv_heads * (L + g))
+
+
 def snapkv_select_heads(qwin, keys, values, W: int, C: int, kernel: int = 3,
                         pooling: str = "avg", heads: Sequence[int] | None = None) -> List[Dict]:
     """Independent selection per head (section "the prompt cache shrinks, the

@@ -56,6 +56,11 @@ lib.kvsel_select_lse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
 lib.kvsel_select_varlen_lse.restype = _i
 lib.kvsel_select_varlen_lse.argtypes = [_vp, _vp, _vp, _vp, _i32p, _i32p, _i, _i, _i, _i, _i, _i, _i,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_gqa_workspace_bytes.restype = _sz
+lib.kvsel_gqa_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+lib.kvsel_select_gqa.restype = _i
+lib.kvsel_select_gqa.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.kvsel_topk_workspace_bytes.restype = _sz
 lib.kvsel_topk_workspace_bytes.argtypes = [_i, _i]
 lib.kvsel_topk.restype = _i
@@ -158,6 +163,23 @@ def kvsel_select_varlen_lse(Qwin, K, V, row_lse, cu_L, C, W, D, heads, kernel, p
                                        _i32_array(C), len(C), W, D, heads, kernel, POOL.get(pooling, pooling),
                                        DTYPE.get(dtype, dtype), _ptr(indices), _ptr(K_out), _ptr(V_out),
                                        _ptr(votes), _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_gqa_workspace_bytes(q_heads: int, kv_heads: int, L: int, W: int, C: int, D: int, dtype) -> int:
+    n = lib.kvsel_gqa_workspace_bytes(q_heads, kv_heads, L, W, C, D, DTYPE.get(dtype, dtype))
+    if n == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return n
+
+
+def kvsel_select_gqa(Qwin, K, V, row_lse, L, W, C, D, q_heads, kv_heads, kernel, pooling, dtype, indices, K_out,
+                     V_out, row_stats=None, votes=None, pooled=None, workspace=None, workspace_bytes=None,
+                     stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_select_gqa(_ptr(Qwin), _ptr(K), _ptr(V), _ptr(row_lse), L, W, C, D, q_heads, kv_heads, kernel,
+                                POOL.get(pooling, pooling), DTYPE.get(dtype, dtype), _ptr(indices), _ptr(K_out),
+                                _ptr(V_out), _ptr(row_stats), _ptr(votes), _ptr(pooled), _ptr(workspace), ws_bytes,
+                                _stream(stream)))
 
 
 def kvsel_topk_workspace_bytes(rows: int, n: int) -> int:

@@ -76,6 +76,7 @@ int check_pool(int kernel, int pooling) {
 // Per-sequence layout of a (possibly ragged) batch.
 struct Plan {
   int B = 0, heads = 0, W = 0, D = 0, dtype = 0;
+  int group = 1;              // query heads per K/V head
   std::vector<int> L, C, nch, fc;
   std::vector<long long> cuL, cuC, cuP, part, fpart;  // exclusive prefix sums
   int fS = 0;                 // single-read scoring: positions per workgroup per round
@@ -98,11 +99,19 @@ int g_scoring = KVSEL_SCORING_AUTO;
 int g_force_fallback = 0;
 int g_validate = 0;
 
-int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p) {
+int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p,
+              int kv_heads = 0) {
   if (cu_L == nullptr || C_host == nullptr) return fail(KVSEL_EINVAL, "cu_L_host and C_host must not be NULL");
   if (B < 1) return fail(KVSEL_EINVAL, "batch B must be >= 1 (got %d)", B);
   int rc = check_shape(heads, W, D, dtype);
   if (rc) return rc;
+  if (kv_heads == 0) kv_heads = heads;
+  if (kv_heads < 1 || heads % kv_heads != 0)
+    return fail(KVSEL_EINVAL, "query heads %d must be a positive multiple of the K/V heads %d", heads, kv_heads);
+  p.group = heads / kv_heads;
+  if (p.group > 1 && (W % 32 != 0 || p.group * W > 128))
+    return fail(KVSEL_EUNSUPPORTED, "grouped heads need W a multiple of 32 and group * W <= 128 (group %d, W %d)",
+                p.group, W);
   if (cu_L[0] != 0) return fail(KVSEL_EINVAL, "cu_L[0] must be 0 (got %d)", cu_L[0]);
   p.B = B;
   p.heads = heads;
@@ -118,7 +127,7 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   p.part.assign(B + 1, 0);
   p.fpart.assign(B + 1, 0);
   p.fc.resize(B);
-  p.fS = fused_positions(W, D);
+  p.fS = p.group == 1 ? fused_positions(W, D) : 0;  // grouped heads: two-pass scoring
   for (int b = 0; b < B; ++b) {
     const long long L = (long long)cu_L[b + 1] - cu_L[b];
     const int C = C_host[b];
@@ -132,7 +141,7 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
     p.cuL[b + 1] = p.cuL[b] + L;
     p.cuC[b + 1] = p.cuC[b] + C;
     p.cuP[b + 1] = p.cuP[b] + (L - W);
-    p.part[b + 1] = p.part[b] + (long long)heads * p.nch[b];
+    p.part[b + 1] = p.part[b] + (long long)(heads / p.group) * p.nch[b];
     p.fc[b] = (L < C || p.fS == 0) ? 0 : (int)((L + p.fS - 1) / p.fS);
     p.fpart[b + 1] = p.fpart[b] + (long long)heads * fused_slot_stride(p.fc[b]);
   }
@@ -140,10 +149,10 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   p.part_slots = p.part[B];
   p.vote_elems = (long long)heads * p.cuP[B];
   size_t off = kHeaderBytes;
-  p.off_pm = off;
-  off = align256(off + (size_t)p.part_slots * W * sizeof(float));
+  p.off_pm = off;  // partial slots per (sequence, K/V head, chunk), group * W rows each
+  off = align256(off + (size_t)p.part_slots * p.group * W * sizeof(float));
   p.off_pz = off;
-  off = align256(off + (size_t)p.part_slots * W * sizeof(float));
+  off = align256(off + (size_t)p.part_slots * p.group * W * sizeof(float));
   p.off_votes = off;
   off = align256(off + (size_t)p.vote_elems * sizeof(float));
   p.off_pooled = off;
@@ -175,6 +184,7 @@ Launch base_launch(const Plan& p, int kernel, int pooling) {
   a.window = 1;
   a.scale2 = (float)(1.4426950408889634074 / sqrt((double)p.D));
   a.err = nullptr;
+  a.group = p.group;
   return a;
 }
 
@@ -302,7 +312,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     // Validating mode: every input element of every sequence is finite.
     const size_t esz = p.dtype == KVSEL_BF16 ? 2 : 4;
     const long long q16 = (long long)p.B * p.heads * p.W * p.D * (long long)esz / 16;
-    const long long kv16 = (long long)p.heads * p.cuL[p.B] * p.D * (long long)esz / 16;
+    const long long kv16 = (long long)(p.heads / p.group) * p.cuL[p.B] * p.D * (long long)esz / 16;
     hipError_t e = timed("check", st, [&] {
       hipError_t r = launch_check_finite(Q, q16, p.dtype, err, st);
       if (r == hipSuccess) r = launch_check_finite(K, kv16, p.dtype, err, st);
@@ -338,7 +348,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       s.idx_ld = s.C;
       s.out_ld = s.C;
       s.vote_ld = s.L - p.W;
-      s.kv_off = (long long)p.heads * p.cuL[b] * p.D;
+      s.kv_off = (long long)(p.heads / p.group) * p.cuL[b] * p.D;
       s.idx_off = (long long)p.heads * p.cuC[b];
       s.out_off = s.idx_off;
       s.vote_off = (long long)p.heads * p.cuP[b];
@@ -349,7 +359,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       s.fnr = s.fhpr > 0 ? (s.nh + s.fhpr - 1) / s.fhpr : 0;
       s.fr0 = a.rounds;
       a.rounds += s.fnr;
-      items += s.nh * s.nch;
+      items += (s.nh / p.group) * s.nch;  // scoring items run over the K/V heads
       rows += s.nh;
       if (s.L >= s.C) maxP = std::max(maxP, s.L - p.W);
       maxN = std::max(maxN, s.L >= s.C ? s.L - p.W : s.L);
@@ -493,6 +503,19 @@ size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_h
   return p.bytes;
 }
 
+size_t kvsel_gqa_workspace_bytes(int q_heads, int kv_heads, int L, int W, int C, int D, int dtype) {
+  if (kv_heads < 1) {
+    fail(KVSEL_EINVAL, "kv_heads must be >= 1 (got %d)", kv_heads);
+    return 0;
+  }
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  Plan p;
+  if (make_plan(cu, c, 1, q_heads, W, D, dtype, p, kv_heads) != KVSEL_OK) return 0;
+  ok();
+  return p.bytes;
+}
+
 size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype) {
   const int32_t cu[2] = {0, L};
   const int32_t c[1] = {C};
@@ -503,9 +526,9 @@ static int select_entry(const void* Qwin, const void* K, const void* V, const fl
                         const int32_t* cu_L_host, const int32_t* C_host, int B, int W, int D, int heads, int kernel,
                         int pooling, int dtype, int32_t* indices, void* K_out, void* V_out, float* row_stats_opt,
                         float* votes_opt, float* pooled_opt, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, int kv_heads = 0) {
   Plan p;
-  int rc = make_plan(cu_L_host, C_host, B, heads, W, D, dtype, p);
+  int rc = make_plan(cu_L_host, C_host, B, heads, W, D, dtype, p, kv_heads);
   if (rc) return rc;
   if ((rc = check_pool(kernel, pooling))) return rc;
   if (!Qwin || !K || !V || !indices || !K_out || !V_out)
@@ -540,6 +563,20 @@ int kvsel_select_varlen_lse(const void* Qwin, const void* K, const void* V, cons
   if ((uintptr_t)row_lse % 4) return fail(KVSEL_EINVAL, "row_lse must be 4-byte aligned");
   return select_entry(Qwin, K, V, row_lse, cu_L_host, C_host, B, W, D, heads, kernel, pooling, dtype, indices,
                       K_out, V_out, nullptr, votes_opt, pooled_opt, workspace, workspace_bytes, stream);
+}
+
+int kvsel_select_gqa(const void* Qwin, const void* K, const void* V, const float* row_lse_opt, int L, int W, int C,
+                     int D, int q_heads, int kv_heads, int kernel, int pooling, int dtype, int32_t* indices,
+                     void* K_out, void* V_out, float* row_stats_opt, float* votes_opt, float* pooled_opt,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_heads < 1) return fail(KVSEL_EINVAL, "kv_heads must be >= 1 (got %d)", kv_heads);
+  if (row_lse_opt && (uintptr_t)row_lse_opt % 4) return fail(KVSEL_EINVAL, "row_lse must be 4-byte aligned");
+  if (row_lse_opt && row_stats_opt)
+    return fail(KVSEL_EINVAL, "row statistics are not computed when they are handed over (row_lse)");
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  return select_entry(Qwin, K, V, row_lse_opt, cu, c, 1, W, D, q_heads, kernel, pooling, dtype, indices, K_out,
+                      V_out, row_stats_opt, votes_opt, pooled_opt, workspace, workspace_bytes, stream, kv_heads);
 }
 
 int kvsel_select_lse(const void* Qwin, const void* K, const void* V, const float* row_lse, int L, int W, int C,

@@ -21,11 +21,13 @@ constexpr int kPoolBlock = 256;
 
 struct Seg {
   int b;          // sequence index (Q and row-stat offsets)
+  // Heads below are query heads; scoring items and K/V run over the K/V
+  // heads (Launch::group query heads each).
   int L;          // prompt length
   int C;          // budget (includes the window); L < C means bypass
   int nout;       // rows to emit per head: min(L, C), or the gather count
   int h0, nh;     // head range
-  int nch;        // scoring chunks per head, ceil(L / kChunk)
+  int nch;        // scoring chunks per K/V head, ceil(L / kChunk)
   int item0;      // first scoring workgroup of this segment in the launch
   int row0;       // first (segment, head) row of this segment in the launch
   int gitem0;     // first gather workgroup of this segment in the launch
@@ -33,11 +35,11 @@ struct Seg {
   int idx_ld;     // indices between heads
   int out_ld;     // K_out / V_out rows between heads
   int vote_ld;    // votes / pooled floats between heads
-  long long kv_off;    // element offset of (b, head 0, row 0) in K and V
+  long long kv_off;    // element offset of (b, K/V head 0, row 0) in K and V
   long long idx_off;   // element offset of (b, head 0) in indices
   long long out_off;   // row offset of (b, head 0) in K_out / V_out
   long long vote_off;  // element offset of (b, head 0) in votes / pooled
-  long long part_base; // two-pass partial-stat slot of (b, head 0, chunk 0)
+  long long part_base; // two-pass partial-stat slot of (b, K/V head 0, chunk 0); a slot has group_rows rows
   long long fslot_base;  // single-read exchange slot of (b, head 0, chunk 0)
   // single-read scoring schedule (see kvsel_fused.hip)
   int fc;         // chunks per head, ceil(L / S)
@@ -57,8 +59,15 @@ struct Launch {
   int rounds;     // single-read scoring: rounds over all segments
   int seg_size;   // selection: positions per emit workgroup (multiple of 2048)
   unsigned* err;  // error flags of the call (the workspace header word), or nullptr
+  int group;      // query heads per K/V head (grouped-query attention); 0 or 1: one each
   Seg seg[kMaxSegs];
 };
+
+// The K/V head that query head h (of a segment) reads: consecutive query
+// heads share one K/V head, group at a time (as repeat_kv expands them).
+__host__ __device__ inline int kv_head(const Launch& a, int h) { return a.group > 1 ? h / a.group : h; }
+// Window rows scored together against one K/V head: the group's query heads.
+__host__ __device__ inline int group_rows(const Launch& a) { return (a.group > 1 ? a.group : 1) * a.W; }
 
 // Error flags of a call, ORed into Launch::err.
 enum : unsigned {

@@ -193,20 +193,21 @@ template <typename T, int D, int RB>
 __device__ __forceinline__ void issue_queries(const Launch& a, const Seg& s, int h, const T* __restrict__ Q,
                                               uint4 (*qt)[TileGeom<T, D>::PIECES], const TileOffsets<T, D>& off,
                                               int wave, int lane) {
-  if (wave < RB) {
-    const T* q = Q + ((long long)s.b * a.heads + h) * (long long)a.W * D + (long long)wave * 32 * D;
-    issue_tile<T, D>(q, min(32, a.W - wave * 32), off, qt[wave], lane);
+  if (wave < RB) {  // the group's query heads are consecutive: one block of group_rows rows
+    const long long qh = (long long)s.b * a.heads + (long long)h * (a.group > 1 ? a.group : 1);
+    const T* q = Q + qh * (long long)a.W * D + (long long)wave * 32 * D;
+    issue_tile<T, D>(q, min(32, group_rows(a) - wave * 32), off, qt[wave], lane);
   }
 }
 
-// Operands of the staged Qwin; rows past W are zero.
+// Operands of the staged Qwin; rows past group_rows are zero.
 template <typename T, int D, int RB>
 __device__ __forceinline__ void queries_from_lds(const Launch& a, const uint4 (*qt)[TileGeom<T, D>::PIECES], int n,
                                                  int g, Operands<T, D> (&qa)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     qa[rb].from_tile(qt[rb], n, g);
-    if (rb * 32 + n >= a.W) qa[rb].zero();
+    if (rb * 32 + n >= group_rows(a)) qa[rb].zero();
   }
 }
 
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
   __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
   __shared__ float sm[2][kWaves][RB * 32], sz[2][kWaves][RB * 32];
-  const int W = a.W;
+  const int W = a.W, R = group_rows(a);  // rows: window row i of the group's query head i / W
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
   int lo, hi;
@@ -337,7 +338,9 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
     zero[q] = 0u;
 
   Operands<T, D> qa[RB];
-  float m[RB][16], z[RB][16];  // this lane's running statistics of the current run
+  // This lane's running statistics of the current run: row n of each row
+  // block over the lane's half of every tile's positions.
+  float m[RB], z[RB];
   int runs = 0;
   for (int item = lo; item < hi; ++item) {
     const Item<T, D> it = locate_item<T, D, false>(a, K, item, wave);
@@ -352,12 +355,10 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
       // previous staging, and has since passed that run's final barrier.
       stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          m[rb][r] = kNegBig;
-          z[rb][r] = 0.f;
-        }
+      for (int rb = 0; rb < RB; ++rb) {
+        m[rb] = kNegBig;
+        z[rb] = 0.f;
+      }
     }
 
     for (int t = 0; t < it.nt; ++t) {
@@ -366,60 +367,70 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
       Operands<T, D> kt;
       kt.from_tile(ws.wait(), n, g);
       ws.release(a, K, wave, lane);  // the tile is in registers: refill its buffer now
-      // Rows i >= W hold zero queries and are never written, so only the
-      // causal bound j <= P + i masks, and only in tiles reaching past P.
+      // K.Q^T puts a lane on a window row (row n of the block) and its
+      // registers on positions p0 + acc_row(r, g), so the tile's maximum
+      // and sum of exponentials are lane-local, then merged into the run's
+      // statistics once per tile.  Rows past R hold zero queries and are
+      // never written, so only the causal bound (position <= P + window row)
+      // masks, and only in tiles reaching past P.  A row block lies within
+      // one query head (W is a multiple of 32 when heads are grouped).
       const bool full = p0 + 31 <= P;
+      (void)j;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const f32x16 acc = tile_dot<D>(qa[rb], kt);
+        f32x16 act = tile_dot<D>(kt, qa[rb]);
+        const int i = (rb * 32) % W + n;  // this lane's window row
+        float tm = kNegBig;
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = rb * 32 + acc_row(r, g);
-          float x = acc[r] * a.scale2;
-          if (!full && j > P + i) x = -INFINITY;
-          online_add(m[rb][r], z[rb][r], x);
+          for (int r = 0; r < 16; ++r) tm = fmaxf(tm, act[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jj = p0 + acc_row(r, g);
+            if (!(jj < L && jj <= P + i)) act[r] = -INFINITY;
+            tm = fmaxf(tm, act[r]);
+          }
         }
+        const float tms = tm * a.scale2;
+        float tz = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tz += exp2_fast(fmaf(act[r], a.scale2, -tms));
+        lse_merge(m[rb], z[rb], tms, tz);
       }
     }
 
-    const long long slot = (s.part_base + (long long)it.h * s.nch + it.c) * W;
+    const long long slot = (s.part_base + (long long)it.h * s.nch + it.c) * R;
     if (!last) {
       // The run's statistics go to its last chunk; the others hold the
       // neutral element of the merge.
-      if ((int)threadIdx.x < W) {
+      if ((int)threadIdx.x < R) {
         part_m[slot + threadIdx.x] = kNegBig;
         part_z[slot + threadIdx.x] = 0.f;
       }
       continue;
     }
 
-    // Across the 32 lanes of each half (same rows, different positions).
+    // Lane n and lane n + 32 hold the same row over the two halves of the
+    // positions: merged in that order.
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) {
-          const float mo = __shfl_xor(m[rb][r], off);
-          const float zo = __shfl_xor(z[rb][r], off);
-          lse_merge(m[rb][r], z[rb][r], mo, zo);
-        }
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mo = __shfl_xor(m[rb], 32), zo = __shfl_xor(z[rb], 32);
+      if (g == 0) lse_merge(m[rb], z[rb], mo, zo);
+    }
 
     // Run k uses buffer k & 1: the merge of run k happens before any wave
     // passes the barrier of run k + 1.
     const int pbuf = runs++ & 1;
-    if (n == 0) {
+    if (g == 0) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = rb * 32 + acc_row(r, g);
-          sm[pbuf][wave][i] = m[rb][r];
-          sz[pbuf][wave][i] = z[rb][r];
-        }
+      for (int rb = 0; rb < RB; ++rb) {
+        sm[pbuf][wave][rb * 32 + n] = m[rb];
+        sz[pbuf][wave][rb * 32 + n] = z[rb];
+      }
     }
     __syncthreads();
-    if ((int)threadIdx.x < W) {
+    if ((int)threadIdx.x < R) {
       const int i = threadIdx.x;
       float mm = sm[pbuf][0][i], zz = sz[pbuf][0][i];
 #pragma unroll
@@ -430,18 +441,22 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
   }
 }
 
-// Final (max, 1/sum) of every window row of head h from its nch partials,
-// into s_m / s_iz (rows W .. RB*32-1 get (0, 0): with zero queries their
-// logits are 0, so they add nothing).  Every thread of the workgroup takes
-// part: thread t < G*W (G = threads / W groups) merges row t % W over chunks
-// t / W, t / W + G, ...; the G results per row are then merged through LDS.
+// Final (max, 1/sum) of every row of K/V head h (R = group_rows rows) from
+// its nch partials, into s_m / s_iz (rows R .. RB*32-1 get (0, 0): with zero
+// queries their logits are 0, so they add nothing).  Thread t < G*R (G =
+// kMergeGroups) merges row t % R over chunks t / R, t / R + G, ...; the G
+// results per row are then merged through LDS.  The merge order depends on
+// the chunks only, not on R, so a row's statistics are the same whether its
+// query head is scored alone or with its group.
+constexpr int kMergeGroups = 2;
+static_assert(kMergeGroups * 128 <= kWaves * 64, "every row of a 128-row group has its threads");
 template <int RBW>
 __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, int h,
                                                const float* __restrict__ part_m, const float* __restrict__ part_z,
                                                float* __restrict__ row_stats, bool write_stats, float* s_gm,
                                                float* s_gz, float* s_m, float* s_iz) {
-  const int W = a.W, t = threadIdx.x;
-  const int G = (kWaves * 64) / W;
+  const int W = group_rows(a), t = threadIdx.x;  // W: rows of the slot here
+  const int G = kMergeGroups;
   const long long base = (s.part_base + (long long)h * s.nch) * W;
   if (t < G * W) {
     const int i = t % W, grp = t / W;
@@ -472,7 +487,8 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
       iz = 1.f / zz;
       if (write_stats && !stats_ok(mm, zz)) raise_error(a.err, kErrNonFinite);
       if (row_stats != nullptr && write_stats) {
-        float* rs = row_stats + (((long long)s.b * a.heads + h) * W + t) * 2;
+        // row t of the slot: window row t % a.W of query head h * group + t / a.W
+        float* rs = row_stats + (((long long)s.b * a.heads) * a.W + (long long)h * W + t) * 2;
         rs[0] = mm * kLn2;
         rs[1] = zz;
       }
@@ -497,7 +513,7 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
   __shared__ uint4 qt[RB][G::PIECES];
   __shared__ float s_m[RB * 32], s_iz[RB * 32];
   __shared__ float s_gm[kWaves * 64], s_gz[kWaves * 64];
-  const int W = a.W;
+  const int W = a.W, R = group_rows(a), Gq = a.group > 1 ? a.group : 1;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
   int lo, hi;
@@ -523,9 +539,9 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
         // Row log-sum-exps handed over by the caller: exp(l - lse) is the
         // probability itself, so M = lse * log2(e) and 1/Z = 1.
         if ((int)threadIdx.x < RB * 32) {
-          const int i = threadIdx.x;
-          const bool row = i < W;
-          const float l = row ? lse[((long long)s.b * a.heads + it.h) * W + i] : 0.f;
+          const int i = threadIdx.x;  // window row i % W of query head it.h * Gq + i / W
+          const bool row = i < R;
+          const float l = row ? lse[((long long)s.b * a.heads) * W + (long long)it.h * R + i] : 0.f;
           if (row && it.c == 0 && !isfinite(l)) raise_error(a.err, kErrNonFinite);
           s_m[i] = l * kLog2e;
           s_iz[i] = row ? 1.f : 0.f;
@@ -548,7 +564,8 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
       __syncthreads();
     }
 
-    float* vout = votes + s.vote_off + (long long)it.h * s.vote_ld;
+    // Votes of each query head of the group: its row blocks' sums.
+    float* vout = votes + s.vote_off + (long long)it.h * Gq * s.vote_ld;
     for (int t = 0; t < it.nt; ++t) {
       const int j = it.pb + t * 32 + n;
       Operands<T, D> kt;
@@ -562,11 +579,14 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) part += exp2_fast(acc[r] * a.scale2 - mr[rb][r]) * izr[rb][r];
         tot += part;
+        if (rb + 1 == RB || (Gq > 1 && ((rb + 1) * 32) % W == 0)) {  // the last row block of a query head
+          const float other = __shfl_xor(tot, 32);
+          // Same expression for every position: (half 0 rows) + (half 1 rows).
+          const float v = g == 0 ? tot + other : other + tot;
+          if (g == 0 && j < P) vout[(long long)((rb * 32) / W) * s.vote_ld + j] = v;
+          tot = 0.f;
+        }
       }
-      const float other = __shfl_xor(tot, 32);
-      // Same expression for every position: (half 0 rows) + (half 1 rows).
-      const float v = g == 0 ? tot + other : other + tot;
-      if (g == 0 && j < P) vout[j] = v;
     }
   }
 }
@@ -610,7 +630,7 @@ static hipError_t votes_t(const Launch& a, int items, const void* Q, const void*
 
 #define KVSEL_DISPATCH(FN, ...)                                                              \
   do {                                                                                       \
-    const int rb = (a.W + 31) / 32;                                                          \
+    const int rb = (group_rows(a) + 31) / 32;                                                \
     if (dtype == 1) {                                                                        \
       if (a.D == 128) {                                                                      \
         if (rb == 1) return FN<__bf16, 128, 1>(__VA_ARGS__);                                 \

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
   const int h = s.h0 + (row - s.row0);
   int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
-  const long long in_row0 = RU > 0 ? s.kv_off / a.D + (long long)h * s.L : 0;
+  const long long in_row0 = RU > 0 ? s.kv_off / a.D + (long long)kv_head(a, h) * s.L : 0;
   const long long out_row0 = RU > 0 ? s.out_off + (long long)h * s.out_ld : 0;
   const int segsz = a.seg_size;
   __shared__ int32_t src[kSegUnit];
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const Launch a, const uint4
   if (m >= s.nout) return;
   int src = idx[s.idx_off + (long long)h * s.idx_ld + m];
   src = min(max(src, 0), s.L - 1);  // never read outside the head's rows
-  const long long in_row = s.kv_off / a.D + (long long)h * s.L + src;
+  const long long in_row = s.kv_off / a.D + (long long)kv_head(a, h) * s.L + src;
   const long long out_row = s.out_off + (long long)h * s.out_ld + m;
   const uint4 kv = K[in_row * RU + part];
   const uint4 vv = V[in_row * RU + part];
@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
   const int h = s.h0 + (row - s.row0);
   int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
-  const long long in_row0 = s.kv_off / a.D + (long long)h * s.L;
+  const long long in_row0 = s.kv_off / a.D + (long long)kv_head(a, h) * s.L;
   const long long out_row0 = s.out_off + (long long)h * s.out_ld;
   // Output rows m0 .. m0 + n from source rows first + i (sel == nullptr)
   // or sel[i].

@@ -108,6 +108,23 @@ def test_lse_argument_errors(B):
     assert rc == -1 and "sequence 1" in B.kvsel_last_error()
 
 
+def test_gqa_argument_errors(B):
+    lib = B.lib
+    def gqa(q_heads=8, kv_heads=2, W=32, lse=None, rs=None, wsb=1 << 30):
+        return lib.kvsel_select_gqa(FAKE, FAKE, FAKE, lse, 4096, W, 512, 128, q_heads, kv_heads, 5, 0, 1, FAKE, FAKE,
+                                    FAKE, rs, None, None, FAKE, wsb, None)
+    assert gqa(kv_heads=0) == -1
+    assert gqa(kv_heads=3) == -1 and "multiple" in B.kvsel_last_error()
+    assert gqa(W=48) == -2                     # grouped heads need W a multiple of 32
+    assert gqa(q_heads=10, kv_heads=2) == -2   # group 5: 5 * 32 rows > 128
+    assert gqa(lse=FAKE, rs=FAKE) == -1
+    assert gqa(wsb=1024) == -3
+    assert lib.kvsel_gqa_workspace_bytes(8, 0, 4096, 32, 512, 128, 1) == 0
+    # grouped heads score on the two-pass path: no single-read exchange slots
+    assert 0 < lib.kvsel_gqa_workspace_bytes(8, 2, 4096, 32, 512, 128, 1) < lib.kvsel_workspace_bytes(8, 4096, 32, 512, 128, 1)
+    assert lib.kvsel_gqa_workspace_bytes(8, 8, 4096, 32, 512, 128, 1) == lib.kvsel_workspace_bytes(8, 4096, 32, 512, 128, 1)
+
+
 def test_varlen_argument_errors(B):
     lib = B.lib
     cu_bad = (ctypes.c_int32 * 3)(0, 5000, 4000)  # negative length

@@ -266,6 +266,39 @@ def test_row_lse_shift_scales_rows():
     np.testing.assert_allclose(one["votes"], base["votes"] - probs[2, : L - W] * (2 / 3), rtol=1e-12)
 
 
+# ------------------------------------------------------------- grouped query heads
+
+def test_gqa_matches_repeat_interleave_expansion():
+    """Query head h reads key/value head h // G: the result equals expanding
+    K and V with PyTorch's repeat_interleave over the head axis (what the
+    model's key/value repetition does) and selecting per query head."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, L, W, D = 6, 2, 60, 4, 8
+    Q = rng.standard_normal((Hq, W, D))
+    K = rng.standard_normal((Hkv, L, D)) * 1.5
+    V = rng.standard_normal((Hkv, L, D))
+    got = O.snapkv_select_gqa(Q, K, V, W, 20, 3, "avg")
+    Ke = torch.from_numpy(K).repeat_interleave(Hq // Hkv, dim=0).numpy()
+    Ve = torch.from_numpy(V).repeat_interleave(Hq // Hkv, dim=0).numpy()
+    ref = O.snapkv_select_heads(Q, Ke, Ve, W, 20, 3, "avg")
+    for h in range(Hq):
+        assert got[h]["indices"].tolist() == ref[h]["indices"].tolist()
+        np.testing.assert_array_equal(got[h]["votes"], ref[h]["votes"])
+        np.testing.assert_array_equal(got[h]["values"], ref[h]["values"])
+    # heads of one group differ (their own queries), heads of different groups read different keys
+    assert got[0]["indices"].tolist() != got[1]["indices"].tolist() or not np.array_equal(got[0]["votes"], got[1]["votes"])
+    with pytest.raises(ValueError):
+        O.snapkv_select_gqa(Q[:5], K, V, W, 20, 3, "avg")
+
+
+def test_expanded_cache_ratio_page_example():
+    """The page's GQA ledger: 32 query heads, 8 key/value heads, L = 16384,
+    C = 1024 and 512 generated tokens keep 4/11 of the native cache (not the
+    1/11 the sequence lengths alone suggest)."""
+    assert O.expanded_cache_ratio(32, 8, 16384, 1024, 512) == pytest.approx(4 / 11, rel=1e-15)
+    assert O.expanded_cache_ratio(8, 8, 16384, 1024, 512) == pytest.approx(1 / 11, rel=1e-15)
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("L,W", [(10, 3), (64, 8), (257, 32)])
