@@ -155,6 +155,60 @@ def cpu_baseline(w, seconds):
                       f"value = L * heads_done / heads_per_layer / time"}
 
 
+def refresh_bench(args, B, torch, np):
+    """The refresh selection of a cache of J kept plus h recent tokens per
+    head (h = J / 4), 32 heads per call, one call per layer, with a protected
+    head (sinks) and tail (recent window); scores, K, V and token ids are
+    synthetic and resident in HBM."""
+    J, h = args.refresh, args.refresh // 4
+    n, rows, layers, D = J + h, 32, args.layers or 32, 128
+    head, tail = 4, 64
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    S = [(torch.rand((rows, n), generator=g) * 4).cuda() for _ in range(layers)]
+    K = [torch.randn((rows, n, D), generator=g).to(torch.bfloat16).cuda() for _ in range(layers)]
+    V = [torch.randn((rows, n, D), generator=g).to(torch.bfloat16).cuda() for _ in range(layers)]
+    T = [torch.randint(0, 1 << 30, (rows, n), generator=g, dtype=torch.int32).cuda() for _ in range(layers)]
+    idx = [torch.empty((rows, J), dtype=torch.int32, device=dev) for _ in range(layers)]
+    Ko = [torch.empty((rows, J, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+    Vo = [torch.empty_like(Ko[0]) for _ in range(layers)]
+    To = [torch.empty((rows, J), dtype=torch.int32, device=dev) for _ in range(layers)]
+    ws = torch.empty(B.kvsel_refresh_workspace_bytes(rows, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(layers):
+            B.kvsel_refresh(S[l], rows, n, J, head, tail, K[l], V[l], D, torch.bfloat16, T[l], idx[l], Ko[l], Vo[l],
+                            To[l], ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    B.kvsel_profile_enable(True)
+    step()
+    torch.cuda.synchronize()
+    per_kernel = B.kvsel_profile_read()
+    B.kvsel_profile_enable(False)
+    moved = rows * (n * 4 + J * 4 * 2 + 4 * J * D * 2 + 2 * J * 4)  # scores, indices, K/V read and written, tokens
+    print(json.dumps({
+        "metric": "refresh selection: cached tokens scored/s (32 heads per call)",
+        "value": round(rows * n * layers / (ms / 1e3), 1), "unit": "cached tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"refresh_J{J}_h{h}_h32", "layers": layers, "J": J, "h": h, "protect_head": head,
+                   "protect_tail": tail, "D": D},
+        "path": {"alg_bytes_per_call": moved, "alg_GBps": round(moved * layers / (ms / 1e3) / 1e9, 1)},
+        "kernels": {k: {"launches": c, "avg_us": round(t / c * 1e3, 2)} for k, (c, t) in per_kernel.items()},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +226,8 @@ def main():
     ap.add_argument("--gqa", type=int, default=1,
                     help="query heads per K/V head: the layer's K/V has heads / GQA heads, each streamed once for "
                          "its group (kvsel_select_gqa)")
+    ap.add_argument("--refresh", type=int, default=0,
+                    help="time the refresh selection instead: J kept of J + J/4 cached tokens per head")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -189,6 +245,9 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a HIP device")
+    if args.refresh:
+        refresh_bench(args, B, torch, np)
+        return
     w = WL.get(args.workload)
     if w.ragged:
         raise SystemExit("bench.py times single-length workloads")

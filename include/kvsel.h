@@ -253,6 +253,33 @@ size_t kvsel_topk_workspace_bytes(int rows, int n);
 int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvsel_refresh: the selection step of a periodic cache refresh.  For each
+ * of `rows` rows (a head's n cached tokens: J kept earlier plus h recent),
+ * keep exactly `keep` entries: the first protect_head positions (mandatory
+ * prefix, attention sinks), the last protect_tail positions (recent window),
+ * and the keep - protect_head - protect_tail highest-scoring positions in
+ * between, equal scores going to the lowest index; indices ascending.
+ * [web page "Signals from the future: KV cache eviction by counter-causal
+ * surprise", section "architecture overview: the inference/refresh loop" and
+ * its memory-refresh step: a refresh scores the J + h cached tokens and keeps
+ * the top J; web page "Jacap: Preserving Nonlinear Information in KV-Cache
+ * Eviction", section "Algorithm 2: a serving-safe integration sketch":
+ * protected prefix, sinks and recent window first, the flexible budget filled
+ * by score, and its sanity checks: the kept count equals the budget.]  The
+ * score is the caller's (the pages' scores need the model).
+ *   scores [rows][n] float32, every value finite and >= 0
+ *   K, V [rows][n][D] (dtype), tokens_opt [rows][n] int32 or NULL
+ *   indices out [rows][keep]; K_out, V_out out [rows][keep][D];
+ *   tokens_out_opt out [rows][keep] (given with tokens_opt)
+ * Rules: 1 <= keep <= n, protect_head, protect_tail >= 0,
+ * protect_head + protect_tail <= keep.  Workspace:
+ * kvsel_refresh_workspace_bytes(rows, n) bytes, 256-byte aligned. */
+size_t kvsel_refresh_workspace_bytes(int rows, int n);
+int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
+                  const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt,
+                  int32_t* indices, void* K_out, void* V_out, int32_t* tokens_out_opt,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* kvsel_pool1d: pooled[r][j] for `rows` rows of n votes (row-major), width
  * `kernel` odd >= 1, KVSEL_POOL_AVG (zero padding, divide by kernel) or
  * KVSEL_POOL_MAX (in-range maximum).  out may not alias votes.

@@ -297,6 +297,33 @@ def expanded_cache_ratio(q_heads: int, kv_heads: int, L: int, C: int, g: int) ->
     return q_heads * (min(L, C) + g) / (kv_heads * (L + g))
 
 
+def refresh_select(scores, keep: int, protect_head: int, protect_tail: int) -> np.ndarray:
+    """The selection step of a periodic cache refresh over n cached tokens:
+    keep exactly `keep` positions.  The first protect_head (mandatory prefix,
+    attention sinks) and the last protect_tail (recent window) are reserved,
+    and the flexible budget keep - protect_head - protect_tail is filled with
+    the highest scores of the positions in between, equal scores going to the
+    lowest index.  Web page "Signals from the future: KV cache eviction by
+    counter-causal surprise", section "architecture overview: the
+    inference/refresh loop" (a refresh keeps the top J of the J + h cached
+    tokens); web page "Jacap: Preserving Nonlinear Information in KV-Cache
+    Eviction", section "Algorithm 2: a serving-safe integration sketch"
+    (protected tokens first, then the flexible budget by score) and its
+    sanity checks (the kept count equals the budget).  Returned ascending
+    (reading: storage order is free; ascending keeps causal order)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    if not (1 <= keep <= n) or protect_head < 0 or protect_tail < 0 or protect_head + protect_tail > keep:
+        raise ValueError("need 1 <= keep <= n and protected tokens that fit the budget")
+    if not np.all(np.isfinite(scores)):
+        raise ValueError("scores must be finite")
+    flexible = keep - protect_head - protect_tail
+    middle = scores[protect_head:n - protect_tail]
+    picked = top_prefix(middle, flexible) + protect_head if flexible > 0 else np.zeros(0, dtype=np.int64)
+    kept = np.concatenate([np.arange(protect_head), picked, np.arange(n - protect_tail, n)])
+    return np.sort(kept).astype(np.int64)
+
+
 def snapkv_select_heads(qwin, keys, values, W: int, C: int, kernel: int = 3,
                         pooling: str = "avg", heads: Sequence[int] | None = None) -> List[Dict]:
     """Independent selection per head (section "the prompt cache shrinks, the

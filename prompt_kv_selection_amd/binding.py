@@ -65,6 +65,10 @@ lib.kvsel_topk_workspace_bytes.restype = _sz
 lib.kvsel_topk_workspace_bytes.argtypes = [_i, _i]
 lib.kvsel_topk.restype = _i
 lib.kvsel_topk.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _sz, _vp]
+lib.kvsel_refresh_workspace_bytes.restype = _sz
+lib.kvsel_refresh_workspace_bytes.argtypes = [_i, _i]
+lib.kvsel_refresh.restype = _i
+lib.kvsel_refresh.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.kvsel_pool1d.restype = _i
 lib.kvsel_pool1d.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
 lib.kvsel_gather.restype = _i
@@ -194,6 +198,21 @@ def kvsel_topk(scores, rows, n, count, out, ld_out, workspace=None, workspace_by
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.kvsel_topk(_ptr(scores), rows, n, count, _ptr(out), ld_out, _ptr(workspace), workspace_bytes,
                           _stream(stream)))
+
+
+def kvsel_refresh_workspace_bytes(rows: int, n: int) -> int:
+    v = lib.kvsel_refresh_workspace_bytes(rows, n)
+    if v == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return v
+
+
+def kvsel_refresh(scores, rows, n, keep, protect_head, protect_tail, K, V, D, dtype, tokens, indices, K_out, V_out,
+                  tokens_out, workspace, workspace_bytes=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_refresh(_ptr(scores), rows, n, keep, protect_head, protect_tail, _ptr(K), _ptr(V), D,
+                             DTYPE.get(dtype, dtype), _ptr(tokens), _ptr(indices), _ptr(K_out), _ptr(V_out),
+                             _ptr(tokens_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kvsel_pool1d(votes, rows, n, kernel, pooling, pooled, stream=None) -> None:

@@ -612,6 +612,37 @@ size_t kvsel_topk_workspace_bytes(int rows, int n) {
   return topk_workspace(rows, n);
 }
 
+// Top-k over rows of scores described by a (one segment: positions 0 .. L-1 of
+// each row at scores + vote_off + row * vote_ld, C - (window ? W : 0) picks,
+// then the window positions when a.window), into out + idx_off + row * idx_ld.
+static int run_topk(Launch& a, int rows, const float* scores, int32_t* out, void* workspace, hipStream_t st) {
+  const Seg& s = a.seg[0];
+  const int n = s.L;
+  a.seg_size = selection_seg_size(n);
+  uint32_t* hist = (uint32_t*)workspace;
+  uint32_t* cut = (uint32_t*)((char*)workspace + align256((size_t)rows * 2048 * 4));
+  uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
+  uint32_t* cand = (uint32_t*)((char*)segcnt + align256((size_t)rows * kSegCntBytes));
+  hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
+  if (e != hipSuccess) return device_error(e, "fill launch");
+  e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
+  if (e != hipSuccess) return device_error(e, "histogram launch");
+  if (n <= select_rows_max()) {  // one workgroup per row
+    e = timed("select", st, [&] { return launch_select_hist(a, rows, scores, hist, out, st); });
+    if (e != hipSuccess) return device_error(e, "select launch");
+    return ok();
+  }
+  e = timed("candidates", st, [&] { return launch_candidates(a, rows, n, scores, hist, cand, segcnt, st); });
+  if (e != hipSuccess) return device_error(e, "candidates launch");
+  e = timed("threshold", st, [&] { return launch_threshold(a, rows, hist, cand, cut, segcnt, st); });
+  if (e != hipSuccess) return device_error(e, "threshold launch");
+  e = timed("emit", st, [&] {
+    return launch_emit(a, rows, n, 0, scores, cut, segcnt, out, nullptr, nullptr, nullptr, nullptr, st);
+  });
+  if (e != hipSuccess) return device_error(e, "emit launch");
+  return ok();
+}
+
 int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, int ld_out, void* workspace,
                size_t workspace_bytes, void* stream) {
   if (!scores || !out) return fail(KVSEL_EINVAL, "scores and out must not be NULL");
@@ -634,29 +665,76 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
   s.nh = rows;
   s.idx_ld = ld_out;
   s.vote_ld = n;
-  a.seg_size = selection_seg_size(n);
+  return run_topk(a, rows, scores, out, workspace, (hipStream_t)stream);
+}
+
+size_t kvsel_refresh_workspace_bytes(int rows, int n) { return kvsel_topk_workspace_bytes(rows, n); }
+
+int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
+                  const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
+                  void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!scores || !indices || !K || !V || !K_out || !V_out)
+    return fail(KVSEL_EINVAL, "scores, indices, K, V, K_out and V_out must not be NULL");
+  if (rows < 1 || n < 1) return fail(KVSEL_EINVAL, "rows and n must be >= 1 (got %d, %d)", rows, n);
+  if (keep < 1 || keep > n) return fail(KVSEL_EINVAL, "keep must be in [1, n] (got %d, n = %d)", keep, n);
+  if (protect_head < 0 || protect_tail < 0 || (long long)protect_head + protect_tail > keep)
+    return fail(KVSEL_EINVAL, "protected head %d and tail %d must be >= 0 and fit the %d kept", protect_head,
+                protect_tail, keep);
+  if (!tokens_opt != !tokens_out_opt) return fail(KVSEL_EINVAL, "tokens and tokens_out go together");
+  if (dtype != KVSEL_F32 && dtype != KVSEL_BF16) return fail(KVSEL_EINVAL, "unknown dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(KVSEL_EUNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+  if ((uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)K_out % 16 || (uintptr_t)V_out % 16)
+    return fail(KVSEL_EINVAL, "K, V, K_out and V_out must be 16-byte aligned");
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = topk_workspace(rows, n);
+  if (workspace_bytes < need)
+    return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
-  uint32_t* hist = (uint32_t*)workspace;
-  uint32_t* cut = (uint32_t*)((char*)workspace + align256((size_t)rows * 2048 * 4));
-  uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
-  uint32_t* cand = (uint32_t*)((char*)segcnt + align256((size_t)rows * kSegCntBytes));
-  hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
-  if (e != hipSuccess) return device_error(e, "fill launch");
-  e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
-  if (e != hipSuccess) return device_error(e, "histogram launch");
-  if (n <= select_rows_max()) {  // one workgroup per row
-    e = timed("select", st, [&] { return launch_select_hist(a, rows, scores, hist, out, st); });
-    if (e != hipSuccess) return device_error(e, "select launch");
-    return ok();
+  const int flexible = keep - protect_head - protect_tail;
+  if (flexible > 0) {
+    // Positions protect_head .. n-1 of each row, the last protect_tail of
+    // them appended as a window after the picks.
+    Launch a{};
+    a.n = 1;
+    a.heads = rows;
+    a.window = 1;
+    a.W = protect_tail;
+    Seg& s = a.seg[0];
+    s.L = n - protect_head;
+    s.C = keep - protect_head;
+    s.nout = s.C;
+    s.nh = rows;
+    s.vote_off = protect_head;
+    s.vote_ld = n;
+    s.idx_off = protect_head;
+    s.idx_ld = keep;
+    const int rc = run_topk(a, rows, scores, indices, workspace, st);
+    if (rc) return rc;
   }
-  e = timed("candidates", st, [&] { return launch_candidates(a, rows, n, scores, hist, cand, segcnt, st); });
-  if (e != hipSuccess) return device_error(e, "candidates launch");
-  e = timed("threshold", st, [&] { return launch_threshold(a, rows, hist, cand, cut, segcnt, st); });
-  if (e != hipSuccess) return device_error(e, "threshold launch");
-  e = timed("emit", st, [&] {
-    return launch_emit(a, rows, n, 0, scores, cut, segcnt, out, nullptr, nullptr, nullptr, nullptr, st);
+  hipError_t e = timed("finish", st, [&] {
+    return launch_refresh_finish(rows, n, keep, protect_head, protect_tail, flexible > 0, indices, tokens_opt,
+                                 tokens_out_opt, st);
   });
-  if (e != hipSuccess) return device_error(e, "emit launch");
+  if (e != hipSuccess) return device_error(e, "finish launch");
+  const int rpb = gather_rows_per_block(D, dtype);
+  Launch g{};
+  g.n = 1;
+  g.heads = rows;
+  g.D = D;
+  Seg& gs = g.seg[0];
+  gs.L = n;
+  gs.C = keep;
+  gs.nout = keep;
+  gs.nh = rows;
+  gs.gblk = (keep + rpb - 1) / rpb;
+  gs.idx_ld = keep;
+  gs.out_ld = keep;
+  const long long items = (long long)rows * gs.gblk;
+  if (items > 0x7FFFFFFFLL) return fail(KVSEL_EUNSUPPORTED, "gather grid too large");
+  e = timed("gather", st, [&] { return launch_gather(g, (int)items, dtype, K, V, indices, K_out, V_out, st); });
+  if (e != hipSuccess) return device_error(e, "gather launch");
   return ok();
 }
 

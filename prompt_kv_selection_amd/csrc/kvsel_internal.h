@@ -240,6 +240,10 @@ hipError_t launch_zero(const ZeroRanges& r, hipStream_t st);
 // Validating mode: sets kErrNonFinite in *err if any of the n 16-byte units
 // at p holds a non-finite value of the element type (dtype 1: bf16, 0: fp32).
 hipError_t launch_check_finite(const void* p, long long n16, int dtype, unsigned* err, hipStream_t st);
+// Refresh selection: turn the selection's relative entries into final
+// indices (protected head first) and gather token ids with them.
+hipError_t launch_refresh_finish(int rows, int n, int keep, int head, int tail, bool picked, int32_t* indices,
+                                 const int32_t* tokens, int32_t* tokens_out, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);

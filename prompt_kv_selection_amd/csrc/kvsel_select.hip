@@ -1403,6 +1403,38 @@ hipError_t launch_emit(const Launch& a, int rows, int max_positions, int dtype, 
   return hipGetLastError();
 }
 
+// Refresh selection: final indices of `rows` rows of `keep` entries.  The
+// first `head` entries are the protected leading positions 0 .. head-1;
+// entries head .. keep-1 were written by the selection relative to position
+// `head` (picks ascending, then the protected tail) and are shifted, or, with
+// no flexible budget (picked == 0), are the tail positions n - tail .. n-1.
+// Token ids (tokens != nullptr) are gathered with the final indices.
+__global__ void refresh_finish_kernel(int rows, int n, int keep, int head, int tail, int picked,
+                                      int32_t* __restrict__ indices, const int32_t* __restrict__ tokens,
+                                      int32_t* __restrict__ tokens_out) {
+  const long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (e >= (long long)rows * keep) return;
+  const int row = (int)(e / keep), m = (int)(e % keep);
+  int idx;
+  if (m < head)
+    idx = m;
+  else if (picked)
+    idx = min(max(indices[e], 0), n - head - 1) + head;
+  else
+    idx = n - tail + (m - head);
+  indices[e] = idx;
+  if (tokens != nullptr) tokens_out[e] = tokens[(long long)row * n + idx];
+}
+
+hipError_t launch_refresh_finish(int rows, int n, int keep, int head, int tail, bool picked, int32_t* indices,
+                                 const int32_t* tokens, int32_t* tokens_out, hipStream_t st) {
+  const long long total = (long long)rows * keep;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(refresh_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, rows, n, keep,
+                     head, tail, picked ? 1 : 0, indices, tokens, tokens_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st) {
   if (items <= 0) return hipSuccess;

@@ -170,6 +170,21 @@ def test_status_entry_point_errors(B):
     assert B.KVSEL_ENONFINITE == -5
 
 
+def test_refresh_argument_errors(B):
+    lib = B.lib
+    def refresh(n=100, keep=10, head=2, tail=2, D=128, tok=None, tok_out=None, wsb=1 << 30):
+        return lib.kvsel_refresh(FAKE, 2, n, keep, head, tail, FAKE, FAKE, D, 1, tok, FAKE, FAKE, FAKE, tok_out,
+                                 FAKE, wsb, None)
+    assert refresh(keep=0) == -1
+    assert refresh(keep=101) == -1
+    assert refresh(head=6, tail=5) == -1 and "fit" in B.kvsel_last_error()
+    assert refresh(head=-1) == -1
+    assert refresh(tok=FAKE) == -1                 # tokens without tokens_out
+    assert refresh(D=96) == -2
+    assert refresh(wsb=1024) == -3
+    assert lib.kvsel_refresh_workspace_bytes(2, 100) == lib.kvsel_topk_workspace_bytes(2, 100)
+
+
 def test_options(B):
     lib = B.lib
     assert lib.kvsel_get_option(2) == 0                       # validating mode off

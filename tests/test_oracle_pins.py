@@ -299,6 +299,43 @@ def test_expanded_cache_ratio_page_example():
     assert O.expanded_cache_ratio(8, 8, 16384, 1024, 512) == pytest.approx(1 / 11, rel=1e-15)
 
 
+# ------------------------------------------------------------- refresh selection
+
+@pytest.mark.parametrize("seed", range(6))
+def test_refresh_select_bruteforce(seed):
+    """Brute force over every subset of the middle region: the kept set is
+    the protected head and tail plus the flexible subset of maximum score
+    sum, lexicographically smallest among equal sums (the lowest-index tie
+    rule), and it always holds exactly `keep` positions."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(4, 11))
+    scores = rng.integers(0, 4, size=n).astype(np.float64)  # many exact ties
+    for keep in range(1, n + 1):
+        for head in range(0, keep + 1):
+            for tail in range(0, keep - head + 1):
+                got = O.refresh_select(scores, keep, head, tail)
+                assert len(got) == keep and len(set(got.tolist())) == keep
+                mid = list(range(head, n - tail))
+                k = keep - head - tail
+                best = None
+                for sub in itertools.combinations(mid, k):
+                    key = (-sum(scores[j] for j in sub), sub)
+                    best = key if best is None or key < best else best
+                expect = sorted(list(range(head)) + list(best[1]) + list(range(n - tail, n)))
+                assert got.tolist() == expect, (scores.tolist(), keep, head, tail)
+
+
+def test_refresh_select_rules():
+    s = np.array([5.0, 1.0, 9.0, 9.0, 2.0, 7.0])
+    assert O.refresh_select(s, 6, 0, 0).tolist() == [0, 1, 2, 3, 4, 5]   # keep everything
+    assert O.refresh_select(s, 3, 1, 1).tolist() == [0, 2, 5]            # ties at 9: the lower index
+    assert O.refresh_select(s, 2, 1, 1).tolist() == [0, 5]               # no flexible budget
+    with pytest.raises(ValueError):
+        O.refresh_select(s, 2, 2, 1)
+    with pytest.raises(ValueError):
+        O.refresh_select(s, 7, 0, 0)
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("L,W", [(10, 3), (64, 8), (257, 32)])
