@@ -324,6 +324,63 @@ def refresh_select(scores, keep: int, protect_head: int, protect_tail: int) -> n
     return np.sort(kept).astype(np.int64)
 
 
+def jacap_scores(keys, outs, mu_q, lambda_q, tau: float) -> Dict:
+    """Jacap leverage scores of N cached tokens of one head (web page "Jacap:
+    Preserving Nonlinear Information in KV-Cache Eviction", sections
+    "Practical approximation" and "Algorithm 1: one eviction event"):
+      z_i = k_i . mu_Q / (tau sqrt(d_k)), alpha = softmax(z) over all N,
+      kappa_i = k_i^T Lambda_Q k_i (Lambda_Q diagonal, given as its diagonal),
+      w_i = [alpha_i (1 - alpha_i)]^2 kappa_i / d_k,
+      A = I + sum_j w_j u_j u_j^T (u_j = outs[j]: W_O v_j, or v_j),
+      r_i = w_i u_i^T A^{-1} u_i, with A factored once (Cholesky) and solved.
+    keys [N, d_k], outs [N, d_u]; float64 throughout.  Returns z, alpha,
+    kappa, w, A and r."""
+    keys = np.asarray(keys, dtype=np.float64)
+    outs = np.asarray(outs, dtype=np.float64)
+    mu = np.asarray(mu_q, dtype=np.float64)
+    lam = np.asarray(lambda_q, dtype=np.float64)
+    N, dk = keys.shape
+    if outs.shape[0] != N or mu.shape != (dk,) or lam.shape != (dk,) or not tau > 0:
+        raise ValueError("shape mismatch or non-positive temperature")
+    if np.any(lam < 0):
+        raise ValueError("Lambda_Q is a second moment: its diagonal is >= 0")
+    z = np.zeros(N)
+    for d in range(dk):
+        z += keys[:, d] * mu[d]
+    z /= tau * math.sqrt(dk)
+    m = z.max()
+    e = np.exp(z - m)
+    alpha = e / math.fsum(e.tolist())
+    kappa = np.zeros(N)
+    for d in range(dk):
+        kappa += lam[d] * keys[:, d] ** 2
+    w = (alpha * (1.0 - alpha)) ** 2 * kappa / dk
+    du = outs.shape[1]
+    A = np.eye(du)
+    for j in range(N):
+        A += w[j] * np.outer(outs[j], outs[j])
+    L = np.linalg.cholesky(A)
+    # A^{-1} u_i by two triangular solves with the factor.
+    y = np.linalg.solve(L, outs.T)          # L y = u
+    x = np.linalg.solve(L.T, y)             # L^T x = y
+    r = w * np.einsum("ij,ji->i", outs, x)
+    return {"z": z, "alpha": alpha, "kappa": kappa, "w": w, "A": A, "r": r}
+
+
+def jacap_select(keys, values, outs, mu_q, lambda_q, tau: float, keep: int, protect_head: int = 0,
+                 protect_tail: int = 0) -> Dict:
+    """One Jacap eviction event for one head: protected head and tail
+    reserved, the flexible budget filled with the highest leverage scores
+    (web page "Jacap: Preserving Nonlinear Information in KV-Cache Eviction",
+    sections "Algorithm 1: one eviction event" and "Algorithm 2: a
+    serving-safe integration sketch"), keys and values gathered."""
+    sc = jacap_scores(keys, outs, mu_q, lambda_q, tau)
+    idx = refresh_select(sc["r"], keep, protect_head, protect_tail)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    return {"indices": idx, "keys": keys[idx], "values": values[idx], **sc}
+
+
 def snapkv_select_heads(qwin, keys, values, W: int, C: int, kernel: int = 3,
                         pooling: str = "avg", heads: Sequence[int] | None = None) -> List[Dict]:
     """Independent selection per head (section "the prompt cache shrinks, the

@@ -336,6 +336,78 @@ def test_refresh_select_rules():
         O.refresh_select(s, 7, 0, 0)
 
 
+# ------------------------------------------------------------- Jacap scores
+
+def test_jacap_sensitivity_closed_forms():
+    """The page's sensitivities: probabilities (0.5, 0.5) give
+    alpha (1 - alpha) = 0.25, (0.99, 0.01) give 0.0099; a key set whose
+    centre logits are equal gives alpha = 1/N exactly."""
+    for probs, rho in (((0.5, 0.5), 0.25), ((0.99, 0.01), 0.0099)):
+        z = np.log(np.array(probs))           # logits with these probabilities
+        keys = np.zeros((2, 4))
+        keys[:, 0] = z * 2.0                  # mu = e_0, tau = 1, sqrt(d_k) = 2
+        sc = O.jacap_scores(keys, np.eye(2), np.eye(4)[0], np.ones(4), 1.0)
+        np.testing.assert_allclose(sc["alpha"], probs, rtol=1e-13)
+        np.testing.assert_allclose(sc["alpha"] * (1 - sc["alpha"]), rho, rtol=1e-12)
+    sc = O.jacap_scores(np.ones((5, 3)), np.eye(5, 2), np.ones(3), np.ones(3), 0.7)
+    np.testing.assert_allclose(sc["alpha"], 0.2, rtol=1e-14)
+
+
+def jacap_toy():
+    """The page's 2-D miniature: u1 = (1, 0), u2 = (0.95, 0.05), u3 = (0, 1)
+    with w = (1, 1, 0.7), realised through keys whose weights come out
+    exactly so (equal centre logits, kappa scaled per token)."""
+    u = np.array([[1.0, 0.0], [0.95, 0.05], [0.0, 1.0]])
+    want_w = np.array([1.0, 1.0, 0.7])
+    N, dk = 3, 4
+    a = 1.0 / N
+    rho2 = (a * (1 - a)) ** 2
+    kappa = want_w * dk / rho2                  # w = rho^2 kappa / d_k
+    keys = np.zeros((N, dk))
+    keys[:, 1] = np.sqrt(kappa)                 # Lambda = e_1: kappa = k_1^2; mu = e_0: equal logits
+    return keys, u, np.eye(dk)[0], np.eye(dk)[1], want_w
+
+
+def test_jacap_leverage_toy_prefers_the_spanning_pair():
+    """Independent weighting prefers tokens 1 and 2; leverage discounts
+    token 2 (nearly collinear with token 1) and keeps tokens 1 and 3, which
+    span both axes (the page's worked miniature)."""
+    keys, u, mu, lam, w = jacap_toy()
+    sc = O.jacap_scores(keys, u, mu, lam, 1.0)
+    np.testing.assert_allclose(sc["w"], w, rtol=1e-12)
+    A = np.eye(2) + sum(w[j] * np.outer(u[j], u[j]) for j in range(3))
+    np.testing.assert_allclose(sc["A"], A, rtol=1e-14)
+    assert sc["r"][2] > sc["r"][0] > sc["r"][1]
+    r = O.jacap_select(keys, np.arange(6.0).reshape(3, 2), u, mu, lam, 1.0, keep=2)
+    assert r["indices"].tolist() == [0, 2]
+    assert sorted(np.argsort(-w, kind="stable")[:2].tolist()) == [0, 1]   # plain weighting would keep 1 and 2
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_jacap_determinant_lemma_and_sanity(seed):
+    """r_i = det(A + w_i u_i u_i^T) / det(A) - 1 (the determinant lemma the
+    page derives the leverage from), checked with explicit determinants;
+    the page's sanity list: A symmetric positive definite, every w >= 0,
+    scores finite, retained count equal to the budget after protection."""
+    rng = np.random.default_rng(seed)
+    N, dk, du = 9, 6, 5
+    keys = rng.standard_normal((N, dk)) * 2
+    outs = rng.standard_normal((N, du))
+    mu = rng.standard_normal(dk)
+    lam = rng.random(dk) * 2
+    sc = O.jacap_scores(keys, outs, mu, lam, 0.8)
+    A = sc["A"]
+    detA = np.linalg.det(A)
+    for i in range(N):
+        lemma = np.linalg.det(A + sc["w"][i] * np.outer(outs[i], outs[i])) / detA - 1
+        np.testing.assert_allclose(sc["r"][i], lemma, rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(A, A.T, rtol=0, atol=0)
+    assert np.all(np.linalg.eigvalsh(A) >= 1 - 1e-12)
+    assert np.all(sc["w"] >= 0) and np.all(np.isfinite(sc["r"]))
+    sel = O.jacap_select(keys, keys, outs, mu, lam, 0.8, keep=5, protect_head=1, protect_tail=2)
+    assert len(sel["indices"]) == 5 and sel["indices"][0] == 0 and sel["indices"][-2:].tolist() == [7, 8]
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("L,W", [(10, 3), (64, 8), (257, 32)])
