@@ -117,7 +117,8 @@ int kvsel_version(void);
 const char* kvsel_last_error(void);
 
 /* Device-side outcome of the last selection call (kvsel_select*,
- * kvsel_select*_lse) that used this workspace: waits for `stream`, then reads
+ * kvsel_select*_lse, kvsel_select_gqa, kvsel_jacap_select) that used this
+ * workspace: waits for `stream`, then reads
  * the flags the call's kernels left in the workspace header.  Returns
  * KVSEL_OK; KVSEL_ENONFINITE if a non-finite input (validating mode) or a
  * non-finite or zero row normaliser was seen (the outputs follow the
@@ -279,6 +280,34 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
                   const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt,
                   int32_t* indices, void* K_out, void* V_out, int32_t* tokens_out_opt,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* kvsel_jacap_select: one Jacap eviction event per head over its N cached
+ * tokens [web page "Jacap: Preserving Nonlinear Information in KV-Cache
+ * Eviction", sections "Practical approximation", "Algorithm 1: one eviction
+ * event" and "Algorithm 2: a serving-safe integration sketch"]:
+ *   z_i = k_i . mu_Q / (tau sqrt(D)), alpha = softmax(z) over the N tokens,
+ *   w_i = [alpha_i (1 - alpha_i)]^2 (k_i^T Lambda_Q k_i) / D,
+ *   A = I + sum_j w_j u_j u_j^T, r_i = w_i u_i^T A^{-1} u_i (Cholesky of A),
+ * then the selection of kvsel_refresh on the scores r: protected head and
+ * tail, the flexible budget by score, ties to the lowest index, ascending,
+ * K, V (and token ids) gathered.
+ *   K, V, U [heads][N][D] bf16: keys, values, and the output directions
+ *           u_i (W_O v_i, or V itself as the page's cheaper proxy)
+ *   mu_q, lambda_q [heads][D] float32: running query mean and diagonal
+ *           second moment (lambda_q >= 0); tau > 0 the temperature
+ *   scores_opt out [heads][N] float32 leverage scores, or NULL
+ *   other arguments and rules as for kvsel_refresh (n = N)
+ * Supported: bf16, D in {64, 128} (else KVSEL_EUNSUPPORTED).  The two
+ * N D^2 contractions run on MFMA with the fp32 factor split into bf16 high
+ * and low parts; the factorisation is fp32.  kvsel_status(workspace) reports
+ * a non-positive pivot or normaliser as KVSEL_ENONFINITE.  Workspace:
+ * kvsel_jacap_workspace_bytes(heads, N, D), 256-byte aligned. */
+size_t kvsel_jacap_workspace_bytes(int heads, int N, int D);
+int kvsel_jacap_select(const void* K, const void* V, const void* U, const float* mu_q, const float* lambda_q,
+                       float tau, int heads, int N, int D, int dtype, int keep, int protect_head,
+                       int protect_tail, const int32_t* tokens_opt, int32_t* indices, void* K_out,
+                       void* V_out, int32_t* tokens_out_opt, float* scores_opt, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* kvsel_pool1d: pooled[r][j] for `rows` rows of n votes (row-major), width
  * `kernel` odd >= 1, KVSEL_POOL_AVG (zero padding, divide by kernel) or

@@ -24,7 +24,7 @@ KVSEL_EWORKSPACE = -3
 KVSEL_EDEVICE = -4
 KVSEL_ENONFINITE = -5
 POOL = {"avg": 0, "max": 1}
-DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1, "f32": 0, "bf16": 1}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m prompt_kv_selection_amd.build`")
@@ -69,6 +69,11 @@ lib.kvsel_refresh_workspace_bytes.restype = _sz
 lib.kvsel_refresh_workspace_bytes.argtypes = [_i, _i]
 lib.kvsel_refresh.restype = _i
 lib.kvsel_refresh.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_jacap_workspace_bytes.restype = _sz
+lib.kvsel_jacap_workspace_bytes.argtypes = [_i, _i, _i]
+lib.kvsel_jacap_select.restype = _i
+lib.kvsel_jacap_select.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i, _i, _i, _i, _i, _i, _i,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.kvsel_pool1d.restype = _i
 lib.kvsel_pool1d.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
 lib.kvsel_gather.restype = _i
@@ -213,6 +218,23 @@ def kvsel_refresh(scores, rows, n, keep, protect_head, protect_tail, K, V, D, dt
     _check(lib.kvsel_refresh(_ptr(scores), rows, n, keep, protect_head, protect_tail, _ptr(K), _ptr(V), D,
                              DTYPE.get(dtype, dtype), _ptr(tokens), _ptr(indices), _ptr(K_out), _ptr(V_out),
                              _ptr(tokens_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_jacap_workspace_bytes(heads: int, N: int, D: int) -> int:
+    v = lib.kvsel_jacap_workspace_bytes(heads, N, D)
+    if v == 0:
+        raise KvselError(KVSEL_EINVAL, kvsel_last_error())
+    return v
+
+
+def kvsel_jacap_select(K, V, U, mu_q, lambda_q, tau, heads, N, D, dtype, keep, protect_head, protect_tail, tokens,
+                       indices, K_out, V_out, tokens_out, scores, workspace, workspace_bytes=None,
+                       stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(lib.kvsel_jacap_select(_ptr(K), _ptr(V), _ptr(U), _ptr(mu_q), _ptr(lambda_q), float(tau), heads, N, D,
+                                  DTYPE.get(dtype, dtype), keep, protect_head, protect_tail, _ptr(tokens),
+                                  _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(tokens_out), _ptr(scores),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kvsel_pool1d(votes, rows, n, kernel, pooling, pooled, stream=None) -> None:

@@ -670,6 +670,10 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
 
 size_t kvsel_refresh_workspace_bytes(int rows, int n) { return kvsel_topk_workspace_bytes(rows, n); }
 
+static int refresh_core(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
+                        const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
+                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st);
+
 int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
                   const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
                   void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, size_t workspace_bytes,
@@ -691,7 +695,13 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
   const size_t need = topk_workspace(rows, n);
   if (workspace_bytes < need)
     return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
-  hipStream_t st = (hipStream_t)stream;
+  return refresh_core(scores, rows, n, keep, protect_head, protect_tail, K, V, D, dtype, tokens_opt, indices, K_out,
+                      V_out, tokens_out_opt, workspace, (hipStream_t)stream);
+}
+
+static int refresh_core(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
+                        const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
+                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st) {
   const int flexible = keep - protect_head - protect_tail;
   if (flexible > 0) {
     // Positions protect_head .. n-1 of each row, the last protect_tail of
@@ -736,6 +746,94 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
   e = timed("gather", st, [&] { return launch_gather(g, (int)items, dtype, K, V, indices, K_out, V_out, st); });
   if (e != hipSuccess) return device_error(e, "gather launch");
   return ok();
+}
+
+// Jacap workspace: z, kappa, w, r ([heads][N] each), softmax partials, the
+// Gram parts, L^{-1} (hi, lo), then the refresh selection's workspace.
+struct JacapPlan {
+  size_t off_z, off_kappa, off_w, off_r, off_part, off_gram, off_minv, off_sel, bytes;
+};
+static JacapPlan jacap_plan(int heads, int N, int D) {
+  JacapPlan q{};
+  const size_t hn = (size_t)heads * N * sizeof(float);
+  size_t off = kHeaderBytes;  // the header's error word, as for the selection calls
+  q.off_z = off;
+  off = align256(off + hn);
+  q.off_kappa = off;
+  off = align256(off + hn);
+  q.off_w = off;
+  off = align256(off + hn);
+  q.off_r = off;
+  off = align256(off + hn);
+  q.off_part = off;
+  off = align256(off + (size_t)heads * jacap_chunks(N) * 2 * sizeof(float));
+  q.off_gram = off;
+  off = align256(off + (size_t)heads * jacap_slices(N) * D * D * sizeof(float));
+  q.off_minv = off;
+  off = align256(off + (size_t)heads * 2 * D * D * 2);
+  q.off_sel = off;
+  off = align256(off + topk_workspace(heads, N));
+  q.bytes = off;
+  return q;
+}
+
+size_t kvsel_jacap_workspace_bytes(int heads, int N, int D) {
+  if (heads < 1 || N < 1 || (D != 64 && D != 128)) {
+    fail(KVSEL_EINVAL, "heads and N must be >= 1 and D 64 or 128 (got %d, %d, %d)", heads, N, D);
+    return 0;
+  }
+  ok();
+  return jacap_plan(heads, N, D).bytes;
+}
+
+int kvsel_jacap_select(const void* K, const void* V, const void* U, const float* mu_q, const float* lambda_q,
+                       float tau, int heads, int N, int D, int dtype, int keep, int protect_head, int protect_tail,
+                       const int32_t* tokens_opt, int32_t* indices, void* K_out, void* V_out,
+                       int32_t* tokens_out_opt, float* scores_opt, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!K || !V || !U || !mu_q || !lambda_q || !indices || !K_out || !V_out)
+    return fail(KVSEL_EINVAL, "K, V, U, mu_q, lambda_q, indices, K_out and V_out must not be NULL");
+  if (heads < 1 || N < 1) return fail(KVSEL_EINVAL, "heads and N must be >= 1 (got %d, %d)", heads, N);
+  if (!(tau > 0.f) || !isfinite(tau)) return fail(KVSEL_EINVAL, "temperature must be finite and > 0");
+  if (keep < 1 || keep > N) return fail(KVSEL_EINVAL, "keep must be in [1, N] (got %d, N = %d)", keep, N);
+  if (protect_head < 0 || protect_tail < 0 || (long long)protect_head + protect_tail > keep)
+    return fail(KVSEL_EINVAL, "protected head %d and tail %d must be >= 0 and fit the %d kept", protect_head,
+                protect_tail, keep);
+  if (!tokens_opt != !tokens_out_opt) return fail(KVSEL_EINVAL, "tokens and tokens_out go together");
+  if (dtype != KVSEL_F32 && dtype != KVSEL_BF16) return fail(KVSEL_EINVAL, "unknown dtype %d", dtype);
+  if (dtype != KVSEL_BF16) return fail(KVSEL_EUNSUPPORTED, "Jacap scores need bf16 keys and outputs");
+  if (D != 64 && D != 128) return fail(KVSEL_EUNSUPPORTED, "head dimension %d not supported (64 or 128)", D);
+  if ((uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)U % 16 || (uintptr_t)K_out % 16 || (uintptr_t)V_out % 16)
+    return fail(KVSEL_EINVAL, "K, V, U, K_out and V_out must be 16-byte aligned");
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  const JacapPlan q = jacap_plan(heads, N, D);
+  if (workspace_bytes < q.bytes)
+    return fail(KVSEL_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, q.bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  JacapArgs j{};
+  j.heads = heads;
+  j.N = N;
+  j.nch = jacap_chunks(N);
+  j.slices = jacap_slices(N);
+  j.tau = tau;
+  j.mu = mu_q;
+  j.lambda = lambda_q;
+  j.z = (float*)(ws + q.off_z);
+  j.kappa = (float*)(ws + q.off_kappa);
+  j.w = (float*)(ws + q.off_w);
+  j.r = scores_opt ? scores_opt : (float*)(ws + q.off_r);
+  j.part = (float*)(ws + q.off_part);
+  j.gpart = (float*)(ws + q.off_gram);
+  j.minv = (__bf16*)(ws + q.off_minv);
+  j.err = (unsigned*)ws;  // cleared by the first kernel
+  hipError_t e = launch_jacap_scores(j, D, K, U, st, [&](const char* name, const std::function<hipError_t()>& f) {
+    return timed(name, st, f);
+  });
+  if (e != hipSuccess) return device_error(e, "jacap launch");
+  return refresh_core(j.r, heads, N, keep, protect_head, protect_tail, K, V, D, dtype, tokens_opt, indices, K_out,
+                      V_out, tokens_out_opt, ws + q.off_sel, st);
 }
 
 int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling, float* pooled, void* stream) {

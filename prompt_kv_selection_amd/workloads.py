@@ -214,3 +214,29 @@ def ragged_arrays(w: Workload, layer: int = 0, threads: Optional[int] = None):
         K[lo:hi] = k.reshape(-1)
         V[lo:hi] = v.reshape(-1)
     return Q, K, V, lengths, budgets(w), cu
+
+
+# ---------------------------------------------------------------- Jacap events
+
+def jacap_arrays(seed: int, heads: int, N: int, D: int, mu_scale: float = 1.0, separate_u: bool = False):
+    """Inputs of one Jacap eviction event over N cached tokens per head:
+    (K, V, U) [heads, N, D] as bf16 bit patterns, mu_q and lambda_q [heads, D]
+    float32.  Per head one PCG64 stream, ``default_rng(SeedSequence(seed,
+    spawn_key=(head,)))``, draws in this order: K standard normal, V standard
+    normal, U standard normal when `separate_u` (a stand-in for W_O v; else
+    U = V, the cheaper proxy), mu_q normal with standard deviation mu_scale,
+    lambda_q uniform on [0.1, 2) (a diagonal second moment with the floor
+    already applied)."""
+    K = np.empty((heads, N, D), dtype=np.uint16)
+    V = np.empty_like(K)
+    U = np.empty_like(K)
+    mu = np.empty((heads, D), dtype=np.float32)
+    lam = np.empty((heads, D), dtype=np.float32)
+    for h in range(heads):
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(h,)))
+        K[h] = f32_to_bf16_bits(rng.standard_normal((N, D), dtype=np.float32))
+        V[h] = f32_to_bf16_bits(rng.standard_normal((N, D), dtype=np.float32))
+        U[h] = f32_to_bf16_bits(rng.standard_normal((N, D), dtype=np.float32)) if separate_u else V[h]
+        mu[h] = (mu_scale * rng.standard_normal(D)).astype(np.float32)
+        lam[h] = rng.uniform(0.1, 2.0, size=D).astype(np.float32)
+    return K, V, U, mu, lam

@@ -185,6 +185,32 @@ def test_refresh_argument_errors(B):
     assert lib.kvsel_refresh_workspace_bytes(2, 100) == lib.kvsel_topk_workspace_bytes(2, 100)
 
 
+def test_jacap_argument_errors(B):
+    lib = B.lib
+    mu = (ctypes.c_float * 128)()
+
+    def jacap(N=100, D=128, dtype=1, keep=10, head=2, tail=2, tau=10.0, tok=None, tok_out=None, wsb=1 << 30,
+              U=FAKE, lam=None):
+        lam = ctypes.addressof(mu) if lam is None else lam
+        return lib.kvsel_jacap_select(FAKE, FAKE, U, ctypes.addressof(mu), lam, tau, 2, N, D, dtype, keep, head,
+                                      tail, tok, FAKE, FAKE, FAKE, tok_out, None, FAKE, wsb, None)
+    assert jacap(keep=0) == -1
+    assert jacap(keep=101) == -1
+    assert jacap(head=6, tail=5) == -1 and "fit" in B.kvsel_last_error()
+    assert jacap(tau=0.0) == -1 and "temperature" in B.kvsel_last_error()
+    assert jacap(tau=float("nan")) == -1
+    assert jacap(U=None) == -1
+    assert jacap(lam=0) == -1
+    assert jacap(tok=FAKE) == -1
+    assert jacap(dtype=0) == -2 and "bf16" in B.kvsel_last_error()   # f32 keys are not supported here
+    assert jacap(D=96) == -2
+    assert jacap(wsb=1024) == -3
+    assert lib.kvsel_jacap_workspace_bytes(2, 100, 96) == 0
+    a = lib.kvsel_jacap_workspace_bytes(2, 100, 128)
+    b = lib.kvsel_jacap_workspace_bytes(2, 5000, 128)
+    assert a % 256 == 0 and b > a
+
+
 def test_options(B):
     lib = B.lib
     assert lib.kvsel_get_option(2) == 0                       # validating mode off
