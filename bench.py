@@ -209,6 +209,96 @@ def refresh_bench(args, B, torch, np):
     }), flush=True)
 
 
+def jacap_alg(name, H, N, D, S):
+    """(bytes, flops) one launch of a Jacap kernel moves and computes for H
+    heads of N cached tokens (S Gram slices per head); flops count each
+    product of the two N D^2 contractions once (the bf16 high/low split
+    issues 3 and 2 times as many)."""
+    e = 2
+    if name == "jacap_logits":      # K once, z and kappa out, mu and lambda
+        return H * N * D * e + H * N * 8 + H * D * 8, 0
+    if name == "jacap_weights":     # z and kappa in, w out
+        return H * N * 12, 0
+    if name == "jacap_gram":        # U once, w, the slices' D x D parts out
+        return H * N * D * e + H * N * 4 + H * S * D * D * 4, 2 * H * N * D * D
+    if name == "jacap_factor":      # the parts in, L^-1 (high, low) out
+        return H * S * D * D * 4 + H * D * D * 4, H * D ** 3 // 3 * 2
+    if name == "jacap_leverage":    # U once, w in, r out, L^-1
+        return H * N * D * e + H * N * 8 + H * D * D * 4, 2 * H * N * D * D
+    return None, None
+
+
+def jacap_bench(args, B, torch, np):
+    """One Jacap eviction event per layer (kvsel_jacap_select): 32 heads of N
+    cached tokens, D = 128, bf16, U = V (the page's cheaper proxy for W_O v),
+    tau = 10, keep = N / 5 (compression 0.8), 4 sink and 64 recent tokens
+    protected.  K, V ~ N(0, 1), mu_q ~ N(0, 1), lambda_q ~ U[0.1, 2), drawn on
+    the device from a seeded generator; every layer has its own K and V."""
+    N, H, D, layers = args.jacap, 32, 128, args.layers or 32
+    keep, head, tail, tau = N // 5, 4, 64, 10.0
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(17)
+    K = [torch.randn((H, N, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    V = [torch.randn((H, N, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    mu = [torch.randn((H, D), generator=g, device=dev) for _ in range(layers)]
+    lam = [torch.rand((H, D), generator=g, device=dev) * 1.9 + 0.1 for _ in range(layers)]
+    idx = [torch.empty((H, keep), dtype=torch.int32, device=dev) for _ in range(layers)]
+    Ko = [torch.empty((H, keep, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+    Vo = [torch.empty_like(Ko[0]) for _ in range(layers)]
+    ws = torch.empty(B.kvsel_jacap_workspace_bytes(H, N, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(layers):
+            B.kvsel_jacap_select(K[l], V[l], V[l], mu[l], lam[l], tau, H, N, D, "bf16", keep, head, tail, None,
+                                 idx[l], Ko[l], Vo[l], None, None, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    if B.kvsel_status(ws, stream) != B.KVSEL_OK:
+        raise SystemExit("Jacap event reported a device-side error: " + B.kvsel_last_error())
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    B.kvsel_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = B.kvsel_profile_read()
+    B.kvsel_profile_enable(False)
+    S = max(1, min(32, (256 + H - 1) // H, (N + 511) // 512))
+    kern = {}
+    for k, (c, t) in per_kernel.items():
+        avg = t / c / 1e3
+        ab, fl = jacap_alg(k, H, N, D, S)
+        kern[k] = {"launches": c, "avg_us": round(avg * 1e6, 2),
+                   "alg_GBps": None if ab is None else round(ab / avg / 1e9, 1),
+                   "alg_TFLOPs": None if not fl else round(fl / avg / 1e12, 2)}
+    dom = max((k for k in per_kernel if jacap_alg(k, H, N, D, S)[0] is not None), key=lambda k: per_kernel[k][1])
+    c, t = per_kernel[dom]
+    achieved = jacap_alg(dom, H, N, D, S)[0] / (t / c / 1e3) / 1e9
+    moved = H * N * D * 2 * 3 + 4 * H * keep * D * 2 + H * keep * 4  # K once, U twice, kept rows, indices
+    print(json.dumps({
+        "metric": f"Jacap eviction event: cached tokens scored/s (32 heads, N={N}, D=128)",
+        "value": round(H * N * layers / (ms / 1e3), 1), "unit": "cached tokens/s (all heads)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"jacap_h32_n{N}_d128", "layers": layers, "N": N, "keep": keep,
+                   "protect_head": head, "protect_tail": tail, "tau": tau, "u": "v"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "path": {"alg_bytes_per_call": moved, "alg_GBps": round(moved * layers / (ms / 1e3) / 1e9, 1),
+                 "us_per_call": round(ms * 1e3 / layers, 2)},
+        "kernels": kern,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +318,8 @@ def main():
                          "its group (kvsel_select_gqa)")
     ap.add_argument("--refresh", type=int, default=0,
                     help="time the refresh selection instead: J kept of J + J/4 cached tokens per head")
+    ap.add_argument("--jacap", type=int, default=0,
+                    help="time the Jacap eviction event instead: 32 heads of N cached tokens per layer call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -247,6 +339,9 @@ def main():
         raise SystemExit("bench.py needs a HIP device")
     if args.refresh:
         refresh_bench(args, B, torch, np)
+        return
+    if args.jacap:
+        jacap_bench(args, B, torch, np)
         return
     w = WL.get(args.workload)
     if w.ragged:

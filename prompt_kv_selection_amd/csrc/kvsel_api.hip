@@ -768,7 +768,7 @@ static JacapPlan jacap_plan(int heads, int N, int D) {
   q.off_part = off;
   off = align256(off + (size_t)heads * jacap_chunks(N) * 2 * sizeof(float));
   q.off_gram = off;
-  off = align256(off + (size_t)heads * jacap_slices(N) * D * D * sizeof(float));
+  off = align256(off + (size_t)heads * jacap_slices(N, heads) * D * D * sizeof(float));
   q.off_minv = off;
   off = align256(off + (size_t)heads * 2 * D * D * 2);
   q.off_sel = off;
@@ -816,7 +816,7 @@ int kvsel_jacap_select(const void* K, const void* V, const void* U, const float*
   j.heads = heads;
   j.N = N;
   j.nch = jacap_chunks(N);
-  j.slices = jacap_slices(N);
+  j.slices = jacap_slices(N, heads);
   j.tau = tau;
   j.mu = mu_q;
   j.lambda = lambda_q;

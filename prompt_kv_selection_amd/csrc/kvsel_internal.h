@@ -264,7 +264,7 @@ struct JacapArgs {
   unsigned* err;
 };
 int jacap_chunks(int N);
-int jacap_slices(int N);
+int jacap_slices(int N, int heads);
 hipError_t launch_jacap_scores(const JacapArgs& j, int D, const void* K, const void* U, hipStream_t st,
                                const std::function<hipError_t(const char*, const std::function<hipError_t()>&)>& timed);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,

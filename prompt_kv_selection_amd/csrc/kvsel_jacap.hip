@@ -18,14 +18,15 @@
 //   jacap_weights  per (head, chunk): the head's partials merged in a fixed
 //                  order, then w of every token.
 //   jacap_gram     per (head, slice): the slice's part of sum w u u^T on MFMA
-//                  (v_mfma_f32_32x32x16_bf16).  x = sqrt(w) u is split into
-//                  bf16 hi + lo and x x^T ~ hi hi^T + hi lo^T + lo hi^T, about
-//                  16 significant bits per product; fp32 accumulation.
-//   jacap_factor   per head: A = I + the slices' parts, Cholesky in LDS
-//                  (fp32), then M = L^{-1} (right-looking, in LDS), stored as
-//                  bf16 hi + lo.
+//                  (v_mfma_f32_32x32x16_bf16), lower tiles only: u^T (exact
+//                  bf16) times (w u) split into bf16 hi + lo, about 16
+//                  significant bits per product; fp32 accumulation.
+//   jacap_factor   per head: A = I + the slices' parts, Cholesky (fp32), then
+//                  M = L^{-1}, both right-looking in registers (an 8 x 8
+//                  block per thread at D = 128), stored as bf16 hi + lo.
 //   jacap_leverage per (head, chunk): Y = M U^T on MFMA (hi and lo of M
-//                  against the exact bf16 u), r = w * column sums of Y^2.
+//                  against the exact bf16 u, the k-steps of the lower
+//                  triangle only), r = w * column sums of Y^2.
 // The two N d^2 contractions are the MFMA part; everything else streams K
 // and U once.
 
@@ -45,7 +46,6 @@ namespace {
 
 constexpr int kJThreads = 256;
 constexpr int kJChunk = 1024;  // tokens per logits / weights / leverage workgroup
-constexpr int kGramSub = 64;   // tokens per Gram step (LDS tile)
 constexpr float kNegBig = -1.0e30f;
 
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
@@ -159,145 +159,328 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(x - (float)hi);
 }
 
-// Part of sum_i w_i u_i u_i^T over tokens [slice * per, (slice + 1) * per) of
-// the head, into gpart[head][slice][D][D].  Tile (p, q) of the D x D result
-// (32 x 32) belongs to wave (p * (D / 32) + q) % 4; x^T (features x tokens)
-// is staged in LDS as hi and lo parts, a row of kGramSub + 8 elements.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as packed bf16 high parts (round to nearest even, one
+// v_cvt_pk_bf16_f32) and the packed bf16 of what each high part leaves over.
+__device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigned& lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+}
+
+// Lower 32 x 32 tiles (p, r), p >= r, of the D x D Gram matrix computed by
+// each of the four waves, coded p * (D / 32) + r (-1: none).  Tiles of a wave
+// share their column r where possible, so that its B operands are read once.
 template <int D>
-__global__ __launch_bounds__(kJThreads) void jacap_gram_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
-  constexpr int NT = D / 32;               // tiles per side
-  constexpr int TPW = NT * NT / 4;         // tiles per wave (4 or 1)
-  constexpr int RS = kGramSub + 8;         // LDS row stride (elements)
-  __shared__ __bf16 xh[D * RS], xl[D * RS];
-  const int head = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
-  const int per = (j.N + j.slices - 1) / j.slices;
-  const int t0 = slice * per, t1 = min(t0 + per, j.N);
-  f32x16 acc[TPW];
+__device__ constexpr int gram_tile(int wave, int q) {
+  if constexpr (D == 128) {
+    constexpr int t[4][3] = {{4, 8, 12}, {5, 9, 13}, {10, 14, 0}, {15, -1, -1}};
+    return t[wave][q];
+  } else {
+    constexpr int t[4][3] = {{0, -1, -1}, {2, -1, -1}, {3, -1, -1}, {-1, -1, -1}};
+    return t[wave][q];
+  }
+}
+
+template <int D>
+struct GramShape {
+  static constexpr int TS = D == 128 ? 64 : 128;  // tokens per step: 256 units of 4 tokens x 8 features
+  static_assert(TS / 4 * D / 8 == 256, "one unit per thread");
+  static constexpr int RS = TS + 8;               // LDS row stride (elements)
+  static constexpr int FG = D / 8;                // feature groups
+  static constexpr int ARR = D * RS;              // one operand array
+};
+
+// One step's share of a thread: 4 tokens x 8 features of U and the 4 weights.
+template <int D>
+__device__ __forceinline__ void gram_load(const JacapArgs& j, const __bf16* __restrict__ U, int head, int t, int t1,
+                                          int fg, uint4 (&d)[4], float (&w)[4]) {
+  // Tokens past the slice load its last row (their weight is zeroed when
+  // staged), so that no load sits in a branch.
 #pragma unroll
-  for (int q = 0; q < TPW; ++q) acc[q] = f32x16{};
-  for (int s0 = t0; s0 < t1; s0 += kGramSub) {
-    __syncthreads();  // the previous step's operands have been read
-    // Stage x = sqrt(w) u of kGramSub tokens, transposed: consecutive
-    // threads take consecutive tokens of one 8-feature group.
-    for (int e = tid; e < kGramSub * (D / 8); e += kJThreads) {
-      const int tk = e % kGramSub, f8 = e / kGramSub, t = s0 + tk;
-      float u[8];
-      float sw = 0.f;
-      if (t < t1) {
-        load8(U + ((long long)head * j.N + t) * D + f8 * 8, u);
-        sw = sqrtf(fmaxf(j.w[(long long)head * j.N + t], 0.f));
+  for (int i = 0; i < 4; ++i) {
+    const int tc = max(min(t + i, t1 - 1), 0);
+    d[i] = *reinterpret_cast<const uint4*>(U + ((long long)head * j.N + tc) * D + fg * 8);
+    w[i] = j.w[(long long)head * j.N + tc];
+  }
+}
+
+// Writes the share into the operand arrays (feature-major: a row per feature,
+// the step's tokens along it): u^T exactly, and (w u)^T as bf16 high + low.
+template <int D>
+__device__ __forceinline__ void gram_stage(__bf16* buf, int fg, int tg, const uint4 (&d)[4], const float (&wl)[4],
+                                           int valid) {
+  using S = GramShape<D>;
+  float w[4];  // tokens past the slice weigh 0: every product has a (w u) factor, so they add nothing
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = i < valid ? wl[i] : 0.f;
+  __bf16* ut = buf;
+  __bf16* bh = buf + S::ARR;
+  __bf16* bl = buf + 2 * S::ARR;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned x[4] = {(&d[0].x)[q], (&d[1].x)[q], (&d[2].x)[q], (&d[3].x)[q]};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // feature 8 fg + 2 q + h: the low (h = 0) or high bf16 of each word
+      const int o = (fg * 8 + 2 * q + h) * S::RS + tg * 4;
+      uint2 u2, hi2, lo2;
+      if (h == 0) {
+        u2.x = (x[0] & 0xFFFFu) | (x[1] << 16);
+        u2.y = (x[2] & 0xFFFFu) | (x[3] << 16);
       } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) u[q] = 0.f;
+        u2.x = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
+        u2.y = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
       }
+      float v[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __bf16 hi, lo;
-        split_bf16(sw * u[q], hi, lo);
-        xh[(f8 * 8 + q) * RS + tk] = hi;
-        xl[(f8 * 8 + q) * RS + tk] = lo;
+      for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(h == 0 ? x[i] << 16 : x[i] & 0xFFFF0000u) * w[i];
+      split2(v[0], v[1], hi2.x, lo2.x);
+      split2(v[2], v[3], hi2.y, lo2.y);
+      *reinterpret_cast<uint2*>(ut + o) = u2;
+      *reinterpret_cast<uint2*>(bh + o) = hi2;
+      *reinterpret_cast<uint2*>(bl + o) = lo2;
+    }
+  }
+}
+
+template <int D, int WV>
+__device__ __forceinline__ void gram_mfma(const __bf16* cur, int n, int g, f32x16 (&acc)[3]) {
+  using S = GramShape<D>;
+  constexpr int NT = D / 32;
+#pragma unroll
+  for (int k0 = 0; k0 < S::TS; k0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int tile = gram_tile<D>(WV, q);
+      if (tile >= 0) {
+        const int p = tile / NT, r = tile % NT;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + (p * 32 + n) * S::RS + k0 + 8 * g);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(cur + S::ARR + (r * 32 + n) * S::RS + k0 + 8 * g);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(cur + 2 * S::ARR + (r * 32 + n) * S::RS + k0 + 8 * g);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[q], 0, 0, 0);
       }
     }
-    __syncthreads();
+  }
+}
+
+// Part of sum_i w_i u_i u_i^T over tokens [slice * per, (slice + 1) * per) of
+// the head, into gpart[head][slice][D][D] (lower 32 x 32 tiles only).  Each
+// MFMA pair multiplies u^T (exact bf16) by the high and the low bf16 part of
+// (w u): products correct to about 2^-17 relative, fp32 accumulation.  The
+// operands of a step are staged by all 256 threads (16-byte loads of token
+// rows, transposed in registers) into one of two LDS buffers while the waves
+// multiply the other, so a step needs one barrier; the loads run kPre steps
+// ahead of the multiplications (a ring of register sets).
+constexpr int kPre = 7;
+template <int D, int WV>
+__device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __restrict__ U, __bf16* lds) {
+  using S = GramShape<D>;
+  const int head = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, n = lane & 31, g = lane >> 5;
+  // A wave stages whole feature rows: QW lanes take consecutive token quads
+  // of one feature group, so that its 8-byte LDS writes cover consecutive
+  // banks (two rows per write at most share a bank).
+  constexpr int QW = S::TS / 4;
+  const int fg = (tid >> 6) * (64 / QW) + lane / QW, tg = lane % QW;
+  const int per = (j.N + j.slices - 1) / j.slices;
+  const int t0 = min(slice * per, j.N), t1 = min(t0 + per, j.N);
+  const int steps = (t1 - t0 + S::TS - 1) / S::TS;
+  f32x16 acc[3];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int tile = wave * TPW + q;
-      const int p = tile / NT, r = tile % NT;
+  for (int q = 0; q < 3; ++q) acc[q] = f32x16{};
+  uint4 d[kPre + 1][4];
+  float w[kPre + 1][4];
 #pragma unroll
-      for (int k0 = 0; k0 < kGramSub; k0 += 16) {
-        const int ra = (p * 32 + n) * RS + k0 + 8 * g, rb = (r * 32 + n) * RS + k0 + 8 * g;
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&xh[ra]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&xl[ra]);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&xh[rb]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&xl[rb]);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[q], 0, 0, 0);
+  for (int u = 0; u < kPre; ++u) gram_load<D>(j, U, head, t0 + u * S::TS + tg * 4, t1, fg, d[u], w[u]);
+  if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 4));
+  __syncthreads();
+  // Step st multiplies buffer st & 1, loads step st + kPre into register set
+  // (st + kPre) % (kPre + 1) and stages step st + 1 from set (st + 1) % (kPre + 1).
+  // Loads and staging past the last step are harmless (rows clamped to the
+  // slice, buffers never multiplied), so a step has no branch and the
+  // scheduler can interleave the staging arithmetic with the MFMAs.
+  for (int s0 = 0; s0 < steps; s0 += 2 * (kPre + 1)) {
+#pragma unroll
+    for (int u = 0; u < 2 * (kPre + 1); ++u) {
+      const int st = s0 + u;
+      if (st < steps) {
+        constexpr int R = kPre + 1;
+        gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
+        gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
+        gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
+                      t1 - (t0 + (st + 1) * S::TS + tg * 4));
+        __syncthreads();
       }
     }
   }
   float* out = j.gpart + ((long long)head * j.slices + slice) * D * D;
 #pragma unroll
-  for (int q = 0; q < TPW; ++q) {
-    const int tile = wave * TPW + q;
-    const int p = tile / NT, r = tile % NT;
+  for (int q = 0; q < 3; ++q) {
+    constexpr int NT = D / 32;
+    const int tile = gram_tile<D>(WV, q);
+    if (tile >= 0) {
+      const int p = tile / NT, r = tile % NT;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) out[(p * 32 + acc_row(e, g)) * D + r * 32 + n] = acc[q][e];
+      for (int e = 0; e < 16; ++e) out[(p * 32 + acc_row(e, g)) * D + r * 32 + n] = acc[q][e];
+    }
   }
 }
 
-// A = I + the slices' parts; Cholesky A = L L^T in LDS (fp32, column by
-// column); M = L^{-1} by forward substitution (a column of M per thread);
-// M stored as bf16 hi and lo, row-major, for the leverage contraction.
+template <int D>
+__global__ __launch_bounds__(kJThreads) void jacap_gram_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 3 * GramShape<D>::ARR];
+  switch (threadIdx.x >> 6) {  // every wave runs the same steps and barriers
+    case 0: gram_body<D, 0>(j, U, lds); break;
+    case 1: gram_body<D, 1>(j, U, lds); break;
+    case 2: gram_body<D, 2>(j, U, lds); break;
+    default: gram_body<D, 3>(j, U, lds); break;
+  }
+}
+
+// A = I + the slices' parts, then A = L L^T (Cholesky, fp32) and M = L^{-1},
+// both right-looking and held in registers: the 256 threads form a 16 x 16
+// grid and thread (ti, tj) owns the B x B block (B = D / 16) at rows ti * B,
+// columns tj * B of A (then L) and of M.  Step c of the factorisation: the
+// owners of column c publish it to LDS; every thread scales it by
+// 1 / sqrt(A[c][c]) and removes L[r][c] L[k][c] from its entries with r, k > c
+// (the whole trailing square, which stays symmetric).  Step k of the inverse
+// (L M = I): the owners of row k of M publish it divided by L[k][k] and the
+// owners of column k of L publish that column; every thread removes
+// L[i][k] M[k][j] from its rows i > k.  The published vectors are double
+// buffered, so each step needs one barrier.  M is stored as bf16 hi and lo.
 template <int D>
 __global__ __launch_bounds__(kJThreads) void jacap_factor_kernel(const JacapArgs j) {
-  __shared__ float a[D * (D + 1)];  // row stride D + 1
-  constexpr int S = D + 1;
+  constexpr int B = D / 16;
+  __shared__ float colv[2][D], rowv[2][D];
   const int head = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < D * D; e += kJThreads) {
-    const int r = e / D, c = e % D;
-    float v = r == c ? 1.f : 0.f;
-    for (int s = 0; s < j.slices; ++s) v += j.gpart[(((long long)head * j.slices + s) * D + r) * D + c];
-    a[r * S + c] = v;
+  const int ti = tid / 16, tj = tid % 16;
+  float a[B][B], m[B][B], rd[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i)
+#pragma unroll
+    for (int q = 0; q < B; ++q) a[i][q] = (ti * B + i == tj * B + q) ? 1.f : 0.f;
+  const float* gp = j.gpart + (long long)head * j.slices * D * D;
+  // Only the lower 32 x 32 tiles are written by the Gram kernel (and only the
+  // lower triangle is read below); blocks of the upper tiles stay zero.
+  const int nsl = (ti * B) / 32 >= (tj * B) / 32 ? j.slices : 0;
+  for (int s = 0; s < nsl; ++s) {  // the slices in order: the same sum on every call
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const float* row = gp + ((long long)s * D + ti * B + i) * D + tj * B;
+#pragma unroll
+      for (int q = 0; q < B; q += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + q);
+        a[i][q] += v.x;
+        a[i][q + 1] += v.y;
+        a[i][q + 2] += v.z;
+        a[i][q + 3] += v.w;
+      }
+    }
   }
-  __syncthreads();
-  __shared__ int s_bad;
-  if (tid == 0) s_bad = 0;
-  for (int c = 0; c < D; ++c) {
-    if (tid == 0) {
-      const float d = a[c * S + c];
-      if (!(d > 0.f) || !isfinite(d)) s_bad = 1;
-      a[c * S + c] = sqrtf(fmaxf(d, 1e-30f));
+  bool bad = false;
+  for (int cb = 0; cb < 16; ++cb) {
+#pragma unroll
+    for (int jj = 0; jj < B; ++jj) {
+      const int c = cb * B + jj;
+      float* cv = colv[c & 1];
+      if (tj == cb) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) cv[ti * B + i] = a[i][jj];
+      }
+      __syncthreads();
+      const float d = cv[c];
+      bad |= !(d > 0.f && isfinite(d));
+      const float sq = sqrtf(fmaxf(d, 1e-30f)), inv = 1.f / sq;
+      float lr[B], lk[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const float v = cv[ti * B + i] * inv;
+        lr[i] = ti * B + i > c ? v : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const float v = cv[tj * B + q] * inv;
+        lk[q] = tj * B + q > c ? v : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q) a[i][q] = fmaf(-lr[i], lk[q], a[i][q]);
+      if (tj == cb) {  // column c of L: below the diagonal, the diagonal, zeros above
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          const int r = ti * B + i;
+          a[i][jj] = r > c ? lr[i] : (r == c ? sq : 0.f);
+        }
+      }
+      if (ti == cb) rd[jj] = inv;  // 1 / L[c][c] for the owners of row c
     }
-    __syncthreads();
-    const float inv = 1.f / a[c * S + c];
-    for (int r = c + 1 + tid; r < D; r += kJThreads) a[r * S + c] *= inv;
-    __syncthreads();
-    // Trailing update of the lower triangle: (r, k) with c < k <= r.
-    const int rem = D - c - 1;
-    for (int e = tid; e < rem * rem; e += kJThreads) {
-      const int r = c + 1 + e / rem, k = c + 1 + e % rem;
-      if (k <= r) a[r * S + k] -= a[r * S + c] * a[k * S + c];
-    }
-    __syncthreads();
   }
-  if (tid == 0 && s_bad) raise_error(j.err, kErrNonFinite);
-  // M = L^{-1}, right-looking: start from I; step k scales row k by 1/L[k][k]
-  // and removes L[i][k] times row k from every row i > k (columns <= k are
-  // the only non-zero ones of row k).
-  __shared__ float m[D * (D + 1)];
-  for (int e = tid; e < D * D; e += kJThreads) m[(e / D) * S + e % D] = (e / D == e % D) ? 1.f : 0.f;
-  __syncthreads();
-  for (int k = 0; k < D; ++k) {
-    const float inv = 1.f / a[k * S + k];
-    for (int c2 = tid; c2 <= k; c2 += kJThreads) m[k * S + c2] *= inv;
-    __syncthreads();
-    const int rows = D - k - 1, cols = k + 1;
-    for (int e = tid; e < rows * cols; e += kJThreads) {
-      const int i = k + 1 + e / cols, c2 = e % cols;
-      m[i * S + c2] -= a[i * S + k] * m[k * S + c2];
+  if (bad && tid == 0) raise_error(j.err, kErrNonFinite);  // every thread saw the same pivots
+#pragma unroll
+  for (int i = 0; i < B; ++i)
+#pragma unroll
+    for (int q = 0; q < B; ++q) m[i][q] = (ti * B + i == tj * B + q) ? 1.f : 0.f;
+  for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < B; ++kk) {
+      const int k = kb * B + kk;
+      float* cv = colv[k & 1];
+      float* rv = rowv[k & 1];
+      if (ti == kb) {
+#pragma unroll
+        for (int q = 0; q < B; ++q) rv[tj * B + q] = m[kk][q] * rd[kk];
+      }
+      if (tj == kb) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) cv[ti * B + i] = a[i][kk];
+      }
+      __syncthreads();
+      float lr[B], mk[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) lr[i] = ti * B + i > k ? cv[ti * B + i] : 0.f;
+#pragma unroll
+      for (int q = 0; q < B; ++q) mk[q] = rv[tj * B + q];
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+#pragma unroll
+        for (int q = 0; q < B; ++q) m[i][q] = fmaf(-lr[i], mk[q], m[i][q]);
+      if (ti == kb) {
+#pragma unroll
+        for (int q = 0; q < B; ++q) m[kk][q] = mk[q];
+      }
     }
-    __syncthreads();
   }
   __bf16* mh = j.minv + (long long)head * 2 * D * D;
   __bf16* ml = mh + D * D;
-  for (int e = tid; e < D * D; e += kJThreads) {
-    __bf16 hi, lo;
-    split_bf16(m[(e / D) * S + e % D], hi, lo);
-    mh[e] = hi;
-    ml[e] = lo;
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    __bf16 h8[B], l8[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) split_bf16(m[i][q], h8[q], l8[q]);
+    const long long o = (long long)(ti * B + i) * D + tj * B;
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      mh[o + q] = h8[q];
+      ml[o + q] = l8[q];
+    }
   }
 }
 
-// r_t = w_t |M u_t|^2 for the chunk's tokens: per 32-token block, Y = M U^T
-// as (D / 32) tiles of 32 x 32, M's hi and lo against the exact bf16 u, and
-// each lane sums the squares of its rows; the two halves of the wave hold
+// r_t = w_t |M u_t|^2 for the chunk's tokens: Y = M U^T on MFMA, a wave
+// taking 64 tokens at a time as two 32-token column groups that share every
+// M operand read; row tile p of M (lower triangular) only needs the k-steps
+// up to its diagonal.  M's high and low parts multiply the exact bf16 u; each
+// lane sums the squares of its rows of Y and the two halves of the wave hold
 // the other rows of the same tokens.  M (hi, lo) is staged in LDS.
 template <int D>
 __global__ __launch_bounds__(kJThreads) void jacap_leverage_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
   constexpr int RS = D + 8;
-  __shared__ __bf16 mh[D * RS], ml[D * RS];
+  constexpr int KS = D / 16;  // k-steps of a full row
+  __shared__ __attribute__((aligned(16))) __bf16 mh[D * RS], ml[D * RS];
   const int head = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
   const __bf16* gm = j.minv + (long long)head * 2 * D * D;
@@ -308,31 +491,46 @@ __global__ __launch_bounds__(kJThreads) void jacap_leverage_kernel(const JacapAr
   }
   __syncthreads();
   const int t0 = c * kJChunk, t1 = min(t0 + kJChunk, j.N);
-  for (int b0 = t0 + wave * 32; b0 < t1; b0 += 4 * 32) {
-    const int t = min(b0 + n, t1 - 1);  // rows past the chunk repeat its last token (not written)
-    const __bf16* ur = U + ((long long)head * j.N + t) * D;
-    bf16x8 ub[D / 16];  // the token's u, loaded once for all row tiles
+  for (int b0 = t0 + wave * 64; b0 < t1; b0 += 4 * 64) {
+    // M's operands are read from LDS in every pass (kept out of registers
+    // across passes, which leaves room for a second workgroup per CU).
+    asm volatile("" ::: "memory");
+    bf16x8 ub[2][KS];  // the two groups' u, loaded once for all row tiles
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) ub[k] = *reinterpret_cast<const bf16x8*>(ur + 16 * k + 8 * g);
-    float sq = 0.f;
+    for (int cg = 0; cg < 2; ++cg) {
+      const int t = min(b0 + cg * 32 + n, t1 - 1);  // columns past the chunk repeat its last token (not written)
+      const __bf16* ur = U + ((long long)head * j.N + t) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ub[cg][k] = *reinterpret_cast<const bf16x8*>(ur + 16 * k + 8 * g);
+    }
+    float sq[2] = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < D / 32; ++p) {
-      f32x16 acc = {};
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int k = 0; k < D / 16; ++k) {
+      for (int k = 0; k < 2 * (p + 1); ++k) {  // M[row][col] = 0 for col > row
         const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&mh[(p * 32 + n) * RS + 16 * k + 8 * g]);
         const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ml[(p * 32 + n) * RS + 16 * k + 8 * g]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ub[k], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, ub[k], acc, 0, 0, 0);
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+          acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ub[cg][k], acc[cg], 0, 0, 0);
+          acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, ub[cg][k], acc[cg], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sq = fmaf(acc[e], acc[e], sq);
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sq[cg] = fmaf(acc[cg][e], acc[cg][e], sq[cg]);
     }
-    const float other = __shfl_xor(sq, 32);
-    const float tot = g == 0 ? sq + other : other + sq;
-    if (g == 0 && b0 + n < t1) {
-      const long long i = (long long)head * j.N + b0 + n;
-      j.r[i] = j.w[i] * tot;
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      const float other = __shfl_xor(sq[cg], 32);
+      const float tot = g == 0 ? sq[cg] + other : other + sq[cg];
+      const int t = b0 + cg * 32 + n;
+      if (g == 0 && t < t1) {
+        const long long i = (long long)head * j.N + t;
+        j.r[i] = j.w[i] * tot;
+      }
     }
   }
 }
@@ -371,7 +569,12 @@ hipError_t launch_all(const JacapArgs& j, const __bf16* K, const __bf16* U, hipS
 }  // namespace
 
 int jacap_chunks(int N) { return (N + kJChunk - 1) / kJChunk; }
-int jacap_slices(int N) { return std::max(1, std::min(32, (N + 2047) / 2048)); }
+// Gram slices per head: about one workgroup per CU over all heads, each slice
+// at least 512 tokens, at most 32 slices.
+int jacap_slices(int N, int heads) {
+  const int fill = (256 + heads - 1) / heads;
+  return std::max(1, std::min({32, fill, (N + 511) / 512}));
+}
 
 hipError_t launch_jacap_scores(const JacapArgs& j, int D, const void* K, const void* U, hipStream_t st,
                                const std::function<hipError_t(const char*, const std::function<hipError_t()>&)>& timed) {
