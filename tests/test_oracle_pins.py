@@ -353,6 +353,23 @@ def test_jacap_sensitivity_closed_forms():
     np.testing.assert_allclose(sc["alpha"], 0.2, rtol=1e-14)
 
 
+def test_jacap_logit_and_curvature_closed_forms():
+    """Hand-computed values: keys (2, 0, 0, 0) and 0 with mu = e_0, tau = 0.5
+    and d_k = 4 give centre logits 2 / (0.5 * 2) = 2 and 0, so alpha_0 =
+    e^2 / (e^2 + 1); with Lambda = (3, 5, 7, 11) the key (1, 2, 0, 0) has
+    kappa = 3 + 20 = 23; w = [alpha (1 - alpha)]^2 kappa / 4."""
+    keys = np.array([[2.0, 0, 0, 0], [0.0, 0, 0, 0]])
+    sc = O.jacap_scores(keys, np.eye(2), np.eye(4)[0], np.array([3.0, 5, 7, 11]), 0.5)
+    np.testing.assert_allclose(sc["z"], [2.0, 0.0], rtol=1e-15)
+    a0 = math.exp(2) / (math.exp(2) + 1)
+    np.testing.assert_allclose(sc["alpha"], [a0, 1 - a0], rtol=1e-14)
+    np.testing.assert_allclose(sc["kappa"], [12.0, 0.0], rtol=1e-15)      # 3 * 2^2
+    sc = O.jacap_scores(np.array([[1.0, 2, 0, 0], [0.0, 0, 0, 0]]), np.eye(2), np.zeros(4),
+                        np.array([3.0, 5, 7, 11]), 1.0)
+    np.testing.assert_allclose(sc["kappa"], [23.0, 0.0], rtol=1e-15)
+    np.testing.assert_allclose(sc["w"], [(0.25 ** 2) * 23 / 4, 0.0], rtol=1e-14)   # equal logits: alpha = 1/2
+
+
 def jacap_toy():
     """The page's 2-D miniature: u1 = (1, 0), u2 = (0.95, 0.05), u3 = (0, 1)
     with w = (1, 1, 0.7), realised through keys whose weights come out
