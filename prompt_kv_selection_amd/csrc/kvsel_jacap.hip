@@ -22,8 +22,8 @@
 //                  bf16) times (w u) split into bf16 hi + lo, about 16
 //                  significant bits per product; fp32 accumulation.
 //   jacap_factor   per head: A = I + the slices' parts, Cholesky (fp32), then
-//                  M = L^{-1}, both right-looking in registers (an 8 x 8
-//                  block per thread at D = 128), stored as bf16 hi + lo.
+//                  M = L^{-1}, both blocked by 8-column panels in LDS,
+//                  stored as bf16 hi + lo.
 //   jacap_leverage per (head, chunk): Y = M U^T on MFMA (hi and lo of M
 //                  against the exact bf16 u, the k-steps of the lower
 //                  triangle only), r = w * column sums of Y^2.
@@ -341,132 +341,248 @@ __global__ __launch_bounds__(kJThreads) void jacap_gram_kernel(const JacapArgs j
 }
 
 // A = I + the slices' parts, then A = L L^T (Cholesky, fp32) and M = L^{-1},
-// both right-looking and held in registers: the 256 threads form a 16 x 16
-// grid and thread (ti, tj) owns the B x B block (B = D / 16) at rows ti * B,
-// columns tj * B of A (then L) and of M.  Step c of the factorisation: the
-// owners of column c publish it to LDS; every thread scales it by
-// 1 / sqrt(A[c][c]) and removes L[r][c] L[k][c] from its entries with r, k > c
-// (the whole trailing square, which stays symmetric).  Step k of the inverse
-// (L M = I): the owners of row k of M publish it divided by L[k][k] and the
-// owners of column k of L publish that column; every thread removes
-// L[i][k] M[k][j] from its rows i > k.  The published vectors are double
-// buffered, so each step needs one barrier.  M is stored as bf16 hi and lo.
+// blocked by 8-column panels with A, L and M in LDS (row stride D + 4 floats:
+// 16-byte aligned rows, consecutive rows four banks apart).  Per panel p,
+// three barriers:
+//   1. lanes 0-7 (a row each) factor the 8 x 8 diagonal block and invert it;
+//   2. the rows below are solved against that inverse (a row per thread), and
+//      block row p of M is inv(L_pp) times the running block row;
+//   3. the trailing lower triangle takes the rank-8 update in 4 x 4 units
+//      spread over the threads, and so do the rows of M below (L M = I
+//      right-looking: X_i -= L_ip M_p).
+// Only lower triangles are computed; the upper parts hold zeros.  M is stored
+// as bf16 hi and lo.
 template <int D>
-__global__ __launch_bounds__(kJThreads) void jacap_factor_kernel(const JacapArgs j) {
-  constexpr int B = D / 16;
-  __shared__ float colv[2][D], rowv[2][D];
+__global__ __launch_bounds__(kJThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void jacap_factor_kernel(const JacapArgs j) {
+  constexpr int S = D + 4;
+  constexpr int P = D / 8;
+  __shared__ __attribute__((aligned(16))) float a[D * S];
+  __shared__ __attribute__((aligned(16))) float m[D * S];
+  __shared__ __attribute__((aligned(16))) float li[64];   // inverse of the current diagonal block
+  __shared__ __attribute__((aligned(16))) float tt[8 * D];  // block row p of M
   const int head = blockIdx.x, tid = threadIdx.x;
-  const int ti = tid / 16, tj = tid % 16;
-  float a[B][B], m[B][B], rd[B];
-#pragma unroll
-  for (int i = 0; i < B; ++i)
-#pragma unroll
-    for (int q = 0; q < B; ++q) a[i][q] = (ti * B + i == tj * B + q) ? 1.f : 0.f;
   const float* gp = j.gpart + (long long)head * j.slices * D * D;
-  // Only the lower 32 x 32 tiles are written by the Gram kernel (and only the
-  // lower triangle is read below); blocks of the upper tiles stay zero.
-  const int nsl = (ti * B) / 32 >= (tj * B) / 32 ? j.slices : 0;
-  for (int s = 0; s < nsl; ++s) {  // the slices in order: the same sum on every call
+  // A = I + the slices' lower parts (the Gram kernel writes the lower 32 x 32
+  // tiles; only the lower triangle is read).
+  {
+    constexpr int E4 = D * D / 4 / kJThreads;  // float4 groups per thread: g = tid + kJThreads * t
+    float4 v[E4];
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const float* row = gp + ((long long)s * D + ti * B + i) * D + tj * B;
-#pragma unroll
-      for (int q = 0; q < B; q += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + q);
-        a[i][q] += v.x;
-        a[i][q + 1] += v.y;
-        a[i][q + 2] += v.z;
-        a[i][q + 3] += v.w;
-      }
+    for (int t = 0; t < E4; ++t) {
+      const int e = 4 * (tid + kJThreads * t), r = e / D, c = e % D;
+      v[t] = make_float4(r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f, r == c + 2 ? 1.f : 0.f, r == c + 3 ? 1.f : 0.f);
     }
-  }
-  bool bad = false;
-  for (int cb = 0; cb < 16; ++cb) {
+    const float4* g4 = reinterpret_cast<const float4*>(gp);
+    for (int q = 0; q < j.slices; q += 2) {  // slices in order, two per batch of loads
+      const int q1 = min(q + 1, j.slices - 1);
+      float4 x0[E4], x1[E4];
 #pragma unroll
-    for (int jj = 0; jj < B; ++jj) {
-      const int c = cb * B + jj;
-      float* cv = colv[c & 1];
-      if (tj == cb) {
-#pragma unroll
-        for (int i = 0; i < B; ++i) cv[ti * B + i] = a[i][jj];
+      for (int t = 0; t < E4; ++t) {
+        x0[t] = g4[(long long)q * D * D / 4 + tid + kJThreads * t];
+        x1[t] = g4[(long long)q1 * D * D / 4 + tid + kJThreads * t];
       }
-      __syncthreads();
-      const float d = cv[c];
-      bad |= !(d > 0.f && isfinite(d));
-      const float sq = sqrtf(fmaxf(d, 1e-30f)), inv = 1.f / sq;
-      float lr[B], lk[B];
+      const bool two = q + 1 < j.slices;
 #pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const float v = cv[ti * B + i] * inv;
-        lr[i] = ti * B + i > c ? v : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < B; ++q) {
-        const float v = cv[tj * B + q] * inv;
-        lk[q] = tj * B + q > c ? v : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-#pragma unroll
-        for (int q = 0; q < B; ++q) a[i][q] = fmaf(-lr[i], lk[q], a[i][q]);
-      if (tj == cb) {  // column c of L: below the diagonal, the diagonal, zeros above
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-          const int r = ti * B + i;
-          a[i][jj] = r > c ? lr[i] : (r == c ? sq : 0.f);
+      for (int t = 0; t < E4; ++t) {
+        v[t].x += x0[t].x;
+        v[t].y += x0[t].y;
+        v[t].z += x0[t].z;
+        v[t].w += x0[t].w;
+        if (two) {
+          v[t].x += x1[t].x;
+          v[t].y += x1[t].y;
+          v[t].z += x1[t].z;
+          v[t].w += x1[t].w;
         }
       }
-      if (ti == cb) rd[jj] = inv;  // 1 / L[c][c] for the owners of row c
+    }
+#pragma unroll
+    for (int t = 0; t < E4; ++t) {  // upper elements (never written by the Gram kernel) are dropped
+      const int e = 4 * (tid + kJThreads * t), r = e / D, c = e % D;
+      *reinterpret_cast<float4*>(a + r * S + c) =
+          make_float4(c <= r ? v[t].x : 0.f, c + 1 <= r ? v[t].y : 0.f, c + 2 <= r ? v[t].z : 0.f,
+                      c + 3 <= r ? v[t].w : 0.f);
+      *reinterpret_cast<float4*>(m + r * S + c) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  if (bad && tid == 0) raise_error(j.err, kErrNonFinite);  // every thread saw the same pivots
-#pragma unroll
-  for (int i = 0; i < B; ++i)
-#pragma unroll
-    for (int q = 0; q < B; ++q) m[i][q] = (ti * B + i == tj * B + q) ? 1.f : 0.f;
-  for (int kb = 0; kb < 16; ++kb) {
-#pragma unroll
-    for (int kk = 0; kk < B; ++kk) {
-      const int k = kb * B + kk;
-      float* cv = colv[k & 1];
-      float* rv = rowv[k & 1];
-      if (ti == kb) {
-#pragma unroll
-        for (int q = 0; q < B; ++q) rv[tj * B + q] = m[kk][q] * rd[kk];
+  __syncthreads();
+  bool bad = false;
+  for (int p = 0; p < P; ++p) {
+    const int k0 = p * 8;
+    if (tid < 8) {  // the diagonal block: lane i of wave 0 holds row i; Cholesky and inverse
+      float x[8], y[8];
+      {
+        const float4 u0 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0);
+        const float4 u1 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0 + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
       }
-      if (tj == kb) {
+      float rsi = 0.f;  // 1 / L[i][i] of this lane's row
 #pragma unroll
-        for (int i = 0; i < B; ++i) cv[ti * B + i] = a[i][kk];
+      for (int c = 0; c < 8; ++c) {
+        const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), c));
+        bad |= !(d > 0.f && isfinite(d));
+        const float dd = fmaxf(d, 1e-30f);
+        const float rs = __builtin_amdgcn_rsqf(dd);
+        if (tid == c) {
+          x[c] = dd * rs;
+          rsi = rs;
+        } else if (tid > c) {
+          x[c] *= rs;
+        }
+        // Column c of L below the diagonal, broadcast: row q's entry from lane q.
+#pragma unroll
+        for (int q = c + 1; q < 8; ++q) {
+          const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), q));
+          if (tid >= q) x[q] = fmaf(-x[c], lq, x[q]);
+        }
       }
-      __syncthreads();
-      float lr[B], mk[B];
+      // Row i of inv(L): y[q] = -rs_i sum_{k=q}^{i-1} L[i][k] y_k[q], rows in order
+      // (row k's entries broadcast from lane k once it is final).
 #pragma unroll
-      for (int i = 0; i < B; ++i) lr[i] = ti * B + i > k ? cv[ti * B + i] : 0.f;
+      for (int q = 0; q < 8; ++q) y[q] = 0.f;
 #pragma unroll
-      for (int q = 0; q < B; ++q) mk[q] = rv[tj * B + q];
+      for (int k = 0; k < 8; ++k) {
+        if (tid == k) {
 #pragma unroll
-      for (int i = 0; i < B; ++i)
+          for (int q = 0; q < 8; ++q) y[q] = q < k ? -y[q] * rsi : (q == k ? rsi : 0.f);
+        }
 #pragma unroll
-        for (int q = 0; q < B; ++q) m[i][q] = fmaf(-lr[i], mk[q], m[i][q]);
-      if (ti == kb) {
+        for (int q = 0; q <= k; ++q) {
+          const float yk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(y[q]), k));
+          if (tid > k) y[q] = fmaf(x[k], yk, y[q]);  // accumulates sum_k L[i][k] y_k[q]
+        }
+      }
 #pragma unroll
-        for (int q = 0; q < B; ++q) m[kk][q] = mk[q];
+      for (int q = 0; q < 8; ++q) x[q] = q <= tid ? x[q] : 0.f;
+      float* ar = a + (k0 + tid) * S + k0;
+      float* mr = m + (k0 + tid) * S + k0;
+      *reinterpret_cast<float4*>(ar) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(ar + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      *reinterpret_cast<float4*>(mr) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4*>(mr + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<float4*>(li + tid * 8) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4*>(li + tid * 8 + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    }
+    __syncthreads();
+    // Rows below: L[r][k0 + q] = sum_c A[r][k0 + c] inv(L_pp)[q][c].
+    const int r = k0 + 8 + tid;
+    if (r < D) {
+      float* row = a + r * S + k0;
+      const float4 v0 = *reinterpret_cast<const float4*>(row), v1 = *reinterpret_cast<const float4*>(row + 4);
+      const float y[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c <= q; ++c) t = fmaf(y[c], li[q * 8 + c], t);
+        o[q] = t;
+      }
+      *reinterpret_cast<float4*>(row) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(row + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+    // Block row p of M: inv(L_pp) times the running block row (rows k0 ..
+    // k0 + 7 of m, which hold minus the earlier panels' contributions left of
+    // the diagonal), into tt; the diagonal block is inv(L_pp) itself.
+    for (int u = tid; u < 2 * k0 + 16; u += kJThreads) {
+      const int ii = u % 8, c0 = (u / 8) * 4;
+      float o[4] = {0.f, 0.f, 0.f, 0.f};
+      if (c0 < k0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float l = li[ii * 8 + q];  // zero for q > ii
+          const float4 xv = *reinterpret_cast<const float4*>(m + (k0 + q) * S + c0);
+          o[0] = fmaf(l, xv.x, o[0]);
+          o[1] = fmaf(l, xv.y, o[1]);
+          o[2] = fmaf(l, xv.z, o[2]);
+          o[3] = fmaf(l, xv.w, o[3]);
+        }
+      } else {
+        const float4 lv = *reinterpret_cast<const float4*>(li + ii * 8 + (c0 - k0));
+        o[0] = lv.x; o[1] = lv.y; o[2] = lv.z; o[3] = lv.w;
+      }
+      *reinterpret_cast<float4*>(tt + ii * D + c0) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    __syncthreads();
+    // Trailing lower triangle, 4 x 4 units (rb >= cb) of rows/columns k0 + 8 ...
+    const int T = (D - k0 - 8) / 4;
+    for (int q = tid; q < T * (T + 1) / 2; q += kJThreads) {
+      int rb = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+      while (rb * (rb + 1) / 2 > q) --rb;
+      while ((rb + 1) * (rb + 2) / 2 <= q) ++rb;
+      const int cb = q - rb * (rb + 1) / 2;
+      const int r0 = k0 + 8 + 4 * rb, c0 = k0 + 8 + 4 * cb;
+      float lr[4][8], lc[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 u0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
+        const float4 u1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
+        const float4 w0 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0);
+        const float4 w1 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0 + 4);
+        lr[i][0] = u0.x; lr[i][1] = u0.y; lr[i][2] = u0.z; lr[i][3] = u0.w;
+        lr[i][4] = u1.x; lr[i][5] = u1.y; lr[i][6] = u1.z; lr[i][7] = u1.w;
+        lc[i][0] = w0.x; lc[i][1] = w0.y; lc[i][2] = w0.z; lc[i][3] = w0.w;
+        lc[i][4] = w1.x; lc[i][5] = w1.y; lc[i][6] = w1.z; lc[i][7] = w1.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = a + (r0 + i) * S + c0;
+        float4 v = *reinterpret_cast<const float4*>(dst);
+        float o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[q2] = fmaf(-lr[i][k], lc[q2][k], o[q2]);
+        if (rb == cb) {  // keep the upper part of a diagonal unit at zero
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) o[q2] = q2 <= i ? o[q2] : 0.f;
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
+    // Rows below of the running M: X[i][c] -= sum_k L[i][k0 + k] M_p[k][c] for
+    // c < k0 + 8 (4 x 4 units); block row p of M moves from tt into m.
+    {
+      const int RQ = (D - k0 - 8) / 4, CQ = (k0 + 8) / 4;
+      for (int u = tid; u < RQ * CQ; u += kJThreads) {
+        const int r0 = k0 + 8 + 4 * (u / CQ), c0 = 4 * (u % CQ);
+        float4 tv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tv[k] = *reinterpret_cast<const float4*>(tt + k * D + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 l0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
+          const float4 l1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
+          const float l[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+          float* dst = m + (r0 + i) * S + c0;
+          float4 x = *reinterpret_cast<const float4*>(dst);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            x.x = fmaf(-l[k], tv[k].x, x.x);
+            x.y = fmaf(-l[k], tv[k].y, x.y);
+            x.z = fmaf(-l[k], tv[k].z, x.z);
+            x.w = fmaf(-l[k], tv[k].w, x.w);
+          }
+          *reinterpret_cast<float4*>(dst) = x;
+        }
+      }
+      for (int u = tid; u < 2 * k0; u += kJThreads) {
+        const int ii = u % 8, c0 = (u / 8) * 4;
+        *reinterpret_cast<float4*>(m + (k0 + ii) * S + c0) = *reinterpret_cast<const float4*>(tt + ii * D + c0);
+      }
+    }
+    __syncthreads();
   }
+  if (bad) raise_error(j.err, kErrNonFinite);  // thread 0 checked every pivot
   __bf16* mh = j.minv + (long long)head * 2 * D * D;
   __bf16* ml = mh + D * D;
-#pragma unroll
-  for (int i = 0; i < B; ++i) {
-    __bf16 h8[B], l8[B];
-#pragma unroll
-    for (int q = 0; q < B; ++q) split_bf16(m[i][q], h8[q], l8[q]);
-    const long long o = (long long)(ti * B + i) * D + tj * B;
-#pragma unroll
-    for (int q = 0; q < B; ++q) {
-      mh[o + q] = h8[q];
-      ml[o + q] = l8[q];
-    }
+  for (int e = tid; e < D * D; e += kJThreads) {
+    __bf16 hi, lo;
+    split_bf16(m[(e / D) * S + e % D], hi, lo);
+    mh[e] = hi;
+    ml[e] = lo;
   }
 }
 
