@@ -221,8 +221,10 @@ def jacap_alg(name, H, N, D, S):
         return H * N * 12, 0
     if name == "jacap_gram":        # U once, w, the slices' D x D parts out
         return H * N * D * e + H * N * 4 + H * S * D * D * 4, 2 * H * N * D * D
-    if name == "jacap_factor":      # the parts in, L^-1 (high, low) out
-        return H * S * D * D * 4 + H * D * D * 4, H * D ** 3 // 3 * 2
+    if name == "jacap_reduce":      # the slices' lower tiles in, their sum out
+        return (S + 1) * H * D * D * 4 * 10 // 16, (S - 1) * H * D * D * 10 // 16
+    if name == "jacap_factor":      # the summed Gram matrix in, L^-1 (high, low) out
+        return H * D * D * 4 + H * D * D * 4, H * D ** 3 // 3 * 2
     if name == "jacap_leverage":    # U once, w in, r out, L^-1
         return H * N * D * e + H * N * 8 + H * D * D * 4, 2 * H * N * D * D
     return None, None

@@ -21,7 +21,8 @@
 //                  (v_mfma_f32_32x32x16_bf16), lower tiles only: u^T (exact
 //                  bf16) times (w u) split into bf16 hi + lo, about 16
 //                  significant bits per product; fp32 accumulation.
-//   jacap_factor   per head: A = I + the slices' parts, Cholesky (fp32), then
+//   jacap_reduce   per (head, part): the slices' parts summed in slice order.
+//   jacap_factor   per head: A = I + the Gram matrix, Cholesky (fp32), then
 //                  M = L^{-1}, both blocked by 8-column panels in LDS,
 //                  stored as bf16 hi + lo.
 //   jacap_leverage per (head, chunk): Y = M U^T on MFMA (hi and lo of M
@@ -340,6 +341,30 @@ __global__ __launch_bounds__(kJThreads) void jacap_gram_kernel(const JacapArgs j
   }
 }
 
+// The slices' parts of each head summed in slice order into slice 0 (lower
+// 32 x 32 tiles only: the Gram kernel writes no others), so that the
+// factorisation reads one D x D matrix.  Grid (kRedParts, heads); a float4
+// per thread and pass.
+constexpr int kRedParts = 16;
+template <int D>
+__global__ __launch_bounds__(kJThreads) void jacap_reduce_kernel(const JacapArgs j) {
+  constexpr int G4 = D * D / 4 / kRedParts;  // float4 groups per workgroup
+  float4* g = reinterpret_cast<float4*>(j.gpart + (long long)blockIdx.y * j.slices * D * D);
+  for (int i = threadIdx.x; i < G4; i += kJThreads) {
+    const int e4 = blockIdx.x * G4 + i, r = (4 * e4) / D, c = (4 * e4) % D;
+    if (r / 32 < c / 32) continue;  // upper tile
+    float4 v = g[e4];
+    for (int q = 1; q < j.slices; ++q) {
+      const float4 x = g[(long long)q * D * D / 4 + e4];
+      v.x += x.x;
+      v.y += x.y;
+      v.z += x.z;
+      v.w += x.w;
+    }
+    g[e4] = v;
+  }
+}
+
 // A = I + the slices' parts, then A = L L^T (Cholesky, fp32) and M = L^{-1},
 // blocked by 8-column panels with A, L and M in LDS (row stride D + 4 floats:
 // 16-byte aligned rows, consecutive rows four banks apart).  Per panel p,
@@ -363,8 +388,8 @@ void jacap_factor_kernel(const JacapArgs j) {
   __shared__ __attribute__((aligned(16))) float tt[8 * D];  // block row p of M
   const int head = blockIdx.x, tid = threadIdx.x;
   const float* gp = j.gpart + (long long)head * j.slices * D * D;
-  // A = I + the slices' lower parts (the Gram kernel writes the lower 32 x 32
-  // tiles; only the lower triangle is read).
+  // A = I + the summed Gram matrix (its lower 32 x 32 tiles are written; only
+  // the lower triangle is read).
   {
     constexpr int E4 = D * D / 4 / kJThreads;  // float4 groups per thread: g = tid + kJThreads * t
     float4 v[E4];
@@ -373,29 +398,14 @@ void jacap_factor_kernel(const JacapArgs j) {
       const int e = 4 * (tid + kJThreads * t), r = e / D, c = e % D;
       v[t] = make_float4(r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f, r == c + 2 ? 1.f : 0.f, r == c + 3 ? 1.f : 0.f);
     }
-    const float4* g4 = reinterpret_cast<const float4*>(gp);
-    for (int q = 0; q < j.slices; q += 2) {  // slices in order, two per batch of loads
-      const int q1 = min(q + 1, j.slices - 1);
-      float4 x0[E4], x1[E4];
+    const float4* g4 = reinterpret_cast<const float4*>(gp);  // slice 0 holds the sum of the slices
 #pragma unroll
-      for (int t = 0; t < E4; ++t) {
-        x0[t] = g4[(long long)q * D * D / 4 + tid + kJThreads * t];
-        x1[t] = g4[(long long)q1 * D * D / 4 + tid + kJThreads * t];
-      }
-      const bool two = q + 1 < j.slices;
-#pragma unroll
-      for (int t = 0; t < E4; ++t) {
-        v[t].x += x0[t].x;
-        v[t].y += x0[t].y;
-        v[t].z += x0[t].z;
-        v[t].w += x0[t].w;
-        if (two) {
-          v[t].x += x1[t].x;
-          v[t].y += x1[t].y;
-          v[t].z += x1[t].z;
-          v[t].w += x1[t].w;
-        }
-      }
+    for (int t = 0; t < E4; ++t) {
+      const float4 x = g4[tid + kJThreads * t];
+      v[t].x += x.x;
+      v[t].y += x.y;
+      v[t].z += x.z;
+      v[t].w += x.w;
     }
 #pragma unroll
     for (int t = 0; t < E4; ++t) {  // upper elements (never written by the Gram kernel) are dropped
@@ -667,6 +677,11 @@ hipError_t launch_all(const JacapArgs& j, const __bf16* K, const __bf16* U, hipS
   if (e == hipSuccess)
     e = timed("jacap_gram", [&] {
       hipLaunchKernelGGL((jacap_gram_kernel<D>), dim3(j.slices, j.heads), dim3(kJThreads), 0, st, j, U);
+      return hipGetLastError();
+    });
+  if (e == hipSuccess && j.slices > 1)
+    e = timed("jacap_reduce", [&] {
+      hipLaunchKernelGGL((jacap_reduce_kernel<D>), dim3(kRedParts, j.heads), dim3(kJThreads), 0, st, j);
       return hipGetLastError();
     });
   if (e == hipSuccess)
