@@ -12,8 +12,8 @@
 // the refresh selection.
 //
 // Kernels:
-//   jacap_logits   per (head, chunk): z and kappa of every token (a group of
-//                  D/8 lanes per token, 16-byte loads), the chunk's softmax
+//   jacap_logits   per (head, chunk): z and kappa of every token (a quad of
+//                  lanes per token, 16-byte loads), the chunk's softmax
 //                  partial (max, sum of exp).
 //   jacap_weights  per (head, chunk): the head's partials merged in a fixed
 //                  order, then w of every token.
@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <type_traits>
 
 #include "kvsel_internal.h"
 
@@ -69,48 +70,71 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo
   m = fmaxf(m, mo);
 }
 
+// Sum over the four lanes of a quad (DPP quad permutations, no LDS).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  return v;
+}
+
 // z_i and kappa_i of the chunk's tokens; (max, sum exp(z - max)) of the chunk.
+// A quad of lanes takes a token: lane p of the quad loads 16-byte pieces
+// p, p + 4, ... of the row (64 contiguous bytes per row and load), so a
+// pass covers 64 tokens and the reduction is two DPP steps.  kLogitPasses
+// passes are loaded before any is reduced.
+constexpr int kLogitPasses = 4;
 template <int D>
 __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs j, const __bf16* __restrict__ K) {
-  constexpr int LPT = D / 8;               // lanes per token
-  constexpr int TPP = kJThreads / LPT;     // tokens per pass
+  constexpr int CPL = D / 8 / 4;  // 16-byte pieces per lane
+  constexpr int TPP = kJThreads / 4;
   const int head = blockIdx.y, c = blockIdx.x;
-  const int tid = threadIdx.x, part = tid % LPT, slot = tid / LPT;
+  const int tid = threadIdx.x, part = tid & 3, slot = tid >> 2;
   __shared__ float sm[kJThreads / 64], sz[kJThreads / 64];
-  float mu[8], lam[8];
+  float mu[CPL][8], lam[CPL][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mu[e] = j.mu[(long long)head * D + part * 8 + e];
-    lam[e] = j.lambda[(long long)head * D + part * 8 + e];
-  }
+  for (int q = 0; q < CPL; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mu[q][e] = j.mu[(long long)head * D + (part + 4 * q) * 8 + e];
+      lam[q][e] = j.lambda[(long long)head * D + (part + 4 * q) * 8 + e];
+    }
   if (head == 0 && c == 0 && tid == 0 && j.err != nullptr) *j.err = 0u;  // the later kernels raise flags
   const float scale = 1.f / (j.tau * sqrtf((float)D));
   float m = kNegBig, s = 0.f;
   const int t0 = c * kJChunk, t1 = min(t0 + kJChunk, j.N);
-  for (int base = t0; base < t1; base += TPP) {  // every lane takes part in the shuffles
-    const int t = base + slot;
-    float zz = 0.f, kk = 0.f;
-    if (t < t1) {
-      float k[8];
-      load8(K + ((long long)head * j.N + t) * D + part * 8, k);
+  const __bf16* kh = K + (long long)head * j.N * D;
+  for (int base = t0; base < t1; base += kLogitPasses * TPP) {  // every lane takes part in the DPP steps
+    uint4 raw[kLogitPasses][CPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        zz = fmaf(k[e], mu[e], zz);
-        kk = fmaf(lam[e] * k[e], k[e], kk);
+    for (int h = 0; h < kLogitPasses; ++h) {
+      const int t = min(base + h * TPP + slot, t1 - 1);  // rows past the chunk repeat its last (not stored)
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) raw[h][q] = *reinterpret_cast<const uint4*>(kh + (long long)t * D + (part + 4 * q) * 8);
+    }
+#pragma unroll
+    for (int h = 0; h < kLogitPasses; ++h) {
+      float zz = 0.f, kk = 0.f;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const unsigned w[4] = {raw[h][q].x, raw[h][q].y, raw[h][q].z, raw[h][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(w[e] << 16), k1 = __uint_as_float(w[e] & 0xFFFF0000u);
+          zz = fmaf(k0, mu[q][2 * e], zz);
+          zz = fmaf(k1, mu[q][2 * e + 1], zz);
+          kk = fmaf(lam[q][2 * e] * k0, k0, kk);
+          kk = fmaf(lam[q][2 * e + 1] * k1, k1, kk);
+        }
       }
-    }
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) {
-      zz += __shfl_xor(zz, o, LPT);
-      kk += __shfl_xor(kk, o, LPT);
-    }
-    if (t < t1) {
-      const float z = zz * scale;
-      if (part == 0) {
+      zz = quad_sum(zz);
+      kk = quad_sum(kk);
+      const int t = base + h * TPP + slot;
+      if (t < t1 && part == 0) {
+        const float z = zz * scale;
         j.z[(long long)head * j.N + t] = z;
         j.kappa[(long long)head * j.N + t] = kk;
+        lse_merge(m, s, z, 1.f);
       }
-      if (part == 0) lse_merge(m, s, z, 1.f);
     }
   }
   // The chunk's partial: lanes of the wave, then the waves in order.
@@ -299,24 +323,40 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
   if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 4));
   __syncthreads();
   // Step st multiplies buffer st & 1, loads step st + kPre into register set
-  // (st + kPre) % (kPre + 1) and stages step st + 1 from set (st + 1) % (kPre + 1).
-  // Loads and staging past the last step are harmless (rows clamped to the
-  // slice, buffers never multiplied), so a step has no branch and the
-  // scheduler can interleave the staging arithmetic with the MFMAs.
-  for (int s0 = 0; s0 < steps; s0 += 2 * (kPre + 1)) {
-#pragma unroll
-    for (int u = 0; u < 2 * (kPre + 1); ++u) {
-      const int st = s0 + u;
-      if (st < steps) {
-        constexpr int R = kPre + 1;
-        gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
-        gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
-        gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
-                      t1 - (t0 + (st + 1) * S::TS + tg * 4));
-        __syncthreads();
-      }
-    }
+  // (st + kPre) % R and stages step st + 1 from set (st + 1) % R (R = kPre + 1,
+  // even, so both patterns repeat every R steps).  Loads and staging past the
+  // last step are harmless (rows clamped to the slice, buffers never
+  // multiplied).  Whole blocks of R steps run without a branch, so that the
+  // compiler's wait counts see the full depth of the load ring; the
+  // remaining steps follow with a test each.
+  constexpr int R = kPre + 1;
+  static_assert(R % 2 == 0, "the ring period must be even");
+  auto step = [&](int st, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
+    gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
+    gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
+                  t1 - (t0 + (st + 1) * S::TS + tg * 4));
+    __syncthreads();
+  };
+  const int full = steps / R * R;
+  for (int s0 = 0; s0 < full; s0 += R) {
+    step(s0 + 0, std::integral_constant<int, 0>{});
+    step(s0 + 1, std::integral_constant<int, 1>{});
+    step(s0 + 2, std::integral_constant<int, 2>{});
+    step(s0 + 3, std::integral_constant<int, 3>{});
+    step(s0 + 4, std::integral_constant<int, 4>{});
+    step(s0 + 5, std::integral_constant<int, 5>{});
+    step(s0 + 6, std::integral_constant<int, 6>{});
+    step(s0 + 7, std::integral_constant<int, 7>{});
   }
+  if (full + 0 < steps) step(full + 0, std::integral_constant<int, 0>{});
+  if (full + 1 < steps) step(full + 1, std::integral_constant<int, 1>{});
+  if (full + 2 < steps) step(full + 2, std::integral_constant<int, 2>{});
+  if (full + 3 < steps) step(full + 3, std::integral_constant<int, 3>{});
+  if (full + 4 < steps) step(full + 4, std::integral_constant<int, 4>{});
+  if (full + 5 < steps) step(full + 5, std::integral_constant<int, 5>{});
+  if (full + 6 < steps) step(full + 6, std::integral_constant<int, 6>{});
   float* out = j.gpart + ((long long)head * j.slices + slice) * D * D;
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
