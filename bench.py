@@ -91,6 +91,12 @@ KERNEL_SOURCES = {
     "emit": ("kvsel_select.hip", "kvsel_internal.h"),
     "gather": ("kvsel_select.hip", "kvsel_internal.h"),
     "select": ("kvsel_select.hip", "kvsel_internal.h"),
+    "jacap_logits": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_weights": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_gram": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_reduce": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_factor": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_leverage": ("kvsel_jacap.hip", "kvsel_internal.h"),
 }
 
 
@@ -258,8 +264,6 @@ def jacap_bench(args, B, torch, np):
 
     for _ in range(args.warmup):
         step()
-    if B.kvsel_status(ws, stream) != B.KVSEL_OK:
-        raise SystemExit("Jacap event reported a device-side error: " + B.kvsel_last_error())
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -268,12 +272,20 @@ def jacap_bench(args, B, torch, np):
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
+    if B.kvsel_status(ws, stream) != B.KVSEL_OK:  # the last timed call's device-side outcome
+        raise SystemExit("Jacap event reported a device-side error: " + B.kvsel_last_error())
     B.kvsel_profile_enable(True)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     per_kernel = B.kvsel_profile_read()
     B.kvsel_profile_enable(False)
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 1 GiB device-to-device copy done")
     S = max(1, min(32, (256 + H - 1) // H, (N + 511) // 512))
     kern = {}
     for k, (c, t) in per_kernel.items():
@@ -294,7 +306,8 @@ def jacap_bench(args, B, torch, np):
         "config": {"workload": f"jacap_h32_n{N}_d128", "layers": layers, "N": N, "keep": keep,
                    "protect_head": head, "protect_tail": tail, "tau": tau, "u": "v"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(dom) if N == 32768 else None},
         "path": {"alg_bytes_per_call": moved, "alg_GBps": round(moved * layers / (ms / 1e3) / 1e9, 1),
                  "us_per_call": round(ms * 1e3 / layers, 2)},
         "kernels": kern,
