@@ -91,12 +91,12 @@ KERNEL_SOURCES = {
     "emit": ("kvsel_select.hip", "kvsel_internal.h"),
     "gather": ("kvsel_select.hip", "kvsel_internal.h"),
     "select": ("kvsel_select.hip", "kvsel_internal.h"),
-    "jacap_logits": ("kvsel_jacap.hip", "kvsel_internal.h"),
-    "jacap_weights": ("kvsel_jacap.hip", "kvsel_internal.h"),
-    "jacap_gram": ("kvsel_jacap.hip", "kvsel_internal.h"),
-    "jacap_reduce": ("kvsel_jacap.hip", "kvsel_internal.h"),
-    "jacap_factor": ("kvsel_jacap.hip", "kvsel_internal.h"),
-    "jacap_leverage": ("kvsel_jacap.hip", "kvsel_internal.h"),
+    "jacap_logits": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
+    "jacap_weights": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
+    "jacap_gram": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
+    "jacap_reduce": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
+    "jacap_factor": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
+    "jacap_leverage": ("kvsel_jacap.hip", "kvsel_jacap.h", "kvsel_internal.h"),
 }
 
 

@@ -22,6 +22,7 @@
 
 #include "kvsel.h"
 #include "kvsel_internal.h"
+#include "kvsel_jacap.h"
 
 using namespace kvsel;
 

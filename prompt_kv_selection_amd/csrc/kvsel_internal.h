@@ -10,7 +10,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <functional>
 
 namespace kvsel {
 
@@ -248,25 +247,6 @@ hipError_t launch_refresh_finish(int rows, int n, int keep, int head, int tail, 
                                  const int32_t* tokens, int32_t* tokens_out, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
 
-// Jacap leverage scores (kvsel_jacap.hip): buffers per head of N tokens.
-struct JacapArgs {
-  int heads, N, nch, slices;
-  float tau;
-  const float* mu;      // [heads][D]
-  const float* lambda;  // [heads][D]
-  float* z;             // [heads][N] centre logits
-  float* kappa;         // [heads][N]
-  float* part;          // [heads][nch][2] softmax partials
-  float* w;             // [heads][N]
-  float* gpart;         // [heads][slices][D][D] parts of sum w u u^T
-  __bf16* minv;         // [heads][2][D][D] L^{-1} as bf16 hi, lo
-  float* r;             // [heads][N] leverage scores
-  unsigned* err;
-};
-int jacap_chunks(int N);
-int jacap_slices(int N, int heads);
-hipError_t launch_jacap_scores(const JacapArgs& j, int D, const void* K, const void* U, hipStream_t st,
-                               const std::function<hipError_t(const char*, const std::function<hipError_t()>&)>& timed);
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);
 

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "kvsel_internal.h"
+#include "kvsel_jacap.h"
 
 namespace kvsel {
 
