@@ -253,14 +253,27 @@ def jacap_bench(args, B, torch, np):
     idx = [torch.empty((H, keep), dtype=torch.int32, device=dev) for _ in range(layers)]
     Ko = [torch.empty((H, keep, D), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
     Vo = [torch.empty_like(Ko[0]) for _ in range(layers)]
-    ws = torch.empty(B.kvsel_jacap_workspace_bytes(H, N, D), dtype=torch.uint8, device=dev)
+    nst = max(1, args.streams)
+    ws = [torch.empty(B.kvsel_jacap_workspace_bytes(H, N, D), dtype=torch.uint8, device=dev) for _ in range(nst)]
     stream = torch.cuda.current_stream()
+    side = [stream] + [torch.cuda.Stream(device=dev) for _ in range(nst - 1)]  # default priority
+    fork = [torch.cuda.Event() for _ in range(nst)]
     torch.cuda.synchronize()
 
     def step():
+        # Layer l goes to stream l % nst (its own workspace); the side streams
+        # start after the step's start on the timing stream and end before its end.
+        if nst > 1:
+            fork[0].record(stream)
+            for k in range(1, nst):
+                side[k].wait_event(fork[0])
         for l in range(layers):
+            k = l % nst
             B.kvsel_jacap_select(K[l], V[l], V[l], mu[l], lam[l], tau, H, N, D, "bf16", keep, head, tail, None,
-                                 idx[l], Ko[l], Vo[l], None, None, ws, stream=stream)
+                                 idx[l], Ko[l], Vo[l], None, None, ws[k], stream=side[k])
+        for k in range(1, nst):
+            fork[k].record(side[k])
+            stream.wait_event(fork[k])
 
     for _ in range(args.warmup):
         step()
@@ -272,8 +285,9 @@ def jacap_bench(args, B, torch, np):
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    if B.kvsel_status(ws, stream) != B.KVSEL_OK:  # the last timed call's device-side outcome
-        raise SystemExit("Jacap event reported a device-side error: " + B.kvsel_last_error())
+    for k in range(nst):  # the last timed calls' device-side outcome
+        if B.kvsel_status(ws[k], side[k]) != B.KVSEL_OK:
+            raise SystemExit("Jacap event reported a device-side error: " + B.kvsel_last_error())
     B.kvsel_profile_enable(True)
     for _ in range(args.steps):
         step()
@@ -304,7 +318,7 @@ def jacap_bench(args, B, torch, np):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"jacap_h32_n{N}_d128", "layers": layers, "N": N, "keep": keep,
-                   "protect_head": head, "protect_tail": tail, "tau": tau, "u": "v"},
+                   "protect_head": head, "protect_tail": tail, "tau": tau, "u": "v", "streams": nst},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(dom) if N == 32768 else None},
@@ -335,6 +349,8 @@ def main():
                     help="time the refresh selection instead: J kept of J + J/4 cached tokens per head")
     ap.add_argument("--jacap", type=int, default=0,
                     help="time the Jacap eviction event instead: 32 heads of N cached tokens per layer call")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="with --jacap: independent layer calls spread over this many streams (own workspaces)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()

@@ -73,6 +73,9 @@ CASES = [
     (1, 1, 64, 1, 0, 0, 1.0, 1.0, False),             # one token: alpha = 1, w = r = 0
     (2, 9000, 128, 3000, 0, 0, 0.5, 2.0, True),       # no protected tokens
     (2, 4096, 64, 64, 32, 32, 2.0, 1.0, False),       # no flexible budget
+    (2, 300, 64, 300, 0, 0, 1.0, 1.0, True),          # keep everything
+    (3, 2047, 128, 1, 0, 0, 0.1, 3.0, True),          # one kept token, very sharp centre softmax
+    (1, 70000, 128, 7000, 4, 64, 10.0, 1.0, False),   # one head: 32 Gram slices, segment-parallel selection
 ]
 
 
