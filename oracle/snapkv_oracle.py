@@ -350,11 +350,19 @@ def jacap_scores(keys, outs, mu_q, lambda_q, tau: float) -> Dict:
     z /= tau * math.sqrt(dk)
     m = z.max()
     e = np.exp(z - m)
-    alpha = e / math.fsum(e.tolist())
+    total = math.fsum(e.tolist())
+    alpha = e / total
+    # 1 - alpha_i is the probability of the other tokens: sum_{j != i} e_j / total.
+    # Formed as (total - e_i) / total except for the largest term, whose
+    # complement is summed directly (total - e_i would cancel when it dominates).
+    rest = total - e
+    top = int(np.argmax(e))
+    rest[top] = math.fsum(np.delete(e, top).tolist())
+    one_minus = rest / total
     kappa = np.zeros(N)
     for d in range(dk):
         kappa += lam[d] * keys[:, d] ** 2
-    w = (alpha * (1.0 - alpha)) ** 2 * kappa / dk
+    w = (alpha * one_minus) ** 2 * kappa / dk
     du = outs.shape[1]
     A = np.eye(du)
     for j in range(N):

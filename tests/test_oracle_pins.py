@@ -370,6 +370,22 @@ def test_jacap_logit_and_curvature_closed_forms():
     np.testing.assert_allclose(sc["w"], [(0.25 ** 2) * 23 / 4, 0.0], rtol=1e-14)   # equal logits: alpha = 1/2
 
 
+def test_jacap_saturated_token_keeps_its_sensitivity():
+    """A centre probability within 1e-20 of one still has alpha (1 - alpha)
+    equal to the other tokens' mass (here e^-50 of it), not zero: two
+    tokens with logits 0 and -50 give 1 - alpha_0 = e^-50 / (1 + e^-50)."""
+    keys = np.zeros((2, 4))
+    keys[1, 0] = -100.0                         # z = -100 / (1 * 2) = -50 with mu = e_0, tau = 1
+    sc = O.jacap_scores(keys, np.eye(2), np.eye(4)[0], np.ones(4), 1.0)
+    q = math.exp(-50)
+    np.testing.assert_allclose(sc["alpha"], [1 / (1 + q), q / (1 + q)], rtol=1e-15)
+    rho0 = (1 / (1 + q)) * (q / (1 + q))
+    assert rho0 > 0
+    assert sc["w"][0] == 0.0                                                        # kappa_0 = 0 (zero key)
+    sc = O.jacap_scores(keys + np.array([0, 1.0, 0, 0]), np.eye(2), np.eye(4)[0], np.ones(4), 1.0)
+    np.testing.assert_allclose(sc["w"][0], rho0 ** 2 * 1.0 / 4, rtol=1e-12)        # kappa_0 = 1
+
+
 def jacap_toy():
     """The page's 2-D miniature: u1 = (1, 0), u2 = (0.95, 0.05), u3 = (0, 1)
     with w = (1, 1, 0.7), realised through keys whose weights come out
