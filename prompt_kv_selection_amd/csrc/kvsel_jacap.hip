@@ -64,11 +64,17 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&v)[8]) {
   }
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
-  const float d = mo - m;
-  const float e = __expf(-fabsf(d));
-  z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
-  m = fmaxf(m, mo);
+// Softmax partials as (m, s1): the maximum and Z - 1 with Z = sum exp(z - m),
+// i.e. the mass of every term but the maximum's.  Keeping Z - 1 rather than Z
+// lets 1 - alpha of the largest term be formed without cancellation.  Empty:
+// (kNegBig, -1); one logit z: (z, 0).
+__device__ __forceinline__ void lse1_merge(float& m, float& s1, float mo, float s1o) {
+  if (mo > m) {
+    s1 = fmaf(1.f + s1, __expf(m - mo), s1o);
+    m = mo;
+  } else {
+    s1 = fmaf(1.f + s1o, __expf(mo - m), s1);
+  }
 }
 
 // Sum over the four lanes of a quad (DPP quad permutations, no LDS).
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
     }
   if (head == 0 && c == 0 && tid == 0 && j.err != nullptr) *j.err = 0u;  // the later kernels raise flags
   const float scale = 1.f / (j.tau * sqrtf((float)D));
-  float m = kNegBig, s = 0.f;
+  float m = kNegBig, s = -1.f;
   const int t0 = c * kJChunk, t1 = min(t0 + kJChunk, j.N);
   const __bf16* kh = K + (long long)head * j.N * D;
   for (int base = t0; base < t1; base += kLogitPasses * TPP) {  // every lane takes part in the DPP steps
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
         const float z = zz * scale;
         j.z[(long long)head * j.N + t] = z;
         j.kappa[(long long)head * j.N + t] = kk;
-        lse_merge(m, s, z, 1.f);
+        lse1_merge(m, s, z, 0.f);
       }
     }
   }
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float mo = __shfl_xor(m, o), so = __shfl_xor(s, o);
-    lse_merge(m, s, mo, so);
+    lse1_merge(m, s, mo, so);
   }
   if ((tid & 63) == 0) {
     sm[tid >> 6] = m;
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
   __syncthreads();
   if (tid == 0) {
     float mm = sm[0], ss = sz[0];
-    for (int w = 1; w < kJThreads / 64; ++w) lse_merge(mm, ss, sm[w], sz[w]);
+    for (int w = 1; w < kJThreads / 64; ++w) lse1_merge(mm, ss, sm[w], sz[w]);
     j.part[((long long)head * j.nch + c) * 2] = mm;
     j.part[((long long)head * j.nch + c) * 2 + 1] = ss;
   }
@@ -161,21 +167,25 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
 __global__ __launch_bounds__(kJThreads) void jacap_weights_kernel(const JacapArgs j, int D) {
   const int head = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   __shared__ float s_m, s_z;
-  if (tid == 0) {  // the head's partials in chunk order: every workgroup gets the same (M, Z)
-    float m = kNegBig, s = 0.f;
+  if (tid == 0) {  // the head's partials in chunk order: every workgroup gets the same (M, Z - 1)
+    float m = kNegBig, s = -1.f;
     for (int q = 0; q < j.nch; ++q)
-      lse_merge(m, s, j.part[((long long)head * j.nch + q) * 2], j.part[((long long)head * j.nch + q) * 2 + 1]);
+      lse1_merge(m, s, j.part[((long long)head * j.nch + q) * 2], j.part[((long long)head * j.nch + q) * 2 + 1]);
     s_m = m;
     s_z = s;
-    if (!(isfinite(m) && isfinite(s) && s > 0.f)) raise_error(j.err, kErrNonFinite);
+    if (!(isfinite(m) && isfinite(s) && s >= 0.f)) raise_error(j.err, kErrNonFinite);
   }
   __syncthreads();
-  const float M = s_m, iz = 1.f / s_z, invd = 1.f / (float)D;
+  const float M = s_m, s1 = s_z, iz = 1.f / (1.f + s1), invd = 1.f / (float)D;
   const int t0 = c * kJChunk, t1 = min(t0 + kJChunk, j.N);
   for (int t = t0 + tid; t < t1; t += kJThreads) {
     const long long i = (long long)head * j.N + t;
-    const float a = __expf(j.z[i] - M) * iz;
-    const float rho = a * (1.f - a);
+    const float d = j.z[i] - M;
+    // alpha = e / Z and 1 - alpha = (Z - e) / Z = ((1 - e) + (Z - 1)) / Z: two
+    // non-negative terms, so a saturated alpha keeps its complement.
+    const float a = __expf(d) * iz;
+    const float om = (s1 - expm1f(d)) * iz;
+    const float rho = a * om;
     j.w[i] = rho * rho * j.kappa[i] * invd;
   }
 }
