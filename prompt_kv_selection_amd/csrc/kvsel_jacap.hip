@@ -305,49 +305,59 @@ __device__ __forceinline__ void gram_mfma(const __bf16* cur, int n, int g, f32x1
 // Part of sum_i w_i u_i u_i^T over tokens [slice * per, (slice + 1) * per) of
 // the head, into gpart[head][slice][D][D] (lower 32 x 32 tiles only).  Each
 // MFMA pair multiplies u^T (exact bf16) by the high and the low bf16 part of
-// (w u): products correct to about 2^-17 relative, fp32 accumulation.  The
-// operands of a step are staged by all 256 threads (16-byte loads of token
-// rows, transposed in registers) into one of two LDS buffers while the waves
-// multiply the other, so a step needs one barrier; the loads run kPre steps
-// ahead of the multiplications (a ring of register sets).
-constexpr int kPre = 7;
-template <int D, int WV>
+// (w u): products correct to about 2^-17 relative, fp32 accumulation.
+// Waves 0-3 multiply; waves 4-7 load and stage (16-byte loads of token rows,
+// transposed in registers, into one of two LDS buffers) the next step while
+// the others multiply the current one, so the staging arithmetic runs beside
+// the MFMAs on the same SIMDs and a step needs one barrier.  The loads run
+// kPre steps ahead of the staging (a ring of register sets).
+constexpr int kPre = 5;
+constexpr int kGramThreads = 512;
+template <int D, int WV>  // WV < 4: the multiplying wave of that tile set; WV == 4: a staging wave
 __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __restrict__ U, __bf16* lds) {
   using S = GramShape<D>;
+  constexpr bool kStage = WV == 4;
   const int head = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, n = lane & 31, g = lane >> 5;
-  // A wave stages whole feature rows: QW lanes take consecutive token quads
-  // of one feature group, so that its 8-byte LDS writes cover consecutive
-  // banks (two rows per write at most share a bank).
+  // A staging wave stages whole feature rows: QW lanes take consecutive token
+  // quads of one feature group, so that its 8-byte LDS writes cover
+  // consecutive banks (two rows per write at most share a bank).
   constexpr int QW = S::TS / 4;
-  const int fg = (tid >> 6) * (64 / QW) + lane / QW, tg = lane % QW;
+  const int ts = tid - 256;
+  const int fg = (ts >> 6) * (64 / QW) + lane / QW, tg = lane % QW;
   const int per = (j.N + j.slices - 1) / j.slices;
   const int t0 = min(slice * per, j.N), t1 = min(t0 + per, j.N);
   const int steps = (t1 - t0 + S::TS - 1) / S::TS;
-  f32x16 acc[3];
-#pragma unroll
-  for (int q = 0; q < 3; ++q) acc[q] = f32x16{};
-  uint4 d[kPre + 1][4];
-  float w[kPre + 1][4];
-#pragma unroll
-  for (int u = 0; u < kPre; ++u) gram_load<D>(j, U, head, t0 + u * S::TS + tg * 4, t1, fg, d[u], w[u]);
-  if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 4));
-  __syncthreads();
-  // Step st multiplies buffer st & 1, loads step st + kPre into register set
-  // (st + kPre) % R and stages step st + 1 from set (st + 1) % R (R = kPre + 1,
-  // even, so both patterns repeat every R steps).  Loads and staging past the
-  // last step are harmless (rows clamped to the slice, buffers never
-  // multiplied).  Whole blocks of R steps run without a branch, so that the
-  // compiler's wait counts see the full depth of the load ring; the
-  // remaining steps follow with a test each.
   constexpr int R = kPre + 1;
   static_assert(R % 2 == 0, "the ring period must be even");
+  f32x16 acc[3];
+  uint4 d[R][4];
+  float w[R][4];
+  if constexpr (kStage) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) gram_load<D>(j, U, head, t0 + u * S::TS + tg * 4, t1, fg, d[u], w[u]);
+    if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 4));
+  } else {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x16{};
+  }
+  __syncthreads();
+  // Step st multiplies buffer st & 1; the staging waves load step st + kPre
+  // into register set (st + kPre) % R and stage step st + 1 from set
+  // (st + 1) % R into the other buffer.  Loads and staging past the last step
+  // are harmless (rows clamped to the slice, buffers never multiplied).
+  // Whole blocks of R steps run without a branch, so that the compiler's wait
+  // counts see the full depth of the load ring; the remaining steps follow
+  // with a test each.
   auto step = [&](int st, auto uc) {
     constexpr int u = decltype(uc)::value;
-    gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
-    gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
-    gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
-                  t1 - (t0 + (st + 1) * S::TS + tg * 4));
+    if constexpr (kStage) {
+      gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
+      gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
+                    t1 - (t0 + (st + 1) * S::TS + tg * 4));
+    } else {
+      gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
+    }
     __syncthreads();
   };
   const int full = steps / R * R;
@@ -358,37 +368,38 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
     step(s0 + 3, std::integral_constant<int, 3>{});
     step(s0 + 4, std::integral_constant<int, 4>{});
     step(s0 + 5, std::integral_constant<int, 5>{});
-    step(s0 + 6, std::integral_constant<int, 6>{});
-    step(s0 + 7, std::integral_constant<int, 7>{});
   }
+  static_assert(R == 6, "the unrolled blocks above and the tail below assume a ring of six");
   if (full + 0 < steps) step(full + 0, std::integral_constant<int, 0>{});
   if (full + 1 < steps) step(full + 1, std::integral_constant<int, 1>{});
   if (full + 2 < steps) step(full + 2, std::integral_constant<int, 2>{});
   if (full + 3 < steps) step(full + 3, std::integral_constant<int, 3>{});
   if (full + 4 < steps) step(full + 4, std::integral_constant<int, 4>{});
-  if (full + 5 < steps) step(full + 5, std::integral_constant<int, 5>{});
-  if (full + 6 < steps) step(full + 6, std::integral_constant<int, 6>{});
-  float* out = j.gpart + ((long long)head * j.slices + slice) * D * D;
+  if constexpr (!kStage) {
+    float* out = j.gpart + ((long long)head * j.slices + slice) * D * D;
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    constexpr int NT = D / 32;
-    const int tile = gram_tile<D>(WV, q);
-    if (tile >= 0) {
-      const int p = tile / NT, r = tile % NT;
+    for (int q = 0; q < 3; ++q) {
+      constexpr int NT = D / 32;
+      const int tile = gram_tile<D>(WV, q);
+      if (tile >= 0) {
+        const int p = tile / NT, r = tile % NT;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) out[(p * 32 + acc_row(e, g)) * D + r * 32 + n] = acc[q][e];
+        for (int e = 0; e < 16; ++e) out[(p * 32 + acc_row(e, g)) * D + r * 32 + n] = acc[q][e];
+      }
     }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kJThreads) void jacap_gram_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
+__global__ __launch_bounds__(kGramThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void jacap_gram_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 3 * GramShape<D>::ARR];
   switch (threadIdx.x >> 6) {  // every wave runs the same steps and barriers
     case 0: gram_body<D, 0>(j, U, lds); break;
     case 1: gram_body<D, 1>(j, U, lds); break;
     case 2: gram_body<D, 2>(j, U, lds); break;
-    default: gram_body<D, 3>(j, U, lds); break;
+    case 3: gram_body<D, 3>(j, U, lds); break;
+    default: gram_body<D, 4>(j, U, lds); break;
   }
 }
 
@@ -727,7 +738,7 @@ hipError_t launch_all(const JacapArgs& j, const __bf16* K, const __bf16* U, hipS
     });
   if (e == hipSuccess)
     e = timed("jacap_gram", [&] {
-      hipLaunchKernelGGL((jacap_gram_kernel<D>), dim3(j.slices, j.heads), dim3(kJThreads), 0, st, j, U);
+      hipLaunchKernelGGL((jacap_gram_kernel<D>), dim3(j.slices, j.heads), dim3(kGramThreads), 0, st, j, U);
       return hipGetLastError();
     });
   if (e == hipSuccess && j.slices > 1)
