@@ -14,7 +14,7 @@
 // Kernels:
 //   jacap_logits   per (head, chunk): z and kappa of every token (a quad of
 //                  lanes per token, 16-byte loads), the chunk's softmax
-//                  partial (max, sum of exp).
+//                  partial (max, and Z - 1: the mass beyond the max).
 //   jacap_weights  per (head, chunk): the head's partials merged in a fixed
 //                  order, then w of every token.
 //   jacap_gram     per (head, slice): the slice's part of sum w u u^T on MFMA
@@ -28,8 +28,8 @@
 //   jacap_leverage per (head, chunk): Y = M U^T on MFMA (hi and lo of M
 //                  against the exact bf16 u, the k-steps of the lower
 //                  triangle only), r = w * column sums of Y^2.
-// The two N d^2 contractions are the MFMA part; everything else streams K
-// and U once.
+// The two N d^2 contractions are the MFMA part.  K is read once and U twice
+// (the Gram matrix must be complete before any leverage score).
 
 #include <math.h>
 
@@ -52,17 +52,6 @@ constexpr int kJChunk = 1024;  // tokens per logits / weights / leverage workgro
 constexpr float kNegBig = -1.0e30f;
 
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
-
-// Eight consecutive bf16 values (16 bytes) as floats.
-__device__ __forceinline__ void load8(const __bf16* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const unsigned w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    v[2 * q] = __uint_as_float(w[q] << 16);
-    v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-  }
-}
 
 // Softmax partials as (m, s1): the maximum and Z - 1 with Z = sum exp(z - m),
 // i.e. the mass of every term but the maximum's.  Keeping Z - 1 rather than Z

@@ -196,3 +196,33 @@ def test_jacap_full_size_sampled_heads(B):
         np.testing.assert_array_equal(got[h], O.refresh_select(r_gpu[h], keep, head, tail))
     gi = out["idx"].long()
     assert torch.equal(bits(out["Ko"]), bits(torch.gather(out["Kd"], 1, gi[:, :, None].expand(H, keep, D))))
+
+
+def test_jacap_concurrent_calls_on_two_streams(B):
+    """Two independent events on two streams, each with its own workspace,
+    give the same bits as the same events run one after the other."""
+    H, N, D = 4, 9000, 128
+    evs = [WL.jacap_arrays(20 + k, H, N, D) for k in range(2)]
+    seq = [run(B, *ev, 1.0, 900, 4, 32) for ev in evs]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for ev, st in zip(evs, (s1, s2)):
+        K, V, U, mu, lam = ev
+        o = dict(idx=torch.full((H, 900), -1, dtype=torch.int32, device="cuda"),
+                 r=torch.empty((H, N), dtype=torch.float32, device="cuda"),
+                 Ko=torch.empty((H, 900, D), dtype=torch.bfloat16, device="cuda"),
+                 ws=torch.empty(B.kvsel_jacap_workspace_bytes(H, N, D), dtype=torch.uint8, device="cuda"),
+                 inp=(dev_bf16(K), dev_bf16(V), dev_bf16(U), torch.from_numpy(mu).cuda(), torch.from_numpy(lam).cuda()))
+        o["Vo"] = torch.empty_like(o["Ko"])
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o, st in zip(outs, (s1, s2)):
+        Kd, Vd, Ud, mud, lamd = o["inp"]
+        B.kvsel_jacap_select(Kd, Vd, Ud, mud, lamd, 1.0, H, N, D, "bf16", 900, 4, 32, None, o["idx"], o["Ko"],
+                             o["Vo"], None, o["r"], o["ws"], stream=st)
+    torch.cuda.synchronize()
+    for o, a, st in zip(outs, seq, (s1, s2)):
+        assert B.kvsel_status(o["ws"], st) == B.KVSEL_OK
+        assert torch.equal(o["idx"], a["idx"])
+        assert torch.equal(bits(o["r"]), bits(a["r"]))
+        assert torch.equal(bits(o["Ko"]), bits(a["Ko"]))
