@@ -468,65 +468,106 @@ void jacap_factor_kernel(const JacapArgs j) {
     }
   }
   __syncthreads();
-  bool bad = false;
+  bool bad = false;  // a pivot that is not finite and positive (lanes 0-7 of wave 0)
+  // The diagonal block of panel k0 / 8: lane i of wave 0 holds row i;
+  // Cholesky and inverse (written to a, m and li).
+  auto diag = [&](int k0) {
+      if (tid < 8) {  // the diagonal block: lane i of wave 0 holds row i; Cholesky and inverse
+        float x[8], y[8];
+        {
+          const float4 u0 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0);
+          const float4 u1 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0 + 4);
+          x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+          x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        }
+        float rsi = 0.f;  // 1 / L[i][i] of this lane's row
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), c));
+          bad |= !(d > 0.f && isfinite(d));
+          const float dd = fmaxf(d, 1e-30f);
+          const float rs = __builtin_amdgcn_rsqf(dd);
+          if (tid == c) {
+            x[c] = dd * rs;
+            rsi = rs;
+          } else if (tid > c) {
+            x[c] *= rs;
+          }
+          // Column c of L below the diagonal, broadcast: row q's entry from lane q.
+#pragma unroll
+          for (int q = c + 1; q < 8; ++q) {
+            const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), q));
+            if (tid >= q) x[q] = fmaf(-x[c], lq, x[q]);
+          }
+        }
+        // Row i of inv(L): y[q] = -rs_i sum_{k=q}^{i-1} L[i][k] y_k[q], rows in order
+        // (row k's entries broadcast from lane k once it is final).
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (tid == k) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) y[q] = q < k ? -y[q] * rsi : (q == k ? rsi : 0.f);
+          }
+#pragma unroll
+          for (int q = 0; q <= k; ++q) {
+            const float yk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(y[q]), k));
+            if (tid > k) y[q] = fmaf(x[k], yk, y[q]);  // accumulates sum_k L[i][k] y_k[q]
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = q <= tid ? x[q] : 0.f;
+        float* ar = a + (k0 + tid) * S + k0;
+        float* mr = m + (k0 + tid) * S + k0;
+        *reinterpret_cast<float4*>(ar) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(ar + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        *reinterpret_cast<float4*>(mr) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(mr + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        *reinterpret_cast<float4*>(li + tid * 8) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(li + tid * 8 + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      }
+  };
+  // One 4 x 4 unit (rb >= cb) of the trailing lower triangle of panel k0 / 8.
+  auto trail = [&](int k0, int q) {
+    int rb = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+    while (rb * (rb + 1) / 2 > q) --rb;
+    while ((rb + 1) * (rb + 2) / 2 <= q) ++rb;
+    const int cb = q - rb * (rb + 1) / 2;
+    const int r0 = k0 + 8 + 4 * rb, c0 = k0 + 8 + 4 * cb;
+    float lr[4][8], lc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 u0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
+      const float4 u1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
+      const float4 w0 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0);
+      const float4 w1 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0 + 4);
+      lr[i][0] = u0.x; lr[i][1] = u0.y; lr[i][2] = u0.z; lr[i][3] = u0.w;
+      lr[i][4] = u1.x; lr[i][5] = u1.y; lr[i][6] = u1.z; lr[i][7] = u1.w;
+      lc[i][0] = w0.x; lc[i][1] = w0.y; lc[i][2] = w0.z; lc[i][3] = w0.w;
+      lc[i][4] = w1.x; lc[i][5] = w1.y; lc[i][6] = w1.z; lc[i][7] = w1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* dst = a + (r0 + i) * S + c0;
+      float4 v = *reinterpret_cast<const float4*>(dst);
+      float o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[q2] = fmaf(-lr[i][k], lc[q2][k], o[q2]);
+      if (rb == cb) {  // keep the upper part of a diagonal unit at zero
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) o[q2] = q2 <= i ? o[q2] : 0.f;
+      }
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  
+  };
+  diag(0);
+  __syncthreads();
   for (int p = 0; p < P; ++p) {
     const int k0 = p * 8;
-    if (tid < 8) {  // the diagonal block: lane i of wave 0 holds row i; Cholesky and inverse
-      float x[8], y[8];
-      {
-        const float4 u0 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0);
-        const float4 u1 = *reinterpret_cast<const float4*>(a + (k0 + tid) * S + k0 + 4);
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-      }
-      float rsi = 0.f;  // 1 / L[i][i] of this lane's row
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), c));
-        bad |= !(d > 0.f && isfinite(d));
-        const float dd = fmaxf(d, 1e-30f);
-        const float rs = __builtin_amdgcn_rsqf(dd);
-        if (tid == c) {
-          x[c] = dd * rs;
-          rsi = rs;
-        } else if (tid > c) {
-          x[c] *= rs;
-        }
-        // Column c of L below the diagonal, broadcast: row q's entry from lane q.
-#pragma unroll
-        for (int q = c + 1; q < 8; ++q) {
-          const float lq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x[c]), q));
-          if (tid >= q) x[q] = fmaf(-x[c], lq, x[q]);
-        }
-      }
-      // Row i of inv(L): y[q] = -rs_i sum_{k=q}^{i-1} L[i][k] y_k[q], rows in order
-      // (row k's entries broadcast from lane k once it is final).
-#pragma unroll
-      for (int q = 0; q < 8; ++q) y[q] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (tid == k) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) y[q] = q < k ? -y[q] * rsi : (q == k ? rsi : 0.f);
-        }
-#pragma unroll
-        for (int q = 0; q <= k; ++q) {
-          const float yk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(y[q]), k));
-          if (tid > k) y[q] = fmaf(x[k], yk, y[q]);  // accumulates sum_k L[i][k] y_k[q]
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = q <= tid ? x[q] : 0.f;
-      float* ar = a + (k0 + tid) * S + k0;
-      float* mr = m + (k0 + tid) * S + k0;
-      *reinterpret_cast<float4*>(ar) = make_float4(x[0], x[1], x[2], x[3]);
-      *reinterpret_cast<float4*>(ar + 4) = make_float4(x[4], x[5], x[6], x[7]);
-      *reinterpret_cast<float4*>(mr) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4*>(mr + 4) = make_float4(y[4], y[5], y[6], y[7]);
-      *reinterpret_cast<float4*>(li + tid * 8) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4*>(li + tid * 8 + 4) = make_float4(y[4], y[5], y[6], y[7]);
-    }
-    __syncthreads();
     // Rows below: L[r][k0 + q] = sum_c A[r][k0 + c] inv(L_pp)[q][c].
     const int r = k0 + 8 + tid;
     if (r < D) {
@@ -567,76 +608,60 @@ void jacap_factor_kernel(const JacapArgs j) {
       *reinterpret_cast<float4*>(tt + ii * D + c0) = make_float4(o[0], o[1], o[2], o[3]);
     }
     __syncthreads();
-    // Trailing lower triangle, 4 x 4 units (rb >= cb) of rows/columns k0 + 8 ...
+    // Wave 0 updates the next diagonal block (the first three trailing
+    // units) and factors it, while waves 1-3 take the other trailing units
+    // and the rows of M below.
     const int T = (D - k0 - 8) / 4;
-    for (int q = tid; q < T * (T + 1) / 2; q += kJThreads) {
-      int rb = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
-      while (rb * (rb + 1) / 2 > q) --rb;
-      while ((rb + 1) * (rb + 2) / 2 <= q) ++rb;
-      const int cb = q - rb * (rb + 1) / 2;
-      const int r0 = k0 + 8 + 4 * rb, c0 = k0 + 8 + 4 * cb;
-      float lr[4][8], lc[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 u0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
-        const float4 u1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
-        const float4 w0 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0);
-        const float4 w1 = *reinterpret_cast<const float4*>(a + (c0 + i) * S + k0 + 4);
-        lr[i][0] = u0.x; lr[i][1] = u0.y; lr[i][2] = u0.z; lr[i][3] = u0.w;
-        lr[i][4] = u1.x; lr[i][5] = u1.y; lr[i][6] = u1.z; lr[i][7] = u1.w;
-        lc[i][0] = w0.x; lc[i][1] = w0.y; lc[i][2] = w0.z; lc[i][3] = w0.w;
-        lc[i][4] = w1.x; lc[i][5] = w1.y; lc[i][6] = w1.z; lc[i][7] = w1.w;
+    const int ntri = T * (T + 1) / 2;
+    if (tid < 64) {
+      if (p + 1 < P) {
+        if (tid < 3) trail(k0, tid);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        diag(k0 + 8);
       }
+    } else {
+      const int t3 = tid - 64;
+      for (int q = 3 + t3; q < ntri; q += 192) trail(k0, q);
+      // Rows below of the running M: X[i][c] -= sum_k L[i][k0 + k] M_p[k][c] for
+      // c < k0 + 8 (4 x 4 units); block row p of M moves from tt into m.
+      {
+        const int RQ = (D - k0 - 8) / 4, CQ = (k0 + 8) / 4;
+        // The trailing units and these share one index space: index i of
+        // thread t3 is t3 + 192 k, trailing unit 3 + i below ntri - 3, unit
+        // i - (ntri - 3) here above it.
+        for (int u = ((t3 - (ntri - 3)) % 192 + 192) % 192; u < RQ * CQ; u += 192) {
+          const int r0 = k0 + 8 + 4 * (u / CQ), c0 = 4 * (u % CQ);
+          float4 tv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* dst = a + (r0 + i) * S + c0;
-        float4 v = *reinterpret_cast<const float4*>(dst);
-        float o[4] = {v.x, v.y, v.z, v.w};
+          for (int k = 0; k < 8; ++k) tv[k] = *reinterpret_cast<const float4*>(tt + k * D + c0);
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2)
+          for (int i = 0; i < 4; ++i) {
+            const float4 l0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
+            const float4 l1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
+            const float l[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            float* dst = m + (r0 + i) * S + c0;
+            float4 x = *reinterpret_cast<const float4*>(dst);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) o[q2] = fmaf(-lr[i][k], lc[q2][k], o[q2]);
-        if (rb == cb) {  // keep the upper part of a diagonal unit at zero
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) o[q2] = q2 <= i ? o[q2] : 0.f;
-        }
-        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-    }
-    // Rows below of the running M: X[i][c] -= sum_k L[i][k0 + k] M_p[k][c] for
-    // c < k0 + 8 (4 x 4 units); block row p of M moves from tt into m.
-    {
-      const int RQ = (D - k0 - 8) / 4, CQ = (k0 + 8) / 4;
-      for (int u = tid; u < RQ * CQ; u += kJThreads) {
-        const int r0 = k0 + 8 + 4 * (u / CQ), c0 = 4 * (u % CQ);
-        float4 tv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) tv[k] = *reinterpret_cast<const float4*>(tt + k * D + c0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 l0 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0);
-          const float4 l1 = *reinterpret_cast<const float4*>(a + (r0 + i) * S + k0 + 4);
-          const float l[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-          float* dst = m + (r0 + i) * S + c0;
-          float4 x = *reinterpret_cast<const float4*>(dst);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            x.x = fmaf(-l[k], tv[k].x, x.x);
-            x.y = fmaf(-l[k], tv[k].y, x.y);
-            x.z = fmaf(-l[k], tv[k].z, x.z);
-            x.w = fmaf(-l[k], tv[k].w, x.w);
+            for (int k = 0; k < 8; ++k) {
+              x.x = fmaf(-l[k], tv[k].x, x.x);
+              x.y = fmaf(-l[k], tv[k].y, x.y);
+              x.z = fmaf(-l[k], tv[k].z, x.z);
+              x.w = fmaf(-l[k], tv[k].w, x.w);
+            }
+            *reinterpret_cast<float4*>(dst) = x;
           }
-          *reinterpret_cast<float4*>(dst) = x;
         }
-      }
-      for (int u = tid; u < 2 * k0; u += kJThreads) {
-        const int ii = u % 8, c0 = (u / 8) * 4;
-        *reinterpret_cast<float4*>(m + (k0 + ii) * S + c0) = *reinterpret_cast<const float4*>(tt + ii * D + c0);
+        for (int u = t3; u < 2 * k0; u += 192) {
+          const int ii = u % 8, c0 = (u / 8) * 4;
+          *reinterpret_cast<float4*>(m + (k0 + ii) * S + c0) = *reinterpret_cast<const float4*>(tt + ii * D + c0);
+        }
       }
     }
     __syncthreads();
   }
-  if (bad) raise_error(j.err, kErrNonFinite);  // thread 0 checked every pivot
+  if (bad) raise_error(j.err, kErrNonFinite);
   __bf16* mh = j.minv + (long long)head * 2 * D * D;
   __bf16* ml = mh + D * D;
   for (int e = tid; e < D * D; e += kJThreads) {
