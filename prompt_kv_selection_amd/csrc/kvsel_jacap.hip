@@ -418,14 +418,16 @@ __global__ __launch_bounds__(kJThreads) void jacap_reduce_kernel(const JacapArgs
 
 // A = I + the slices' parts, then A = L L^T (Cholesky, fp32) and M = L^{-1},
 // blocked by 8-column panels with A, L and M in LDS (row stride D + 4 floats:
-// 16-byte aligned rows, consecutive rows four banks apart).  Per panel p,
-// three barriers:
-//   1. lanes 0-7 (a row each) factor the 8 x 8 diagonal block and invert it;
-//   2. the rows below are solved against that inverse (a row per thread), and
-//      block row p of M is inv(L_pp) times the running block row;
-//   3. the trailing lower triangle takes the rank-8 update in 4 x 4 units
-//      spread over the threads, and so do the rows of M below (L M = I
-//      right-looking: X_i -= L_ip M_p).
+// 16-byte aligned rows, consecutive rows four banks apart).  Lanes 0-7 of
+// wave 0 (a row each) factor and invert an 8 x 8 diagonal block.  Per panel
+// p, two barriers:
+//   1. the rows below are solved against the inverse of diagonal block p (a
+//      row per thread), and block row p of M is that inverse times the
+//      running block row;
+//   2. waves 1-3 take the rank-8 update of the trailing lower triangle in
+//      4 x 4 units, and the rows of M below (L M = I right-looking:
+//      X_i -= L_ip M_p); wave 0 meanwhile updates diagonal block p + 1 (the
+//      first three units) and factors it (look-ahead).
 // Only lower triangles are computed; the upper parts hold zeros.  M is stored
 // as bf16 hi and lo.
 template <int D>
