@@ -290,18 +290,27 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
  *   A = I + sum_j w_j u_j u_j^T, r_i = w_i u_i^T A^{-1} u_i (Cholesky of A),
  * then the selection of kvsel_refresh on the scores r: protected head and
  * tail, the flexible budget by score, ties to the lowest index, ascending,
- * K, V (and token ids) gathered.
- *   K, V, U [heads][N][D] bf16: keys, values, and the output directions
- *           u_i (W_O v_i, or V itself as the page's cheaper proxy)
- *   mu_q, lambda_q [heads][D] float32: running query mean and diagonal
- *           second moment (lambda_q >= 0); tau > 0 the temperature
+ * K, V (and token ids) gathered.  Scores cover all N tokens, protected ones
+ * included (the softmax is over the full pool).
+ *   K, V, U [heads][N][D] bf16 device arrays: keys, values, and the output
+ *           directions u_i (W_O v_i, or V itself as the page's cheaper proxy)
+ *   mu_q, lambda_q [heads][D] float32 device arrays: the query mean and the
+ *           diagonal second moment (lambda_q >= 0); tau > 0 the temperature
+ *   indices out [heads][keep]; K_out, V_out out [heads][keep][D];
+ *   tokens_opt / tokens_out_opt [heads][N] / [heads][keep] int32 or both NULL
  *   scores_opt out [heads][N] float32 leverage scores, or NULL
- *   other arguments and rules as for kvsel_refresh (n = N)
- * Supported: bf16, D in {64, 128} (else KVSEL_EUNSUPPORTED).  The two
- * N D^2 contractions run on MFMA with the fp32 factor split into bf16 high
- * and low parts; the factorisation is fp32.  kvsel_status(workspace) reports
- * a non-positive pivot or normaliser as KVSEL_ENONFINITE.  Workspace:
- * kvsel_jacap_workspace_bytes(heads, N, D), 256-byte aligned. */
+ *   keep, protect_head, protect_tail as for kvsel_refresh (n = N)
+ * All pointers are device pointers owned by the caller; nothing is
+ * allocated.  KVSEL_EINVAL: a NULL input or output, heads or N < 1, tau not
+ * finite and positive, keep outside [1, N], protection that does not fit,
+ * tokens without tokens_out, misaligned K, V, U, outputs (16 bytes) or
+ * workspace (256 bytes).  KVSEL_EUNSUPPORTED: dtype other than bf16, D not
+ * 64 or 128.  KVSEL_EWORKSPACE: workspace smaller than
+ * kvsel_jacap_workspace_bytes(heads, N, D).  The two N D^2 contractions run
+ * on bf16 MFMA with one operand exact (u) and the other (w u, or L^{-1})
+ * split into bf16 high and low parts; logits, weights and the factorisation
+ * are fp32.  kvsel_status(workspace) reports a non-finite or non-positive
+ * normaliser or pivot (e.g. a non-finite key) as KVSEL_ENONFINITE. */
 size_t kvsel_jacap_workspace_bytes(int heads, int N, int D);
 int kvsel_jacap_select(const void* K, const void* V, const void* U, const float* mu_q, const float* lambda_q,
                        float tau, int heads, int N, int D, int dtype, int keep, int protect_head,
