@@ -16,7 +16,8 @@
 //                  lanes per token, 16-byte loads), the chunk's softmax
 //                  partial (max, and Z - 1: the mass beyond the max).
 //   jacap_weights  per (head, chunk): the head's partials merged in a fixed
-//                  order, then w of every token.
+//                  order (a lane per chunk, then a butterfly), then w of
+//                  every token.
 //   jacap_gram     per (head, slice): the slice's part of sum w u u^T on MFMA
 //                  (v_mfma_f32_32x32x16_bf16), lower tiles only: u^T (exact
 //                  bf16) times (w u) split into bf16 hi + lo, about 16
@@ -156,13 +157,20 @@ __global__ __launch_bounds__(kJThreads) void jacap_logits_kernel(const JacapArgs
 __global__ __launch_bounds__(kJThreads) void jacap_weights_kernel(const JacapArgs j, int D) {
   const int head = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   __shared__ float s_m, s_z;
-  if (tid == 0) {  // the head's partials in chunk order: every workgroup gets the same (M, Z - 1)
+  if (tid < 64) {  // the head's partials: lane l takes chunks l, l + 64, ..., then the wave merges
     float m = kNegBig, s = -1.f;
-    for (int q = 0; q < j.nch; ++q)
+    for (int q = tid; q < j.nch; q += 64)
       lse1_merge(m, s, j.part[((long long)head * j.nch + q) * 2], j.part[((long long)head * j.nch + q) * 2 + 1]);
-    s_m = m;
-    s_z = s;
-    if (!(isfinite(m) && isfinite(s) && s >= 0.f)) raise_error(j.err, kErrNonFinite);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float mo = __shfl_xor(m, o), so = __shfl_xor(s, o);
+      lse1_merge(m, s, mo, so);
+    }
+    if (tid == 0) {  // lane 0's result, the same fixed order in every workgroup of the head
+      s_m = m;
+      s_z = s;
+      if (!(isfinite(m) && isfinite(s) && s >= 0.f)) raise_error(j.err, kErrNonFinite);
+    }
   }
   __syncthreads();
   const float M = s_m, s1 = s_z, iz = 1.f / (1.f + s1), invd = 1.f / (float)D;
