@@ -219,21 +219,22 @@ __device__ constexpr int gram_tile(int wave, int q) {
 
 template <int D>
 struct GramShape {
-  static constexpr int TS = D == 128 ? 64 : 128;  // tokens per step: 256 units of 4 tokens x 8 features
-  static_assert(TS / 4 * D / 8 == 256, "one unit per thread");
+  static constexpr int TS = D == 128 ? 64 : 128;  // tokens per step: 512 units of 2 tokens x 8 features
+  static_assert(TS / 2 * D / 8 == 512, "one unit per staging thread");
   static constexpr int RS = TS + 8;               // LDS row stride (elements)
   static constexpr int FG = D / 8;                // feature groups
   static constexpr int ARR = D * RS;              // one operand array
 };
 
-// One step's share of a thread: 4 tokens x 8 features of U and the 4 weights.
+// One step's share of a staging thread: 2 tokens x 8 features of U and the
+// 2 weights.
 template <int D>
 __device__ __forceinline__ void gram_load(const JacapArgs& j, const __bf16* __restrict__ U, int head, int t, int t1,
-                                          int fg, uint4 (&d)[4], float (&w)[4]) {
+                                          int fg, uint4 (&d)[2], float (&w)[2]) {
   // Tokens past the slice load its last row (their weight is zeroed when
   // staged), so that no load sits in a branch.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int tc = max(min(t + i, t1 - 1), 0);
     d[i] = *reinterpret_cast<const uint4*>(U + ((long long)head * j.N + tc) * D + fg * 8);
     w[i] = j.w[(long long)head * j.N + tc];
@@ -243,37 +244,29 @@ __device__ __forceinline__ void gram_load(const JacapArgs& j, const __bf16* __re
 // Writes the share into the operand arrays (feature-major: a row per feature,
 // the step's tokens along it): u^T exactly, and (w u)^T as bf16 high + low.
 template <int D>
-__device__ __forceinline__ void gram_stage(__bf16* buf, int fg, int tg, const uint4 (&d)[4], const float (&wl)[4],
+__device__ __forceinline__ void gram_stage(__bf16* buf, int fg, int tg, const uint4 (&d)[2], const float (&wl)[2],
                                            int valid) {
   using S = GramShape<D>;
-  float w[4];  // tokens past the slice weigh 0: every product has a (w u) factor, so they add nothing
+  float w[2];  // tokens past the slice weigh 0: every product has a (w u) factor, so they add nothing
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = i < valid ? wl[i] : 0.f;
+  for (int i = 0; i < 2; ++i) w[i] = i < valid ? wl[i] : 0.f;
   __bf16* ut = buf;
   __bf16* bh = buf + S::ARR;
   __bf16* bl = buf + 2 * S::ARR;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const unsigned x[4] = {(&d[0].x)[q], (&d[1].x)[q], (&d[2].x)[q], (&d[3].x)[q]};
+    const unsigned x[2] = {(&d[0].x)[q], (&d[1].x)[q]};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // feature 8 fg + 2 q + h: the low (h = 0) or high bf16 of each word
-      const int o = (fg * 8 + 2 * q + h) * S::RS + tg * 4;
-      uint2 u2, hi2, lo2;
-      if (h == 0) {
-        u2.x = (x[0] & 0xFFFFu) | (x[1] << 16);
-        u2.y = (x[2] & 0xFFFFu) | (x[3] << 16);
-      } else {
-        u2.x = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
-        u2.y = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
-      }
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(h == 0 ? x[i] << 16 : x[i] & 0xFFFF0000u) * w[i];
-      split2(v[0], v[1], hi2.x, lo2.x);
-      split2(v[2], v[3], hi2.y, lo2.y);
-      *reinterpret_cast<uint2*>(ut + o) = u2;
-      *reinterpret_cast<uint2*>(bh + o) = hi2;
-      *reinterpret_cast<uint2*>(bl + o) = lo2;
+      const int o = (fg * 8 + 2 * q + h) * S::RS + tg * 2;
+      const unsigned u = h == 0 ? (x[0] & 0xFFFFu) | (x[1] << 16) : (x[0] >> 16) | (x[1] & 0xFFFF0000u);
+      const float v0 = __uint_as_float(h == 0 ? x[0] << 16 : x[0] & 0xFFFF0000u) * w[0];
+      const float v1 = __uint_as_float(h == 0 ? x[1] << 16 : x[1] & 0xFFFF0000u) * w[1];
+      unsigned hi, lo;
+      split2(v0, v1, hi, lo);
+      *reinterpret_cast<unsigned*>(ut + o) = u;
+      *reinterpret_cast<unsigned*>(bh + o) = hi;
+      *reinterpret_cast<unsigned*>(bl + o) = lo;
     }
   }
 }
@@ -303,13 +296,13 @@ __device__ __forceinline__ void gram_mfma(const __bf16* cur, int n, int g, f32x1
 // the head, into gpart[head][slice][D][D] (lower 32 x 32 tiles only).  Each
 // MFMA pair multiplies u^T (exact bf16) by the high and the low bf16 part of
 // (w u): products correct to about 2^-17 relative, fp32 accumulation.
-// Waves 0-3 multiply; waves 4-7 load and stage (16-byte loads of token rows,
+// Waves 0-3 multiply; waves 4-11 load and stage (16-byte loads of token rows,
 // transposed in registers, into one of two LDS buffers) the next step while
 // the others multiply the current one, so the staging arithmetic runs beside
 // the MFMAs on the same SIMDs and a step needs one barrier.  The loads run
 // kPre steps ahead of the staging (a ring of register sets).
 constexpr int kPre = 5;
-constexpr int kGramThreads = 512;
+constexpr int kGramThreads = 768;  // waves 0-3 multiply, waves 4-11 stage
 template <int D, int WV>  // WV < 4: the multiplying wave of that tile set; WV == 4: a staging wave
 __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __restrict__ U, __bf16* lds) {
   using S = GramShape<D>;
@@ -317,9 +310,9 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
   const int head = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, n = lane & 31, g = lane >> 5;
   // A staging wave stages whole feature rows: QW lanes take consecutive token
-  // quads of one feature group, so that its 8-byte LDS writes cover
-  // consecutive banks (two rows per write at most share a bank).
-  constexpr int QW = S::TS / 4;
+  // pairs of one feature group, so that its 4-byte LDS writes cover
+  // consecutive banks (the two rows of a write fall on disjoint halves).
+  constexpr int QW = S::TS / 2;
   const int ts = tid - 256;
   const int fg = (ts >> 6) * (64 / QW) + lane / QW, tg = lane % QW;
   const int per = (j.N + j.slices - 1) / j.slices;
@@ -328,12 +321,12 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
   constexpr int R = kPre + 1;
   static_assert(R % 2 == 0, "the ring period must be even");
   f32x16 acc[3];
-  uint4 d[R][4];
-  float w[R][4];
+  uint4 d[R][2];
+  float w[R][2];
   if constexpr (kStage) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) gram_load<D>(j, U, head, t0 + u * S::TS + tg * 4, t1, fg, d[u], w[u]);
-    if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 4));
+    for (int u = 0; u < kPre; ++u) gram_load<D>(j, U, head, t0 + u * S::TS + tg * 2, t1, fg, d[u], w[u]);
+    if (steps > 0) gram_stage<D>(lds, fg, tg, d[0], w[0], t1 - (t0 + tg * 2));
   } else {
 #pragma unroll
     for (int q = 0; q < 3; ++q) acc[q] = f32x16{};
@@ -349,9 +342,9 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
   auto step = [&](int st, auto uc) {
     constexpr int u = decltype(uc)::value;
     if constexpr (kStage) {
-      gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 4, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
+      gram_load<D>(j, U, head, t0 + (st + kPre) * S::TS + tg * 2, t1, fg, d[(u + kPre) % R], w[(u + kPre) % R]);
       gram_stage<D>(lds + ((u + 1) & 1) * 3 * S::ARR, fg, tg, d[(u + 1) % R], w[(u + 1) % R],
-                    t1 - (t0 + (st + 1) * S::TS + tg * 4));
+                    t1 - (t0 + (st + 1) * S::TS + tg * 2));
     } else {
       gram_mfma<D, WV>(lds + (u & 1) * 3 * S::ARR, n, g, acc);
     }
@@ -388,7 +381,7 @@ __device__ __forceinline__ void gram_body(const JacapArgs& j, const __bf16* __re
 }
 
 template <int D>
-__global__ __launch_bounds__(kGramThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kGramThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void jacap_gram_kernel(const JacapArgs j, const __bf16* __restrict__ U) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 3 * GramShape<D>::ARR];
   switch (threadIdx.x >> 6) {  // every wave runs the same steps and barriers
