@@ -448,7 +448,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
 
 extern "C" {
 
-int kvsel_version(void) { return (0 << 16) | 2; }
+int kvsel_version(void) { return (0 << 16) | 3; }
 
 int kvsel_set_option(int option, int value) {
   if (option == KVSEL_OPT_SCORING) {
