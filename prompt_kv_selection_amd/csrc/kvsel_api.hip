@@ -616,7 +616,8 @@ size_t kvsel_topk_workspace_bytes(int rows, int n) {
 // Top-k over rows of scores described by a (one segment: positions 0 .. L-1 of
 // each row at scores + vote_off + row * vote_ld, C - (window ? W : 0) picks,
 // then the window positions when a.window), into out + idx_off + row * idx_ld.
-static int run_topk(Launch& a, int rows, const float* scores, int32_t* out, void* workspace, hipStream_t st) {
+static int run_topk(Launch& a, int rows, const float* scores, int32_t* out, void* workspace, hipStream_t st,
+                    bool hist_zeroed = false) {
   const Seg& s = a.seg[0];
   const int n = s.L;
   a.seg_size = selection_seg_size(n);
@@ -624,8 +625,11 @@ static int run_topk(Launch& a, int rows, const float* scores, int32_t* out, void
   uint32_t* cut = (uint32_t*)((char*)workspace + align256((size_t)rows * 2048 * 4));
   uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
   uint32_t* cand = (uint32_t*)((char*)segcnt + align256((size_t)rows * kSegCntBytes));
-  hipError_t e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
-  if (e != hipSuccess) return device_error(e, "fill launch");
+  hipError_t e = hipSuccess;
+  if (!hist_zeroed) {  // otherwise an earlier kernel of the call cleared the histograms
+    e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
+    if (e != hipSuccess) return device_error(e, "fill launch");
+  }
   e = timed("pool", st, [&] { return launch_pool(a, rows, n, scores, nullptr, hist, st); });
   if (e != hipSuccess) return device_error(e, "histogram launch");
   if (n <= select_rows_max()) {  // one workgroup per row
@@ -673,7 +677,8 @@ size_t kvsel_refresh_workspace_bytes(int rows, int n) { return kvsel_topk_worksp
 
 static int refresh_core(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
                         const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
-                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st);
+                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st,
+                        bool hist_zeroed = false);
 
 int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
                   const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
@@ -702,7 +707,8 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
 
 static int refresh_core(const float* scores, int rows, int n, int keep, int protect_head, int protect_tail,
                         const void* K, const void* V, int D, int dtype, const int32_t* tokens_opt, int32_t* indices,
-                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st) {
+                        void* K_out, void* V_out, int32_t* tokens_out_opt, void* workspace, hipStream_t st,
+                        bool hist_zeroed) {
   const int flexible = keep - protect_head - protect_tail;
   if (flexible > 0) {
     // Positions protect_head .. n-1 of each row, the last protect_tail of
@@ -721,7 +727,7 @@ static int refresh_core(const float* scores, int rows, int n, int keep, int prot
     s.vote_ld = n;
     s.idx_off = protect_head;
     s.idx_ld = keep;
-    const int rc = run_topk(a, rows, scores, indices, workspace, st);
+    const int rc = run_topk(a, rows, scores, indices, workspace, st, hist_zeroed);
     if (rc) return rc;
   }
   hipError_t e = timed("finish", st, [&] {
@@ -829,12 +835,14 @@ int kvsel_jacap_select(const void* K, const void* V, const void* U, const float*
   j.gpart = (float*)(ws + q.off_gram);
   j.minv = (__bf16*)(ws + q.off_minv);
   j.err = (unsigned*)ws;  // cleared by the first kernel
+  j.hist = (uint32_t*)(ws + q.off_sel);  // the selection's histograms, cleared by the weights kernel
+  j.hist_words = (long long)heads * 2048;
   hipError_t e = launch_jacap_scores(j, D, K, U, st, [&](const char* name, const std::function<hipError_t()>& f) {
     return timed(name, st, f);
   });
   if (e != hipSuccess) return device_error(e, "jacap launch");
   return refresh_core(j.r, heads, N, keep, protect_head, protect_tail, K, V, D, dtype, tokens_opt, indices, K_out,
-                      V_out, tokens_out_opt, ws + q.off_sel, st);
+                      V_out, tokens_out_opt, ws + q.off_sel, st, true);
 }
 
 int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling, float* pooled, void* stream) {

@@ -22,6 +22,8 @@ struct JacapArgs {
   __bf16* minv;         // [heads][2][D][D] L^{-1} as bf16 hi, lo
   float* r;             // [heads][N] leverage scores
   unsigned* err;
+  uint32_t* hist;       // [hist_words] selection histograms, cleared by the weights kernel
+  long long hist_words;
 };
 int jacap_chunks(int N);
 int jacap_slices(int N, int heads);

@@ -17,7 +17,7 @@
 //                  partial (max, and Z - 1: the mass beyond the max).
 //   jacap_weights  per (head, chunk): the head's partials merged in a fixed
 //                  order (a lane per chunk, then a butterfly), then w of
-//                  every token.
+//                  every token; also clears the selection's histograms.
 //   jacap_gram     per (head, slice): the slice's part of sum w u u^T on MFMA
 //                  (v_mfma_f32_32x32x16_bf16), lower tiles only: u^T (exact
 //                  bf16) times (w u) split into bf16 hi + lo, about 16
@@ -184,6 +184,13 @@ __global__ __launch_bounds__(kJThreads) void jacap_weights_kernel(const JacapArg
     const float om = (s1 - expm1f(d)) * iz;
     const float rho = a * om;
     j.w[i] = rho * rho * j.kappa[i] * invd;
+  }
+  // The refresh selection's first-digit histograms start from zero: cleared
+  // here (the grid, in 16-byte stores) instead of by a launch of their own.
+  if (j.hist != nullptr) {
+    const long long nwg = (long long)gridDim.x * gridDim.y, wg = (long long)blockIdx.y * gridDim.x + blockIdx.x;
+    uint4* h4 = reinterpret_cast<uint4*>(j.hist);
+    for (long long q = wg * kJThreads + tid; q < j.hist_words / 4; q += nwg * kJThreads) h4[q] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
