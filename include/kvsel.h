@@ -124,10 +124,56 @@ const char* kvsel_last_error(void);
  * non-finite or zero row normaliser was seen (the outputs follow the
  * arithmetic but carry no meaning); KVSEL_EDEVICE if a bounded wait between
  * workgroups timed out (the outputs of that call are unreliable); or
- * KVSEL_EINVAL for a NULL or misaligned workspace.  Each selection call
+ * KVSEL_EINVAL for a NULL or misaligned workspace, or for an input outside
+ * its domain found on the device (kvsel_jacap_select: a negative or NaN
+ * lambda_q entry).  Each selection call
  * clears the flags at its start.  This is the only entry point that
  * synchronises. */
 int kvsel_status(const void* workspace, void* stream);
+
+/* Device-side flags of a workspace, for callers that check a run of calls
+ * (a benchmark's timed region) or want to know which way a residency
+ * handshake went.  Waits for `stream`, then stores the flags of the last call
+ * in *last_flags and the OR of the flags of every call since the last reset
+ * in *sticky_flags (either pointer may be NULL); with reset != 0 the sticky
+ * word is then cleared.  A freshly allocated workspace holds arbitrary bits
+ * there: reset once before the run.  KVSEL_OK, KVSEL_EINVAL (NULL or
+ * misaligned workspace) or KVSEL_EDEVICE.  Synchronises; host memory only.
+ * Flag bits (KVSEL_FLAG_*): the three waits and the non-finite and domain
+ * conditions that kvsel_status reports, and two that are not errors:
+ * SCORING_FALLBACK (the single-read scoring found its grid not all resident,
+ * as on a device shared with other work, and scored each head alone in two
+ * passes) and SELECT_FALLBACK (the same for the cooperative selection, which
+ * then resolves each row in one workgroup).  Results are identical either
+ * way; only the time differs. */
+#define KVSEL_FLAG_EXCHANGE_WAIT 0x1u
+#define KVSEL_FLAG_LDS_WAIT 0x2u
+#define KVSEL_FLAG_SELECT_WAIT 0x4u
+#define KVSEL_FLAG_NONFINITE 0x8u
+#define KVSEL_FLAG_DOMAIN 0x10u
+#define KVSEL_FLAG_SCORING_FALLBACK 0x100u
+#define KVSEL_FLAG_SELECT_FALLBACK 0x200u
+int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned* last_flags,
+                       unsigned* sticky_flags);
+
+/* Kernel path the library chose for the last selection call made on this
+ * thread (host decisions, taken from the shape and the options):
+ * KVSEL_PATH_* bits.  Scoring: SINGLE_READ (K streamed once, statistics
+ * exchanged between workgroups), TWO_PASS (statistics pass, then votes pass),
+ * VOTES_ONLY (handed-over statistics on the two-pass kernels), HANDED_OVER
+ * (row_lse given); BYPASS (a prompt shorter than its budget); selection:
+ * SELECT_COOP (one cooperative launch: pooling, top-k, picks and the K/V
+ * copy), SELECT_ROWS (a workgroup per row, then the gather), SELECT_SEGMENTS
+ * (the segment-parallel chain).  0 before the first call. */
+#define KVSEL_PATH_SINGLE_READ 0x1u
+#define KVSEL_PATH_TWO_PASS 0x2u
+#define KVSEL_PATH_VOTES_ONLY 0x4u
+#define KVSEL_PATH_HANDED_OVER 0x8u
+#define KVSEL_PATH_BYPASS 0x10u
+#define KVSEL_PATH_SELECT_COOP 0x20u
+#define KVSEL_PATH_SELECT_ROWS 0x40u
+#define KVSEL_PATH_SELECT_SEGMENTS 0x80u
+unsigned kvsel_last_path(void);
 
 /* Workspace bytes kvsel_select needs for these sizes; 0 if the arguments are
  * invalid (kvsel_last_error() says why).  Host-only, enqueues nothing. */
@@ -243,7 +289,7 @@ int kvsel_select_varlen_lse(const void* Qwin, const void* K, const void* V, cons
  * above), for callers that bring their own scores or indices.
  *
  * kvsel_topk: for each of `rows` score rows of length n (row r at
- *   scores + r * n, float32, every value finite and >= 0), write the `count`
+ *   scores + r * n, float32, every value finite and >= 0; -0 ranks as +0), write the `count`
  *   positions with the highest score, equal scores going to the lowest index,
  *   in ascending order, to out + r * ld_out.  1 <= count <= n.
  *   Workspace: kvsel_topk_workspace_bytes(rows, n) bytes, 256-byte aligned
@@ -268,7 +314,7 @@ int kvsel_topk(const float* scores, int rows, int n, int count, int32_t* out, in
  * protected prefix, sinks and recent window first, the flexible budget filled
  * by score, and its sanity checks: the kept count equals the budget.]  The
  * score is the caller's (the pages' scores need the model).
- *   scores [rows][n] float32, every value finite and >= 0
+ *   scores [rows][n] float32, every value finite and >= 0 (-0 ranks as +0)
  *   K, V [rows][n][D] (dtype), tokens_opt [rows][n] int32 or NULL
  *   indices out [rows][keep]; K_out, V_out out [rows][keep][D];
  *   tokens_out_opt out [rows][keep] (given with tokens_opt)
@@ -310,7 +356,8 @@ int kvsel_refresh(const float* scores, int rows, int n, int keep, int protect_he
  * on bf16 MFMA with one operand exact (u) and the other (w u, or L^{-1})
  * split into bf16 high and low parts; logits, weights and the factorisation
  * are fp32.  kvsel_status(workspace) reports a non-finite or non-positive
- * normaliser or pivot (e.g. a non-finite key) as KVSEL_ENONFINITE. */
+ * normaliser or pivot (e.g. a non-finite key) as KVSEL_ENONFINITE, and a
+ * negative or NaN lambda_q entry as KVSEL_EINVAL. */
 size_t kvsel_jacap_workspace_bytes(int heads, int N, int D);
 int kvsel_jacap_select(const void* K, const void* V, const void* U, const float* mu_q, const float* lambda_q,
                        float tau, int heads, int N, int D, int dtype, int keep, int protect_head,
@@ -334,6 +381,19 @@ int kvsel_pool1d(const float* votes, int rows, int n, int kernel, int pooling,
 int kvsel_gather(const void* K, const void* V, const int32_t* indices, int ld_idx,
                  int heads, int L, int count, int D, int dtype,
                  void* K_out, void* V_out, void* stream);
+
+/* Streaming-read probe for benchmarks (not part of the selection): reads
+ * `bytes` of device memory at src once and writes a checksum word per wave
+ * to sink (device memory of kvsel_probe_sink_bytes() bytes), so that the
+ * time of the launch is what HBM (or the last-level cache) delivers to one
+ * of the scoring kernels' access patterns.  mode 0: one workgroup per CU of
+ * 8 waves, each with one 8 KiB tile of direct-to-LDS loads in flight (the
+ * single-read scoring kernel's pattern); mode 1: the same with two tiles per
+ * wave; mode 2: 4 waves with four tiles each; mode 3: 16-byte vector loads
+ * into registers, grid-stride, four per lane in flight.  Modes 0-2 read whole
+ * 128 KiB blocks (bytes a multiple of 131072).  Asynchronous on `stream`. */
+size_t kvsel_probe_sink_bytes(void);
+int kvsel_probe_stream(const void* src, size_t bytes, int mode, void* sink, size_t sink_bytes, void* stream);
 
 /* Per-kernel timing for benchmarks (not part of the selection itself).
  * kvsel_profile_enable(1) clears the record and, until kvsel_profile_enable(0),

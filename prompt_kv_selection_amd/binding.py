@@ -40,6 +40,18 @@ lib.kvsel_last_error.restype = ctypes.c_char_p
 lib.kvsel_last_error.argtypes = []
 lib.kvsel_status.restype = _i
 lib.kvsel_status.argtypes = [_vp, _vp]
+lib.kvsel_status_flags.restype = _i
+lib.kvsel_status_flags.argtypes = [_vp, _vp, _i, ctypes.POINTER(ctypes.c_uint), ctypes.POINTER(ctypes.c_uint)]
+lib.kvsel_last_path.restype = ctypes.c_uint
+lib.kvsel_last_path.argtypes = []
+FLAG = {"exchange_wait": 0x1, "lds_wait": 0x2, "select_wait": 0x4, "nonfinite": 0x8, "domain": 0x10,
+        "scoring_fallback": 0x100, "select_fallback": 0x200}
+PATH = {"single_read": 0x1, "two_pass": 0x2, "votes_only": 0x4, "handed_over": 0x8, "bypass": 0x10,
+        "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80}
+lib.kvsel_probe_sink_bytes.restype = _sz
+lib.kvsel_probe_sink_bytes.argtypes = []
+lib.kvsel_probe_stream.restype = _i
+lib.kvsel_probe_stream.argtypes = [_vp, _sz, _i, _vp, _sz, _vp]
 lib.kvsel_workspace_bytes.restype = _sz
 lib.kvsel_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 lib.kvsel_varlen_workspace_bytes.restype = _sz
@@ -104,6 +116,38 @@ def _stream(stream) -> ctypes.c_void_p:
 def _i32_array(values: Sequence[int]):
     arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
     return arr
+
+
+def kvsel_status_flags(workspace, stream=None, reset=False):
+    """(last call's flags, sticky flags since the last reset) of a
+    workspace; waits for the stream.  reset=True clears the sticky word."""
+    last, sticky = ctypes.c_uint(0), ctypes.c_uint(0)
+    _check(lib.kvsel_status_flags(_ptr(workspace), _stream(stream), 1 if reset else 0, ctypes.byref(last),
+                                  ctypes.byref(sticky)))
+    return last.value, sticky.value
+
+
+def kvsel_probe_stream(src, mode, sink, stream=None, nbytes=None) -> None:
+    """Streaming-read probe over src (a device tensor; nbytes of it)."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib.kvsel_probe_stream(_ptr(src), n, mode, _ptr(sink), sink.numel() * sink.element_size(),
+                                  _stream(stream)))
+
+
+def kvsel_probe_sink_bytes() -> int:
+    return lib.kvsel_probe_sink_bytes()
+
+
+def kvsel_last_path() -> int:
+    return lib.kvsel_last_path()
+
+
+def flag_names(flags: int):
+    return [k for k, v in FLAG.items() if flags & v]
+
+
+def path_names(path: int):
+    return [k for k, v in PATH.items() if path & v]
 
 
 def kvsel_version() -> int:

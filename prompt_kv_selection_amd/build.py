@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvsel.so")
 ARCH = os.environ.get("KVSEL_ARCH", "gfx950")
 
-SOURCES = ["kvsel_api.hip", "kvsel_score.hip", "kvsel_select.hip", "kvsel_fused.hip", "kvsel_jacap.hip"]
+SOURCES = ["kvsel_api.hip", "kvsel_score.hip", "kvsel_select.hip", "kvsel_fused.hip", "kvsel_jacap.hip",
+           "kvsel_probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -95,6 +95,9 @@ constexpr size_t kHeaderBytes = 256;
 constexpr size_t kCutBytes = 2 * sizeof(uint32_t);
 constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
 
+// Host-side path of the last selection call on this thread (kvsel_last_path).
+thread_local unsigned g_last_path = 0u;
+
 // Process-wide options.
 int g_scoring = KVSEL_SCORING_AUTO;
 int g_force_fallback = 0;
@@ -175,8 +178,30 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   return KVSEL_OK;
 }
 
+// Wall-clock ticks of the residency bound on the current device: the rate
+// of the device's constant-rate clock (kHz) is read once per device.
+long long residency_ticks() {
+  static std::mutex mu;
+  static int rate_khz[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int khz;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (rate_khz[dev] == 0) {
+      int r = 0;
+      if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) != hipSuccess || r <= 0)
+        r = 100000;  // the CDNA constant clock runs at 100 MHz where the attribute is missing
+      rate_khz[dev] = r;
+    }
+    khz = rate_khz[dev];
+  }
+  return kResidencyMicros * (long long)khz / 1000;
+}
+
 Launch base_launch(const Plan& p, int kernel, int pooling) {
   Launch a{};
+  a.residency_ticks = residency_ticks();
   a.heads = p.heads;
   a.W = p.W;
   a.D = p.D;
@@ -291,6 +316,17 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   for (int gsegs : coop_segs) all_coop = all_coop && gsegs > 0;
   unsigned* err = (unsigned*)ws;  // the header's error word
   {
+    unsigned path = 0u;
+    if (need_scoring)
+      path |= use_fused ? KVSEL_PATH_SINGLE_READ : (lse != nullptr ? KVSEL_PATH_VOTES_ONLY : KVSEL_PATH_TWO_PASS);
+    if (need_scoring && lse != nullptr) path |= KVSEL_PATH_HANDED_OVER;
+    for (int b = 0; b < p.B; ++b)
+      if (p.L[b] < p.C[b]) path |= KVSEL_PATH_BYPASS;
+    if (any_coop) path |= KVSEL_PATH_SELECT_COOP;
+    if (!all_coop) path |= whole_rows ? KVSEL_PATH_SELECT_ROWS : KVSEL_PATH_SELECT_SEGMENTS;
+    g_last_path = path;
+  }
+  {
     // The header, and the exchange records, status words, histograms and
     // the cooperative selection's words that are in use, start at zero (on
     // the two-pass path without the cooperative selection the statistics
@@ -301,7 +337,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     const size_t hi1 = hists ? p.off_coop : (use_fused ? p.off_hist : lo1);
     ZeroRanges z{};
     z.p[0] = ws;
-    z.bytes[0] = (long long)kHeaderBytes;
+    z.bytes[0] = 16;  // the call's flag words; the sticky word (kStickyWord) is left alone
     z.p[1] = ws + lo1;
     z.bytes[1] = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
     z.p[2] = ws + p.off_coop;
@@ -318,7 +354,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       hipError_t r = launch_check_finite(Q, q16, p.dtype, err, st);
       if (r == hipSuccess) r = launch_check_finite(K, kv16, p.dtype, err, st);
       if (r == hipSuccess) r = launch_check_finite(V, kv16, p.dtype, err, st);
-      if (r == hipSuccess && lse != nullptr) r = launch_check_finite(lse, (long long)p.B * p.heads * p.W / 4, 0, err, st);
+      if (r == hipSuccess && lse != nullptr) r = launch_check_finite_f32(lse, (long long)p.B * p.heads * p.W, err, st);
       return r;
     });
     if (e != hipSuccess) return device_error(e, "check launch");
@@ -490,9 +526,58 @@ int kvsel_status(const void* workspace, void* stream) {
   if (flags & (kErrExchangeWait | kErrLdsWait | kErrSelectWait))
     return fail(KVSEL_EDEVICE, "a bounded device-side wait timed out (flags 0x%x): the outputs of that call are "
                                "unreliable", flags);
+  if (flags & kErrDomain)
+    return fail(KVSEL_EINVAL, "an input outside its domain: a negative or NaN lambda_q entry (flags 0x%x)", flags);
   if (flags & kErrNonFinite)
     return fail(KVSEL_ENONFINITE, "a non-finite input value or a non-finite or zero row normaliser (flags 0x%x)",
                 flags);
+  return ok();
+}
+
+int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned* last_flags, unsigned* sticky_flags) {
+  if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
+  unsigned words[kStickyWord + 1] = {};
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(words, workspace, sizeof words, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && reset) {
+    static const unsigned zero = 0u;
+    e = hipMemcpyAsync((unsigned*)workspace + kStickyWord, &zero, sizeof zero, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  if (e != hipSuccess) return device_error(e, "status read");
+  if (last_flags) *last_flags = words[0];
+  if (sticky_flags) *sticky_flags = words[kStickyWord];
+  return ok();
+}
+
+unsigned kvsel_last_path(void) { return g_last_path; }
+
+size_t kvsel_probe_sink_bytes(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return (size_t)probe_sink_words(cus) * sizeof(unsigned);
+}
+
+int kvsel_probe_stream(const void* src, size_t bytes, int mode, void* sink, size_t sink_bytes, void* stream) {
+  if (!src || !sink) return fail(KVSEL_EINVAL, "src and sink must not be NULL");
+  if (mode < 0 || mode > 3) return fail(KVSEL_EINVAL, "probe mode must be 0..3 (got %d)", mode);
+  if ((uintptr_t)src % 16 || (uintptr_t)sink % 4) return fail(KVSEL_EINVAL, "src must be 16-byte aligned");
+  if (mode <= 2 && bytes % (128 * 1024) != 0)
+    return fail(KVSEL_EINVAL, "tile probes read whole 128 KiB blocks (%zu bytes)", bytes);
+  if (bytes % 16 != 0 || bytes == 0) return fail(KVSEL_EINVAL, "bytes must be a positive multiple of 16");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_error(e, "device query");
+  if (sink_bytes < (size_t)probe_sink_words(cus) * sizeof(unsigned))
+    return fail(KVSEL_EWORKSPACE, "sink of %zu bytes is smaller than the %zu required", sink_bytes,
+                (size_t)probe_sink_words(cus) * sizeof(unsigned));
+  e = timed(mode == 3 ? "probe_vector" : "probe_tiles", (hipStream_t)stream,
+            [&] { return launch_probe(mode, src, (long long)bytes, (unsigned*)sink, cus, (hipStream_t)stream); });
+  if (e != hipSuccess) return device_error(e, "probe launch");
   return ok();
 }
 

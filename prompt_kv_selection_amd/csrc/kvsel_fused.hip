@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   if (wave == kSW) {
     if constexpr (kLse)
       ctl_lse(a, lse, s_m, &sy);  // no workgroup waits for another
-    else if (decide(status, arrived) == kFusedGo)
+    else if (decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks) == kFusedGo)
       ctl_exchange<D>(a, ex, status, row_stats, s_m, &sy);
     else
       lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
@@ -932,6 +932,15 @@ __global__ void check_finite_kernel(const uint4* __restrict__ p, long long n, in
   if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) raise_error(err, kErrNonFinite);
 }
 
+// Validating mode for float32 arrays of any length and 4-byte alignment
+// (the handed-over log-sum-exps): scalar loads, every element checked.
+__global__ void check_finite_f32_kernel(const float* __restrict__ p, long long n, unsigned* err) {
+  bool bad = false;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    bad = bad || (__float_as_uint(p[i]) & 0x7F800000u) == 0x7F800000u;
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) raise_error(err, kErrNonFinite);
+}
+
 struct GridCache {
   int device = -1;
   int grid[2][2] = {{-1, -1}, {-1, -1}};
@@ -1022,6 +1031,13 @@ hipError_t launch_check_finite(const void* p, long long n16, int dtype, unsigned
   const long long blocks = std::min<long long>((n16 + 255) / 256, 4096);
   hipLaunchKernelGGL(check_finite_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)p, n16,
                      dtype == 1 ? 1 : 0, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite_f32(const float* p, long long n, unsigned* err, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = std::min<long long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(check_finite_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, err);
   return hipGetLastError();
 }
 

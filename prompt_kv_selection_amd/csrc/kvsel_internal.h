@@ -61,6 +61,7 @@ struct Launch {
   int seg_size;   // selection: positions per emit workgroup (multiple of 2048)
   unsigned* err;  // error flags of the call (the workspace header word), or nullptr
   int group;      // query heads per K/V head (grouped-query attention); 0 or 1: one each
+  long long residency_ticks;  // wall-clock ticks of the residency bound (kResidencyMicros)
   Seg seg[kMaxSegs];
 };
 
@@ -76,9 +77,20 @@ enum : unsigned {
   kErrLdsWait = 2u,       // single-read scoring: a wait between the waves of a workgroup timed out
   kErrSelectWait = 4u,    // selection: a wait for another workgroup's histogram or counts timed out
   kErrNonFinite = 8u,     // a non-finite input (validating mode) or a non-finite or zero row normaliser
+  kErrDomain = 16u,       // an input outside its documented domain (a negative second-moment entry)
+  // Not errors: which way a residency handshake went.
+  kFlagScoringFallback = 256u,  // single-read scoring: not all resident, whole heads scored alone
+  kFlagSelectFallback = 512u,   // cooperative selection: not all resident, whole rows by one workgroup
 };
+// The workspace header: word 0 holds the flags of the last call (cleared by
+// every call), word kStickyWord the OR of every call's flags since the
+// caller last reset it (kvsel_status_flags).
+constexpr int kStickyWord = 4;
 __device__ inline void raise_error(unsigned* err, unsigned bit) {
-  if (err != nullptr) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (err != nullptr) {
+    __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(err + kStickyWord, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 // A window row's statistics are usable: finite maximum, finite positive normaliser.
 __device__ inline bool stats_ok(float m, float z) { return isfinite(m) && isfinite(z) && z > 0.f; }
@@ -179,22 +191,33 @@ constexpr int kFusedStatusWords = kArriveStride * (kArriveGroups + 1);
 //    bound decides ABORT.  Both are a compare-and-swap on one zeroed word,
 //    so every workgroup follows the same decision, and GO implies that all
 //    of them are resident.
-constexpr long long kResidencyTicks = 20000;  // 200 us of the 100 MHz wall clock
+// The residency bound: a workgroup that has waited this long for the others
+// to arrive decides ABORT.  200 us, in ticks of the device's constant-rate
+// wall clock (s_memrealtime), whose rate the host reads from the device
+// (hipDeviceAttributeWallClockRate) and passes in Launch::residency_ticks.
+constexpr long long kResidencyMicros = 200;
+// Workgroup number and count over the whole grid (1-, 2- or 3-dimensional).
+__device__ inline unsigned flat_block() {
+  return blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+}
+__device__ inline unsigned flat_grid() { return gridDim.x * gridDim.y * gridDim.z; }
 __device__ inline unsigned arrival_group(unsigned grid) {
   const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
-  return blockIdx.x % ng;
+  return flat_block() % ng;
 }
 __device__ inline unsigned arrive(unsigned* status) {
-  unsigned* ctr = status + kArriveStride * (1 + arrival_group(gridDim.x));
+  unsigned* ctr = status + kArriveStride * (1 + arrival_group(flat_grid()));
   return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 }
 // Lane 0 of the calling wave decides; the decision is returned to every lane.
-__device__ inline unsigned decide(unsigned* status, unsigned arrived) {
+// An ABORT is also recorded as fallback_bit in the call's flags (err).
+__device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* err, unsigned fallback_bit,
+                                  long long ticks) {
   unsigned s = 0u;
   if ((threadIdx.x & 63) == 0) {
     unsigned* groups = status + 1;
     unsigned* state = status + 2;
-    const unsigned grid = gridDim.x;
+    const unsigned grid = flat_grid();
     const unsigned ng = grid < (unsigned)kArriveGroups ? grid : (unsigned)kArriveGroups;
     const unsigned g = arrival_group(grid);
     const unsigned members = (grid - g + ng - 1) / ng;
@@ -208,13 +231,14 @@ __device__ inline unsigned decide(unsigned* status, unsigned arrived) {
     }
     const long long t0 = wall_clock64();
     while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-      if (wall_clock64() - t0 > kResidencyTicks) {
+      if (wall_clock64() - t0 > ticks) {
         unsigned expect = 0u;
         __hip_atomic_compare_exchange_strong(state, &expect, kFusedAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
       }
       __builtin_amdgcn_s_sleep(2);
     }
+    if (s == kFusedAbort) raise_error(err, fallback_bit);
   }
   return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
 }
@@ -241,11 +265,19 @@ hipError_t launch_zero(const ZeroRanges& r, hipStream_t st);
 // Validating mode: sets kErrNonFinite in *err if any of the n 16-byte units
 // at p holds a non-finite value of the element type (dtype 1: bf16, 0: fp32).
 hipError_t launch_check_finite(const void* p, long long n16, int dtype, unsigned* err, hipStream_t st);
+// The same for n float32 values (any count, 4-byte alignment).
+hipError_t launch_check_finite_f32(const float* p, long long n, unsigned* err, hipStream_t st);
 // Refresh selection: turn the selection's relative entries into final
 // indices (protected head first) and gather token ids with them.
 hipError_t launch_refresh_finish(int rows, int n, int keep, int head, int tail, bool picked, int32_t* indices,
                                  const int32_t* tokens, int32_t* tokens_out, hipStream_t st);
 int gather_rows_per_block(int D, int dtype);
+
+// Streaming-read probes (kvsel_probe.hip): mode 0, 1, 2 direct-to-LDS tiles
+// (8 waves x 1 tile, 8 waves x 2 tiles, 4 waves x 4 tiles in flight; bytes a
+// multiple of 128 KB), mode 3 vector loads; one workgroup per CU (cus).
+int probe_sink_words(int cus);
+hipError_t launch_probe(int mode, const void* src, long long bytes, unsigned* sink, int cus, hipStream_t st);
 
 hipError_t launch_gather(const Launch& a, int items, int dtype, const void* K, const void* V,
                          const int32_t* indices, void* K_out, void* V_out, hipStream_t st);

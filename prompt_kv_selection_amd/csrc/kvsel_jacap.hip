@@ -172,6 +172,14 @@ __global__ __launch_bounds__(kJThreads) void jacap_weights_kernel(const JacapArg
       if (!(isfinite(m) && isfinite(s) && s >= 0.f)) raise_error(j.err, kErrNonFinite);
     }
   }
+  // The second moment is a variance-like diagonal: a negative (or NaN)
+  // entry would make weights and scores negative and rank them wrongly.
+  // Checked once per head; the later kernels run regardless.
+  if (c == 0 && tid < 64) {
+    bool bad = false;
+    for (int d = tid; d < D; d += 64) bad = bad || !(j.lambda[(long long)head * D + d] >= 0.f);
+    if (__ballot(bad) != 0 && tid == 0) raise_error(j.err, kErrDomain);
+  }
   __syncthreads();
   const float M = s_m, s1 = s_z, iz = 1.f / (1.f + s1), invd = 1.f / (float)D;
   const int t0 = c * kJChunk, t1 = min(t0 + kJChunk, j.N);

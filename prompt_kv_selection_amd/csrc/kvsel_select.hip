@@ -14,7 +14,7 @@
 //    position.
 //
 // Top-k.  Pooled scores are finite and >= 0, so their float32 bit patterns
-// order like the values.  A most-significant-first radix select (digits of
+// order like the values (-0 is read as +0).  A most-significant-first radix select (digits of
 // 11, 11 and 10 bits) finds the threshold pattern tau of the (C-W)-th largest
 // score and how many tau-equal positions are still needed.  The first digit's
 // histogram is built by the pooling kernel across many workgroups.  A
@@ -42,6 +42,11 @@
 #endif
 
 namespace kvsel {
+
+// Radix key of a score word.  Scores are >= 0, so the bit patterns order like
+// the values, except that -0 (sign bit alone) would rank above every positive
+// score: it is taken as +0, which it equals.
+__device__ __forceinline__ uint32_t score_key(uint32_t bits) { return bits == 0x80000000u ? 0u : bits; }
 
 // Inclusive scan over the NT threads of the block; `total` gets the sum.
 template <int NT>
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(const Launch a
 #pragma unroll
   for (int u = 0; u < kCandPer; ++u) {
     const int j = j0 + u * kCandThreads + tid;
-    kk[u] = j < end ? key[j] : 0u;
+    kk[u] = j < end ? score_key(key[j]) : 0u;
   }
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t sh[8];
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(const Launch a
 #pragma unroll
       for (int u = 0; u < kCandPer; ++u) {
         const int j = jb + u * kCandThreads + tid;
-        kk[u] = j < end ? key[j] : 0u;
+        kk[u] = j < end ? score_key(key[j]) : 0u;
       }
     }
     // Count, scan the per-wave counts, then write at the scanned offsets.
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
 #pragma unroll
   for (int u = 0; u < kEmitPer; ++u) {
     const int j = seg * segsz + u * kEmitThreads + tid;
-    first[u] = j < end ? key[j] : 0u;
+    first[u] = j < end ? score_key(key[j]) : 0u;
   }
   // Picks above tau and tau-equal positions in the segments before this one
   // (exclusive prefixes written by the threshold kernel).
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kEmitThreads) void emit_kernel(const Launch a, cons
     for (int u = 0; u < kEmitPer; ++u) {
       const int i = u * kEmitThreads + tid;
       const int j = j0 + i;
-      const uint32_t v = j0 == seg * segsz ? first[u] : (j < end ? key[j] : 0u);
+      const uint32_t v = j0 == seg * segsz ? first[u] : (j < end ? score_key(key[j]) : 0u);
       stage[(i / kEmitPer) * (kEmitPer + 1) + i % kEmitPer] = v;
     }
     __syncthreads();
@@ -576,7 +581,7 @@ __global__ __launch_bounds__(kPoolBlock) void pool_hist_kernel(const Launch a, c
       }
     }
     res_out[i0 + u] = res;
-    const uint32_t bin = __float_as_uint(res) >> 21;
+    const uint32_t bin = score_key(__float_as_uint(res)) >> 21;
     if (bin != run_bin) {
       if (run_len && ghist != nullptr) atomicAdd(&hist[run_bin], run_len);
       run_bin = bin;
@@ -671,7 +676,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(const Launch a
 #pragma unroll
   for (int u = 0; u < kSelCols; ++u) {
     const int j = u * kSelThreads + tid;
-    key[u] = j < P ? kr[j] : 0u;
+    key[u] = j < P ? score_key(kr[j]) : 0u;
   }
   const uint32_t* gh = ghist + (long long)row * 2048;
   for (int d = tid; d < 2048; d += kSelThreads) hist[d] = gh[d];
@@ -918,7 +923,7 @@ __device__ __forceinline__ void coop_keys(const float* __restrict__ v, int P, in
 #pragma unroll
     for (int q = 0; q < KW - 1; ++q) w[q] = w[q + 1];
     w[KW - 1] = sv[at(i0 + u + r)];
-    key[u] = j0 + i0 + u < P ? __float_as_uint(pool_window<KW, MAX>(w)) : 0u;
+    key[u] = j0 + i0 + u < P ? score_key(__float_as_uint(pool_window<KW, MAX>(w))) : 0u;
   }
 }
 
@@ -1067,7 +1072,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     coop_copy_rows<RU>(m0, n, first, sel, in_row0, out_row0, K, V, Ko, Vo);
   };
   if (s.L < s.C) {  // bypass: every position, segment by segment
-    if (tid == 0) s_go = decide(status, arrived);
+    if (tid == 0) s_go = decide(status, arrived, a.err, kFlagSelectFallback, a.residency_ticks);
     __syncthreads();
     const bool go = s_go == kFusedGo;
     if (!go && seg != 0) return;
@@ -1096,7 +1101,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     coop_keys<KW, MAX>(v, P, seg, sv, key);
     coop_local_hist(key, valid_of(seg), 21, 11, 0u, true, hist);
   }
-  if (tid == 0) s_go = decide(status, arrived);
+  if (tid == 0) s_go = decide(status, arrived, a.err, kFlagSelectFallback, a.residency_ticks);
   __syncthreads();
   const bool go = s_go == kFusedGo;
   KVSEL_SELROWS_MARK(1);

@@ -226,3 +226,21 @@ def test_jacap_concurrent_calls_on_two_streams(B):
         assert torch.equal(o["idx"], a["idx"])
         assert torch.equal(bits(o["r"]), bits(a["r"]))
         assert torch.equal(bits(o["Ko"]), bits(a["Ko"]))
+
+
+def test_negative_second_moment_is_reported(B):
+    """lambda_q is a diagonal second moment (>= 0).  A negative entry would
+    make weights and scores negative and rank them wrongly: the call still
+    completes, and the status names the input as out of its domain."""
+    H, N, D = 2, 3000, 128
+    K, V, U, mu, lam = WL.jacap_arrays(5, H, N, D, 1.0, False)
+    out = run(B, K, V, U, mu, lam, 10.0, 600, 4, 32)
+    assert out["status"] == B.KVSEL_OK, B.kvsel_last_error()
+    lam = lam.copy()
+    lam[1, 77] = -0.5
+    log("jacap: negative lambda entry")
+    out = run(B, K, V, U, mu, lam, 10.0, 600, 4, 32)
+    assert out["status"] == B.KVSEL_EINVAL, B.kvsel_last_error()
+    assert "lambda_q" in B.kvsel_last_error()
+    idx = out["idx"].cpu().numpy()
+    assert np.all((idx >= 0) & (idx < N))

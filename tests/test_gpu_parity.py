@@ -242,6 +242,26 @@ def test_topk_step_exact(B, rows, n, count):
         assert np.all(got[r, count:] == -1)
 
 
+@pytest.mark.parametrize("rows,n,count", [(3, 1000, 17), (2, 40000, 4000), (2, 9000, 8990)])
+def test_topk_negative_zero_ranks_as_zero(B, rows, n, count):
+    """-0.0 equals +0.0: a score row holding both ranks them as one tie class
+    (lowest index first), never -0.0 above the positive scores."""
+    rng = np.random.default_rng(n + 3 * count)
+    s = (rng.integers(0, 8, size=(rows, n)) * 0.25).astype(np.float32)
+    zero = s == 0.0
+    s[zero & (rng.random((rows, n)) < 0.5)] = np.float32(-0.0)
+    assert np.signbit(s).any()
+    sd = torch.from_numpy(s).cuda()
+    out = torch.full((rows, count), -1, dtype=torch.int32, device="cuda")
+    log(f"topk with -0.0 rows={rows} n={n} count={count}")
+    ws = torch.empty(B.kvsel_topk_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+    B.kvsel_topk(sd, rows, n, count, out, count, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], O.top_prefix(s[r].astype(np.float64), count))
+
+
 @pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9, 11, 13, 31])
 @pytest.mark.parametrize("pooling", ["avg", "max"])
 def test_pool_step(B, kernel, pooling):

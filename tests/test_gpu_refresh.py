@@ -60,3 +60,24 @@ def test_refresh_matches_oracle(B, case):
     assert torch.equal(bits(Ko), bits(torch.gather(K, 1, gi[:, :, None].expand(rows, keep, D))))
     assert torch.equal(bits(Vo), bits(torch.gather(V, 1, gi[:, :, None].expand(rows, keep, D))))
     assert torch.equal(to, torch.gather(tokens, 1, gi))
+
+
+def test_refresh_negative_zero_scores(B):
+    """-0.0 scores rank with the +0.0 ones (the oracle compares values)."""
+    rows, n, keep, head, tail, D = 2, 6000, 1500, 4, 64, 128
+    rng = np.random.default_rng(11)
+    scores = (rng.integers(0, 6, size=(rows, n)) / 4.0).astype(np.float32)
+    scores[(scores == 0.0) & (rng.random((rows, n)) < 0.5)] = np.float32(-0.0)
+    K = torch.randn((rows, n, D), dtype=torch.float32).to(torch.bfloat16).cuda()
+    V = torch.randn((rows, n, D), dtype=torch.float32).to(torch.bfloat16).cuda()
+    idx = torch.full((rows, keep), -1, dtype=torch.int32, device="cuda")
+    Ko = torch.zeros((rows, keep, D), dtype=torch.bfloat16, device="cuda")
+    Vo = torch.zeros_like(Ko)
+    ws = torch.empty(B.kvsel_refresh_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+    log("refresh with -0.0 scores")
+    B.kvsel_refresh(torch.from_numpy(scores).cuda(), rows, n, keep, head, tail, K, V, D, torch.bfloat16, None, idx,
+                    Ko, Vo, None, ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], O.refresh_select(scores[r].astype(np.float64), keep, head, tail))

@@ -114,3 +114,21 @@ def test_status_nonfinite_lse(B, scoring):
     log(f"status: infinite lse, scoring={scoring}")
     rc, _ = call(B, Qd, Kd, Vd, w, lse=lse, scoring=scoring)
     assert rc == B.KVSEL_ENONFINITE, B.kvsel_last_error()
+
+
+@pytest.mark.parametrize("H,W", [(1, 2), (3, 5), (2, 32)])
+def test_validating_mode_checks_every_lse(B, H, W):
+    """The validating scan reads every handed-over log-sum-exp, including a
+    tail that is not a whole 16-byte unit (heads * W not a multiple of 4)."""
+    w = WL.Workload("status_lse", seed=21, heads=H, L=3000, W=W, C=400, D=128, dtype="bf16", kernel=3,
+                    pooling="avg", keys="normal")
+    Q, K, V = WL.layer_arrays(w)
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    lse = torch.full((H, W), 12.0, dtype=torch.float32, device="cuda")
+    log(f"status: validating mode, finite lse H={H} W={W}")
+    rc, _ = call(B, Qd, Kd, Vd, w, lse=lse, validate=True)
+    assert rc == B.KVSEL_OK, B.kvsel_last_error()
+    lse[H - 1, W - 1] = math.nan  # the very last element
+    log(f"status: validating mode, NaN in the last lse H={H} W={W}")
+    rc, _ = call(B, Qd, Kd, Vd, w, lse=lse, validate=True)
+    assert rc == B.KVSEL_ENONFINITE, B.kvsel_last_error()

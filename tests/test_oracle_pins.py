@@ -299,6 +299,31 @@ def test_expanded_cache_ratio_page_example():
     assert O.expanded_cache_ratio(8, 8, 16384, 1024, 512) == pytest.approx(1 / 11, rel=1e-15)
 
 
+@pytest.mark.parametrize("L,C", [(40, 60), (40, 40), (40, 39), (40, 9), (9, 9)])
+def test_cache_ledger_after_decode(L, C):
+    """The compressed cache serves decode: after the prefill selection a head
+    holds min(L, C) prompt rows (all L when the prompt is shorter than the
+    budget), and g generated tokens are appended to it, so the ledger reads
+    min(L, C) + g rows; a refresh that keeps J of those J + g rows returns it
+    to J (SnapKV page, section "prefill still reads the full K/V; the
+    compressed cache serves decode"; counter-causal page, the refresh loop).
+    The expanded GQA ledger counts the same rows per query head."""
+    rng = np.random.default_rng(L * 100 + C)
+    W, D = 8, 4
+    q, k, v = (rng.standard_normal((n, D)) for n in (W, L, L))
+    out = O.snapkv_select(q, k, v, W, C, 3, "avg")
+    kept = len(out["indices"])
+    assert kept == min(L, C) and len(out["keys"]) == kept and len(out["values"]) == kept
+    for g in (0, 1, 7, 64):
+        rows = kept + g                       # decode appends one row per generated token
+        assert rows == min(L, C) + g
+        scores = rng.random(rows)
+        J = kept
+        after = O.refresh_select(scores, J, min(2, J), 0)
+        assert len(after) == J                # a refresh returns the cache to J rows
+        assert O.expanded_cache_ratio(32, 8, L, C, g) == pytest.approx(32 * rows / (8 * (L + g)), rel=1e-15)
+
+
 # ------------------------------------------------------------- refresh selection
 
 @pytest.mark.parametrize("seed", range(6))
