@@ -285,6 +285,28 @@ int kvsel_select_varlen_lse(const void* Qwin, const void* K, const void* V, cons
                             float* votes_opt, float* pooled_opt,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvsel_select_noalloc: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and kernels are those of kvsel_select,
+ * without the workspace: the call uses a device array of the library,
+ * KVSEL_NOALLOC_SCRATCH_BYTES bytes on every GPU it runs on, allocated with
+ * the library's code object and held until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree, event or library allocation).
+ * The caller still owns every input and output.
+ *   Errors: those of kvsel_select, and KVSEL_EWORKSPACE when the shape needs
+ *   more scratch than the array holds (kvsel_workspace_bytes() of the shape
+ *   must not exceed KVSEL_NOALLOC_SCRATCH_BYTES; 32 heads of L = 32768 at
+ *   W = 32, C = 1024, D = 128 fit).
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents (each call clears what must start at zero): calls that overlap
+ *   on one GPU (other streams, other threads) race and must be serialised by
+ *   the caller.  The device-side flags that kvsel_status reads for a
+ *   workspace are kept in the array and are not readable through the ABI. */
+#define KVSEL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int kvsel_select_noalloc(const void* Qwin, const void* K, const void* V, int L, int W, int C, int D, int heads,
+                         int kernel, int pooling, int dtype, int32_t* indices, void* K_out, void* V_out,
+                         float* row_stats_opt, float* votes_opt, float* pooled_opt, void* stream);
+
 /* Steps of the selection as separate entry points (same definitions as
  * above), for callers that bring their own scores or indices.
  *

@@ -73,6 +73,10 @@ lib.kvsel_gqa_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 lib.kvsel_select_gqa.restype = _i
 lib.kvsel_select_gqa.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.kvsel_select_noalloc.restype = _i
+lib.kvsel_select_noalloc.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+KVSEL_NOALLOC_SCRATCH_BYTES = 32 << 20
 lib.kvsel_topk_workspace_bytes.restype = _sz
 lib.kvsel_topk_workspace_bytes.argtypes = [_i, _i]
 lib.kvsel_topk.restype = _i
@@ -187,6 +191,16 @@ def kvsel_select(Qwin, K, V, L, W, C, D, heads, kernel, pooling, dtype, indices,
                             POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
                             _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(row_stats), _ptr(votes),
                             _ptr(pooled), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvsel_select_noalloc(Qwin, K, V, L, W, C, D, heads, kernel, pooling, dtype, indices, K_out, V_out,
+                         row_stats=None, votes=None, pooled=None, stream=None) -> None:
+    """kvsel_select without a workspace: the library's per-device scratch
+    array serves instead (calls on one GPU must not overlap)."""
+    _check(lib.kvsel_select_noalloc(_ptr(Qwin), _ptr(K), _ptr(V), L, W, C, D, heads, kernel,
+                                    POOL.get(pooling, pooling), DTYPE.get(dtype, dtype),
+                                    _ptr(indices), _ptr(K_out), _ptr(V_out), _ptr(row_stats), _ptr(votes),
+                                    _ptr(pooled), _stream(stream)))
 
 
 def kvsel_select_varlen(Qwin, K, V, cu_L, C, W, D, heads, kernel, pooling, dtype, indices, K_out, V_out,

@@ -26,6 +26,15 @@
 
 using namespace kvsel;
 
+// Workspace of the allocation-free entry point (kvsel_select_noalloc): a
+// device array of the library, of which every GPU the library runs on holds
+// its own copy, allocated with the code object and kept until the process
+// ends.  In host code its name is only a stand-in, never an address: the
+// device address is taken once per device with hipGetSymbolAddress and that
+// address is what every launch receives.
+constexpr size_t kScratchBytes = KVSEL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_error;
@@ -227,8 +236,12 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<TimedLaunch> g_prof;
 
+// Set for the duration of an allocation-free call: no events are created.
+thread_local bool g_no_events = false;
+
 template <typename F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  if (g_no_events) return launch();
   bool on;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -479,6 +492,39 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   }
   return ok();
 }
+
+// ---- allocation-free selection (kvsel_select_noalloc): the per-device
+// scratch address (the array is declared at file scope above).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's scratch address, looked up on the first call made on
+// that device.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(KVSEL_EUNSUPPORTED, "device ordinal %d exceeds the %d devices the scratch table holds", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_error(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || (uintptr_t)p % 256 != 0)
+      return fail(KVSEL_EDEVICE, "scratch array at an unusable address %p", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVSEL_OK;
+}
+
+struct NoEvents {
+  NoEvents() { g_no_events = true; }
+  ~NoEvents() { g_no_events = false; }
+};
 
 }  // namespace
 
@@ -1013,6 +1059,29 @@ int kvsel_profile_read(kvsel_kernel_time* out, int max_entries) {
   for (int i = 0; i < (int)acc.size() && i < max_entries && out; ++i) out[i] = acc[i];
   ok();
   return (int)acc.size();
+}
+
+int kvsel_select_noalloc(const void* Qwin, const void* K, const void* V, int L, int W, int C, int D, int heads,
+                         int kernel, int pooling, int dtype, int32_t* indices, void* K_out, void* V_out,
+                         float* row_stats_opt, float* votes_opt, float* pooled_opt, void* stream) {
+  const int32_t cu[2] = {0, L};
+  const int32_t c[1] = {C};
+  {
+    Plan p;
+    const int rc = make_plan(cu, c, 1, heads, W, D, dtype, p);
+    if (rc) return rc;
+    if (p.bytes > kScratchBytes)
+      return fail(KVSEL_EWORKSPACE,
+                  "kvsel_select_noalloc: this shape needs %zu bytes of scratch, more than the %zu bytes the "
+                  "library holds per device; call kvsel_select with a workspace instead",
+                  p.bytes, kScratchBytes);
+  }
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  NoEvents guard;
+  return kvsel_select(Qwin, K, V, L, W, C, D, heads, kernel, pooling, dtype, indices, K_out, V_out, row_stats_opt,
+                      votes_opt, pooled_opt, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"
