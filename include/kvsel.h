@@ -104,8 +104,21 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  * KVSEL_OPT_VALIDATE: 1 makes every selection call first scan its Qwin, K
  *   and V (and row_lse) for non-finite values (two extra reads of K and V);
  *   0 (default) off.
+ * KVSEL_OPT_FUSED_SELECT: 1 runs the selection (pooling, top-k, window,
+ *   K/V copy) inside the single-read scoring kernel, behind the streaming of
+ *   later rounds, for calls where the single-read kernel runs, every head has
+ *   its own K/V head, the pooling width is at most 7, no prompt is shorter
+ *   than its budget and a workgroup owns at most 2048 chunks; such calls
+ *   launch one kernel.  0 (default) runs the selection as separate launches,
+ *   which is faster on MI355X today: the selection's end phase waits on
+ *   device-scope round trips that the separate kernels avoid.  The indices
+ *   and K/V rows are identical either way.  The fused kernel needs the same
+ *   residency; when its workgroups are not all resident it takes work from
+ *   counters instead (statistics and votes per chunk, two passes over K, then
+ *   each row's selection in one workgroup).  KVSEL_OPT_FORCE_FALLBACK forces
+ *   that too.
  * Not thread-safe with respect to concurrent calls. */
-enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1, KVSEL_OPT_VALIDATE = 2 };
+enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1, KVSEL_OPT_VALIDATE = 2, KVSEL_OPT_FUSED_SELECT = 3 };
 enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };
 int kvsel_set_option(int option, int value);
 int kvsel_get_option(int option);
@@ -164,7 +177,8 @@ int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned*
  * (row_lse given); BYPASS (a prompt shorter than its budget); selection:
  * SELECT_COOP (one cooperative launch: pooling, top-k, picks and the K/V
  * copy), SELECT_ROWS (a workgroup per row, then the gather), SELECT_SEGMENTS
- * (the segment-parallel chain).  0 before the first call. */
+ * (the segment-parallel chain), SELECT_FUSED (the selection inside the
+ * single-read scoring kernel).  0 before the first call. */
 #define KVSEL_PATH_SINGLE_READ 0x1u
 #define KVSEL_PATH_TWO_PASS 0x2u
 #define KVSEL_PATH_VOTES_ONLY 0x4u
@@ -173,6 +187,7 @@ int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned*
 #define KVSEL_PATH_SELECT_COOP 0x20u
 #define KVSEL_PATH_SELECT_ROWS 0x40u
 #define KVSEL_PATH_SELECT_SEGMENTS 0x80u
+#define KVSEL_PATH_SELECT_FUSED 0x100u
 unsigned kvsel_last_path(void);
 
 /* Workspace bytes kvsel_select needs for these sizes; 0 if the arguments are

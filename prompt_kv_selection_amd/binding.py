@@ -47,7 +47,7 @@ lib.kvsel_last_path.argtypes = []
 FLAG = {"exchange_wait": 0x1, "lds_wait": 0x2, "select_wait": 0x4, "nonfinite": 0x8, "domain": 0x10,
         "scoring_fallback": 0x100, "select_fallback": 0x200}
 PATH = {"single_read": 0x1, "two_pass": 0x2, "votes_only": 0x4, "handed_over": 0x8, "bypass": 0x10,
-        "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80}
+        "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80, "select_fused": 0x100}
 lib.kvsel_probe_sink_bytes.restype = _sz
 lib.kvsel_probe_sink_bytes.argtypes = []
 lib.kvsel_probe_stream.restype = _i
@@ -360,6 +360,7 @@ def kvsel_profile_read() -> dict:
 KVSEL_OPT_SCORING = 0
 KVSEL_OPT_FORCE_FALLBACK = 1
 KVSEL_OPT_VALIDATE = 2
+KVSEL_OPT_FUSED_SELECT = 3
 SCORING = {"auto": 0, "two_pass": 1, "single_read": 2}
 lib.kvsel_set_option.restype = _i
 lib.kvsel_set_option.argtypes = [_i, _i]

@@ -16,8 +16,12 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kvsel.h"
@@ -94,6 +98,9 @@ struct Plan {
   long long vote_elems = 0;   // heads * sum of P_b
   size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_cut = 0, off_segcnt = 0, off_ctr = 0,
          off_status = 0, off_hist = 0, off_coop = 0, bytes = 0;
+  // The selection fused into the single-read scoring kernel.
+  size_t off_cw = 0, off_halo = 0, off_flags = 0, off_cslot = 0, off_fslot = 0, off_rowfb = 0, off_cand = 0,
+         off_kslot = 0;
 };
 
 // The workspace starts with a 256-byte header; word 0 holds the error flags
@@ -111,6 +118,51 @@ thread_local unsigned g_last_path = 0u;
 int g_scoring = KVSEL_SCORING_AUTO;
 int g_force_fallback = 0;
 int g_validate = 0;
+int g_fused_select = 0;
+
+// Per-call tokens of the fused selection: the arrival and decision words and
+// the tagged flag word carry them, so nothing has to be cleared before a
+// call.  Bits 2..31 count calls (never 0), bits 32..63 are random per process.
+unsigned long long next_token() {
+  static std::atomic<unsigned long long> calls{0};
+  static const unsigned long long salt = [] {
+    std::random_device rd;
+    return ((unsigned long long)rd() ^ (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count()) &
+           0xFFFFFFFFull;
+  }();
+  unsigned long long n = (++calls) & 0x3FFFFFFFull;
+  if (n == 0) n = 1;
+  return (salt << 32) | (n << 2);
+}
+
+// What the last selection call on a workspace left in its header: whether
+// the call cleared word 0 (then word 0 holds its flags) and its token (the
+// tagged word holds its flags when the tags match).
+struct LastCall {
+  bool cleared = false;
+  unsigned long long token = 0;
+};
+std::mutex g_calls_mu;
+std::unordered_map<const void*, LastCall> g_calls;
+
+void record_call(const void* ws, bool cleared, unsigned long long token) {
+  std::lock_guard<std::mutex> lk(g_calls_mu);
+  g_calls[ws] = LastCall{cleared, token};
+}
+
+// The last call's flags from the header words (word 0, the tagged word).
+unsigned last_call_flags(const void* ws, unsigned w0, unsigned long long tagged) {
+  LastCall c;
+  {
+    std::lock_guard<std::mutex> lk(g_calls_mu);
+    auto it = g_calls.find(ws);
+    if (it == g_calls.end()) return w0;  // not a selection call of this process: word 0 as written
+    c = it->second;
+  }
+  unsigned f = c.cleared ? w0 : 0u;
+  if (c.token != 0 && (tagged >> 24) == token_tag(c.token)) f |= (unsigned)(tagged & 0xFFFFFFull);
+  return f;
+}
 
 int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int W, int D, int dtype, Plan& p,
               int kv_heads = 0) {
@@ -183,6 +235,28 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   p.off_coop = off;  // cooperative selection: status per launch group, then per-row words
   off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned) +
                  (size_t)B * heads * coop_row_words() * sizeof(unsigned));
+  // Fused selection (single-read shapes only): per exchange slot a count
+  // word and the halo words; per launch group the arrival tokens, decision
+  // and claim counters; per exchange slot the chunk's histograms; per row two
+  // completion counters; the candidates, laid out like the votes; per
+  // exchange slot the chunk's pooled scores.
+  const bool fused_words = p.fS > 0;
+  p.off_cw = off;
+  off = align256(off + (fused_words ? (size_t)p.fpart[B] * 8 : 0));
+  p.off_halo = off;
+  off = align256(off + (fused_words ? (size_t)p.fpart[B] * kHaloWords * 8 : 0));
+  p.off_cslot = off;  // per exchange slot the chunk's coarse and fine histograms
+  off = align256(off + (fused_words ? (size_t)p.fpart[B] * 64 * 4 : 0));
+  p.off_fslot = off;
+  off = align256(off + (fused_words ? (size_t)p.fpart[B] * 32 * 4 : 0));
+  p.off_flags = off;  // (the count, halo and histogram words above form one range the kernel clears)
+  off = align256(off + (fused_words ? (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedFlagWords * 8 : 0));
+  p.off_rowfb = off;
+  off = align256(off + (fused_words ? (size_t)B * heads * 2 * 8 : 0));
+  p.off_cand = off;
+  off = align256(off + (fused_words ? (size_t)p.vote_elems * 8 : 0));
+  p.off_kslot = off;  // per exchange slot the chunk's pooled scores
+  off = align256(off + (fused_words ? (size_t)p.fpart[B] * p.fS * 4 : 0));
   p.bytes = off;
   return KVSEL_OK;
 }
@@ -311,9 +385,36 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   // one launch, a workgroup per segment of a row) where its grid fits the
   // device at once.
   const int coop_cap = (kernel == 1 || kernel == 3 || kernel == 5 || kernel == 7) ? coop_grid_capacity(p.D, p.dtype) : 0;
-  std::vector<int> coop_segs((p.B + kMaxSegs - 1) / kMaxSegs, 0);
+  const int ngroups = (p.B + kMaxSegs - 1) / kMaxSegs;
+  // The selection fused into the single-read scoring kernel, per launch
+  // group: pooling widths up to 7, one query head per K/V head, and no
+  // sequence shorter than its budget in the group.
+  std::vector<char> fsel(ngroups, 0);
+  bool any_fsel = false, any_old = false;
+  for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
+    bool ok = use_fused && g_fused_select && fused_select_kernel_ok(kernel) && p.group == 1;
+    for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b) ok = p.L[b] >= p.C[b];
+    {
+      // Rounds of the launch group (as the launch below counts them).
+      long long rounds = 0;
+      const int grid = use_fused ? fused_grid(p.W, p.D) : 0;
+      for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b) {
+        const int fhpr = (p.fc[b] > 0 && grid > 0) ? std::min(p.heads, grid / p.fc[b]) : 0;
+        rounds += fhpr > 0 ? (p.heads + fhpr - 1) / fhpr : 0;
+      }
+      ok = ok && rounds <= kFusedMaxRounds;
+      // The end phase takes a row's chunks two groups of 64 at a time.
+      for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b)
+        ok = (p.L[b] - p.W + p.fS - 1) / p.fS <= 128;
+    }
+    fsel[gi] = ok;
+    any_fsel = any_fsel || ok;
+    any_old = any_old || !ok;
+  }
+  std::vector<int> coop_segs(ngroups, 0);
   bool any_coop = false;
   for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
+    if (fsel[gi]) continue;
     const int nb = std::min(kMaxSegs, p.B - b0);
     int segs = 1;
     for (int b = b0; b < b0 + nb; ++b) {
@@ -326,7 +427,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     }
   }
   bool all_coop = true;
-  for (int gsegs : coop_segs) all_coop = all_coop && gsegs > 0;
+  for (int gi = 0; gi < ngroups; ++gi) all_coop = all_coop && (fsel[gi] || coop_segs[gi] > 0);
   unsigned* err = (unsigned*)ws;  // the header's error word
   {
     unsigned path = 0u;
@@ -337,9 +438,15 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       if (p.L[b] < p.C[b]) path |= KVSEL_PATH_BYPASS;
     if (any_coop) path |= KVSEL_PATH_SELECT_COOP;
     if (!all_coop) path |= whole_rows ? KVSEL_PATH_SELECT_ROWS : KVSEL_PATH_SELECT_SEGMENTS;
+    if (any_fsel) path |= KVSEL_PATH_SELECT_FUSED;
     g_last_path = path;
   }
-  {
+  // Calls made only of fused-selection groups clear nothing before they
+  // start: their kernels clear what they own and carry a token.
+  const bool fill = any_old || g_validate;
+  const unsigned long long token = any_fsel ? next_token() : 0ull;
+  record_call(ws, fill, token);
+  if (fill) {
     // The header, and the exchange records, status words, histograms and
     // the cooperative selection's words that are in use, start at zero (on
     // the two-pass path without the cooperative selection the statistics
@@ -419,15 +526,43 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     uint32_t* gcut = (uint32_t*)((char*)cut + (size_t)b0 * p.heads * kCutBytes);
     uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
+    FusedSel sel{};
+    if (fsel[b0 / kMaxSegs]) {
+      sel.on = 1;
+      sel.force_abort = g_force_fallback;
+      sel.token = token;
+      sel.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
+      sel.flags = (unsigned long long*)(ws + p.off_flags) + (long long)kFusedFlagWords * (b0 / kMaxSegs);
+      sel.cw = (unsigned long long*)(ws + p.off_cw);
+      sel.halo = (unsigned long long*)(ws + p.off_halo);
+      sel.cslot = (unsigned*)(ws + p.off_cslot);
+      sel.fslot = (unsigned*)(ws + p.off_fslot);
+      // Cleared by the kernel's workgroups, a share each: the exchange slots
+      // (not read with handed-over statistics), then the count, halo and
+      // histogram words (contiguous).
+      sel.clr[0] = lse == nullptr ? (unsigned long long*)(ws + p.off_ctr) : nullptr;
+      sel.clr_words[0] = lse == nullptr ? (long long)(p.off_status - p.off_ctr) / 8 : 0;
+      sel.clr[1] = (unsigned long long*)(ws + p.off_cw);
+      sel.clr_words[1] = (long long)(p.off_flags - p.off_cw) / 8;
+      sel.rowfb = (unsigned long long*)(ws + p.off_rowfb) + (long long)b0 * p.heads * 2;
+      sel.cand = (unsigned long long*)(ws + p.off_cand);
+      sel.pooled = pooled_opt;
+      sel.kslot = (float*)(ws + p.off_kslot);
+      sel.indices = indices;
+      sel.V = V;
+      sel.K_out = K_out;
+      sel.V_out = V_out;
+    }
     if (items > 0 && use_fused) {
       unsigned* gstatus = status + (long long)kFusedStatusWords * (b0 / kMaxSegs);
-      if (g_force_fallback && lse == nullptr) {
+      if (g_force_fallback && lse == nullptr && !sel.on) {
         e = launch_fill_u32(gstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
         if (e != hipSuccess) return device_error(e, "fill launch");
       }
       e = timed("window_fused", st,
-                [&] { return launch_fused_scoring(a, Q, K, lse, counters, gstatus, votes, row_stats, st); });
+                [&] { return launch_fused_scoring(a, Q, K, lse, counters, gstatus, votes, row_stats, sel, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
+      if (sel.on) continue;  // the selection ran in the same kernel
     } else if (items > 0 && lse != nullptr) {
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, lse, votes, nullptr, st); });
@@ -549,6 +684,11 @@ int kvsel_set_option(int option, int value) {
     g_validate = value;
     return ok();
   }
+  if (option == KVSEL_OPT_FUSED_SELECT) {
+    if (value != 0 && value != 1) return fail(KVSEL_EINVAL, "invalid fused-select value %d", value);
+    g_fused_select = value;
+    return ok();
+  }
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
@@ -556,6 +696,7 @@ int kvsel_get_option(int option) {
   if (option == KVSEL_OPT_SCORING) return g_scoring;
   if (option == KVSEL_OPT_FORCE_FALLBACK) return g_force_fallback;
   if (option == KVSEL_OPT_VALIDATE) return g_validate;
+  if (option == KVSEL_OPT_FUSED_SELECT) return g_fused_select;
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
@@ -564,11 +705,13 @@ const char* kvsel_last_error(void) { return g_error.c_str(); }
 int kvsel_status(const void* workspace, void* stream) {
   if (!workspace) return fail(KVSEL_EINVAL, "workspace must not be NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(KVSEL_EINVAL, "workspace must be 256-byte aligned");
-  unsigned flags = 0;
+  unsigned words[4] = {};
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(&flags, workspace, sizeof flags, hipMemcpyDeviceToHost, st);
+  hipError_t e = hipMemcpyAsync(words, workspace, sizeof words, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return device_error(e, "status read");
+  const unsigned flags =
+      last_call_flags(workspace, words[0], ((unsigned long long)words[kTaggedWord + 1] << 32) | words[kTaggedWord]);
   if (flags & (kErrExchangeWait | kErrLdsWait | kErrSelectWait))
     return fail(KVSEL_EDEVICE, "a bounded device-side wait timed out (flags 0x%x): the outputs of that call are "
                                "unreliable", flags);
@@ -593,7 +736,9 @@ int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned*
     if (e == hipSuccess) e = hipStreamSynchronize(st);
   }
   if (e != hipSuccess) return device_error(e, "status read");
-  if (last_flags) *last_flags = words[0];
+  if (last_flags)
+    *last_flags = last_call_flags(workspace, words[0],
+                                  ((unsigned long long)words[kTaggedWord + 1] << 32) | words[kTaggedWord]);
   if (sticky_flags) *sticky_flags = words[kStickyWord];
   return ok();
 }
@@ -966,6 +1111,7 @@ int kvsel_jacap_select(const void* K, const void* V, const void* U, const float*
   j.gpart = (float*)(ws + q.off_gram);
   j.minv = (__bf16*)(ws + q.off_minv);
   j.err = (unsigned*)ws;  // cleared by the first kernel
+  record_call(workspace, true, 0ull);
   j.hist = (uint32_t*)(ws + q.off_sel);  // the selection's histograms, cleared by the weights kernel
   j.hist_words = (long long)heads * 2048;
   hipError_t e = launch_jacap_scores(j, D, K, U, st, [&](const char* name, const std::function<hipError_t()>& f) {

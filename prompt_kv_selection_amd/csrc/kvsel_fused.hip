@@ -52,9 +52,42 @@
 //    waves have their row statistics.
 //  * The memory wave loads Qwin (double buffered in LDS) and writes the
 //    votes.
+//  * The selection wave (when the selection is fused, see below) takes each
+//    round's votes out of LDS, writes them, and selects.
 // All exchange accesses are agent scope (they bypass the per-XCD L2); every
 // wait is bounded, and a timed-out wait records a flag and marks the head's
 // votes NaN, so the grid always drains.
+//
+// Fused selection (web page "SnapKV: selecting the KV cache for long prompts
+// with an observation window", sections "pooling spreads a peak into a
+// neighbourhood preference" and "one full selection computed from Q and K").
+// The chunks of a head are segments of its selection: pooling of width k
+// (odd, at most 7) over the prefix votes with zero padding (avg divides by k)
+// or the in-range maximum; the C - W prefix positions with the highest pooled
+// score, equal scores to the lowest index, ascending, then the W window
+// positions; K and V rows gathered with the same indices.  During the
+// streaming the selection wave takes each round's votes out of LDS, writes
+// them, publishes the chunk's first and last three votes (tagged halo words)
+// and stores the pooled scores of its interior positions as radix keys (float
+// bits: scores are >= 0) in the chunk's key slot; nothing there waits on
+// memory.  After the streaming all waves run the end phase in four steps, each
+// waiting only for the same step of the row's other chunks: the edge
+// positions and a 64-bin coarse histogram per chunk, the fine histogram inside
+// the coarse bin of the threshold tau, the candidates of tau's first digit,
+// and the pick (the rest of tau, then each chunk's picks in index order, the
+// K/V copy and the window).  Every published word carries count + 1, so a
+// written word is never zero and no atomics are needed.  This path is opt-in:
+// its end phase costs more device-scope round trips than the separate
+// selection kernels take in all.
+// Nothing is cleared by a separate launch: before it arrives, each workgroup
+// clears its share of the words the call publishes (exchange slots, halo,
+// histogram, count and flag words), and the arrival and the residency
+// decision carry a per-call token instead of counting from zero.
+// GO therefore also means every shared word is clear.  On ABORT (not all
+// resident) the workgroups take work from token-tagged counters instead: the
+// chunks' statistics, then their votes (two passes over K), then whole rows'
+// selections, each phase waiting only on work already claimed by running
+// workgroups.
 //
 // LDS tiles use an XOR swizzle (piece c of row r stored at c ^ (r % pieces))
 // so that the direct-to-LDS writes stay contiguous and the MFMA operand reads
@@ -86,7 +119,8 @@ constexpr float kNegBig = -1.0e30f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
-constexpr int kThreads = (kSW + 3) * 64;  // plus the exchange, memory and publisher waves
+constexpr int kThreads = (kSW + 4) * 64;  // plus the exchange, memory, publisher and selection waves
+constexpr int kExWave = kSW, kMemWave = kSW + 1, kPubWave = kSW + 2, kSelWave = kSW + 3;
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
 constexpr int kNBuf = 1;                  // K tiles in flight per streaming wave
 constexpr int kS = kSW * kTT * 32;        // positions per workgroup per round
@@ -162,6 +196,28 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo
   m = fmaxf(m, mo);
 }
 
+// A flag of the call: the tagged word when nothing was cleared before the
+// call (fused selection), else the header's flag word.
+__device__ __forceinline__ void flag_error(const Launch& a, const FusedSel& f, unsigned bit) {
+  if (f.on)
+    raise_tagged(f.errw, f.token, bit);
+  else
+    raise_error(a.err, bit);
+}
+
+__device__ __forceinline__ unsigned long long load64(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store64(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned load32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- exchange slots in the workspace, zeroed per call: per (sequence,
 // head, chunk) 32 words of 64 bits, word i = (tagged m_i bits, z_i bits).
 constexpr int kSlotWords = 32;
@@ -183,6 +239,9 @@ struct Sync {
   unsigned v_done;                 // votes of rounds < v_done have left LDS
   unsigned timeout;
   unsigned abort;                  // the grid is not all resident: every wave leaves its loop
+  unsigned issued;                 // the clears of the shared words are issued (fused selection)
+  unsigned zeroed;                 // this workgroup's shared words are clear (fused selection)
+  unsigned go;                     // the residency decision (kFusedGo / kFusedAbort), once taken
 };
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned lds_get(const unsigned* p) {
@@ -521,7 +580,7 @@ __device__ __forceinline__ bool ctl_head_stats(const Launch& a, const Work& w, c
 // buffer, once the votes of round j - kNR, which read the same buffer, are
 // done.  s_ready = j + 1 announces round j.
 template <int D>
-__device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ ex, unsigned* __restrict__ status,
+__device__ __forceinline__ void ctl_exchange(const Launch& a, const FusedSel& f, unsigned long long* __restrict__ ex,
                              float* __restrict__ row_stats, float (*s_m)[32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
@@ -532,8 +591,8 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
     if (w.on) {
       float M, Z;
       const bool ok = ctl_head_stats(a, w, ex, M, Z);
-      if (!ok && lane == 0) raise_error(a.err, kErrExchangeWait);
-      if (__ballot(ok && lane < W && !stats_ok(M, Z)) != 0 && lane == 0) raise_error(a.err, kErrNonFinite);
+      if (!ok && lane == 0) flag_error(a, f, kErrExchangeWait);
+      if (__ballot(ok && lane < W && !stats_ok(M, Z)) != 0 && lane == 0) flag_error(a, f, kErrNonFinite);
       if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
       if (lane < W) {
         s_m[j % kNR][lane] = ok ? M + __log2f(Z) : __builtin_nanf("");
@@ -554,7 +613,8 @@ __device__ void ctl_exchange(const Launch& a, unsigned long long* __restrict__ e
 // Exchange wave with the row statistics given as natural-log log-sum-exps
 // (lse[sequence][head][W]): the base-2 log-normaliser is lse * log2(e).
 // Each round's values are loaded one round ahead.
-__device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*s_m)[32], Sync* sy) {
+__device__ __forceinline__ void ctl_lse(const Launch& a, const FusedSel& f, const float* __restrict__ lse, float (*s_m)[32],
+                        Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   auto load = [&](int r) -> float {
@@ -568,7 +628,7 @@ __device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*
     if (j >= kNR && round_work(a, j - kNR).on) ++votes_due[j % kNR];
     const float cur = next;
     next = load(j + 1);
-    if (__ballot(w.on && lane < W && !isfinite(cur)) != 0 && lane == 0) raise_error(a.err, kErrNonFinite);
+    if (__ballot(w.on && lane < W && !isfinite(cur)) != 0 && lane == 0) flag_error(a, f, kErrNonFinite);
     if (w.on) {
       if (!lds_wait_ge(sy, &sy->cnt_c[j % kNR], kSW * votes_due[j % kNR])) return;
       if (lane < 32) s_m[j % kNR][lane] = lane < W ? cur * kLog2e : INFINITY;  // rows past W drop out
@@ -581,11 +641,14 @@ __device__ void ctl_lse(const Launch& a, const float* __restrict__ lse, float (*
 // round k, merged from the streaming waves' pairs, goes to its slot.  A wave
 // of its own, so that publication never waits behind a Qwin load or a votes
 // write (which waits for the previous exchange).
-__device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex, float (*s_maxp)[kSW * 32],
+__device__ __forceinline__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex, float (*s_maxp)[kSW * 32],
                             float (*s_zp)[kSW * 32], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   unsigned on_b[kNR] = {};  // owned rounds awaited so far, per residue
+  // The slots this workgroup writes are clear: its own clears (separate
+  // selection), or every workgroup's (fused selection: GO).
+  if (!lds_wait_ge(sy, &sy->zeroed, 1u)) return;
   for (int k = 0; k < a.rounds; ++k) {
     const Work w0 = round_work(a, k);
     if (!w0.on) continue;
@@ -619,7 +682,7 @@ __device__ void ctl_publish(const Launch& a, unsigned long long* __restrict__ ex
 // once round k's phase A is done; (2) votes of round k - kLag to memory, then
 // the votes buffer may be reused (v_done).
 template <int D>
-__device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float* __restrict__ votes,
+__device__ __forceinline__ void ctl_memory(const Launch& a, bool write_votes, const __bf16* __restrict__ Q, float* __restrict__ votes,
                            uint4 (*qbufs)[TileGeom<D>::PIECES], float (*s_votes)[kS], Sync* sy) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
@@ -629,9 +692,9 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
   ctl_finish_q<D>(W, qbufs[1]);
   lds_set(&sy->q_ready, 2u);
   unsigned on_b[kNR] = {}, on_c[kNR] = {};  // owned rounds awaited so far, per residue
-  for (int k = 0; k < a.rounds + kLag; ++k) {
+  for (int k = 0; k < a.rounds + (write_votes ? kLag : 0); ++k) {
     const int kv = k - kLag;  // round whose votes leave in this step
-    const Work w0 = round_work(a, k), w1 = round_work(a, kv);
+    const Work w0 = round_work(a, k), w1 = write_votes ? round_work(a, kv) : Work{0, 0, 0, 0, false};
     if (w0.on) {
       ++on_b[k % kNR];
       if (!lds_wait_ge(sy, &sy->cnt_b[k % kNR], kSW * on_b[k % kNR])) return;
@@ -652,7 +715,7 @@ __device__ void ctl_memory(const Launch& a, const __bf16* __restrict__ Q, float*
       for (int i = lane; i < kS; i += 64)
         if (j0 + i < P) vout[j0 + i] = s_votes[kv & 1][i];
     }
-    if (kv >= 0) lds_set(&sy->v_done, (unsigned)(kv + 1));  // votes of rounds <= kv are out of LDS
+    if (write_votes && kv >= 0) lds_set(&sy->v_done, (unsigned)(kv + 1));  // votes of rounds <= kv are out of LDS
     KVSEL_FUSED_CTL_MARK(k, 7);
   }
 }
@@ -723,7 +786,7 @@ __device__ __forceinline__ void solo_pass(const Launch& a, const Seg& s, const _
 }
 
 template <int D>
-__device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__device__ __forceinline__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                            unsigned* __restrict__ counter, float* __restrict__ votes, float* __restrict__ row_stats,
                            uint4 (*s_ring)[kNBuf][TileGeom<D>::PIECES], uint4* qbuf, float* s_maxp, float* s_zp,
                            float* s_m, float* s_iz) {
@@ -802,8 +865,1121 @@ __device__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const 
   }
 }
 
+// ===================================================================
+// Fused selection
+// ===================================================================
+
+__device__ __forceinline__ uint32_t sel_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b == 0x80000000u ? 0u : b;  // -0 ranks as +0
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
+  return v;
+}
+// Inclusive prefix sum over the lanes of the wave.
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Pooled score of the centre of a window of 7 (w[3]) for width k (odd,
+// 1..7): avg sums the k neighbours (out-of-range ones are the zero padding,
+// already in w) in ascending order and divides by k; max takes the maximum
+// (out-of-range neighbours are -inf in w).  Unused slots (|offset| > k / 2)
+// are -1 for avg (they sort below every score) and -inf for max, so the
+// ascending sum of the top k equals the sum of the k neighbours in
+// ascending order.
+__device__ __forceinline__ float pool7(float (&w)[7], int k, bool mx) {
+  if (k == 1) return w[3];
+  if (mx) {
+    float res = w[3];
+#pragma unroll
+    for (int t = 0; t < 7; ++t) res = fmaxf(res, w[t]);
+    return res;
+  }
+#pragma unroll
+  for (int i = 1; i < 7; ++i)
+#pragma unroll
+    for (int q = i; q > 0; --q) {
+      const float lo = fminf(w[q - 1], w[q]), hi = fmaxf(w[q - 1], w[q]);
+      w[q - 1] = lo;
+      w[q] = hi;
+    }
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 7; ++t)
+    if (t >= 7 - k) sum += w[t];
+  return sum / (float)k;
+}
+
+// Window of 7 around position j (centre w[3]) of a row of P prefix votes,
+// given the value at j + o for |o| <= 3 through `at`; offsets beyond the
+// pooling radius are unused.
+template <typename At>
+__device__ __forceinline__ float pool_at(int j, int P, int k, bool mx, At at) {
+  const int r = k >> 1;
+  float w[7];
+#pragma unroll
+  for (int t = 0; t < 7; ++t) {
+    const int o = t - 3, q = j + o;
+    const bool used = o >= -r && o <= r;
+    const bool in = q >= 0 && q < P;
+    w[t] = !used ? (mx ? -INFINITY : -1.f) : (in ? at(t) : (mx ? -INFINITY : 0.f));
+  }
+  return pool7(w, k, mx);
+}
+
+// The chunk a workgroup owns in round r, as the selection sees it.
+struct SelRound {
+  bool own;        // the workgroup owns a chunk in round r
+  bool on;         // ... and it holds prefix positions (the chunk takes part in the selection)
+  int e, h, c, row, P, nchp, count, L;
+  long long sl;    // exchange-slot index of the chunk (slots of a head's chunks are consecutive)
+  long long vbase; // element offset of the row in the votes, pooled scores and candidates
+};
+
+__device__ __forceinline__ SelRound sel_round(const Launch& a, int r) {
+  SelRound q{};
+  const Work w = round_work(a, r);
+  if (!w.on) return q;
+  const Seg& s = a.seg[w.e];
+  q.own = true;
+  q.e = w.e;
+  q.h = w.h;
+  q.c = w.c;
+  q.L = s.L;
+  q.P = s.L - a.W;
+  q.nchp = (q.P + kS - 1) / kS;
+  q.count = s.C - a.W;
+  q.row = s.row0 + (w.h - s.h0);
+  q.sl = s.fslot_base + (long long)w.h * fused_slot_stride(s.fc) + w.c;
+  q.vbase = s.vote_off + (long long)w.h * s.vote_ld;
+  q.on = w.c < q.nchp;
+  return q;
+}
+
+// Exchange wave, at kernel start, before any other load of the workgroup is
+// issued: clear this workgroup's share of the words the call's workgroups
+// publish to each other (exchange, count, halo and histogram slots).  The
+// arrival follows once the stores are done, so GO means every word is clear;
+// nothing is published before GO.
+__device__ __forceinline__ void sel_clear(const FusedSel& f) {
+  const int lane = threadIdx.x & 63;
+  const long long nwg = gridDim.x;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const long long n = f.clr_words[r];
+    const long long per = (n + nwg - 1) / nwg;
+    const long long lo = per * blockIdx.x, hi = min(n, lo + per);
+    for (long long i = lo + lane; i < hi; i += 64) store64(f.clr[r] + i, 0ull);
+  }
+}
+__device__ __forceinline__ void sel_arrive(const FusedSel& f) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clears are done
+  if ((threadIdx.x & 63) == 0) store64(f.flags + blockIdx.x, f.token);
+}
+
+// Exchange wave: the residency decision of the call.  A workgroup that sees
+// every arrival token of this call decides GO; one that has waited past the
+// bound decides ABORT.  Both are a compare-and-swap of the one decision word
+// to this call's token plus the decision, and the first one for this token
+// wins, so every workgroup follows the same decision.  The wait always ends:
+// ABORT is decided by the bound at the latest.
+__device__ __forceinline__ unsigned sel_decide(const Launch& a, const FusedSel& f) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long* dec = f.flags + kFlagWordsMax;
+  const unsigned grid = gridDim.x;
+  const long long t0 = wall_clock64();
+  for (;;) {
+    // The decision word and every arrival token, loaded together.
+    unsigned long long cur = 0ull;
+    if (lane == 0) cur = load64(dec);
+    unsigned long long tk[kFlagWordsMax / 64];
+#pragma unroll
+    for (int t = 0; t < kFlagWordsMax / 64; ++t) {
+      const unsigned i = (unsigned)(lane + 64 * t);
+      tk[t] = i < grid ? load64(f.flags + i) : f.token;
+    }
+    bool all = !f.force_abort;
+#pragma unroll
+    for (int t = 0; t < kFlagWordsMax / 64; ++t) all = all && tk[t] == f.token;
+    cur = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(cur >> 32)) << 32) |
+          (unsigned)__builtin_amdgcn_readfirstlane((int)cur);
+    if ((cur & ~3ull) == f.token) return (unsigned)(cur & 3ull);
+    unsigned want = 0u;
+    if (__ballot(!all) == 0ull) want = kFusedGo;
+    if (want == 0u && (f.force_abort || wall_clock64() - t0 > a.residency_ticks)) want = kFusedAbort;
+    if (want != 0u) {
+      // The swap's outcome is the decision: ours if it took, else the value
+      // that was there (another workgroup's decision for this token).
+      unsigned long long now = 0ull;
+      if (lane == 0) {
+        unsigned long long expect = cur;
+        now = __hip_atomic_compare_exchange_strong(dec, &expect, f.token | want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                  ? (f.token | want)
+                  : expect;
+      }
+      now = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(now >> 32)) << 32) |
+            (unsigned)__builtin_amdgcn_readfirstlane((int)now);
+      if ((now & ~3ull) == f.token) return (unsigned)(now & 3ull);
+      continue;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Bounded wait of the calling wave (or lane) until pred() holds (pred must
+// give a wave-uniform answer when the whole wave waits).  False once fifty
+// residency bounds (10 ms) have passed: far beyond any wait of a working
+// call, short enough that a broken one drains quickly.
+template <typename Pred>
+__device__ __forceinline__ bool sel_wait(const Launch& a, Pred pred) {
+  const long long t0 = wall_clock64();
+  for (;;) {
+    if (pred()) return true;
+    if (wall_clock64() - t0 > 50 * a.residency_ticks) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Lanes of the wave where pred holds, and those of them below this lane.
+__device__ __forceinline__ uint32_t wave_count(bool pred) { return (uint32_t)__popcll(__ballot(pred)); }
+__device__ __forceinline__ uint32_t lanes_below(bool pred) {
+  const unsigned long long m = __ballot(pred);
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// Digit of tau in a histogram of nb bins held by the wave (lane l holds
+// bins (63 - l) * per .. + per - 1, per = nb / 64, in h[]): the bin holding
+// the need-th largest key, and how many keys of that bin are still needed.
+// False if the bins add up to less than need.
+__device__ __forceinline__ bool find_digit(const uint32_t (&h)[32], int per, uint32_t need, uint32_t& digit,
+                                           uint32_t& left) {
+  const int lane = threadIdx.x & 63;
+  const int base = (63 - lane) * per;
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int t = 0; t < 32; ++t)
+    if (t < per) sum += h[t];
+  const uint32_t incl = wave_incl_u32(sum), excl = incl - sum;
+  const bool here = excl < need && need <= incl;
+  const unsigned long long hb = __ballot(here);
+  if (hb == 0ull) return false;
+  uint32_t d = 0u, n = 0u, cum = excl;
+  bool found = false;
+#pragma unroll
+  for (int t = 31; t >= 0; --t) {
+    if (t < per) {
+      const bool hit = !found && cum + h[t] >= need;
+      if (hit) {
+        d = (uint32_t)(base + t);
+        n = need - cum;
+        found = true;
+      }
+      cum += h[t];
+    }
+  }
+  const int bl = __builtin_ctzll(hb);
+  digit = (uint32_t)__builtin_amdgcn_readlane((int)d, bl);
+  left = (uint32_t)__builtin_amdgcn_readlane((int)n, bl);
+  return true;
+}
+
+// The lane where a running count over the lanes (each lane's value c, in the
+// order of the lanes) first reaches need, and how much of that lane's value
+// is still needed; false if the values add up to less than need.
+__device__ __forceinline__ bool wave_find(uint32_t c, uint32_t need, int& at, uint32_t& left) {
+  const uint32_t incl = wave_incl_u32(c), excl = incl - c;
+  const unsigned long long hb = __ballot(excl < need && need <= incl);
+  if (hb == 0ull) return false;
+  at = __builtin_ctzll(hb);
+  left = need - (uint32_t)__builtin_amdgcn_readlane((int)excl, at);
+  return true;
+}
+
+// Pooled scores of a lane's 8 positions (S0 + u) from its window values ext
+// (positions S0 - 3 .. S0 + 10).
+__device__ __forceinline__ void sel_pool8(const Launch& a, const SelRound& q, const float (&ext)[14], float (&pv)[8]) {
+  const int S0 = q.c * kS + (threadIdx.x & 63) * 8;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) pv[u] = pool_at(S0 + u, q.P, a.kernel, a.pooling == 1, [&](int t) { return ext[u + t]; });
+}
+
+// Stage A of a round (selection wave, during the streaming): the chunk's
+// votes v (lane * 8 + u of the chunk) go to memory; a chunk holding prefix
+// positions publishes its first and last three votes (tagged halo words) and
+// stores the pooled scores of every position whose window it holds in its
+// key slot.  Nothing here waits for memory, so the streaming never does
+// either; the three positions at each edge whose windows reach into a
+// neighbour are pooled in the end phase.
+__device__ __forceinline__ void sel_stage_a(const Launch& a, const FusedSel& f, const SelRound& q, const float (&v)[8],
+                                            float* __restrict__ votes) {
+  const int lane = threadIdx.x & 63;
+  const int S0 = q.c * kS + lane * 8;  // this lane's first position
+  float* vo = votes + q.vbase;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (S0 + u < q.P) vo[S0 + u] = v[u];
+  if (!q.on) return;
+  if (lane == 0)
+#pragma unroll
+    for (int t = 0; t < 3; ++t) store64(f.halo + q.sl * kHaloWords + t, (1ull << 32) | __float_as_uint(v[t]));
+  if (lane == 63)
+#pragma unroll
+    for (int t = 0; t < 3; ++t) store64(f.halo + q.sl * kHaloWords + 3 + t, (1ull << 32) | __float_as_uint(v[5 + t]));
+  float ext[14];  // positions S0 - 3 .. S0 + 10; lane 0's first three and lane 63's last three are not known yet
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    ext[t] = __shfl_up(v[5 + t], 1);
+    ext[11 + t] = __shfl_down(v[t], 1);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ext[3 + u] = v[u];
+  float pv[8];
+  sel_pool8(a, q, ext, pv);
+  float* ks = f.kslot + q.sl * kS + lane * 8;
+  reinterpret_cast<float4*>(ks)[0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+  reinterpret_cast<float4*>(ks)[1] = make_float4(pv[4], pv[5], pv[6], pv[7]);
+}
+
+// Selection wave during the streaming: stage A of each owned round once the
+// streaming waves have its votes in LDS.  The votes leave LDS first, so the
+// streaming waves may reuse the buffer at once.
+__device__ __forceinline__ void ctl_select(const Launch& a, const FusedSel& f, float* __restrict__ votes,
+                                           float (*s_votes)[kS], Sync* sy) {
+  if (!lds_wait_ge(sy, &sy->go, 1u) || lds_get(&sy->go) != kFusedGo) return;
+  const int lane = threadIdx.x & 63;
+  unsigned on_c[kNR] = {};
+  for (int ra = 0; ra < a.rounds; ++ra) {
+    const SelRound q = sel_round(a, ra);
+    KVSEL_FUSED_MARK(ra, 0);
+    if (q.own) {
+      ++on_c[ra % kNR];
+      if (!lds_wait_ge(sy, &sy->cnt_c[ra % kNR], kSW * on_c[ra % kNR])) return;
+      KVSEL_FUSED_MARK(ra, 1);
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s_votes[ra & 1][lane * 8 + u];
+      lds_set(&sy->v_done, (unsigned)(ra + 1));  // the votes of rounds <= ra have left LDS
+      sel_stage_a(a, f, q, v, votes);
+      KVSEL_FUSED_MARK(ra, 3);
+    } else {
+      lds_set(&sy->v_done, (unsigned)(ra + 1));
+    }
+  }
+}
+
+// ---- end phase (all waves of the workgroup, after the streaming)
+//
+// Each chunk the workgroup holds goes to one wave, which takes it through
+// five steps; a step's waits are for the same step of the row's other
+// chunks, so every wave runs a step for all its chunks before the next.
+//  1  edges: the three positions at each end are pooled with the
+//     neighbours' halos; then the chunk's keys give its coarse histogram
+//     (64 bins: bits 31..26), published as 64 words of count + 1.
+//  2  coarse: once every chunk's words are there, their sum gives the coarse
+//     bin D0 of tau and how many of its keys are needed; the chunk publishes
+//     its fine histogram inside D0 (32 bins: bits 25..21), count + 1.
+//  3  fine: once those are there, the first digit d1 (bits 31..21) of tau and
+//     the keys still needed in bin d1; the chunk stores its keys of bin d1 with
+//     their positions in its own range of the candidate list and, once they
+//     are written, its count word: keys above bin d1 and its candidates.
+//  4  pick: once every count word is there, each lane takes one chunk's
+//     candidates; the remaining 21 bits of tau come from them bit by bit (a
+//     ballot per held candidate), and every chunk's candidates above and on
+//     tau tell where the chunk's picks go; it writes them in index order
+//     (tau-equal ones lowest index first) and copies their K and V rows; the
+//     row's last prefix chunk adds the window.
+// Words published for other workgroups are cleared by their owners before the
+// arrival and carry count + 1 (or the +1 of the count word), so a written word
+// is never zero.
+
+// The chunk's keys (lane * 8 + u), read back from its key slot (written by
+// this workgroup); positions past P are 0.
+__device__ __forceinline__ void sel_load_keys(const FusedSel& f, const SelRound& q, uint32_t (&key)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int S0 = q.c * kS + lane * 8;
+  const float4* ks = reinterpret_cast<const float4*>(f.kslot + q.sl * kS + lane * 8);
+  const float4 x = ks[0], y = ks[1];
+  const float pv[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) key[u] = S0 + u < q.P ? sel_key(pv[u]) : 0u;
+}
+
+// Histogram of the chunk's keys over the bins of field (key >> shift) & mask
+// (mask 63 or 31), counting only keys for which pass(key) holds: lane b ends
+// with the count of bin b.  One round per distinct bin of the wave.
+template <typename Pass>
+__device__ __forceinline__ uint32_t sel_hist64(const uint32_t (&key)[8], int valid, int shift, uint32_t mask,
+                                               Pass pass) {
+  const int lane = threadIdx.x & 63;
+  uint32_t pend = 0u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < valid && pass(key[u])) pend |= 1u << u;
+  uint32_t mine = 0u;
+  for (int it = 0; it < 64; ++it) {
+    const unsigned long long any = __ballot(pend != 0u);
+    if (any == 0ull) break;
+    const int leader = __builtin_ctzll(any);
+    uint32_t fb = 0u;
+#pragma unroll
+    for (int u = 7; u >= 0; --u)
+      if ((pend >> u) & 1u) fb = (key[u] >> shift) & mask;
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)fb, leader);
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool hit = ((pend >> u) & 1u) && ((key[u] >> shift) & mask) == b;
+      tot += wave_count(hit);
+      if (hit) pend &= ~(1u << u);
+    }
+    if ((uint32_t)lane == b) mine = tot;
+  }
+  return mine;
+}
+
+// Step 1: the edge positions, then the chunk's coarse histogram.
+__device__ __forceinline__ bool sel_end_edges(const Launch& a, const FusedSel& f, const SelRound& q,
+                                              const float* __restrict__ votes) {
+  const int lane = threadIdx.x & 63;
+  const int S0 = q.c * kS + lane * 8;
+  const bool left = q.c > 0, right = (q.c + 1) * kS < q.P;
+  const bool reads = (lane < 3 && left) || (lane >= 3 && lane < 6 && right);
+  const unsigned long long* src =
+      !reads ? nullptr : (lane < 3 ? f.halo + (q.sl - 1) * kHaloWords + 3 + lane : f.halo + (q.sl + 1) * kHaloWords + (lane - 3));
+  unsigned long long hw = reads ? load64(src) : 0ull;
+  const bool edge_lane = (lane == 0 && left) || (lane == 63 && right);
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = edge_lane && S0 + u < q.P ? votes[q.vbase + S0 + u] : 0.f;
+  const bool ok = sel_wait(a, [&] {
+    const bool missing = reads && (hw >> 32) == 0ull;
+    if (__ballot(missing) == 0ull) return true;
+    if (missing) hw = load64(src);
+    return false;
+  });
+  if (!ok) {
+    if (lane == 0) flag_error(a, f, kErrSelectWait);
+    return false;
+  }
+  float ext[14];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    ext[t] = __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)(unsigned)hw, t));
+    ext[11 + t] = __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)(unsigned)hw, 3 + t));
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ext[3 + u] = v[u];
+  const int valid = max(0, min(8, q.P - S0));
+  float pv[8];
+  sel_pool8(a, q, ext, pv);
+  float* ks = f.kslot + q.sl * kS + lane * 8;
+  const uint32_t emask = (lane == 0 && left ? 7u : 0u) | (lane == 63 && right ? 0xE0u : 0u);
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (((emask >> u) & 1u) && u < valid) ks[u] = pv[u];
+  uint32_t key[8];
+  sel_load_keys(f, q, key);  // after the edge stores (the same wave's accesses to an address stay in order)
+  if (f.pooled != nullptr) {
+    const float* kf = f.kslot + q.sl * kS + lane * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < valid) f.pooled[q.vbase + S0 + u] = kf[u];
+  }
+  const uint32_t cnt = sel_hist64(key, valid, 26, 63u, [](uint32_t) { return true; });
+  store32(f.cslot + q.sl * 64 + lane, cnt + 1u);
+  return true;
+}
+
+// The row's histogram over 64 bins from every chunk's published words
+// (words of chunk i at base + i * stride, bin b at + b), polled until all are
+// written: lane l gets the count of bin 63 - l (highest first).  Only lanes
+// below `bins` take part (the rest get 0).  False on a timeout.
+__device__ __forceinline__ bool sel_row_hist(const Launch& a, const unsigned* base, int stride, int nchp, int bins,
+                                             uint32_t& count) {
+  const int lane = threadIdx.x & 63;
+  const int b = bins - 1 - lane;
+  return sel_wait(a, [&] {
+    uint32_t sum = 0u;
+    bool all = true;
+    constexpr int kBatch = 16;
+    for (int i0 = 0; i0 < nchp; i0 += kBatch) {
+      uint32_t w[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) w[t] = (lane < bins && i0 + t < nchp) ? load32(base + (i0 + t) * stride + b) : 1u;
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        all = all && w[t] != 0u;
+        sum += w[t] - 1u;
+      }
+    }
+    count = sum;
+    return __ballot(!all) == 0ull;
+  });
+}
+
+// Step 2: the coarse bin of tau, then the chunk's fine histogram inside it.
+__device__ __forceinline__ bool sel_end_coarse(const Launch& a, const FusedSel& f, const SelRound& q, uint32_t* st) {
+  const int lane = threadIdx.x & 63;
+  uint32_t cnt = 0u, need0 = 0u;
+  int at = 0;
+  const bool ok = sel_row_hist(a, f.cslot + (q.sl - q.c) * 64, 64, q.nchp, 64, cnt) &&
+                  wave_find(cnt, (uint32_t)q.count, at, need0);
+  if (!ok) {
+    if (lane == 0) flag_error(a, f, kErrSelectWait);
+    return false;
+  }
+  const uint32_t d0 = 63u - (uint32_t)at;
+  uint32_t key[8];
+  sel_load_keys(f, q, key);
+  const int valid = max(0, min(8, q.P - (q.c * kS + lane * 8)));
+  const uint32_t fc = sel_hist64(key, valid, 21, 31u, [&](uint32_t k) { return (k >> 26) == d0; });
+  if (lane < 32) store32(f.fslot + q.sl * 32 + lane, fc + 1u);
+  if (lane == 0) {
+    st[0] = d0;
+    st[1] = need0;
+  }
+  return true;
+}
+
+// Step 3: the first digit of tau, then the chunk's candidates and count word.
+__device__ __forceinline__ bool sel_end_fine(const Launch& a, const FusedSel& f, const SelRound& q, uint32_t* st) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t d0 = st[0], need0 = st[1];
+  uint32_t cnt = 0u, need = 0u;
+  int at = 0;
+  const bool ok = sel_row_hist(a, f.fslot + (q.sl - q.c) * 32, 32, q.nchp, 32, cnt) && wave_find(cnt, need0, at, need);
+  if (!ok) {
+    if (lane == 0) flag_error(a, f, kErrSelectWait);
+    return false;
+  }
+  const uint32_t d1 = d0 * 32u + 31u - (uint32_t)at;
+  uint32_t key[8];
+  sel_load_keys(f, q, key);
+  const int S0 = q.c * kS + lane * 8;
+  const int valid = max(0, min(8, q.P - S0));
+  uint32_t tot_above = 0u, tot_mine = 0u;
+  bool mine_u[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    tot_above += wave_count(u < valid && (key[u] >> 21) > d1);
+    mine_u[u] = u < valid && (key[u] >> 21) == d1;
+  }
+  unsigned long long* cb = f.cand + q.vbase + q.c * kS;  // the chunk's own range
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t at_u = tot_mine + lanes_below(mine_u[u]);
+    if (mine_u[u]) store64(cb + at_u, ((unsigned long long)(S0 + u) << 32) | key[u]);
+    tot_mine += wave_count(mine_u[u]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the candidates are there before the count word says so
+  if (lane == 0) {
+    store64(f.cw + q.sl, (unsigned long long)(tot_above + 1u) | ((unsigned long long)tot_mine << 20));
+    st[2] = d1;
+    st[3] = need;
+  }
+  return true;
+}
+
+// Copy n rows of D bf16 (RU 16-byte pieces each) by the wave: output row
+// out_row0 + i from input row in_row0 + (list ? list[i] : first + i).
+template <int RU>
+__device__ __forceinline__ void wave_copy_rows(const uint4* __restrict__ Ki, const uint4* __restrict__ Vi,
+                                               uint4* __restrict__ Ko, uint4* __restrict__ Vo, long long in_row0,
+                                               long long out_row0, const int32_t* list, int first, int n) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kFly = 4;
+  const int total = n * RU;
+  for (int e0 = 0; e0 < total; e0 += kFly * 64) {
+    uint4 kv[kFly], vv[kFly];
+#pragma unroll
+    for (int t = 0; t < kFly; ++t) {
+      const int e = min(e0 + t * 64 + lane, total - 1);
+      const int i = e / RU;
+      const long long from = (in_row0 + (list ? list[i] : first + i)) * RU + e % RU;
+      kv[t] = Ki[from];
+      vv[t] = Vi[from];
+    }
+#pragma unroll
+    for (int t = 0; t < kFly; ++t) {
+      const int e = e0 + t * 64 + lane;
+      if (e < total) {
+        const long long to = (out_row0 + e / RU) * RU + e % RU;
+        Ko[to] = kv[t];
+        Vo[to] = vv[t];
+      }
+    }
+  }
+}
+
+// Step 4: tau, the chunk's picks in index order and their rows (see above).
+// Chunk i of the row is lane i % 64 of group i / 64 (at most kPickGroups);
+// each lane holds up to kHeld of its chunk's candidates per group and re-reads
+// the rest where a chunk has more.
+constexpr int kPickGroups = 2;
+constexpr int kHeld = 16;
+template <int D>
+__device__ __forceinline__ void sel_end_pick(const Launch& a, const FusedSel& f, const SelRound& q, const uint32_t* st,
+                                             const __bf16* __restrict__ K, int32_t* list) {
+  constexpr int RU = D * 2 / 16;
+  const int lane = threadIdx.x & 63;
+  const Seg& s = a.seg[q.e];
+  const unsigned long long* cw0 = f.cw + (q.sl - q.c);  // the row's first chunk
+  const int nchp = q.nchp;
+  unsigned long long w[kPickGroups];
+  const bool ok = sel_wait(a, [&] {
+    bool all = true;
+#pragma unroll
+    for (int g = 0; g < kPickGroups; ++g) {
+      const int i = g * 64 + lane;
+      w[g] = i < nchp ? load64(cw0 + i) : 1ull;
+      all = all && w[g] != 0ull;
+    }
+    return __ballot(!all) == 0ull;
+  });
+  if (!ok) {
+    if (lane == 0) flag_error(a, f, kErrSelectWait);
+    return;
+  }
+  uint32_t above[kPickGroups], len[kPickGroups], ck[kPickGroups][kHeld];
+  bool extra = false;
+#pragma unroll
+  for (int g = 0; g < kPickGroups; ++g) {
+    const int i = g * 64 + lane;
+    above[g] = i < nchp ? (uint32_t)(w[g] & 0xFFFFFu) - 1u : 0u;
+    len[g] = i < nchp ? (uint32_t)(w[g] >> 20) & 0xFFFFFu : 0u;
+    extra = extra || len[g] > (uint32_t)kHeld;
+    const unsigned long long* cb = f.cand + q.vbase + (long long)i * kS;
+#pragma unroll
+    for (int t = 0; t < kHeld; ++t) ck[g][t] = (uint32_t)t < len[g] ? (uint32_t)load64(cb + t) : 0u;
+  }
+  const bool any_extra = __ballot(extra) != 0ull;
+  uint32_t key[8];
+  sel_load_keys(f, q, key);
+  // The rest of tau, bit by bit.
+  uint32_t prefix = st[2], need = st[3];
+  for (int bit = 20; bit >= 0; --bit) {
+    const uint32_t target = (prefix << 1) | 1u;
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int g = 0; g < kPickGroups; ++g)
+#pragma unroll
+      for (int t = 0; t < kHeld; ++t) tot += wave_count((uint32_t)t < len[g] && (ck[g][t] >> bit) == target);
+    if (any_extra) {
+      uint32_t more = 0u;
+#pragma unroll
+      for (int g = 0; g < kPickGroups; ++g) {
+        const unsigned long long* cb = f.cand + q.vbase + (long long)(g * 64 + lane) * kS;
+        for (uint32_t t = kHeld; t < len[g]; ++t) more += ((uint32_t)load64(cb + t) >> bit) == target;
+      }
+      tot += wave_sum_u32(more);
+    }
+    if (tot >= need) {
+      prefix = target;
+    } else {
+      prefix <<= 1;
+      need -= tot;
+    }
+  }
+  const uint32_t tau = prefix, need_eq = need;
+  // Every chunk's picks in index order: above its bin, above tau among its
+  // candidates, and the tau-equal ones still needed (lowest index first).
+  uint32_t before = 0u, take_c = 0u, carry_p = 0u, carry_e = 0u;
+#pragma unroll
+  for (int g = 0; g < kPickGroups; ++g) {
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int t = 0; t < kHeld; ++t)
+      if ((uint32_t)t < len[g]) {
+        gt += ck[g][t] > tau;
+        eq += ck[g][t] == tau;
+      }
+    if (len[g] > (uint32_t)kHeld) {
+      const unsigned long long* cb = f.cand + q.vbase + (long long)(g * 64 + lane) * kS;
+      for (uint32_t t = kHeld; t < len[g]; ++t) {
+        const uint32_t kk = (uint32_t)load64(cb + t);
+        gt += kk > tau;
+        eq += kk == tau;
+      }
+    }
+    const uint32_t eq_incl = wave_incl_u32(eq);
+    const uint32_t eqb = carry_e + eq_incl - eq;
+    const uint32_t take = need_eq > eqb ? min(eq, need_eq - eqb) : 0u;
+    const uint32_t picks = above[g] + gt + take;
+    const uint32_t p_incl = wave_incl_u32(picks);
+    if (q.c >= g * 64 && q.c < g * 64 + 64) {
+      before = (uint32_t)__builtin_amdgcn_readlane((int)(carry_p + p_incl - picks), q.c - g * 64);
+      take_c = (uint32_t)__builtin_amdgcn_readlane((int)take, q.c - g * 64);
+    }
+    carry_e += (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63);
+    carry_p += (uint32_t)__builtin_amdgcn_readlane((int)p_incl, 63);
+  }
+  // This chunk's picks.
+  const int S0 = q.c * kS + lane * 8;
+  const int valid = max(0, min(8, q.P - S0));
+  uint32_t seen = 0u;  // tau-equal keys of the chunk before this lane's current one
+  {
+    uint32_t eqb = 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) eqb += u < valid && key[u] == tau;
+    seen = wave_incl_u32(eqb) - eqb;
+  }
+  uint32_t pm = 0u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (u >= valid) continue;
+    if (key[u] > tau) {
+      pm |= 1u << u;
+    } else if (key[u] == tau) {
+      if (seen < take_c) pm |= 1u << u;
+      ++seen;
+    }
+  }
+  const uint32_t np = (uint32_t)__popc(pm);
+  const uint32_t p_incl = wave_incl_u32(np);
+  const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)p_incl, 63);
+  uint32_t slot = p_incl - np;
+  int32_t* out = f.indices + s.idx_off + (long long)q.h * s.idx_ld;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if ((pm >> u) & 1u) {
+      if (before + slot < (uint32_t)q.count) {  // always, unless a timed-out wait left the counts short
+        out[before + slot] = S0 + u;
+        list[slot] = S0 + u;
+      }
+      ++slot;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint4* Ki = reinterpret_cast<const uint4*>(K);
+  const uint4* Vi = reinterpret_cast<const uint4*>(f.V);
+  uint4* Ko = reinterpret_cast<uint4*>(f.K_out);
+  uint4* Vo = reinterpret_cast<uint4*>(f.V_out);
+  const long long in_row0 = s.kv_off / D + (long long)q.h * s.L;
+  const long long out_row0 = s.out_off + (long long)q.h * s.out_ld;
+  const int n_copy = (int)min(n_c, (uint32_t)q.count > before ? (uint32_t)q.count - before : 0u);
+  wave_copy_rows<RU>(Ki, Vi, Ko, Vo, in_row0, out_row0 + before, list, 0, n_copy);
+  if (q.c == nchp - 1) {  // the window follows the picks
+    for (int i = lane; i < a.W; i += 64) out[q.count + i] = q.P + i;
+    wave_copy_rows<RU>(Ki, Vi, Ko, Vo, in_row0, out_row0 + q.count, nullptr, q.P, a.W);
+  }
+}
+
+// End phase of the fused selection (all waves): the workgroup's chunks are
+// dealt to its waves, which run each step for all of theirs before the next.
+// lds: per round four words (the digits and what is still needed), then per
+// wave kS words for its picks.
+template <int D>
+__device__ __forceinline__ void sel_finish(const Launch& a, const FusedSel& f, const __bf16* __restrict__ K,
+                                           const float* __restrict__ votes, uint32_t* lds) {
+  constexpr int kWv = kThreads / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* st = lds;
+  int32_t* list = reinterpret_cast<int32_t*>(lds + 4 * kFusedMaxRounds) + wave * kS;
+  KVSEL_FUSED_MARK(20, 0);
+  constexpr uint32_t kFail = 0xFFFFFFFFu;  // in a round's first word: a step timed out
+  for (int step = 0; step < 4; ++step) {
+    for (int r = 0, n = 0; r < a.rounds; ++r) {
+      const SelRound q = sel_round(a, r);
+      if (!q.on) continue;
+      if (n++ % kWv != wave) continue;
+      uint32_t* sr = st + 4 * r;
+      bool ok = true;
+      if (step == 0)
+        ok = sel_end_edges(a, f, q, votes);
+      else if (sr[0] == kFail)
+        continue;
+      else if (step == 1)
+        ok = sel_end_coarse(a, f, q, sr);
+      else if (step == 2)
+        ok = sel_end_fine(a, f, q, sr);
+      else
+        sel_end_pick<D>(a, f, q, sr, K, list);
+      if (lane == 0 && (step == 0 || !ok)) sr[0] = ok ? 0u : kFail;
+    }
+    KVSEL_FUSED_MARK(20, 1 + step);
+  }
+}
+
+// ---- fallback of the fused selection (ABORT: not all resident)
+
+// Token-tagged counters: (tag << 24) | count, where a word whose tag is not
+// this call's counts as zero.  Claim returns the count before the claim.
+__device__ __forceinline__ unsigned tok_claim(unsigned long long* w, unsigned long long tag) {
+  unsigned long long cur = load64(w);
+  for (;;) {
+    const unsigned cnt = (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
+    unsigned long long expect = cur;
+    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + 1u),
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return cnt;
+    cur = expect;
+  }
+}
+__device__ __forceinline__ unsigned tok_count(const unsigned long long* w, unsigned long long tag) {
+  const unsigned long long cur = load64(w);
+  return (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
+}
+
+// Inclusive scan over the workgroup (kThreads); total gets the sum.
+__device__ __forceinline__ uint32_t wg_incl(uint32_t v, uint32_t* sh, uint32_t& total) {
+  constexpr int kWv = kThreads / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  v = wave_incl_u32(v);
+  if (lane == 63) sh[wv] = v;
+  __syncthreads();
+  uint32_t base = 0u, tot = 0u;
+#pragma unroll
+  for (int i = 0; i < kWv; ++i) {
+    const uint32_t t = sh[i];
+    if (i < wv) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return v + base;
+}
+
+// Work item t of the fallback's scoring phases: (row, chunk) over the
+// launch's rows, chunk-minor.
+struct FbItem {
+  bool on;
+  int e, h, c, row;
+};
+__device__ __forceinline__ FbItem fb_item(const Launch& a, unsigned t) {
+  FbItem it{false, 0, 0, 0, 0};
+  unsigned base = 0;
+  for (int e = 0; e < a.n; ++e) {
+    const Seg& s = a.seg[e];
+    const unsigned n = (unsigned)(s.nh * s.fc);
+    if (t < base + n) {
+      const unsigned loc = t - base;
+      it.on = true;
+      it.e = e;
+      it.h = s.h0 + (int)(loc / (unsigned)s.fc);
+      it.c = (int)(loc % (unsigned)s.fc);
+      it.row = s.row0 + (it.h - s.h0);
+      return it;
+    }
+    base += n;
+  }
+  return it;
+}
+__device__ __forceinline__ int fb_rows(const Launch& a) { return a.seg[a.n - 1].row0 + a.seg[a.n - 1].nh; }
+
+// One pass of the streaming waves over positions [lo, hi) of a head's K
+// (tiles lo + 32 t, wave-strided): with votes, the votes of the prefix
+// positions from the base-2 log-normalisers s_m (agent-scope stores, read by
+// other workgroups later); without, the lane's running (max, sum) per row.
+template <int D>
+__device__ __forceinline__ void fb_pass(const Launch& a, int L, int P, const __bf16* __restrict__ kh, int lo, int hi, bool with_votes,
+                        uint4 (*ring)[TileGeom<D>::PIECES], const uint4* qbuf, const float* s_m, float* vout,
+                        float (&m)[16], float (&z)[16]) {
+  using G = TileGeom<D>;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const float sc = a.scale2;
+  const int tiles = (hi - lo + 31) / 32;
+  const int nw = tiles > wave ? (tiles - wave + kSW - 1) / kSW : 0;
+  float mr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mr[r] = with_votes ? s_m[acc_row(r, g)] : 0.f;
+  int issued = 0;
+  if (nw > 0) {
+    issue_tile<D>(kh, L, lo + wave * 32, ring[0], lane);
+    issued = 1;
+  }
+  for (int i = 0; i < nw; ++i) {
+    wait_tiles<D>(0);
+    const uint4* tile = ring[0];
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int c = 2 * kk + g;
+      const int off = n * G::PR + (c ^ (n & (G::PR - 1)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qbuf[off]),
+                                                    __builtin_bit_cast(bf16x8, tile[off]), acc, 0, 0, 0);
+    }
+    lds_fence();
+    if (issued < nw) {
+      issue_tile<D>(kh, L, lo + (wave + kSW * issued) * 32, ring[0], lane);
+      ++issued;
+    }
+    const int j = lo + (wave + kSW * i) * 32 + n;
+    if (with_votes) {
+      float tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot += exp2_fast(fmaf(acc[r], sc, -mr[r]));
+      const float other = __shfl_xor(tot, 32);
+      const float v = g == 0 ? tot + other : other + tot;
+      if (g == 0 && j < hi && j < P) __hip_atomic_store(vout + j, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, g);
+        const float x = (j < hi && j <= P + row) ? acc[r] * sc : -INFINITY;
+        const float d = x - m[r];
+        const float e = exp2_fast(-fabsf(d));
+        z[r] = d > 0.f ? fmaf(z[r], e, 1.f) : z[r] + e;
+        m[r] = fmaxf(m[r], x);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Qwin of (sequence, head) hs into qbuf (wave kExWave), rows W..31 cleared.
+template <int D>
+__device__ __forceinline__ void fb_load_q(const Launch& a, const __bf16* __restrict__ Q, int hs, uint4* qbuf) {
+  if ((int)(threadIdx.x >> 6) == kExWave) {
+    issue_tile<D>(Q + (long long)hs * a.W * D, a.W, 0, qbuf, threadIdx.x & 63);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    ctl_finish_q<D>(a.W, qbuf);
+  }
+}
+
+// Pooled score of position j of a row whose votes other workgroups wrote.
+__device__ __forceinline__ float fb_pooled(const Launch& a, const float* v, int j, int P) {
+  return pool_at(j, P, a.kernel, a.pooling == 1, [&](int t) {
+    return __hip_atomic_load(v + j + t - 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+}
+
+// Whole-row selection by the workgroup: three radix digits of tau over the
+// row's pooled keys (recomputed from the votes in each pass), then the picks
+// in index order and their K and V rows, then the window.
+template <int D>
+__device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f, int e, int h, const float* __restrict__ votes,
+                              const __bf16* __restrict__ K, uint32_t* lds) {
+  constexpr int RU = D * 2 / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const Seg& s = a.seg[e];
+  const int P = s.L - a.W, count = s.C - a.W;
+  const long long vbase = s.vote_off + (long long)h * s.vote_ld;
+  const float* v = votes + vbase;
+  uint32_t* hist = lds;             // 2048 bins
+  uint32_t* sh = lds + 2048;        // 32 words of scan scratch, then the digit and what is still needed
+  int32_t* list = reinterpret_cast<int32_t*>(lds + 2048 + 64);  // kThreads picks
+  uint32_t prefix = 0u, need = (uint32_t)count;
+  for (int digit = 0; digit < 3; ++digit) {
+    const int shift = digit == 0 ? 21 : (digit == 1 ? 10 : 0);
+    const int bits = digit == 2 ? 10 : 11;
+    const int nb = 1 << bits;
+    for (int d = tid; d < nb; d += kThreads) hist[d] = 0u;
+    __syncthreads();
+    for (int j = tid; j < P; j += kThreads) {
+      const float pv = fb_pooled(a, v, j, P);
+      const uint32_t k = sel_key(pv);
+      if (digit == 0 && f.pooled != nullptr) f.pooled[vbase + j] = pv;
+      if (digit == 0 || (k >> (shift + bits)) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const int per = nb / 64;
+      uint32_t hh[32];
+#pragma unroll
+      for (int t = 0; t < 32; ++t) hh[t] = t < per ? hist[(63 - lane) * per + t] : 0u;
+      uint32_t dg = 0u, left = 0u;
+      if (!find_digit(hh, per, need, dg, left)) {
+        dg = 0u;
+        left = 0u;
+        if (lane == 0) flag_error(a, f, kErrSelectWait);
+      }
+      if (lane == 0) {
+        sh[32] = dg;
+        sh[33] = left;
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << bits) | sh[32];
+    need = sh[33];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix, need_eq = need;
+  int32_t* out = f.indices + s.idx_off + (long long)h * s.idx_ld;
+  const uint4* Ki = reinterpret_cast<const uint4*>(K);
+  const uint4* Vi = reinterpret_cast<const uint4*>(f.V);
+  uint4* Ko = reinterpret_cast<uint4*>(f.K_out);
+  uint4* Vo = reinterpret_cast<uint4*>(f.V_out);
+  const long long in_row0 = s.kv_off / D + (long long)h * s.L;
+  const long long out_row0 = s.out_off + (long long)h * s.out_ld;
+  uint32_t before = 0u, eq_seen = 0u;
+  for (int base = 0; base < P; base += kThreads) {
+    const int j = base + tid;
+    const uint32_t k = j < P ? sel_key(fb_pooled(a, v, j, P)) : 0u;
+    const bool gt = j < P && k > tau, eq = j < P && k == tau;
+    uint32_t eq_tot, take_tot;
+    const uint32_t eq_rank = wg_incl(eq ? 1u : 0u, sh, eq_tot) - (eq ? 1u : 0u);
+    const bool take = gt || (eq && eq_seen + eq_rank < need_eq);
+    const uint32_t pos = wg_incl(take ? 1u : 0u, sh, take_tot) - (take ? 1u : 0u);
+    if (take && before + pos < (uint32_t)count) {
+      out[before + pos] = j;
+      list[pos] = j;
+    }
+    __syncthreads();
+    const int n = (int)min(take_tot, (uint32_t)count > before ? (uint32_t)count - before : 0u);
+    for (int q = tid; q < n * RU; q += kThreads) {
+      const long long from = (in_row0 + list[q / RU]) * RU + q % RU, to = (out_row0 + before + q / RU) * RU + q % RU;
+      Ko[to] = Ki[from];
+      Vo[to] = Vi[from];
+    }
+    before += take_tot;
+    eq_seen += eq_tot;
+    __syncthreads();
+  }
+  for (int i = tid; i < a.W; i += kThreads) out[count + i] = P + i;
+  for (int q = tid; q < a.W * RU; q += kThreads) {
+    const long long from = (in_row0 + P + q / RU) * RU + q % RU, to = (out_row0 + count + q / RU) * RU + q % RU;
+    Ko[to] = Ki[from];
+    Vo[to] = Vi[from];
+  }
+  (void)lane;
+}
+
+// The fallback: scoring in two phases over (row, chunk) items (statistics,
+// then votes; with handed-over statistics only the votes), then whole rows'
+// selections.  Items are claimed in order from token-tagged counters, and a
+// phase waits only for items of the phase before, which running workgroups
+// have claimed, so the fallback finishes with any number of workgroups.
 template <int D, bool kLse>
-__global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const __bf16* __restrict__ Q,
+__device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f, const __bf16* __restrict__ Q,
+                             const __bf16* __restrict__ K, const float* __restrict__ lse,
+                             unsigned long long* __restrict__ ex, float* __restrict__ votes,
+                             float* __restrict__ row_stats, uint4 (*ring)[TileGeom<D>::PIECES], uint4* qbuf,
+                             float* s_maxp, float* s_zp, float* s_m, uint32_t* lds_u32) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const bool streams = wave < kSW;
+  const unsigned long long tag = token_tag(f.token);
+  unsigned long long* ctr = f.flags + kFlagWordsMax + 1;
+  const int W = a.W;
+  __shared__ unsigned s_claim;
+  unsigned items = 0;
+  for (int e = 0; e < a.n; ++e) items += (unsigned)(a.seg[e].nh * a.seg[e].fc);
+  for (int phase = kLse ? 1 : 0; phase < 2; ++phase) {
+    for (;;) {
+      if (tid == 0) s_claim = tok_claim(ctr + phase, tag);
+      __syncthreads();
+      const unsigned t = s_claim;
+      __syncthreads();
+      if (t >= items) break;
+      const FbItem it = fb_item(a, t);
+      const Seg& s = a.seg[it.e];
+      const int L = s.L, P = L - W;
+      const int hs = s.b * a.heads + it.h;
+      const long long sl = s.fslot_base + (long long)it.h * fused_slot_stride(s.fc) + it.c;
+      // The chunk statistics go to the chunk's key slot, which nothing clears
+      // (a workgroup that starts late still clears its share of the exchange
+      // slots).
+      unsigned long long* fbs = reinterpret_cast<unsigned long long*>(f.kslot);
+      const __bf16* kh = K + s.kv_off + (long long)it.h * L * D;
+      const int lo = it.c * kS, hi = min(L, lo + kS);
+      fb_load_q<D>(a, Q, hs, qbuf);
+      if (phase == 1 && tid == 0) {  // the statistics of every chunk of the row are there
+        const bool ok = kLse || sel_wait(a, [&] { return tok_count(f.rowfb + 2ll * it.row, tag) >= (unsigned)s.fc; });
+        if (!ok) flag_error(a, f, kErrExchangeWait);
+      }
+      __syncthreads();
+      float m[16], z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        m[r] = kNegBig;
+        z[r] = 0.f;
+      }
+      if (phase == 0) {
+        if (streams) fb_pass<D>(a, L, P, kh, lo, hi, false, ring + wave, qbuf, s_m, nullptr, m, z);
+        if (streams) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float mh0 = half_max(m[r]);
+            const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 31));
+            const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 63));
+            const float mh = g == 0 ? m0 : m1;
+            const float zz = half_sum(z[r] != 0.f ? z[r] * exp2_fast(m[r] - mh) : 0.f);
+            if ((lane & 31) == 31) {
+              s_maxp[wave * 32 + acc_row(r, g)] = mh;
+              s_zp[wave * 32 + acc_row(r, g)] = zz;
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < W) {  // the chunk's (max, sum) per row into its slot
+          float M = s_maxp[tid];
+          for (int w2 = 1; w2 < kSW; ++w2) M = fmaxf(M, s_maxp[w2 * 32 + tid]);
+          float Z = 0.f;
+          for (int w2 = 0; w2 < kSW; ++w2) {
+            const float zv = s_zp[w2 * 32 + tid];
+            if (zv != 0.f) Z += zv * exp2_fast(s_maxp[w2 * 32 + tid] - M);
+          }
+          store64(fbs + sl * (kS / 2) + tid, pack_slot(M, Z));
+        }
+      } else {
+        if (tid < 32) {  // the row's log-normalisers: merged slots in chunk order, or the given ones
+          float lm = INFINITY;
+          if (tid < W) {
+            if (kLse) {
+              lm = lse[(long long)hs * W + tid] * kLog2e;
+              if (!isfinite(lm)) flag_error(a, f, kErrNonFinite);
+            } else {
+              const unsigned long long* s0 = fbs + (sl - it.c) * (kS / 2) + tid;
+              float M = kNegBig, Z = 0.f;
+              for (int c2 = 0; c2 < s.fc; ++c2) {
+                const unsigned long long wd = load64(s0 + (long long)c2 * (kS / 2));
+                const float mo = __uint_as_float((unsigned)wd), zo = __uint_as_float((unsigned)(wd >> 32));
+                if (zo != 0.f) lse_merge(M, Z, mo, zo);
+              }
+              if (!stats_ok(M, Z)) flag_error(a, f, kErrNonFinite);
+              lm = M + __log2f(Z);
+              if (row_stats != nullptr && it.c == 0) {
+                row_stats[((long long)hs * W + tid) * 2] = M * kLn2;
+                row_stats[((long long)hs * W + tid) * 2 + 1] = Z;
+              }
+            }
+          }
+          s_m[tid] = lm;  // rows past W: zero queries, dropped by the infinite normaliser
+        }
+        __syncthreads();
+        float* vout = votes + s.vote_off + (long long)it.h * s.vote_ld;
+        if (streams) fb_pass<D>(a, L, P, kh, lo, min(hi, P), true, ring + wave, qbuf, s_m, vout, m, z);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) (void)tok_claim(f.rowfb + 2ll * it.row + phase, tag);  // one more chunk of the row done
+      __syncthreads();
+    }
+  }
+  const int rows = fb_rows(a);
+  for (;;) {
+    if (tid == 0) s_claim = tok_claim(ctr + 2, tag);
+    __syncthreads();
+    const unsigned t = s_claim;
+    __syncthreads();
+    if (t >= (unsigned)rows) break;
+    const int e = find_seg<kFieldRow>(a, (int)t);
+    const Seg& s = a.seg[e];
+    const int h = s.h0 + ((int)t - s.row0);
+    if (tid == 0) {  // every chunk's votes of the row are there
+      const bool ok = sel_wait(a, [&] { return tok_count(f.rowfb + 2ll * t + 1, tag) >= (unsigned)s.fc; });
+      if (!ok) flag_error(a, f, kErrSelectWait);
+    }
+    __syncthreads();
+    fb_select_row<D>(a, f, e, h, votes, K, lds_u32);
+    __syncthreads();
+  }
+  (void)lane;
+}
+
+template <int D, bool kLse>
+__global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const FusedSel f,
+                                                                  const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,
                                                                   const float* __restrict__ lse,
                                                                   unsigned long long* __restrict__ ex,
@@ -818,33 +1994,69 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __shared__ float s_m[kNR][32], s_iz[32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
+  static_assert(sizeof(s_x) >= 4 * (4 * kFusedMaxRounds + (kThreads / 64) * kS), "the end phase's words fit s_x");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  KVSEL_FUSED_MARK(23, 0);
   unsigned arrived = 0u;
-  if (!kLse && wave == kSW && lane == 0) arrived = arrive(status);
-  if (threadIdx.x == 0) sy = Sync{};
+  if (!f.on && !kLse && wave == kExWave && lane == 0) arrived = arrive(status);
+  if (threadIdx.x == 0) {
+    sy = Sync{};
+    sy.zeroed = f.on ? 0u : 1u;
+  }
   __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
-  // The first K tiles and Qwin of rounds 0 and 1.
+  // The clears of the fused selection's shared words go first, so that they
+  // do not queue behind the K tiles; then the first K tiles and Qwin of
+  // rounds 0 and 1.
+  if (f.on) {
+    if (wave == kExWave) {
+      KVSEL_FUSED_MARK(22, 0);
+      sel_clear(f);
+      KVSEL_FUSED_MARK(22, 1);
+      lds_set(&sy.issued, 1u);
+    } else if (wave < kSW || wave == kMemWave) {
+      (void)lds_wait_ge(&sy, &sy.issued, 1u);
+    }
+  }
   WaveTiles cur{K, 0, 0, false};
   int issued = 0, consumed = 0;
   if (wave < kSW) {
     cur = wave_tiles<D>(a, K, 0, wave);
     issue_wave_tile<D>(cur, 0, s_ring[wave][0], issued);
-  } else if (wave == kSW + 1) {
+  } else if (wave == kMemWave) {
     ctl_issue_q<D>(a, 0, Q, s_q[0]);
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
-  if (wave == kSW) {
-    if constexpr (kLse)
-      ctl_lse(a, lse, s_m, &sy);  // no workgroup waits for another
-    else if (decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks) == kFusedGo)
-      ctl_exchange<D>(a, ex, status, row_stats, s_m, &sy);
-    else
+  if (wave == kExWave) {
+    if (f.on) {
+      // Arrive once the clears are done, decide; then the statistics.
+      sel_arrive(f);
+      KVSEL_FUSED_MARK(22, 2);
+      KVSEL_FUSED_MARK(23, 4);
+      const unsigned d = sel_decide(a, f);
+      KVSEL_FUSED_MARK(23, 5);
+      lds_set(&sy.zeroed, 1u);  // every workgroup's clears are done (GO), or nothing is published (ABORT)
+      if (d != kFusedGo && lane == 0) flag_error(a, f, kFlagScoringFallback);
+      lds_set(&sy.go, d);
+      if (d != kFusedGo)
+        lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
+      else if constexpr (kLse)
+        ctl_lse(a, f, lse, s_m, &sy);
+      else
+        ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
+    } else if constexpr (kLse) {
+      ctl_lse(a, f, lse, s_m, &sy);  // no workgroup waits for another
+    } else if (decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks) == kFusedGo) {
+      ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
+    } else {
       lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
-  } else if (wave == kSW + 1) {
-    ctl_memory<D>(a, Q, votes, s_q, s_votes, &sy);
-  } else if (wave == kSW + 2) {
+    }
+  } else if (wave == kMemWave) {
+    ctl_memory<D>(a, !f.on, Q, votes, s_q, s_votes, &sy);
+  } else if (wave == kPubWave) {
     if constexpr (!kLse) ctl_publish(a, ex, s_maxp, s_zp, &sy);
+  } else if (wave == kSelWave) {
+    if (f.on) ctl_select(a, f, votes, s_votes, &sy);
   } else {
     uint4* buf = s_ring[wave][0];
     float4* sx = s_x[wave];
@@ -883,14 +2095,23 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   }
   // Every wave's loads have landed before LDS is reused or the wave ends.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  KVSEL_FUSED_MARK(23, 1);
   __syncthreads();
-  if constexpr (!kLse) {
-    if (sy.abort) {  // not all resident: whole heads, one workgroup each
+  KVSEL_FUSED_MARK(23, 2);
+  if (sy.abort) {  // not all resident
+    if (f.on) {    // work from counters: statistics, votes, whole rows' selections
+      sel_fallback<D, kLse>(a, f, Q, K, lse, ex, votes, row_stats, s_ring[0], s_q[0], s_maxp[0], s_zp[0], s_m[0],
+                            reinterpret_cast<uint32_t*>(&s_x[0][0]));
+      return;
+    }
+    if constexpr (!kLse) {  // whole heads, one workgroup each
       solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz);
       return;
     }
   }
-  if (threadIdx.x == 0 && sy.timeout) raise_error(a.err, kErrLdsWait);
+  if (f.on) sel_finish<D>(a, f, K, votes, reinterpret_cast<uint32_t*>(&s_x[0][0]));  // the selection's end phase
+  KVSEL_FUSED_MARK(23, 3);
+  if (threadIdx.x == 0 && sy.timeout) flag_error(a, f, kErrLdsWait);
 }
 
 __global__ void fill_u32_kernel(unsigned* p, long long n, unsigned v) {
@@ -968,14 +2189,14 @@ int grid_for() {
 }
 
 template <int D, bool kLse>
-hipError_t launch_t(const Launch& a, const void* Q, const void* K, const float* lse, unsigned long long* ex,
-                    unsigned* status, float* votes, float* row_stats, hipStream_t st) {
+hipError_t launch_t(const Launch& a, const FusedSel& f, const void* Q, const void* K, const float* lse,
+                    unsigned long long* ex, unsigned* status, float* votes, float* row_stats, hipStream_t st) {
   const int grid = grid_for<D, kLse>();
-  if (grid <= 0) return hipErrorNotSupported;
+  if (grid <= 0 || grid > kFlagWordsMax) return hipErrorNotSupported;
   Launch la = a;
   const __bf16* q = (const __bf16*)Q;
   const __bf16* k = (const __bf16*)K;
-  hipLaunchKernelGGL((window_fused_kernel<D, kLse>), dim3(grid), dim3(kThreads), 0, st, la, q, k, lse, ex, status,
+  hipLaunchKernelGGL((window_fused_kernel<D, kLse>), dim3(grid), dim3(kThreads), 0, st, la, f, q, k, lse, ex, status,
                      votes, row_stats);
   return hipGetLastError();
 }
@@ -998,16 +2219,18 @@ int fused_grid(int W, int D) {
 int fused_exchange_bytes() { return kSlotWords * 8; }
 
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* ex,
-                                unsigned* status, float* votes, float* row_stats, hipStream_t st) {
+                                unsigned* status, float* votes, float* row_stats, const FusedSel& sel,
+                                hipStream_t st) {
   if (a.W > 32 || a.S != kS) return hipErrorNotSupported;
+  if (sel.on && (!fused_select_kernel_ok(a.kernel) || a.group > 1)) return hipErrorNotSupported;
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(ex);
   if (lse != nullptr) {
-    if (a.D == 128) return launch_t<128, true>(a, Q, K, lse, slots, status, votes, nullptr, st);
-    if (a.D == 64) return launch_t<64, true>(a, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 128) return launch_t<128, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 64) return launch_t<64, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
     return hipErrorNotSupported;
   }
-  if (a.D == 128) return launch_t<128, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
-  if (a.D == 64) return launch_t<64, false>(a, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 128) return launch_t<128, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 64) return launch_t<64, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
   return hipErrorNotSupported;
 }
 

@@ -86,6 +86,29 @@ enum : unsigned {
 // every call), word kStickyWord the OR of every call's flags since the
 // caller last reset it (kvsel_status_flags).
 constexpr int kStickyWord = 4;
+// Calls that clear nothing before they start (the fused selection) record
+// their flags in the 64-bit header word at byte 8 instead of word 0:
+// (tag << 24) | flags, where tag identifies the call (token_tag); a flag
+// word whose tag is not the last call's carries none of its flags.
+constexpr int kTaggedWord = 2;  // in 32-bit words: bytes 8..15
+__host__ __device__ inline unsigned long long token_tag(unsigned long long token) {
+  return (token >> 2) & ((1ull << 40) - 1);
+}
+__device__ inline void raise_tagged(unsigned long long* w, unsigned long long token, unsigned bit) {
+  const unsigned long long tag = token_tag(token);
+  unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const unsigned long long nv = (cur >> 24) == tag ? (cur | bit) : ((tag << 24) | bit);
+    if (nv == cur) break;
+    unsigned long long expect = cur;
+    if (__hip_atomic_compare_exchange_strong(w, &expect, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+    cur = expect;
+  }
+  unsigned* sticky = reinterpret_cast<unsigned*>(w) - kTaggedWord + kStickyWord;
+  __hip_atomic_fetch_or(sticky, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline void raise_error(unsigned* err, unsigned bit) {
   if (err != nullptr) {
     __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -243,6 +266,40 @@ __device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* 
   return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
 }
 
+// The selection fused into the single-read scoring kernel (pooling, top-k,
+// window, K/V copy), and its words in the workspace.  Shared words are
+// cleared by the workgroups that own them before they arrive; the arrival
+// and residency decision carry a per-call token instead of starting from
+// zero, so the call needs no fill launch.
+constexpr int kHaloWords = 8;           // per chunk: its first 3 and last 3 votes, tagged
+
+struct FusedSel {
+  int on;                       // 1: select in the scoring kernel (the arrays below are used)
+  int force_abort;              // testing: decide ABORT at once
+  unsigned long long token;     // this call's token (low two bits zero)
+  unsigned long long* errw;     // the header's tagged flag word (kTaggedWord)
+  unsigned long long* flags;    // [grid] arrival tokens, then the decision word, then 3 claim counters
+  unsigned long long* cw;       // [exchange slot] the chunk's count word
+  unsigned long long* halo;     // [exchange slot][kHaloWords]
+  unsigned long long* clr[2];   // ranges of 8-byte words every call clears (a share per workgroup)
+  long long clr_words[2];
+  unsigned* cslot;              // [exchange slot][64] the chunk's coarse histogram, count + 1
+  unsigned* fslot;              // [exchange slot][32] its fine histogram inside the coarse bin of tau, count + 1
+  unsigned long long* rowfb;    // [row][2] fallback completion counters (token-tagged)
+  unsigned long long* cand;     // candidates, indexed like the votes
+  float* pooled;                // optional pooled scores out (indexed like the votes), or nullptr
+  float* kslot;                 // [exchange slot][512] the chunk's pooled scores, kept for the end phase
+  int32_t* indices;
+  const void* V;
+  void* K_out;
+  void* V_out;
+};
+constexpr int kFlagWordsMax = 1024;     // arrival tokens of a grid of up to this many workgroups
+constexpr int kFusedMaxRounds = 2048;   // rounds of one fused-selection launch
+constexpr int kFusedFlagWords = kFlagWordsMax + 8;
+// Pooling widths the fused selection covers (radius up to 3).
+__host__ __device__ inline bool fused_select_kernel_ok(int kernel) { return kernel >= 1 && kernel <= 7 && kernel % 2 == 1; }
+
 int fused_positions(int W, int D);
 int fused_grid(int W, int D);
 int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
@@ -251,8 +308,11 @@ int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
 __host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64 * 64; }
 // With lse != nullptr (as for launch_window_votes) the workgroups exchange
 // nothing and need not be co-resident: exchange and status are not used.
+// With sel.on the kernel also selects: indices and K/V rows are written, and
+// exchange, sel's arrays and status need no clearing (status is unused).
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* exchange,
-                                unsigned* status, float* votes, float* row_stats, hipStream_t st);
+                                unsigned* status, float* votes, float* row_stats, const FusedSel& sel,
+                                hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
 // Zero up to kZeroRanges byte ranges in one launch (16-byte aligned pointers
 // and sizes, else hipErrorInvalidValue; empty ranges are skipped).

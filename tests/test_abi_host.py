@@ -47,10 +47,16 @@ def test_workspace_sizes(B):
     # status words (error flags, decision, fallback counter and 16 arrival
     # counters on lines of their own), first-digit histograms, the
     # cooperative selection's status words and per-row words (histograms,
-    # segment counts, candidate entries)
+    # segment counts, candidate entries); then the fused selection's words:
+    # a count word and 8 halo words per exchange slot, the arrival tokens,
+    # decision and claim counters, per exchange slot 64 + 32 histogram words,
+    # per row two completion counters, 8-byte candidates laid out like the
+    # votes, and per exchange slot the chunk's 512 pooled scores
     expect_min = (256 + 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128 + 8192) * 4)
-    assert expect_min <= n <= expect_min + 7 * 256
+                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128 + 8192) * 4
+                  + 32 * 64 * 8 + 32 * 64 * 8 * 8 + (1024 + 8) * 8 + 32 * 64 * (64 + 32) * 4 + 32 * 2 * 8
+                  + 32 * (32768 - 32) * 8 + 32 * 64 * 512 * 4)
+    assert expect_min <= n <= expect_min + 13 * 256
     assert n % 256 == 0
     assert B.lib.kvsel_workspace_bytes(32, 100, 32, 32, 128, 1) == 0  # C <= W
     assert "budget" in B.kvsel_last_error()
@@ -225,6 +231,9 @@ def test_options(B):
     assert lib.kvsel_set_option(1, 0) == 0 and lib.kvsel_get_option(1) == 0
     assert lib.kvsel_set_option(4, 0) == -1
     assert lib.kvsel_get_option(5) == -1
-    assert lib.kvsel_set_option(3, 0) == -1
+    assert lib.kvsel_get_option(3) == 0                       # fused selection off
+    assert lib.kvsel_set_option(3, 2) == -1
+    assert lib.kvsel_set_option(3, 1) == 0 and lib.kvsel_get_option(3) == 1
+    assert lib.kvsel_set_option(3, 0) == 0 and lib.kvsel_get_option(3) == 0
     assert lib.kvsel_set_option(0, 1) == 0 and lib.kvsel_get_option(0) == 1
     assert lib.kvsel_set_option(0, 0) == 0 and lib.kvsel_get_option(0) == 0
