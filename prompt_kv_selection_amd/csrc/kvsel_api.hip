@@ -139,7 +139,7 @@ unsigned long long next_token() {
 // the call cleared word 0 (then word 0 holds its flags) and its token (the
 // tagged word holds its flags when the tags match).
 struct LastCall {
-  bool cleared = false;
+  bool cleared = false;  // the header was zeroed before the call
   unsigned long long token = 0;
 };
 std::mutex g_calls_mu;
@@ -461,7 +461,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     z.p[1] = ws + lo1;
     z.bytes[1] = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
     z.p[2] = ws + p.off_coop;
-    z.bytes[2] = any_coop ? (long long)(p.bytes - p.off_coop) : 0;
+    z.bytes[2] = any_coop ? (long long)(p.off_cw - p.off_coop) : 0;  // the fused selection's words follow
     hipError_t e = timed("fill", st, [&] { return launch_zero(z, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");
   }

@@ -120,6 +120,7 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kSW = 8;                    // streaming waves (two per SIMD)
 constexpr int kThreads = (kSW + 4) * 64;  // plus the exchange, memory, publisher and selection waves
+constexpr int kThreadsPlain = (kSW + 3) * 64;  // without the selection wave
 constexpr int kExWave = kSW, kMemWave = kSW + 1, kPubWave = kSW + 2, kSelWave = kSW + 3;
 constexpr int kTT = 2;                    // 32-position tiles per streaming wave per round
 constexpr int kNBuf = 1;                  // K tiles in flight per streaming wave
@@ -197,9 +198,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo
 }
 
 // A flag of the call: the tagged word when nothing was cleared before the
-// call (fused selection), else the header's flag word.
+// call (the fused selection), else the header's flag word.
 __device__ __forceinline__ void flag_error(const Launch& a, const FusedSel& f, unsigned bit) {
-  if (f.on)
+  if (f.token != 0ull)
     raise_tagged(f.errw, f.token, bit);
   else
     raise_error(a.err, bit);
@@ -216,6 +217,24 @@ __device__ __forceinline__ unsigned load32(const unsigned* p) {
 }
 __device__ __forceinline__ void store32(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Token-tagged counters: (tag << 24) | count, where a word whose tag is not
+// this call's counts as zero.  Claim returns the count before the claim.
+__device__ __forceinline__ unsigned tok_claim(unsigned long long* w, unsigned long long tag) {
+  unsigned long long cur = load64(w);
+  for (;;) {
+    const unsigned cnt = (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
+    unsigned long long expect = cur;
+    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + 1u),
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return cnt;
+    cur = expect;
+  }
+}
+__device__ __forceinline__ unsigned tok_count(const unsigned long long* w, unsigned long long tag) {
+  const unsigned long long cur = load64(w);
+  return (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
 }
 
 // ---- exchange slots in the workspace, zeroed per call: per (sequence,
@@ -646,8 +665,8 @@ __device__ __forceinline__ void ctl_publish(const Launch& a, unsigned long long*
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   unsigned on_b[kNR] = {};  // owned rounds awaited so far, per residue
-  // The slots this workgroup writes are clear: its own clears (separate
-  // selection), or every workgroup's (fused selection: GO).
+  // The slots this workgroup writes are clear: cleared before the launch, or
+  // with the fused selection by every workgroup before the decision (GO).
   if (!lds_wait_ge(sy, &sy->zeroed, 1u)) return;
   for (int k = 0; k < a.rounds; ++k) {
     const Work w0 = round_work(a, k);
@@ -1612,24 +1631,6 @@ __device__ __forceinline__ void sel_finish(const Launch& a, const FusedSel& f, c
 
 // ---- fallback of the fused selection (ABORT: not all resident)
 
-// Token-tagged counters: (tag << 24) | count, where a word whose tag is not
-// this call's counts as zero.  Claim returns the count before the claim.
-__device__ __forceinline__ unsigned tok_claim(unsigned long long* w, unsigned long long tag) {
-  unsigned long long cur = load64(w);
-  for (;;) {
-    const unsigned cnt = (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
-    unsigned long long expect = cur;
-    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + 1u),
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      return cnt;
-    cur = expect;
-  }
-}
-__device__ __forceinline__ unsigned tok_count(const unsigned long long* w, unsigned long long tag) {
-  const unsigned long long cur = load64(w);
-  return (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
-}
-
 // Inclusive scan over the workgroup (kThreads); total gets the sum.
 __device__ __forceinline__ uint32_t wg_incl(uint32_t v, uint32_t* sh, uint32_t& total) {
   constexpr int kWv = kThreads / 64;
@@ -1977,8 +1978,8 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
   (void)lane;
 }
 
-template <int D, bool kLse>
-__global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch a, const FusedSel f,
+template <int D, bool kLse, bool kSel>
+__global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fused_kernel(const Launch a, const FusedSel f,
                                                                   const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,
                                                                   const float* __restrict__ lse,
@@ -1999,16 +2000,17 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   const int lane = threadIdx.x & 63;
   KVSEL_FUSED_MARK(23, 0);
   unsigned arrived = 0u;
-  if (!f.on && !kLse && wave == kExWave && lane == 0) arrived = arrive(status);
+  if (!kSel && !kLse && wave == kExWave && lane == 0) arrived = arrive(status);
   if (threadIdx.x == 0) {
     sy = Sync{};
-    sy.zeroed = f.on ? 0u : 1u;
+    sy.zeroed = kSel ? 0u : 1u;
   }
   __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
-  // The clears of the fused selection's shared words go first, so that they
-  // do not queue behind the K tiles; then the first K tiles and Qwin of
+  // With the fused selection the clears of the shared words go first, so
+  // that they do not queue behind the K tiles (the decision that follows them
+  // gates the publication of every round); then the first K tiles and Qwin of
   // rounds 0 and 1.
-  if (f.on) {
+  if constexpr (kSel) {
     if (wave == kExWave) {
       KVSEL_FUSED_MARK(22, 0);
       sel_clear(f);
@@ -2028,7 +2030,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
   if (wave == kExWave) {
-    if (f.on) {
+    if constexpr (kSel) {
       // Arrive once the clears are done, decide; then the statistics.
       sel_arrive(f);
       KVSEL_FUSED_MARK(22, 2);
@@ -2046,17 +2048,21 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
         ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
     } else if constexpr (kLse) {
       ctl_lse(a, f, lse, s_m, &sy);  // no workgroup waits for another
-    } else if (decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks) == kFusedGo) {
-      ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
     } else {
-      lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
+      KVSEL_FUSED_MARK(23, 4);
+      const unsigned d = decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks);
+      KVSEL_FUSED_MARK(23, 5);
+      if (d == kFusedGo)
+        ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
+      else
+        lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
     }
   } else if (wave == kMemWave) {
-    ctl_memory<D>(a, !f.on, Q, votes, s_q, s_votes, &sy);
+    ctl_memory<D>(a, !kSel, Q, votes, s_q, s_votes, &sy);
   } else if (wave == kPubWave) {
     if constexpr (!kLse) ctl_publish(a, ex, s_maxp, s_zp, &sy);
   } else if (wave == kSelWave) {
-    if (f.on) ctl_select(a, f, votes, s_votes, &sy);
+    if constexpr (kSel) ctl_select(a, f, votes, s_votes, &sy);
   } else {
     uint4* buf = s_ring[wave][0];
     float4* sx = s_x[wave];
@@ -2099,7 +2105,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
   __syncthreads();
   KVSEL_FUSED_MARK(23, 2);
   if (sy.abort) {  // not all resident
-    if (f.on) {    // work from counters: statistics, votes, whole rows' selections
+    if constexpr (kSel) {  // work from counters: statistics, votes, whole rows' selections
       sel_fallback<D, kLse>(a, f, Q, K, lse, ex, votes, row_stats, s_ring[0], s_q[0], s_maxp[0], s_zp[0], s_m[0],
                             reinterpret_cast<uint32_t*>(&s_x[0][0]));
       return;
@@ -2109,7 +2115,7 @@ __global__ __launch_bounds__(kThreads, 1) void window_fused_kernel(const Launch 
       return;
     }
   }
-  if (f.on) sel_finish<D>(a, f, K, votes, reinterpret_cast<uint32_t*>(&s_x[0][0]));  // the selection's end phase
+  if constexpr (kSel) sel_finish<D>(a, f, K, votes, reinterpret_cast<uint32_t*>(&s_x[0][0]));  // the selection's end phase
   KVSEL_FUSED_MARK(23, 3);
   if (threadIdx.x == 0 && sy.timeout) flag_error(a, f, kErrLdsWait);
 }
@@ -2164,11 +2170,13 @@ __global__ void check_finite_f32_kernel(const float* __restrict__ p, long long n
 
 struct GridCache {
   int device = -1;
-  int grid[2][2] = {{-1, -1}, {-1, -1}};
+  int grid[2][2][2] = {};  // [kSel][kLse][D == 128], 0: not looked up yet (-1: does not fit)
 };
 GridCache g_grid;
 
-template <int D, bool kLse>
+// One workgroup per CU when the kernel fits a CU at all (the same grid for
+// every variant of a head size: the workgroups of a call must all fit).
+template <int D, bool kLse, bool kSel>
 int grid_for() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -2176,29 +2184,36 @@ int grid_for() {
     g_grid = GridCache{};
     g_grid.device = dev;
   }
-  int& slot = g_grid.grid[kLse][D == 128];
-  if (slot < 0) {
+  int& slot = g_grid.grid[kSel][kLse][D == 128];
+  if (slot == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_fused_kernel<D, kLse>, kThreads, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_fused_kernel<D, kLse, kSel>,
+                                                     kSel ? kThreads : kThreadsPlain, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    slot = per_cu >= 1 ? cus : 0;
+    slot = per_cu >= 1 ? cus : -1;
   }
-  return slot;
+  return slot > 0 ? slot : 0;
 }
 
-template <int D, bool kLse>
+template <int D, bool kLse, bool kSel>
 hipError_t launch_t(const Launch& a, const FusedSel& f, const void* Q, const void* K, const float* lse,
                     unsigned long long* ex, unsigned* status, float* votes, float* row_stats, hipStream_t st) {
-  const int grid = grid_for<D, kLse>();
+  const int grid = grid_for<D, kLse, kSel>();
   if (grid <= 0 || grid > kFlagWordsMax) return hipErrorNotSupported;
   Launch la = a;
   const __bf16* q = (const __bf16*)Q;
   const __bf16* k = (const __bf16*)K;
-  hipLaunchKernelGGL((window_fused_kernel<D, kLse>), dim3(grid), dim3(kThreads), 0, st, la, f, q, k, lse, ex, status,
-                     votes, row_stats);
+  hipLaunchKernelGGL((window_fused_kernel<D, kLse, kSel>), dim3(grid), dim3(kSel ? kThreads : kThreadsPlain), 0, st,
+                     la, f, q, k, lse, ex, status, votes, row_stats);
   return hipGetLastError();
+}
+
+template <int D, bool kLse>
+hipError_t launch_d(const Launch& a, const FusedSel& f, const void* Q, const void* K, const float* lse,
+                    unsigned long long* ex, unsigned* status, float* votes, float* row_stats, hipStream_t st) {
+  if (f.on) return launch_t<D, kLse, true>(a, f, Q, K, lse, ex, status, votes, row_stats, st);
+  return launch_t<D, kLse, false>(a, f, Q, K, lse, ex, status, votes, row_stats, st);
 }
 
 }  // namespace
@@ -2210,9 +2225,10 @@ int fused_positions(int W, int D) {
 
 int fused_grid(int W, int D) {
   if (W > 32) return 0;
-  // The variant with given row statistics has the same resources.
-  if (D == 128) return grid_for<128, false>();
-  if (D == 64) return grid_for<64, false>();
+  // The variants with given row statistics or the fused selection fit a CU
+  // the same way (checked at launch).
+  if (D == 128) return grid_for<128, false, false>();
+  if (D == 64) return grid_for<64, false, false>();
   return 0;
 }
 
@@ -2225,12 +2241,12 @@ hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, c
   if (sel.on && (!fused_select_kernel_ok(a.kernel) || a.group > 1)) return hipErrorNotSupported;
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(ex);
   if (lse != nullptr) {
-    if (a.D == 128) return launch_t<128, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
-    if (a.D == 64) return launch_t<64, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 128) return launch_d<128, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 64) return launch_d<64, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
     return hipErrorNotSupported;
   }
-  if (a.D == 128) return launch_t<128, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
-  if (a.D == 64) return launch_t<64, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 128) return launch_d<128, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 64) return launch_d<64, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
   return hipErrorNotSupported;
 }
 

@@ -232,11 +232,10 @@ __device__ inline unsigned arrive(unsigned* status) {
   unsigned* ctr = status + kArriveStride * (1 + arrival_group(flat_grid()));
   return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 }
-// Lane 0 of the calling wave decides; the decision is returned to every lane.
-// An ABORT is also recorded as fallback_bit in the call's flags (err).
-__device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* err, unsigned fallback_bit,
-                                  long long ticks) {
-  unsigned s = 0u;
+// The first half of the decision, once the arrival's count has returned:
+// the last arrival of a group counts the group, and the last group decides
+// GO.  Lane 0 of the calling wave acts.
+__device__ inline void decide_begin(unsigned* status, unsigned arrived) {
   if ((threadIdx.x & 63) == 0) {
     unsigned* groups = status + 1;
     unsigned* state = status + 2;
@@ -252,6 +251,15 @@ __device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* 
                                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+}
+// The second half: wait for the decision, deciding ABORT after the bound.
+// Lane 0 of the calling wave waits; the decision is returned to every lane.
+// An ABORT is also recorded as fallback_bit in the call's flags (err).
+__device__ inline unsigned decide_end(unsigned* status, unsigned* err, unsigned fallback_bit, long long ticks) {
+  unsigned s = 0u;
+  if ((threadIdx.x & 63) == 0) {
+    unsigned* state = status + 2;
     const long long t0 = wall_clock64();
     while ((s = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
       if (wall_clock64() - t0 > ticks) {
@@ -265,12 +273,18 @@ __device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* 
   }
   return (unsigned)__builtin_amdgcn_readfirstlane((int)s);
 }
+__device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* err, unsigned fallback_bit,
+                                  long long ticks) {
+  decide_begin(status, arrived);
+  return decide_end(status, err, fallback_bit, ticks);
+}
 
 // The selection fused into the single-read scoring kernel (pooling, top-k,
 // window, K/V copy), and its words in the workspace.  Shared words are
-// cleared by the workgroups that own them before they arrive; the arrival
-// and residency decision carry a per-call token instead of starting from
-// zero, so the call needs no fill launch.
+// cleared by the kernel's workgroups, a share each, before they arrive; the
+// arrival and residency decision carry a per-call token instead of starting
+// from zero, and flags go to the tagged header word, so the call needs no
+// fill launch.
 constexpr int kHaloWords = 8;           // per chunk: its first 3 and last 3 votes, tagged
 
 struct FusedSel {

@@ -1047,6 +1047,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   __shared__ uint32_t s_ret[2048];                               // first-digit bins before this segment's adds
   __shared__ uint32_t s_cg[kCoopMaxSeg], s_ce[kCoopMaxSeg];      // candidates above / on tau per segment
   __shared__ unsigned long long s_cw[kCoopMaxSeg];                // the segments' count words
+  __shared__ uint32_t s_h7[3 * 128];                               // the candidate round's three 7-bit digits
   static_assert(kCandCap <= kCoopHalo, "candidate keys alias sv");
   static_assert(kCandCap < 65536, "a candidate range packs into 16-bit fields");
   static_assert(kCoopPer == 8, "the window ranks below use 8 positions per thread");
@@ -1095,13 +1096,20 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   unsigned long long* cbuf = cnt + kCoopMaxSeg;  // the candidate round's entries (position + 1, key)
   uint32_t key[kCoopPer];
   auto valid_of = [&](int g) { return max(0, min(kCoopPer, P - g * kCoopSeg - tid * kCoopPer)); };
-  // The own segment's keys and their first-digit histogram depend on no
-  // other workgroup: computed before the decision.
+  // The own segment's keys, their first-digit histogram and its adds into
+  // the row's histogram depend on no other workgroup: they overlap the
+  // decision, whose group step is taken as soon as the keys are in.  After
+  // an ABORT nothing reads the row's histogram: the fallback builds its
+  // histograms in LDS.
+  if (seg < nseg) coop_keys<KW, MAX>(v, P, seg, sv, key);
+  KVSEL_SELROWS_MARK(14);
+  if (tid == 0) decide_begin(status, arrived);
   if (seg < nseg) {
-    coop_keys<KW, MAX>(v, P, seg, sv, key);
     coop_local_hist(key, valid_of(seg), 21, 11, 0u, true, hist);
+    coop_push_hist(11, hist, gh1, s_ret);
   }
-  if (tid == 0) s_go = decide(status, arrived, a.err, kFlagSelectFallback, a.residency_ticks);
+  KVSEL_SELROWS_MARK(15);
+  if (tid == 0) s_go = decide_end(status, a.err, kFlagSelectFallback, a.residency_ticks);
   __syncthreads();
   const bool go = s_go == kFusedGo;
   KVSEL_SELROWS_MARK(1);
@@ -1117,21 +1125,41 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     const int shift = digit == 0 ? 21 : (digit == 1 ? 10 : 0);
     const int bits = digit == 2 ? 10 : 11;
     uint32_t* gh = digit == 0 ? gh1 : (digit == 1 ? gh2 : gh3);
-    for (int g = g0; g < g1; ++g) {
-      if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
+    uint32_t* rh = hist;  // the row's histogram of the digit (LDS)
+    if (go) {
       if (digit == 0 && pooled != nullptr) {
-        float* o = pooled + s.vote_off + (long long)h * s.vote_ld + g * kCoopSeg + tid * kCoopPer;
-        const int n = valid_of(g);
+        float* o = pooled + s.vote_off + (long long)h * s.vote_ld + seg * kCoopSeg + tid * kCoopPer;
+        const int n = valid_of(seg);
 #pragma unroll
         for (int u = 0; u < kCoopPer; ++u)
           if (u < n) o[u] = __uint_as_float(key[u]);
       }
-      if (!(go && digit == 0)) coop_local_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist);  // else done
-      coop_push_hist(bits, hist, gh, go && digit == 0 ? s_ret : nullptr);
+      if (digit > 0) {  // the first digit's adds are in
+        coop_local_hist(key, valid_of(seg), shift, bits, prefix, false, hist);
+        coop_push_hist(bits, hist, gh, nullptr);
+      }
+      coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, a.err);
+    } else {
+      // One workgroup runs every segment of the row: the row's histogram is
+      // summed in LDS (s_ret), segment by segment.
+      rh = s_ret;
+      for (int d = tid; d < (1 << bits); d += kCoopThreads) rh[d] = 0u;
+      for (int g = 0; g < nseg; ++g) {
+        coop_keys<KW, MAX>(v, P, g, sv, key);  // begins with a barrier: rh is cleared or summed
+        if (digit == 0 && pooled != nullptr) {
+          float* o = pooled + s.vote_off + (long long)h * s.vote_ld + g * kCoopSeg + tid * kCoopPer;
+          const int n = valid_of(g);
+#pragma unroll
+          for (int u = 0; u < kCoopPer; ++u)
+            if (u < n) o[u] = __uint_as_float(key[u]);
+        }
+        coop_local_hist(key, valid_of(g), shift, bits, prefix, digit == 0, hist);
+        for (int d = tid; d < (1 << bits); d += kCoopThreads) rh[d] += hist[d];
+      }
+      __syncthreads();
     }
-    coop_read_hist<kCoopThreads>(gh, 1 << bits, total, hist, sh, a.err);
-    pick_digit<kCoopThreads>(hist, 1 << bits, need, sh, &s_digit, &s_need);
-    total = hist[s_digit];
+    pick_digit<kCoopThreads>(rh, 1 << bits, need, sh, &s_digit, &s_need);
+    total = rh[s_digit];
     prefix = (prefix << bits) | s_digit;
     need = s_need;
     __syncthreads();  // hist is rewritten by the next digit
@@ -1173,24 +1201,42 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     }
     __syncthreads();  // sv becomes the candidate keys
     KVSEL_SELROWS_MARK(3);
+    for (int i = tid; i < 3 * 128; i += kCoopThreads) s_h7[i] = 0u;  // the digits' bins (below)
     coop_read_candidates(cnt, nseg, cbuf, (int)total, s_cw, ck, sh, a.err);
     KVSEL_SELROWS_MARK(4);
-    // The last two digits of tau over the candidates, in LDS.
-    for (int digit = 1; digit < 3; ++digit) {
-      const int shift = digit == 1 ? 10 : 0;
-      const int bits = digit == 1 ? 11 : 10;
-      const int nb = 1 << bits;
-      for (int d = tid; d < nb; d += kCoopThreads) hist[d] = 0u;
-      __syncthreads();
-      for (int i = tid; i < (int)total; i += kCoopThreads)
-        if ((ck[i] >> (shift + bits)) == prefix) atomicAdd(&hist[(ck[i] >> shift) & (uint32_t)(nb - 1)], 1u);
-      __syncthreads();
-      KVSEL_SELROWS_MARK(6 + 2 * digit);
-      pick_digit<kCoopThreads>(hist, nb, need, sh, &s_digit, &s_need);
-      prefix = (prefix << bits) | s_digit;
-      need = s_need;
-      __syncthreads();
-      KVSEL_SELROWS_MARK(7 + 2 * digit);
+    {
+      // The other 21 bits of tau in three digits of 7 bits over the
+      // candidates: each digit's 128-bin histogram (LDS atomics), then one
+      // wave finds the bin holding the need-th largest.  Two barriers a digit.
+      uint32_t t = prefix << 21;
+      for (int dg = 0; dg < 3; ++dg) {
+        const int shift = 14 - 7 * dg;
+        const uint32_t hi = ~((1u << (shift + 7)) - 1u);  // tau's bits found so far
+        uint32_t* h7 = s_h7 + 128 * dg;
+        for (int i = tid; i < (int)total; i += kCoopThreads)
+          if ((ck[i] & hi) == t) atomicAdd(&h7[(ck[i] >> shift) & 127u], 1u);
+        __syncthreads();
+        if (tid < 64) {  // lane l: bins 127 - 2l and 126 - 2l, highest first
+          const uint32_t a0 = h7[127 - 2 * lane], a1 = h7[126 - 2 * lane];
+          uint32_t incl = a0 + a1;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t x = __shfl_up(incl, o);
+            if (lane >= o) incl += x;
+          }
+          const uint32_t excl = incl - a0 - a1;
+          if (excl < need && need <= incl) {
+            const bool first = excl + a0 >= need;
+            s_digit = first ? 127u - 2u * lane : 126u - 2u * lane;
+            s_need = first ? need - excl : need - excl - a0;
+          }
+        }
+        __syncthreads();
+        t |= s_digit << shift;
+        need = s_need;
+      }
+      prefix = t;
+      KVSEL_SELROWS_MARK(11);
     }
     // Every segment's candidates above and on tau: a wave per segment over
     // the segment's range of candidates.
@@ -1272,27 +1318,37 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     s_pre[tid] = p_incl - mine_picks;  // picks before segment tid
   }
   __syncthreads();
+  KVSEL_SELROWS_MARK(5);
   for (int g = g0; g < g1; ++g) {
     if (!go) coop_keys<KW, MAX>(v, P, g, sv, key);
     const uint32_t before = s_pre[g], eq_before = s_cnt[g];
-    uint32_t eq = 0;
+    // One scan of both counts (each at most kCoopSeg < 2^16): keys above tau
+    // and tau-equal keys before this thread's first position.  Tau-equal
+    // positions are picked in index order while the row still needs them,
+    // the first `left` of this segment's.
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int u = 0; u < kCoopPer; ++u) eq += g * kCoopSeg + tid * kCoopPer + u < P && key[u] == tau;
+    for (int u = 0; u < kCoopPer; ++u) {
+      const bool valid = g * kCoopSeg + tid * kCoopPer + u < P;
+      gt += valid && key[u] > tau;
+      eq += valid && key[u] == tau;
+    }
     uint32_t tot;
-    const uint32_t eqb = eq_before + block_scan<kCoopThreads>(eq, sh, tot) - eq;  // tau-equal before my first
+    const uint32_t excl = block_scan<kCoopThreads>(gt | (eq << 16), sh, tot) - (gt | (eq << 16));
+    const uint32_t gtb = excl & 0xFFFFu, eqb = excl >> 16;
+    const uint32_t left = need_eq > eq_before ? need_eq - eq_before : 0u;
     uint32_t pm = 0, seen = eqb;
 #pragma unroll
     for (int u = 0; u < kCoopPer; ++u) {
       const bool valid = g * kCoopSeg + tid * kCoopPer + u < P;
       if (valid && key[u] > tau) pm |= 1u << u;
       if (valid && key[u] == tau) {
-        if (seen < need_eq) pm |= 1u << u;
+        if (seen < left) pm |= 1u << u;
         ++seen;
       }
     }
-    const uint32_t np = (uint32_t)__popc(pm);
-    uint32_t ntot;
-    uint32_t off = block_scan<kCoopThreads>(np, sh, ntot) - np;
+    const uint32_t ntot = (tot & 0xFFFFu) + min(tot >> 16, left);
+    uint32_t off = gtb + min(eqb, left);
 #pragma unroll
     for (int u = 0; u < kCoopPer; ++u)
       if ((pm >> u) & 1u) {
@@ -1301,6 +1357,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
         picks[off++] = j;
       }
     __syncthreads();
+    KVSEL_SELROWS_MARK(6);
     if (RU > 0) copy((int)before, (int)ntot, 0, picks);
     if (g == nseg - 1 && W > 0) {  // the window follows the picks
       for (int i = tid; i < W; i += kCoopThreads) out[count + i] = P + i;
