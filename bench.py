@@ -42,12 +42,13 @@ def seq_shapes(w):
     return [(w.L, w.C)]
 
 
-def kernel_alg_bytes(name, w, lse=False, group=1, seqs=None):
-    """Algorithmic bytes one launch of a kernel moves for one layer call over
-    the sequences seqs [(L, C)] (lse: the row statistics are handed over, so
-    only the prefix keys, Qwin and the W log-sum-exps per head are read for
-    the votes; group: query heads per K/V head, whose K is read once for the
-    whole group)."""
+def kernel_alg_bytes(name, w, lse=False, group=1, seqs=None, rows=False):
+    """Algorithmic bytes one launch of a kernel moves for one call of w.heads
+    heads over the sequences seqs [(L, C)] (lse: the row statistics are handed
+    over, so only the prefix keys, Qwin and the W log-sum-exps per head are
+    read for the votes; group: query heads per K/V head, whose K is read once
+    for the whole group; rows: the selection ran one workgroup per row and
+    the gather kernel copied the rows)."""
     e = 2 if w.dtype == "bf16" else 4
     H, W, D = w.heads, w.W, w.D
     seqs = seqs or seq_shapes(w)
@@ -78,8 +79,12 @@ def kernel_alg_bytes(name, w, lse=False, group=1, seqs=None):
         return len(seqs) * H * (2048 * 4 + 2 * 512 * 4)
     if name == "emit":              # pooled scores, kept K and V rows read and written, indices
         return H * sumP * 4 + 4 * H * sumC * D * e + H * sumC * 4
+    if name == "select" and rows:   # whole rows: pooled scores read, indices written (the copy is gather's)
+        return H * sumP * 4 + H * sumC * 4
     if name == "select":            # votes read, indices written, kept K and V rows read and written
         return H * sumP * 4 + H * sumC * 4 + 4 * H * sumC * D * e
+    if name == "gather":            # indices read, kept K and V rows read and written
+        return H * sumC * 4 + 4 * H * sumC * D * e
     return None                     # fill: workspace clearing, not the method's traffic
 
 
@@ -585,6 +590,9 @@ def main():
                     help="time the Jacap eviction event instead: 32 heads of N cached tokens per layer call")
     ap.add_argument("--streams", type=int, default=1,
                     help="with --jacap: independent layer calls spread over this many streams (own workspaces)")
+    ap.add_argument("--fold", action="store_true",
+                    help="all layers of a step in one call of layers x heads query heads (the per-layer calls "
+                         "stay the headline)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     ap.add_argument("--digest", nargs=3, metavar=("TAG", "NAME", "TITLE"),
@@ -623,8 +631,10 @@ def main():
     G = args.gqa
     if G < 1 or H % G:
         raise SystemExit(f"--gqa must divide the {H} heads")
-    if w.ragged and (G > 1 or args.lse):
-        raise SystemExit("--gqa and --lse time single-length workloads")
+    if w.ragged and (G > 1 or args.lse or args.fold):
+        raise SystemExit("--gqa, --lse and --fold time single-length workloads")
+    if args.fold and (G > 1 or args.lse):
+        raise SystemExit("--fold times the computed-statistics path of one query head per K/V head")
     Hkv = H // G
     stream = torch.cuda.current_stream()
 
@@ -650,8 +660,15 @@ def main():
         Ks.append(conv(K))
         Vs.append(conv(V))
         del Q, K, V
+    # Folded: the layers' heads side by side, one call per step.
+    wc = w
+    if args.fold:
+        Qs, Ks, Vs = [torch.cat(Qs, 0)], [torch.cat(Ks, 0)], [torch.cat(Vs, 0)]
+        wc = WL.reduced(w, name=w.name, heads=H * layers, layers=1)
     torch.cuda.synchronize()
     log(f"inputs resident in HBM after {time.time() - t0:.1f} s")
+    calls = 1 if args.fold else layers  # calls per step
+    Hc = wc.heads                       # query heads per call
 
     cuL = [0]
     for L, _ in seqs:
@@ -665,10 +682,10 @@ def main():
         Vo = [torch.empty((H * sum(Cs), D), dtype=td, device=dev) for _ in range(layers)]
     else:
         L, C = seqs[0]
-        ws_bytes = B.kvsel_gqa_workspace_bytes(H, Hkv, L, W, C, D, td)
-        idx = [torch.empty((H, C), dtype=torch.int32, device=dev) for _ in range(layers)]
-        Ko = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
-        Vo = [torch.empty((H, C, D), dtype=td, device=dev) for _ in range(layers)]
+        ws_bytes = B.kvsel_gqa_workspace_bytes(Hc, Hc // G, L, W, C, D, td)
+        idx = [torch.empty((Hc, C), dtype=torch.int32, device=dev) for _ in range(calls)]
+        Ko = [torch.empty((Hc, C, D), dtype=td, device=dev) for _ in range(calls)]
+        Vo = [torch.empty((Hc, C, D), dtype=td, device=dev) for _ in range(calls)]
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[args.scoring])
     B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 1 if args.force_fallback else 0)
@@ -685,7 +702,7 @@ def main():
         log("row log-sum-exps of every layer ready")
 
     def step():
-        for layer in range(layers):
+        for layer in range(calls):
             if w.ragged:
                 B.kvsel_select_varlen(Qs[layer], Ks[layer], Vs[layer], cuL, Cs, W, D, H, w.kernel, w.pooling, td,
                                       idx[layer], Ko[layer], Vo[layer], None, None, None, ws, stream=stream)
@@ -699,7 +716,7 @@ def main():
                 B.kvsel_select_lse(Qs[layer], Ks[layer], Vs[layer], lses[layer], L, W, C, D, H, w.kernel,
                                    w.pooling, td, idx[layer], Ko[layer], Vo[layer], None, None, ws, stream=stream)
             else:
-                B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, H, w.kernel, w.pooling, td,
+                B.kvsel_select(Qs[layer], Ks[layer], Vs[layer], L, W, C, D, Hc, w.kernel, w.pooling, td,
                                idx[layer], Ko[layer], Vo[layer], None, None, None, ws, stream=stream)
 
     for _ in range(args.warmup):
@@ -753,17 +770,18 @@ def main():
     tokens_step = layers * sum(L for L, _ in seqs)
     tokens_per_s = tokens_step * args.steps / (ms_total / 1e3)
     kern = {}
+    rows = "gather" in per_kernel
     for name, (n, ms) in per_kernel.items():
-        ab = kernel_alg_bytes(name, w, args.lse, G, seqs)
+        ab = kernel_alg_bytes(name, wc, args.lse, G, seqs, rows)
         avg = ms / n
         kern[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
                       "alg_GBps": None if ab is None else round(ab / (avg / 1e3) / 1e9, 1)}
-    dom = max((k for k in per_kernel if kernel_alg_bytes(k, w, False, 1, seqs) is not None),
+    dom = max((k for k in per_kernel if kernel_alg_bytes(k, wc, False, 1, seqs, rows) is not None),
               key=lambda k: per_kernel[k][1])
     n_dom, ms_dom = per_kernel[dom]
-    ab_dom = kernel_alg_bytes(dom, w, args.lse, G, seqs)
+    ab_dom = kernel_alg_bytes(dom, wc, args.lse, G, seqs, rows)
     achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
-    counted = {} if (G > 1 or w.name != "spike_l32x_h32_l32k" or args.force_fallback) else \
+    counted = {} if (G > 1 or w.name != "spike_l32x_h32_l32k" or args.force_fallback or args.fold) else \
         counters_from_profiles(dom + "_lse" if args.lse else dom)
     path_gbps = path_alg_bytes(w, G, seqs) * layers / (ms_step / 1e3) / 1e9
 
@@ -786,6 +804,7 @@ def main():
                    "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys,
                    "scoring": args.scoring, "row_stats": "handed_over" if args.lse else "computed",
                    "kv_heads": Hkv, "path": path, "fallbacks": fallbacks,
+                   "calls_per_step": calls, "heads_per_call": Hc,
                    "forced_fallback": bool(args.force_fallback), "status": "ok"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
