@@ -404,6 +404,7 @@ PROFILE_TAGS = {
     "c2": ["--workload", "lognorm_h32_l16k"],
     "c4": ["--workload", "ragged_b8_h32_l4k_64k"],
     "c5": ["--workload", "tied_h64_l128k"],
+    "fold": ["--fold"],
 }
 # (pattern in the mangled kernel name, short name), first match wins.
 SHORT_NAMES = [("window_fused_kernelILi128ELb1E", "window_fused_lse"), ("window_fused", "window_fused"),
@@ -425,7 +426,7 @@ def profile_commands(tag):
     """The rocprofv3 commands of a profiling tag: kernel trace, FETCH_SIZE,
     WRITE_SIZE and the MFMA counters, each its own run."""
     extra = " ".join(PROFILE_TAGS[tag])
-    layered = "--workload" not in PROFILE_TAGS[tag]
+    layered = "--workload" not in PROFILE_TAGS[tag] and "--fold" not in PROFILE_TAGS[tag]
     short = f"--steps 1 --warmup 0 {'--layers 4 ' if layered else ''}--no-cpu-baseline --no-ceiling"
     base = "python3 bench.py"
     return {
@@ -455,6 +456,8 @@ def digest(tag, name, title):
     args = PROFILE_TAGS[tag]
     wname = args[args.index("--workload") + 1] if "--workload" in args else "spike_l32x_h32_l32k"
     wl = WL.get(wname)
+    if "--fold" in args:  # one launch covers every layer
+        wl = WL.reduced(wl, name=wl.name, heads=wl.heads * wl.layers, layers=1)
     lse, group = "--lse" in args, int(args[args.index("--gqa") + 1]) if "--gqa" in args else 1
 
     def rows(path):
@@ -462,13 +465,17 @@ def digest(tag, name, title):
             return list(csv.DictReader(f))
 
     def per_kernel(path, counter):
+        """Average counter value per dispatch of each kernel, and dispatch
+        counts.  For the probe copy, the largest dispatch: the runtime also
+        launches a few tiny copies of its own."""
         if not os.path.exists(path):
             return {}, {}
         agg = collections.defaultdict(list)
         for r in rows(path):
             if r["Counter_Name"] == counter:
                 agg[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
+        avg = {k: (max(v) if k == "copy" else sum(v) / len(v)) for k, v in agg.items()}
+        return avg, {k: len(v) for k, v in agg.items()}
 
     stats = rows(os.path.join(out_dir, f"prof_trace_{tag}", "trace_kernel_stats.csv"))
     fetch, nf = per_kernel(os.path.join(out_dir, f"prof_fetch_{tag}", "fetch_counter_collection.csv"), "FETCH_SIZE")
@@ -501,7 +508,8 @@ def digest(tag, name, title):
         fs, wsc = copy_bytes / 1024 / fetch["copy"], copy_bytes / 1024 / write["copy"]
         md += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "", "```",
                cmds["fetch"], cmds["write"], "```", "",
-               f"Scale: a 1 GiB device copy (`__amd_rocclr_copyBuffer`, run by `--copy-probe`) reads FETCH_SIZE = "
+               f"Scale: a 1 GiB device copy (`__amd_rocclr_copyBuffer`, run by `--copy-probe`: its one large "
+               f"dispatch) reads FETCH_SIZE = "
                f"{fetch['copy']:.0f} KiB and writes WRITE_SIZE = {write['copy']:.0f} KiB, so FETCH_SIZE is "
                f"multiplied by {fs:.3f} and WRITE_SIZE by {wsc:.3f} to get bytes.", "",
                "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | write MB (scaled) | "
@@ -510,7 +518,7 @@ def digest(tag, name, title):
             if k == "copy":
                 continue
             rb, wb = fetch[k] * 1024 * fs, write.get(k, 0) * 1024 * wsc
-            ab = kernel_alg_bytes(k.replace("_lse", ""), wl, k.endswith("_lse") or lse, group)
+            ab = kernel_alg_bytes(k.replace("_lse", ""), wl, k.endswith("_lse") or lse, group, None, "gather" in fetch)
             md.append(f"| `{k}` | {nf[k]} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rb / 1e6:.1f} | "
                       f"{wb / 1e6:.1f} | {'' if ab is None else f'{ab / 1e6:.1f}'} |")
             if tag in ("auto", "lse", "two_pass") and k in KERNEL_SOURCES:
