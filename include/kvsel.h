@@ -155,8 +155,8 @@ int kvsel_status(const void* workspace, void* stream);
  * Flag bits (KVSEL_FLAG_*): the three waits and the non-finite and domain
  * conditions that kvsel_status reports, and two that are not errors:
  * SCORING_FALLBACK (the single-read scoring found its grid not all resident,
- * as on a device shared with other work, and scored each head alone in two
- * passes) and SELECT_FALLBACK (the same for the cooperative selection, which
+ * as on a device shared with other work, and its workgroups scored (head,
+ * chunk) items from counters in two passes over K) and SELECT_FALLBACK (the same for the cooperative selection, which
  * then resolves each row in one workgroup).  Results are identical either
  * way; only the time differs. */
 #define KVSEL_FLAG_EXCHANGE_WAIT 0x1u

@@ -442,9 +442,11 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     g_last_path = path;
   }
   // Calls made only of fused-selection groups clear nothing before they
-  // start: their kernels clear what they own and carry a token.
+  // start: their kernels clear what they own and carry a token.  Every
+  // single-read call carries one: its fallback claims work from
+  // token-tagged counters, and its flags go to the tagged header word.
   const bool fill = any_old || g_validate;
-  const unsigned long long token = any_fsel ? next_token() : 0ull;
+  const unsigned long long token = use_fused && need_scoring ? next_token() : 0ull;
   record_call(ws, fill, token);
   if (fill) {
     // The header, and the exchange records, status words, histograms and
@@ -462,6 +464,10 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     z.bytes[1] = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
     z.p[2] = ws + p.off_coop;
     z.bytes[2] = any_coop ? (long long)(p.off_cw - p.off_coop) : 0;  // the fused selection's words follow
+    // The single-read fallback's claim counters and per-row completion counts
+    // (contiguous).
+    z.p[3] = ws + p.off_flags;
+    z.bytes[3] = use_fused && need_scoring ? (long long)(p.off_cand - p.off_flags) : 0;
     hipError_t e = timed("fill", st, [&] { return launch_zero(z, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");
   }
@@ -552,6 +558,13 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       sel.V = V;
       sel.K_out = K_out;
       sel.V_out = V_out;
+    }
+    if (!sel.on && use_fused) {  // the fallback's counters, completion counts and chunk statistics
+      sel.token = token;
+      sel.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
+      sel.flags = (unsigned long long*)(ws + p.off_flags) + (long long)kFusedFlagWords * (b0 / kMaxSegs);
+      sel.rowfb = (unsigned long long*)(ws + p.off_rowfb) + (long long)b0 * p.heads * 2;
+      sel.kslot = (float*)(ws + p.off_kslot);
     }
     if (items > 0 && use_fused) {
       unsigned* gstatus = status + (long long)kFusedStatusWords * (b0 / kMaxSegs);

@@ -220,13 +220,13 @@ __device__ __forceinline__ void store32(unsigned* p, unsigned v) {
 }
 
 // Token-tagged counters: (tag << 24) | count, where a word whose tag is not
-// this call's counts as zero.  Claim returns the count before the claim.
-__device__ __forceinline__ unsigned tok_claim(unsigned long long* w, unsigned long long tag) {
+// this call's counts as zero.  Adding returns the count before the add.
+__device__ __forceinline__ unsigned tok_add(unsigned long long* w, unsigned long long tag, unsigned n) {
   unsigned long long cur = load64(w);
   for (;;) {
     const unsigned cnt = (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
     unsigned long long expect = cur;
-    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + 1u),
+    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + n),
                                              __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
       return cnt;
     cur = expect;
@@ -736,151 +736,6 @@ __device__ __forceinline__ void ctl_memory(const Launch& a, bool write_votes, co
     }
     if (write_votes && kv >= 0) lds_set(&sy->v_done, (unsigned)(kv + 1));  // votes of rounds <= kv are out of LDS
     KVSEL_FUSED_CTL_MARK(k, 7);
-  }
-}
-
-// Fallback when the grid is not all resident (ABORT): the workgroups take
-// whole (segment, head) units from a counter and score each one alone, in
-// two passes over its K (row statistics, then votes), so no workgroup ever
-// waits for another.  The streaming waves do the passes; every wave of the
-// workgroup takes part in each barrier.  Slower than the round schedule,
-// same arithmetic.
-template <int D>
-__device__ __forceinline__ void solo_pass(const Launch& a, const Seg& s, const __bf16* __restrict__ kh, int limit,
-                                          bool votes_pass, uint4 (*ring)[TileGeom<D>::PIECES], const uint4* qbuf,
-                                          const float* s_m, const float* s_iz, float* vout, float (&m)[16],
-                                          float (&z)[16]) {
-  using G = TileGeom<D>;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 31, g = lane >> 5;
-  const int L = s.L, P = L - a.W;
-  const int tiles = (limit + 31) / 32;
-  const int nw = tiles > wave ? (tiles - wave + kSW - 1) / kSW : 0;  // tiles wave, wave + kSW, ...
-  float mr[16], iz[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    mr[r] = votes_pass ? s_m[acc_row(r, g)] : 0.f;
-    iz[r] = votes_pass ? s_iz[acc_row(r, g)] : 0.f;
-  }
-  int issued = 0;
-  for (; issued < kNBuf && issued < nw; ++issued)
-    issue_tile<D>(kh, L, (wave + kSW * issued) * 32, ring[issued % kNBuf], lane);
-  for (int i = 0; i < nw; ++i) {
-    wait_tiles<D>(issued - i - 1);
-    const uint4* tile = ring[i % kNBuf];
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int c = 2 * kk + g;
-      const int off = n * G::PR + (c ^ (n & (G::PR - 1)));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qbuf[off]),
-                                                    __builtin_bit_cast(bf16x8, tile[off]), acc, 0, 0, 0);
-    }
-    lds_fence();
-    if (issued < nw) {
-      issue_tile<D>(kh, L, (wave + kSW * issued) * 32, ring[issued % kNBuf], lane);
-      ++issued;
-    }
-    const int j = (wave + kSW * i) * 32 + n;
-    if (votes_pass) {
-      float tot = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tot += exp2_fast(acc[r] * a.scale2 - mr[r]) * iz[r];
-      const float other = __shfl_xor(tot, 32);
-      const float v = g == 0 ? tot + other : other + tot;
-      if (g == 0 && j < P) vout[j] = v;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(r, g);
-        const float x = (j < L && j <= P + row) ? acc[r] * a.scale2 : -INFINITY;
-        const float d = x - m[r];
-        const float e = exp2_fast(-fabsf(d));
-        z[r] = d > 0.f ? fmaf(z[r], e, 1.f) : z[r] + e;
-        m[r] = fmaxf(m[r], x);
-      }
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-template <int D>
-__device__ __forceinline__ void solo_heads(const Launch& a, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                           unsigned* __restrict__ counter, float* __restrict__ votes, float* __restrict__ row_stats,
-                           uint4 (*s_ring)[kNBuf][TileGeom<D>::PIECES], uint4* qbuf, float* s_maxp, float* s_zp,
-                           float* s_m, float* s_iz) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, W = a.W;
-  const bool streams = wave < kSW;
-  const Seg& last = a.seg[a.n - 1];
-  const unsigned units = (unsigned)(last.row0 + last.nh);
-  __shared__ unsigned s_unit;
-  for (;;) {
-    if (threadIdx.x == 0) s_unit = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const unsigned u = s_unit;
-    __syncthreads();
-    if (u >= units) break;
-    const int e = find_seg<kFieldRow>(a, (int)u);
-    const Seg& s = a.seg[e];
-    if (s.L < s.C) continue;  // bypass: nothing to score
-    const int h = s.h0 + ((int)u - s.row0);
-    const int hs = s.b * a.heads + h;
-    if (wave == 0) {
-      issue_tile<D>(Q + (long long)hs * W * D, W, 0, qbuf, lane);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      ctl_finish_q<D>(W, qbuf);
-    }
-    __syncthreads();
-    const __bf16* kh = K + s.kv_off + (long long)h * s.L * D;
-    float m[16], z[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      m[r] = kNegBig;
-      z[r] = 0.f;
-    }
-    if (streams) solo_pass<D>(a, s, kh, s.L, false, s_ring[wave], qbuf, s_m, s_iz, nullptr, m, z);
-    // This wave's (max, sum) per row, then the waves merged in order.
-    if (streams) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float mh0 = half_max(m[r]);
-      const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 31));
-      const float m1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(mh0), 63));
-      const float mh = g == 0 ? m0 : m1;
-      const float zz = half_sum(z[r] != 0.f ? z[r] * exp2_fast(m[r] - mh) : 0.f);  // a NaN sum propagates
-      if ((lane & 31) == 31) {
-        s_maxp[wave * 32 + acc_row(r, g)] = mh;
-        s_zp[wave * 32 + acc_row(r, g)] = zz;
-      }
-    }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < W) {
-      const int i = threadIdx.x;
-      float M = s_maxp[i];
-      for (int v = 1; v < kSW; ++v) M = fmaxf(M, s_maxp[v * 32 + i]);
-      float Z = 0.f;
-      for (int v = 0; v < kSW; ++v) {
-        const float zv = s_zp[v * 32 + i];
-        if (zv != 0.f) Z += zv * exp2_fast(s_maxp[v * 32 + i] - M);  // a NaN sum propagates
-      }
-      s_m[i] = M;
-      s_iz[i] = 1.f / Z;
-      if (!stats_ok(M, Z)) raise_error(a.err, kErrNonFinite);
-      if (row_stats != nullptr) {
-        float* rs = row_stats + ((long long)hs * W + i) * 2;
-        rs[0] = M * kLn2;
-        rs[1] = Z;
-      }
-    } else if ((int)threadIdx.x < 32) {
-      s_m[threadIdx.x] = 0.f;  // rows past W: zero queries, dropped by 1/Z = 0
-      s_iz[threadIdx.x] = 0.f;
-    }
-    __syncthreads();
-    float* vout = votes + s.vote_off + (long long)h * s.vote_ld;
-    if (streams) solo_pass<D>(a, s, kh, s.L - W, true, s_ring[wave], qbuf, s_m, s_iz, vout, m, z);
-    __syncthreads();  // s_m, s_iz and qbuf are rewritten for the next unit
   }
 }
 
@@ -1629,7 +1484,22 @@ __device__ __forceinline__ void sel_finish(const Launch& a, const FusedSel& f, c
   }
 }
 
-// ---- fallback of the fused selection (ABORT: not all resident)
+// ---- fallback (ABORT: not all resident), of both kernel variants
+
+// Claims and completion counts of the fallback.  With the fused selection
+// nothing was cleared before the call, so they are token-tagged (a claim is
+// a compare-and-swap loop); otherwise the fill zeroed them and a claim is
+// one atomic add, which many workgroups can make at once without retries.
+template <bool kTok>
+__device__ __forceinline__ unsigned fb_claim(unsigned long long* w, unsigned long long tag, unsigned n = 1u) {
+  if constexpr (kTok) return tok_add(w, tag, n);
+  return (unsigned)__hip_atomic_fetch_add(w, (unsigned long long)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool kTok>
+__device__ __forceinline__ unsigned fb_count(const unsigned long long* w, unsigned long long tag) {
+  if constexpr (kTok) return tok_count(w, tag);
+  return (unsigned)load64(w);
+}
 
 // Inclusive scan over the workgroup (kThreads); total gets the sum.
 __device__ __forceinline__ uint32_t wg_incl(uint32_t v, uint32_t* sh, uint32_t& total) {
@@ -1650,24 +1520,30 @@ __device__ __forceinline__ uint32_t wg_incl(uint32_t v, uint32_t* sh, uint32_t& 
   return v + base;
 }
 
-// Work item t of the fallback's scoring phases: (row, chunk) over the
-// launch's rows, chunk-minor.
+// Work item t of the fallback's scoring phases: (row, group of up to
+// kFbChunks chunks) over the launch's rows, group-minor.  Groups amortise
+// an item's fixed costs (Qwin load, claim, completion count) over several
+// chunks; a row still has several items, so every workgroup gets work.
+constexpr int kFbChunks = 4;
 struct FbItem {
   bool on;
-  int e, h, c, row;
+  int e, h, c, nc, row;  // chunks c .. c + nc - 1 of row `row`
 };
+__device__ __forceinline__ int fb_groups(const Seg& s) { return (s.fc + kFbChunks - 1) / kFbChunks; }
 __device__ __forceinline__ FbItem fb_item(const Launch& a, unsigned t) {
-  FbItem it{false, 0, 0, 0, 0};
+  FbItem it{false, 0, 0, 0, 0, 0};
   unsigned base = 0;
   for (int e = 0; e < a.n; ++e) {
     const Seg& s = a.seg[e];
-    const unsigned n = (unsigned)(s.nh * s.fc);
+    const unsigned ng = (unsigned)fb_groups(s);
+    const unsigned n = (unsigned)s.nh * ng;
     if (t < base + n) {
       const unsigned loc = t - base;
       it.on = true;
       it.e = e;
-      it.h = s.h0 + (int)(loc / (unsigned)s.fc);
-      it.c = (int)(loc % (unsigned)s.fc);
+      it.h = s.h0 + (int)(loc / ng);
+      it.c = (int)(loc % ng) * kFbChunks;
+      it.nc = min(kFbChunks, s.fc - it.c);
       it.row = s.row0 + (it.h - s.h0);
       return it;
     }
@@ -1846,12 +1722,14 @@ __device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f
   (void)lane;
 }
 
-// The fallback: scoring in two phases over (row, chunk) items (statistics,
-// then votes; with handed-over statistics only the votes), then whole rows'
-// selections.  Items are claimed in order from token-tagged counters, and a
-// phase waits only for items of the phase before, which running workgroups
-// have claimed, so the fallback finishes with any number of workgroups.
-template <int D, bool kLse>
+// The fallback (ABORT: not all resident): scoring in two phases over (row,
+// chunk) items, statistics then votes (with handed-over statistics only the
+// votes), then with the fused selection whole rows' selections.  Items are
+// claimed in order from token-tagged counters, and a phase waits only for
+// items of the phase before, which running workgroups have claimed, so the
+// fallback finishes with any number of workgroups, and every workgroup that
+// runs takes part.
+template <int D, bool kLse, bool kSel>
 __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f, const __bf16* __restrict__ Q,
                              const __bf16* __restrict__ K, const float* __restrict__ lse,
                              unsigned long long* __restrict__ ex, float* __restrict__ votes,
@@ -1864,10 +1742,10 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
   const int W = a.W;
   __shared__ unsigned s_claim;
   unsigned items = 0;
-  for (int e = 0; e < a.n; ++e) items += (unsigned)(a.seg[e].nh * a.seg[e].fc);
+  for (int e = 0; e < a.n; ++e) items += (unsigned)(a.seg[e].nh * fb_groups(a.seg[e]));
   for (int phase = kLse ? 1 : 0; phase < 2; ++phase) {
     for (;;) {
-      if (tid == 0) s_claim = tok_claim(ctr + phase, tag);
+      if (tid == 0) s_claim = fb_claim<kSel>(ctr + phase, tag);
       __syncthreads();
       const unsigned t = s_claim;
       __syncthreads();
@@ -1882,10 +1760,10 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
       // slots).
       unsigned long long* fbs = reinterpret_cast<unsigned long long*>(f.kslot);
       const __bf16* kh = K + s.kv_off + (long long)it.h * L * D;
-      const int lo = it.c * kS, hi = min(L, lo + kS);
+      const int lo = it.c * kS, hi = min(L, lo + it.nc * kS);
       fb_load_q<D>(a, Q, hs, qbuf);
       if (phase == 1 && tid == 0) {  // the statistics of every chunk of the row are there
-        const bool ok = kLse || sel_wait(a, [&] { return tok_count(f.rowfb + 2ll * it.row, tag) >= (unsigned)s.fc; });
+        const bool ok = kLse || sel_wait(a, [&] { return fb_count<kSel>(f.rowfb + 2ll * it.row, tag) >= (unsigned)s.fc; });
         if (!ok) flag_error(a, f, kErrExchangeWait);
       }
       __syncthreads();
@@ -1921,6 +1799,8 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
             if (zv != 0.f) Z += zv * exp2_fast(s_maxp[w2 * 32 + tid] - M);
           }
           store64(fbs + sl * (kS / 2) + tid, pack_slot(M, Z));
+          // The item's other chunks hold nothing: zero sums, skipped by the merge.
+          for (int q = 1; q < it.nc; ++q) store64(fbs + (sl + q) * (kS / 2) + tid, pack_slot(kNegBig, 0.f));
         }
       } else {
         if (tid < 32) {  // the row's log-normalisers: merged slots in chunk order, or the given ones
@@ -1953,13 +1833,14 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) (void)tok_claim(f.rowfb + 2ll * it.row + phase, tag);  // one more chunk of the row done
+      if (tid == 0) (void)fb_claim<kSel>(f.rowfb + 2ll * it.row + phase, tag, (unsigned)it.nc);  // chunks done
       __syncthreads();
     }
   }
+  if constexpr (!kSel) return;
   const int rows = fb_rows(a);
   for (;;) {
-    if (tid == 0) s_claim = tok_claim(ctr + 2, tag);
+    if (tid == 0) s_claim = fb_claim<kSel>(ctr + 2, tag);
     __syncthreads();
     const unsigned t = s_claim;
     __syncthreads();
@@ -1968,7 +1849,7 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
     const Seg& s = a.seg[e];
     const int h = s.h0 + ((int)t - s.row0);
     if (tid == 0) {  // every chunk's votes of the row are there
-      const bool ok = sel_wait(a, [&] { return tok_count(f.rowfb + 2ll * t + 1, tag) >= (unsigned)s.fc; });
+      const bool ok = sel_wait(a, [&] { return fb_count<kSel>(f.rowfb + 2ll * t + 1, tag) >= (unsigned)s.fc; });
       if (!ok) flag_error(a, f, kErrSelectWait);
     }
     __syncthreads();
@@ -1992,7 +1873,7 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
   __shared__ uint4 s_q[2][G::PIECES];
   __shared__ float4 s_x[kSW][kTT * 4 * 64];  // each wave's logits of one round
   __shared__ float s_maxp[kNR][kSW * 32], s_zp[kNR][kSW * 32];
-  __shared__ float s_m[kNR][32], s_iz[32];
+  __shared__ float s_m[kNR][32];
   __shared__ float s_votes[2][kS];
   __shared__ Sync sy;
   static_assert(sizeof(s_x) >= 4 * (4 * kFusedMaxRounds + (kThreads / 64) * kS), "the end phase's words fit s_x");
@@ -2104,16 +1985,10 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
   KVSEL_FUSED_MARK(23, 1);
   __syncthreads();
   KVSEL_FUSED_MARK(23, 2);
-  if (sy.abort) {  // not all resident
-    if constexpr (kSel) {  // work from counters: statistics, votes, whole rows' selections
-      sel_fallback<D, kLse>(a, f, Q, K, lse, ex, votes, row_stats, s_ring[0], s_q[0], s_maxp[0], s_zp[0], s_m[0],
-                            reinterpret_cast<uint32_t*>(&s_x[0][0]));
-      return;
-    }
-    if constexpr (!kLse) {  // whole heads, one workgroup each
-      solo_heads<D>(a, Q, K, status + 3, votes, row_stats, s_ring, s_q[0], s_maxp[0], s_zp[0], s_m[0], s_iz);
-      return;
-    }
+  if (sy.abort) {  // not all resident: work from counters (statistics, votes, with the fused selection rows)
+    sel_fallback<D, kLse, kSel>(a, f, Q, K, lse, ex, votes, row_stats, s_ring[0], s_q[0], s_maxp[0], s_zp[0],
+                                s_m[0], reinterpret_cast<uint32_t*>(&s_x[0][0]));
+    return;
   }
   if constexpr (kSel) sel_finish<D>(a, f, K, votes, reinterpret_cast<uint32_t*>(&s_x[0][0]));  // the selection's end phase
   KVSEL_FUSED_MARK(23, 3);

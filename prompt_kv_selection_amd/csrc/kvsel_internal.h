@@ -79,7 +79,7 @@ enum : unsigned {
   kErrNonFinite = 8u,     // a non-finite input (validating mode) or a non-finite or zero row normaliser
   kErrDomain = 16u,       // an input outside its documented domain (a negative second-moment entry)
   // Not errors: which way a residency handshake went.
-  kFlagScoringFallback = 256u,  // single-read scoring: not all resident, whole heads scored alone
+  kFlagScoringFallback = 256u,  // single-read scoring: not all resident, (row, chunk) items from counters
   kFlagSelectFallback = 512u,   // cooperative selection: not all resident, whole rows by one workgroup
 };
 // The workspace header: word 0 holds the flags of the last call (cleared by
@@ -330,7 +330,7 @@ hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, c
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
 // Zero up to kZeroRanges byte ranges in one launch (16-byte aligned pointers
 // and sizes, else hipErrorInvalidValue; empty ranges are skipped).
-constexpr int kZeroRanges = 3;
+constexpr int kZeroRanges = 4;
 struct ZeroRanges {
   void* p[kZeroRanges];
   long long bytes[kZeroRanges];
