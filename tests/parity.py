@@ -154,7 +154,9 @@ def _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype):
     pl = torch.full((H, L - W), float("nan"), dtype=torch.float32, device="cuda")
     B.kvsel_select(Qd, Kd, Vd, L, W, C, D, H, kernel, pooling, td, idx, Ko, Vo, rs, vt, pl, ws)
     torch.cuda.synchronize()
-    return dict(idx=idx, Ko=Ko, Vo=Vo, rs=rs.cpu().numpy(), votes=vt.cpu().numpy(), pooled=pl.cpu().numpy())
+    assert B.kvsel_status(ws) == B.KVSEL_OK, B.kvsel_last_error()
+    return dict(idx=idx, Ko=Ko, Vo=Vo, rs=rs.cpu().numpy(), votes=vt.cpu().numpy(), pooled=pl.cpu().numpy(),
+                path=B.path_names(B.kvsel_last_path()), flags=B.flag_names(B.kvsel_status_flags(ws)[0]))
 
 
 def check_head(out, h, ref, L, W, C, what, gather_rows=True):

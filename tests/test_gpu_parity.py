@@ -396,19 +396,35 @@ def test_repeated_ragged_calls_agree(B):
 
 FULL = [
     ("fp32_h1_l1k", [0], 0),
-    ("lognorm_h32_l16k", [0, 17, 31], 0),
-    ("spike_l32x_h32_l32k", [0, 13, 31], 0),
+    ("lognorm_h32_l16k", list(range(32)), 0),
+    ("spike_l32x_h32_l32k", list(range(32)), 0),
     ("spike_l32x_h32_l32k", [5], 31),
     ("tied_h64_l128k", [0, 63], 0),
 ]
 
 
+def oracle_heads(w, heads, layer=0, seq=None, L=None, C=None):
+    """The oracle's selection of each listed head (a thread pool: numpy's
+    matrix products release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(h):
+        q, k, v = WL.head_arrays(w, h, layer=layer) if seq is None else WL.head_arrays(w, h, seq=seq)
+        return h, O.snapkv_select(WL.to_float64(q, w.dtype), WL.to_float64(k, w.dtype), WL.to_float64(v, w.dtype),
+                                  w.W, C if C is not None else w.C, w.kernel, w.pooling)
+
+    workers = max(1, min(8, len(heads), (os.cpu_count() or 2) // 2))
+    with ThreadPoolExecutor(workers) as ex:
+        return dict(ex.map(one, heads))
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name,heads,layer", FULL, ids=[f"{n}-layer{l}" for n, _, l in FULL])
+@pytest.mark.parametrize("name,heads,layer", FULL, ids=[f"{n}-layer{l}-h{len(h)}" for n, h, l in FULL])
 def test_full_size_workloads(B, name, heads, layer):
     """Full-size workloads in the configuration the benchmark times (one call
-    per layer over all heads); the oracle checks sampled heads, every head's
-    gather is checked bit-exact and its picks against its own scores."""
+    per layer over all heads); the oracle checks the listed heads (every head
+    of the headline layer and of the 16K workload), every head's gather is
+    checked bit-exact and its picks against its own scores."""
     w = WL.get(name)
     log(f"full size {name} layer {layer}: drawing inputs")
     Q, K, V = WL.layer_arrays(w, layer=layer)
@@ -421,16 +437,39 @@ def test_full_size_workloads(B, name, heads, layer):
     idx = out["idx"].cpu().numpy()
     for h in range(w.heads):
         gpu_internal_topk(idx[h, :n], out["pooled"][h], n, f"{name} head {h}")
-    for h in heads:
-        log(f"full size {name}: oracle head {h}")
-        q, k, v = WL.head_arrays(w, h, layer=layer)
-        ref = O.snapkv_select(WL.to_float64(q, w.dtype), WL.to_float64(k, w.dtype), WL.to_float64(v, w.dtype),
-                              w.W, w.C, w.kernel, w.pooling)
+    log(f"full size {name}: oracle on {len(heads)} head(s)")
+    for h, ref in sorted(oracle_heads(w, heads, layer).items()):
         check_head(out, h, ref, w.L, w.W, w.C, f"{name} head {h}")
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("path", ["two_pass", "fallback"])
+def test_full_size_headline_paths(B, path):
+    """The headline layer on the two-pass scoring and on the residency
+    fallback forced from the host (both handshakes decide ABORT), against
+    the oracle on eight heads spread over the layer."""
+    w = WL.get("spike_l32x_h32_l32k")
+    Q, K, V = WL.layer_arrays(w, layer=0)
+    Qd, Kd, Vd = to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    del K, V
+    log(f"full size headline layer, {path}")
+    out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, w.dtype,
+                     scoring="two_pass" if path == "two_pass" else "single_read_fallback")
+    if path == "two_pass":
+        assert "two_pass" in out["path"], out["path"]
+    else:
+        assert "single_read" in out["path"] and "select_coop" in out["path"], out["path"]
+        assert "scoring_fallback" in out["flags"] and "select_fallback" in out["flags"], out["flags"]
+    check_gather(out, Kd, Vd, w.C, w.L)
+    heads = [0, 4, 9, 13, 18, 22, 27, 31]
+    for h, ref in sorted(oracle_heads(w, heads).items()):
+        check_head(out, h, ref, w.L, w.W, w.C, f"headline {path} head {h}")
+
+
+@pytest.mark.slow
 def test_full_size_ragged(B):
+    """Every sequence of the ragged batch on four heads against the oracle,
+    and every row of K_out bit-exact."""
     w = WL.get("ragged_b8_h32_l4k_64k")
     log("full size ragged: drawing inputs")
     Q, K, V, Ls, Cs, cu = WL.ragged_arrays(w)
@@ -451,19 +490,18 @@ def test_full_size_ragged(B):
     B.kvsel_select_varlen(Qd, Kd, Vd, cu.tolist(), Cs, W, D, H, w.kernel, w.pooling, torch.bfloat16, idx, Ko, Vo,
                           rs, vt, pl, ws)
     torch.cuda.synchronize()
-    for b in (0, 7):
+    for b in range(len(Ls)):
         L, C = Ls[b], Cs[b]
-        h = 3 * b % H
-        log(f"full size ragged: oracle sequence {b} head {h}")
-        q, k, v = WL.head_arrays(w, h, seq=b)
-        ref = O.snapkv_select(WL.to_float64(q, "bf16"), WL.to_float64(k, "bf16"), WL.to_float64(v, "bf16"),
-                              W, C, w.kernel, w.pooling)
+        heads = sorted({(3 * b + 8 * j) % H for j in range(4)})
+        log(f"full size ragged: oracle sequence {b} (L={L}) heads {heads}")
         sub = dict(idx=idx[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C),
                    votes=vt[H * int(cuP[b]): H * int(cuP[b + 1])].view(H, L - W).cpu().numpy(),
                    pooled=pl[H * int(cuP[b]): H * int(cuP[b + 1])].view(H, L - W).cpu().numpy(),
                    rs=rs[b].cpu().numpy())
-        check_head(sub, h, ref, L, W, C, f"ragged seq {b} head {h}")
+        for h, ref in sorted(oracle_heads(w, heads, seq=b, C=C).items()):
+            check_head(sub, h, ref, L, W, C, f"ragged seq {b} head {h}")
         kk = Kd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D)
-        got = Ko[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C, D)
-        ii = sub["idx"].long()
-        assert torch.equal(bits(got), bits(torch.gather(kk, 1, ii[:, :, None].expand(H, C, D))))
+        vv = Vd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D)
+        ii = sub["idx"].long()[:, :, None].expand(H, C, D)
+        assert torch.equal(bits(Ko[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C, D)), bits(torch.gather(kk, 1, ii)))
+        assert torch.equal(bits(Vo[H * int(cuC[b]): H * int(cuC[b + 1])].view(H, C, D)), bits(torch.gather(vv, 1, ii)))
