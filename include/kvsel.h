@@ -129,6 +129,18 @@ int kvsel_version(void);
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* kvsel_last_error(void);
 
+/* Debug builds (libkvsel_debug.so, compiled with KVSEL_DEBUG) check every
+ * index that becomes a row address: the selection's picks, the gather of
+ * caller indices, the refresh's positions.  A violation is clamped or skipped
+ * as in release builds (nothing traps) and recorded as KVSEL_FLAG_INDEX_RANGE:
+ * in the call's workspace header (kvsel_status returns KVSEL_EDEVICE), or,
+ * for entry points without a workspace (kvsel_gather, kvsel_refresh's final
+ * positions), in a library-wide word that this call returns (and clears when
+ * `reset` is non-zero) after the device is idle.  Release builds return
+ * KVSEL_EUNSUPPORTED.  Not for production use: the word is shared by every
+ * caller of the library. */
+int kvsel_debug_flags(int reset);
+
 /* Device-side outcome of the last selection call (kvsel_select*,
  * kvsel_select*_lse, kvsel_select_gqa, kvsel_jacap_select) that used this
  * workspace: waits for `stream`, then reads
@@ -139,7 +151,8 @@ const char* kvsel_last_error(void);
  * workgroups timed out (the outputs of that call are unreliable); or
  * KVSEL_EINVAL for a NULL or misaligned workspace, or for an input outside
  * its domain found on the device (kvsel_jacap_select: a negative or NaN
- * lambda_q entry).  Each selection call
+ * lambda_q entry).  Debug builds also report KVSEL_EDEVICE for an index
+ * outside its range (see kvsel_debug_flags).  Each selection call
  * clears the flags at its start.  This is the only entry point that
  * synchronises. */
 int kvsel_status(const void* workspace, void* stream);
@@ -152,18 +165,21 @@ int kvsel_status(const void* workspace, void* stream);
  * word is then cleared.  A freshly allocated workspace holds arbitrary bits
  * there: reset once before the run.  KVSEL_OK, KVSEL_EINVAL (NULL or
  * misaligned workspace) or KVSEL_EDEVICE.  Synchronises; host memory only.
- * Flag bits (KVSEL_FLAG_*): the three waits and the non-finite and domain
- * conditions that kvsel_status reports, and two that are not errors:
- * SCORING_FALLBACK (the single-read scoring found its grid not all resident,
- * as on a device shared with other work, and its workgroups scored (head,
- * chunk) items from counters in two passes over K) and SELECT_FALLBACK (the same for the cooperative selection, which
- * then resolves each row in one workgroup).  Results are identical either
- * way; only the time differs. */
+ * Flag bits (KVSEL_FLAG_*): the three waits, the non-finite and domain
+ * conditions and the debug builds' index check that kvsel_status reports,
+ * and two that are not errors: SCORING_FALLBACK (the single-read scoring
+ * found its grid not all resident, as on a device shared with other work,
+ * and its workgroups scored (head, chunk-range) items from counters in two
+ * passes over K; the statistics are then merged in another grouping, so the
+ * votes agree with the resident path up to rounding) and SELECT_FALLBACK
+ * (the same for the cooperative selection, which then resolves each row in
+ * one workgroup, with identical results). */
 #define KVSEL_FLAG_EXCHANGE_WAIT 0x1u
 #define KVSEL_FLAG_LDS_WAIT 0x2u
 #define KVSEL_FLAG_SELECT_WAIT 0x4u
 #define KVSEL_FLAG_NONFINITE 0x8u
 #define KVSEL_FLAG_DOMAIN 0x10u
+#define KVSEL_FLAG_INDEX_RANGE 0x20u
 #define KVSEL_FLAG_SCORING_FALLBACK 0x100u
 #define KVSEL_FLAG_SELECT_FALLBACK 0x200u
 int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned* last_flags,

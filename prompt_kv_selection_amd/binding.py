@@ -16,6 +16,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libkvsel_debug.so")  # the same library built with KVSEL_DEBUG
 
 KVSEL_OK = 0
 KVSEL_EINVAL = -1
@@ -45,7 +46,9 @@ lib.kvsel_status_flags.argtypes = [_vp, _vp, _i, ctypes.POINTER(ctypes.c_uint), 
 lib.kvsel_last_path.restype = ctypes.c_uint
 lib.kvsel_last_path.argtypes = []
 FLAG = {"exchange_wait": 0x1, "lds_wait": 0x2, "select_wait": 0x4, "nonfinite": 0x8, "domain": 0x10,
-        "scoring_fallback": 0x100, "select_fallback": 0x200}
+        "index_range": 0x20, "scoring_fallback": 0x100, "select_fallback": 0x200}
+lib.kvsel_debug_flags.restype = _i
+lib.kvsel_debug_flags.argtypes = [_i]
 PATH = {"single_read": 0x1, "two_pass": 0x2, "votes_only": 0x4, "handed_over": 0x8, "bypass": 0x10,
         "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80, "select_fused": 0x100}
 lib.kvsel_probe_sink_bytes.restype = _sz
@@ -377,3 +380,23 @@ def kvsel_get_option(option: int) -> int:
     if v < 0:
         raise KvselError(v, kvsel_last_error())
     return v
+
+
+def kvsel_debug_flags(reset: bool = False, library=None) -> int:
+    """The library-wide index-check word of a KVSEL_DEBUG build (then cleared
+    if reset); KVSEL_EUNSUPPORTED from a release build."""
+    return (library or lib).kvsel_debug_flags(1 if reset else 0)
+
+
+def debug_library():
+    """libkvsel_debug.so with the same C declarations as the release library,
+    for checks of the debug build's index flags (a separate handle: its calls
+    take raw pointers, as lib's do)."""
+    if not os.path.exists(DEBUG_LIB_PATH):
+        raise ImportError(f"{DEBUG_LIB_PATH} is missing: build it with `python -m prompt_kv_selection_amd.build`")
+    dl = ctypes.CDLL(DEBUG_LIB_PATH)
+    for name, f in list(lib.__dict__.items()):
+        if name.startswith("kvsel_") and hasattr(f, "argtypes"):
+            g = getattr(dl, name)
+            g.restype, g.argtypes = f.restype, f.argtypes
+    return dl

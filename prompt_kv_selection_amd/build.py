@@ -21,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvsel.so")
+DEBUG_LIB = os.path.join(HERE, "libkvsel_debug.so")
 ARCH = os.environ.get("KVSEL_ARCH", "gfx950")
 
 SOURCES = ["kvsel_api.hip", "kvsel_score.hip", "kvsel_select.hip", "kvsel_fused.hip", "kvsel_jacap.hip",
@@ -55,24 +56,32 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Build libkvsel.so, and with debug libkvsel_debug.so: the same sources
+    with KVSEL_DEBUG defined (device-side index checks that set a flag)."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
+    variants = [("", [], LIB)] + ([("debug", ["-DKVSEL_DEBUG=1"], DEBUG_LIB)] if debug else [])
 
-    def compile_one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        tag, defs, src = job
+        obj_dir = os.path.join(BUILD, tag) if tag else BUILD
+        os.makedirs(obj_dir, exist_ok=True)
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        out = _run([cc, *HIPCC_FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    jobs = [(tag, defs, src) for tag, defs, _ in variants for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, jobs))
+    for i, (tag, _, lib) in enumerate(variants):
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs[i * len(SOURCES):(i + 1) * len(SOURCES)]])
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

@@ -680,6 +680,13 @@ extern "C" {
 
 int kvsel_version(void) { return (0 << 16) | 3; }
 
+int kvsel_debug_flags(int reset) {
+  const int v = debug_flags_read(reset);
+  if (v < 0) return fail(KVSEL_EUNSUPPORTED, "not a KVSEL_DEBUG build (or the device word could not be read)");
+  ok();
+  return v;
+}
+
 int kvsel_set_option(int option, int value) {
   if (option == KVSEL_OPT_SCORING) {
     if (value < KVSEL_SCORING_AUTO || value > KVSEL_SCORING_SINGLE_READ)
@@ -728,6 +735,9 @@ int kvsel_status(const void* workspace, void* stream) {
   if (flags & (kErrExchangeWait | kErrLdsWait | kErrSelectWait))
     return fail(KVSEL_EDEVICE, "a bounded device-side wait timed out (flags 0x%x): the outputs of that call are "
                                "unreliable", flags);
+  if (flags & kErrIndexRange)
+    return fail(KVSEL_EDEVICE, "an index outside its range reached a row copy (flags 0x%x, a KVSEL_DEBUG build "
+                               "check): the outputs of that call are unreliable", flags);
   if (flags & kErrDomain)
     return fail(KVSEL_EINVAL, "an input outside its domain: a negative or NaN lambda_q entry (flags 0x%x)", flags);
   if (flags & kErrNonFinite)

@@ -1427,6 +1427,7 @@ __device__ __forceinline__ void sel_end_pick(const Launch& a, const FusedSel& f,
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     if ((pm >> u) & 1u) {
+      KVSEL_DEBUG_CHECK(before + slot < (uint32_t)q.count, a.err);
       if (before + slot < (uint32_t)q.count) {  // always, unless a timed-out wait left the counts short
         out[before + slot] = S0 + u;
         list[slot] = S0 + u;
@@ -1698,6 +1699,7 @@ __device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f
     const uint32_t eq_rank = wg_incl(eq ? 1u : 0u, sh, eq_tot) - (eq ? 1u : 0u);
     const bool take = gt || (eq && eq_seen + eq_rank < need_eq);
     const uint32_t pos = wg_incl(take ? 1u : 0u, sh, take_tot) - (take ? 1u : 0u);
+    KVSEL_DEBUG_CHECK(!take || before + pos < (uint32_t)count, a.err);
     if (take && before + pos < (uint32_t)count) {
       out[before + pos] = j;
       list[pos] = j;

@@ -78,6 +78,7 @@ enum : unsigned {
   kErrSelectWait = 4u,    // selection: a wait for another workgroup's histogram or counts timed out
   kErrNonFinite = 8u,     // a non-finite input (validating mode) or a non-finite or zero row normaliser
   kErrDomain = 16u,       // an input outside its documented domain (a negative second-moment entry)
+  kErrIndexRange = 32u,   // built with KVSEL_DEBUG: an index outside its range reached a row copy
   // Not errors: which way a residency handshake went.
   kFlagScoringFallback = 256u,  // single-read scoring: not all resident, (row, chunk) items from counters
   kFlagSelectFallback = 512u,   // cooperative selection: not all resident, whole rows by one workgroup
@@ -115,6 +116,42 @@ __device__ inline void raise_error(unsigned* err, unsigned bit) {
     __hip_atomic_fetch_or(err + kStickyWord, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+// Debug builds (KVSEL_DEBUG defined) check every index that turns into a row
+// address (the K/V copies, the gather of caller indices) and record a
+// violation as kErrIndexRange in the call's flags, or, for entry points
+// without a workspace header, in a library-wide word (kvsel_debug_flags).
+// The access itself is still clamped or skipped: the check never traps.
+// Release builds compile the checks away.
+#ifdef KVSEL_DEBUG
+constexpr bool kDebug = true;
+// The word of entry points without a workspace header (one per translation
+// unit; the gather and step kernels that can have none live in
+// kvsel_select.hip, whose word kvsel_debug_flags reads).
+static __device__ unsigned g_debug_word;
+#else
+constexpr bool kDebug = false;
+#endif
+__device__ inline void debug_raise(unsigned* err, unsigned bit) {
+#ifdef KVSEL_DEBUG
+  if (err != nullptr)
+    raise_error(err, bit);
+  else
+    __hip_atomic_fetch_or(&g_debug_word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  (void)err;
+  (void)bit;
+#endif
+}
+#define KVSEL_DEBUG_CHECK(ok, err)                        \
+  do {                                                    \
+    if constexpr (kDebug) {                               \
+      if (!(ok)) debug_raise((err), kErrIndexRange);      \
+    }                                                     \
+  } while (0)
+// The library-wide debug word (host side, kvsel_select.hip): its value, then
+// cleared if reset; -1 in release builds.
+int debug_flags_read(int reset);
+
 // A window row's statistics are usable: finite maximum, finite positive normaliser.
 __device__ inline bool stats_ok(float m, float z) { return isfinite(m) && isfinite(z) && z > 0.f; }
 

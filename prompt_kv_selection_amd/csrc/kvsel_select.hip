@@ -614,6 +614,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const Launch a, const uint4
   const int m = blk * RPB + (int)threadIdx.x / RU, part = (int)threadIdx.x % RU;
   if (m >= s.nout) return;
   int src = idx[s.idx_off + (long long)h * s.idx_ld + m];
+  KVSEL_DEBUG_CHECK(src >= 0 && src < s.L, a.err);
   src = min(max(src, 0), s.L - 1);  // never read outside the head's rows
   const long long in_row = s.kv_off / a.D + (long long)kv_head(a, h) * s.L + src;
   const long long out_row = s.out_off + (long long)h * s.out_ld + m;
@@ -770,7 +771,11 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(const Launch a
   for (int u = 0; u < kSelCols; ++u) {
     const bool pick = (pm >> u) & 1ull;
     const uint64_t m = __ballot(pick);
-    if (pick) out[cw[u * kSelWaves + wv] + lanes_below(m)] = u * kSelThreads + tid;
+    if (pick) {
+      const uint32_t slot = cw[u * kSelWaves + wv] + lanes_below(m);
+      KVSEL_DEBUG_CHECK(slot < (uint32_t)count, a.err);
+      if (slot < (uint32_t)count) out[slot] = u * kSelThreads + tid;
+    }
   }
   for (int i = tid; i < W; i += kSelThreads) out[count + i] = P + i;
 }
@@ -1353,12 +1358,15 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     for (int u = 0; u < kCoopPer; ++u)
       if ((pm >> u) & 1u) {
         const int j = g * kCoopSeg + tid * kCoopPer + u;
-        out[before + off] = j;
+        // Always inside the row's picks, unless a timed-out wait (a flagged
+        // error) left the counts short.
+        KVSEL_DEBUG_CHECK(before + off < (uint32_t)count && j < P, a.err);
+        if (before + off < (uint32_t)count) out[before + off] = j;
         picks[off++] = j;
       }
     __syncthreads();
     KVSEL_SELROWS_MARK(6);
-    if (RU > 0) copy((int)before, (int)ntot, 0, picks);
+    if (RU > 0) copy((int)before, (int)min(ntot, before < (uint32_t)count ? (uint32_t)count - before : 0u), 0, picks);
     if (g == nseg - 1 && W > 0) {  // the window follows the picks
       for (int i = tid; i < W; i += kCoopThreads) out[count + i] = P + i;
       if (RU > 0) copy(count, W, P, nullptr);
@@ -1367,6 +1375,22 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   }
   KVSEL_SELROWS_MARK(13);
   (void)lane;
+}
+
+int debug_flags_read(int reset) {
+#ifdef KVSEL_DEBUG
+  unsigned v = 0u;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_word), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  if (reset) {
+    const unsigned zero = 0u;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
+      return -1;
+  }
+  return (int)v;
+#else
+  (void)reset;
+  return -1;
+#endif
 }
 
 int coop_max_segments() { return kCoopMaxSeg; }
@@ -1480,8 +1504,10 @@ __global__ void refresh_finish_kernel(int rows, int n, int keep, int head, int t
   int idx;
   if (m < head)
     idx = m;
-  else if (picked)
+  else if (picked) {
+    KVSEL_DEBUG_CHECK(indices[e] >= 0 && indices[e] < n - head, nullptr);
     idx = min(max(indices[e], 0), n - head - 1) + head;
+  }
   else
     idx = n - tail + (m - head);
   indices[e] = idx;

@@ -237,3 +237,66 @@ def test_options(B):
     assert lib.kvsel_set_option(3, 0) == 0 and lib.kvsel_get_option(3) == 0
     assert lib.kvsel_set_option(0, 1) == 0 and lib.kvsel_get_option(0) == 1
     assert lib.kvsel_set_option(0, 0) == 0 and lib.kvsel_get_option(0) == 0
+
+
+# ---------------------------------------------------------------- host sanitizers
+
+def _sanitized_plan_check():
+    """Build tests/host_check/plan_check.cpp against the library sources with
+    AddressSanitizer and UndefinedBehaviorSanitizer on the host code (the
+    device code is compiled as usual and never launched), once per source
+    digest, into tests/host_check/_build."""
+    import hashlib
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc is not installed")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    csrc = os.path.join(root, "prompt_kv_selection_amd", "csrc")
+    srcs = [os.path.join(csrc, f"kvsel_{s}.hip") for s in ("api", "score", "select", "fused", "jacap", "probe")]
+    deps = srcs + [os.path.join(here, "host_check", "plan_check.cpp"), os.path.join(root, "include", "kvsel.h")]
+    deps += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith(".h")]
+    digest = hashlib.sha256(b"".join(open(p, "rb").read() for p in deps)).hexdigest()[:16]
+    build = os.path.join(here, "host_check", "_build")
+    exe = os.path.join(build, f"plan_check_{digest}")
+    if os.path.exists(exe):
+        return exe
+    os.makedirs(build, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-Wno-unused-function",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I" + os.path.join(root, "include"), "-I" + csrc] + san
+    objs, procs = [], []
+    for src in srcs + [os.path.join(here, "host_check", "plan_check.cpp")]:
+        obj = os.path.join(build, os.path.basename(src) + f".{digest}.o")
+        objs.append(obj)
+        procs.append(subprocess.Popen([hipcc] + flags + ["-c", src, "-o", obj], stdout=subprocess.PIPE,
+                                      stderr=subprocess.STDOUT))
+    for p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        assert p.returncode == 0, out[-3000:]
+    r = subprocess.run([hipcc, "--offload-arch=gfx950"] + san + ["-o", exe] + objs, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    for o in objs:
+        os.remove(o)
+    return exe
+
+
+def test_validation_and_planning_under_sanitizers():
+    """Argument validation and workspace planning of every entry point run
+    clean under ASan and UBSan: no out-of-bounds host access (the cu_L and C
+    arrays are exactly sized heap blocks), no signed overflow or other
+    undefined behaviour, and the expected return codes.  No call reaches the
+    device (invalid arguments, or a workspace one byte short)."""
+    import subprocess
+    exe = _sanitized_plan_check()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:exitcode=99",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1:exitcode=98")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    out = r.stdout + r.stderr
+    assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
+    assert r.returncode == 0, out[-4000:]
+    assert "plan_check: 0 unexpected" in out
