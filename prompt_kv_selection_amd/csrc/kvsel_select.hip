@@ -818,8 +818,8 @@ __device__ __forceinline__ float pool_window(const float (&w)[KW]) {
 // means every bin is final.  Each segment then publishes its counts above
 // and on tau (one 64-bit word, zero until written), and from the earlier
 // segments' counts knows where its picks go: it writes them in index order
-// (tau-equal ones lowest index first) and copies their K and V rows; the
-// last segment adds the window.  The grid must be resident at once; the
+// (tau-equal ones lowest index first) and copies their K and V rows, and a
+// share of the window's rows.  The grid must be resident at once; the
 // residency handshake decides this, and otherwise the first workgroup of
 // each row runs every segment of its row in turn, with the same arithmetic
 // and results.
@@ -1367,9 +1367,10 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     __syncthreads();
     KVSEL_SELROWS_MARK(6);
     if (RU > 0) copy((int)before, (int)min(ntot, before < (uint32_t)count ? (uint32_t)count - before : 0u), 0, picks);
-    if (g == nseg - 1 && W > 0) {  // the window follows the picks
-      for (int i = tid; i < W; i += kCoopThreads) out[count + i] = P + i;
-      if (RU > 0) copy(count, W, P, nullptr);
+    if (W > 0) {  // the window follows the picks: each segment writes and copies a share of its rows
+      const int w0 = (int)((long long)g * W / nseg), w1 = (int)((long long)(g + 1) * W / nseg);
+      for (int i = w0 + tid; i < w1; i += kCoopThreads) out[count + i] = P + i;
+      if (RU > 0 && w1 > w0) copy(count + w0, w1 - w0, P + w0, nullptr);
     }
     __syncthreads();  // picks[] is rewritten by the next segment
   }
