@@ -117,9 +117,33 @@ enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 };
  *   counters instead (statistics and votes per chunk, two passes over K, then
  *   each row's selection in one workgroup).  KVSEL_OPT_FORCE_FALLBACK forces
  *   that too.
+ * KVSEL_OPT_SELECT picks the selection kernels (when the selection is not
+ *   fused into the scoring kernel):
+ *   KVSEL_SELECT_AUTO (default): the cooperative selection where its grid
+ *     fits the device at once, else the split selection where it applies
+ *     (pooling widths 1, 3, 5, 7 and at most 65535 prefix positions per
+ *     prompt), else the per-row or segment-parallel chain;
+ *   KVSEL_SELECT_SPLIT: the split selection only; calls it does not cover
+ *     return KVSEL_EUNSUPPORTED;
+ *   KVSEL_SELECT_EXCHANGE: never the split selection: the cooperative
+ *     selection where its grid fits the device, else the per-row or
+ *     segment-parallel chain.
+ *   The split selection gives each row S workgroups that each find the
+ *   row's threshold on their own and write and copy a share of its output;
+ *   no workgroup waits for another, so it suits calls with more rows than
+ *   the device holds at once.  The indices and K/V rows are identical on
+ *   every path.  The option applies to kvsel_topk and kvsel_refresh too
+ *   (rows of at most 65535 scores; AUTO takes the split selection there).
  * Not thread-safe with respect to concurrent calls. */
-enum { KVSEL_OPT_SCORING = 0, KVSEL_OPT_FORCE_FALLBACK = 1, KVSEL_OPT_VALIDATE = 2, KVSEL_OPT_FUSED_SELECT = 3 };
+enum {
+  KVSEL_OPT_SCORING = 0,
+  KVSEL_OPT_FORCE_FALLBACK = 1,
+  KVSEL_OPT_VALIDATE = 2,
+  KVSEL_OPT_FUSED_SELECT = 3,
+  KVSEL_OPT_SELECT = 4
+};
 enum { KVSEL_SCORING_AUTO = 0, KVSEL_SCORING_TWO_PASS = 1, KVSEL_SCORING_SINGLE_READ = 2 };
+enum { KVSEL_SELECT_AUTO = 0, KVSEL_SELECT_SPLIT = 1, KVSEL_SELECT_EXCHANGE = 2 };
 int kvsel_set_option(int option, int value);
 int kvsel_get_option(int option);
 
@@ -194,7 +218,10 @@ int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned*
  * SELECT_COOP (one cooperative launch: pooling, top-k, picks and the K/V
  * copy), SELECT_ROWS (a workgroup per row, then the gather), SELECT_SEGMENTS
  * (the segment-parallel chain), SELECT_FUSED (the selection inside the
- * single-read scoring kernel).  0 before the first call. */
+ * single-read scoring kernel), SELECT_SPLIT (one launch, S workgroups per row
+ * that each find the threshold and copy a share of the rows).  kvsel_topk and
+ * kvsel_refresh record their selection kernels too.  0 before the first
+ * call. */
 #define KVSEL_PATH_SINGLE_READ 0x1u
 #define KVSEL_PATH_TWO_PASS 0x2u
 #define KVSEL_PATH_VOTES_ONLY 0x4u
@@ -204,6 +231,7 @@ int kvsel_status_flags(const void* workspace, void* stream, int reset, unsigned*
 #define KVSEL_PATH_SELECT_ROWS 0x40u
 #define KVSEL_PATH_SELECT_SEGMENTS 0x80u
 #define KVSEL_PATH_SELECT_FUSED 0x100u
+#define KVSEL_PATH_SELECT_SPLIT 0x200u
 unsigned kvsel_last_path(void);
 
 /* Workspace bytes kvsel_select needs for these sizes; 0 if the arguments are

@@ -50,7 +50,8 @@ FLAG = {"exchange_wait": 0x1, "lds_wait": 0x2, "select_wait": 0x4, "nonfinite": 
 lib.kvsel_debug_flags.restype = _i
 lib.kvsel_debug_flags.argtypes = [_i]
 PATH = {"single_read": 0x1, "two_pass": 0x2, "votes_only": 0x4, "handed_over": 0x8, "bypass": 0x10,
-        "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80, "select_fused": 0x100}
+        "select_coop": 0x20, "select_rows": 0x40, "select_segments": 0x80, "select_fused": 0x100,
+        "select_split": 0x200}
 lib.kvsel_probe_sink_bytes.restype = _sz
 lib.kvsel_probe_sink_bytes.argtypes = []
 lib.kvsel_probe_stream.restype = _i
@@ -364,6 +365,8 @@ KVSEL_OPT_SCORING = 0
 KVSEL_OPT_FORCE_FALLBACK = 1
 KVSEL_OPT_VALIDATE = 2
 KVSEL_OPT_FUSED_SELECT = 3
+KVSEL_OPT_SELECT = 4
+KVSEL_SELECT_AUTO, KVSEL_SELECT_SPLIT, KVSEL_SELECT_EXCHANGE = 0, 1, 2
 SCORING = {"auto": 0, "two_pass": 1, "single_read": 2}
 lib.kvsel_set_option.restype = _i
 lib.kvsel_set_option.argtypes = [_i, _i]

@@ -119,6 +119,7 @@ int g_scoring = KVSEL_SCORING_AUTO;
 int g_force_fallback = 0;
 int g_validate = 0;
 int g_fused_select = 0;
+int g_select = KVSEL_SELECT_AUTO;
 
 // Per-call tokens of the fused selection: the arrival and decision words and
 // the tagged flag word carry them, so nothing has to be cleared before a
@@ -411,23 +412,61 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     any_fsel = any_fsel || ok;
     any_old = any_old || !ok;
   }
-  std::vector<int> coop_segs(ngroups, 0);
-  bool any_coop = false;
-  for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
-    if (fsel[gi]) continue;
+  // Groups the cooperative selection takes (AUTO prefers it where its grid
+  // fits the device: its workgroups share a row's keys, where the split
+  // selection's each redo the whole row).
+  auto coop_segments = [&](int b0) {
     const int nb = std::min(kMaxSegs, p.B - b0);
     int segs = 1;
     for (int b = b0; b < b0 + nb; ++b) {
       const int n = p.L[b] < p.C[b] ? p.L[b] : p.L[b] - p.W;
       segs = std::max(segs, (n + coop_segment() - 1) / coop_segment());
     }
-    if (segs <= coop_max_segments() && (long long)segs * nb * p.heads <= coop_cap) {
-      coop_segs[gi] = segs;
-      any_coop = true;
+    return segs <= coop_max_segments() && (long long)segs * nb * p.heads <= coop_cap ? segs : 0;
+  };
+  // The split selection per launch group: S workgroups per row, S as large
+  // as the device holds at once (more rows than that: one each), and large
+  // enough that a workgroup's share of the picks fits its list.
+  std::vector<int> split_s(ngroups, 0), split_k(ngroups, 0);
+  bool any_split = false;
+  if (g_select != KVSEL_SELECT_EXCHANGE && (kernel == 1 || kernel == 3 || kernel == 5 || kernel == 7)) {
+    for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
+      if (fsel[gi] || (g_select == KVSEL_SELECT_AUTO && coop_segments(b0) > 0)) continue;
+      const int nb = std::min(kMaxSegs, p.B - b0);
+      int maxP = 0, maxCount = 0;
+      for (int b = b0; b < b0 + nb; ++b)
+        if (p.L[b] >= p.C[b]) {
+          maxP = std::max(maxP, p.L[b] - p.W);
+          maxCount = std::max(maxCount, p.C[b] - p.W);
+        }
+      const int kpt = split_kpt(maxP);
+      if (kpt == 0) continue;
+      const int rows = nb * p.heads;
+      const int cap = split_grid_capacity(kpt, p.D, p.dtype);
+      int S = std::max(1, std::min(split_max_splits(), cap / rows));
+      S = std::max(S, (maxCount + split_list_capacity(kpt) - 1) / split_list_capacity(kpt));
+      if (S > split_max_splits()) continue;
+      split_s[gi] = S;
+      split_k[gi] = kpt;
+      any_split = true;
     }
   }
-  bool all_coop = true;
-  for (int gi = 0; gi < ngroups; ++gi) all_coop = all_coop && (fsel[gi] || coop_segs[gi] > 0);
+  if (g_select == KVSEL_SELECT_SPLIT)
+    for (int gi = 0; gi < ngroups; ++gi)
+      if (!fsel[gi] && split_s[gi] == 0)
+        return fail(KVSEL_EUNSUPPORTED, "the split selection does not cover this call (pooling widths 1, 3, 5, 7; at "
+                                        "most %d prefix positions)", split_max_positions());
+  std::vector<int> coop_segs(ngroups, 0);
+  bool any_coop = false;
+  for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
+    if (fsel[gi] || split_s[gi] > 0) continue;
+    coop_segs[gi] = coop_segments(b0);
+    any_coop = any_coop || coop_segs[gi] > 0;
+  }
+  // Groups left to the per-row or segment-parallel chain (which use the
+  // pooled scores' histograms).
+  bool no_chain = true;
+  for (int gi = 0; gi < ngroups; ++gi) no_chain = no_chain && (fsel[gi] || coop_segs[gi] > 0 || split_s[gi] > 0);
   unsigned* err = (unsigned*)ws;  // the header's error word
   {
     unsigned path = 0u;
@@ -437,7 +476,8 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     for (int b = 0; b < p.B; ++b)
       if (p.L[b] < p.C[b]) path |= KVSEL_PATH_BYPASS;
     if (any_coop) path |= KVSEL_PATH_SELECT_COOP;
-    if (!all_coop) path |= whole_rows ? KVSEL_PATH_SELECT_ROWS : KVSEL_PATH_SELECT_SEGMENTS;
+    if (any_split) path |= KVSEL_PATH_SELECT_SPLIT;
+    if (!no_chain) path |= whole_rows ? KVSEL_PATH_SELECT_ROWS : KVSEL_PATH_SELECT_SEGMENTS;
     if (any_fsel) path |= KVSEL_PATH_SELECT_FUSED;
     g_last_path = path;
   }
@@ -454,7 +494,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     // the two-pass path without the cooperative selection the statistics
     // kernel clears the histograms).  Exchange records, status words and
     // histograms are contiguous, then the cooperative selection's words.
-    const bool hists = !all_coop && (use_fused || lse != nullptr);
+    const bool hists = !no_chain && (use_fused || lse != nullptr);
     const size_t lo1 = use_fused ? p.off_ctr : p.off_hist;
     const size_t hi1 = hists ? p.off_coop : (use_fused ? p.off_hist : lo1);
     ZeroRanges z{};
@@ -589,6 +629,14 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, nullptr, votes, row_stats, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     }
+    if (split_s[b0 / kMaxSegs] > 0) {
+      e = timed("select", st, [&] {
+        return launch_select_split(a, rows, split_s[b0 / kMaxSegs], split_k[b0 / kMaxSegs], p.dtype, votes, pooled_opt,
+                                   indices, K, V, K_out, V_out, st);
+      });
+      if (e != hipSuccess) return device_error(e, "select launch");
+      continue;
+    }
     if (coop_segs[b0 / kMaxSegs] > 0) {
       unsigned* cstatus = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * (b0 / kMaxSegs);
       unsigned* crows = (unsigned*)(ws + p.off_coop) +
@@ -709,6 +757,11 @@ int kvsel_set_option(int option, int value) {
     g_fused_select = value;
     return ok();
   }
+  if (option == KVSEL_OPT_SELECT) {
+    if (value < KVSEL_SELECT_AUTO || value > KVSEL_SELECT_EXCHANGE) return fail(KVSEL_EINVAL, "invalid select value %d", value);
+    g_select = value;
+    return ok();
+  }
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
@@ -717,6 +770,7 @@ int kvsel_get_option(int option) {
   if (option == KVSEL_OPT_FORCE_FALLBACK) return g_force_fallback;
   if (option == KVSEL_OPT_VALIDATE) return g_validate;
   if (option == KVSEL_OPT_FUSED_SELECT) return g_fused_select;
+  if (option == KVSEL_OPT_SELECT) return g_select;
   return fail(KVSEL_EINVAL, "unknown option %d", option);
 }
 
@@ -925,6 +979,30 @@ static int run_topk(Launch& a, int rows, const float* scores, int32_t* out, void
   uint32_t* segcnt = (uint32_t*)((char*)cut + align256((size_t)rows * kCutBytes));
   uint32_t* cand = (uint32_t*)((char*)segcnt + align256((size_t)rows * kSegCntBytes));
   hipError_t e = hipSuccess;
+  // The split selection (indices only, no pooling) where it covers the rows.
+  const int W = a.window ? a.W : 0;
+  const int kpt = g_select != KVSEL_SELECT_EXCHANGE ? split_kpt(n - W) : 0;
+  if (kpt > 0) {
+    const int count = s.C - W;
+    int S = std::max(1, std::min(split_max_splits(), split_grid_capacity(kpt, 0, 0) / rows));
+    S = std::max(S, (count + split_list_capacity(kpt) - 1) / split_list_capacity(kpt));
+    if (S <= split_max_splits()) {
+      Launch b = a;
+      b.kernel = 1;
+      b.pooling = KVSEL_POOL_AVG;
+      e = timed("select", st, [&] {
+        return launch_select_split(b, rows, S, kpt, KVSEL_F32, scores, nullptr, out, nullptr, nullptr, nullptr, nullptr,
+                                   st);
+      });
+      if (e != hipSuccess) return device_error(e, "select launch");
+      g_last_path = KVSEL_PATH_SELECT_SPLIT;
+      return ok();
+    }
+  }
+  if (g_select == KVSEL_SELECT_SPLIT)
+    return fail(KVSEL_EUNSUPPORTED, "the split selection does not cover rows of %d scores (at most %d)", n - W,
+                split_max_positions());
+  g_last_path = n <= select_rows_max() ? KVSEL_PATH_SELECT_ROWS : KVSEL_PATH_SELECT_SEGMENTS;
   if (!hist_zeroed) {  // otherwise an earlier kernel of the call cleared the histograms
     e = timed("fill", st, [&] { return launch_fill_u32(hist, (long long)rows * 2048, 0u, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");

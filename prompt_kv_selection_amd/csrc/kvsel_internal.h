@@ -223,6 +223,21 @@ int coop_grid_capacity(int D, int dtype);
 hipError_t launch_select_coop(const Launch& a, int rows, int segs, int dtype, const float* votes, float* pooled,
                               unsigned* coop, unsigned* status, int32_t* indices, const void* K, const void* V,
                               void* K_out, void* V_out, hipStream_t st);
+// Split selection: rows * splits workgroups, each finding its row's
+// threshold and writing and copying slots [split * count / splits, (split
+// + 1) * count / splits) of the picks and a share of the window (pooling
+// widths 1, 3, 5, 7).  split_kpt() gives the kernel variant (1 ..)
+// covering max_p prefix positions (0: none, above split_max_positions()); a
+// workgroup's share of the picks must fit split_list_capacity(variant)
+// entries.  pooled may be nullptr.  Needs no zeroed words.
+int split_kpt(int max_p);
+int split_max_positions();
+int split_max_splits();
+int split_list_capacity(int kpt);
+int split_grid_capacity(int kpt, int D, int dtype);
+hipError_t launch_select_split(const Launch& a, int rows, int splits, int kpt, int dtype, const float* votes,
+                               float* pooled, int32_t* indices, const void* K, const void* V, void* K_out, void* V_out,
+                               hipStream_t st);
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns

@@ -27,6 +27,8 @@
 // in index order, writes its picks (the lowest tau-equal indices first) at
 // their final slots, and copies their K and V rows.
 
+#include <mutex>
+
 #include "kvsel_internal.h"
 
 // Instrumentation hook at the phases of the select kernel (point 0..4);
@@ -896,7 +898,7 @@ __device__ __forceinline__ void coop_keys(const float* __restrict__ v, int P, in
   const int tid = threadIdx.x, j0 = g * kCoopSeg;
   const float pad = MAX ? -INFINITY : 0.f;
   auto at = [](int i) {  // LDS index of segment position i (-r <= i < kCoopSeg + r)
-    return i < 0 ? kCoopHalo + (i + r) : (i >= kCoopSeg ? kCoopHalo + 2 * r + (i - kCoopSeg)
+    return i < 0 ? kCoopHalo + (i + r) : (i >= kCoopSeg ? kCoopHalo + r + (i - kCoopSeg)
                                                          : (i / kCoopPer) * kCoopStride + i % kCoopPer);
   };
   __syncthreads();  // the previous segment's reads are done
@@ -1007,26 +1009,27 @@ __device__ void coop_read_candidates(const unsigned long long* cnt, int nseg, co
 // Copy output rows m0 .. m0 + n of K and V from source rows first + i
 // (sel == nullptr) or sel[i] (LDS), RU 16-byte pieces per row, consecutive
 // threads on consecutive pieces, four pieces of each in flight per thread.
-template <int RU>
-__device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const int32_t* sel, long long in_row0,
+// Source rows are clamped into the head's L rows: never a read outside them.
+template <int RU, int NT = kCoopThreads, int kFly = 4>
+__device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const int32_t* sel, int L, long long in_row0,
                                                long long out_row0, const uint4* __restrict__ K,
                                                const uint4* __restrict__ V, uint4* __restrict__ Ko,
                                                uint4* __restrict__ Vo) {
-  constexpr int kFly = 4;
   const int total = n * RU, tid = threadIdx.x;
-  for (int e0 = 0; e0 < total; e0 += kFly * kCoopThreads) {
+  for (int e0 = 0; e0 < total; e0 += kFly * NT) {
     uint4 kv[kFly], vv[kFly];
 #pragma unroll
     for (int f = 0; f < kFly; ++f) {
-      const int e = min(e0 + f * kCoopThreads + tid, total - 1);
+      const int e = min(e0 + f * NT + tid, total - 1);
       const int i = e / RU;
-      const long long from = (in_row0 + (sel ? sel[i] : first + i)) * RU + e % RU;
+      const int src = min(max(sel ? sel[i] : first + i, 0), L - 1);
+      const long long from = (in_row0 + src) * RU + e % RU;
       kv[f] = K[from];
       vv[f] = V[from];
     }
 #pragma unroll
     for (int f = 0; f < kFly; ++f) {
-      const int e = e0 + f * kCoopThreads + tid;
+      const int e = e0 + f * NT + tid;
       if (e < total) {
         const long long to = (out_row0 + m0 + e / RU) * RU + e % RU;
         Ko[to] = kv[f];
@@ -1075,7 +1078,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   // Output rows m0 .. m0 + n from source rows first + i (sel == nullptr)
   // or sel[i].
   auto copy = [&](int m0, int n, int first, const int32_t* sel) {
-    coop_copy_rows<RU>(m0, n, first, sel, in_row0, out_row0, K, V, Ko, Vo);
+    coop_copy_rows<RU>(m0, n, first, sel, s.L, in_row0, out_row0, K, V, Ko, Vo);
   };
   if (s.L < s.C) {  // bypass: every position, segment by segment
     if (tid == 0) s_go = decide(status, arrived, a.err, kFlagSelectFallback, a.residency_ticks);
@@ -1444,6 +1447,459 @@ hipError_t launch_select_coop(const Launch& a, int rows, int segs, int dtype, co
       return launch_select_coop_ru<16>(a, grid, votes, pooled, coop, status, indices, k, v, ko, vo, st);
     case 32:
       return launch_select_coop_ru<32>(a, grid, votes, pooled, coop, status, indices, k, v, ko, vo, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+// ---- split selection: every workgroup of a row finds the threshold itself
+//
+// A row is split over S workgroups of NT threads.  Each of them
+// stages the row's votes through LDS with coalesced loads, pools them into
+// keys held in registers (thread t owns the KPT consecutive positions
+// t * KPT ...), and finds the threshold tau of the (C-W)-th largest key and
+// how many tau-equal positions are still needed.  Every workgroup of the row
+// sees every key, so all of them find the same tau.  A workgroup then writes
+// only its share of the output: the picks whose slots (index order, tau-equal
+// positions lowest index first) fall in [split * count / S, (split + 1) *
+// count / S), and a share of the window's slots, and copies those K and V
+// rows.  No workgroup waits for another: there is no residency requirement
+// and no exchange through memory, at the price of S reads of the row's votes
+// (from the last-level cache after the first).
+//
+// First digit of tau (bits 31..21 of the key): one key per thread forms a
+// sample, whose histogram gives an estimate b of the boundary bin.  Each
+// thread then counts its keys above b + 3 and in each of the bins b - 3 ..
+// b + 3 (packed counters in registers, no atomics per key); the boundary bin
+// follows exactly from these counts whenever it lies in that window, and
+// otherwise from a full histogram of the first digit (LDS atomics).  The
+// other 21 bits come from three 7-bit digits over the boundary bin's keys,
+// compacted into LDS when they fit there.
+constexpr int kSplitWin = 7;   // first-digit bins counted exactly, centred on the estimate
+constexpr int kSplitMaxS = 64;  // workgroups per row
+constexpr int kSplitStage = 16384;  // positions staged in LDS at a time (at most)
+
+// NT threads with KPT keys each; the row is staged in rounds of kStage
+// positions, each held by kOwners threads.
+template <int NT, int KPT>
+struct SplitGeom {
+  static constexpr int kStage = NT * KPT < kSplitStage ? NT * KPT : kSplitStage;
+  static constexpr int kRounds = NT * KPT / kStage;
+  static constexpr int kOwners = kStage / KPT;
+  static constexpr int kLoads = kStage / NT;          // coalesced loads per thread per round
+  static constexpr int kStride = KPT + 1;             // LDS words per owner (odd: conflict-free)
+  static constexpr int kHalo = kOwners * kStride;     // LDS index of the halo slots
+  static constexpr int kWords = kHalo + 2 * 3;        // staging words (pooling radius up to 3)
+  static_assert(kRounds * kStage == NT * KPT && kOwners * kRounds == NT, "rounds hold whole owners");
+};
+
+// Keys of the calling thread's KPT positions: pooled votes of row v
+// (P positions; 0 past P), staged through LDS round by round.
+template <int NT, int KPT, int KW, bool MAX>
+__device__ __forceinline__ void split_keys(const float* __restrict__ v, int P, float* sv, uint32_t (&key)[KPT]) {
+  using G = SplitGeom<NT, KPT>;
+  constexpr int r = KW / 2;
+  constexpr int kLoads = G::kLoads;
+  const float pad = MAX ? -INFINITY : 0.f;
+  auto at = [](int i) {  // LDS index of round position i (-r <= i < kOwners * KPT + r)
+    return i < 0 ? G::kHalo + (i + r)
+                 : (i >= G::kOwners * KPT ? G::kHalo + r + (i - G::kOwners * KPT) : (i / KPT) * G::kStride + i % KPT);
+  };
+#pragma unroll
+  for (int rd = 0; rd < G::kRounds; ++rd) {
+    const int j0 = rd * G::kOwners * KPT;
+    if (rd > 0) __syncthreads();  // the previous round's reads are done
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // each round derives its own addresses (none kept across rounds)
+    float tv[kLoads];
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int p = j0 + q * NT + tid;
+      tv[q] = p < P ? v[p] : pad;
+    }
+    float hl = pad, hh = pad;
+    if (tid < r) {
+      const int pl = j0 - r + tid, ph = j0 + G::kOwners * KPT + tid;
+      hl = pl >= 0 && pl < P ? v[pl] : pad;
+      hh = ph < P ? v[ph] : pad;
+    }
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) sv[at(q * NT + tid)] = tv[q];
+    if (tid < r) {
+      sv[at(tid - r)] = hl;
+      sv[at(G::kOwners * KPT + tid)] = hh;
+    }
+    __syncthreads();
+    const int own = tid - rd * G::kOwners;  // this thread's place among the round's owners
+    if (own >= 0 && own < G::kOwners) {
+      float w[KW];
+      const int i0 = own * KPT;
+#pragma unroll
+      for (int q = 0; q < KW - 1; ++q) w[q + 1] = sv[at(i0 - r + q)];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+#pragma unroll
+        for (int q = 0; q < KW - 1; ++q) w[q] = w[q + 1];
+        w[KW - 1] = sv[at(i0 + u + r)];
+        key[u] = j0 + i0 + u < P ? score_key(__float_as_uint(pool_window<KW, MAX>(w))) : 0u;
+        if ((u & 15) == 15) asm volatile("" ::: "memory");  // LDS reads in groups of 16 keys (register pressure)
+      }
+    }
+  }
+  __syncthreads();  // sv is free for the candidates and the pick list
+}
+
+// An empty asm per key: values derived from the keys (their bins, the
+// comparisons) are not kept across phases, which would double the registers.
+template <int KPT>
+__device__ __forceinline__ void split_launder(uint32_t (&key)[KPT]) {
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) asm volatile("" : "+v"(key[u]));
+}
+
+template <int NT, int KPT, int RU>
+__global__ __launch_bounds__(NT) void select_split_kernel(const Launch a, int rows, int splits,
+                                                                     const float* __restrict__ votes,
+                                                                     float* __restrict__ pooled,
+                                                                     int32_t* __restrict__ indices,
+                                                                     const uint4* __restrict__ K,
+                                                                     const uint4* __restrict__ V,
+                                                                     uint4* __restrict__ Ko, uint4* __restrict__ Vo) {
+  using G = SplitGeom<NT, KPT>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Workgroup b serves row b % rows, split b / rows: the splits of a row are
+  // rows apart, which keeps them on one XCD when rows is a multiple of 8.
+  const int row = (int)blockIdx.x % rows, sp = (int)blockIdx.x / rows;
+  __shared__ float sv[G::kWords];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_h7[3 * 128];
+  __shared__ uint32_t sh[32];
+  __shared__ uint32_t s_win[kSplitWin + 1];
+  __shared__ uint32_t s_digit, s_need;
+  KVSEL_SELROWS_MARK(0);
+  const Seg& s = a.seg[find_seg<kFieldRow>(a, row)];
+  const int h = s.h0 + (row - s.row0);
+  int32_t* out = indices + s.idx_off + (long long)h * s.idx_ld;
+  // RU == 0: indices only (no K/V rows; a.D may be 0).
+  const long long in_row0 = RU > 0 ? s.kv_off / a.D + (long long)kv_head(a, h) * s.L : 0;
+  const long long out_row0 = RU > 0 ? s.out_off + (long long)h * s.out_ld : 0;
+  auto copy = [&](int m0, int n, int first, const int32_t* sel) {
+    if constexpr (RU > 0) coop_copy_rows<RU, NT, 8>(m0, n, first, sel, s.L, in_row0, out_row0, K, V, Ko, Vo);
+  };
+  if (s.L < s.C) {  // bypass: every position; this split's share of them
+    const int m0 = (int)((long long)sp * s.L / splits), m1 = (int)((long long)(sp + 1) * s.L / splits);
+    for (int m = m0 + tid; m < m1; m += NT) out[m] = m;
+    if (m1 > m0) copy(m0, m1 - m0, m0, nullptr);
+    return;
+  }
+  const int W = a.window ? a.W : 0;
+  const int P = s.L - W, count = s.C - W;
+  const float* v = votes + s.vote_off + (long long)h * s.vote_ld;
+  if (tid < 3 * 128) s_h7[tid] = 0u;
+  for (int d = tid; d < 2048; d += NT) hist[d] = 0u;
+  if (tid <= kSplitWin) s_win[tid] = 0u;
+  if (tid == 0) {
+    s_digit = 0u;
+    s_need = 0u;
+  }
+
+  uint32_t key[KPT];
+  {
+    const bool mx = a.pooling == 1;
+    switch (a.kernel) {
+      case 1: split_keys<NT, KPT, 1, false>(v, P, sv, key); break;
+      case 3: if (mx) split_keys<NT, KPT, 3, true>(v, P, sv, key); else split_keys<NT, KPT, 3, false>(v, P, sv, key); break;
+      case 5: if (mx) split_keys<NT, KPT, 5, true>(v, P, sv, key); else split_keys<NT, KPT, 5, false>(v, P, sv, key); break;
+      default: if (mx) split_keys<NT, KPT, 7, true>(v, P, sv, key); else split_keys<NT, KPT, 7, false>(v, P, sv, key); break;
+    }
+  }
+  const int n = max(0, min(KPT, P - tid * KPT));  // this thread's valid positions
+  split_launder(key);
+  KVSEL_SELROWS_MARK(1);
+  if (pooled != nullptr && sp == 0) {
+    float* o = pooled + s.vote_off + (long long)h * s.vote_ld + tid * KPT;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (u < n) o[u] = __uint_as_float(key[u]);
+  }
+
+  // Sample estimate of the boundary bin: one key per thread (two offsets,
+  // alternating, against periodic patterns).
+  const uint32_t k = (uint32_t)count;
+  const int us = (tid & 1) ? KPT / 4 : (3 * KPT) / 4;
+  uint32_t skey = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (u == us) skey = key[u];
+  const bool has_sample = us < n;
+  if (has_sample) atomicAdd(&hist[skey >> 21], 1u);
+  uint32_t m;
+  (void)block_scan<NT>(has_sample ? 1u : 0u, sh, m);  // also orders the adds before the reads
+  int lo = 0;
+  bool found = false;
+  uint32_t b = 0u, need = k, ncand = 0u;
+  if (m > 0) {
+    const uint32_t rho = (uint32_t)min((unsigned long long)m, ((unsigned long long)k * m + (P - 1)) / (unsigned long long)P);
+    pick_digit<NT>(hist, 2048, rho < 1u ? 1u : rho, sh, &s_digit, &s_need);
+    lo = (int)s_digit - kSplitWin / 2;
+    KVSEL_SELROWS_MARK(2);
+    // Exact counts of the window's bins and of the keys above it.
+    uint32_t above = 0u;
+    unsigned long long c03 = 0ull, c46 = 0ull;  // 16-bit counters of bins lo .. lo + 3 and lo + 4 .. lo + 6
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int d = (int)(key[u] >> 21) - lo;
+      const bool valid = u < n;
+      above += valid && d >= kSplitWin;
+      if (valid && d >= 0 && d < 4) c03 += 1ull << (16 * d);
+      if (valid && d >= 4 && d < kSplitWin) c46 += 1ull << (16 * (d - 4));
+    }
+    // Per wave each field is at most 64 * KPT < 2^16.
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      above += __shfl_xor(above, o);
+      c03 += __shfl_xor(c03, o);
+      c46 += __shfl_xor(c46, o);
+    }
+    if (lane == 0) {
+      atomicAdd(&s_win[kSplitWin], above);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) atomicAdd(&s_win[d], (uint32_t)(c03 >> (16 * d)) & 0xFFFFu);
+#pragma unroll
+      for (int d = 4; d < kSplitWin; ++d) atomicAdd(&s_win[d], (uint32_t)(c46 >> (16 * (d - 4))) & 0xFFFFu);
+    }
+    __syncthreads();
+    split_launder(key);
+    KVSEL_SELROWS_MARK(3);
+    uint32_t cum = s_win[kSplitWin];
+    for (int d = kSplitWin - 1; d >= 0 && !found && cum < k; --d) {
+      const uint32_t c = s_win[d];
+      if (lo + d >= 0 && cum + c >= k) {
+        found = true;
+        b = (uint32_t)(lo + d);
+        need = k - cum;
+        ncand = c;
+      }
+      cum += c;
+    }
+  }
+  if (!found) {  // the window missed (or no sample): the full first-digit histogram
+    KVSEL_SELROWS_MARK(9);
+    __syncthreads();
+    for (int d = tid; d < 2048; d += NT) hist[d] = 0u;
+    __syncthreads();
+    uint32_t run_bin = 0xFFFFFFFFu, run_len = 0u;  // equal bins of consecutive positions: one add per run
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      if (u < n) {
+        const uint32_t bin = key[u] >> 21;
+        if (bin != run_bin) {
+          if (run_len) atomicAdd(&hist[run_bin], run_len);
+          run_bin = bin;
+          run_len = 0u;
+        }
+        ++run_len;
+      }
+    }
+    if (run_len) atomicAdd(&hist[run_bin], run_len);
+    __syncthreads();
+    pick_digit<NT>(hist, 2048, k, sh, &s_digit, &s_need);
+    b = s_digit;
+    need = s_need;
+    ncand = hist[b];
+  }
+  split_launder(key);
+
+  // The boundary bin's keys into LDS (any order), when they fit.
+  uint32_t* cl = reinterpret_cast<uint32_t*>(sv);
+  const bool in_lds = ncand <= (uint32_t)G::kWords;
+  if (in_lds) {
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) mine += u < n && (key[u] >> 21) == b;
+    uint32_t tot;
+    uint32_t off = block_scan<NT>(mine, sh, tot) - mine;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (u < n && (key[u] >> 21) == b) cl[off++] = key[u];
+    __syncthreads();
+  }
+  split_launder(key);
+  KVSEL_SELROWS_MARK(4);
+  // The other 21 bits in three 7-bit digits: each digit's 128-bin histogram
+  // (LDS atomics), then one wave finds the bin holding the need-th largest.
+  uint32_t t = b << 21;
+  for (int dg = 0; dg < 3; ++dg) {
+    const int shift = 14 - 7 * dg;
+    const uint32_t hi = ~((1u << (shift + 7)) - 1u);  // tau's bits found so far
+    uint32_t* h7 = s_h7 + 128 * dg;
+    if (in_lds) {
+      for (int i = tid; i < (int)ncand; i += NT)
+        if ((cl[i] & hi) == t) atomicAdd(&h7[(cl[i] >> shift) & 127u], 1u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (u < n && (key[u] & hi) == t) atomicAdd(&h7[(key[u] >> shift) & 127u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // lane l: bins 127 - 2l and 126 - 2l, highest first
+      const uint32_t a0 = h7[127 - 2 * lane], a1 = h7[126 - 2 * lane];
+      uint32_t incl = a0 + a1;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o);
+        if (lane >= o) incl += x;
+      }
+      const uint32_t excl = incl - a0 - a1;
+      if (excl < need && need <= incl) {
+        const bool first = excl + a0 >= need;
+        s_digit = first ? 127u - 2u * lane : 126u - 2u * lane;
+        s_need = first ? need - excl : need - excl - a0;
+      }
+    }
+    __syncthreads();
+    t |= s_digit << shift;
+    need = s_need;
+  }
+  const uint32_t tau = t, need_eq = need;
+  split_launder(key);
+  KVSEL_SELROWS_MARK(5);
+
+  // Slots: picks in index order, tau-equal positions lowest index first.
+  // Both counts of a row are below 2^16 (P < 65536): one scan of the pair.
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    gt += u < n && key[u] > tau;
+    eq += u < n && key[u] == tau;
+  }
+  uint32_t tot;
+  const uint32_t incl = block_scan<NT>(gt | (eq << 16), sh, tot);
+  const uint32_t gt_before = (incl & 0xFFFFu) - gt, eq_before = (incl >> 16) - eq;
+  KVSEL_SELROWS_MARK(6);
+  const int s0 = (int)((long long)sp * count / splits), s1 = (int)((long long)(sp + 1) * count / splits);
+  int32_t* list = reinterpret_cast<int32_t*>(sv);  // this split's source positions, by slot
+  {
+    uint32_t slot = gt_before + min(eq_before, need_eq), eqs = eq_before;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool valid = u < n;
+      const bool e = valid && key[u] == tau;
+      const bool pick = (valid && key[u] > tau) || (e && eqs < need_eq);
+      eqs += e;
+      if (pick) {
+        KVSEL_DEBUG_CHECK(slot < (uint32_t)count, a.err);
+        if ((int)slot >= s0 && (int)slot < s1) {
+          out[slot] = tid * KPT + u;
+          list[slot - s0] = tid * KPT + u;
+        }
+        ++slot;
+      }
+    }
+  }
+  // This split's share of the window (it follows the picks).
+  const int w0 = (int)((long long)sp * W / splits), w1 = (int)((long long)(sp + 1) * W / splits);
+  for (int i = w0 + tid; i < w1; i += NT) out[count + i] = P + i;
+  __syncthreads();  // the list is complete
+  KVSEL_SELROWS_MARK(7);
+  if (s1 > s0) copy(s0, s1 - s0, 0, list);
+  if (w1 > w0) copy(count + w0, w1 - w0, P + w0, nullptr);
+  KVSEL_SELROWS_MARK(8);
+}
+
+// Variants of the split selection: (threads, keys per thread), the first
+// covering max_p positions is used.  Rows are below 65536 positions (the
+// slot scan packs two 16-bit counts).
+constexpr int kSplitVariants = 4;
+constexpr int kSplitNT[kSplitVariants] = {512, 512, 512, 1024};
+constexpr int kSplitKPT[kSplitVariants] = {16, 32, 64, 64};
+constexpr int kSplitWords[kSplitVariants] = {SplitGeom<512, 16>::kWords, SplitGeom<512, 32>::kWords,
+                                             SplitGeom<512, 64>::kWords, SplitGeom<1024, 64>::kWords};
+int split_kpt(int max_p) {
+  for (int v = 0; v < kSplitVariants; ++v)
+    if (max_p <= kSplitNT[v] * kSplitKPT[v] && max_p < 65536) return v + 1;
+  return 0;
+}
+int split_max_positions() { return 65535; }
+int split_max_splits() { return kSplitMaxS; }
+int split_list_capacity(int kpt) { return kpt >= 1 && kpt <= kSplitVariants ? kSplitWords[kpt - 1] : 0; }
+
+template <int NT, int KPT>
+const void* split_kernel_ptr(int ru) {
+  return ru == 0   ? (const void*)select_split_kernel<NT, KPT, 0>
+         : ru == 8 ? (const void*)select_split_kernel<NT, KPT, 8>
+         : ru == 16 ? (const void*)select_split_kernel<NT, KPT, 16>
+                    : (const void*)select_split_kernel<NT, KPT, 32>;
+}
+
+// Workgroups of the split selection that fit the device at once (looked up
+// once per device and variant).  D == 0: the indices-only variant.
+int split_grid_capacity(int kpt, int D, int dtype) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const int ru = D * (dtype == 1 ? 2 : 4) / 16;
+  if (kpt < 1 || kpt > kSplitVariants) return 0;
+  const int ki = kpt - 1, ri = ru == 0 ? 0 : ru == 8 ? 1 : ru == 16 ? 2 : 3;
+  static std::mutex mu;
+  static int cache_dev[kSplitVariants][4] = {}, cache_cap[kSplitVariants][4] = {};  // device + 1, capacity
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache_dev[ki][ri] == dev + 1) return cache_cap[ki][ri];
+  }
+  const void* f = kpt == 1   ? split_kernel_ptr<512, 16>(ru)
+                  : kpt == 2 ? split_kernel_ptr<512, 32>(ru)
+                  : kpt == 3 ? split_kernel_ptr<512, 64>(ru)
+                             : split_kernel_ptr<1024, 64>(ru);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kSplitNT[ki], 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  cache_dev[ki][ri] = dev + 1;
+  cache_cap[ki][ri] = per_cu * cus;
+  return per_cu * cus;
+}
+
+template <int NT, int KPT>
+hipError_t launch_split_kpt(const Launch& a, int rows, int splits, int ru, const float* votes, float* pooled,
+                            int32_t* indices, const uint4* k, const uint4* v, uint4* ko, uint4* vo, hipStream_t st) {
+  const dim3 grid((unsigned)(rows * splits));
+  switch (ru) {
+    case 0:
+      hipLaunchKernelGGL((select_split_kernel<NT, KPT, 0>), grid, dim3(NT), 0, st, a, rows, splits, votes, pooled,
+                         indices, k, v, ko, vo);
+      break;
+    case 8:
+      hipLaunchKernelGGL((select_split_kernel<NT, KPT, 8>), grid, dim3(NT), 0, st, a, rows, splits, votes, pooled,
+                         indices, k, v, ko, vo);
+      break;
+    case 16:
+      hipLaunchKernelGGL((select_split_kernel<NT, KPT, 16>), grid, dim3(NT), 0, st, a, rows, splits, votes, pooled,
+                         indices, k, v, ko, vo);
+      break;
+    case 32:
+      hipLaunchKernelGGL((select_split_kernel<NT, KPT, 32>), grid, dim3(NT), 0, st, a, rows, splits, votes, pooled,
+                         indices, k, v, ko, vo);
+      break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_split(const Launch& a, int rows, int splits, int kpt, int dtype, const float* votes,
+                               float* pooled, int32_t* indices, const void* K, const void* V, void* K_out, void* V_out,
+                               hipStream_t st) {
+  if (rows <= 0 || splits <= 0) return hipSuccess;
+  if (splits > kSplitMaxS || (long long)rows * splits > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  if (a.kernel != 1 && a.kernel != 3 && a.kernel != 5 && a.kernel != 7) return hipErrorNotSupported;
+  const int ru = K == nullptr ? 0 : a.D * (dtype == 1 ? 2 : 4) / 16;  // K == nullptr: indices only
+  const uint4* k = (const uint4*)K;
+  const uint4* v = (const uint4*)V;
+  uint4* ko = (uint4*)K_out;
+  uint4* vo = (uint4*)V_out;
+  switch (kpt) {
+    case 1: return launch_split_kpt<512, 16>(a, rows, splits, ru, votes, pooled, indices, k, v, ko, vo, st);
+    case 2: return launch_split_kpt<512, 32>(a, rows, splits, ru, votes, pooled, indices, k, v, ko, vo, st);
+    case 3: return launch_split_kpt<512, 64>(a, rows, splits, ru, votes, pooled, indices, k, v, ko, vo, st);
+    case 4: return launch_split_kpt<1024, 64>(a, rows, splits, ru, votes, pooled, indices, k, v, ko, vo, st);
     default: return hipErrorNotSupported;
   }
 }

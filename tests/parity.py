@@ -84,29 +84,37 @@ def gpu_internal_topk(gpu_prefix: np.ndarray, gpu_pooled_f32: np.ndarray, n: int
                                   err_msg=f"{what}: GPU picks differ from top-n of the GPU's own scores")
 
 
-def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto"):
+SELECT = {"auto": 0, "split": 1, "exchange": 2}
+
+
+def run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto", select: str = "auto"):
     """Run kvsel_select with every optional output; returns host numpy arrays.
     `scoring` picks the scoring path (auto, two_pass, single_read, or
     single_read_fallback: the single-read launch forced onto its two-pass
-    fallback)."""
+    fallback); `select` the selection kernels (auto, split, or exchange:
+    the cooperative selection or the per-row / segment chains)."""
     from prompt_kv_selection_amd import binding as B
     fallback = scoring == "single_read_fallback"
     B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING["single_read" if fallback else scoring])
     B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 1 if fallback else 0)
+    B.kvsel_set_option(B.KVSEL_OPT_SELECT, SELECT[select])
     try:
         return _run_select(B, Qd, Kd, Vd, L, W, C, kernel, pooling, dtype)
     finally:
         B.kvsel_set_option(B.KVSEL_OPT_SCORING, 0)
         B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 0)
+        B.kvsel_set_option(B.KVSEL_OPT_SELECT, 0)
 
 
-def run_select_lse(Qd, Kd, Vd, lse_d, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto"):
+def run_select_lse(Qd, Kd, Vd, lse_d, L, W, C, kernel, pooling, dtype: str, scoring: str = "auto",
+                   select: str = "auto"):
     """Run kvsel_select_lse (row statistics handed over as lse_d [H, W]
     float32 on the device) with votes and pooled outputs; host numpy arrays."""
     from prompt_kv_selection_amd import binding as B
     H, _, D = Kd.shape
     td = torch_dtype(dtype)
     B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[scoring])
+    B.kvsel_set_option(B.KVSEL_OPT_SELECT, SELECT[select])
     try:
         ws = torch.empty(B.kvsel_workspace_bytes(H, L, W, C, D, td), dtype=torch.uint8, device="cuda")
         idx = torch.full((H, C), -7, dtype=torch.int32, device="cuda")
@@ -118,6 +126,7 @@ def run_select_lse(Qd, Kd, Vd, lse_d, L, W, C, kernel, pooling, dtype: str, scor
         torch.cuda.synchronize()
     finally:
         B.kvsel_set_option(B.KVSEL_OPT_SCORING, 0)
+        B.kvsel_set_option(B.KVSEL_OPT_SELECT, 0)
     return dict(idx=idx, Ko=Ko, Vo=Vo, votes=vt.cpu().numpy(), pooled=pl.cpu().numpy())
 
 

@@ -229,7 +229,12 @@ def test_options(B):
     assert lib.kvsel_set_option(1, 2) == -1
     assert lib.kvsel_set_option(1, 1) == 0 and lib.kvsel_get_option(1) == 1
     assert lib.kvsel_set_option(1, 0) == 0 and lib.kvsel_get_option(1) == 0
-    assert lib.kvsel_set_option(4, 0) == -1
+    assert lib.kvsel_get_option(4) == 0                       # selection kernels: automatic
+    assert lib.kvsel_set_option(4, 3) == -1
+    assert lib.kvsel_set_option(4, 1) == 0 and lib.kvsel_get_option(4) == 1
+    assert lib.kvsel_set_option(4, 2) == 0 and lib.kvsel_get_option(4) == 2
+    assert lib.kvsel_set_option(4, 0) == 0 and lib.kvsel_get_option(4) == 0
+    assert lib.kvsel_set_option(5, 0) == -1
     assert lib.kvsel_get_option(5) == -1
     assert lib.kvsel_get_option(3) == 0                       # fused selection off
     assert lib.kvsel_set_option(3, 2) == -1

@@ -104,23 +104,24 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("select", ["auto", "exchange"])
 @pytest.mark.parametrize("scoring", ["two_pass", "single_read"])
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[1]}-H{c[2]}-L{c[3]}-W{c[4]}-C{c[5]}-k{c[6]}{c[7]}"
                                              for c in CASES])
-def test_random_cases(B, case, scoring):
+def test_random_cases(B, case, scoring, select):
     dtype, D, H, L, W, C, kernel, pooling = case
     keys = "codebook" if (L, C) == (20000, 2048) else "spike"
     w = WL.Workload("case", seed=L * 7 + W, heads=H, L=L, W=W, C=C, D=D, dtype=dtype, kernel=kernel,
                     pooling=pooling, keys=keys, spike_frac=0.02 if L - W >= 50 else 0.0)
     Q, K, V = WL.layer_arrays(w)
-    log(f"random case {case} keys={keys} scoring={scoring}")
+    log(f"random case {case} keys={keys} scoring={scoring} select={select}")
     Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
     if scoring == "single_read" and not single_read_covers(dtype, D, W) and L >= C:
         with pytest.raises(B.KvselError) as ei:
-            run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring)
+            run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring, select)
         assert ei.value.code == B.KVSEL_EUNSUPPORTED
         return
-    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring)
+    out = run_select(Qd, Kd, Vd, L, W, C, kernel, pooling, dtype, scoring, select)
     for h in range(H):
         ref = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h], dtype),
                               WL.to_float64(V[h], dtype), W, C, kernel, pooling)
@@ -219,9 +220,10 @@ def test_deterministic(B, scoring):
 
 # ----------------------------------------------------------------- steps
 
+@pytest.mark.parametrize("select", [0, 2])
 @pytest.mark.parametrize("rows,n,count", [(1, 1, 1), (3, 1000, 17), (4, 32736, 992), (2, 131008, 4032),
                                           (5, 70001, 70001), (2, 9000, 1)])
-def test_topk_step_exact(B, rows, n, count):
+def test_topk_step_exact(B, rows, n, count, select):
     """Top-k on given fp32 scores: exactly the oracle's ranking of the same
     values, lowest index first on ties (many exact ties here)."""
     rng = np.random.default_rng(n + count)
@@ -232,10 +234,14 @@ def test_topk_step_exact(B, rows, n, count):
     sd = torch.from_numpy(s).cuda()
     ld = count + 3
     out = torch.full((rows, ld), -1, dtype=torch.int32, device="cuda")
-    log(f"topk rows={rows} n={n} count={count}")
+    log(f"topk rows={rows} n={n} count={count} select option {select}")
     ws = torch.empty(B.kvsel_topk_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
-    B.kvsel_topk(sd, rows, n, count, out, ld, ws)
-    torch.cuda.synchronize()
+    B.kvsel_set_option(B.KVSEL_OPT_SELECT, select)
+    try:
+        B.kvsel_topk(sd, rows, n, count, out, ld, ws)
+        torch.cuda.synchronize()
+    finally:
+        B.kvsel_set_option(B.KVSEL_OPT_SELECT, 0)
     got = out.cpu().numpy()
     for r in range(rows):
         np.testing.assert_array_equal(got[r, :count], O.top_prefix(s[r].astype(np.float64), count))
@@ -453,8 +459,11 @@ def test_full_size_headline_paths(B, path):
     Qd, Kd, Vd = to_device(Q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
     del K, V
     log(f"full size headline layer, {path}")
+    # The fallback case takes the cooperative selection, whose residency
+    # fallback is forced too.
     out = run_select(Qd, Kd, Vd, w.L, w.W, w.C, w.kernel, w.pooling, w.dtype,
-                     scoring="two_pass" if path == "two_pass" else "single_read_fallback")
+                     scoring="two_pass" if path == "two_pass" else "single_read_fallback",
+                     select="auto" if path == "two_pass" else "exchange")
     if path == "two_pass":
         assert "two_pass" in out["path"], out["path"]
     else:
