@@ -584,6 +584,8 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probes")
     ap.add_argument("--scoring", choices=("auto", "two_pass", "single_read"), default="auto",
                     help="scoring path (auto: single-read wherever it applies)")
+    ap.add_argument("--select", choices=("auto", "split", "exchange"), default="auto",
+                    help="selection kernels (auto: the cooperative selection where its grid fits, else split)")
     ap.add_argument("--force-fallback", action="store_true",
                     help="time the residency fallbacks (the handshakes decide ABORT from the host)")
     ap.add_argument("--lse", action="store_true",
@@ -697,6 +699,8 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[args.scoring])
     B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 1 if args.force_fallback else 0)
+    B.kvsel_set_option(B.KVSEL_OPT_SELECT, {"auto": B.KVSEL_SELECT_AUTO, "split": B.KVSEL_SELECT_SPLIT,
+                                            "exchange": B.KVSEL_SELECT_EXCHANGE}[args.select])
 
     lses = []
     if args.lse:
@@ -810,7 +814,7 @@ def main():
                    "L": [L for L, _ in seqs] if w.ragged else seqs[0][0],
                    "C": Cs if w.ragged else Cs[0],
                    "pooling": w.pooling, "kernel": w.kernel, "keys": w.keys,
-                   "scoring": args.scoring, "row_stats": "handed_over" if args.lse else "computed",
+                   "scoring": args.scoring, "select": args.select, "row_stats": "handed_over" if args.lse else "computed",
                    "kv_heads": Hkv, "path": path, "fallbacks": fallbacks,
                    "calls_per_step": calls, "heads_per_call": Hc,
                    "forced_fallback": bool(args.force_fallback), "status": "ok"},

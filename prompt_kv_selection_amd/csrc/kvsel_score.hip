@@ -31,6 +31,12 @@
 
 #include "kvsel_internal.h"
 
+// Instrumentation hook (kernel k: 0 statistics, 1 votes; point 0..15 of the
+// calling wave); empty unless a profiling build defines it.
+#ifndef KVSEL_SCORE_MARK
+#define KVSEL_SCORE_MARK(k, point)
+#endif
+
 namespace kvsel {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -172,6 +178,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Add one logit x to (running maximum m, sum z of exp2(. - m)) with a single
 // exponential: exp2(-|x - m|) rescales whichever side is smaller.
 __device__ __forceinline__ void online_add(float& m, float& z, float x) {
+#pragma clang fp contract(off)
   const float d = x - m;
   const float e = exp2_fast(-fabsf(d));
   z = d > 0.f ? fmaf(z, e, 1.f) : z + e;
@@ -181,6 +188,7 @@ __device__ __forceinline__ void online_add(float& m, float& z, float x) {
 // Merge (mo, zo) into (m, z): running maximum in base 2 and the sum of
 // exponentials rescaled to it (one exponential: the larger side keeps scale 1).
 __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
+#pragma clang fp contract(off)
   const float d = mo - m;
   const float e = exp2_fast(-fabsf(d));
   z = d > 0.f ? fmaf(z, e, zo) : fmaf(zo, e, z);
@@ -211,8 +219,33 @@ __device__ __forceinline__ void queries_from_lds(const Launch& a, const uint4 (*
   }
 }
 
+// Waves of a scoring workgroup.  Up to two 32-row blocks of window rows, four
+// waves, each holding the Qwin operands in registers and two K tiles in
+// flight.  Three or four blocks of bf16 rows (grouped heads), eight waves,
+// two per SIMD, each with one tile in flight and the Qwin operands read from
+// LDS per tile: a tile's MFMA and exponential chains for 128 rows take a
+// wave about 2 us, so with one wave per SIMD nothing would cover them (fp32
+// tiles are twice the size and do not fit eight waves' buffers).  The item
+// is kChunk positions either way.
+template <typename T, int D, int RB>
+struct ScoreGeom {
+  static constexpr bool kQLds = RB >= 3 && sizeof(T) == 2;  // Qwin operands (and, for votes, row scales) from LDS
+  static constexpr int NW = kQLds ? 8 : kWaves;            // waves per workgroup
+  static constexpr int WT = kChunk / (NW * 32);            // tiles per wave per item
+  static constexpr int RING = kQLds ? 1 : TileGeom<T, D>::RING;  // tiles in flight per wave
+  static_assert(NW * WT * 32 == kChunk, "an item is kChunk positions");
+  // Row statistics are kept per sub-range of kSubTiles tiles of every item
+  // (a wave's tiles of each item form SUB of them), and a chunk's partial
+  // merges the kSubs sub-ranges in order: the same summation for either
+  // wave count, so grouped heads match their expanded heads bit for bit.
+  static constexpr int kSubTiles = 4;
+  static constexpr int SUB = WT / kSubTiles;
+  static constexpr int kSubs = NW * SUB;
+  static_assert(SUB * kSubTiles == WT && kSubs == kChunk / (32 * kSubTiles), "sub-ranges tile the item");
+};
+
 // One scoring item: chunk c (kChunk positions) of head h of segment e.  A
-// wave covers kWaveTiles tiles of the chunk starting at pb, of which nt hold
+// wave covers WT tiles of the chunk starting at pb, of which nt hold
 // positions below the kernel's limit (L for statistics, P for votes).
 template <typename T, int D>
 struct Item {
@@ -221,7 +254,7 @@ struct Item {
   int L;
 };
 
-template <typename T, int D, bool kVotes>
+template <typename T, int D, bool kVotes, int WT>
 __device__ __forceinline__ Item<T, D> locate_item(const Launch& a, const T* __restrict__ K, int item, int wave) {
   Item<T, D> it;
   it.e = find_seg<kFieldItem>(a, item);
@@ -232,9 +265,9 @@ __device__ __forceinline__ Item<T, D> locate_item(const Launch& a, const T* __re
   it.h = s.h0 + hl;
   it.L = s.L;
   it.kh = K + s.kv_off + (long long)it.h * s.L * D;
-  it.pb = it.c * kChunk + wave * (kWaveTiles * 32);
+  it.pb = it.c * kChunk + wave * (WT * 32);
   const int limit = kVotes ? s.L - a.W : s.L;
-  it.nt = max(0, min(kWaveTiles, (limit - it.pb + 31) / 32));
+  it.nt = max(0, min(WT, (limit - it.pb + 31) / 32));
   return it;
 }
 
@@ -247,7 +280,7 @@ __device__ __forceinline__ void item_range(int items, int& lo, int& hi) {
 // The K tile stream of one wave over all items of its workgroup's range:
 // tile loads run up to RING tiles ahead of the consumer, across item
 // boundaries; buffer = tile count % RING.
-template <typename T, int D, bool kVotes>
+template <typename T, int D, bool kVotes, int WT, int RING>
 struct WaveStream {
   using G = TileGeom<T, D>;
   uint4 (*ring)[G::PIECES];
@@ -262,25 +295,25 @@ struct WaveStream {
     hi = hi_;
     item = lo;
     t = 0;
-    if (item < hi) cur = locate_item<T, D, kVotes>(a, K, item, wave);
-    for (int r = 0; r < G::RING; ++r) issue_next(a, K, wave, lane);
+    if (item < hi) cur = locate_item<T, D, kVotes, WT>(a, K, item, wave);
+    for (int r = 0; r < RING; ++r) issue_next(a, K, wave, lane);
   }
   __device__ __forceinline__ void issue_next(const Launch& a, const T* __restrict__ K, int wave, int lane) {
     while (item < hi && t >= cur.nt) {
       ++item;
       t = 0;
-      if (item < hi) cur = locate_item<T, D, kVotes>(a, K, item, wave);
+      if (item < hi) cur = locate_item<T, D, kVotes, WT>(a, K, item, wave);
     }
     if (item >= hi) return;
     const int p0 = cur.pb + t * 32;
-    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % G::RING], lane);
+    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % RING], lane);
     ++t;
     ++issued;
   }
   // The next tile in stream order has landed; returns its buffer.
   __device__ __forceinline__ const uint4* wait() {
     wait_tiles<G::NL>(issued - done - 1);
-    return ring[done % G::RING];
+    return ring[done % RING];
   }
   // After the operand reads of the tile (waited for here): reuse its buffer
   // for the next load.
@@ -291,9 +324,10 @@ struct WaveStream {
   }
 };
 
-// Stage Qwin of (segment e, head h) and read it into operand registers.  On
-// entry no wave still reads qt; on exit every wave has its copy.  Waits for
-// all of this wave's loads in flight (a K tile stream drains once here).
+// Stage Qwin of (segment e, head h) and read it into operand registers
+// (unless they are read from LDS per tile).  On entry no wave still reads qt;
+// on exit every wave has its copy, or qt holds it.  Waits for all of this
+// wave's loads in flight (a K tile stream drains once here).
 template <typename T, int D, int RB>
 __device__ __forceinline__ void stage_queries(const Launch& a, int e, int h, const T* __restrict__ Q,
                                               uint4 (*qt)[TileGeom<T, D>::PIECES], const TileOffsets<T, D>& off,
@@ -301,7 +335,22 @@ __device__ __forceinline__ void stage_queries(const Launch& a, int e, int h, con
   issue_queries<T, D, RB>(a, a.seg[e], h, Q, qt, off, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  queries_from_lds<T, D, RB>(a, qt, lane & 31, lane >> 5, qa);
+  if constexpr (!ScoreGeom<T, D, RB>::kQLds) queries_from_lds<T, D, RB>(a, qt, lane & 31, lane >> 5, qa);
+}
+
+// Row block rb's Qwin operands: the registers staged above, or read from
+// LDS for this tile (rows past group_rows are zero).
+template <typename T, int D, int RB>
+__device__ __forceinline__ Operands<T, D> query_block(const Launch& a, const uint4 (*qt)[TileGeom<T, D>::PIECES],
+                                                      const Operands<T, D> (&qa)[RB], int rb, int n, int g) {
+  if constexpr (ScoreGeom<T, D, RB>::kQLds) {
+    Operands<T, D> q;
+    q.from_tile(qt[rb], n, g);
+    if (rb * 32 + n >= group_rows(a)) q.zero();
+    return q;
+  } else {
+    return qa[rb];
+  }
 }
 
 // Partial row statistics.  Persistent workgroups of kWaves waves walk a
@@ -311,24 +360,30 @@ __device__ __forceinline__ void stage_queries(const Launch& a, int e, int h, con
 // last chunk, and the other chunks of the run get (kNegBig, 0), which leaves
 // any merge unchanged.
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch a, int items,
+__global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_stats_kernel(const Launch a, int items,
                                                                   const T* __restrict__ Q,
                                                                   const T* __restrict__ K,
                                                                   float* __restrict__ part_m,
                                                                   float* __restrict__ part_z,
                                                                   uint32_t* __restrict__ zero,
                                                                   long long zero_words) {
+  // Every multiply-add below is written out (fmaf) and nothing else is
+  // fused, so the statistics do not depend on how the compiler schedules a
+  // kernel variant: grouped heads match their expanded heads bit for bit.
+#pragma clang fp contract(off)
   using G = TileGeom<T, D>;
-  __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
+  using SG = ScoreGeom<T, D, RB>;
+  __shared__ uint4 ring[SG::NW][SG::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
-  __shared__ float sm[2][kWaves][RB * 32], sz[2][kWaves][RB * 32];
+  __shared__ float sm[2][SG::kSubs][RB * 32], sz[2][SG::kSubs][RB * 32];
   const int W = a.W, R = group_rows(a);  // rows: window row i of the group's query head i / W
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
   int lo, hi;
   item_range(items, lo, hi);
 
-  WaveStream<T, D, false> ws;
+  KVSEL_SCORE_MARK(0, 0);
+  WaveStream<T, D, false, SG::WT, SG::RING> ws;
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
 
@@ -340,10 +395,10 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
   Operands<T, D> qa[RB];
   // This lane's running statistics of the current run: row n of each row
   // block over the lane's half of every tile's positions.
-  float m[RB], z[RB];
+  float m[SG::SUB][RB], z[SG::SUB][RB];
   int runs = 0;
   for (int item = lo; item < hi; ++item) {
-    const Item<T, D> it = locate_item<T, D, false>(a, K, item, wave);
+    const Item<T, D> it = locate_item<T, D, false, SG::WT>(a, K, item, wave);
     const Seg& s = a.seg[it.e];
     const int L = s.L, P = L - W;
     const bool first = item == lo || find_seg<kFieldItem>(a, item - 1) != it.e ||
@@ -354,11 +409,14 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
       // qt is free: every wave read it before the barrier that ended the
       // previous staging, and has since passed that run's final barrier.
       stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
+      KVSEL_SCORE_MARK(0, 1);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        m[rb] = kNegBig;
-        z[rb] = 0.f;
-      }
+      for (int u = 0; u < SG::SUB; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          m[u][rb] = kNegBig;
+          z[u][rb] = 0.f;
+        }
     }
 
     for (int t = 0; t < it.nt; ++t) {
@@ -366,6 +424,7 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
       const int j = p0 + n;
       Operands<T, D> kt;
       kt.from_tile(ws.wait(), n, g);
+      KVSEL_SCORE_MARK(0, 2 + (t & 7));
       ws.release(a, K, wave, lane);  // the tile is in registers: refill its buffer now
       // K.Q^T puts a lane on a window row (row n of the block) and its
       // registers on positions p0 + acc_row(r, g), so the tile's maximum
@@ -378,7 +437,7 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
       (void)j;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        f32x16 act = tile_dot<D>(kt, qa[rb]);
+        f32x16 act = tile_dot<D>(kt, query_block<T, D, RB>(a, qt, qa, rb, n, g));
         const int i = (rb * 32) % W + n;  // this lane's window row
         float tm = kNegBig;
         if (full) {
@@ -396,7 +455,10 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
         float tz = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tz += exp2_fast(fmaf(act[r], a.scale2, -tms));
-        lse_merge(m[rb], z[rb], tms, tz);
+        // The tile's sub-range (t / kSubTiles) keeps its own running statistics.
+#pragma unroll
+        for (int u = 0; u < SG::SUB; ++u)
+          if (t / SG::kSubTiles == u) lse_merge(m[u][rb], z[u][rb], tms, tz);
       }
     }
 
@@ -414,31 +476,36 @@ __global__ __launch_bounds__(kWaves * 64) void window_stats_kernel(const Launch 
     // Lane n and lane n + 32 hold the same row over the two halves of the
     // positions: merged in that order.
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float mo = __shfl_xor(m[rb], 32), zo = __shfl_xor(z[rb], 32);
-      if (g == 0) lse_merge(m[rb], z[rb], mo, zo);
-    }
+    for (int u = 0; u < SG::SUB; ++u)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mo = __shfl_xor(m[u][rb], 32), zo = __shfl_xor(z[u][rb], 32);
+        if (g == 0) lse_merge(m[u][rb], z[u][rb], mo, zo);
+      }
 
     // Run k uses buffer k & 1: the merge of run k happens before any wave
-    // passes the barrier of run k + 1.
+    // passes the barrier of run k + 1.  Sub-range wave * SUB + u of the item.
     const int pbuf = runs++ & 1;
     if (g == 0) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        sm[pbuf][wave][rb * 32 + n] = m[rb];
-        sz[pbuf][wave][rb * 32 + n] = z[rb];
-      }
+      for (int u = 0; u < SG::SUB; ++u)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          sm[pbuf][wave * SG::SUB + u][rb * 32 + n] = m[u][rb];
+          sz[pbuf][wave * SG::SUB + u][rb * 32 + n] = z[u][rb];
+        }
     }
     __syncthreads();
     if ((int)threadIdx.x < R) {
       const int i = threadIdx.x;
       float mm = sm[pbuf][0][i], zz = sz[pbuf][0][i];
 #pragma unroll
-      for (int v = 1; v < kWaves; ++v) lse_merge(mm, zz, sm[pbuf][v][i], sz[pbuf][v][i]);
+      for (int v = 1; v < SG::kSubs; ++v) lse_merge(mm, zz, sm[pbuf][v][i], sz[pbuf][v][i]);
       part_m[slot + i] = mm;
       part_z[slot + i] = zz;
     }
   }
+  KVSEL_SCORE_MARK(0, 10);
 }
 
 // Final (max, 1/sum) of every row of K/V head h (R = group_rows rows) from
@@ -462,18 +529,21 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
     const int i = t % W, grp = t / W;
     float mm = kNegBig, zz = 0.f;
     int c = grp;
-    // Batches of four independent loads.
-    for (; c + 3 * G < s.nch; c += 4 * G) {
-      float pm[4], pz[4];
+    // Batches of kMergeBatch independent loads (one batch covers 32 chunks),
+    // merged in chunk order.
+    constexpr int kMergeBatch = 16;
+    for (; c < s.nch; c += kMergeBatch * G) {
+      float pm[kMergeBatch], pz[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        pm[u] = part_m[base + (long long)(c + u * G) * W + i];
-        pz[u] = part_z[base + (long long)(c + u * G) * W + i];
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const bool in = c + u * G < s.nch;
+        pm[u] = in ? part_m[base + (long long)(c + u * G) * W + i] : kNegBig;
+        pz[u] = in ? part_z[base + (long long)(c + u * G) * W + i] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) lse_merge(mm, zz, pm[u], pz[u]);
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (c + u * G < s.nch) lse_merge(mm, zz, pm[u], pz[u]);
     }
-    for (; c < s.nch; c += G) lse_merge(mm, zz, part_m[base + (long long)c * W + i], part_z[base + (long long)c * W + i]);
     s_gm[t] = mm;
     s_gz[t] = zz;
   }
@@ -504,34 +574,42 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
 // recompute each chunk's logits and sum the softmax probabilities over the
 // window rows.
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
+__global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_votes_kernel(
     const Launch a, int items, const T* __restrict__ Q, const T* __restrict__ K,
     const float* __restrict__ part_m, const float* __restrict__ part_z, const float* __restrict__ lse,
     float* __restrict__ votes, float* __restrict__ row_stats) {
+#pragma clang fp contract(off)  // as in window_stats_kernel
   using G = TileGeom<T, D>;
-  __shared__ uint4 ring[kWaves][G::RING][G::PIECES];
+  using SG = ScoreGeom<T, D, RB>;
+  __shared__ uint4 ring[SG::NW][SG::RING][G::PIECES];
   __shared__ uint4 qt[RB][G::PIECES];
-  __shared__ float s_m[RB * 32], s_iz[RB * 32];
-  __shared__ float s_gm[kWaves * 64], s_gz[kWaves * 64];
+  __shared__ __align__(16) float s_m[RB * 32], s_iz[RB * 32];
+  __shared__ float s_gm[SG::NW * 64], s_gz[SG::NW * 64];
   const int W = a.W, R = group_rows(a), Gq = a.group > 1 ? a.group : 1;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, g = lane >> 5;
   int lo, hi;
   item_range(items, lo, hi);
 
-  WaveStream<T, D, true> ws;
+  KVSEL_SCORE_MARK(1, 0);
+  WaveStream<T, D, true, SG::WT, SG::RING> ws;
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
 
   Operands<T, D> qa[RB];
-  float mr[RB][16], izr[RB][16];
+  // Row scales of the lane's accumulator rows (registers, or read from LDS
+  // per tile with eight waves).
+  float mr[SG::kQLds ? 1 : RB][16], izr[SG::kQLds ? 1 : RB][16];
   int qe = -1, qh = -1;
   for (int item = lo; item < hi; ++item) {
-    const Item<T, D> it = locate_item<T, D, true>(a, K, item, wave);
+    const Item<T, D> it = locate_item<T, D, true, SG::WT>(a, K, item, wave);
     const Seg& s = a.seg[it.e];
     const int L = s.L, P = L - W;
     if (it.c * kChunk >= P) continue;  // chunk holds window positions only
     if (it.e != qe || it.h != qh) {
+      // With operands read from LDS every wave is done with the previous
+      // head's Qwin and scales before they are rewritten.
+      if (SG::kQLds && qe >= 0) __syncthreads();
       stage_queries<T, D, RB>(a, it.e, it.h, Q, qt, ws.off, wave, lane, qa);
       qe = it.e;
       qh = it.h;
@@ -552,16 +630,19 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
         // alone writes the row statistics.
         merge_partials<RB * 32>(a, s, it.h, part_m, part_z, row_stats, it.c == 0, s_gm, s_gz, s_m, s_iz);
       }
+      if constexpr (!SG::kQLds) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = rb * 32 + acc_row(r, g);
-          mr[rb][r] = s_m[i];
-          izr[rb][r] = s_iz[i];
-        }
-      // Nobody reads qt or s_m again before the next staging rewrites them.
-      __syncthreads();
+          for (int r = 0; r < 16; ++r) {
+            const int i = rb * 32 + acc_row(r, g);
+            mr[rb][r] = s_m[i];
+            izr[rb][r] = s_iz[i];
+          }
+        // Nobody reads qt or s_m again before the next staging rewrites them.
+        __syncthreads();
+      }
+      KVSEL_SCORE_MARK(1, 1);
     }
 
     // Votes of each query head of the group: its row blocks' sums.
@@ -570,14 +651,32 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
       const int j = it.pb + t * 32 + n;
       Operands<T, D> kt;
       kt.from_tile(ws.wait(), n, g);
+      KVSEL_SCORE_MARK(1, 2 + (t & 7));
       ws.release(a, K, wave, lane);  // the tile is in registers: refill its buffer now
       float tot = 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const f32x16 acc = tile_dot<D>(qa[rb], kt);
+        const f32x16 acc = tile_dot<D>(query_block<T, D, RB>(a, qt, qa, rb, n, g), kt);
+        const int sr = SG::kQLds ? 0 : rb;  // the scales' register set
+        if constexpr (SG::kQLds) {
+          // acc_row(r, g) for r = 4q .. 4q + 3 is four consecutive rows.
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 m4 = *reinterpret_cast<const float4*>(&s_m[rb * 32 + 8 * q + 4 * g]);
+            const float4 z4 = *reinterpret_cast<const float4*>(&s_iz[rb * 32 + 8 * q + 4 * g]);
+            mr[0][4 * q] = m4.x;
+            mr[0][4 * q + 1] = m4.y;
+            mr[0][4 * q + 2] = m4.z;
+            mr[0][4 * q + 3] = m4.w;
+            izr[0][4 * q] = z4.x;
+            izr[0][4 * q + 1] = z4.y;
+            izr[0][4 * q + 2] = z4.z;
+            izr[0][4 * q + 3] = z4.w;
+          }
+        }
         float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part += exp2_fast(acc[r] * a.scale2 - mr[rb][r]) * izr[rb][r];
+        for (int r = 0; r < 16; ++r) part = fmaf(exp2_fast(fmaf(acc[r], a.scale2, -mr[sr][r])), izr[sr][r], part);
         tot += part;
         if (rb + 1 == RB || (Gq > 1 && ((rb + 1) * 32) % W == 0)) {  // the last row block of a query head
           const float other = __shfl_xor(tot, 32);
@@ -589,19 +688,20 @@ __global__ __launch_bounds__(kWaves * 64) void window_votes_kernel(
       }
     }
   }
+  KVSEL_SCORE_MARK(1, 10);
 }
 
 // Persistent grid: as many workgroups as can be resident at once (cached per
 // kernel variant and device), never more than there are items.
 template <typename Kern>
-static int resident_grid(Kern kern, int items) {
+static int resident_grid(Kern kern, int threads, int items) {
   static int per_cu[64] = {};
   static int cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return items;
   if (per_cu[dev] == 0) {
     int n = 0, c = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kWaves * 64, 0) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess || n < 1) n = 1;
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 1;
     cus[dev] = c;
     per_cu[dev] = n;
@@ -613,8 +713,9 @@ static int resident_grid(Kern kern, int items) {
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
                           uint32_t* zero, long long zero_words, hipStream_t st) {
-  const int grid = resident_grid(window_stats_kernel<T, D, RB>, items);
-  hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
+  constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
+  const int grid = resident_grid(window_stats_kernel<T, D, RB>, threads, items);
+  hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(threads), 0, st, a, items,
                      (const T*)Q, (const T*)K, pm, pz, zero, zero_words);
   return hipGetLastError();
 }
@@ -622,8 +723,9 @@ static hipError_t stats_t(const Launch& a, int items, const void* Q, const void*
 template <typename T, int D, int RB>
 static hipError_t votes_t(const Launch& a, int items, const void* Q, const void* K, const float* pm,
                           const float* pz, const float* lse, float* votes, float* rs, hipStream_t st) {
-  const int grid = resident_grid(window_votes_kernel<T, D, RB>, items);
-  hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(kWaves * 64), 0, st, a, items,
+  constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
+  const int grid = resident_grid(window_votes_kernel<T, D, RB>, threads, items);
+  hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(threads), 0, st, a, items,
                      (const T*)Q, (const T*)K, pm, pz, lse, votes, rs);
   return hipGetLastError();
 }

@@ -1294,13 +1294,14 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
 
   // Phase 4: picks in index order at their final slots, and their rows.
   // Per segment: the picks and tau-equal positions of the earlier segments
-  // (all counts read at once, a lane each, and scanned).  In the candidate
-  // round a segment's count word holds its keys above the boundary bin, and
-  // the candidates add those above and on tau.
+  // (all counts at once, a lane each, and scanned).  In the candidate round
+  // a segment's count word (already read into s_cw) holds its keys above the
+  // boundary bin, and the candidates add those above and on tau.
   if (tid < 64) {
     uint32_t gq = 0u, eqq = 0u;
     if (tid < nseg) {
-      const unsigned long long c = __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long c =
+          cand_round ? s_cw[tid] : __hip_atomic_load(cnt + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       gq = (uint32_t)c - 1u;
       eqq = (uint32_t)(c >> 32);
       if (cand_round) {  // the word holds the keys above the boundary bin and the candidate range
