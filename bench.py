@@ -406,6 +406,11 @@ PROFILE_TAGS = {
     "c5": ["--workload", "tied_h64_l128k"],
     "fold": ["--fold"],
 }
+# The kernels whose counters a tag records in profiles/traffic.json: only
+# the ones that tag's timed calls launch (the --lse run also makes untimed
+# full-path calls for its log-sum-exps, whose kernels it does not own).
+TRAFFIC_OWNER = {"auto": ("window_fused", "select", "fill"), "lse": ("window_fused_lse",),
+                 "two_pass": ("window_stats", "window_votes")}
 # (pattern in the mangled kernel name, short name), first match wins.
 SHORT_NAMES = [("window_fused_kernelILi128ELb1E", "window_fused_lse"), ("window_fused", "window_fused"),
                ("select_coop", "select"), ("fill_u32", "fill"), ("zero_kernel", "fill"),
@@ -521,7 +526,7 @@ def digest(tag, name, title):
             ab = kernel_alg_bytes(k.replace("_lse", ""), wl, k.endswith("_lse") or lse, group, None, "gather" in fetch)
             md.append(f"| `{k}` | {nf[k]} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rb / 1e6:.1f} | "
                       f"{wb / 1e6:.1f} | {'' if ab is None else f'{ab / 1e6:.1f}'} |")
-            if tag in ("auto", "lse", "two_pass") and k in KERNEL_SOURCES:
+            if k in TRAFFIC_OWNER.get(tag, ()) and k in KERNEL_SOURCES:
                 ent = traffic["kernels"].get(k, {})
                 ent.update({"read_bytes": rb, "write_bytes": wb, "bytes_per_launch": rb + wb,
                             "source_digest": source_digest(k), "workload": wname,
@@ -541,7 +546,7 @@ def digest(tag, name, title):
             t = avg_ns.get(k)
             rate = f"{fl / (t * 1e-9) / 1e12:.1f}" if t else ""
             md.append(f"| `{k}` | {mutil[k]:.2f} | {fl / 1e9:.2f} | {rate} |")
-            if tag in ("auto", "lse", "two_pass") and k in KERNEL_SOURCES and k in traffic["kernels"]:
+            if k in TRAFFIC_OWNER.get(tag, ()) and k in KERNEL_SOURCES and k in traffic["kernels"]:
                 traffic["kernels"][k].update({"mfma_busy": round(mutil[k] / 100.0, 5), "mfma_flops": fl,
                                               "mfma_command": cmds["mfma"]})
     for k in list(traffic["kernels"]):
