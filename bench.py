@@ -413,7 +413,7 @@ TRAFFIC_OWNER = {"auto": ("window_fused", "select", "fill"), "lse": ("window_fus
                  "two_pass": ("window_stats", "window_votes")}
 # (pattern in the mangled kernel name, short name), first match wins.
 SHORT_NAMES = [("window_fused_kernelILi128ELb1E", "window_fused_lse"), ("window_fused", "window_fused"),
-               ("select_coop", "select"), ("fill_u32", "fill"), ("zero_kernel", "fill"),
+               ("select_coop", "select"), ("select_split", "select"), ("fill_u32", "fill"), ("zero_kernel", "fill"),
                ("window_stats", "window_stats"), ("window_votes", "window_votes"), ("pool_hist", "pool"),
                ("candidates", "candidates"), ("threshold", "threshold"), ("emit_kernel", "emit"),
                ("gather_kernel", "gather"), ("select_hist", "select_hist"), ("copyBuffer", "copy"),
