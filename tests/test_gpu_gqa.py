@@ -57,6 +57,8 @@ GQA_CASES = [
     ("f32", 4, 2, 2049, 32, 300, 64, 7, "avg"),
     ("bf16", 8, 2, 20000, 32, 1024, 128, 5, "max"),   # several selection segments
     ("bf16", 4, 1, 300, 32, 1024, 128, 5, "avg"),     # bypass
+    ("bf16", 6, 2, 7001, 32, 800, 128, 5, "avg"),     # three row blocks per K/V head (eight-wave kernels)
+    ("bf16", 3, 1, 5000, 32, 600, 64, 3, "max"),      # three row blocks, D = 64
 ]
 
 
@@ -82,6 +84,25 @@ def test_gqa_equals_expanded_heads(B, case):
             r = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h // G], dtype),
                                 WL.to_float64(V[h // G], dtype), W, C, kernel, pooling)
             check_head(got, h, r, L, W, C, f"gqa {case} head {h}")
+
+
+def test_gqa_workgroups_walk_several_chunks(B):
+    """More chunks than resident workgroups (16 K/V heads x 20 chunks of
+    1024 positions): each workgroup of the eight-wave kernels scores one or
+    two chunks, some of them across a K/V head boundary, with its Qwin
+    re-staged for the second head.  The expanded heads' launch splits the
+    chunks differently, so the statistics may differ in the last bits: heads
+    are checked against the oracle instead."""
+    dtype, Hq, Hkv, L, W, C, D, kernel, pooling = "bf16", 64, 16, 20000, 32, 1024, 128, 5, "max"
+    Q, K, V = draw(dtype, Hq, Hkv, L, W, C, D, kernel, pooling, seed=64)
+    Qd, Kd, Vd = to_device(Q, dtype), to_device(K, dtype), to_device(V, dtype)
+    log("gqa, several chunks per workgroup")
+    got = gqa_call(B, Qd, Kd, Vd, Hq, Hkv, L, W, C, kernel, pooling, dtype)
+    G = Hq // Hkv
+    for h in (0, 3, 17, 30, 33, 46, 62, 63):
+        r = O.snapkv_select(WL.to_float64(Q[h], dtype), WL.to_float64(K[h // G], dtype),
+                            WL.to_float64(V[h // G], dtype), W, C, kernel, pooling)
+        check_head(got, h, r, L, W, C, f"gqa several chunks head {h}")
 
 
 def test_gqa_oracle_heads_and_lse(B):
