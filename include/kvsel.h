@@ -313,8 +313,12 @@ int kvsel_select_gqa(const void* Qwin, const void* K, const void* V, const float
 size_t kvsel_varlen_workspace_bytes(const int32_t* cu_L_host, const int32_t* C_host, int B,
                                     int heads, int W, int D, int dtype);
 
-/* Ragged batch of B sequences, packed without padding (the page's example is
- * one unpadded sample; a ragged batch is B such samples side by side).
+/* Ragged batch of B sequences, packed without padding.  SnapKV page,
+ * section "one full selection computed from Q and K": its example selects
+ * for one unpadded sample; a ragged batch is B such samples side by side,
+ * each (sequence, head) selected on its own as in kvsel_select (section
+ * "the prompt cache shrinks, the positions keep their origin": indices are
+ * positions within the sequence).
  *   cu_L_host [B+1]  host array, cu_L[0] = 0, L_b = cu_L[b+1] - cu_L[b]
  *   C_host    [B]    host array, budget of each sequence; cu_C is its
  *                    exclusive prefix sum, cu_P that of P_b = L_b - W
