@@ -107,6 +107,11 @@ struct Plan {
 // of the last selection call (kvsel_status).
 constexpr size_t kHeaderBytes = 256;
 
+// Cooperative-selection launches per launch group at most: rows whose grid
+// does not fit the device at once are selected a subset at a time, each
+// launch with its own status block.
+constexpr int kCoopLaunches = 8;
+
 // Selection workspace per (sequence, head) row: threshold and segment counts.
 constexpr size_t kCutBytes = 2 * sizeof(uint32_t);
 constexpr size_t kSegCntBytes = 2 * kMaxSegRow * sizeof(uint32_t);
@@ -233,8 +238,8 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned));
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
   off = align256(off + (size_t)B * heads * 2048 * 4);
-  p.off_coop = off;  // cooperative selection: status per launch group, then per-row words
-  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned) +
+  p.off_coop = off;  // cooperative selection: status per launch (kCoopLaunches per launch group), then per-row words
+  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kCoopLaunches * kFusedStatusWords * sizeof(unsigned) +
                  (size_t)B * heads * coop_row_words() * sizeof(unsigned));
   // Fused selection (single-read shapes only): per exchange slot a count
   // word and the halo words; per launch group the arrival tokens, decision
@@ -414,15 +419,28 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   }
   // Groups the cooperative selection takes (AUTO prefers it where its grid
   // fits the device: its workgroups share a row's keys, where the split
-  // selection's each redo the whole row).
-  auto coop_segments = [&](int b0) {
+  // selection's each redo the whole row).  coop_launches() gives the
+  // launches a group needs when its rows are taken a subset at a time (0:
+  // more than kCoopLaunches, or rows longer than the segments cover).
+  auto group_segments = [&](int b0) {
     const int nb = std::min(kMaxSegs, p.B - b0);
     int segs = 1;
     for (int b = b0; b < b0 + nb; ++b) {
       const int n = p.L[b] < p.C[b] ? p.L[b] : p.L[b] - p.W;
       segs = std::max(segs, (n + coop_segment() - 1) / coop_segment());
     }
+    return segs;
+  };
+  auto coop_segments = [&](int b0) {
+    const int nb = std::min(kMaxSegs, p.B - b0), segs = group_segments(b0);
     return segs <= coop_max_segments() && (long long)segs * nb * p.heads <= coop_cap ? segs : 0;
+  };
+  auto coop_launches = [&](int b0) {
+    const int rows = std::min(kMaxSegs, p.B - b0) * p.heads, segs = group_segments(b0);
+    if (segs > coop_max_segments() || coop_cap < segs) return 0;
+    const int per = coop_cap / segs;  // rows per launch
+    const int n = (rows + per - 1) / per;
+    return n <= kCoopLaunches ? n : 0;
   };
   // The split selection per launch group: S workgroups per row, S as large
   // as the device holds at once (more rows than that: one each), and large
@@ -456,11 +474,12 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       if (!fsel[gi] && split_s[gi] == 0)
         return fail(KVSEL_EUNSUPPORTED, "the split selection does not cover this call (pooling widths 1, 3, 5, 7; at "
                                         "most %d prefix positions)", split_max_positions());
-  std::vector<int> coop_segs(ngroups, 0);
+  std::vector<int> coop_segs(ngroups, 0), coop_nl(ngroups, 0);
   bool any_coop = false;
   for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
     if (fsel[gi] || split_s[gi] > 0) continue;
-    coop_segs[gi] = coop_segments(b0);
+    coop_nl[gi] = coop_launches(b0);
+    coop_segs[gi] = coop_nl[gi] > 0 ? group_segments(b0) : 0;
     any_coop = any_coop || coop_segs[gi] > 0;
   }
   // Groups left to the per-row or segment-parallel chain (which use the
@@ -638,19 +657,41 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       continue;
     }
     if (coop_segs[b0 / kMaxSegs] > 0) {
-      unsigned* cstatus = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * (b0 / kMaxSegs);
+      const int gi = b0 / kMaxSegs, nl = coop_nl[gi];
+      unsigned* cstatus0 = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * kCoopLaunches * gi;
       unsigned* crows = (unsigned*)(ws + p.off_coop) +
-                        (long long)kFusedStatusWords * ((p.B + kMaxSegs - 1) / kMaxSegs) +
+                        (long long)kFusedStatusWords * kCoopLaunches * ngroups +
                         (long long)b0 * p.heads * coop_row_words();
-      if (g_force_fallback) {
-        e = launch_fill_u32(cstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
-        if (e != hipSuccess) return device_error(e, "fill launch");
+      // Launch k takes rows [k * per, (k + 1) * per) of the group: its
+      // segment table holds those rows' head ranges, renumbered from 0.
+      const int per = (rows + nl - 1) / nl;
+      for (int k = 0; k < nl; ++k) {
+        const int r_lo = k * per, r_hi = std::min(rows, r_lo + per);
+        if (r_lo >= r_hi) break;
+        Launch ak = a;
+        ak.n = 0;
+        for (int q = 0; q < a.n; ++q) {
+          const Seg& sq = a.seg[q];
+          const int lo = std::max(sq.row0, r_lo), hi = std::min(sq.row0 + sq.nh, r_hi);
+          if (lo >= hi) continue;
+          Seg t = sq;
+          t.h0 = sq.h0 + (lo - sq.row0);
+          t.nh = hi - lo;
+          t.row0 = lo - r_lo;
+          ak.seg[ak.n++] = t;
+        }
+        unsigned* cstatus = cstatus0 + (long long)kFusedStatusWords * k;
+        if (g_force_fallback) {
+          e = launch_fill_u32(cstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
+          if (e != hipSuccess) return device_error(e, "fill launch");
+        }
+        e = timed("select", st, [&] {
+          return launch_select_coop(ak, r_hi - r_lo, coop_segs[gi], p.dtype, votes, pooled_opt,
+                                    crows + (long long)r_lo * coop_row_words(), cstatus, indices, K, V, K_out,
+                                    V_out, st);
+        });
+        if (e != hipSuccess) return device_error(e, "select launch");
       }
-      e = timed("select", st, [&] {
-        return launch_select_coop(a, rows, coop_segs[b0 / kMaxSegs], p.dtype, votes, pooled_opt, crows, cstatus,
-                                  indices, K, V, K_out, V_out, st);
-      });
-      if (e != hipSuccess) return device_error(e, "select launch");
       continue;
     }
     if (whole_rows) {

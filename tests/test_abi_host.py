@@ -46,14 +46,15 @@ def test_workspace_sizes(B):
     # (per head and 512-position chunk),
     # status words (error flags, decision, fallback counter and 16 arrival
     # counters on lines of their own), first-digit histograms, the
-    # cooperative selection's status words and per-row words (histograms,
+    # cooperative selection's status words (one block for each of up to 8
+    # launches) and per-row words (histograms,
     # segment counts, candidate entries); then the fused selection's words:
     # a count word and 8 halo words per exchange slot, the arrival tokens,
     # decision and claim counters, per exchange slot 64 + 32 histogram words,
     # per row two completion counters, 8-byte candidates laid out like the
     # votes, and per exchange slot the chunk's 512 pooled scores
     expect_min = (256 + 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 17 * 256 + 32 * (5120 + 128 + 8192) * 4
+                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 8 * 17 * 256 + 32 * (5120 + 128 + 8192) * 4
                   + 32 * 64 * 8 + 32 * 64 * 8 * 8 + (1024 + 8) * 8 + 32 * 64 * (64 + 32) * 4 + 32 * 2 * 8
                   + 32 * (32768 - 32) * 8 + 32 * 64 * 512 * 4)
     assert expect_min <= n <= expect_min + 13 * 256
