@@ -519,11 +519,14 @@ def digest(tag, name, title):
                f"multiplied by {fs:.3f} and WRITE_SIZE by {wsc:.3f} to get bytes.", "",
                "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | write MB (scaled) | "
                "algorithmic MB |", "|---|---|---|---|---|---|---|"]
+        n_calls = min(v for k, v in nf.items() if k != "copy")
         for k in fetch:
             if k == "copy":
                 continue
             rb, wb = fetch[k] * 1024 * fs, write.get(k, 0) * 1024 * wsc
             ab = kernel_alg_bytes(k.replace("_lse", ""), wl, k.endswith("_lse") or lse, group, None, "gather" in fetch)
+            if ab is not None:  # per dispatch: a call may launch a kernel several times
+                ab /= nf[k] / n_calls
             md.append(f"| `{k}` | {nf[k]} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rb / 1e6:.1f} | "
                       f"{wb / 1e6:.1f} | {'' if ab is None else f'{ab / 1e6:.1f}'} |")
             if k in TRAFFIC_OWNER.get(tag, ()) and k in KERNEL_SOURCES:
@@ -532,7 +535,8 @@ def digest(tag, name, title):
                             "source_digest": source_digest(k), "workload": wname,
                             "commands": [cmds["fetch"], cmds["write"]]})
                 traffic["kernels"][k] = ent
-        traffic["scale"] = {"FETCH_SIZE": fs, "WRITE_SIZE": wsc}
+        if TRAFFIC_OWNER.get(tag):
+            traffic["scale"] = {"FETCH_SIZE": fs, "WRITE_SIZE": wsc}
     if mutil:
         md += ["", "## MFMA utilisation per dispatch (rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
                "```", cmds["mfma"], "```", "",
@@ -788,16 +792,21 @@ def main():
     tokens_per_s = tokens_step * args.steps / (ms_total / 1e3)
     kern = {}
     rows = "gather" in per_kernel
+    # The algorithmic bytes are per call; a kernel launched several times in
+    # one call (the cooperative selection over several launches) is rated on
+    # its time per call, not per launch.
+    n_calls = args.steps * calls
     for name, (n, ms) in per_kernel.items():
         ab = kernel_alg_bytes(name, wc, args.lse, G, seqs, rows)
-        avg = ms / n
-        kern[name] = {"launches": n, "avg_us": round(avg * 1e3, 2),
-                      "alg_GBps": None if ab is None else round(ab / (avg / 1e3) / 1e9, 1)}
+        kern[name] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),
+                      "alg_GBps": None if ab is None else round(ab / (ms / n_calls / 1e3) / 1e9, 1)}
+        if n > n_calls:
+            kern[name]["launches_per_call"] = round(n / n_calls, 2)
     dom = max((k for k in per_kernel if kernel_alg_bytes(k, wc, False, 1, seqs, rows) is not None),
               key=lambda k: per_kernel[k][1])
-    n_dom, ms_dom = per_kernel[dom]
+    ms_dom = per_kernel[dom][1]
     ab_dom = kernel_alg_bytes(dom, wc, args.lse, G, seqs, rows)
-    achieved = ab_dom / (ms_dom / n_dom / 1e3) / 1e9
+    achieved = ab_dom / (ms_dom / n_calls / 1e3) / 1e9
     counted = {} if (G > 1 or w.name != "spike_l32x_h32_l32k" or args.force_fallback or args.fold) else \
         counters_from_profiles(dom + "_lse" if args.lse else dom)
     path_gbps = path_alg_bytes(w, G, seqs) * layers / (ms_step / 1e3) / 1e9
