@@ -97,7 +97,7 @@ struct Plan {
   long long part_slots = 0;   // (sequence, head, chunk) partial-stat slots, either path
   long long vote_elems = 0;   // heads * sum of P_b
   size_t off_pm = 0, off_pz = 0, off_votes = 0, off_pooled = 0, off_cut = 0, off_segcnt = 0, off_ctr = 0,
-         off_status = 0, off_hist = 0, off_coop = 0, bytes = 0;
+         off_hist = 0, off_coop = 0, bytes = 0;
   // The selection fused into the single-read scoring kernel.
   size_t off_cw = 0, off_halo = 0, off_flags = 0, off_cslot = 0, off_fslot = 0, off_rowfb = 0, off_cand = 0,
          off_kslot = 0;
@@ -234,8 +234,6 @@ int make_plan(const int32_t* cu_L, const int32_t* C_host, int B, int heads, int 
   off = align256(off + (size_t)B * heads * kSegCntBytes);
   p.off_ctr = off;  // single-read scoring: one exchange slot per (sequence, head, chunk)
   off = align256(off + (size_t)p.fpart[B] * fused_exchange_bytes());
-  p.off_status = off;  // per launch group: error flags, arrivals, residency decision, fallback counter
-  off = align256(off + (size_t)((B + kMaxSegs - 1) / kMaxSegs) * kFusedStatusWords * sizeof(unsigned));
   p.off_hist = off;  // first-digit histogram of the pooled scores, per (sequence, head)
   off = align256(off + (size_t)B * heads * 2048 * 4);
   p.off_coop = off;  // cooperative selection: status per launch (kCoopLaunches per launch group), then per-row words
@@ -359,7 +357,6 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   float* votes = votes_opt ? votes_opt : (float*)(ws + p.off_votes);
   float* pooled = pooled_opt ? pooled_opt : (float*)(ws + p.off_pooled);
   unsigned* counters = (unsigned*)(ws + p.off_ctr);
-  unsigned* status = (unsigned*)(ws + p.off_status);
   uint32_t* cut = (uint32_t*)(ws + p.off_cut);
   uint32_t* segcnt = (uint32_t*)(ws + p.off_segcnt);
   // The selection's candidate scores reuse the workspace votes buffer, which
@@ -396,7 +393,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
   // group: pooling widths up to 7, one query head per K/V head, and no
   // sequence shorter than its budget in the group.
   std::vector<char> fsel(ngroups, 0);
-  bool any_fsel = false, any_old = false;
+  bool any_fsel = false;
   for (int b0 = 0, gi = 0; b0 < p.B; b0 += kMaxSegs, ++gi) {
     bool ok = use_fused && g_fused_select && fused_select_kernel_ok(kernel) && p.group == 1;
     for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b) ok = p.L[b] >= p.C[b];
@@ -415,7 +412,6 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     }
     fsel[gi] = ok;
     any_fsel = any_fsel || ok;
-    any_old = any_old || !ok;
   }
   // Groups the cooperative selection takes (AUTO prefers it where its grid
   // fits the device: its workgroups share a row's keys, where the split
@@ -500,33 +496,37 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     if (any_fsel) path |= KVSEL_PATH_SELECT_FUSED;
     g_last_path = path;
   }
-  // Calls made only of fused-selection groups clear nothing before they
-  // start: their kernels clear what they own and carry a token.  Every
-  // single-read call carries one: its fallback claims work from
-  // token-tagged counters, and its flags go to the tagged header word.
-  const bool fill = any_old || g_validate;
+  // Single-read calls whose every group selects in the scoring kernel or
+  // with the cooperative or split selection (every sequence at least its
+  // budget) clear nothing before they start: the scoring kernel's
+  // workgroups clear the exchange slots, the cooperative selection's words
+  // and, in the call's first launch, header word 0 (where the selection
+  // kernels' flags go), a share each.  Every single-read call carries a
+  // token: its arrival, decision and fallback counters are token-tagged, and
+  // its flags go to the tagged header word.
+  bool self_clear = use_fused && !g_validate;
+  for (int b0 = 0, gi = 0; b0 < p.B && self_clear; b0 += kMaxSegs, ++gi) {
+    bool ok = fsel[gi] || coop_segs[gi] > 0 || split_s[gi] > 0;
+    for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b) ok = p.L[b] >= p.C[b];
+    self_clear = ok;
+  }
+  const bool fill = !self_clear;
   const unsigned long long token = use_fused && need_scoring ? next_token() : 0ull;
-  record_call(ws, fill, token);
+  record_call(ws, true, token);  // word 0 is cleared by the fill or by the call's first kernel
   if (fill) {
-    // The header, and the exchange records, status words, histograms and
-    // the cooperative selection's words that are in use, start at zero (on
-    // the two-pass path without the cooperative selection the statistics
-    // kernel clears the histograms).  Exchange records, status words and
-    // histograms are contiguous, then the cooperative selection's words.
+    // The header, and the histograms and the cooperative selection's words
+    // that are in use, start at zero (on the two-pass path without the
+    // cooperative selection the statistics kernel clears the histograms; a
+    // single-read scoring kernel clears its own words).  The histograms and
+    // the cooperative selection's words are contiguous.
     const bool hists = !no_chain && (use_fused || lse != nullptr);
-    const size_t lo1 = use_fused ? p.off_ctr : p.off_hist;
-    const size_t hi1 = hists ? p.off_coop : (use_fused ? p.off_hist : lo1);
     ZeroRanges z{};
     z.p[0] = ws;
     z.bytes[0] = 16;  // the call's flag words; the sticky word (kStickyWord) is left alone
-    z.p[1] = ws + lo1;
-    z.bytes[1] = hi1 > lo1 ? (long long)(hi1 - lo1) : 0;
+    z.p[1] = ws + p.off_hist;
+    z.bytes[1] = hists ? (long long)(p.off_coop - p.off_hist) : 0;
     z.p[2] = ws + p.off_coop;
     z.bytes[2] = any_coop ? (long long)(p.off_cw - p.off_coop) : 0;  // the fused selection's words follow
-    // The single-read fallback's claim counters and per-row completion counts
-    // (contiguous).
-    z.p[3] = ws + p.off_flags;
-    z.bytes[3] = use_fused && need_scoring ? (long long)(p.off_cand - p.off_flags) : 0;
     hipError_t e = timed("fill", st, [&] { return launch_zero(z, st); });
     if (e != hipSuccess) return device_error(e, "fill launch");
   }
@@ -592,47 +592,54 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     uint32_t* gseg = (uint32_t*)((char*)segcnt + (size_t)b0 * p.heads * kSegCntBytes);
     hipError_t e;
     FusedSel sel{};
-    if (fsel[b0 / kMaxSegs]) {
-      sel.on = 1;
+    if (use_fused) {
+      // Every single-read launch: the token, the arrival tokens, decision and
+      // fallback counters, the completion counts and chunk statistics of the
+      // fallback; the exchange slots (not read with handed-over statistics)
+      // are cleared by the kernel's workgroups, a share each.
+      const int gi = b0 / kMaxSegs;
       sel.force_abort = g_force_fallback;
       sel.token = token;
       sel.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
-      sel.flags = (unsigned long long*)(ws + p.off_flags) + (long long)kFusedFlagWords * (b0 / kMaxSegs);
+      sel.flags = (unsigned long long*)(ws + p.off_flags) + (long long)kFusedFlagWords * gi;
+      sel.rowfb = (unsigned long long*)(ws + p.off_rowfb) + (long long)b0 * p.heads * 2;
+      sel.kslot = (float*)(ws + p.off_kslot);
+      sel.clr[0] = lse == nullptr ? (unsigned long long*)(ws + p.off_ctr) : nullptr;
+      sel.clr_words[0] = lse == nullptr ? (long long)(p.off_hist - p.off_ctr) / 8 : 0;
+      if (!fill && coop_segs[gi] > 0) {
+        // The cooperative selection's status blocks and row words of this
+        // group, which its launches after this one need at zero.
+        sel.clr[1] = (unsigned long long*)(ws + p.off_coop) + (long long)kFusedStatusWords * kCoopLaunches * gi / 2;
+        sel.clr_words[1] = (long long)kFusedStatusWords * kCoopLaunches / 2;
+        sel.clr[2] = (unsigned long long*)(ws + p.off_coop) +
+                     ((long long)kFusedStatusWords * kCoopLaunches * ngroups + (long long)b0 * p.heads * coop_row_words()) / 2;
+        sel.clr_words[2] = (long long)rows * coop_row_words() / 2;
+      }
+      if (!fill && b0 == 0) {  // header words 0 and 1: the selection kernels' flags of this call
+        sel.clr[3] = (unsigned long long*)ws;
+        sel.clr_words[3] = 1;
+      }
+    }
+    if (fsel[b0 / kMaxSegs]) {
+      sel.on = 1;
       sel.cw = (unsigned long long*)(ws + p.off_cw);
       sel.halo = (unsigned long long*)(ws + p.off_halo);
       sel.cslot = (unsigned*)(ws + p.off_cslot);
       sel.fslot = (unsigned*)(ws + p.off_fslot);
-      // Cleared by the kernel's workgroups, a share each: the exchange slots
-      // (not read with handed-over statistics), then the count, halo and
+      // Also cleared by the kernel's workgroups: the count, halo and
       // histogram words (contiguous).
-      sel.clr[0] = lse == nullptr ? (unsigned long long*)(ws + p.off_ctr) : nullptr;
-      sel.clr_words[0] = lse == nullptr ? (long long)(p.off_status - p.off_ctr) / 8 : 0;
       sel.clr[1] = (unsigned long long*)(ws + p.off_cw);
       sel.clr_words[1] = (long long)(p.off_flags - p.off_cw) / 8;
-      sel.rowfb = (unsigned long long*)(ws + p.off_rowfb) + (long long)b0 * p.heads * 2;
       sel.cand = (unsigned long long*)(ws + p.off_cand);
       sel.pooled = pooled_opt;
-      sel.kslot = (float*)(ws + p.off_kslot);
       sel.indices = indices;
       sel.V = V;
       sel.K_out = K_out;
       sel.V_out = V_out;
     }
-    if (!sel.on && use_fused) {  // the fallback's counters, completion counts and chunk statistics
-      sel.token = token;
-      sel.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
-      sel.flags = (unsigned long long*)(ws + p.off_flags) + (long long)kFusedFlagWords * (b0 / kMaxSegs);
-      sel.rowfb = (unsigned long long*)(ws + p.off_rowfb) + (long long)b0 * p.heads * 2;
-      sel.kslot = (float*)(ws + p.off_kslot);
-    }
     if (items > 0 && use_fused) {
-      unsigned* gstatus = status + (long long)kFusedStatusWords * (b0 / kMaxSegs);
-      if (g_force_fallback && lse == nullptr && !sel.on) {
-        e = launch_fill_u32(gstatus + 2, 1, kFusedAbort, st);  // decided before any workgroup arrives
-        if (e != hipSuccess) return device_error(e, "fill launch");
-      }
       e = timed("window_fused", st,
-                [&] { return launch_fused_scoring(a, Q, K, lse, counters, gstatus, votes, row_stats, sel, st); });
+                [&] { return launch_fused_scoring(a, Q, K, lse, counters, votes, row_stats, sel, st); });
       if (e != hipSuccess) return device_error(e, "window_fused launch");
       if (sel.on) continue;  // the selection ran in the same kernel
     } else if (items > 0 && lse != nullptr) {

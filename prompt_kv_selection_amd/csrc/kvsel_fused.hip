@@ -33,7 +33,7 @@
 // head and merges them in a fixed order (the result does not depend on arrival order).  The
 // lowest mantissa bit of every published m_i is set, and the same tagged m_i
 // is used for the chunk's exponentials, so a set bit marks a written word in a
-// slot array that starts zeroed.
+// slot array that the workgroups clear before the residency decision.
 //
 // Roles inside a workgroup.  Eight streaming waves, an exchange wave, a
 // memory wave and a publisher wave.
@@ -79,13 +79,15 @@
 // written word is never zero and no atomics are needed.  This path is opt-in:
 // its end phase costs more device-scope round trips than the separate
 // selection kernels take in all.
-// Nothing is cleared by a separate launch: before it arrives, each workgroup
-// clears its share of the words the call publishes (exchange slots, halo,
-// histogram, count and flag words), and the arrival and the residency
-// decision carry a per-call token instead of counting from zero.
-// GO therefore also means every shared word is clear.  On ABORT (not all
-// resident) the workgroups take work from token-tagged counters instead: the
-// chunks' statistics, then their votes (two passes over K), then whole rows'
+// Nothing is cleared by a separate launch, with or without the fused
+// selection: before it arrives, each workgroup clears its share of the words
+// the call publishes (exchange slots, halo, histogram, count and flag words)
+// and of the words the selection kernels after it in the call need at zero,
+// and the arrival and the residency decision carry a per-call token instead
+// of counting from zero.  GO therefore also means every shared word is
+// clear.  On ABORT (not all resident) the workgroups take work from
+// token-tagged counters instead: the chunks' statistics, then their votes
+// (two passes over K), then with the fused selection whole rows'
 // selections, each phase waiting only on work already claimed by running
 // workgroups.
 //
@@ -206,6 +208,12 @@ __device__ __forceinline__ void flag_error(const Launch& a, const FusedSel& f, u
     raise_error(a.err, bit);
 }
 
+// Debug builds: an index outside its range is recorded in the call's flags.
+__device__ __forceinline__ void fused_debug_check(const Launch& a, const FusedSel& f, bool ok) {
+  if constexpr (kDebug)
+    if (!ok) flag_error(a, f, kErrIndexRange);
+}
+
 __device__ __forceinline__ unsigned long long load64(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -220,16 +228,24 @@ __device__ __forceinline__ void store32(unsigned* p, unsigned v) {
 }
 
 // Token-tagged counters: (tag << 24) | count, where a word whose tag is not
-// this call's counts as zero.  Adding returns the count before the add.
+// this call's counts as zero.  Adding returns the count before the add.  An
+// add is one atomic add; the call's first add finds another tag there and
+// swaps in (tag, n), and adds that reached the old word before that swap are
+// made again.  (Counts stay far below 2^24; a carry out of a stale count
+// into the tag bits cannot produce this call's tag but by a 2^-40 chance.)
 __device__ __forceinline__ unsigned tok_add(unsigned long long* w, unsigned long long tag, unsigned n) {
-  unsigned long long cur = load64(w);
   for (;;) {
-    const unsigned cnt = (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
-    unsigned long long expect = cur;
-    if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)(cnt + n),
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      return cnt;
-    cur = expect;
+    const unsigned long long old =
+        __hip_atomic_fetch_add(w, (unsigned long long)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old >> 24) == tag) return (unsigned)(old & 0xFFFFFFull);
+    unsigned long long cur = old + n;
+    while ((cur >> 24) != tag) {
+      unsigned long long expect = cur;
+      if (__hip_atomic_compare_exchange_strong(w, &expect, (tag << 24) | (unsigned long long)n, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        return 0u;
+      cur = expect;
+    }
   }
 }
 __device__ __forceinline__ unsigned tok_count(const unsigned long long* w, unsigned long long tag) {
@@ -237,7 +253,7 @@ __device__ __forceinline__ unsigned tok_count(const unsigned long long* w, unsig
   return (cur >> 24) == tag ? (unsigned)(cur & 0xFFFFFFull) : 0u;
 }
 
-// ---- exchange slots in the workspace, zeroed per call: per (sequence,
+// ---- exchange slots in the workspace, cleared per call: per (sequence,
 // head, chunk) 32 words of 64 bits, word i = (tagged m_i bits, z_i bits).
 constexpr int kSlotWords = 32;
 __device__ __forceinline__ float tag_max(float m) { return __uint_as_float(__float_as_uint(m) | 1u); }
@@ -259,7 +275,7 @@ struct Sync {
   unsigned timeout;
   unsigned abort;                  // the grid is not all resident: every wave leaves its loop
   unsigned issued;                 // the clears of the shared words are issued (fused selection)
-  unsigned zeroed;                 // this workgroup's shared words are clear (fused selection)
+  unsigned zeroed;                 // every workgroup's shared words are clear (after GO)
   unsigned go;                     // the residency decision (kFusedGo / kFusedAbort), once taken
 };
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -665,8 +681,8 @@ __device__ __forceinline__ void ctl_publish(const Launch& a, unsigned long long*
   const int lane = threadIdx.x & 63;
   const int W = a.W;
   unsigned on_b[kNR] = {};  // owned rounds awaited so far, per residue
-  // The slots this workgroup writes are clear: cleared before the launch, or
-  // with the fused selection by every workgroup before the decision (GO).
+  // The slots this workgroup writes are clear: every workgroup cleared its
+  // share before the decision (GO).
   if (!lds_wait_ge(sy, &sy->zeroed, 1u)) return;
   for (int k = 0; k < a.rounds; ++k) {
     const Work w0 = round_work(a, k);
@@ -842,54 +858,60 @@ __device__ __forceinline__ SelRound sel_round(const Launch& a, int r) {
 
 // Exchange wave, at kernel start, before any other load of the workgroup is
 // issued: clear this workgroup's share of the words the call's workgroups
-// publish to each other (exchange, count, halo and histogram slots).  The
-// arrival follows once the stores are done, so GO means every word is clear;
-// nothing is published before GO.
+// publish to each other (exchange, count, halo and histogram slots) and of
+// the words later kernels of the call need at zero.  The arrival follows once
+// the stores are done, so GO means every word is clear; nothing is published
+// before GO.  Words only later kernels read are clear once the launch ends.
 __device__ __forceinline__ void sel_clear(const FusedSel& f) {
   const int lane = threadIdx.x & 63;
   const long long nwg = gridDim.x;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < 4; ++r) {
     const long long n = f.clr_words[r];
     const long long per = (n + nwg - 1) / nwg;
     const long long lo = per * blockIdx.x, hi = min(n, lo + per);
     for (long long i = lo + lane; i < hi; i += 64) store64(f.clr[r] + i, 0ull);
   }
 }
+// Arrival: the workgroup's own word takes the call's token (a store: no
+// atomics to contend).
 __device__ __forceinline__ void sel_arrive(const FusedSel& f) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clears are done
   if ((threadIdx.x & 63) == 0) store64(f.flags + blockIdx.x, f.token);
 }
 
-// Exchange wave: the residency decision of the call.  A workgroup that sees
-// every arrival token of this call decides GO; one that has waited past the
-// bound decides ABORT.  Both are a compare-and-swap of the one decision word
-// to this call's token plus the decision, and the first one for this token
-// wins, so every workgroup follows the same decision.  The wait always ends:
-// ABORT is decided by the bound at the latest.
+// Exchange wave: the residency decision of the call.  Workgroup 0, once it
+// sees every arrival token of this call, decides GO (GO needs every
+// workgroup resident, workgroup 0 among them; only one workgroup polls the
+// grid's words, the others the decision word alone, so the polling stays
+// off the memory system the K stream uses); any workgroup that has waited
+// past the bound decides ABORT.  Both are a compare-and-swap of the one
+// decision word to this call's token plus the decision, and the first one
+// for this token wins, so every workgroup follows the same decision.  The
+// wait always ends: ABORT is decided by the bound at the latest.
 __device__ __forceinline__ unsigned sel_decide(const Launch& a, const FusedSel& f) {
   const int lane = threadIdx.x & 63;
   unsigned long long* dec = f.flags + kFlagWordsMax;
   const unsigned grid = gridDim.x;
   const long long t0 = wall_clock64();
   for (;;) {
-    // The decision word and every arrival token, loaded together.
+    // The decision word and (workgroup 0) every arrival token, loaded together.
     unsigned long long cur = 0ull;
     if (lane == 0) cur = load64(dec);
-    unsigned long long tk[kFlagWordsMax / 64];
+    bool mine = blockIdx.x == 0 && !f.force_abort;
+    if (blockIdx.x == 0) {
 #pragma unroll
-    for (int t = 0; t < kFlagWordsMax / 64; ++t) {
-      const unsigned i = (unsigned)(lane + 64 * t);
-      tk[t] = i < grid ? load64(f.flags + i) : f.token;
+      for (int t = 0; t < kFlagWordsMax / 64; ++t) {
+        const unsigned i = (unsigned)(lane + 64 * t);
+        if (i < grid) mine = mine && load64(f.flags + i) == f.token;
+      }
     }
-    bool all = !f.force_abort;
-#pragma unroll
-    for (int t = 0; t < kFlagWordsMax / 64; ++t) all = all && tk[t] == f.token;
+    const bool all = __ballot(!mine) == 0ull;
     cur = ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(cur >> 32)) << 32) |
           (unsigned)__builtin_amdgcn_readfirstlane((int)cur);
     if ((cur & ~3ull) == f.token) return (unsigned)(cur & 3ull);
     unsigned want = 0u;
-    if (__ballot(!all) == 0ull) want = kFusedGo;
+    if (all) want = kFusedGo;
     if (want == 0u && (f.force_abort || wall_clock64() - t0 > a.residency_ticks)) want = kFusedAbort;
     if (want != 0u) {
       // The swap's outcome is the decision: ours if it took, else the value
@@ -1427,7 +1449,7 @@ __device__ __forceinline__ void sel_end_pick(const Launch& a, const FusedSel& f,
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     if ((pm >> u) & 1u) {
-      KVSEL_DEBUG_CHECK(before + slot < (uint32_t)q.count, a.err);
+      fused_debug_check(a, f, before + slot < (uint32_t)q.count);
       if (before + slot < (uint32_t)q.count) {  // always, unless a timed-out wait left the counts short
         out[before + slot] = S0 + u;
         list[slot] = S0 + u;
@@ -1487,19 +1509,13 @@ __device__ __forceinline__ void sel_finish(const Launch& a, const FusedSel& f, c
 
 // ---- fallback (ABORT: not all resident), of both kernel variants
 
-// Claims and completion counts of the fallback.  With the fused selection
-// nothing was cleared before the call, so they are token-tagged (a claim is
-// a compare-and-swap loop); otherwise the fill zeroed them and a claim is
-// one atomic add, which many workgroups can make at once without retries.
-template <bool kTok>
+// Claims and completion counts of the fallback.  Nothing was cleared before
+// the call, so they are token-tagged: a claim is a compare-and-swap loop.
 __device__ __forceinline__ unsigned fb_claim(unsigned long long* w, unsigned long long tag, unsigned n = 1u) {
-  if constexpr (kTok) return tok_add(w, tag, n);
-  return (unsigned)__hip_atomic_fetch_add(w, (unsigned long long)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return tok_add(w, tag, n);
 }
-template <bool kTok>
 __device__ __forceinline__ unsigned fb_count(const unsigned long long* w, unsigned long long tag) {
-  if constexpr (kTok) return tok_count(w, tag);
-  return (unsigned)load64(w);
+  return tok_count(w, tag);
 }
 
 // Inclusive scan over the workgroup (kThreads); total gets the sum.
@@ -1699,7 +1715,7 @@ __device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f
     const uint32_t eq_rank = wg_incl(eq ? 1u : 0u, sh, eq_tot) - (eq ? 1u : 0u);
     const bool take = gt || (eq && eq_seen + eq_rank < need_eq);
     const uint32_t pos = wg_incl(take ? 1u : 0u, sh, take_tot) - (take ? 1u : 0u);
-    KVSEL_DEBUG_CHECK(!take || before + pos < (uint32_t)count, a.err);
+    fused_debug_check(a, f, !take || before + pos < (uint32_t)count);
     if (take && before + pos < (uint32_t)count) {
       out[before + pos] = j;
       list[pos] = j;
@@ -1747,7 +1763,7 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
   for (int e = 0; e < a.n; ++e) items += (unsigned)(a.seg[e].nh * fb_groups(a.seg[e]));
   for (int phase = kLse ? 1 : 0; phase < 2; ++phase) {
     for (;;) {
-      if (tid == 0) s_claim = fb_claim<kSel>(ctr + phase, tag);
+      if (tid == 0) s_claim = fb_claim(ctr + phase, tag);
       __syncthreads();
       const unsigned t = s_claim;
       __syncthreads();
@@ -1765,7 +1781,7 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
       const int lo = it.c * kS, hi = min(L, lo + it.nc * kS);
       fb_load_q<D>(a, Q, hs, qbuf);
       if (phase == 1 && tid == 0) {  // the statistics of every chunk of the row are there
-        const bool ok = kLse || sel_wait(a, [&] { return fb_count<kSel>(f.rowfb + 2ll * it.row, tag) >= (unsigned)s.fc; });
+        const bool ok = kLse || sel_wait(a, [&] { return fb_count(f.rowfb + 2ll * it.row, tag) >= (unsigned)s.fc; });
         if (!ok) flag_error(a, f, kErrExchangeWait);
       }
       __syncthreads();
@@ -1835,14 +1851,14 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) (void)fb_claim<kSel>(f.rowfb + 2ll * it.row + phase, tag, (unsigned)it.nc);  // chunks done
+      if (tid == 0) (void)fb_claim(f.rowfb + 2ll * it.row + phase, tag, (unsigned)it.nc);  // chunks done
       __syncthreads();
     }
   }
   if constexpr (!kSel) return;
   const int rows = fb_rows(a);
   for (;;) {
-    if (tid == 0) s_claim = fb_claim<kSel>(ctr + 2, tag);
+    if (tid == 0) s_claim = fb_claim(ctr + 2, tag);
     __syncthreads();
     const unsigned t = s_claim;
     __syncthreads();
@@ -1851,7 +1867,7 @@ __device__ __forceinline__ void sel_fallback(const Launch& a, const FusedSel& f,
     const Seg& s = a.seg[e];
     const int h = s.h0 + ((int)t - s.row0);
     if (tid == 0) {  // every chunk's votes of the row are there
-      const bool ok = sel_wait(a, [&] { return fb_count<kSel>(f.rowfb + 2ll * t + 1, tag) >= (unsigned)s.fc; });
+      const bool ok = sel_wait(a, [&] { return fb_count(f.rowfb + 2ll * t + 1, tag) >= (unsigned)s.fc; });
       if (!ok) flag_error(a, f, kErrSelectWait);
     }
     __syncthreads();
@@ -1867,7 +1883,6 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
                                                                   const __bf16* __restrict__ K,
                                                                   const float* __restrict__ lse,
                                                                   unsigned long long* __restrict__ ex,
-                                                                  unsigned* __restrict__ status,
                                                                   float* __restrict__ votes,
                                                                   float* __restrict__ row_stats) {
   using G = TileGeom<D>;
@@ -1881,27 +1896,25 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
   static_assert(sizeof(s_x) >= 4 * (4 * kFusedMaxRounds + (kThreads / 64) * kS), "the end phase's words fit s_x");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  // Variants whose workgroups wait for each other: those that exchange row
+  // statistics or select.
+  constexpr bool kHandshake = kSel || !kLse;
   KVSEL_FUSED_MARK(23, 0);
-  unsigned arrived = 0u;
-  if (!kSel && !kLse && wave == kExWave && lane == 0) arrived = arrive(status);
   if (threadIdx.x == 0) {
     sy = Sync{};
-    sy.zeroed = kSel ? 0u : 1u;
+    sy.zeroed = kHandshake ? 0u : 1u;
   }
   __syncthreads();  // afterwards waves meet through LDS flags (and once more at the end)
-  // With the fused selection the clears of the shared words go first, so
-  // that they do not queue behind the K tiles (the decision that follows them
-  // gates the publication of every round); then the first K tiles and Qwin of
-  // rounds 0 and 1.
-  if constexpr (kSel) {
-    if (wave == kExWave) {
-      KVSEL_FUSED_MARK(22, 0);
-      sel_clear(f);
-      KVSEL_FUSED_MARK(22, 1);
-      lds_set(&sy.issued, 1u);
-    } else if (wave < kSW || wave == kMemWave) {
-      (void)lds_wait_ge(&sy, &sy.issued, 1u);
-    }
+  // The clears go first, so that they do not queue behind the K tiles (the
+  // decision that follows them gates the publication of every round); then
+  // the first K tiles and Qwin of rounds 0 and 1.
+  if (wave == kExWave) {
+    KVSEL_FUSED_MARK(22, 0);
+    sel_clear(f);
+    KVSEL_FUSED_MARK(22, 1);
+    lds_set(&sy.issued, 1u);
+  } else if (wave < kSW || wave == kMemWave) {
+    (void)lds_wait_ge(&sy, &sy.issued, 1u);
   }
   WaveTiles cur{K, 0, 0, false};
   int issued = 0, consumed = 0;
@@ -1913,7 +1926,7 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
     ctl_issue_q<D>(a, 1, Q, s_q[1]);
   }
   if (wave == kExWave) {
-    if constexpr (kSel) {
+    if constexpr (kHandshake) {
       // Arrive once the clears are done, decide; then the statistics.
       sel_arrive(f);
       KVSEL_FUSED_MARK(22, 2);
@@ -1929,16 +1942,8 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
         ctl_lse(a, f, lse, s_m, &sy);
       else
         ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
-    } else if constexpr (kLse) {
-      ctl_lse(a, f, lse, s_m, &sy);  // no workgroup waits for another
     } else {
-      KVSEL_FUSED_MARK(23, 4);
-      const unsigned d = decide(status, arrived, a.err, kFlagScoringFallback, a.residency_ticks);
-      KVSEL_FUSED_MARK(23, 5);
-      if (d == kFusedGo)
-        ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
-      else
-        lds_set(&sy.abort, 1u);  // not all resident: every wave leaves its loop
+      ctl_lse(a, f, lse, s_m, &sy);  // no workgroup waits for another
     }
   } else if (wave == kMemWave) {
     ctl_memory<D>(a, !kSel, Q, votes, s_q, s_votes, &sy);
@@ -2075,22 +2080,22 @@ int grid_for() {
 
 template <int D, bool kLse, bool kSel>
 hipError_t launch_t(const Launch& a, const FusedSel& f, const void* Q, const void* K, const float* lse,
-                    unsigned long long* ex, unsigned* status, float* votes, float* row_stats, hipStream_t st) {
+                    unsigned long long* ex, float* votes, float* row_stats, hipStream_t st) {
   const int grid = grid_for<D, kLse, kSel>();
   if (grid <= 0 || grid > kFlagWordsMax) return hipErrorNotSupported;
   Launch la = a;
   const __bf16* q = (const __bf16*)Q;
   const __bf16* k = (const __bf16*)K;
   hipLaunchKernelGGL((window_fused_kernel<D, kLse, kSel>), dim3(grid), dim3(kSel ? kThreads : kThreadsPlain), 0, st,
-                     la, f, q, k, lse, ex, status, votes, row_stats);
+                     la, f, q, k, lse, ex, votes, row_stats);
   return hipGetLastError();
 }
 
 template <int D, bool kLse>
 hipError_t launch_d(const Launch& a, const FusedSel& f, const void* Q, const void* K, const float* lse,
-                    unsigned long long* ex, unsigned* status, float* votes, float* row_stats, hipStream_t st) {
-  if (f.on) return launch_t<D, kLse, true>(a, f, Q, K, lse, ex, status, votes, row_stats, st);
-  return launch_t<D, kLse, false>(a, f, Q, K, lse, ex, status, votes, row_stats, st);
+                    unsigned long long* ex, float* votes, float* row_stats, hipStream_t st) {
+  if (f.on) return launch_t<D, kLse, true>(a, f, Q, K, lse, ex, votes, row_stats, st);
+  return launch_t<D, kLse, false>(a, f, Q, K, lse, ex, votes, row_stats, st);
 }
 
 }  // namespace
@@ -2112,18 +2117,17 @@ int fused_grid(int W, int D) {
 int fused_exchange_bytes() { return kSlotWords * 8; }
 
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* ex,
-                                unsigned* status, float* votes, float* row_stats, const FusedSel& sel,
-                                hipStream_t st) {
+                                float* votes, float* row_stats, const FusedSel& sel, hipStream_t st) {
   if (a.W > 32 || a.S != kS) return hipErrorNotSupported;
   if (sel.on && (!fused_select_kernel_ok(a.kernel) || a.group > 1)) return hipErrorNotSupported;
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(ex);
   if (lse != nullptr) {
-    if (a.D == 128) return launch_d<128, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
-    if (a.D == 64) return launch_d<64, true>(a, sel, Q, K, lse, slots, status, votes, nullptr, st);
+    if (a.D == 128) return launch_d<128, true>(a, sel, Q, K, lse, slots, votes, nullptr, st);
+    if (a.D == 64) return launch_d<64, true>(a, sel, Q, K, lse, slots, votes, nullptr, st);
     return hipErrorNotSupported;
   }
-  if (a.D == 128) return launch_d<128, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
-  if (a.D == 64) return launch_d<64, false>(a, sel, Q, K, nullptr, slots, status, votes, row_stats, st);
+  if (a.D == 128) return launch_d<128, false>(a, sel, Q, K, nullptr, slots, votes, row_stats, st);
+  if (a.D == 64) return launch_d<64, false>(a, sel, Q, K, nullptr, slots, votes, row_stats, st);
   return hipErrorNotSupported;
 }
 

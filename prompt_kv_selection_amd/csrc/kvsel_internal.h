@@ -241,12 +241,13 @@ hipError_t launch_select_split(const Launch& a, int rows, int splits, int kpt, i
 // Single-read scoring (persistent kernel, one workgroup per CU).
 // fused_positions() gives S for the kernel variant, fused_grid() the grid (0
 // if the variant cannot run); launch_fused_scoring() returns
-// hipErrorNotSupported when the shape is not covered.  status points at
-// kFusedStatusWords zeroed words: error flags, arrived groups, the residency
-// decision (kFusedGo or kFusedAbort; a host-written kFusedAbort forces the
-// fallback), the fallback's work counter, then kArriveGroups arrival counters
-// kArriveStride words apart (same-address atomics serialise, so the
-// workgroups' arrivals are spread over separate lines).
+// hipErrorNotSupported when the shape is not covered.
+// The cooperative selection's status block: kFusedStatusWords zeroed words:
+// error flags, arrived groups, the residency decision (kFusedGo or
+// kFusedAbort; a host-written kFusedAbort forces the fallback), the
+// fallback's work counter, then kArriveGroups arrival counters kArriveStride
+// words apart (same-address atomics serialise, so the workgroups' arrivals
+// are spread over separate lines).
 constexpr unsigned kFusedGo = 1, kFusedAbort = 2;
 constexpr int kArriveGroups = 16;
 constexpr int kArriveStride = 64;
@@ -331,24 +332,25 @@ __device__ inline unsigned decide(unsigned* status, unsigned arrived, unsigned* 
   return decide_end(status, err, fallback_bit, ticks);
 }
 
-// The selection fused into the single-read scoring kernel (pooling, top-k,
-// window, K/V copy), and its words in the workspace.  Shared words are
-// cleared by the kernel's workgroups, a share each, before they arrive; the
-// arrival and residency decision carry a per-call token instead of starting
-// from zero, and flags go to the tagged header word, so the call needs no
-// fill launch.
+// The single-read scoring kernel's per-call words, and the selection that
+// can be fused into it (pooling, top-k, window, K/V copy).  Shared words are
+// cleared by the kernel's workgroups, a share each, before they arrive (and
+// so are words that the kernels after it in the call need at zero); the
+// arrival, the residency decision and the fallback's counters carry a
+// per-call token instead of starting from zero, and the kernel's flags go to
+// the tagged header word, so the call needs no fill launch.
 constexpr int kHaloWords = 8;           // per chunk: its first 3 and last 3 votes, tagged
 
 struct FusedSel {
-  int on;                       // 1: select in the scoring kernel (the arrays below are used)
+  int on;                       // 1: select in the scoring kernel (the selection's arrays are used)
   int force_abort;              // testing: decide ABORT at once
   unsigned long long token;     // this call's token (low two bits zero)
   unsigned long long* errw;     // the header's tagged flag word (kTaggedWord)
   unsigned long long* flags;    // [grid] arrival tokens, then the decision word, then 3 claim counters
   unsigned long long* cw;       // [exchange slot] the chunk's count word
   unsigned long long* halo;     // [exchange slot][kHaloWords]
-  unsigned long long* clr[2];   // ranges of 8-byte words every call clears (a share per workgroup)
-  long long clr_words[2];
+  unsigned long long* clr[4];   // ranges of 8-byte words the launch clears (a share per workgroup), or nullptr
+  long long clr_words[4];
   unsigned* cslot;              // [exchange slot][64] the chunk's coarse histogram, count + 1
   unsigned* fslot;              // [exchange slot][32] its fine histogram inside the coarse bin of tau, count + 1
   unsigned long long* rowfb;    // [row][2] fallback completion counters (token-tagged)
@@ -373,12 +375,14 @@ int fused_exchange_bytes();  // per (sequence, head, chunk) exchange slot
 // of the exchange wave (the padding is never written and never merged).
 __host__ __device__ inline int fused_slot_stride(int fc) { return (fc + 63) / 64 * 64; }
 // With lse != nullptr (as for launch_window_votes) the workgroups exchange
-// nothing and need not be co-resident: exchange and status are not used.
-// With sel.on the kernel also selects: indices and K/V rows are written, and
-// exchange, sel's arrays and status need no clearing (status is unused).
+// nothing and need not be co-resident: exchange is not used.
+// With sel.on the kernel also selects: indices and K/V rows are written.
+// Nothing needs clearing before the launch: the workgroups clear sel.clr's
+// ranges (the exchange slots among them) before their arrival, and the
+// arrival, the decision, the fallback's counters and the flags carry
+// sel.token.  sel.force_abort decides ABORT at once (testing).
 hipError_t launch_fused_scoring(const Launch& a, const void* Q, const void* K, const float* lse, unsigned* exchange,
-                                unsigned* status, float* votes, float* row_stats, const FusedSel& sel,
-                                hipStream_t st);
+                                float* votes, float* row_stats, const FusedSel& sel, hipStream_t st);
 hipError_t launch_fill_u32(unsigned* p, long long n, unsigned v, hipStream_t st);
 // Zero up to kZeroRanges byte ranges in one launch (16-byte aligned pointers
 // and sizes, else hipErrorInvalidValue; empty ranges are skipped).

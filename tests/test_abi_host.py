@@ -43,9 +43,7 @@ def test_workspace_sizes(B):
     n = B.lib.kvsel_workspace_bytes(32, 32768, 32, 1024, 128, 1)
     # header (error flags), two-pass partial (max, sum) per (head, chunk, row), votes, pooled,
     # selection threshold and per-segment counts, single-read exchange slots
-    # (per head and 512-position chunk),
-    # status words (error flags, decision, fallback counter and 16 arrival
-    # counters on lines of their own), first-digit histograms, the
+    # (per head and 512-position chunk), first-digit histograms, the
     # cooperative selection's status words (one block for each of up to 8
     # launches) and per-row words (histograms,
     # segment counts, candidate entries); then the fused selection's words:
@@ -54,7 +52,7 @@ def test_workspace_sizes(B):
     # per row two completion counters, 8-byte candidates laid out like the
     # votes, and per exchange slot the chunk's 512 pooled scores
     expect_min = (256 + 2 * 32 * 32 * 32 * 4 + 2 * 32 * (32768 - 32) * 4 + 32 * 8 + 32 * 2 * 512 * 4
-                  + 32 * 64 * 256 + 17 * 256 + 32 * 2048 * 4 + 8 * 17 * 256 + 32 * (5120 + 128 + 8192) * 4
+                  + 32 * 64 * 256 + 32 * 2048 * 4 + 8 * 17 * 256 + 32 * (5120 + 128 + 8192) * 4
                   + 32 * 64 * 8 + 32 * 64 * 8 * 8 + (1024 + 8) * 8 + 32 * 64 * (64 + 32) * 4 + 32 * 2 * 8
                   + 32 * (32768 - 32) * 8 + 32 * 64 * 512 * 4)
     assert expect_min <= n <= expect_min + 13 * 256
