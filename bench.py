@@ -519,14 +519,17 @@ def digest(tag, name, title):
                f"multiplied by {fs:.3f} and WRITE_SIZE by {wsc:.3f} to get bytes.", "",
                "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | write MB (scaled) | "
                "algorithmic MB |", "|---|---|---|---|---|---|---|"]
-        n_calls = min(v for k, v in nf.items() if k != "copy")
+        # Calls profiled: one dispatch of a scoring kernel starts each.
+        starts = [k for k in ("window_fused", "window_fused_lse", "window_stats") if k in nf] or \
+            [k for k in ("window_votes",) if k in nf]
+        n_calls = sum(nf[k] for k in starts) if starts else None
         for k in fetch:
             if k == "copy":
                 continue
             rb, wb = fetch[k] * 1024 * fs, write.get(k, 0) * 1024 * wsc
             ab = kernel_alg_bytes(k.replace("_lse", ""), wl, k.endswith("_lse") or lse, group, None, "gather" in fetch)
-            if ab is not None:  # per dispatch: a call may launch a kernel several times
-                ab /= nf[k] / n_calls
+            if ab is not None and n_calls:  # per dispatch: a call may launch a kernel several times
+                ab /= max(1.0, nf[k] / n_calls)
             md.append(f"| `{k}` | {nf[k]} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {rb / 1e6:.1f} | "
                       f"{wb / 1e6:.1f} | {'' if ab is None else f'{ab / 1e6:.1f}'} |")
             if k in TRAFFIC_OWNER.get(tag, ()) and k in KERNEL_SOURCES:
