@@ -496,22 +496,25 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     if (any_fsel) path |= KVSEL_PATH_SELECT_FUSED;
     g_last_path = path;
   }
-  // Single-read calls whose every group selects in the scoring kernel or
-  // with the cooperative or split selection (every sequence at least its
-  // budget) clear nothing before they start: the scoring kernel's
-  // workgroups clear the exchange slots, the cooperative selection's words
-  // and, in the call's first launch, header word 0 (where the selection
-  // kernels' flags go), a share each.  Every single-read call carries a
-  // token: its arrival, decision and fallback counters are token-tagged, and
-  // its flags go to the tagged header word.
-  bool self_clear = use_fused && !g_validate;
+  // Calls whose first kernel clears what the call needs at zero launch no
+  // fill: single-read calls whose every group selects in the scoring kernel
+  // or with the cooperative or split selection, and two-pass calls that
+  // compute the row statistics, every sequence at least its budget.  The
+  // scoring kernel's workgroups clear the exchange slots (single-read), the
+  // histograms (whole-row and segment selections), the cooperative
+  // selection's words and, in the call's first launch, header word 0 (where
+  // the selection kernels' flags go), a share each.  Such calls and every
+  // single-read call carry a token: the scoring kernels' flags go to the
+  // tagged header word, and the single-read arrival, decision and fallback
+  // counters are token-tagged.
+  bool self_clear = !g_validate && (use_fused || lse == nullptr);
   for (int b0 = 0, gi = 0; b0 < p.B && self_clear; b0 += kMaxSegs, ++gi) {
-    bool ok = fsel[gi] || coop_segs[gi] > 0 || split_s[gi] > 0;
+    bool ok = !use_fused || fsel[gi] || coop_segs[gi] > 0 || split_s[gi] > 0;
     for (int b = b0; b < std::min(p.B, b0 + kMaxSegs) && ok; ++b) ok = p.L[b] >= p.C[b];
     self_clear = ok;
   }
   const bool fill = !self_clear;
-  const unsigned long long token = use_fused && need_scoring ? next_token() : 0ull;
+  const unsigned long long token = (use_fused && need_scoring) || self_clear ? next_token() : 0ull;
   record_call(ws, true, token);  // word 0 is cleared by the fill or by the call's first kernel
   if (fill) {
     // The header, and the histograms and the cooperative selection's words
@@ -549,6 +552,8 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     const int nb = std::min(kMaxSegs, p.B - b0);
     Launch a = base_launch(p, kernel, pooling);
     a.err = err;
+    a.token = token;
+    a.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
     a.n = nb;
     a.S = p.fS;
     a.rounds = 0;
@@ -610,7 +615,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
         // The cooperative selection's status blocks and row words of this
         // group, which its launches after this one need at zero.
         sel.clr[1] = (unsigned long long*)(ws + p.off_coop) + (long long)kFusedStatusWords * kCoopLaunches * gi / 2;
-        sel.clr_words[1] = (long long)kFusedStatusWords * kCoopLaunches / 2;
+        sel.clr_words[1] = (long long)kFusedStatusWords * coop_nl[gi] / 2;  // the launches made
         sel.clr[2] = (unsigned long long*)(ws + p.off_coop) +
                      ((long long)kFusedStatusWords * kCoopLaunches * ngroups + (long long)b0 * p.heads * coop_row_words()) / 2;
         sel.clr_words[2] = (long long)rows * coop_row_words() / 2;
@@ -647,9 +652,27 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, lse, votes, nullptr, st); });
       if (e != hipSuccess) return device_error(e, "window_votes launch");
     } else if (items > 0) {
-      e = timed("window_stats", st, [&] {
-        return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, ghist, (long long)rows * 2048, st);
-      });
+      // Cleared by the statistics kernel for the kernels after it: the
+      // histograms of a whole-row or segment selection; without a fill, the
+      // cooperative selection's words of this group and (first group) header
+      // words 0 and 1.
+      const int gi = b0 / kMaxSegs;
+      const bool chain = coop_segs[gi] == 0 && split_s[gi] == 0;
+      WordRanges clear{};
+      clear.p[0] = ghist;
+      clear.n[0] = chain ? (long long)rows * 2048 : 0;
+      if (!fill && coop_segs[gi] > 0) {
+        clear.p[1] = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * kCoopLaunches * gi;
+        clear.n[1] = (long long)kFusedStatusWords * coop_nl[gi];  // the status lines of the launches made
+        clear.p[2] = (unsigned*)(ws + p.off_coop) + (long long)kFusedStatusWords * kCoopLaunches * ngroups +
+                     (long long)b0 * p.heads * coop_row_words();
+        clear.n[2] = (long long)rows * coop_row_words();
+      }
+      if (!fill && b0 == 0) {
+        clear.p[3] = (unsigned*)ws;
+        clear.n[3] = 2;
+      }
+      e = timed("window_stats", st, [&] { return launch_window_stats(a, items, p.dtype, Q, K, pm, pz, clear, st); });
       if (e != hipSuccess) return device_error(e, "window_stats launch");
       e = timed("window_votes", st,
                 [&] { return launch_window_votes(a, items, p.dtype, Q, K, pm, pz, nullptr, votes, row_stats, st); });

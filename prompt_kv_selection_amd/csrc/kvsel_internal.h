@@ -60,6 +60,11 @@ struct Launch {
   int rounds;     // single-read scoring: rounds over all segments
   int seg_size;   // selection: positions per emit workgroup (multiple of 2048)
   unsigned* err;  // error flags of the call (the workspace header word), or nullptr
+  // With token != 0 the two-pass scoring kernels record their flags in the
+  // tagged header word errw instead (raise_flag), so that a launch of the
+  // call may clear word 0 for the kernels after it.
+  unsigned long long token;
+  unsigned long long* errw;
   int group;      // query heads per K/V head (grouped-query attention); 0 or 1: one each
   long long residency_ticks;  // wall-clock ticks of the residency bound (kResidencyMicros)
   Seg seg[kMaxSegs];
@@ -116,6 +121,20 @@ __device__ inline void raise_error(unsigned* err, unsigned bit) {
     __hip_atomic_fetch_or(err + kStickyWord, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+// A flag of a scoring kernel: the tagged word with a token, else word 0.
+__device__ inline void raise_flag(const Launch& a, unsigned bit) {
+  if (a.token != 0ull)
+    raise_tagged(a.errw, a.token, bit);
+  else
+    raise_error(a.err, bit);
+}
+// Ranges of 32-bit words a kernel clears for the kernels after it in the
+// call (empty ranges have n = 0).
+constexpr int kClearRanges = 4;
+struct WordRanges {
+  unsigned* p[kClearRanges];
+  long long n[kClearRanges];
+};
 // Debug builds (KVSEL_DEBUG defined) check every index that turns into a row
 // address (the K/V copies, the gather of caller indices) and record a
 // violation as kErrIndexRange in the call's flags, or, for entry points
@@ -169,11 +188,11 @@ __device__ __forceinline__ int find_seg(const Launch& a, int item) {
 enum { kFieldItem = 0, kFieldRow = 1, kFieldGather = 2 };
 
 // Host-side launchers (return hipSuccess or the launch error).
-// window_stats also zeroes zero_words words at zero (the selection's
-// histograms), which the kernels after it accumulate into.
+// window_stats also zeroes the words of clear (the selection's histograms
+// or the cooperative selection's words, and header word 0), which only the
+// kernels after it use.
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               float* part_m, float* part_z, uint32_t* zero, long long zero_words,
-                               hipStream_t st);
+                               float* part_m, float* part_z, const WordRanges& clear, hipStream_t st);
 // With lse != nullptr ([sequence][head][W] natural-log row log-sum-exps,
 // one per window row) the partials are not read and no row statistics are
 // written.

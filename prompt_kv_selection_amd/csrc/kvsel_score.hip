@@ -365,8 +365,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_stats_k
                                                                   const T* __restrict__ K,
                                                                   float* __restrict__ part_m,
                                                                   float* __restrict__ part_z,
-                                                                  uint32_t* __restrict__ zero,
-                                                                  long long zero_words) {
+                                                                  const WordRanges clear) {
   // Every multiply-add below is written out (fmaf) and nothing else is
   // fused, so the statistics do not depend on how the compiler schedules a
   // kernel variant: grouped heads match their expanded heads bit for bit.
@@ -387,10 +386,18 @@ __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_stats_k
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
 
-  // Side duty: clear the histograms of the selection that follows.
-  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < zero_words;
-       q += (long long)gridDim.x * blockDim.x)
-    zero[q] = 0u;
+  // Side duty: clear the words the kernels after this one use, 16 bytes a
+  // store where the range allows.
+  {
+    const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x, nt = (long long)gridDim.x * blockDim.x;
+#pragma unroll
+    for (int r = 0; r < kClearRanges; ++r) {
+      const bool wide = (reinterpret_cast<uintptr_t>(clear.p[r]) & 15) == 0;
+      const long long n4 = wide ? clear.n[r] / 4 : 0;
+      for (long long q = t0; q < n4; q += nt) reinterpret_cast<uint4*>(clear.p[r])[q] = make_uint4(0u, 0u, 0u, 0u);
+      for (long long q = 4 * n4 + t0; q < clear.n[r]; q += nt) clear.p[r][q] = 0u;
+    }
+  }
 
   Operands<T, D> qa[RB];
   // This lane's running statistics of the current run: row n of each row
@@ -555,7 +562,7 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
       mm = kNegBig;
       for (int grp = 0; grp < G; ++grp) lse_merge(mm, zz, s_gm[grp * W + t], s_gz[grp * W + t]);
       iz = 1.f / zz;
-      if (write_stats && !stats_ok(mm, zz)) raise_error(a.err, kErrNonFinite);
+      if (write_stats && !stats_ok(mm, zz)) raise_flag(a, kErrNonFinite);
       if (row_stats != nullptr && write_stats) {
         // row t of the slot: window row t % a.W of query head h * group + t / a.W
         float* rs = row_stats + (((long long)s.b * a.heads) * a.W + (long long)h * W + t) * 2;
@@ -620,7 +627,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_votes_k
           const int i = threadIdx.x;  // window row i % W of query head it.h * Gq + i / W
           const bool row = i < R;
           const float l = row ? lse[((long long)s.b * a.heads) * W + (long long)it.h * R + i] : 0.f;
-          if (row && it.c == 0 && !isfinite(l)) raise_error(a.err, kErrNonFinite);
+          if (row && it.c == 0 && !isfinite(l)) raise_flag(a, kErrNonFinite);
           s_m[i] = l * kLog2e;
           s_iz[i] = row ? 1.f : 0.f;
         }
@@ -712,11 +719,11 @@ static int resident_grid(Kern kern, int threads, int items) {
 
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
-                          uint32_t* zero, long long zero_words, hipStream_t st) {
+                          const WordRanges& clear, hipStream_t st) {
   constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
   const int grid = resident_grid(window_stats_kernel<T, D, RB>, threads, items);
   hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(threads), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, zero, zero_words);
+                     (const T*)Q, (const T*)K, pm, pz, clear);
   return hipGetLastError();
 }
 
@@ -758,9 +765,8 @@ static hipError_t votes_t(const Launch& a, int items, const void* Q, const void*
   } while (0)
 
 hipError_t launch_window_stats(const Launch& a, int items, int dtype, const void* Q, const void* K,
-                               float* part_m, float* part_z, uint32_t* zero, long long zero_words,
-                               hipStream_t st) {
-  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, zero, zero_words, st);
+                               float* part_m, float* part_z, const WordRanges& clear, hipStream_t st) {
+  KVSEL_DISPATCH(stats_t, a, items, Q, K, part_m, part_z, clear, st);
 }
 
 hipError_t launch_window_votes(const Launch& a, int items, int dtype, const void* Q, const void* K,

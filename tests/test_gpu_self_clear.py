@@ -1,6 +1,8 @@
 """Calls that launch no fill: single-read scoring followed by the
 cooperative or split selection clears its own shared words (exchange slots,
 the cooperative selection's words, header word 0) inside the scoring
+kernel, and two-pass scoring clears the words of any selection (with the
+histograms of the whole-row and segment selections) in its statistics
 kernel.  A workspace holding any bytes, or the previous call's words, must
 give the same outputs, bit for bit, as a zeroed one, on the residency path
 and on the forced fallback, and report only the call's own flags."""
@@ -24,10 +26,10 @@ def B():
     return binding
 
 
-def run(B, w, arrs, ws, select, fallback=False):
+def run(B, w, arrs, ws, select, fallback=False, scoring="single_read"):
     Q, K, V = arrs
     H, L, D = K.shape
-    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING["single_read"])
+    B.kvsel_set_option(B.KVSEL_OPT_SCORING, B.SCORING[scoring])
     B.kvsel_set_option(B.KVSEL_OPT_SELECT, SELECT[select])
     B.kvsel_set_option(B.KVSEL_OPT_FORCE_FALLBACK, 1 if fallback else 0)
     try:
@@ -59,32 +61,37 @@ def same(a, b, what):
 
 
 CASES = [
-    # (select, heads, L, C, expected selection path)
-    ("auto", 8, 20000, 1024, "select_coop"),
-    ("exchange", 40, 70000, 2000, "select_coop"),   # several cooperative launches
-    ("split", 8, 20000, 1024, "select_split"),
+    # (scoring, select, heads, L, C, pooling width, expected selection path)
+    ("single_read", "auto", 8, 20000, 1024, 5, "select_coop"),
+    ("single_read", "exchange", 40, 70000, 2000, 5, "select_coop"),   # several cooperative launches
+    ("single_read", "split", 8, 20000, 1024, 5, "select_split"),
+    ("two_pass", "auto", 8, 20000, 1024, 5, "select_coop"),
+    ("two_pass", "exchange", 40, 70000, 2000, 3, "select_coop"),
+    ("two_pass", "split", 8, 20000, 1024, 7, "select_split"),
+    ("two_pass", "auto", 6, 20000, 1024, 9, "select_rows"),            # width 9: the whole-row selection
+    ("two_pass", "auto", 3, 50000, 2048, 9, "select_segments"),       # and the segment chain
 ]
 
 
 @pytest.mark.parametrize("fallback", [False, True], ids=["resident", "forced_fallback"])
-@pytest.mark.parametrize("select,H,L,C,path", CASES)
-def test_garbage_workspace_matches_zeroed(B, select, H, L, C, path, fallback):
-    w = WL.Workload("self_clear", seed=H + L, heads=H, L=L, W=32, C=C, D=128, dtype="bf16", kernel=5,
+@pytest.mark.parametrize("scoring,select,H,L,C,kernel,path", CASES)
+def test_garbage_workspace_matches_zeroed(B, scoring, select, H, L, C, kernel, path, fallback):
+    w = WL.Workload("self_clear", seed=H + L, heads=H, L=L, W=32, C=C, D=128, dtype="bf16", kernel=kernel,
                     pooling="avg", keys="spike", spike_frac=0.01)
     Q, K, V = WL.layer_arrays(w)
     arrs = (to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"))
     nbytes = B.kvsel_workspace_bytes(H, L, w.W, C, w.D, torch.bfloat16)
-    log(f"self-clear: select={select} H={H} L={L} C={C} fallback={fallback}: zeroed workspace")
-    ref = run(B, w, arrs, torch.zeros(nbytes, dtype=torch.uint8, device="cuda"), select, fallback)
+    log(f"self-clear: {scoring} select={select} H={H} L={L} C={C} k={kernel} fallback={fallback}: zeroed workspace")
+    ref = run(B, w, arrs, torch.zeros(nbytes, dtype=torch.uint8, device="cuda"), select, fallback, scoring)
     assert ref["rc"] == B.KVSEL_OK, B.kvsel_last_error()
-    assert path in ref["path"] and "single_read" in ref["path"], ref["path"]
+    assert path in ref["path"] and scoring in ref["path"], ref["path"]
     assert "fill" not in ref["launches"], f"a fill was launched: {ref['launches']}"
-    assert ("scoring_fallback" in ref["flags"]) == fallback, ref["flags"]
+    assert ("scoring_fallback" in ref["flags"]) == (fallback and scoring == "single_read"), ref["flags"]
     for pattern in (0xAB, 0xFF):
         log(f"self-clear: workspace filled with {pattern:#x}, then the same workspace again")
         ws = torch.full((nbytes,), pattern, dtype=torch.uint8, device="cuda")
         for rep in range(2):
-            out = run(B, w, arrs, ws, select, fallback)
+            out = run(B, w, arrs, ws, select, fallback, scoring)
             assert out["rc"] == B.KVSEL_OK, (pattern, rep, B.kvsel_last_error())
             assert out["flags"] == ref["flags"], (pattern, rep, out["flags"], ref["flags"])
             same(out, ref, f"pattern {pattern:#x} call {rep}")
@@ -110,12 +117,13 @@ def test_stale_error_flags_do_not_carry_over(B):
     bad = (good[0], to_device(K2, "bf16"), good[2])
     nbytes = B.kvsel_workspace_bytes(w.heads, w.L, w.W, w.C, w.D, torch.bfloat16)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    for select in ("auto", "split"):
-        log(f"stale flags: NaN key, select={select}")
-        out = run(B, w, bad, ws, select)
-        assert out["rc"] == B.KVSEL_ENONFINITE, (select, B.kvsel_last_error())
-        assert "fill" not in out["launches"], out["launches"]
-        log(f"stale flags: clean call on the same workspace, select={select}")
-        out = run(B, w, good, ws, select)
-        assert out["rc"] == B.KVSEL_OK, (select, B.kvsel_last_error())
-        assert out["flags"] == [], out["flags"]
+    for scoring in ("single_read", "two_pass"):
+        for select in ("auto", "split"):
+            log(f"stale flags: NaN key, {scoring}, select={select}")
+            out = run(B, w, bad, ws, select, scoring=scoring)
+            assert out["rc"] == B.KVSEL_ENONFINITE, (scoring, select, B.kvsel_last_error())
+            assert "fill" not in out["launches"], out["launches"]
+            log(f"stale flags: clean call on the same workspace, {scoring}, select={select}")
+            out = run(B, w, good, ws, select, scoring=scoring)
+            assert out["rc"] == B.KVSEL_OK, (scoring, select, B.kvsel_last_error())
+            assert out["flags"] == [], out["flags"]
