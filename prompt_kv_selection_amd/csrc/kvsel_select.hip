@@ -1007,22 +1007,24 @@ __device__ void coop_read_candidates(const unsigned long long* cnt, int nseg, co
 }
 
 // Copy output rows m0 .. m0 + n of K and V from source rows first + i
-// (sel == nullptr) or sel[i] (LDS), RU 16-byte pieces per row, consecutive
-// threads on consecutive pieces, four pieces of each in flight per thread.
-// Source rows are clamped into the head's L rows: never a read outside them.
+// (sel == nullptr) or sel[i] (LDS), then output rows m1 .. m1 + n1 from
+// source rows first1 + i, in one pass (one round of loads where both fit):
+// RU 16-byte pieces per row, consecutive threads on consecutive pieces, kFly
+// pieces of each in flight per thread.  Source rows are clamped into the
+// head's L rows: never a read outside them.
 template <int RU, int NT = kCoopThreads, int kFly = 4>
-__device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const int32_t* sel, int L, long long in_row0,
-                                               long long out_row0, const uint4* __restrict__ K,
-                                               const uint4* __restrict__ V, uint4* __restrict__ Ko,
-                                               uint4* __restrict__ Vo) {
-  const int total = n * RU, tid = threadIdx.x;
+__device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const int32_t* sel, int m1, int n1,
+                                               int first1, int L, long long in_row0, long long out_row0,
+                                               const uint4* __restrict__ K, const uint4* __restrict__ V,
+                                               uint4* __restrict__ Ko, uint4* __restrict__ Vo) {
+  const int total = (n + n1) * RU, tid = threadIdx.x;
   for (int e0 = 0; e0 < total; e0 += kFly * NT) {
     uint4 kv[kFly], vv[kFly];
 #pragma unroll
     for (int f = 0; f < kFly; ++f) {
       const int e = min(e0 + f * NT + tid, total - 1);
       const int i = e / RU;
-      const int src = min(max(sel ? sel[i] : first + i, 0), L - 1);
+      const int src = min(max(i < n ? (sel ? sel[i] : first + i) : first1 + (i - n), 0), L - 1);
       const long long from = (in_row0 + src) * RU + e % RU;
       kv[f] = K[from];
       vv[f] = V[from];
@@ -1031,7 +1033,8 @@ __device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const i
     for (int f = 0; f < kFly; ++f) {
       const int e = e0 + f * NT + tid;
       if (e < total) {
-        const long long to = (out_row0 + m0 + e / RU) * RU + e % RU;
+        const int i = e / RU;
+        const long long to = (out_row0 + (i < n ? m0 + i : m1 + (i - n))) * RU + e % RU;
         Ko[to] = kv[f];
         Vo[to] = vv[f];
       }
@@ -1077,8 +1080,8 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
   const long long out_row0 = s.out_off + (long long)h * s.out_ld;
   // Output rows m0 .. m0 + n from source rows first + i (sel == nullptr)
   // or sel[i].
-  auto copy = [&](int m0, int n, int first, const int32_t* sel) {
-    coop_copy_rows<RU>(m0, n, first, sel, s.L, in_row0, out_row0, K, V, Ko, Vo);
+  auto copy = [&](int m0, int n, int first, const int32_t* sel, int m1 = 0, int n1 = 0, int first1 = 0) {
+    coop_copy_rows<RU>(m0, n, first, sel, m1, n1, first1, s.L, in_row0, out_row0, K, V, Ko, Vo);
   };
   if (s.L < s.C) {  // bypass: every position, segment by segment
     if (tid == 0) s_go = decide(status, arrived, a.err, kFlagSelectFallback, a.residency_ticks);
@@ -1370,12 +1373,13 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
       }
     __syncthreads();
     KVSEL_SELROWS_MARK(6);
-    if (RU > 0) copy((int)before, (int)min(ntot, before < (uint32_t)count ? (uint32_t)count - before : 0u), 0, picks);
-    if (W > 0) {  // the window follows the picks: each segment writes and copies a share of its rows
-      const int w0 = (int)((long long)g * W / nseg), w1 = (int)((long long)(g + 1) * W / nseg);
-      for (int i = w0 + tid; i < w1; i += kCoopThreads) out[count + i] = P + i;
-      if (RU > 0 && w1 > w0) copy(count + w0, w1 - w0, P + w0, nullptr);
-    }
+    // The window follows the picks: each segment writes and copies a share
+    // of its rows, in the same pass as its picks' rows.
+    const int w0 = (int)((long long)g * W / nseg), w1 = (int)((long long)(g + 1) * W / nseg);
+    for (int i = w0 + tid; i < w1; i += kCoopThreads) out[count + i] = P + i;
+    if (RU > 0)
+      copy((int)before, (int)min(ntot, before < (uint32_t)count ? (uint32_t)count - before : 0u), 0, picks, count + w0,
+           w1 - w0, P + w0);
     __syncthreads();  // picks[] is rewritten by the next segment
   }
   KVSEL_SELROWS_MARK(13);
@@ -1583,8 +1587,9 @@ __global__ __launch_bounds__(NT) void select_split_kernel(const Launch a, int ro
   // RU == 0: indices only (no K/V rows; a.D may be 0).
   const long long in_row0 = RU > 0 ? s.kv_off / a.D + (long long)kv_head(a, h) * s.L : 0;
   const long long out_row0 = RU > 0 ? s.out_off + (long long)h * s.out_ld : 0;
-  auto copy = [&](int m0, int n, int first, const int32_t* sel) {
-    if constexpr (RU > 0) coop_copy_rows<RU, NT, 8>(m0, n, first, sel, s.L, in_row0, out_row0, K, V, Ko, Vo);
+  auto copy = [&](int m0, int n, int first, const int32_t* sel, int m1 = 0, int n1 = 0, int first1 = 0) {
+    if constexpr (RU > 0)
+      coop_copy_rows<RU, NT, 8>(m0, n, first, sel, m1, n1, first1, s.L, in_row0, out_row0, K, V, Ko, Vo);
   };
   if (s.L < s.C) {  // bypass: every position; this split's share of them
     const int m0 = (int)((long long)sp * s.L / splits), m1 = (int)((long long)(sp + 1) * s.L / splits);
@@ -1802,8 +1807,7 @@ __global__ __launch_bounds__(NT) void select_split_kernel(const Launch a, int ro
   for (int i = w0 + tid; i < w1; i += NT) out[count + i] = P + i;
   __syncthreads();  // the list is complete
   KVSEL_SELROWS_MARK(7);
-  if (s1 > s0) copy(s0, s1 - s0, 0, list);
-  if (w1 > w0) copy(count + w0, w1 - w0, P + w0, nullptr);
+  copy(s0, max(0, s1 - s0), 0, list, count + w0, w1 - w0, P + w0);  // the picks and the window in one pass
   KVSEL_SELROWS_MARK(8);
 }
 
