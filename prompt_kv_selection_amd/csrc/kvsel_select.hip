@@ -1347,6 +1347,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
     }
     uint32_t tot;
     const uint32_t excl = block_scan<kCoopThreads>(gt | (eq << 16), sh, tot) - (gt | (eq << 16));
+    KVSEL_SELROWS_MARK(7);
     const uint32_t gtb = excl & 0xFFFFu, eqb = excl >> 16;
     const uint32_t left = need_eq > eq_before ? need_eq - eq_before : 0u;
     uint32_t pm = 0, seen = eqb;
@@ -1371,6 +1372,7 @@ __global__ __launch_bounds__(kCoopThreads) void select_coop_kernel(
         if (before + off < (uint32_t)count) out[before + off] = j;
         picks[off++] = j;
       }
+    KVSEL_SELROWS_MARK(8);
     __syncthreads();
     KVSEL_SELROWS_MARK(6);
     // The window follows the picks: each segment writes and copies a share
