@@ -611,6 +611,7 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       sel.kslot = (float*)(ws + p.off_kslot);
       sel.clr[0] = lse == nullptr ? (unsigned long long*)(ws + p.off_ctr) : nullptr;
       sel.clr_words[0] = lse == nullptr ? (long long)(p.off_hist - p.off_ctr) / 8 : 0;
+      sel.clr_early = 1;  // the exchange slots; the rest only later kernels read
       if (!fill && coop_segs[gi] > 0) {
         // The cooperative selection's status blocks and row words of this
         // group, which its launches after this one need at zero.
@@ -631,10 +632,11 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
       sel.halo = (unsigned long long*)(ws + p.off_halo);
       sel.cslot = (unsigned*)(ws + p.off_cslot);
       sel.fslot = (unsigned*)(ws + p.off_fslot);
-      // Also cleared by the kernel's workgroups: the count, halo and
-      // histogram words (contiguous).
+      // Also cleared by the kernel's workgroups before they arrive: the
+      // count, halo and histogram words (contiguous).
       sel.clr[1] = (unsigned long long*)(ws + p.off_cw);
       sel.clr_words[1] = (long long)(p.off_flags - p.off_cw) / 8;
+      sel.clr_early = 2;
       sel.cand = (unsigned long long*)(ws + p.off_cand);
       sel.pooled = pooled_opt;
       sel.indices = indices;

@@ -856,17 +856,20 @@ __device__ __forceinline__ SelRound sel_round(const Launch& a, int r) {
   return q;
 }
 
-// Exchange wave, at kernel start, before any other load of the workgroup is
-// issued: clear this workgroup's share of the words the call's workgroups
-// publish to each other (exchange, count, halo and histogram slots) and of
-// the words later kernels of the call need at zero.  The arrival follows once
-// the stores are done, so GO means every word is clear; nothing is published
-// before GO.  Words only later kernels read are clear once the launch ends.
-__device__ __forceinline__ void sel_clear(const FusedSel& f) {
+// Exchange wave: clear this workgroup's share of ranges r0 .. r1 - 1 of
+// f.clr.  At kernel start, before any other load of the workgroup is issued,
+// the words the call's workgroups publish to each other (exchange, count,
+// halo and histogram slots: the first f.clr_early ranges); the arrival
+// follows once those stores are done, so GO means every such word is clear,
+// and nothing is published before GO.  Right after the arrival, the words
+// only later kernels of the call read (clear once the launch ends), so that
+// they do not delay the arrival.
+__device__ __forceinline__ void sel_clear(const FusedSel& f, int r0, int r1) {
   const int lane = threadIdx.x & 63;
   const long long nwg = gridDim.x;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    if (r < r0 || r >= r1) continue;
     const long long n = f.clr_words[r];
     const long long per = (n + nwg - 1) / nwg;
     const long long lo = per * blockIdx.x, hi = min(n, lo + per);
@@ -1910,7 +1913,7 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
   // the first K tiles and Qwin of rounds 0 and 1.
   if (wave == kExWave) {
     KVSEL_FUSED_MARK(22, 0);
-    sel_clear(f);
+    sel_clear(f, 0, f.clr_early);
     KVSEL_FUSED_MARK(22, 1);
     lds_set(&sy.issued, 1u);
   } else if (wave < kSW || wave == kMemWave) {
@@ -1927,8 +1930,10 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
   }
   if (wave == kExWave) {
     if constexpr (kHandshake) {
-      // Arrive once the clears are done, decide; then the statistics.
+      // Arrive once the clears are done, clear the words later kernels
+      // use, decide; then the statistics.
       sel_arrive(f);
+      sel_clear(f, f.clr_early, 4);
       KVSEL_FUSED_MARK(22, 2);
       KVSEL_FUSED_MARK(23, 4);
       const unsigned d = sel_decide(a, f);
@@ -1943,6 +1948,7 @@ __global__ __launch_bounds__(kSel ? kThreads : kThreadsPlain, 1) void window_fus
       else
         ctl_exchange<D>(a, f, ex, row_stats, s_m, &sy);
     } else {
+      sel_clear(f, f.clr_early, 4);
       ctl_lse(a, f, lse, s_m, &sy);  // no workgroup waits for another
     }
   } else if (wave == kMemWave) {

@@ -370,6 +370,7 @@ struct FusedSel {
   unsigned long long* halo;     // [exchange slot][kHaloWords]
   unsigned long long* clr[4];   // ranges of 8-byte words the launch clears (a share per workgroup), or nullptr
   long long clr_words[4];
+  int clr_early;                // the first clr_early ranges are published words: cleared before the arrival
   unsigned* cslot;              // [exchange slot][64] the chunk's coarse histogram, count + 1
   unsigned* fslot;              // [exchange slot][32] its fine histogram inside the coarse bin of tau, count + 1
   unsigned long long* rowfb;    // [row][2] fallback completion counters (token-tagged)
