@@ -14,7 +14,7 @@ import torch
 from oracle import snapkv_oracle as O
 from prompt_kv_selection_amd import workloads as WL
 
-from parity import SELECT, band_check, bits, close, log, to_device
+from parity import SELECT, band_check, bits, close, log, run_select, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,61 @@ def test_stale_error_flags_do_not_carry_over(B):
             out = run(B, w, good, ws, select, scoring=scoring)
             assert out["rc"] == B.KVSEL_OK, (scoring, select, B.kvsel_last_error())
             assert out["flags"] == [], out["flags"]
+
+
+@pytest.mark.parametrize("select", ["auto", "split"])
+def test_many_sequences_on_a_garbage_workspace(B, select):
+    """A ragged batch of 20 sequences runs as two launch groups (up to 16
+    sequences each): each group's scoring kernel clears its own words, and
+    only the first clears header word 0.  A workspace of 0xAB bytes, used
+    twice, gives what per-sequence calls on zeroed workspaces give."""
+    w = WL.reduced(WL.get("ragged_b8_h32_l4k_64k"), heads=2, batch=20, L_min=1500, L_max=6000)
+    Q, K, V, Ls, Cs, cu = WL.ragged_arrays(w)
+    Ls, Cs = list(Ls), list(Cs)
+    assert all(L >= C for L, C in zip(Ls, Cs))
+    H, W, D = w.heads, w.W, w.D
+    Qd, Kd, Vd = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    cuC = np.concatenate([[0], np.cumsum(Cs)])
+    nbytes = B.kvsel_varlen_workspace_bytes(cu.tolist(), Cs, H, W, D, torch.bfloat16)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    B.kvsel_set_option(B.KVSEL_OPT_SELECT, SELECT[select])
+    try:
+        outs = []
+        for rep in range(2):
+            log(f"many sequences: select={select} call {rep}")
+            idx = torch.full((H * int(cuC[-1]),), -1, dtype=torch.int32, device="cuda")
+            Ko = torch.zeros((H * int(cuC[-1]), D), dtype=torch.bfloat16, device="cuda")
+            Vo = torch.zeros_like(Ko)
+            torch.cuda.synchronize()
+            B.kvsel_profile_enable(True)
+            B.kvsel_select_varlen(Qd, Kd, Vd, cu.tolist(), Cs, W, D, H, w.kernel, w.pooling, torch.bfloat16, idx, Ko,
+                                  Vo, None, None, None, ws)
+            torch.cuda.synchronize()
+            launches = B.kvsel_profile_read()
+            B.kvsel_profile_enable(False)
+            assert B.kvsel_status(ws) == B.KVSEL_OK, B.kvsel_last_error()
+            assert "fill" not in launches, launches
+            outs.append((idx.cpu().numpy(), bits(Ko).cpu(), bits(Vo).cpu()))
+    finally:
+        B.kvsel_set_option(B.KVSEL_OPT_SELECT, 0)
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
+    idx, Ko, Vo = outs[0]
+    for b in (0, 7, 15, 16, 19):  # both groups
+        L, C = Ls[b], Cs[b]
+        k = Kd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D).contiguous()
+        v = Vd[H * int(cu[b]) * D: H * int(cu[b + 1]) * D].view(H, L, D).contiguous()
+        single = run_select(Qd[b].contiguous(), k, v, L, W, C, w.kernel, w.pooling, "bf16", select=select)
+        got = idx[H * int(cuC[b]): H * int(cuC[b + 1])].reshape(H, C)
+        np.testing.assert_array_equal(got, single["idx"].cpu().numpy(), err_msg=f"sequence {b}")
+        got_k = Ko[H * int(cuC[b]): H * int(cuC[b + 1])].reshape(H, C, D)
+        assert torch.equal(got_k, bits(single["Ko"]).cpu()), f"sequence {b} K_out"
+    # One sequence's head against the oracle.
+    b, h = 16, 1
+    q1, k1, v1 = WL.head_arrays(w, h, seq=b)
+    ref = O.snapkv_select(WL.to_float64(q1, "bf16"), WL.to_float64(k1, "bf16"), WL.to_float64(v1, "bf16"), W, Cs[b],
+                          w.kernel, w.pooling)
+    n = Cs[b] - W
+    got = idx[H * int(cuC[b]): H * int(cuC[b + 1])].reshape(H, Cs[b])[h]
+    band_check(got[:n], ref["pooled"], n, f"sequence {b} head {h}")
+    np.testing.assert_array_equal(got[n:], np.arange(Ls[b] - W, Ls[b]))
