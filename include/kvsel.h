@@ -254,7 +254,12 @@ size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype);
  *   votes_opt, pooled_opt  out [heads][L-W] float32 votes / pooled scores, or
  *            NULL.  Not written for L < C.
  *   workspace, workspace_bytes  device scratch of at least
- *            kvsel_workspace_bytes(...) bytes, 256-byte aligned.
+ *            kvsel_workspace_bytes(...) bytes, 256-byte aligned.  Its
+ *            contents on entry do not matter: the call clears what it needs
+ *            at zero, in its first kernel or, for some shapes (a sequence
+ *            shorter than its budget, handed-over statistics on the two-pass
+ *            path, the validating mode), in a fill launch before it.  Calls
+ *            that share a workspace must be ordered (one stream).
  */
 int kvsel_select(const void* Qwin, const void* K, const void* V,
                  int L, int W, int C, int D, int heads,
