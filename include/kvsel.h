@@ -256,10 +256,11 @@ size_t kvsel_workspace_bytes(int heads, int L, int W, int C, int D, int dtype);
  *   workspace, workspace_bytes  device scratch of at least
  *            kvsel_workspace_bytes(...) bytes, 256-byte aligned.  Its
  *            contents on entry do not matter: the call clears what it needs
- *            at zero, in its first kernel or, for some shapes (a sequence
+ *            at zero, in its first kernel or, for some calls (a sequence
  *            shorter than its budget, handed-over statistics on the two-pass
- *            path, the validating mode), in a fill launch before it.  Calls
- *            that share a workspace must be ordered (one stream).
+ *            path, single-read scoring with a pooling width above 7, the
+ *            validating mode), in a fill launch before it.  Calls that share
+ *            a workspace must be ordered (one stream).
  */
 int kvsel_select(const void* Qwin, const void* K, const void* V,
                  int L, int W, int C, int D, int heads,
