@@ -1314,8 +1314,8 @@ __device__ __forceinline__ void wave_copy_rows(const uint4* __restrict__ Ki, con
       const int e = e0 + t * 64 + lane;
       if (e < total) {
         const long long to = (out_row0 + e / RU) * RU + e % RU;
-        Ko[to] = kv[t];
-        Vo[to] = vv[t];
+        store_stream(Ko + to, kv[t]);
+        store_stream(Vo + to, vv[t]);
       }
     }
   }
@@ -1727,8 +1727,8 @@ __device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f
     const int n = (int)min(take_tot, (uint32_t)count > before ? (uint32_t)count - before : 0u);
     for (int q = tid; q < n * RU; q += kThreads) {
       const long long from = (in_row0 + list[q / RU]) * RU + q % RU, to = (out_row0 + before + q / RU) * RU + q % RU;
-      Ko[to] = Ki[from];
-      Vo[to] = Vi[from];
+      store_stream(Ko + to, Ki[from]);
+      store_stream(Vo + to, Vi[from]);
     }
     before += take_tot;
     eq_seen += eq_tot;
@@ -1737,8 +1737,8 @@ __device__ __forceinline__ void fb_select_row(const Launch& a, const FusedSel& f
   for (int i = tid; i < a.W; i += kThreads) out[count + i] = P + i;
   for (int q = tid; q < a.W * RU; q += kThreads) {
     const long long from = (in_row0 + P + q / RU) * RU + q % RU, to = (out_row0 + count + q / RU) * RU + q % RU;
-    Ko[to] = Ki[from];
-    Vo[to] = Vi[from];
+    store_stream(Ko + to, Ki[from]);
+    store_stream(Vo + to, Vi[from]);
   }
   (void)lane;
 }

@@ -128,6 +128,15 @@ __device__ inline void raise_flag(const Launch& a, unsigned bit) {
   else
     raise_error(a.err, bit);
 }
+// A 16-byte store of an output nothing in the call reads back (the kept K
+// and V rows): non-temporal, so it does not fill the L2 with dirty lines
+// that the kernel's end, or the next call's K stream, would have to write
+// back.
+typedef unsigned kvsel_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
+  const kvsel_u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<kvsel_u32x4*>(p));
+}
 // Ranges of 32-bit words a kernel clears for the kernels after it in the
 // call (empty ranges have n = 0).
 constexpr int kClearRanges = 4;

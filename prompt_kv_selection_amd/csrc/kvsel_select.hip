@@ -354,8 +354,8 @@ __device__ __forceinline__ void emit_rows(int n, int dst0, const int32_t* src, i
         const int e = e0 + f * kEmitThreads + (int)threadIdx.x;
         if (e < total) {
           const long long to = (out_row0 + dst0 + e / RU) * RU + e % RU;
-          Ko[to] = kv[f];
-          Vo[to] = vv[f];
+          store_stream(Ko + to, kv[f]);
+          store_stream(Vo + to, vv[f]);
         }
       }
     }
@@ -622,8 +622,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const Launch a, const uint4
   const long long out_row = s.out_off + (long long)h * s.out_ld + m;
   const uint4 kv = K[in_row * RU + part];
   const uint4 vv = V[in_row * RU + part];
-  Ko[out_row * RU + part] = kv;
-  Vo[out_row * RU + part] = vv;
+  store_stream(Ko + out_row * RU + part, kv);
+  store_stream(Vo + out_row * RU + part, vv);
 }
 
 hipError_t launch_pool(const Launch& a, int rows, int max_n, const float* votes, float* pooled, uint32_t* hist,
@@ -1035,8 +1035,8 @@ __device__ __forceinline__ void coop_copy_rows(int m0, int n, int first, const i
       if (e < total) {
         const int i = e / RU;
         const long long to = (out_row0 + (i < n ? m0 + i : m1 + (i - n))) * RU + e % RU;
-        Ko[to] = kv[f];
-        Vo[to] = vv[f];
+        store_stream(Ko + to, kv[f]);
+        store_stream(Vo + to, vv[f]);
       }
     }
   }
