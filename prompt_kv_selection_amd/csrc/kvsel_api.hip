@@ -107,6 +107,15 @@ struct Plan {
 // of the last selection call (kvsel_status).
 constexpr size_t kHeaderBytes = 256;
 
+// K bytes of a launch group above which its tiles are loaded
+// non-temporally: beyond about this much the last-level cache (256 MiB)
+// keeps little of K for a later read (the two-pass votes pass, the
+// selection's copy of the kept rows, the same call repeated), and cached
+// lines only evict what is still useful.  Measured: a 268 MB layer is
+// faster with non-temporal loads on either scoring path, a 67 MB grouped
+// layer and a 134 MB layer are slower.
+constexpr double kTwoPassCachedBytes = 192.0 * 1024 * 1024;
+
 // Cooperative-selection launches per launch group at most: rows whose grid
 // does not fit the device at once are selected a subset at a time, each
 // launch with its own status block.
@@ -554,6 +563,14 @@ int run_select(const void* Q, const void* K, const void* V, const float* lse, co
     a.err = err;
     a.token = token;
     a.errw = (unsigned long long*)(ws + 4 * kTaggedWord);
+    {
+      // K tiles bypass the caches when the group's K is larger than the
+      // last-level cache could keep for a later read.
+      long long kv_rows = 0;
+      for (int b = b0; b < b0 + nb; ++b) kv_rows += (long long)(p.heads / p.group) * p.L[b];
+      const double k_bytes = (double)kv_rows * p.D * (p.dtype == KVSEL_BF16 ? 2 : 4);
+      a.k_nt = k_bytes > kTwoPassCachedBytes ? 1 : 0;
+    }
     a.n = nb;
     a.S = p.fS;
     a.rounds = 0;

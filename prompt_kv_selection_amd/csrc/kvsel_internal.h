@@ -65,6 +65,10 @@ struct Launch {
   // call may clear word 0 for the kernels after it.
   unsigned long long token;
   unsigned long long* errw;
+  // 1: the two-pass kernels load K tiles non-temporally (a call whose K is
+  // larger than the last-level cache keeps none of it for the second pass
+  // anyway, and cached lines would only evict what is still useful).
+  int k_nt;
   int group;      // query heads per K/V head (grouped-query attention); 0 or 1: one each
   long long residency_ticks;  // wall-clock ticks of the residency bound (kResidencyMicros)
   Seg seg[kMaxSegs];

@@ -88,18 +88,25 @@ struct TileOffsets {
 
 // Load the `rows` (1..32) rows starting at `first` as one tile; rows past
 // `rows` repeat the last row (read, never used).
+// With nt the loads are non-temporal (wave-uniform choice).
 template <typename T, int D>
 __device__ __forceinline__ void issue_tile(const T* first, int rows, const TileOffsets<T, D>& off,
-                                           const uint4* lds_tile, int lane) {
+                                           const uint4* lds_tile, int lane, bool nt) {
   using G = TileGeom<T, D>;
   const unsigned base = (unsigned)(uintptr_t)lds_tile;
 #pragma unroll
   for (int i = 0; i < G::NL; ++i) {
     const unsigned o = rows >= 32 ? off.v[i] : TileOffsets<T, D>::piece_offset(i, lane, rows);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(o), "s"(first)
-                 : "memory", "m0");
+    if (nt)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(o), "s"(first)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(o), "s"(first)
+                   : "memory", "m0");
   }
 }
 
@@ -204,7 +211,7 @@ __device__ __forceinline__ void issue_queries(const Launch& a, const Seg& s, int
   if (wave < RB) {  // the group's query heads are consecutive: one block of group_rows rows
     const long long qh = (long long)s.b * a.heads + (long long)h * (a.group > 1 ? a.group : 1);
     const T* q = Q + qh * (long long)a.W * D + (long long)wave * 32 * D;
-    issue_tile<T, D>(q, min(32, group_rows(a) - wave * 32), off, qt[wave], lane);
+    issue_tile<T, D>(q, min(32, group_rows(a) - wave * 32), off, qt[wave], lane, false);
   }
 }
 
@@ -306,7 +313,7 @@ struct WaveStream {
     }
     if (item >= hi) return;
     const int p0 = cur.pb + t * 32;
-    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % RING], lane);
+    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % RING], lane, a.k_nt != 0);
     ++t;
     ++issued;
   }
