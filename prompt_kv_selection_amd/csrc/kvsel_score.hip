@@ -88,16 +88,16 @@ struct TileOffsets {
 
 // Load the `rows` (1..32) rows starting at `first` as one tile; rows past
 // `rows` repeat the last row (read, never used).
-// With nt the loads are non-temporal (wave-uniform choice).
-template <typename T, int D>
+// With kNT the loads are non-temporal.
+template <typename T, int D, bool kNT>
 __device__ __forceinline__ void issue_tile(const T* first, int rows, const TileOffsets<T, D>& off,
-                                           const uint4* lds_tile, int lane, bool nt) {
+                                           const uint4* lds_tile, int lane) {
   using G = TileGeom<T, D>;
   const unsigned base = (unsigned)(uintptr_t)lds_tile;
 #pragma unroll
   for (int i = 0; i < G::NL; ++i) {
     const unsigned o = rows >= 32 ? off.v[i] : TileOffsets<T, D>::piece_offset(i, lane, rows);
-    if (nt)
+    if constexpr (kNT)
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                    :
                    : "s"(__builtin_amdgcn_readfirstlane(base + i * 1024)), "v"(o), "s"(first)
@@ -211,7 +211,7 @@ __device__ __forceinline__ void issue_queries(const Launch& a, const Seg& s, int
   if (wave < RB) {  // the group's query heads are consecutive: one block of group_rows rows
     const long long qh = (long long)s.b * a.heads + (long long)h * (a.group > 1 ? a.group : 1);
     const T* q = Q + qh * (long long)a.W * D + (long long)wave * 32 * D;
-    issue_tile<T, D>(q, min(32, group_rows(a) - wave * 32), off, qt[wave], lane, false);
+    issue_tile<T, D, false>(q, min(32, group_rows(a) - wave * 32), off, qt[wave], lane);
   }
 }
 
@@ -287,7 +287,7 @@ __device__ __forceinline__ void item_range(int items, int& lo, int& hi) {
 // The K tile stream of one wave over all items of its workgroup's range:
 // tile loads run up to RING tiles ahead of the consumer, across item
 // boundaries; buffer = tile count % RING.
-template <typename T, int D, bool kVotes, int WT, int RING>
+template <typename T, int D, bool kVotes, int WT, int RING, bool kNT>
 struct WaveStream {
   using G = TileGeom<T, D>;
   uint4 (*ring)[G::PIECES];
@@ -313,7 +313,7 @@ struct WaveStream {
     }
     if (item >= hi) return;
     const int p0 = cur.pb + t * 32;
-    issue_tile<T, D>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % RING], lane, a.k_nt != 0);
+    issue_tile<T, D, kNT>(cur.kh + (long long)p0 * D, min(32, cur.L - p0), off, ring[issued % RING], lane);
     ++t;
     ++issued;
   }
@@ -366,7 +366,7 @@ __device__ __forceinline__ Operands<T, D> query_block(const Launch& a, const uin
 // the visible logits and sum of exp2(x - max) are written to the slot of its
 // last chunk, and the other chunks of the run get (kNegBig, 0), which leaves
 // any merge unchanged.
-template <typename T, int D, int RB>
+template <typename T, int D, int RB, bool kNT>
 __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_stats_kernel(const Launch a, int items,
                                                                   const T* __restrict__ Q,
                                                                   const T* __restrict__ K,
@@ -389,7 +389,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_stats_k
   item_range(items, lo, hi);
 
   KVSEL_SCORE_MARK(0, 0);
-  WaveStream<T, D, false, SG::WT, SG::RING> ws;
+  WaveStream<T, D, false, SG::WT, SG::RING, kNT> ws;
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
 
@@ -587,7 +587,7 @@ __device__ __forceinline__ void merge_partials(const Launch& a, const Seg& s, in
 // items; at each new head they merge its partial row statistics, then
 // recompute each chunk's logits and sum the softmax probabilities over the
 // window rows.
-template <typename T, int D, int RB>
+template <typename T, int D, int RB, bool kNT>
 __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_votes_kernel(
     const Launch a, int items, const T* __restrict__ Q, const T* __restrict__ K,
     const float* __restrict__ part_m, const float* __restrict__ part_z, const float* __restrict__ lse,
@@ -606,7 +606,7 @@ __global__ __launch_bounds__((ScoreGeom<T, D, RB>::NW * 64)) void window_votes_k
   item_range(items, lo, hi);
 
   KVSEL_SCORE_MARK(1, 0);
-  WaveStream<T, D, true, SG::WT, SG::RING> ws;
+  WaveStream<T, D, true, SG::WT, SG::RING, kNT> ws;
   ws.ring = ring[wave];
   ws.start(a, K, lo, hi, wave, lane);
 
@@ -724,23 +724,35 @@ static int resident_grid(Kern kern, int threads, int items) {
   return (int)(items < slots ? items : slots);
 }
 
+template <typename T, int D, int RB, bool kNT>
+static hipError_t stats_nt(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
+                           const WordRanges& clear, hipStream_t st) {
+  constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
+  const int grid = resident_grid(window_stats_kernel<T, D, RB, kNT>, threads, items);
+  hipLaunchKernelGGL((window_stats_kernel<T, D, RB, kNT>), dim3(grid), dim3(threads), 0, st, a, items,
+                     (const T*)Q, (const T*)K, pm, pz, clear);
+  return hipGetLastError();
+}
 template <typename T, int D, int RB>
 static hipError_t stats_t(const Launch& a, int items, const void* Q, const void* K, float* pm, float* pz,
                           const WordRanges& clear, hipStream_t st) {
-  constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
-  const int grid = resident_grid(window_stats_kernel<T, D, RB>, threads, items);
-  hipLaunchKernelGGL((window_stats_kernel<T, D, RB>), dim3(grid), dim3(threads), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, clear);
-  return hipGetLastError();
+  return a.k_nt ? stats_nt<T, D, RB, true>(a, items, Q, K, pm, pz, clear, st)
+                : stats_nt<T, D, RB, false>(a, items, Q, K, pm, pz, clear, st);
 }
 
 template <typename T, int D, int RB>
 static hipError_t votes_t(const Launch& a, int items, const void* Q, const void* K, const float* pm,
                           const float* pz, const float* lse, float* votes, float* rs, hipStream_t st) {
   constexpr int threads = ScoreGeom<T, D, RB>::NW * 64;
-  const int grid = resident_grid(window_votes_kernel<T, D, RB>, threads, items);
-  hipLaunchKernelGGL((window_votes_kernel<T, D, RB>), dim3(grid), dim3(threads), 0, st, a, items,
-                     (const T*)Q, (const T*)K, pm, pz, lse, votes, rs);
+  if (a.k_nt) {
+    const int grid = resident_grid(window_votes_kernel<T, D, RB, true>, threads, items);
+    hipLaunchKernelGGL((window_votes_kernel<T, D, RB, true>), dim3(grid), dim3(threads), 0, st, a, items,
+                       (const T*)Q, (const T*)K, pm, pz, lse, votes, rs);
+  } else {
+    const int grid = resident_grid(window_votes_kernel<T, D, RB, false>, threads, items);
+    hipLaunchKernelGGL((window_votes_kernel<T, D, RB, false>), dim3(grid), dim3(threads), 0, st, a, items,
+                       (const T*)Q, (const T*)K, pm, pz, lse, votes, rs);
+  }
   return hipGetLastError();
 }
 
