@@ -481,8 +481,10 @@ int kvsel_gather(const void* K, const void* V, const int32_t* indices, int ld_id
  * 8 waves, each with one 8 KiB tile of direct-to-LDS loads in flight (the
  * single-read scoring kernel's pattern); mode 1: the same with two tiles per
  * wave; mode 2: 4 waves with four tiles each; mode 3: 16-byte vector loads
- * into registers, grid-stride, four per lane in flight.  Modes 0-2 read whole
- * 128 KiB blocks (bytes a multiple of 131072).  Asynchronous on `stream`. */
+ * into registers, grid-stride, four per lane in flight; mode 4: mode 0 with
+ * non-temporal loads (the scoring kernels' loads of a K larger than the
+ * last-level cache).  Modes 0-2 and 4 read whole 128 KiB blocks (bytes a
+ * multiple of 131072).  Asynchronous on `stream`. */
 size_t kvsel_probe_sink_bytes(void);
 int kvsel_probe_stream(const void* src, size_t bytes, int mode, void* sink, size_t sink_bytes, void* stream);
 

@@ -921,9 +921,9 @@ size_t kvsel_probe_sink_bytes(void) {
 
 int kvsel_probe_stream(const void* src, size_t bytes, int mode, void* sink, size_t sink_bytes, void* stream) {
   if (!src || !sink) return fail(KVSEL_EINVAL, "src and sink must not be NULL");
-  if (mode < 0 || mode > 3) return fail(KVSEL_EINVAL, "probe mode must be 0..3 (got %d)", mode);
+  if (mode < 0 || mode > 4) return fail(KVSEL_EINVAL, "probe mode must be 0..4 (got %d)", mode);
   if ((uintptr_t)src % 16 || (uintptr_t)sink % 4) return fail(KVSEL_EINVAL, "src must be 16-byte aligned");
-  if (mode <= 2 && bytes % (128 * 1024) != 0)
+  if (mode != 3 && bytes % (128 * 1024) != 0)
     return fail(KVSEL_EINVAL, "tile probes read whole 128 KiB blocks (%zu bytes)", bytes);
   if (bytes % 16 != 0 || bytes == 0) return fail(KVSEL_EINVAL, "bytes must be a positive multiple of 16");
   int dev = 0, cus = 0;

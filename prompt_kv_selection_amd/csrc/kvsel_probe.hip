@@ -24,7 +24,7 @@ namespace {
 constexpr int kTileBytes = 8192;                 // 32 rows of 256 bytes
 constexpr int kBlockBytes = 128 * 1024;          // a workgroup's block per round
 
-template <int kWaves, int kDepth>
+template <int kWaves, int kDepth, bool kNT = false>
 __global__ __launch_bounds__(kWaves * 64, 1) void probe_tiles_kernel(const uint8_t* __restrict__ src,
                                                                      long long blocks, unsigned* __restrict__ sink) {
   constexpr int kTilesPerWave = kBlockBytes / kTileBytes / kWaves;
@@ -53,10 +53,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void probe_tiles_kernel(const uint8
 #pragma unroll
     for (int k = 0; k < kTileBytes / 1024; ++k) {
       const unsigned off = (unsigned)(k * 1024 + lane * 16);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(__builtin_amdgcn_readfirstlane(base + k * 1024)), "v"(off), "s"(first)
-                   : "memory", "m0");
+      if constexpr (kNT)  // non-temporal, as the scoring kernels load a K larger than the cache
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(base + k * 1024)), "v"(off), "s"(first)
+                     : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(base + k * 1024)), "v"(off), "s"(first)
+                     : "memory", "m0");
     }
   };
   long long issued = 0;
@@ -100,13 +106,15 @@ __global__ __launch_bounds__(256) void probe_vector_kernel(const uint4* __restri
 int probe_sink_words(int cus) { return cus * 8 * 256 / 64; }
 
 hipError_t launch_probe(int mode, const void* src, long long bytes, unsigned* sink, int cus, hipStream_t st) {
-  if (mode == 0 || mode == 1 || mode == 2) {
+  if (mode == 0 || mode == 1 || mode == 2 || mode == 4) {
     if (bytes % kBlockBytes != 0) return hipErrorInvalidValue;
     const long long blocks = bytes / kBlockBytes;
     const uint8_t* p = (const uint8_t*)src;
     if (mode == 0) hipLaunchKernelGGL((probe_tiles_kernel<8, 1>), dim3(cus), dim3(8 * 64), 0, st, p, blocks, sink);
     if (mode == 1) hipLaunchKernelGGL((probe_tiles_kernel<8, 2>), dim3(cus), dim3(8 * 64), 0, st, p, blocks, sink);
     if (mode == 2) hipLaunchKernelGGL((probe_tiles_kernel<4, 4>), dim3(cus), dim3(4 * 64), 0, st, p, blocks, sink);
+    if (mode == 4)
+      hipLaunchKernelGGL((probe_tiles_kernel<8, 1, true>), dim3(cus), dim3(8 * 64), 0, st, p, blocks, sink);
     return hipGetLastError();
   }
   if (mode == 3) {
